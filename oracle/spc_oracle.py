@@ -1,0 +1,344 @@
+"""Plain CPU oracle (NumPy, float64) of SpeContext's per-step sparse-KV decode path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the HIP library and its binding) never imports, calls or links it, and this
+module imports nothing from the product path.
+
+Every stage follows the pages' description step by step, in the pages'
+notation, with no blocking, fusion or reordering:
+
+  O1  retrieval scores      softmax(q K^T / sqrt(d)) per query head
+      (SpeContext blog, section 2 "why only part of the KV cache is needed",
+       the AttentionWeight formula; paper summary section 2.1)
+  O2  group score           element-wise max over the query heads of a GQA
+      group; MQA = one group; MHA = each head on its own
+      (blog section 5 "C1 retrieval head"; paper summary section 4.3)
+  O3  Top-K selection       the K positions with the largest group score
+      (blog section 2, "KV budget"; blog section 4 pseudocode, topk(k=kv_budget))
+  O4  elastic plan          to_load = S_now - S_last, written in place into the
+      slots freed by positions that left the selection
+      (blog section 4 pseudocode; blog section 6 worked example
+       {1,8,21,35} -> {1,8,21,50}; paper summary section 5.4 / Figure 7)
+  O5  elastic copy          host row -> device slot for every (pos, slot) pair
+      (blog section 4, async_prefetch(kv_cache[to_load]))
+  O6  sparse attention      softmax(q K_S^T / sqrt(d)) V_S over the selected
+      positions only, read from the host store BY POSITION
+      (blog section 4 pseudocode llm.forward(..., sparse_kv=resident_kv);
+       AttentionWeight formula of blog section 2)
+  O6m MLA                   select latent rows, expand ONLY the selected rows to
+      per-head K/V with the up-projections, then attend
+      (blog section 5 last paragraph; paper summary section 4.3, MLA bullet)
+  O7  statistics            adjacent-step overlap, bytes moved vs full reload
+      (blog section 6; paper summary sections 1 and 5.3)
+
+Readings taken where the pages are silent (each listed in the design doc):
+  * lower index wins a tie in the Top-K;
+  * the i-th ascending position to load goes to the i-th ascending freed slot;
+  * a sequence with n <= K valid positions selects all n; n = 0 selects none
+    and its attention output is zero;
+  * query head i belongs to KV head / group i // (H_q / H_kv) (consecutive
+    heads share a KV head);
+  * MLA scale is 1/sqrt(128 + 64) for scoring and attention.
+
+Inputs are NumPy arrays.  bf16 tensors are passed as their raw uint16 bit
+patterns together with ``dtype="bf16"``; ``to_f64`` widens them exactly.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# widening of stored inputs
+# ----------------------------------------------------------------------------
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of a stored input array to float64.
+
+    ``dtype`` is ``"f32"`` (float32 values) or ``"bf16"`` (uint16 bit patterns:
+    a bfloat16 is the upper half of an IEEE float32, so shifting its 16 bits
+    into the top of a 32-bit word gives the float32 with the same value).
+    """
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(x).view(np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ----------------------------------------------------------------------------
+# O1: retrieval scores  (AttentionWeight = softmax(Q K^T / sqrt(d)))
+# ----------------------------------------------------------------------------
+
+
+def softmax(x: np.ndarray) -> np.ndarray:
+    """softmax of a 1-D vector, computed with the usual max shift."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return x.copy()
+    e = np.exp(x - np.max(x))
+    return e / np.sum(e)
+
+
+def retrieval_scores(q: np.ndarray, k: np.ndarray, lengths: Sequence[int],
+                     scale: float) -> np.ndarray:
+    """Per-head attention weights of the retrieval head over the cached keys.
+
+    q: [B][H_q][d] float64, the retrieval head's query of the new token.
+    k: [B][H_kv][L_max][d] float64, the cached DLM keys.
+    lengths[b]: number of valid cached positions n of sequence b.
+    Returns probs [B][H_q][L_max]: probs[b, i, j] = softmax_j(scale * q_i . k_{g(i), j})
+    over j < n, and 0 for j >= n.  g(i) = i // (H_q / H_kv).
+    """
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    L = k.shape[2]
+    assert Hq % Hkv == 0
+    per_kv = Hq // Hkv
+    probs = np.zeros((B, Hq, L), dtype=np.float64)
+    for b in range(B):
+        n = int(min(max(int(lengths[b]), 0), L))
+        if n == 0:
+            continue
+        for i in range(Hq):
+            g = i // per_kv
+            logits = (k[b, g, :n, :] @ q[b, i, :]) * scale
+            probs[b, i, :n] = softmax(logits)
+    return probs
+
+
+# ----------------------------------------------------------------------------
+# O2: group score (element-wise max over the query heads of a group)
+# ----------------------------------------------------------------------------
+
+
+def group_scores(probs: np.ndarray, n_groups: int) -> np.ndarray:
+    """probs [B][H_q][L] -> group scores [B][n_groups][L].
+
+    Group r holds the consecutive query heads r*G .. r*G+G-1, G = H_q / n_groups;
+    its score at position j is the element-wise max of those heads' weights.
+    GQA: n_groups = H_kv.  MQA: n_groups = 1.  MHA / MLA: n_groups = H_q.
+    """
+    B, Hq, L = probs.shape
+    assert Hq % n_groups == 0
+    G = Hq // n_groups
+    out = np.empty((B, n_groups, L), dtype=np.float64)
+    for b in range(B):
+        for r in range(n_groups):
+            out[b, r] = np.max(probs[b, r * G:(r + 1) * G, :], axis=0)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O3: Top-K selection
+# ----------------------------------------------------------------------------
+
+
+def topk_select(scores: np.ndarray, n: int, budget: int) -> np.ndarray:
+    """The first min(K, n) positions of [0, n) ordered by (score desc, index asc).
+
+    scores: 1-D array of length >= n.  Returns the selected positions sorted
+    ascending (int64).  The order is a full sort of the candidates; the lower
+    index wins among equal scores.
+    """
+    n = int(n)
+    if n <= 0:
+        return np.zeros(0, dtype=np.int64)
+    s = np.asarray(scores[:n], dtype=np.float64)
+    idx = np.arange(n)
+    order = np.lexsort((idx, -s))  # primary key: -score; secondary: index
+    chosen = order[:min(int(budget), n)]
+    return np.sort(chosen).astype(np.int64)
+
+
+def select_all(group: np.ndarray, lengths: Sequence[int], budget: int) -> List[List[np.ndarray]]:
+    """Top-K of every (b, group) instance: returns sel[b][r] (ascending arrays)."""
+    B, Gn, _ = group.shape
+    return [[topk_select(group[b, r], int(lengths[b]), budget) for r in range(Gn)]
+            for b in range(B)]
+
+
+# ----------------------------------------------------------------------------
+# O4: elastic plan (set difference, in-place slot reuse)
+# ----------------------------------------------------------------------------
+
+
+def elastic_plan(selected: Sequence[int], slot_pos: Sequence[int]) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One (b, group) instance of the elastic-loading plan.
+
+    selected: the new selection S_now (any order).
+    slot_pos: the resident slot map before the step: slot x holds position
+              slot_pos[x], or -1 if empty.  Its non-empty entries are S_last.
+    Returns (to_load, load_slot, new_slot_pos):
+      to_load   = sorted(S_now - S_last), the positions to copy in;
+      freed     = sorted slots that are empty or hold a position not in S_now;
+      load_slot = freed[:len(to_load)]: to_load[i] is written into freed[i];
+      new_slot_pos: slot map after the step; kept positions never move,
+      freed slots left over become -1.
+    """
+    S_now = set(int(p) for p in selected)
+    slots = [int(p) for p in slot_pos]
+    S_last = set(p for p in slots if p != -1)
+    to_load = sorted(S_now - S_last)
+    freed = sorted(x for x in range(len(slots)) if slots[x] == -1 or slots[x] not in S_now)
+    assert len(to_load) <= len(freed), "budget exceeded: more positions to load than free slots"
+    new = list(slots)
+    for i, pos in enumerate(to_load):
+        new[freed[i]] = pos
+    for x in freed[len(to_load):]:
+        new[x] = -1
+    return (np.asarray(to_load, dtype=np.int64),
+            np.asarray(freed[:len(to_load)], dtype=np.int64),
+            np.asarray(new, dtype=np.int64))
+
+
+# ----------------------------------------------------------------------------
+# O5: elastic copy
+# ----------------------------------------------------------------------------
+
+
+def elastic_copy(host_rows: np.ndarray, dev_rows: np.ndarray,
+                 to_load: Sequence[int], load_slot: Sequence[int]) -> None:
+    """dev_rows[slot] <- host_rows[pos] for every (pos, slot) pair (any dtype, exact)."""
+    for pos, slot in zip(to_load, load_slot):
+        dev_rows[int(slot)] = host_rows[int(pos)]
+
+
+# ----------------------------------------------------------------------------
+# O6: sparse decode attention over the selected positions
+# ----------------------------------------------------------------------------
+
+
+def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                     positions: Sequence[int], scale: float) -> np.ndarray:
+    """softmax(scale * q . K[j]) weighted sum of V[j] over j in positions.
+
+    q: [d]; K: [L][d]; V: [L][dv]; returns [dv] (zeros if positions is empty).
+    """
+    pos = np.asarray(list(positions), dtype=np.int64)
+    if pos.size == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    logits = (K[pos] @ q) * scale
+    w = softmax(logits)
+    return w @ V[pos]
+
+
+def sparse_decode_layer(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                        sel: List[List[np.ndarray]], n_groups: int, scale: float) -> np.ndarray:
+    """All query heads of one target layer.
+
+    q: [B][H_q][d]; K, V: [B][H_kv][L][d] (read by position);
+    sel[b][r]: selected positions of group r, shared by its query heads.
+    Query head i reads group r = i // (H_q / n_groups) and KV head
+    i // (H_q / H_kv).  Returns [B][H_q][dv].
+    """
+    B, Hq, _ = q.shape
+    Hkv = K.shape[1]
+    Gq = Hq // n_groups
+    per_kv = Hq // Hkv
+    out = np.zeros((B, Hq, V.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for i in range(Hq):
+            r = i // Gq
+            g = i // per_kv
+            out[b, i] = sparse_attention(q[b, i], K[b, g], V[b, g], sel[b][r], scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O1/O6 for MLA: latent cache, literal expansion of the selected rows
+# ----------------------------------------------------------------------------
+
+
+def mla_expand_keys(latent: np.ndarray, rope: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
+    """Per-head keys of the given latent rows: K_h[j] = (W_UK[h] c_j) || r_j.
+
+    latent: [n][C]; rope: [n][R]; W_UK: [H][dn][C].  Returns [H][n][dn + R].
+    """
+    H = W_UK.shape[0]
+    n = latent.shape[0]
+    out = np.empty((H, n, W_UK.shape[1] + rope.shape[1]), dtype=np.float64)
+    for h in range(H):
+        out[h, :, :W_UK.shape[1]] = latent @ W_UK[h].T
+        out[h, :, W_UK.shape[1]:] = rope
+    return out
+
+
+def mla_retrieval_scores(q_nope: np.ndarray, q_rope: np.ndarray, latent: np.ndarray,
+                         rope: np.ndarray, W_UK: np.ndarray, lengths: Sequence[int],
+                         scale: float, heads: Sequence[int] | None = None) -> Dict[Tuple[int, int], np.ndarray]:
+    """Head-level retrieval scores over the MLA latent cache, keys expanded literally.
+
+    q_nope: [B][H][dn]; q_rope: [B][H][R]; latent: [B][L][C]; rope: [B][L][R];
+    W_UK: [H][dn][C].  Returns {(b, h): probs over the n valid positions}.
+    ``heads`` restricts the heads evaluated (all by default).
+    """
+    B, H, _ = q_nope.shape
+    out = {}
+    hs = range(H) if heads is None else heads
+    for b in range(B):
+        n = int(lengths[b])
+        for h in hs:
+            if n <= 0:
+                out[(b, h)] = np.zeros(0)
+                continue
+            Kh = np.concatenate([latent[b, :n] @ W_UK[h].T, rope[b, :n]], axis=1)
+            qh = np.concatenate([q_nope[b, h], q_rope[b, h]])
+            out[(b, h)] = softmax((Kh @ qh) * scale)
+    return out
+
+
+def mla_sparse_attention(q_nope: np.ndarray, q_rope: np.ndarray, latent: np.ndarray,
+                         rope: np.ndarray, W_UK: np.ndarray, W_UV: np.ndarray,
+                         positions: Sequence[int], h: int, scale: float) -> np.ndarray:
+    """One MLA head over its selected latent rows, expanding ONLY those rows.
+
+    K_h[j] = (W_UK[h] c_j) || r_j,  V_h[j] = W_UV[h] c_j, for j in positions;
+    then out = softmax(scale * q . K_h[j]) weighted sum of V_h[j].
+    q_nope: [dn]; q_rope: [R]; latent: [L][C]; rope: [L][R]; W_UK, W_UV: [H][d][C].
+    """
+    pos = np.asarray(list(positions), dtype=np.int64)
+    if pos.size == 0:
+        return np.zeros(W_UV.shape[1], dtype=np.float64)
+    c = latent[pos]
+    K = np.concatenate([c @ W_UK[h].T, rope[pos]], axis=1)
+    V = c @ W_UV[h].T
+    q = np.concatenate([q_nope, q_rope])
+    w = softmax((K @ q) * scale)
+    return w @ V
+
+
+# ----------------------------------------------------------------------------
+# O7: statistics the pages quote
+# ----------------------------------------------------------------------------
+
+
+def overlap(prev: Sequence[int], now: Sequence[int]) -> float:
+    """|S_now intersect S_prev| / |S_now| (1.0 for an empty S_now)."""
+    now = set(int(x) for x in now)
+    if not now:
+        return 1.0
+    return len(now & set(int(x) for x in prev)) / len(now)
+
+
+def transfer_fraction(n_loaded: int, n_full: int) -> float:
+    """Rows moved by elastic loading over the rows a full reload would move."""
+    return n_loaded / n_full if n_full else 0.0
+
+
+def kv_cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, elem_bytes: int,
+                   seq_len: int, batch: int = 1) -> int:
+    """Size of a full K+V cache: layers x KV heads x d x (K and V) x bytes x L x B."""
+    return n_layers * n_kv_heads * head_dim * 2 * elem_bytes * seq_len * batch
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(d), the scale of the AttentionWeight formula."""
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,149 @@
+"""Each pin must catch a plausible mistake: plant one in a copy of an oracle
+function (on the CPU) and check that the matching pin fails."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import spc_oracle as O
+from tests import pins
+
+
+def _scores(q, k, lengths, scale, *, sign=1.0, scale_pow=1.0, head_map="div", mask_len=True):
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    per_kv = Hq // Hkv
+    probs = np.zeros((B, Hq, L))
+    for b in range(B):
+        n = int(lengths[b]) if mask_len else L
+        if n == 0:
+            continue
+        for i in range(Hq):
+            g = i // per_kv if head_map == "div" else i % Hkv
+            logits = sign * (k[b, g, :n] @ q[b, i]) * scale ** scale_pow
+            probs[b, i, :n] = O.softmax(logits)
+    return probs
+
+
+def _fails(check, *args):
+    with pytest.raises(AssertionError):
+        check(*args)
+
+
+def test_pins_catch_score_mistakes():
+    _fails(pins.check_scores_closed_form, lambda *a: _scores(*a, sign=-1.0))
+    _fails(pins.check_scores_closed_form, lambda *a: _scores(*a, scale_pow=2.0))
+    _fails(pins.check_scores_vs_library, lambda *a: _scores(*a, head_map="mod"))
+    _fails(pins.check_scores_length_masking, lambda *a: _scores(*a, mask_len=False))
+
+
+def test_pins_catch_group_mistakes():
+    def mean_groups(p, n_groups):
+        B, Hq, L = p.shape
+        G = Hq // n_groups
+        return p.reshape(B, n_groups, G, L).mean(axis=2)
+
+    def strided_groups(p, n_groups):
+        B, Hq, L = p.shape
+        return np.stack([p[:, r::n_groups].max(axis=1) for r in range(n_groups)], axis=1)
+
+    _fails(pins.check_group_max_is_max_of_per_head, O.retrieval_scores, mean_groups)
+    _fails(pins.check_group_max_is_max_of_per_head, O.retrieval_scores, strided_groups)
+    _fails(pins.check_group_modes, mean_groups)
+
+
+def test_pins_catch_topk_mistakes():
+    def high_index_wins(s, n, k):
+        if n <= 0:
+            return np.zeros(0, dtype=np.int64)
+        order = np.lexsort((-np.arange(n), -np.asarray(s[:n])))
+        return np.sort(order[:min(k, n)])
+
+    def ascending_scores(s, n, k):
+        if n <= 0:
+            return np.zeros(0, dtype=np.int64)
+        order = np.lexsort((np.arange(n), np.asarray(s[:n])))
+        return np.sort(order[:min(k, n)])
+
+    def unsorted_output(s, n, k):
+        if n <= 0:
+            return np.zeros(0, dtype=np.int64)
+        return np.lexsort((np.arange(n), -np.asarray(s[:n])))[:min(k, n)]
+
+    def ignores_length(s, n, k):
+        return O.topk_select(s, len(s), k)[:min(k, n)] if n > 0 else np.zeros(0, dtype=np.int64)
+
+    for bad in (high_index_wins, ascending_scores, unsorted_output):
+        _fails(pins.check_topk_bruteforce, bad)
+        _fails(pins.check_topk_python_sorted, bad)
+    _fails(pins.check_topk_edge_cases, ignores_length)
+
+
+def test_pins_catch_plan_mistakes():
+    def rebuild_slots(selected, slot_pos):
+        # loads everything again into slots 0.. (no reuse, no in-place)
+        S = sorted(int(p) for p in selected)
+        new = np.full(len(slot_pos), -1); new[:len(S)] = S
+        return np.asarray(S), np.arange(len(S)), new
+
+    def descending_freed(selected, slot_pos):
+        S = set(int(p) for p in selected)
+        slots = [int(p) for p in slot_pos]
+        to_load = sorted(S - set(p for p in slots if p != -1))
+        freed = sorted((x for x in range(len(slots)) if slots[x] == -1 or slots[x] not in S), reverse=True)
+        new = list(slots)
+        for i, p in enumerate(to_load):
+            new[freed[i]] = p
+        for x in freed[len(to_load):]:
+            new[x] = -1
+        return np.asarray(to_load), np.asarray(freed[:len(to_load)]), np.asarray(new)
+
+    def union_not_difference(selected, slot_pos):
+        t, s, new = O.elastic_plan(selected, slot_pos)
+        return np.asarray(sorted(int(p) for p in selected)), s, new
+
+    _fails(pins.check_plan_worked_example, rebuild_slots)
+    _fails(pins.check_plan_invariants, rebuild_slots)
+    _fails(pins.check_plan_invariants, descending_freed)
+    _fails(pins.check_plan_worked_example, union_not_difference)
+
+
+def test_pins_catch_attention_mistakes():
+    def no_scale(q, K, V, positions, scale):
+        return O.sparse_attention(q, K, V, positions, 1.0)
+
+    def keys_as_values(q, K, V, positions, scale):
+        pos = np.asarray(list(positions), dtype=np.int64)
+        if pos.size == 0:
+            return np.zeros(V.shape[1])
+        return O.softmax(K[pos] @ q * scale) @ K[pos][:, :V.shape[1]] if K.shape[1] >= V.shape[1] \
+            else O.softmax(K[pos] @ q * scale) @ np.resize(K[pos], (pos.size, V.shape[1]))
+
+    def wrong_head_layer(q, K, V, sel, n_groups, scale):
+        B, Hq, _ = q.shape
+        Hkv = K.shape[1]
+        out = np.zeros((B, Hq, V.shape[-1]))
+        for b in range(B):
+            for i in range(Hq):
+                g = i % Hkv
+                out[b, i] = O.sparse_attention(q[b, i], K[b, g], V[b, g], sel[b][g], scale)
+        return out
+
+    _fails(pins.check_attention_subset_vs_masked_library, no_scale)
+    _fails(pins.check_attention_subset_vs_masked_library, keys_as_values)
+    _fails(pins.check_attention_full_budget, O.topk_select, wrong_head_layer)
+
+
+def test_pins_catch_mla_mistakes():
+    def keys_from_value_proj(q_nope, q_rope, latent, rope, W_UK, W_UV, positions, h, scale):
+        return O.mla_sparse_attention(q_nope, q_rope, latent, rope, W_UV, W_UV, positions, h, scale)
+
+    def dropped_rope(q_nope, q_rope, latent, rope, W_UK, W_UV, positions, h, scale):
+        return O.mla_sparse_attention(q_nope, 0 * q_rope, latent, rope, W_UK, W_UV, positions, h, scale)
+
+    _fails(pins.check_mla_literal_vs_absorbed, keys_from_value_proj, O.mla_retrieval_scores)
+    _fails(pins.check_mla_literal_vs_absorbed, dropped_rope, O.mla_retrieval_scores)
+
+
+def test_pins_catch_size_mistakes():
+    _fails(pins.check_kv_cache_size, lambda l, h, d, e, s, b=1: l * h * d * e * s * b)   # forgot K and V
