@@ -1,0 +1,206 @@
+/*
+ * spc.h - C ABI of the MI355X (gfx950) sparse-KV decode path of SpeContext
+ * ("speculative context sparsity", Xu et al.).
+ *
+ * One decode step is four stages; each is a call below and runs as
+ * hand-written HIP kernels on the caller's stream(s):
+ *
+ *   spc_retrieval_scores     per-head attention weights softmax(q K^T / sqrt(d))
+ *                            of the retrieval head over every cached key
+ *   spc_group_max_topk       element-wise max over each GQA group, then the
+ *                            Top-K positions per group (the KV budget)
+ *   spc_elastic_update       to_load = selected - resident; copy only those
+ *                            K/V rows, in place, from pinned host memory into
+ *                            the freed device slots
+ *   spc_sparse_decode_attn   decode attention over the resident sparse KV only
+ *
+ * Conventions shared by every call:
+ *   - All calls are asynchronous on the given HIP stream(s) (void* holding a
+ *     hipStream_t; NULL = the null stream).  None allocates device memory,
+ *     frees, or synchronizes.  Device faults surface at the caller's next
+ *     synchronization.
+ *   - The caller owns every buffer.  Device buffers are plain device pointers.
+ *     Scratch space is the caller's `ws` buffer of at least
+ *     spc_workspace_size(call, shape) bytes; ws contents need no
+ *     initialization and are not preserved between calls.
+ *   - Every argument is validated on the host before anything is launched;
+ *     a call that returns an error has launched nothing.
+ *   - Device pointers of vector data must be 16-byte aligned.
+ *   - Errors are returned as spc_status; spc_last_error() gives a
+ *     thread-local message for the last failing call.  Nothing aborts or
+ *     prints across the ABI.
+ *   - lengths[b] (valid cached positions of sequence b) are clamped to
+ *     [0, max_len] on the device.
+ *   - Head maps: query head i reads KV head i / (n_q_heads / n_kv_heads) and
+ *     belongs to selection group i / (n_q_heads / n_groups) (consecutive
+ *     heads share).  GQA: n_groups = n_kv_heads; MQA: n_groups = 1;
+ *     MHA: n_groups = n_q_heads = n_kv_heads; MLA (one shared latent KV
+ *     head): n_kv_heads = 1, n_groups = n_q_heads.
+ */
+#ifndef SPC_H
+#define SPC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPC_ABI_VERSION 1
+
+typedef enum spc_status {
+  SPC_OK = 0,
+  SPC_ERR_INVALID_ARG = 1,  /* null pointer, bad size, head counts that do not divide, misalignment */
+  SPC_ERR_UNSUPPORTED = 2,  /* a dtype / head_dim combination this library does not build */
+  SPC_ERR_WORKSPACE = 3,    /* ws smaller than spc_workspace_size() */
+  SPC_ERR_NOT_MAPPED = 4,   /* host KV pointer is not pinned, device-mapped memory */
+  SPC_ERR_HIP = 5           /* a HIP runtime call or launch failed; see spc_last_error() */
+} spc_status;
+
+typedef enum spc_dtype { SPC_F32 = 0, SPC_BF16 = 1 } spc_dtype;
+
+/* Problem shape, shared by all calls. */
+typedef struct spc_shape {
+  int32_t batch;       /* B: sequences */
+  int32_t n_q_heads;   /* H_q */
+  int32_t n_kv_heads;  /* H_kv: key heads of the scored cache (MLA: 1) */
+  int32_t n_groups;    /* selection groups (see head maps above) */
+  int32_t head_dim;    /* d of the scored keys: 128 (MLA: 512 latent + 64 rope = 576) */
+  int32_t v_dim;       /* value dimension: 128 (MLA: 512) */
+  int32_t max_len;     /* L_max: capacity of the position axis */
+  int32_t budget;      /* K: KV budget per group, 1 <= K <= max_len */
+  int32_t n_layers;    /* target layers held in the KV stores */
+  int32_t dtype;       /* spc_dtype of q, keys and K/V */
+  float scale;         /* logit scale, 1/sqrt(d) (MLA: 1/sqrt(192)) */
+} spc_shape;
+
+/* Element strides (not bytes) of a K/V store, host or device.  A K row of
+ * head_dim elements and a V row of v_dim elements are each contiguous
+ * (unit stride).  Row `r` of layer `l`, KV head `h`, sequence `b`:
+ *   K at  base + b*s_b + l*s_layer + h*s_head + r*s_row
+ *   V at  the same + s_kv
+ * s_kv = 0 reads V from the first v_dim elements of the K row (MLA latent). */
+typedef struct spc_kv_layout {
+  int64_t s_b, s_layer, s_head, s_row, s_kv;
+} spc_kv_layout;
+
+/* Element strides of the per-layer target queries q[b][layer][head][0..d).
+ * s_layer = 0 lets every layer read the same query. */
+typedef struct spc_q_layout {
+  int64_t s_b, s_layer, s_head;
+} spc_q_layout;
+
+/* which_call for spc_workspace_size */
+enum { SPC_CALL_SCORES = 1, SPC_CALL_TOPK = 2, SPC_CALL_ELASTIC = 3, SPC_CALL_ATTN = 4 };
+
+/* flags of spc_elastic_update */
+enum { SPC_PLAN = 1u, SPC_COPY = 2u };
+
+/* row modes of spc_sparse_decode_attn */
+enum {
+  SPC_ROWS_SLOTS = 0,  /* rows = slot map [B][n_groups][budget]; slot x is attended iff rows[x] >= 0,
+                          and its K/V is row x of the store */
+  SPC_ROWS_GATHER = 1  /* rows = position lists [B][n_groups][budget], first row_count[b][g] valid;
+                          K/V is row rows[i] of the store (e.g. selections into a full cache) */
+};
+
+int spc_abi_version(void);
+const char* spc_status_string(int status);
+const char* spc_last_error(void);
+
+/* Bytes of scratch the call needs for this shape (0 if none). */
+size_t spc_workspace_size(int which_call, const spc_shape* s);
+
+/*
+ * Stage 1 - retrieval scores.  The retrieval head's attention weights of one
+ * new query token over all cached keys, per query head:
+ *   probs[b][i][j] = softmax_j( scale * q[b][i] . k[b][i / (H_q/H_kv)][j] ),  j < lengths[b]
+ * (SpeContext blog section 2, AttentionWeight formula; blog section 5 and paper
+ * summary sections 4.2-4.3: only the Q/K path of the distilled model is kept,
+ * head-level weights.)
+ *   q        device [B][H_q][head_dim], dtype s->dtype (MLA: absorbed query, see spc_mla_absorb_q)
+ *   k        device [B][H_kv][max_len][head_dim], dtype s->dtype
+ *   lengths  device [B] int32
+ *   probs    device [B][H_q][max_len] float32 out; entries j >= lengths[b] are left untouched
+ * Requires head_dim % 8 == 0.  The softmax is exact up to float32 rounding
+ * (all positions, no approximation).
+ */
+int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const int32_t* lengths,
+                         float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 2 - group max and Top-K.
+ *   v[b][g][j] = max over the query heads i of group g of probs[b][i][j]
+ *   S[b][g]    = the first min(K, n) positions j < n = lengths[b] ordered by
+ *                (v desc, j asc): the lower index wins a tie
+ * (blog section 5, GQA element-wise max then per-group Top-K, MQA one group,
+ * MHA per head; blog section 2, the KV budget K; paper summary section 4.3.)
+ *   probs      device [B][H_q][max_len] float32 (as written by stage 1)
+ *   sel_idx    device [B][n_groups][budget] int32 out: S ascending, -1 after sel_count
+ *   sel_count  device [B][n_groups] int32 out: min(K, n)
+ * The selection is exact on the float32 values (no approximation).
+ */
+int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
+                       int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 3 - elastic loading (blog section 4 pseudocode: to_load = selected -
+ * resident_kv_indices, async_prefetch(kv_cache[to_load]); blog section 6
+ * worked example {1,8,21,35} -> {1,8,21,50} loads only 50, in place of 35;
+ * paper summary section 5.4: fixed budget, in place).
+ *
+ * State, per (b, g), owned by the caller and initialised by spc_elastic_reset:
+ *   slot_pos     device [B][n_groups][budget] int32: position held by slot x, or -1
+ *   resident_bm  device [B][n_groups][ceil(max_len/32)] uint32: bit j set iff some
+ *                slot holds position j
+ * SPC_PLAN (on plan_stream):
+ *   to_load = sorted(S - R) where R = {slot_pos[x] != -1}
+ *   freed   = sorted slots that are empty or hold a position not in S
+ *   load_pos[i] = to_load[i], load_slot[i] = freed[i], load_count = |to_load|;
+ *   slot_pos[freed[i]] = to_load[i]; freed slots left over become -1; resident_bm
+ *   follows.  Kept positions never move.  Entries after load_count are -1.
+ *   load_pos, load_slot: device [B][n_groups][budget] int32; load_count [B][n_groups].
+ * SPC_COPY (on copy_stream, reading the load lists): for every layer l in
+ *   [layer_begin, layer_end) and i < load_count[b][g]:
+ *     dev_kv  K,V row load_slot[i] of (b, l, g)  <-  host_kv K,V row load_pos[i] of (b, l, g)
+ *   host_kv must be pinned host memory mapped for the device (hipHostMalloc,
+ *   torch pin_memory=True); the device reads it directly over the host link.
+ *   Requires n_groups == n_kv_heads.
+ * With both flags, the plan runs on plan_stream and the copy on copy_stream;
+ * the caller orders copy_stream after plan_stream (e.g. with an event) when they
+ * differ.  Run SPC_PLAN exactly once per step: a repeated plan is empty.
+ */
+int spc_elastic_update(const spc_shape* s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
+                       uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                       const void* host_kv, const spc_kv_layout* host_l, void* dev_kv,
+                       const spc_kv_layout* dev_l, int32_t layer_begin, int32_t layer_end, unsigned flags,
+                       void* plan_stream, void* copy_stream);
+
+/* Empty every slot of sequence `batch_index` (or of all sequences if -1):
+ * slot_pos = -1, resident_bm = 0.  The next plan loads its whole selection. */
+int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos, uint32_t* resident_bm,
+                      void* stream);
+
+/*
+ * Stage 4 - sparse decode attention over the resident sparse KV only
+ * (blog section 4 pseudocode, llm.forward(..., sparse_kv=resident_kv); the
+ * AttentionWeight formula of blog section 2):
+ *   out[b][l][i] = sum_r softmax_r(scale * q_l[b][i] . K[r]) V[r]
+ * over the rows r of group i / (H_q/n_groups) (see row modes above), for every
+ * layer l in [layer_begin, layer_end).
+ *   q, q_l   device queries, dtype s->dtype, strides q_l (elements)
+ *   kv, kv_l device K/V store, dtype s->dtype (slots, or a full cache for GATHER)
+ *   rows, row_count  see SPC_ROWS_*; row_count is ignored for SLOTS
+ *   out      device [B][n_layers][H_q][v_dim] float32; only layers in range are written
+ * A group with no rows writes zeros.  Accumulation is float32.
+ */
+int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                           const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count,
+                           int rows_mode, int32_t layer_begin, int32_t layer_end, float* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPC_H */

@@ -1,0 +1,132 @@
+"""Thin Python binding of libspc with the C-ABI's names (argument marshalling only).
+
+Tensors are torch tensors; their ``data_ptr()`` is handed to the library.  Every
+stage runs in the library's HIP kernels; nothing here computes.  A non-OK
+status raises ``SpcError`` carrying the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_SCORES, SPC_COPY, SPC_F32, SPC_PLAN, SPC_ROWS_GATHER,
+                   SPC_ROWS_SLOTS, SpcKvLayout, SpcQLayout, SpcShape)
+
+__all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version", "spc_workspace_size",
+           "spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_elastic_reset",
+           "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
+           "SPC_CALL_SCORES", "SPC_CALL_ATTN"]
+
+
+class SpcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = L.lib()
+        msg = lib.spc_last_error().decode() or lib.spc_status_string(status).decode()
+        raise SpcError(status, msg)
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, n_groups, head_dim, v_dim, max_len, budget, n_layers, dtype,
+               scale) -> SpcShape:
+    dt = {"f32": SPC_F32, "bf16": SPC_BF16, torch.float32: SPC_F32, torch.bfloat16: SPC_BF16}[dtype]
+    return SpcShape(batch, n_q_heads, n_kv_heads, n_groups, head_dim, v_dim, max_len, budget, n_layers, dt,
+                    float(scale))
+
+
+def kv_layout(t: torch.Tensor) -> SpcKvLayout:
+    """Layout of a K/V store shaped [B][layers][H][rows][2][d] (any strides)."""
+    assert t.dim() == 6, "expected [B][layers][H][rows][2][d]"
+    s = t.stride()
+    assert s[5] == 1, "d must be contiguous"
+    return SpcKvLayout(s[0], s[1], s[2], s[3], s[4])
+
+
+def q_layout(s_b: int, s_layer: int, s_head: int) -> SpcQLayout:
+    return SpcQLayout(int(s_b), int(s_layer), int(s_head))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def spc_abi_version() -> int:
+    return L.lib().spc_abi_version()
+
+
+def spc_workspace_size(call: int, shape: SpcShape) -> int:
+    return int(L.lib().spc_workspace_size(call, ctypes.byref(shape)))
+
+
+_ws_cache = {}
+
+
+def _workspace(call: int, shape: SpcShape, device) -> torch.Tensor:
+    n = spc_workspace_size(call, shape)
+    key = (call, n, str(device))
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def spc_retrieval_scores(shape: SpcShape, q, k, lengths, probs, ws=None, stream=None) -> None:
+    for t, n in ((q, "q"), (k, "k"), (lengths, "lengths"), (probs, "probs")):
+        _dev(t, n)
+    ws = _workspace(SPC_CALL_SCORES, shape, q.device) if ws is None else ws
+    _check(L.lib().spc_retrieval_scores(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(lengths), _ptr(probs),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spc_group_max_topk(shape: SpcShape, probs, lengths, sel_idx, sel_count, stream=None) -> None:
+    for t, n in ((probs, "probs"), (lengths, "lengths"), (sel_idx, "sel_idx"), (sel_count, "sel_count")):
+        _dev(t, n)
+    _check(L.lib().spc_group_max_topk(ctypes.byref(shape), _ptr(probs), _ptr(lengths), _ptr(sel_idx),
+                                      _ptr(sel_count), None, 0, _stream(stream)))
+
+
+def spc_elastic_update(shape: SpcShape, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,
+                       load_count, host_kv=None, host_l: Optional[SpcKvLayout] = None, dev_kv=None,
+                       dev_l: Optional[SpcKvLayout] = None, layer_begin: int = 0, layer_end: int = 0,
+                       flags: int = SPC_PLAN, plan_stream=None, copy_stream=None) -> None:
+    _check(L.lib().spc_elastic_update(
+        ctypes.byref(shape), _ptr(sel_idx), _ptr(sel_count), _ptr(slot_pos), _ptr(resident_bm), _ptr(load_pos),
+        _ptr(load_slot), _ptr(load_count), _ptr(host_kv), ctypes.byref(host_l) if host_l is not None else None,
+        _ptr(dev_kv), ctypes.byref(dev_l) if dev_l is not None else None, int(layer_begin), int(layer_end),
+        int(flags), _stream(plan_stream), _stream(copy_stream if copy_stream is not None else plan_stream)))
+
+
+def spc_elastic_reset(shape: SpcShape, batch_index: int, slot_pos, resident_bm, stream=None) -> None:
+    _check(L.lib().spc_elastic_reset(ctypes.byref(shape), int(batch_index), _ptr(slot_pos), _ptr(resident_bm),
+                                     _stream(stream)))
+
+
+def spc_sparse_decode_attn(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvLayout, rows, row_count,
+                           rows_mode: int, layer_begin: int, layer_end: int, out, ws=None, stream=None) -> None:
+    _dev(out, "out")
+    ws = _workspace(SPC_CALL_ATTN, shape, out.device) if ws is None else ws
+    _check(L.lib().spc_sparse_decode_attn(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
+        int(rows_mode), int(layer_begin), int(layer_end), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))

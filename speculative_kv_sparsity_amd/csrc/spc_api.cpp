@@ -1,0 +1,220 @@
+// C ABI of libspc: argument validation, workspace sizes, error reporting and
+// dispatch to the HIP launchers.  Nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/spc.h"
+#include "spc_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SPC_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SPC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_bytes(const spc_shape* s) { return s->dtype == SPC_BF16 ? 2 : 4; }
+
+int check_shape(const spc_shape* s) {
+  if (!s) return fail(SPC_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_groups < 1)
+    return fail(SPC_ERR_INVALID_ARG, "batch and head counts must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(SPC_ERR_INVALID_ARG, "n_q_heads (%d) %% n_kv_heads (%d) != 0", s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads % s->n_groups != 0)
+    return fail(SPC_ERR_INVALID_ARG, "n_q_heads (%d) %% n_groups (%d) != 0", s->n_q_heads, s->n_groups);
+  if (s->n_groups % s->n_kv_heads != 0)
+    return fail(SPC_ERR_INVALID_ARG, "n_groups (%d) must be a multiple of n_kv_heads (%d)", s->n_groups,
+                s->n_kv_heads);
+  if (s->max_len < 1) return fail(SPC_ERR_INVALID_ARG, "max_len must be >= 1");
+  if (s->budget < 1 || s->budget > s->max_len)
+    return fail(SPC_ERR_INVALID_ARG, "budget (%d) must be in [1, max_len=%d]", s->budget, s->max_len);
+  if (s->n_layers < 1) return fail(SPC_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (s->dtype != SPC_F32 && s->dtype != SPC_BF16) return fail(SPC_ERR_UNSUPPORTED, "dtype %d", s->dtype);
+  if (s->head_dim < 1 || s->v_dim < 1) return fail(SPC_ERR_INVALID_ARG, "head_dim and v_dim must be >= 1");
+  if (!(s->scale > 0.f)) return fail(SPC_ERR_INVALID_ARG, "scale must be > 0");
+  return SPC_OK;
+}
+
+hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
+
+}  // namespace
+
+extern "C" {
+
+int spc_abi_version(void) { return SPC_ABI_VERSION; }
+
+const char* spc_status_string(int status) {
+  switch (status) {
+    case SPC_OK: return "ok";
+    case SPC_ERR_INVALID_ARG: return "invalid argument";
+    case SPC_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SPC_ERR_WORKSPACE: return "workspace too small";
+    case SPC_ERR_NOT_MAPPED: return "host pointer is not pinned device-mapped memory";
+    case SPC_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* spc_last_error(void) { return g_last_error.c_str(); }
+
+size_t spc_workspace_size(int which_call, const spc_shape* s) {
+  if (check_shape(s) != SPC_OK) return 0;
+  switch (which_call) {
+    case SPC_CALL_SCORES: return spc::scores_ws_bytes(*s);
+    case SPC_CALL_ATTN: return spc::attn_ws_bytes(*s);
+    default: return 0;
+  }
+}
+
+int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const int32_t* lengths, float* probs,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!q || !k || !lengths || !probs) return fail(SPC_ERR_INVALID_ARG, "NULL q, k, lengths or probs");
+  if (!spc::scores_supported(*s))
+    return fail(SPC_ERR_UNSUPPORTED, "retrieval scores: head_dim %d with dtype %d", s->head_dim, s->dtype);
+  if (!aligned16(q) || !aligned16(k)) return fail(SPC_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (!aligned4(probs) || !aligned4(lengths)) return fail(SPC_ERR_INVALID_ARG, "probs/lengths misaligned");
+  const size_t need = spc::scores_ws_bytes(*s);
+  if (ws_bytes < need || (need && !ws))
+    return fail(SPC_ERR_WORKSPACE, "retrieval scores need %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = spc::launch_scores(*s, q, k, lengths, probs, ws, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "retrieval scores launch");
+}
+
+int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
+                       int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (int e = check_shape(s)) return e;
+  if (!probs || !lengths || !sel_idx || !sel_count)
+    return fail(SPC_ERR_INVALID_ARG, "NULL probs, lengths, sel_idx or sel_count");
+  if (!aligned4(probs) || !aligned4(sel_idx) || !aligned4(sel_count) || !aligned4(lengths))
+    return fail(SPC_ERR_INVALID_ARG, "misaligned int32/float buffer");
+  const hipError_t e = spc::launch_topk(*s, probs, lengths, sel_idx, sel_count, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "group max / top-k launch");
+}
+
+int spc_elastic_update(const spc_shape* s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
+                       uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                       const void* host_kv, const spc_kv_layout* host_l, void* dev_kv, const spc_kv_layout* dev_l,
+                       int32_t layer_begin, int32_t layer_end, unsigned flags, void* plan_stream,
+                       void* copy_stream) {
+  if (int e = check_shape(s)) return e;
+  if ((flags & ~(unsigned)(SPC_PLAN | SPC_COPY)) != 0 || flags == 0)
+    return fail(SPC_ERR_INVALID_ARG, "flags must be a non-empty combination of SPC_PLAN and SPC_COPY");
+  if (!load_pos || !load_slot || !load_count) return fail(SPC_ERR_INVALID_ARG, "NULL load lists");
+  if (flags & SPC_PLAN) {
+    if (!sel_idx || !sel_count || !slot_pos || !resident_bm)
+      return fail(SPC_ERR_INVALID_ARG, "plan needs sel_idx, sel_count, slot_pos and resident_bm");
+    if (s->budget > spc::kPlanMaxBudget)
+      return fail(SPC_ERR_UNSUPPORTED, "budget %d exceeds the plan kernel's %d", s->budget, spc::kPlanMaxBudget);
+  }
+  const void* host_dev = nullptr;
+  if (flags & SPC_COPY) {
+    if (!host_kv || !host_l || !dev_kv || !dev_l)
+      return fail(SPC_ERR_INVALID_ARG, "copy needs host_kv, host layout, dev_kv and device layout");
+    if (s->n_groups != s->n_kv_heads)
+      return fail(SPC_ERR_UNSUPPORTED, "copy needs one selection group per KV head (n_groups == n_kv_heads)");
+    if ((long long)s->batch * s->n_groups > spc::kCopyMaxInstances)
+      return fail(SPC_ERR_UNSUPPORTED, "batch * n_groups exceeds %d", spc::kCopyMaxInstances);
+    if (layer_begin < 0 || layer_end > s->n_layers || layer_begin >= layer_end)
+      return fail(SPC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
+                  s->n_layers);
+    const int eb = elem_bytes(s);
+    if ((s->head_dim * eb) % 16 || (s->v_dim * eb) % 16)
+      return fail(SPC_ERR_UNSUPPORTED, "K and V rows must be whole 16-byte vectors");
+    const spc_kv_layout* ls[2] = {host_l, dev_l};
+    for (const spc_kv_layout* l : ls) {
+      if ((l->s_b * eb) % 16 || (l->s_layer * eb) % 16 || (l->s_head * eb) % 16 || (l->s_row * eb) % 16 ||
+          (l->s_kv * eb) % 16)
+        return fail(SPC_ERR_INVALID_ARG, "K/V layout strides must be multiples of 16 bytes");
+    }
+    if (!aligned16(host_kv) || !aligned16(dev_kv)) return fail(SPC_ERR_INVALID_ARG, "KV stores must be 16-byte aligned");
+    hipPointerAttribute_t attr;
+    hipError_t he = hipPointerGetAttributes(&attr, host_kv);
+    if (he != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+      (void)hipGetLastError();
+      return fail(SPC_ERR_NOT_MAPPED, "host_kv %p is not pinned, device-mapped host memory", host_kv);
+    }
+    host_dev = attr.devicePointer;
+  }
+  if (flags & SPC_PLAN) {
+    const hipError_t e = spc::launch_plan(*s, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,
+                                          load_count, as_stream(plan_stream));
+    if (e != hipSuccess) return hip_fail(e, "elastic plan launch");
+  }
+  if (flags & SPC_COPY) {
+    const hipError_t e = spc::launch_copy(*s, load_pos, load_slot, load_count, host_dev, *host_l, dev_kv, *dev_l,
+                                          layer_begin, layer_end, as_stream(copy_stream));
+    if (e != hipSuccess) return hip_fail(e, "elastic copy launch");
+  }
+  return ok();
+}
+
+int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos, uint32_t* resident_bm,
+                      void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!slot_pos || !resident_bm) return fail(SPC_ERR_INVALID_ARG, "NULL slot_pos or resident_bm");
+  if (batch_index < -1 || batch_index >= s->batch)
+    return fail(SPC_ERR_INVALID_ARG, "batch_index %d outside [-1, %d)", batch_index, s->batch);
+  const int b0 = batch_index < 0 ? 0 : batch_index;
+  const int b1 = batch_index < 0 ? s->batch : batch_index + 1;
+  const hipError_t e = spc::launch_reset(*s, b0, b1, slot_pos, resident_bm, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "elastic reset launch");
+}
+
+int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                           const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
+                           int32_t layer_begin, int32_t layer_end, float* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!q || !q_l || !kv || !kv_l || !rows || !out) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (rows_mode != SPC_ROWS_SLOTS && rows_mode != SPC_ROWS_GATHER)
+    return fail(SPC_ERR_INVALID_ARG, "rows_mode %d", rows_mode);
+  if (rows_mode == SPC_ROWS_GATHER && !row_count) return fail(SPC_ERR_INVALID_ARG, "GATHER needs row_count");
+  if (layer_begin < 0 || layer_end > s->n_layers || layer_begin >= layer_end)
+    return fail(SPC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end, s->n_layers);
+  if (!spc::attn_supported(*s))
+    return fail(SPC_ERR_UNSUPPORTED, "attention: head_dim %d / v_dim %d with dtype %d", s->head_dim, s->v_dim,
+                s->dtype);
+  const int eb = elem_bytes(s);
+  if (!aligned16(q) || !aligned16(kv)) return fail(SPC_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
+  if ((q_l->s_b * eb) % 16 || (q_l->s_layer * eb) % 16 || (q_l->s_head * eb) % 16)
+    return fail(SPC_ERR_INVALID_ARG, "query strides must be multiples of 16 bytes");
+  if ((kv_l->s_b * eb) % 16 || (kv_l->s_layer * eb) % 16 || (kv_l->s_head * eb) % 16 || (kv_l->s_row * eb) % 16 ||
+      (kv_l->s_kv * eb) % 16)
+    return fail(SPC_ERR_INVALID_ARG, "K/V strides must be multiples of 16 bytes");
+  const size_t need = spc::attn_ws_bytes(*s);
+  if (ws_bytes < need || !ws)
+    return fail(SPC_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = spc::launch_attn(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin, layer_end,
+                                        out, ws, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "sparse decode attention launch");
+}
+
+}  // extern "C"

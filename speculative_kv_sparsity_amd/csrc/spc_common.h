@@ -1,0 +1,174 @@
+// Internal device helpers shared by the HIP kernels of libspc (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spc.h"
+
+namespace spc {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- element access
+
+// A 16-byte vector of stored elements: 8 bf16 or 4 fp32.
+struct alignas(16) Vec16 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Vec16 ld16(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  Vec16 r;
+  r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  return r;
+}
+
+__device__ __forceinline__ void st16(void* p, const Vec16& r) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+}
+
+// bf16 is the upper half of an fp32: widening is a shift.
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c on packed bf16 pairs (v_dot2_f32_bf16), fp32 result.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// Dot product of two 16-byte chunks (8 bf16 or 4 fp32), accumulated into c.
+template <int DT>
+__device__ __forceinline__ float dot16(const Vec16& a, const Vec16& b, float c);
+
+template <>
+__device__ __forceinline__ float dot16<SPC_BF16>(const Vec16& a, const Vec16& b, float c) {
+  c = dot2_bf16(a.w[0], b.w[0], c);
+  c = dot2_bf16(a.w[1], b.w[1], c);
+  c = dot2_bf16(a.w[2], b.w[2], c);
+  c = dot2_bf16(a.w[3], b.w[3], c);
+  return c;
+}
+
+template <>
+__device__ __forceinline__ float dot16<SPC_F32>(const Vec16& a, const Vec16& b, float c) {
+  c = fmaf(__uint_as_float(a.w[0]), __uint_as_float(b.w[0]), c);
+  c = fmaf(__uint_as_float(a.w[1]), __uint_as_float(b.w[1]), c);
+  c = fmaf(__uint_as_float(a.w[2]), __uint_as_float(b.w[2]), c);
+  c = fmaf(__uint_as_float(a.w[3]), __uint_as_float(b.w[3]), c);
+  return c;
+}
+
+// Elements per 16-byte chunk.
+template <int DT> struct ElemsPerChunk;
+template <> struct ElemsPerChunk<SPC_BF16> { static constexpr int value = 8; };
+template <> struct ElemsPerChunk<SPC_F32> { static constexpr int value = 4; };
+
+// Widen a 16-byte chunk into EPC floats.
+template <int DT>
+__device__ __forceinline__ void widen16(const Vec16& a, float* out);
+
+template <>
+__device__ __forceinline__ void widen16<SPC_BF16>(const Vec16& a, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = bf_lo(a.w[i]);
+    out[2 * i + 1] = bf_hi(a.w[i]);
+  }
+}
+
+template <>
+__device__ __forceinline__ void widen16<SPC_F32>(const Vec16& a, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(a.w[i]);
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+// DPP move within rows of 16 lanes (bound_ctrl: out-of-range reads give 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within each 8-lane half row
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the total.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Max / sum over lanes that share (lane & 7): the 8 lanes l, l+8, ..., l+56.
+__device__ __forceinline__ float max_across_rows8(float v) {
+  v = fmaxf(v, __shfl_xor(v, 8, kWave));
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float sum_across_rows8(float v) {
+  v += __shfl_xor(v, 8, kWave);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Inclusive scan of a uint32 over the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan over the block (blockDim.x a multiple of 64, <= 1024).
+// `smem` holds >= 16 words; returns the exclusive prefix, `total` the block sum.
+// Ends with a barrier so smem can be reused right away.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* smem, uint32_t& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == kWave - 1) smem[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t w = lane < nw ? smem[lane] : 0u;
+    w = wave_incl_scan(w);
+    if (lane < nw) smem[lane] = w;
+  }
+  __syncthreads();
+  const uint32_t base = wid ? smem[wid - 1] : 0u;
+  total = smem[nw - 1];
+  __syncthreads();
+  return base + incl - v;
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* lengths, int b, int max_len) {
+  int n = lengths[b];
+  return n < 0 ? 0 : (n > max_len ? max_len : n);
+}
+
+}  // namespace spc

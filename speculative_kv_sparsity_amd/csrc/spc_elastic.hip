@@ -1,0 +1,233 @@
+// Stage 3 - elastic loading: plan (set difference, in-place slot reuse) and copy.
+//
+// The SpeContext blog's section 4 loop computes to_load = selected -
+// resident_kv_indices and prefetches only kv_cache[to_load]; its section 6
+// worked example ({1,8,21,35} -> {1,8,21,50}) loads only 50, into the place of
+// 35; the paper summary's section 5.4 keeps the budget fixed and loads in place.
+//
+// plan_kernel  one workgroup (1024 threads) per (b, g).  A slot is kept iff its
+//   position is in S (binary search in the ascending S held in LDS); a
+//   position of S is loaded iff its bit in the resident bitmap is clear.  Two
+//   ordered compactions (block scans over contiguous ranges) give the freed
+//   slots and the positions to load, both ascending; the i-th position goes to
+//   the i-th freed slot.  Slot map and bitmap are then updated in place.
+// copy_kernel  a grid-stride gather over (layer, instance, entry, 16-byte
+//   vector): every lane reads 16 bytes of a K||V row straight from pinned,
+//   device-mapped host memory over the host link and writes them into the
+//   row's slot in HBM.  Consecutive lanes cover consecutive bytes of a row, so
+//   each wave reads whole rows; each lane keeps several reads in flight.
+#include "spc_common.h"
+#include "spc_launch.h"
+
+namespace spc {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPerThreadMax = kPlanMaxBudget / kPlanThreads;   // contiguous slots / entries per thread
+
+__device__ __forceinline__ bool sorted_contains(const int32_t* a, int n, int32_t v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo < n && a[lo] == v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ sel_idx,
+                                                            const int32_t* __restrict__ sel_count,
+                                                            int32_t* __restrict__ slot_pos,
+                                                            uint32_t* __restrict__ resident_bm,
+                                                            int32_t* __restrict__ load_pos,
+                                                            int32_t* __restrict__ load_slot,
+                                                            int32_t* __restrict__ load_count, int K, int bm_words) {
+  __shared__ int32_t sS[kPlanMaxBudget];   // the new selection, ascending
+  __shared__ int32_t sL[kPlanMaxBudget];   // positions to load, ascending
+  __shared__ int32_t sF[kPlanMaxBudget];   // freed slots, ascending
+  __shared__ uint32_t scan_smem[16];
+
+  const int inst = blockIdx.x;
+  const int tid = threadIdx.x;
+  int c = sel_count[inst];
+  c = c < 0 ? 0 : (c > K ? K : c);
+  const int32_t* S = sel_idx + (size_t)inst * K;
+  int32_t* sp = slot_pos + (size_t)inst * K;
+  uint32_t* bm = resident_bm + (size_t)inst * bm_words;
+
+  for (int i = tid; i < c; i += kPlanThreads) sS[i] = S[i];
+  __syncthreads();
+
+  // freed slots: empty, or holding a position that left the selection
+  const int Cx = (K + kPlanThreads - 1) / kPlanThreads;
+  const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
+  uint32_t fmask = 0u, nf_loc = 0u;
+  for (int x = x0; x < x1; ++x) {
+    const int32_t pos = sp[x];
+    const bool keep = pos >= 0 && sorted_contains(sS, c, pos);
+    if (!keep) { fmask |= 1u << (x - x0); ++nf_loc; }
+  }
+  // positions of S not resident
+  const int Ci = (c + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(tid * Ci, c), i1 = min(i0 + Ci, c);
+  uint32_t lmask = 0u, nl_loc = 0u;
+  const int32_t pos_end = bm_words * 32;     // positions outside [0, pos_end) are never loaded
+  for (int i = i0; i < i1; ++i) {
+    const int32_t j = sS[i];
+    if (j < 0 || j >= pos_end) continue;
+    const bool resident = (bm[j >> 5] >> (j & 31)) & 1u;
+    if (!resident) { lmask |= 1u << (i - i0); ++nl_loc; }
+  }
+  uint32_t nf, nl;
+  uint32_t fo = block_excl_scan(nf_loc, scan_smem, nf);
+  uint32_t lo = block_excl_scan(nl_loc, scan_smem, nl);
+  for (int x = x0; x < x1; ++x)
+    if (fmask >> (x - x0) & 1u) sF[fo++] = x;
+  for (int i = i0; i < i1; ++i)
+    if (lmask >> (i - i0) & 1u) sL[lo++] = sS[i];
+  __syncthreads();
+
+  // apply: the i-th position to load goes to the i-th freed slot; the rest empty
+  for (int i = tid; i < (int)nf; i += kPlanThreads) {
+    const int x = sF[i];
+    const int32_t old = sp[x];
+    if (old >= 0 && old < pos_end) atomicAnd(&bm[old >> 5], ~(1u << (old & 31)));
+    if (i < (int)nl) {
+      const int32_t pos = sL[i];
+      sp[x] = pos;
+      atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+    } else {
+      sp[x] = -1;
+    }
+  }
+  int32_t* lp = load_pos + (size_t)inst * K;
+  int32_t* ls = load_slot + (size_t)inst * K;
+  for (int i = tid; i < K; i += kPlanThreads) {
+    const bool v = i < (int)nl;
+    lp[i] = v ? sL[i] : -1;
+    ls[i] = v ? sF[i] : -1;
+  }
+  if (tid == 0) load_count[inst] = (int32_t)nl;
+}
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 8;
+constexpr int kCopyBlocks = 1024;
+
+struct ByteLayout {
+  int64_t b, layer, head, row, kv;
+};
+
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const int32_t* __restrict__ load_pos,
+                                                            const int32_t* __restrict__ load_slot,
+                                                            const int32_t* __restrict__ load_count,
+                                                            const char* __restrict__ host, ByteLayout hl,
+                                                            char* __restrict__ dev, ByteLayout dl, int n_inst,
+                                                            int n_groups, int K, int max_len, int layer_begin,
+                                                            int n_lay, int vk, int vrow) {
+  __shared__ uint32_t pre[kCopyMaxInstances + 1];
+  __shared__ uint32_t scan_smem[16];
+  // prefix sums of the load counts over instances
+  uint32_t carry = 0u;
+  for (int base = 0; base < n_inst; base += kCopyThreads) {
+    const int i = base + threadIdx.x;
+    uint32_t v = 0u;
+    if (i < n_inst) {
+      const int32_t cnt = load_count[i];
+      v = cnt < 0 ? 0u : (cnt > K ? (uint32_t)K : (uint32_t)cnt);
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(v, scan_smem, tot);
+    if (i < n_inst) pre[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) pre[n_inst] = carry;
+  __syncthreads();
+  const uint64_t total = carry;
+  const uint64_t nvec = total * (uint64_t)n_lay * (uint64_t)vrow;
+  const uint64_t stride = (uint64_t)gridDim.x * kCopyThreads;
+
+  for (uint64_t v0 = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x; v0 < nvec; v0 += stride * kCopyUnroll) {
+    Vec16 buf[kCopyUnroll];
+    char* dst[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t vid = v0 + (uint64_t)u * stride;
+      dst[u] = nullptr;
+      if (vid < nvec) {
+        const uint64_t item = vid / (uint64_t)vrow;
+        const int v = (int)(vid - item * (uint64_t)vrow);
+        const int lo_ = (int)(item / total);
+        const uint32_t e = (uint32_t)(item - (uint64_t)lo_ * total);
+        // instance holding entry e: last inst with pre[inst] <= e
+        int a = 0, z = n_inst;
+        while (z - a > 1) {
+          const int mid = (a + z) >> 1;
+          if (pre[mid] <= e) a = mid; else z = mid;
+        }
+        const int inst = a;
+        const int i = (int)(e - pre[inst]);
+        const int b = inst / n_groups, g = inst - (inst / n_groups) * n_groups;
+        const int layer = layer_begin + lo_;
+        const int32_t pos = load_pos[(size_t)inst * K + i];
+        const int32_t slot = load_slot[(size_t)inst * K + i];
+        if (pos < 0 || pos >= max_len || slot < 0 || slot >= K) continue;   // malformed entry: skipped
+        const int64_t off_h = v < vk ? (int64_t)v * 16 : hl.kv + (int64_t)(v - vk) * 16;
+        const int64_t off_d = v < vk ? (int64_t)v * 16 : dl.kv + (int64_t)(v - vk) * 16;
+        const char* src = host + b * hl.b + layer * hl.layer + g * hl.head + (int64_t)pos * hl.row + off_h;
+        dst[u] = dev + b * dl.b + layer * dl.layer + g * dl.head + (int64_t)slot * dl.row + off_d;
+        buf[u] = ld16(src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (dst[u]) st16(dst[u], buf[u]);
+  }
+}
+
+__global__ void reset_kernel(int32_t* __restrict__ slot_pos, uint32_t* __restrict__ bm, int64_t n_slot,
+                             int64_t n_words) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slot; i += stride) slot_pos[i] = -1;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride) bm[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
+                       uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                       hipStream_t st) {
+  const int bm_words = (s.max_len + 31) / 32;
+  plan_kernel<<<dim3(s.batch * s.n_groups), kPlanThreads, 0, st>>>(sel_idx, sel_count, slot_pos, resident_bm,
+                                                                   load_pos, load_slot, load_count, s.budget,
+                                                                   bm_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const spc_shape& s, const int32_t* load_pos, const int32_t* load_slot,
+                       const int32_t* load_count, const void* host_dev_ptr, const spc_kv_layout& hl, void* dev_kv,
+                       const spc_kv_layout& dl, int layer_begin, int layer_end, hipStream_t st) {
+  const int eb = s.dtype == SPC_BF16 ? 2 : 4;
+  const int vk = s.head_dim * eb / 16;
+  const int vrow = vk + s.v_dim * eb / 16;
+  const ByteLayout hb{hl.s_b * eb, hl.s_layer * eb, hl.s_head * eb, hl.s_row * eb, hl.s_kv * eb};
+  const ByteLayout db{dl.s_b * eb, dl.s_layer * eb, dl.s_head * eb, dl.s_row * eb, dl.s_kv * eb};
+  copy_kernel<<<dim3(kCopyBlocks), kCopyThreads, 0, st>>>(
+      load_pos, load_slot, load_count, static_cast<const char*>(host_dev_ptr), hb, static_cast<char*>(dev_kv), db,
+      s.batch * s.n_groups, s.n_groups, s.budget, s.max_len, layer_begin, layer_end - layer_begin, vk, vrow);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(const spc_shape& s, int batch_begin, int batch_end, int32_t* slot_pos,
+                        uint32_t* resident_bm, hipStream_t st) {
+  const int64_t bm_words = (s.max_len + 31) / 32;
+  const int64_t per_b_slots = (int64_t)s.n_groups * s.budget;
+  const int64_t per_b_words = (int64_t)s.n_groups * bm_words;
+  const int64_t nb = batch_end - batch_begin;
+  reset_kernel<<<dim3(256), 256, 0, st>>>(slot_pos + batch_begin * per_b_slots,
+                                          resident_bm + batch_begin * per_b_words, nb * per_b_slots,
+                                          nb * per_b_words);
+  return hipGetLastError();
+}
+
+}  // namespace spc

@@ -1,0 +1,47 @@
+// Internal launchers of libspc: validated arguments in, kernels enqueued on a stream.
+// Each returns hipSuccess or the launch error; the C-ABI layer (spc_api.cpp)
+// validates every argument before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spc.h"
+
+namespace spc {
+
+// ---- stage 1: scores
+constexpr int kScoreTile = 256;        // positions per workgroup of the logits kernel
+constexpr int kNormChunk = 2048;       // positions per workgroup of the normalize kernel
+size_t scores_ws_bytes(const spc_shape& s);
+bool scores_supported(const spc_shape& s);
+hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* probs,
+                         void* ws, hipStream_t st);
+
+// ---- stage 2: group max + Top-K
+constexpr int kTopkLdsKeys = 32768;    // lengths up to this keep their keys in LDS
+hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
+                       int32_t* sel_count, hipStream_t st);
+
+// ---- stage 3: elastic plan / copy / reset
+constexpr int kPlanMaxBudget = 8192;
+constexpr int kCopyMaxInstances = 4096;
+hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
+                       uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                       hipStream_t st);
+hipError_t launch_copy(const spc_shape& s, const int32_t* load_pos, const int32_t* load_slot,
+                       const int32_t* load_count, const void* host_dev_ptr, const spc_kv_layout& hl, void* dev_kv,
+                       const spc_kv_layout& dl, int layer_begin, int layer_end, hipStream_t st);
+hipError_t launch_reset(const spc_shape& s, int batch_begin, int batch_end, int32_t* slot_pos,
+                        uint32_t* resident_bm, hipStream_t st);
+
+// ---- stage 4: sparse decode attention
+constexpr int kAttnRowsPerSplit = 128;
+size_t attn_ws_bytes(const spc_shape& s);
+bool attn_supported(const spc_shape& s);
+hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql, const void* kv,
+                       const spc_kv_layout& kl, const int32_t* rows, const int32_t* row_count, int mode,
+                       int layer_begin, int layer_end, float* out, void* ws, hipStream_t st);
+
+}  // namespace spc

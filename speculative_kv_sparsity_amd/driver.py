@@ -1,0 +1,108 @@
+"""One sparse-KV decode step ordered on HIP streams (host-side ordering only).
+
+SpeContext's dataflow (blog section 4; paper summary section 5.1): the
+retrieval head runs first on the step's input, its Top-K selection drives the
+elastic load of the missing K/V rows on a second stream, and the target
+model's attention consumes the resident sparse KV.  Here:
+
+  main stream : scores -> group max / Top-K -> plan --ev_plan-->
+  copy stream :                                  wait ev_plan -> copy(layer chunk c) -> ev_copy[c]
+  main stream :                                  wait ev_copy[c] -> attention(layer chunk c)
+
+so the copy of chunk c+1 overlaps the attention of chunk c.  The next step's
+scores are stream-ordered after this step's last attention (the next query
+depends on this step's output), and the next plan, which frees slots, is
+ordered after every attention that read them.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional
+
+import torch
+
+from . import api
+from .workload import Preset
+
+
+class SparseDecoder:
+    """Device buffers, state and streams of the sparse decode path for one workload.
+
+    dlm_k:   device [B][H_kv][L][d]  retrieval-head key cache
+    host_kv: pinned host [B][layers][H_kv][L][2][d]  full target K/V store
+    """
+
+    def __init__(self, p: Preset, dlm_k: torch.Tensor, host_kv: torch.Tensor, layer_chunks: int = 4,
+                 device: Optional[torch.device] = None):
+        assert p.kind in ("gqa", "mha", "mqa"), "MLA uses MlaDecoder"
+        self.p = p
+        dev = device or dlm_k.device
+        self.device = dev
+        B, Hq, Hkv, G, d, L, K = p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.max_len, p.budget
+        self.shape = api.make_shape(B, Hq, Hkv, G, d, p.v_dim, L, K, p.n_layers, p.dtype, p.scale)
+        self.dlm_k = dlm_k
+        self.host_kv = host_kv
+        self.host_l = api.kv_layout(host_kv)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.probs = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.sel_idx = torch.empty((B, G, K), **i32)
+        self.sel_count = torch.empty((B, G), **i32)
+        self.slot_pos = torch.empty((B, G, K), **i32)
+        self.resident_bm = torch.empty((B, G, (L + 31) // 32), **i32)
+        self.load_pos = torch.empty((B, G, K), **i32)
+        self.load_slot = torch.empty((B, G, K), **i32)
+        self.load_count = torch.empty((B, G), **i32)
+        self.dev_kv = torch.zeros((B, p.n_layers, Hkv, K, 2, d), dtype=p.torch_dtype, device=dev)
+        self.dev_l = api.kv_layout(self.dev_kv)
+        self.out = torch.zeros((B, p.n_layers, Hq, p.v_dim), dtype=torch.float32, device=dev)
+        self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
+                                     dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
+                                   dtype=torch.uint8, device=dev)
+        self.q_l = api.q_layout(Hq * d, 0, d)   # the same query serves every layer
+        n = max(1, min(layer_chunks, p.n_layers))
+        step = math.ceil(p.n_layers / n)
+        self.chunks: List[tuple] = [(a, min(a + step, p.n_layers)) for a in range(0, p.n_layers, step)]
+        self.main = torch.cuda.current_stream(dev)
+        self.copy = torch.cuda.Stream(device=dev)
+        self.ev_plan = torch.cuda.Event()
+        self.ev_copy = [torch.cuda.Event() for _ in self.chunks]
+        self.reset()
+
+    def reset(self, batch_index: int = -1) -> None:
+        api.spc_elastic_reset(self.shape, batch_index, self.slot_pos, self.resident_bm, stream=self.main)
+
+    # --- the four stages --------------------------------------------------------------
+    def select(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
+        api.spc_retrieval_scores(self.shape, q, self.dlm_k, lengths, self.probs, ws=self.ws_scores, stream=self.main)
+        api.spc_group_max_topk(self.shape, self.probs, lengths, self.sel_idx, self.sel_count, stream=self.main)
+
+    def plan(self) -> None:
+        api.spc_elastic_update(self.shape, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm,
+                               self.load_pos, self.load_slot, self.load_count, flags=api.SPC_PLAN,
+                               plan_stream=self.main)
+
+    def copy_chunk(self, c: int) -> None:
+        a, z = self.chunks[c]
+        api.spc_elastic_update(self.shape, None, None, None, None, self.load_pos, self.load_slot, self.load_count,
+                               self.host_kv, self.host_l, self.dev_kv, self.dev_l, a, z, flags=api.SPC_COPY,
+                               plan_stream=self.copy, copy_stream=self.copy)
+
+    def attend_chunk(self, q: torch.Tensor, c: int) -> None:
+        a, z = self.chunks[c]
+        api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.dev_kv, self.dev_l, self.slot_pos, None,
+                                   api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn, stream=self.main)
+
+    # --- one step -----------------------------------------------------------------------
+    def step(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
+        """q: device [B][H_q][d]; lengths: device int32 [B].  Asynchronous."""
+        self.select(q, lengths)
+        self.plan()
+        self.ev_plan.record(self.main)
+        self.copy.wait_event(self.ev_plan)
+        for c in range(len(self.chunks)):
+            self.copy_chunk(c)
+            self.ev_copy[c].record(self.copy)
+        for c in range(len(self.chunks)):
+            self.main.wait_event(self.ev_copy[c])
+            self.attend_chunk(q, c)

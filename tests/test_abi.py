@@ -1,0 +1,90 @@
+"""The C-ABI library loads and exports every symbol include/spc.h declares;
+host-side validation rejects bad arguments before anything is launched (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_kv_sparsity_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "spc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_stage_calls():
+    names = _declared()
+    for n in ("spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_sparse_decode_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_strings():
+    lib = L.lib()
+    assert lib.spc_abi_version() == 1
+    assert lib.spc_status_string(0) == b"ok"
+    assert b"workspace" in lib.spc_status_string(L.SPC_ERR_WORKSPACE)
+
+
+def _shape(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, n_groups=8, head_dim=128, v_dim=128, max_len=4096,
+                budget=256, n_layers=1, dtype=L.SPC_BF16, scale=128 ** -0.5)
+    base.update(kw)
+    return L.SpcShape(**base)
+
+
+@pytest.mark.parametrize("bad", [dict(n_q_heads=30), dict(n_groups=3), dict(budget=0), dict(budget=5000),
+                                 dict(batch=0), dict(scale=0.0), dict(dtype=7), dict(n_groups=4)])
+def test_invalid_shapes_are_rejected_before_launch(bad):
+    lib = L.lib()
+    s = _shape(**bad)
+    dummy = ctypes.c_void_p(16)
+    st = lib.spc_retrieval_scores(ctypes.byref(s), dummy, dummy, dummy, dummy, dummy, 1 << 30, None)
+    assert st in (L.SPC_ERR_INVALID_ARG, L.SPC_ERR_UNSUPPORTED)
+    assert lib.spc_last_error()
+
+
+def test_null_pointers_and_small_workspace_rejected():
+    lib = L.lib()
+    s = _shape()
+    p = ctypes.c_void_p(256)
+    assert lib.spc_retrieval_scores(ctypes.byref(s), None, p, p, p, p, 1 << 30, None) == L.SPC_ERR_INVALID_ARG
+    need = lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(s))
+    assert need > 0
+    assert lib.spc_retrieval_scores(ctypes.byref(s), p, p, p, p, p, need - 1, None) == L.SPC_ERR_WORKSPACE
+    assert b"workspace" in lib.spc_last_error()
+    unaligned = ctypes.c_void_p(258)
+    assert lib.spc_retrieval_scores(ctypes.byref(s), unaligned, p, p, p, p, need, None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_group_max_topk(ctypes.byref(s), None, p, p, p, None, 0, None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_elastic_update(ctypes.byref(s), p, p, p, p, p, p, p, None, None, None, None, 0, 1, 0,
+                                  None, None) == L.SPC_ERR_INVALID_ARG            # no flags
+    assert lib.spc_elastic_reset(ctypes.byref(s), 3, p, p, None) == L.SPC_ERR_INVALID_ARG   # batch index
+    ql = L.SpcQLayout(32 * 128, 0, 128)
+    kl = L.SpcKvLayout(0, 0, 0, 256, 128)
+    assert lib.spc_sparse_decode_attn(ctypes.byref(s), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                      L.SPC_ROWS_GATHER, 0, 1, p, p, 1 << 30, None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_sparse_decode_attn(ctypes.byref(s), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                      L.SPC_ROWS_SLOTS, 0, 2, p, p, 1 << 30, None) == L.SPC_ERR_INVALID_ARG
+    s2 = _shape(head_dim=96, v_dim=96)
+    assert lib.spc_sparse_decode_attn(ctypes.byref(s2), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                      L.SPC_ROWS_SLOTS, 0, 1, p, p, 1 << 30, None) == L.SPC_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes():
+    lib = L.lib()
+    s = _shape(batch=2, max_len=32768, budget=2048, n_layers=32)
+    assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(s)) == 2 * 32 * 128 * 8
+    # one (max, sum) pair and one v_dim vector per head, layer and split of 128 rows
+    assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s)) == 2 * 32 * 32 * 16 * (128 * 4 + 8)
+    assert lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s)) == 0

@@ -1,0 +1,322 @@
+"""Stage-by-stage parity of the HIP path against the CPU oracle (through the C-ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spc_oracle as O
+from speculative_kv_sparsity_amd import api
+from speculative_kv_sparsity_amd import workload as W
+from tests.gpu_util import (ATTN_DERIVED, ATTN_MAX_ABS, PROBS_RTOL, check_topk_tolerance, dev_lengths, f64, raw,
+                            sel_lists, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+GQA_SMALL = W.Preset("gqa_small", "gqa", batch=2, n_layers=4, n_q_heads=8, n_kv_heads=2, head_dim=128, v_dim=128,
+                     dtype="bf16", max_len=1000, budget=96, steps=4)
+
+
+def _scores(p, w, lengths):
+    shape = shape_of(p)
+    probs = torch.full((p.batch, p.n_q_heads, p.max_len), float("nan"), device="cuda")
+    api.spc_retrieval_scores(shape, w.q[0].contiguous(), w.dlm_k, dev_lengths(lengths), probs)
+    torch.cuda.synchronize()
+    return shape, probs
+
+
+SCORE_CASES = [
+    ("tiny_f32", W.PRESETS["tiny"], None),
+    ("gqa_ragged", GQA_SMALL, [1000, 517]),
+    ("gqa_edge_lengths", GQA_SMALL.with_(batch=4), [0, 1, 255, 1000]),
+    ("mha", GQA_SMALL.with_(kind="mha", n_q_heads=4, n_kv_heads=4, max_len=777), [777, 300]),
+    ("mqa", GQA_SMALL.with_(kind="mqa", n_q_heads=8, n_kv_heads=1, max_len=600), [600, 599]),
+    ("heads_per_kv_16", GQA_SMALL.with_(n_q_heads=32, n_kv_heads=2, max_len=513), [513, 257]),
+    ("d64", GQA_SMALL.with_(head_dim=64, v_dim=64, max_len=300), [300, 3]),
+]
+
+
+@pytest.mark.parametrize("name,p,lengths", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_scores_match_oracle(name, p, lengths):
+    w = W.generate(p, device="cuda", seed=11, steps=1)
+    lengths = list(w.lengths[0]) if lengths is None else lengths
+    _, probs = _scores(p, w, lengths)
+    ref = O.retrieval_scores(f64(w.q[0], p.dtype), f64(w.dlm_k, p.dtype), lengths, p.scale)
+    got = probs.cpu().numpy().astype(np.float64)
+    for b, n in enumerate(lengths):
+        if n == 0:
+            continue
+        np.testing.assert_allclose(got[b, :, :n], ref[b, :, :n], rtol=PROBS_RTOL, atol=0)
+        assert np.all(np.isnan(got[b, :, n:]))          # positions past the length are not written
+
+
+def _topk_gpu(shape, probs, lengths):
+    B, G, K = shape.batch, shape.n_groups, shape.budget
+    sel_idx = torch.full((B, G, K), -7, dtype=torch.int32, device="cuda")
+    sel_count = torch.full((B, G), -7, dtype=torch.int32, device="cuda")
+    api.spc_group_max_topk(shape, probs, dev_lengths(lengths), sel_idx, sel_count)
+    torch.cuda.synchronize()
+    return sel_idx, sel_count
+
+
+def _oracle_topk(probs_f64, lengths, n_groups, K):
+    return O.select_all(O.group_scores(probs_f64, n_groups), lengths, K)
+
+
+def _assert_sel_equal(sel_idx, sel_count, ref, K):
+    si, sc = sel_idx.cpu().numpy(), sel_count.cpu().numpy()
+    for b in range(len(ref)):
+        for g in range(len(ref[b])):
+            r = ref[b][g]
+            assert sc[b, g] == len(r), (b, g)
+            np.testing.assert_array_equal(si[b, g, :len(r)], r)
+            assert np.all(si[b, g, len(r):] == -1)
+
+
+@pytest.mark.parametrize("name,p,lengths", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_topk_exact_on_gpu_scores_and_tolerant_vs_oracle_chain(name, p, lengths):
+    w = W.generate(p, device="cuda", seed=12, steps=1)
+    lengths = list(w.lengths[0]) if lengths is None else lengths
+    shape, probs = _scores(p, w, lengths)
+    sel_idx, sel_count = _topk_gpu(shape, probs, lengths)
+    # bit-exact against the oracle's Top-K run on the GPU's own float32 scores
+    gp = np.nan_to_num(probs.cpu().numpy().astype(np.float64), nan=0.0)
+    _assert_sel_equal(sel_idx, sel_count, _oracle_topk(gp, lengths, p.n_groups, p.budget), p.budget)
+    # against the fp64 oracle chain: only near-ties may differ
+    ref_probs = O.retrieval_scores(f64(w.q[0], p.dtype), f64(w.dlm_k, p.dtype), lengths, p.scale)
+    ref_grp = O.group_scores(ref_probs, p.n_groups)
+    ref_sel = O.select_all(ref_grp, lengths, p.budget)
+    check_topk_tolerance(sel_lists(sel_idx, sel_count), ref_sel, ref_grp, p.budget)
+
+
+TIE_CASES = [
+    # (B, Hq, G, L, K, lengths, value pool or None)
+    (2, 8, 2, 5000, 300, [5000, 4097], [0.0, 0.25, 0.5]),          # heavy ties across radix passes
+    (1, 4, 4, 3000, 64, [3000], [0.125]),                           # all equal: lowest indices
+    (3, 2, 1, 2000, 100, [100, 101, 0], None),                      # n = K, n = K + 1, n = 0
+    (1, 2, 2, 40000, 2048, [40000], None),                          # keys streamed from global memory
+    (1, 2, 2, 70000, 4096, [65537], [0.0, 1e-30, 2.0 ** -126, 1.0]), # streaming + ties + subnormal-ish
+    (2, 4, 4, 1500, 1, [1500, 7], None),                            # K = 1
+    (1, 6, 2, 33000, 5000, [33000], [-1.0, -0.5, 0.0, 0.5]),        # negative scores, heads 3 per group
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=[f"tie{i}" for i in range(len(TIE_CASES))])
+def test_topk_exact_with_ties_and_edges(case):
+    B, Hq, G, L, K, lengths, pool = case
+    rng = np.random.default_rng(99)
+    if pool is None:
+        vals = rng.random((B, Hq, L)).astype(np.float32)
+    else:
+        vals = rng.choice(np.asarray(pool, dtype=np.float32), size=(B, Hq, L))
+    shape = api.make_shape(B, Hq, G, G, 128, 128, L, K, 1, "bf16", 1.0)
+    probs = torch.from_numpy(vals).cuda()
+    sel_idx, sel_count = _topk_gpu(shape, probs, lengths)
+    ref = _oracle_topk(vals.astype(np.float64), lengths, G, K)
+    _assert_sel_equal(sel_idx, sel_count, ref, K)
+
+
+# ------------------------------------------------------------------------------ plan
+
+
+def _random_selection_sequence(rng, B, G, L, K, steps):
+    seqs = []
+    prev = [[set() for _ in range(G)] for _ in range(B)]
+    for t in range(steps):
+        step = []
+        for b in range(B):
+            row = []
+            n = int(rng.choice([0, 1, K - 1, K, L // 2, L])) if t % 5 == 4 else L
+            for g in range(G):
+                m = min(K, n)
+                keep = [x for x in prev[b][g] if x < n and rng.random() < 0.8][:m]
+                pool = np.setdiff1d(np.arange(n), np.asarray(keep, dtype=np.int64))
+                extra = rng.choice(pool, size=m - len(keep), replace=False) if m > len(keep) else []
+                s = np.sort(np.asarray(list(keep) + list(extra), dtype=np.int64))
+                row.append(s)
+                prev[b][g] = set(s.tolist())
+            step.append(row)
+        seqs.append(step)
+    return seqs
+
+
+@pytest.mark.parametrize("B,G,L,K", [(2, 3, 5000, 300), (1, 8, 32768, 2048), (1, 1, 9000, 8192), (3, 2, 50, 1)])
+def test_plan_bit_exact_over_steps(B, G, L, K):
+    rng = np.random.default_rng(B * 1000 + K)
+    shape = api.make_shape(B, G, G, G, 128, 128, L, K, 1, "bf16", 1.0)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    slot_pos = torch.empty((B, G, K), **i32)
+    bm = torch.empty((B, G, (L + 31) // 32), **i32)
+    load_pos, load_slot = torch.empty((B, G, K), **i32), torch.empty((B, G, K), **i32)
+    load_count = torch.empty((B, G), **i32)
+    api.spc_elastic_reset(shape, -1, slot_pos, bm)
+    ref_slots = [[np.full(K, -1, dtype=np.int64) for _ in range(G)] for _ in range(B)]
+    for step in _random_selection_sequence(rng, B, G, L, K, 12):
+        si = np.full((B, G, K), -1, dtype=np.int32)
+        sc = np.zeros((B, G), dtype=np.int32)
+        for b in range(B):
+            for g in range(G):
+                si[b, g, :len(step[b][g])] = step[b][g]
+                sc[b, g] = len(step[b][g])
+        api.spc_elastic_update(shape, torch.from_numpy(si).cuda(), torch.from_numpy(sc).cuda(), slot_pos, bm,
+                               load_pos, load_slot, load_count, flags=api.SPC_PLAN)
+        torch.cuda.synchronize()
+        sp, lp, ls, lc = (t.cpu().numpy() for t in (slot_pos, load_pos, load_slot, load_count))
+        bmn = bm.cpu().numpy().view(np.uint32)
+        for b in range(B):
+            for g in range(G):
+                to_load, lslot, new = O.elastic_plan(step[b][g], ref_slots[b][g])
+                ref_slots[b][g] = new
+                assert lc[b, g] == len(to_load)
+                np.testing.assert_array_equal(lp[b, g, :len(to_load)], to_load)
+                np.testing.assert_array_equal(ls[b, g, :len(to_load)], lslot)
+                assert np.all(lp[b, g, len(to_load):] == -1) and np.all(ls[b, g, len(to_load):] == -1)
+                np.testing.assert_array_equal(sp[b, g], new)
+                bits = np.zeros(bmn.shape[-1] * 32, dtype=bool)
+                bits[new[new >= 0]] = True
+                np.testing.assert_array_equal(np.unpackbits(bmn[b, g].view(np.uint8), bitorder="little")
+                                              .astype(bool), bits)
+
+
+# ------------------------------------------------------------------------------ copy
+
+
+def _pinned_kv(rng, B, NL, H, L, d, dtype):
+    t = torch.empty((B, NL, H, L, 2, d), dtype=dtype, pin_memory=True)
+    if dtype == torch.bfloat16:
+        bits = rng.integers(-(2 ** 15), 2 ** 15, size=t.shape, dtype=np.int16)
+        t.view(torch.int16).copy_(torch.from_numpy(bits))
+    else:
+        t.copy_(torch.from_numpy(rng.standard_normal(t.shape).astype(np.float32)))
+    return t
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_copy_moves_exactly_the_loaded_rows(dtype):
+    rng = np.random.default_rng(5)
+    B, G, NL, L, K, d = 2, 3, 4, 700, 64, 128
+    dt = "bf16" if dtype == torch.bfloat16 else "f32"
+    shape = api.make_shape(B, G, G, G, d, d, L, K, NL, dt, 1.0)
+    host = _pinned_kv(rng, B, NL, G, L, d, dtype)
+    dev = torch.zeros((B, NL, G, K, 2, d), dtype=dtype, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    slot_pos, bm = torch.empty((B, G, K), **i32), torch.empty((B, G, (L + 31) // 32), **i32)
+    lp, ls, lc = torch.empty((B, G, K), **i32), torch.empty((B, G, K), **i32), torch.empty((B, G), **i32)
+    api.spc_elastic_reset(shape, -1, slot_pos, bm)
+    for step in _random_selection_sequence(rng, B, G, L, K, 6):
+        si = np.full((B, G, K), -1, dtype=np.int32); sc = np.zeros((B, G), dtype=np.int32)
+        for b in range(B):
+            for g in range(G):
+                si[b, g, :len(step[b][g])] = step[b][g]; sc[b, g] = len(step[b][g])
+        before = dev.clone()
+        api.spc_elastic_update(shape, torch.from_numpy(si).cuda(), torch.from_numpy(sc).cuda(), slot_pos, bm,
+                               lp, ls, lc, host, api.kv_layout(host), dev, api.kv_layout(dev), 1, 3,
+                               flags=api.SPC_PLAN | api.SPC_COPY)
+        torch.cuda.synchronize()
+        sp = slot_pos.cpu().numpy(); lpn, lsn, lcn = lp.cpu().numpy(), ls.cpu().numpy(), lc.cpu().numpy()
+        hraw, draw, braw = raw(host), raw(dev), raw(before)
+        # layers outside [1, 3) untouched
+        np.testing.assert_array_equal(draw[:, [0, 3]], braw[:, [0, 3]])
+        for b in range(B):
+            for g in range(G):
+                for layer in (1, 2):
+                    ref = braw[b, layer, g].copy()
+                    O.elastic_copy(hraw[b, layer, g], ref, lpn[b, g, :lcn[b, g]], lsn[b, g, :lcn[b, g]])
+                    np.testing.assert_array_equal(draw[b, layer, g], ref)
+        # copies of every step leave the slots of layers 1-2 holding exactly their positions
+        for b in range(B):
+            for g in range(G):
+                for x in np.nonzero(sp[b, g] >= 0)[0]:
+                    np.testing.assert_array_equal(draw[b, 1:3, g, x], hraw[b, 1:3, g, sp[b, g, x]])
+
+
+def test_copy_rejects_unpinned_host_memory():
+    B, G, NL, L, K, d = 1, 1, 1, 64, 8, 128
+    shape = api.make_shape(B, G, G, G, d, d, L, K, NL, "bf16", 1.0)
+    host = torch.zeros((B, NL, G, L, 2, d), dtype=torch.bfloat16)          # pageable
+    dev = torch.zeros((B, NL, G, K, 2, d), dtype=torch.bfloat16, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    lp, ls, lc = torch.full((B, G, K), -1, **i32), torch.full((B, G, K), -1, **i32), torch.zeros((B, G), **i32)
+    with pytest.raises(api.SpcError) as e:
+        api.spc_elastic_update(shape, None, None, None, None, lp, ls, lc, host, api.kv_layout(host), dev,
+                               api.kv_layout(dev), 0, 1, flags=api.SPC_COPY)
+    assert e.value.status == 4
+
+
+# ------------------------------------------------------------------------------ attention
+
+
+def _attn_case(p, lengths, mode, seed=21):
+    """Selections from the GPU scores + Top-K, K/V placed by plan + copy (SLOTS) or a full cache (GATHER)."""
+    w = W.generate(p, device="cuda", seed=seed, steps=1, pin_host=True)
+    shape, probs = _scores(p, w, lengths)
+    sel_idx, sel_count = _topk_gpu(shape, probs, lengths)
+    B, G, K, NL = p.batch, p.n_groups, p.budget, p.n_layers
+    out = torch.full((B, NL, p.n_q_heads, p.v_dim), float("nan"), device="cuda")
+    q = w.q[0].contiguous()
+    ql = api.q_layout(p.n_q_heads * p.head_dim, 0, p.head_dim)
+    if mode == api.SPC_ROWS_SLOTS:
+        i32 = dict(dtype=torch.int32, device="cuda")
+        slot_pos, bm = torch.empty((B, G, K), **i32), torch.empty((B, G, (p.max_len + 31) // 32), **i32)
+        lp, ls, lc = torch.empty((B, G, K), **i32), torch.empty((B, G, K), **i32), torch.empty((B, G), **i32)
+        dev = torch.zeros((B, NL, p.n_kv_heads, K, 2, p.head_dim), dtype=p.torch_dtype, device="cuda")
+        api.spc_elastic_reset(shape, -1, slot_pos, bm)
+        api.spc_elastic_update(shape, sel_idx, sel_count, slot_pos, bm, lp, ls, lc, w.host_kv,
+                               api.kv_layout(w.host_kv), dev, api.kv_layout(dev), 0, NL,
+                               flags=api.SPC_PLAN | api.SPC_COPY)
+        api.spc_sparse_decode_attn(shape, q, ql, dev, api.kv_layout(dev), slot_pos, None, mode, 0, NL, out)
+    else:
+        full = w.host_kv.cuda()
+        api.spc_sparse_decode_attn(shape, q, ql, full, api.kv_layout(full), sel_idx, sel_count, mode, 0, NL, out)
+    torch.cuda.synchronize()
+    return w, sel_lists(sel_idx, sel_count), out.cpu().numpy().astype(np.float64)
+
+
+def _oracle_out(p, w, sel):
+    from oracle import OracleDecoder
+    dec = OracleDecoder(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.budget, p.scale, p.dtype)
+    return dec.attend(raw(w.q[0]), raw(w.host_kv), sel, list(range(p.n_layers)))
+
+
+ATTN_CASES = [
+    ("gqa_slots", GQA_SMALL, [1000, 517], api.SPC_ROWS_SLOTS),
+    ("gqa_gather", GQA_SMALL, [1000, 517], api.SPC_ROWS_GATHER),
+    ("gqa_short_and_empty", GQA_SMALL.with_(batch=3), [40, 0, 96], api.SPC_ROWS_SLOTS),
+    ("tiny_f32_slots", W.PRESETS["tiny"].with_(n_layers=2), [4096], api.SPC_ROWS_SLOTS),
+    ("mha_slots", GQA_SMALL.with_(kind="mha", n_q_heads=4, n_kv_heads=4, max_len=777, budget=200), [777, 500],
+     api.SPC_ROWS_SLOTS),
+    ("mqa_gather", GQA_SMALL.with_(kind="mqa", n_q_heads=8, n_kv_heads=1, max_len=600), [600, 33],
+     api.SPC_ROWS_GATHER),
+    ("d64_slots", GQA_SMALL.with_(head_dim=64, v_dim=64, max_len=300), [300, 299], api.SPC_ROWS_SLOTS),
+    ("budget1", GQA_SMALL.with_(budget=1), [1000, 5], api.SPC_ROWS_SLOTS),
+    ("split_tail", GQA_SMALL.with_(budget=333, max_len=2000), [2000, 1999], api.SPC_ROWS_SLOTS),
+]
+
+
+@pytest.mark.parametrize("name,p,lengths,mode", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_matches_oracle(name, p, lengths, mode):
+    w, sel, got = _attn_case(p, lengths, mode)
+    ref = _oracle_out(p, w, sel)
+    err = np.max(np.abs(got - ref))
+    assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, err
+    for b, n in enumerate(lengths):
+        if n == 0:
+            assert np.all(got[b] == 0)
+
+
+def test_full_budget_reproduces_dense_attention():
+    """K = L (>= n): sparse attention equals dense attention over every position."""
+    p = GQA_SMALL.with_(max_len=512, budget=512, n_layers=2)
+    lengths = [512, 300]
+    w, sel, got = _attn_case(p, lengths, api.SPC_ROWS_SLOTS)
+    for b, n in enumerate(lengths):
+        assert all(len(s) == n for s in sel[b])
+    q = f64(w.q[0], p.dtype)
+    kv = f64(w.host_kv, p.dtype)
+    import torch.nn.functional as F
+    for b, n in enumerate(lengths):
+        for layer in range(p.n_layers):
+            K_ = torch.from_numpy(kv[b, layer, :, :n, 0]); V_ = torch.from_numpy(kv[b, layer, :, :n, 1])
+            ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], K_, V_, enable_gqa=True,
+                                                 scale=p.scale)[:, 0, :].numpy()
+            assert np.max(np.abs(got[b, layer] - ref)) <= ATTN_DERIVED
