@@ -1,0 +1,178 @@
+"""Benchmark of the sparse-KV decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 60] [--warmup 4] [--config b1_32k]
+
+A step is one pass of the whole path over one batch of synthetic input:
+retrieval scores -> group max / Top-K -> elastic plan -> elastic copy (side
+stream, per layer chunk) -> sparse decode attention (per layer chunk).  The
+default workload is the Llama3.1-8B-shaped 32K step (batch 1, 32 layers,
+32 q-heads / 8 KV heads, d=128, bf16, budget 2048, target K/V in pinned host
+memory).  Inputs are resident (HBM / pinned host) before timing starts.
+
+Prints one JSON line: steps/s from a clean timed pass (events only at its two
+ends), per-stage times from a second, instrumented pass (events around every
+stage call on its own stream), the rooflines of the attention, scoring and
+elastic-copy kernels, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+HOST_LINK_PEAK_GBS = 63.0      # PCIe Gen5 x16 per direction: 32 GT/s x 16 x 128/130 / 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--config", default="b1_32k")
+    ap.add_argument("--layer-chunks", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(p, w, t0, budget_s):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload."""
+    from oracle import OracleDecoder
+    from speculative_kv_sparsity_amd.workload import to_numpy_raw
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    dec = OracleDecoder(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.budget, p.scale, p.dtype)
+    k = to_numpy_raw(w.dlm_k)
+    kv = to_numpy_raw(w.host_kv)
+    layers = list(range(p.n_layers))
+    n, start = 0, time.perf_counter()
+    t = t0
+    while True:
+        dec.step(to_numpy_raw(w.q[t]), k, w.lengths[t], kv, layers)
+        n += 1
+        t = min(t + 1, w.steps - 1)
+        if time.perf_counter() - start >= budget_s:
+            break
+    el = time.perf_counter() - start
+    return {"value": n / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} consecutive decode steps of the same workload (all {p.n_layers} layers, "
+                      f"fp64 NumPy), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures the path on one GPU only; --gpus {args.gpus} is not supported "
+              "(the per-sequence / per-KV-head sharding across GPUs is described, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from speculative_kv_sparsity_amd import workload as W
+    from speculative_kv_sparsity_amd.driver import SparseDecoder, StageTimer
+
+    torch.cuda.set_device(0)
+    p = W.PRESETS[args.config]
+    K_, Wm = args.steps, args.warmup
+    total = Wm + 2 * K_
+    w = W.generate(p, device="cuda", seed=args.seed, steps=total, pin_host=True)
+    dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=args.layer_chunks)
+    lens = torch.as_tensor(w.lengths, device="cuda")
+    qs = w.q.contiguous()
+    torch.cuda.synchronize()
+
+    for t in range(Wm):                          # step 0 is the cold full-budget load
+        dec.step(qs[t], lens[t])
+    torch.cuda.synchronize()
+
+    # clean timed pass
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(dec.main)
+    for t in range(Wm, Wm + K_):
+        dec.step(qs[t], lens[t])
+    e1.record(dec.main)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / K_
+
+    # instrumented pass: per-stage event times and the rows actually moved
+    stage = {k: [] for k in ("scores", "topk", "plan", "copy", "attn")}
+    loaded_rows, sel_rows = [], []
+    nch = len(dec.chunks)
+    for t in range(Wm + K_, Wm + 2 * K_):
+        tm = StageTimer()
+        dec.step(qs[t], lens[t], timer=tm)
+        torch.cuda.synchronize()
+        stage["scores"].append(tm.ms("scores", "topk"))
+        stage["topk"].append(tm.ms("topk", "plan"))
+        stage["plan"].append(tm.ms("plan", "plan_end"))
+        for c in range(nch):
+            stage["copy"].append(tm.ms(f"copy{c}", f"copy{c}_end"))
+            stage["attn"].append(tm.ms(f"attn{c}", f"attn{c}_end"))
+        loaded_rows.append(int(dec.load_count.sum().item()))
+        sel_rows.append(int(dec.sel_count.sum().item()))
+    avg = {k: float(np.mean(v)) for k, v in stage.items()}
+
+    eb = p.elem_bytes
+    lay_per_chunk = [z - a for a, z in dec.chunks]
+    B, Hkv, Hq, d, K, L = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget, p.max_len
+    n_valid = float(np.mean(w.lengths[Wm + K_:Wm + 2 * K_].sum(axis=1)))
+    row = 2 * d * eb                                             # one K||V row
+    # algorithmic bytes per call (one launch of the stage)
+    attn_bytes = B * lay_per_chunk[0] * Hkv * K * row + B * lay_per_chunk[0] * Hq * d * 4   # K/V read + out write
+    score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4                                  # keys read + probs write
+    copy_bytes = float(np.mean(loaded_rows)) * lay_per_chunk[0] * row                        # host reads per chunk
+    full_reload = float(np.mean(sel_rows)) * p.n_layers * row
+
+    def roof(bound, nbytes, ms, peak, kernel, calls):
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "GB/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel": kernel,
+                "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 2), "launches_per_step": calls}
+
+    result = {
+        "metric": "sparse decode steps/s (score+TopK+elastic load+attn) and % HBM peak at 32K",
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{p.name}: Llama3.1-8B-shaped decode step" if p.name == "b1_32k" else p.name,
+                   "batch": B, "layers": p.n_layers, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "cached_tokens": L, "kv_budget": K, "layer_chunks": nch, "parallelism": "single GPU"},
+        "roofline": roof("hbm", attn_bytes, avg["attn"], HBM_PEAK_GBS,
+                         "attn_split_kernel + attn_combine_kernel (sparse decode attention)", nch),
+        "roofline_scores": roof("hbm", score_bytes, avg["scores"], HBM_PEAK_GBS,
+                                "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1),
+        "roofline_host_link": roof("host_link", copy_bytes, avg["copy"], HOST_LINK_PEAK_GBS,
+                                   "copy_kernel (elastic host->HBM gather)", nch),
+        "stage_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "elastic": {"rows_loaded_per_step": float(np.mean(loaded_rows)), "rows_selected_per_step": float(np.mean(sel_rows)),
+                    "transfer_fraction_vs_full_reload": round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
+                    "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * p.n_layers * row)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, w, Wm, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -139,6 +139,8 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
  *   probs      device [B][H_q][max_len] float32 (as written by stage 1)
  *   sel_idx    device [B][n_groups][budget] int32 out: S ascending, -1 after sel_count
  *   sel_count  device [B][n_groups] int32 out: min(K, n)
+ *   ws         scratch of spc_workspace_size(SPC_CALL_TOPK) bytes (the keys and
+ *              first-digit histograms of the radix select)
  * The selection is exact on the float32 values (no approximation).
  */
 int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,

@@ -12,13 +12,13 @@ from typing import Optional
 import torch
 
 from . import _lib as L
-from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_SCORES, SPC_COPY, SPC_F32, SPC_PLAN, SPC_ROWS_GATHER,
+from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_SCORES, SPC_CALL_TOPK, SPC_COPY, SPC_F32, SPC_PLAN, SPC_ROWS_GATHER,
                    SPC_ROWS_SLOTS, SpcKvLayout, SpcQLayout, SpcShape)
 
 __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version", "spc_workspace_size",
            "spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_elastic_reset",
            "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
-           "SPC_CALL_SCORES", "SPC_CALL_ATTN"]
+           "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN"]
 
 
 class SpcError(RuntimeError):
@@ -99,11 +99,12 @@ def spc_retrieval_scores(shape: SpcShape, q, k, lengths, probs, ws=None, stream=
                                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def spc_group_max_topk(shape: SpcShape, probs, lengths, sel_idx, sel_count, stream=None) -> None:
+def spc_group_max_topk(shape: SpcShape, probs, lengths, sel_idx, sel_count, ws=None, stream=None) -> None:
     for t, n in ((probs, "probs"), (lengths, "lengths"), (sel_idx, "sel_idx"), (sel_count, "sel_count")):
         _dev(t, n)
+    ws = _workspace(SPC_CALL_TOPK, shape, probs.device) if ws is None else ws
     _check(L.lib().spc_group_max_topk(ctypes.byref(shape), _ptr(probs), _ptr(lengths), _ptr(sel_idx),
-                                      _ptr(sel_count), None, 0, _stream(stream)))
+                                      _ptr(sel_count), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spc_elastic_update(shape: SpcShape, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,

@@ -84,6 +84,7 @@ size_t spc_workspace_size(int which_call, const spc_shape* s) {
   if (check_shape(s) != SPC_OK) return 0;
   switch (which_call) {
     case SPC_CALL_SCORES: return spc::scores_ws_bytes(*s);
+    case SPC_CALL_TOPK: return spc::topk_ws_bytes(*s);
     case SPC_CALL_ATTN: return spc::attn_ws_bytes(*s);
     default: return 0;
   }
@@ -107,14 +108,16 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
 
 int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
                        int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (int e = check_shape(s)) return e;
   if (!probs || !lengths || !sel_idx || !sel_count)
     return fail(SPC_ERR_INVALID_ARG, "NULL probs, lengths, sel_idx or sel_count");
   if (!aligned4(probs) || !aligned4(sel_idx) || !aligned4(sel_count) || !aligned4(lengths))
     return fail(SPC_ERR_INVALID_ARG, "misaligned int32/float buffer");
-  const hipError_t e = spc::launch_topk(*s, probs, lengths, sel_idx, sel_count, as_stream(stream));
+  const size_t need = spc::topk_ws_bytes(*s);
+  if (ws_bytes < need || !ws)
+    return fail(SPC_ERR_WORKSPACE, "group max / top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = spc::launch_topk(*s, probs, lengths, sel_idx, sel_count, ws, as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "group max / top-k launch");
 }
 
@@ -145,6 +148,11 @@ int spc_elastic_update(const spc_shape* s, const int32_t* sel_idx, const int32_t
       return fail(SPC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
                   s->n_layers);
     const int eb = elem_bytes(s);
+    const double vecs = (double)s->batch * s->n_groups * s->budget * (layer_end - layer_begin) *
+                        ((double)(s->head_dim + s->v_dim) * eb / 16.0);
+    if (vecs >= 4294967296.0)
+      return fail(SPC_ERR_UNSUPPORTED, "copy of %.0f 16-byte vectors exceeds one launch; split the layer range",
+                  vecs);
     if ((s->head_dim * eb) % 16 || (s->v_dim * eb) % 16)
       return fail(SPC_ERR_UNSUPPORTED, "K and V rows must be whole 16-byte vectors");
     const spc_kv_layout* ls[2] = {host_l, dev_l};
@@ -201,6 +209,8 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
   if (!spc::attn_supported(*s))
     return fail(SPC_ERR_UNSUPPORTED, "attention: head_dim %d / v_dim %d with dtype %d", s->head_dim, s->v_dim,
                 s->dtype);
+  if (s->head_dim == 576 && kv_l->s_kv != 0)
+    return fail(SPC_ERR_UNSUPPORTED, "head_dim 576 reads V from the latent row itself (s_kv must be 0)");
   const int eb = elem_bytes(s);
   if (!aligned16(q) || !aligned16(kv)) return fail(SPC_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
   if ((q_l->s_b * eb) % 16 || (q_l->s_layer * eb) % 16 || (q_l->s_head * eb) % 16)

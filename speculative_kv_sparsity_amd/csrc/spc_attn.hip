@@ -6,17 +6,22 @@
 // section 2).
 //
 // attn_split_kernel  split-K: one workgroup per (b, layer, group, head chunk,
-//   split of kAttnRowsPerSplit rows).  The GQC query heads of the chunk share
-//   every K/V row read.  Three phases:
-//     1. logits: 8 lanes per row (lane p holds the 16-byte chunks p, p+8, ...;
-//        one wave load covers 8 rows x 128 contiguous bytes), v_dot2 on packed
-//        bf16, DPP 8-lane sums; logits of the split go to LDS;
-//     2. per head max and exp in LDS (exact two-pass softmax of the split);
-//     3. V rows in the same lane layout; every lane accumulates its dims for
-//        all GQC heads; lanes holding the same dims are summed across the wave
-//        and the 4 waves through LDS.
+//   split of 64 or 128 rows).  The GQC query heads of the chunk share every
+//   K/V row read.  Every lane issues ALL of its K and V loads up front, so a
+//   workgroup has its whole tile in flight at once.
+//     K: 8 lanes per row (lane p holds the 16-byte chunks p, p+8, ...; one wave
+//        load covers 8 rows x 128 contiguous bytes); v_dot2_f32_bf16 on packed
+//        pairs and DPP 8-lane sums give every lane of the group the logits.
+//     softmax: each wave keeps its own max per head; the exp weights of its
+//        rows go to LDS.
+//     V: 32 lanes per row, each lane owning d/32 fixed output dims; the two
+//        wave halves take alternate rows, so one permlane swap finishes the
+//        wave's sums, and the four waves are merged through LDS with their
+//        max-rescaling.
 //   Writes the split's (max, sum) and unnormalised output per head.
-// attn_combine_kernel  merges the splits of a head with their log-sum-exp
+// attn_split_latent_kernel  the same for MLA latent rows, where V is the first
+//   v_dim elements of the K row (read once, used twice) and one head per group.
+// attn_combine_kernel  merges the splits of every head with their log-sum-exp
 //   weights into the float32 output.
 #include "spc_common.h"
 #include "spc_launch.h"
@@ -26,23 +31,64 @@ namespace spc {
 namespace {
 
 constexpr int kThreads = 256;                 // 4 waves
-constexpr int kRps = kAttnRowsPerSplit;
-constexpr int kIters = kRps / 32;             // 4 waves x 8 rows per iteration
 
 struct QL { int64_t b, layer, head; };        // byte strides
 struct KL { int64_t b, layer, head, row, kv; };
 
-template <int DT, int D, int DV, int GQC>
+// Loads of 4, 8 or 16 bytes for the V layout.
+template <int BYTES> struct VLoad;
+template <> struct VLoad<4> {
+  uint32_t w[1];
+  __device__ __forceinline__ void load(const char* p) { w[0] = *reinterpret_cast<const uint32_t*>(p); }
+};
+template <> struct VLoad<8> {
+  uint32_t w[2];
+  __device__ __forceinline__ void load(const char* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  }
+};
+template <> struct VLoad<16> {
+  uint32_t w[4];
+  __device__ __forceinline__ void load(const char* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+};
+
+template <int DT, int N>
+__device__ __forceinline__ void widen_words(const uint32_t* w, float* out) {
+  if (DT == SPC_BF16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) { out[2 * i] = bf_lo(w[i]); out[2 * i + 1] = bf_hi(w[i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = __uint_as_float(w[i]);
+  }
+}
+
+// Row ids of a split: -1 for an empty slot / invalid position / past the count.
+__device__ __forceinline__ int32_t split_row(const int32_t* rl, int idx, int cnt, int mode, int max_rows) {
+  if (idx >= cnt) return -1;
+  const int32_t v = rl[idx];
+  return mode == SPC_ROWS_SLOTS ? (v >= 0 ? idx : -1) : (v >= 0 && v < max_rows ? v : -1);
+}
+
+// NI: K iterations of 8 rows per wave (rows per wave = 8 NI).
+template <int DT, int D, int GQC, int NI>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
     int n_lay, int nsplit, int nhc, int max_rows, float scale, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
   constexpr int EB = DT == SPC_BF16 ? 2 : 4;
-  constexpr int EPC = ElemsPerChunk<DT>::value;
-  constexpr int CPLK = D * EB / 16 / 8;
-  constexpr int CPLV = DV * EB / 16 / 8;
-  static_assert(D * EB % 128 == 0 && DV * EB % 128 == 0, "rows must be whole 8 x 16-byte chunks");
+  constexpr int CPLK = D * EB / 16 / 8;              // K: 16-byte chunks per lane
+  constexpr int RPW = 8 * NI;                        // rows per wave
+  constexpr int RPS = 4 * RPW;                       // rows per split
+  constexpr int EPL = D / 32;                        // V: dims per lane
+  constexpr int VB = EPL * EB;                       // V: bytes per lane and row
+  constexpr int NV = RPW / 2;                        // V: rows per lane
+  static_assert(D * EB % 128 == 0 && D % 32 == 0, "row layout");
 
   const int split = blockIdx.x;
   const int hcix = blockIdx.z;
@@ -58,11 +104,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int p = lane & 7, rr = lane >> 3;
+  const int half = lane >> 5, vl = lane & 31;
 
-  __shared__ float sP[GQC][kRps];
-  __shared__ int32_t sRow[kRps];
-  __shared__ float sM[GQC], sL[GQC];
-  __shared__ float red[4][GQC][DV];
+  __shared__ int32_t sRow[RPS];
+  __shared__ float sW[4][RPW][GQC];
+  __shared__ float s_m[4][GQC], s_l[4][GQC];
+  __shared__ float red[4][GQC][D];
 
   const int32_t* rl = rows + ((size_t)b * n_groups + r) * K;
   int cnt = K;
@@ -70,17 +117,30 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     cnt = row_count[(size_t)b * n_groups + r];
     cnt = cnt < 0 ? 0 : (cnt > K ? K : cnt);
   }
-  const int i0 = split * kRps;
-  for (int i = tid; i < kRps; i += kThreads) {
-    const int idx = i0 + i;
-    int32_t row = -1;
-    if (idx < cnt) {
-      const int32_t v = rl[idx];
-      row = mode == SPC_ROWS_SLOTS ? (v >= 0 ? idx : -1) : (v >= 0 && v < max_rows ? v : -1);
-    }
-    sRow[i] = row;
-  }
+  const int i0 = split * RPS;
+  for (int i = tid; i < RPS; i += kThreads) sRow[i] = split_row(rl, i0 + i, cnt, mode, max_rows);
+  __syncthreads();
 
+  const char* kbase = kv + b * kl.b + layer * kl.layer + (int64_t)kvh * kl.head;
+  const int wrow = wid * RPW;                        // first row of this wave within the split
+  int32_t rowk[NI];
+  Vec16 kc[NI][CPLK];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    rowk[it] = sRow[wrow + it * 8 + rr];
+    if (rowk[it] >= 0) {
+      const char* kr = kbase + (int64_t)rowk[it] * kl.row;
+#pragma unroll
+      for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16(kr + (p + 8 * c) * 16);
+    }
+  }
+  int32_t rowv[NV];
+  VLoad<VB> vv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    rowv[i] = sRow[wrow + 2 * i + half];
+    if (rowv[i] >= 0) vv[i].load(kbase + (int64_t)rowv[i] * kl.row + kl.kv + vl * VB);
+  }
   Vec16 qv[GQC][CPLK];
 #pragma unroll
   for (int h = 0; h < GQC; ++h) {
@@ -88,139 +148,278 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 #pragma unroll
     for (int c = 0; c < CPLK; ++c) qv[h][c] = ld16(qh + (p + 8 * c) * 16);
   }
-  const char* kbase = kv + b * kl.b + layer * kl.layer + (int64_t)kvh * kl.head;
-  __syncthreads();
 
-  // phase 1: logits
+  // logits (every lane of an 8-lane group holds its row's logits for all heads)
+  float lg[NI][GQC];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int li = it * 32 + wid * 8 + rr;
-    const int32_t row = sRow[li];
-    float acc[GQC];
-#pragma unroll
-    for (int h = 0; h < GQC; ++h) acc[h] = 0.f;
-    if (row >= 0) {
-      Vec16 kc[CPLK];
-      const char* kr = kbase + (int64_t)row * kl.row;
-#pragma unroll
-      for (int c = 0; c < CPLK; ++c) kc[c] = ld16(kr + (p + 8 * c) * 16);
-#pragma unroll
-      for (int h = 0; h < GQC; ++h)
-#pragma unroll
-        for (int c = 0; c < CPLK; ++c) acc[h] = dot16<DT>(kc[c], qv[h][c], acc[h]);
-    }
+  for (int it = 0; it < NI; ++it) {
 #pragma unroll
     for (int h = 0; h < GQC; ++h) {
-      const float t = sum8(acc[h]);
-      if (p == h) sP[h][li] = row >= 0 ? t * scale : -INFINITY;
+      float a = 0.f;
+      if (rowk[it] >= 0) {
+#pragma unroll
+        for (int c = 0; c < CPLK; ++c) a = dot16<DT>(kc[it][c], qv[h][c], a);
+      }
+      a = sum8(a);
+      lg[it][h] = rowk[it] >= 0 ? a * scale : -INFINITY;
     }
   }
-  __syncthreads();
-
-  // phase 2: per-head max, exp, sum over the split
-  for (int h = wid; h < GQC; h += 4) {
+  // per-wave max, exp weights to LDS, per-wave sums
+  float mw[GQC], lw[GQC];
+#pragma unroll
+  for (int h = 0; h < GQC; ++h) {
     float m = -INFINITY;
-    for (int i = lane; i < kRps; i += 64) m = fmaxf(m, sP[h][i]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int i = lane; i < kRps; i += 64) {
-      const float x = sP[h][i];
-      const float e = x == -INFINITY ? 0.f : __expf(x - m);
-      sP[h][i] = e;
-      s += e;
+#pragma unroll
+    for (int it = 0; it < NI; ++it) m = fmaxf(m, lg[it][h]);
+    mw[h] = max_across_rows8(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const float e = lg[it][h] == -INFINITY ? 0.f : __expf(lg[it][h] - mw[h]);
+      lg[it][h] = e;
+      sum += e;
     }
-    s = wave_sum(s);
-    if (lane == 0) { sM[h] = m; sL[h] = s; }
+    lw[h] = sum_across_rows8(sum);
+  }
+  if (p == 0) {
+#pragma unroll
+    for (int it = 0; it < NI; ++it)
+#pragma unroll
+      for (int h = 0; h < GQC; ++h) sW[wid][it * 8 + rr][h] = lg[it][h];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GQC; ++h) { s_m[wid][h] = mw[h]; s_l[wid][h] = lw[h]; }
   }
   __syncthreads();
 
-  // phase 3: weighted sum of V rows
-  float acc[GQC][CPLV * EPC];
+  // weighted V rows: lane (half, vl) accumulates dims vl*EPL .. +EPL of rows 2i + half
+  float acc[GQC][EPL];
 #pragma unroll
   for (int h = 0; h < GQC; ++h)
 #pragma unroll
-    for (int e = 0; e < CPLV * EPC; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int li = it * 32 + wid * 8 + rr;
-    const int32_t row = sRow[li];
-    if (row >= 0) {
-      const char* vr = kbase + (int64_t)row * kl.row + kl.kv;
-      Vec16 vc[CPLV];
+  for (int i = 0; i < NV; ++i) {
+    if (rowv[i] >= 0) {
+      float x[EPL];
+      widen_words<DT, VB / 4>(vv[i].w, x);
 #pragma unroll
-      for (int c = 0; c < CPLV; ++c) vc[c] = ld16(vr + (p + 8 * c) * 16);
-      float w[GQC];
+      for (int h = 0; h < GQC; ++h) {
+        const float w = sW[wid][2 * i + half][h];
 #pragma unroll
-      for (int h = 0; h < GQC; ++h) w[h] = sP[h][li];
-#pragma unroll
-      for (int c = 0; c < CPLV; ++c) {
-        float x[EPC];
-        widen16<DT>(vc[c], x);
-#pragma unroll
-        for (int h = 0; h < GQC; ++h)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[h][c * EPC + e] = fmaf(w[h], x[e], acc[h][c * EPC + e]);
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w, x[e], acc[h][e]);
       }
     }
   }
+  // merge the halves, then the waves (rescaled to the workgroup max)
+  float fw[GQC];
+#pragma unroll
+  for (int h = 0; h < GQC; ++h) {
+    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    fw[h] = mw[h] == -INFINITY ? 0.f : __expf(mw[h] - M);
+  }
 #pragma unroll
   for (int h = 0; h < GQC; ++h)
 #pragma unroll
-    for (int e = 0; e < CPLV * EPC; ++e) acc[h][e] = sum_across_rows8(acc[h][e]);
-  if (rr == 0) {
+    for (int e = 0; e < EPL; ++e) acc[h][e] = add_xor32(acc[h][e]);
+  if (half == 0) {
 #pragma unroll
     for (int h = 0; h < GQC; ++h)
 #pragma unroll
-      for (int c = 0; c < CPLV; ++c)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) red[wid][h][(p + 8 * c) * EPC + e] = acc[h][c * EPC + e];
+      for (int e = 0; e < EPL; ++e) red[wid][h][vl * EPL + e] = acc[h][e] * fw[h];
   }
   __syncthreads();
   const size_t pbase = ((size_t)inst * nhc + hcix) * nsplit + split;
-  for (int t = tid; t < GQC * DV; t += kThreads) {
-    const int h = t / DV, d = t - (t / DV) * DV;
-    const float v = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
-    part_o[(pbase * GQC + h) * DV + d] = v;
+  for (int t = tid; t < GQC * D; t += kThreads) {
+    const int h = t / D, d = t - (t / D) * D;
+    part_o[(pbase * GQC + h) * D + d] = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
   }
-  if (tid < GQC) part_ml[pbase * GQC + tid] = make_float2(sM[tid], sL[tid]);
+  if (tid < GQC) {
+    const int h = tid;
+    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) L += s_m[w][h] == -INFINITY ? 0.f : s_l[w][h] * __expf(s_m[w][h] - M);
+    }
+    part_ml[pbase * GQC + h] = make_float2(M, L);
+  }
 }
 
-template <int GQC>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml,
-                                                           float* __restrict__ out, int DV, int Hq, int n_layers,
-                                                           int n_groups, int layer_begin, int n_lay, int nsplit,
-                                                           int nhc) {
-  const int inst = blockIdx.x;
-  const int hcix = blockIdx.y;
-  const int h = blockIdx.z;
+// MLA latent rows: V is the first DV elements of the K row; one head per group.
+template <int D, int DV, int NI>
+__global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
+    const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
+    int n_lay, int nsplit, int nhc, int max_rows, float scale, float* __restrict__ part_o,
+    float2* __restrict__ part_ml) {
+  constexpr int EB = 2, EPC = 8;
+  constexpr int CPLK = D * EB / 16 / 8;
+  constexpr int CPLV = DV * EB / 16 / 8;
+  constexpr int RPW = 8 * NI, RPS = 4 * RPW;
+  static_assert(CPLV <= CPLK && D * EB % 128 == 0 && DV * EB % 128 == 0, "latent row layout");
+
+  const int split = blockIdx.x;
+  const int inst = blockIdx.y;
   const int r = inst % n_groups;
   const int bl = inst / n_groups;
   const int lo = bl % n_lay;
   const int b = bl / n_lay;
-  const int GQ = Hq / n_groups;
-  const int head = r * GQ + hcix * GQC + h;
-  const size_t pb = ((size_t)inst * nhc + hcix) * nsplit;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float2 ml = part_ml[(pb + sp) * GQC + h];
-    if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  const int layer = layer_begin + lo;
+  const int kvh = r / (n_groups / Hkv);
+  const int head = r * (Hq / n_groups);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int p = lane & 7, rr = lane >> 3;
+
+  __shared__ int32_t sRow[RPS];
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float red[4][DV];
+
+  const int32_t* rl = rows + ((size_t)b * n_groups + r) * K;
+  int cnt = K;
+  if (mode == SPC_ROWS_GATHER) {
+    cnt = row_count[(size_t)b * n_groups + r];
+    cnt = cnt < 0 ? 0 : (cnt > K ? K : cnt);
   }
-  float L = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float2 ml = part_ml[(pb + sp) * GQC + h];
-    if (ml.y > 0.f) L += ml.y * __expf(ml.x - M);
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* o = out + (((size_t)b * n_layers + layer_begin + lo) * Hq + head) * DV;
-  for (int d = threadIdx.x; d < DV; d += blockDim.x) {
-    float acc = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float2 ml = part_ml[(pb + sp) * GQC + h];
-      if (ml.y > 0.f) acc += part_o[((pb + sp) * GQC + h) * DV + d] * __expf(ml.x - M);
+  const int i0 = split * RPS;
+  for (int i = tid; i < RPS; i += kThreads) sRow[i] = split_row(rl, i0 + i, cnt, mode, max_rows);
+  __syncthreads();
+  const char* kbase = kv + b * kl.b + layer * kl.layer + (int64_t)kvh * kl.head;
+  int32_t row[NI];
+  Vec16 kc[NI][CPLK];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    row[it] = sRow[wid * RPW + it * 8 + rr];
+    if (row[it] >= 0) {
+      const char* kr = kbase + (int64_t)row[it] * kl.row;
+#pragma unroll
+      for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16(kr + (p + 8 * c) * 16);
     }
-    o[d] = acc * inv;
   }
+  Vec16 qv[CPLK];
+  const char* qh = q + b * ql.b + layer * ql.layer + (int64_t)head * ql.head;
+#pragma unroll
+  for (int c = 0; c < CPLK; ++c) qv[c] = ld16(qh + (p + 8 * c) * 16);
+  float lg[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    float a = 0.f;
+    if (row[it] >= 0) {
+#pragma unroll
+      for (int c = 0; c < CPLK; ++c) a = dot16<SPC_BF16>(kc[it][c], qv[c], a);
+    }
+    a = sum8(a);
+    lg[it] = row[it] >= 0 ? a * scale : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) m = fmaxf(m, lg[it]);
+  const float mw = max_across_rows8(m);
+  float sum = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    lg[it] = lg[it] == -INFINITY ? 0.f : __expf(lg[it] - mw);
+    sum += lg[it];
+  }
+  const float lw = sum_across_rows8(sum);
+  float acc[CPLV * EPC];
+#pragma unroll
+  for (int e = 0; e < CPLV * EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    if (row[it] >= 0) {
+#pragma unroll
+      for (int c = 0; c < CPLV; ++c) {
+        float x[EPC];
+        widen16<SPC_BF16>(kc[it][c], x);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[c * EPC + e] = fmaf(lg[it], x[e], acc[c * EPC + e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < CPLV * EPC; ++e) acc[e] = sum_across_rows8(acc[e]);
+  if (lane == 0) { s_m[wid] = mw; s_l[wid] = lw; }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const float fw = mw == -INFINITY ? 0.f : __expf(mw - M);
+  if (rr == 0) {
+#pragma unroll
+    for (int c = 0; c < CPLV; ++c)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) red[wid][(p + 8 * c) * EPC + e] = acc[c * EPC + e] * fw;
+  }
+  __syncthreads();
+  const size_t pbase = (size_t)inst * nsplit + split;
+  for (int d = tid; d < DV; d += kThreads) part_o[pbase * DV + d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
+  if (tid == 0) {
+    float L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) L += s_m[w] == -INFINITY ? 0.f : s_l[w] * __expf(s_m[w] - M);
+    }
+    part_ml[pbase] = make_float2(M, L);
+  }
+}
+
+constexpr int kCombineChunk = 16;
+
+// One thread per (instance, head chunk, head, dim); the split partials are read
+// 16 at a time (all loads of a chunk issued together) and merged online.
+template <int GQC>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml,
+                                                           float* __restrict__ out, int DV, int Hq, int n_layers,
+                                                           int n_groups, int layer_begin, int n_lay, int nsplit,
+                                                           int nhc, int64_t n_out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_out) return;
+  const int d = (int)(t % DV);
+  const int64_t ih = t / DV;                 // ((inst * nhc + hcix) * GQC + h)
+  const int h = (int)(ih % GQC);
+  const int64_t ic = ih / GQC;               // inst * nhc + hcix
+  const int hcix = (int)(ic % nhc);
+  const int inst = (int)(ic / nhc);
+  const int r = inst % n_groups;
+  const int bl = inst / n_groups;
+  const int lo = bl % n_lay;
+  const int b = bl / n_lay;
+  const int head = r * (Hq / n_groups) + hcix * GQC + h;
+  const size_t pb = (size_t)ic * nsplit;
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineChunk) {
+    float2 ml[kCombineChunk];
+    float po[kCombineChunk];
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i) {
+      if (s0 + i < nsplit) {
+        ml[i] = part_ml[(pb + s0 + i) * GQC + h];
+        po[i] = part_o[((pb + s0 + i) * GQC + h) * DV + d];
+      } else {
+        ml[i] = make_float2(-INFINITY, 0.f);
+        po[i] = 0.f;
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i)
+      if (ml[i].y > 0.f) Mc = fmaxf(Mc, ml[i].x);
+    if (Mc == -INFINITY) continue;
+    const float rescale = M == -INFINITY ? 0.f : __expf(M - Mc);
+    L *= rescale;
+    acc *= rescale;
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i) {
+      if (ml[i].y > 0.f) {
+        const float w = __expf(ml[i].x - Mc);
+        L += ml[i].y * w;
+        acc += po[i] * w;
+      }
+    }
+    M = Mc;
+  }
+  out[(((size_t)b * n_layers + layer_begin + lo) * Hq + head) * DV + d] = L > 0.f ? acc / L : 0.f;
 }
 
 int head_chunk(const spc_shape& s) {
@@ -231,27 +430,30 @@ int head_chunk(const spc_shape& s) {
   return 1;
 }
 
-template <int DT, int D, int DV, int GQC>
-hipError_t launch_split(const spc_shape& s, dim3 grid, hipStream_t st, const char* q, QL ql, const char* kv, KL kl,
-                        const int32_t* rows, const int32_t* row_count, int mode, int layer_begin, int n_lay,
-                        int nsplit, int nhc, float* part_o, float2* part_ml) {
-  attn_split_kernel<DT, D, DV, GQC><<<grid, kThreads, 0, st>>>(q, ql, kv, kl, rows, row_count, mode, s.n_q_heads,
-                                                               s.n_kv_heads, s.n_groups, s.budget, layer_begin,
-                                                               n_lay, nsplit, nhc,
-                                                               mode == SPC_ROWS_SLOTS ? s.budget : s.max_len, s.scale,
-                                                               part_o, part_ml);
+// rows per split = 4 waves x 8 rows x NI of the instantiation launched below
+// (NI = 4, or 2 where registers are tight: 8 heads per workgroup, MLA rows)
+int rows_per_split(const spc_shape& s) { return (s.head_dim > 256 || head_chunk(s) >= 8) ? 64 : 128; }
+
+struct SplitArgs {
+  const char* q; QL ql; const char* kv; KL kl; const int32_t* rows; const int32_t* row_count; int mode;
+  int layer_begin, n_lay, nsplit, nhc, max_rows; float* part_o; float2* part_ml;
+};
+
+template <int DT, int D, int GQC, int NI>
+hipError_t launch_split(const spc_shape& s, dim3 grid, hipStream_t st, const SplitArgs& a) {
+  attn_split_kernel<DT, D, GQC, NI><<<grid, kThreads, 0, st>>>(
+      a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
+      a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
   return hipGetLastError();
 }
 
-template <int DT, int D, int DV>
-hipError_t launch_split_gqc(int gqc, const spc_shape& s, dim3 grid, hipStream_t st, const char* q, QL ql,
-                            const char* kv, KL kl, const int32_t* rows, const int32_t* row_count, int mode,
-                            int layer_begin, int n_lay, int nsplit, int nhc, float* part_o, float2* part_ml) {
+template <int DT, int D>
+hipError_t launch_split_gqc(int gqc, const spc_shape& s, dim3 grid, hipStream_t st, const SplitArgs& a) {
   switch (gqc) {
-    case 1: return launch_split<DT, D, DV, 1>(s, grid, st, q, ql, kv, kl, rows, row_count, mode, layer_begin, n_lay, nsplit, nhc, part_o, part_ml);
-    case 2: return launch_split<DT, D, DV, 2>(s, grid, st, q, ql, kv, kl, rows, row_count, mode, layer_begin, n_lay, nsplit, nhc, part_o, part_ml);
-    case 4: return launch_split<DT, D, DV, 4>(s, grid, st, q, ql, kv, kl, rows, row_count, mode, layer_begin, n_lay, nsplit, nhc, part_o, part_ml);
-    case 8: return launch_split<DT, D, DV, 8>(s, grid, st, q, ql, kv, kl, rows, row_count, mode, layer_begin, n_lay, nsplit, nhc, part_o, part_ml);
+    case 1: return launch_split<DT, D, 1, 4>(s, grid, st, a);
+    case 2: return launch_split<DT, D, 2, 4>(s, grid, st, a);
+    case 4: return launch_split<DT, D, 4, 4>(s, grid, st, a);
+    case 8: return launch_split<DT, D, 8, 2>(s, grid, st, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -260,12 +462,12 @@ hipError_t launch_split_gqc(int gqc, const spc_shape& s, dim3 grid, hipStream_t 
 
 bool attn_supported(const spc_shape& s) {
   if (s.dtype == SPC_F32) return s.head_dim == 128 && s.v_dim == 128;
-  return (s.head_dim == 128 && s.v_dim == 128) || (s.head_dim == 64 && s.v_dim == 64) ||
-         (s.head_dim == 576 && s.v_dim == 512);
+  if (s.head_dim == 576) return s.v_dim == 512 && head_chunk(s) == 1;   // MLA latent: one head per group
+  return (s.head_dim == 128 && s.v_dim == 128) || (s.head_dim == 64 && s.v_dim == 64);
 }
 
 size_t attn_ws_bytes(const spc_shape& s) {
-  const size_t nsplit = (size_t)(s.budget + kRps - 1) / kRps;
+  const size_t nsplit = (size_t)(s.budget + rows_per_split(s) - 1) / rows_per_split(s);
   const size_t heads = (size_t)s.batch * s.n_layers * s.n_q_heads;   // one partial per head per split
   return heads * nsplit * ((size_t)s.v_dim * sizeof(float) + sizeof(float2));
 }
@@ -275,38 +477,48 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
                        int layer_begin, int layer_end, float* out, void* ws, hipStream_t st) {
   const int eb = s.dtype == SPC_BF16 ? 2 : 4;
   const int n_lay = layer_end - layer_begin;
-  const int nsplit = (s.budget + kRps - 1) / kRps;
+  const int rps = rows_per_split(s);
+  const int nsplit = (s.budget + rps - 1) / rps;
   const int gqc = head_chunk(s);
   const int nhc = s.n_q_heads / s.n_groups / gqc;
-  const QL ql{qlay.s_b * eb, qlay.s_layer * eb, qlay.s_head * eb};
-  const KL kl{klay.s_b * eb, klay.s_layer * eb, klay.s_head * eb, klay.s_row * eb, klay.s_kv * eb};
   const size_t n_inst = (size_t)s.batch * n_lay * s.n_groups;
-  float* part_o = static_cast<float*>(ws);
-  float2* part_ml = reinterpret_cast<float2*>(part_o + n_inst * nhc * nsplit * gqc * s.v_dim);
+  SplitArgs a;
+  a.q = static_cast<const char*>(q);
+  a.ql = QL{qlay.s_b * eb, qlay.s_layer * eb, qlay.s_head * eb};
+  a.kv = static_cast<const char*>(kv);
+  a.kl = KL{klay.s_b * eb, klay.s_layer * eb, klay.s_head * eb, klay.s_row * eb, klay.s_kv * eb};
+  a.rows = rows;
+  a.row_count = row_count;
+  a.mode = mode;
+  a.layer_begin = layer_begin;
+  a.n_lay = n_lay;
+  a.nsplit = nsplit;
+  a.nhc = nhc;
+  a.max_rows = mode == SPC_ROWS_SLOTS ? s.budget : s.max_len;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float2*>(a.part_o + n_inst * nhc * nsplit * gqc * s.v_dim);
   const dim3 grid(nsplit, (unsigned)n_inst, nhc);
-  const char* qc = static_cast<const char*>(q);
-  const char* kc = static_cast<const char*>(kv);
   hipError_t e = hipErrorInvalidValue;
   if (s.dtype == SPC_F32) {
-    e = launch_split_gqc<SPC_F32, 128, 128>(gqc, s, grid, st, qc, ql, kc, kl, rows, row_count, mode, layer_begin,
-                                            n_lay, nsplit, nhc, part_o, part_ml);
+    e = launch_split_gqc<SPC_F32, 128>(gqc, s, grid, st, a);
   } else if (s.head_dim == 128) {
-    e = launch_split_gqc<SPC_BF16, 128, 128>(gqc, s, grid, st, qc, ql, kc, kl, rows, row_count, mode, layer_begin,
-                                             n_lay, nsplit, nhc, part_o, part_ml);
+    e = launch_split_gqc<SPC_BF16, 128>(gqc, s, grid, st, a);
   } else if (s.head_dim == 64) {
-    e = launch_split_gqc<SPC_BF16, 64, 64>(gqc, s, grid, st, qc, ql, kc, kl, rows, row_count, mode, layer_begin,
-                                           n_lay, nsplit, nhc, part_o, part_ml);
-  } else if (s.head_dim == 576) {
-    e = launch_split_gqc<SPC_BF16, 576, 512>(gqc, s, grid, st, qc, ql, kc, kl, rows, row_count, mode, layer_begin,
-                                             n_lay, nsplit, nhc, part_o, part_ml);
+    e = launch_split_gqc<SPC_BF16, 64>(gqc, s, grid, st, a);
+  } else if (s.head_dim == 576 && gqc == 1) {
+    attn_split_latent_kernel<576, 512, 2><<<grid, kThreads, 0, st>>>(
+        a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
+        a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
+    e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  const dim3 g2((unsigned)n_inst, nhc, gqc);
+  const int64_t n_out = (int64_t)n_inst * nhc * gqc * s.v_dim;
+  const dim3 g2((unsigned)((n_out + 255) / 256));
   switch (gqc) {
-#define SPC_CASE(N)                                                                                       \
-  case N:                                                                                                 \
-    attn_combine_kernel<N><<<g2, 128, 0, st>>>(part_o, part_ml, out, s.v_dim, s.n_q_heads, s.n_layers,   \
-                                               s.n_groups, layer_begin, n_lay, nsplit, nhc);              \
+#define SPC_CASE(N)                                                                                         \
+  case N:                                                                                                   \
+    attn_combine_kernel<N><<<g2, 256, 0, st>>>(a.part_o, a.part_ml, out, s.v_dim, s.n_q_heads, s.n_layers, \
+                                               s.n_groups, layer_begin, n_lay, nsplit, nhc, n_out);         \
     break;
     SPC_CASE(1)
     SPC_CASE(2)

@@ -126,11 +126,25 @@ __device__ __forceinline__ float max_across_rows8(float v) {
   return v;
 }
 
+constexpr int kDppRowRor8 = 0x128;      // lane i <- lane (i+8) mod 16 within each 16-lane row
+
+// Sum of a lane's value and its partner's across the 16-lane-row pairs (l ^ 16)
+// and the wave halves (l ^ 32), with gfx950's permlane swaps: each swap hands
+// every lane its partner's value in one of the two results.
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 __device__ __forceinline__ float sum_across_rows8(float v) {
-  v += __shfl_xor(v, 8, kWave);
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  v += dpp_f<kDppRowRor8>(v);
+  v = add_xor16(v);
+  return add_xor32(v);
 }
 
 // Inclusive scan of a uint32 over the wave.

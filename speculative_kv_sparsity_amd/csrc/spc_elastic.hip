@@ -16,6 +16,8 @@
 //   device-mapped host memory over the host link and writes them into the
 //   row's slot in HBM.  Consecutive lanes cover consecutive bytes of a row, so
 //   each wave reads whole rows; each lane keeps several reads in flight.
+#include <cstdlib>
+
 #include "spc_common.h"
 #include "spc_launch.h"
 
@@ -24,7 +26,6 @@ namespace spc {
 namespace {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kPerThreadMax = kPlanMaxBudget / kPlanThreads;   // contiguous slots / entries per thread
 
 __device__ __forceinline__ bool sorted_contains(const int32_t* a, int n, int32_t v) {
   int lo = 0, hi = n;
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   __shared__ int32_t sS[kPlanMaxBudget];   // the new selection, ascending
   __shared__ int32_t sL[kPlanMaxBudget];   // positions to load, ascending
   __shared__ int32_t sF[kPlanMaxBudget];   // freed slots, ascending
+  __shared__ int32_t sP[kPlanMaxBudget];   // slot map before the step
   __shared__ uint32_t scan_smem[16];
 
   const int inst = blockIdx.x;
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   uint32_t* bm = resident_bm + (size_t)inst * bm_words;
 
   for (int i = tid; i < c; i += kPlanThreads) sS[i] = S[i];
+  for (int x = tid; x < K; x += kPlanThreads) sP[x] = sp[x];
   __syncthreads();
 
   // freed slots: empty, or holding a position that left the selection
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
   uint32_t fmask = 0u, nf_loc = 0u;
   for (int x = x0; x < x1; ++x) {
-    const int32_t pos = sp[x];
+    const int32_t pos = sP[x];
     const bool keep = pos >= 0 && sorted_contains(sS, c, pos);
     if (!keep) { fmask |= 1u << (x - x0); ++nf_loc; }
   }
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   // apply: the i-th position to load goes to the i-th freed slot; the rest empty
   for (int i = tid; i < (int)nf; i += kPlanThreads) {
     const int x = sF[i];
-    const int32_t old = sp[x];
+    const int32_t old = sP[x];
     if (old >= 0 && old < pos_end) atomicAnd(&bm[old >> 5], ~(1u << (old & 31)));
     if (i < (int)nl) {
       const int32_t pos = sL[i];
@@ -112,7 +115,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 8;
-constexpr int kCopyBlocks = 1024;
 
 struct ByteLayout {
   int64_t b, layer, head, row, kv;
@@ -143,22 +145,23 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const int32_t* __res
   }
   if (threadIdx.x == 0) pre[n_inst] = carry;
   __syncthreads();
-  const uint64_t total = carry;
-  const uint64_t nvec = total * (uint64_t)n_lay * (uint64_t)vrow;
-  const uint64_t stride = (uint64_t)gridDim.x * kCopyThreads;
+  // 32-bit vector ids: the host checks n_inst * K * n_lay * vrow < 2^32
+  const uint32_t total = carry;
+  const uint32_t nvec = total * (uint32_t)n_lay * (uint32_t)vrow;
+  const uint32_t stride = gridDim.x * kCopyThreads;
 
-  for (uint64_t v0 = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x; v0 < nvec; v0 += stride * kCopyUnroll) {
+  for (uint32_t v0 = blockIdx.x * kCopyThreads + threadIdx.x; v0 < nvec; v0 += stride * kCopyUnroll) {
     Vec16 buf[kCopyUnroll];
     char* dst[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
-      const uint64_t vid = v0 + (uint64_t)u * stride;
+      const uint32_t vid = v0 + (uint32_t)u * stride;
       dst[u] = nullptr;
       if (vid < nvec) {
-        const uint64_t item = vid / (uint64_t)vrow;
-        const int v = (int)(vid - item * (uint64_t)vrow);
+        const uint32_t item = vid / (uint32_t)vrow;
+        const int v = (int)(vid - item * (uint32_t)vrow);
         const int lo_ = (int)(item / total);
-        const uint32_t e = (uint32_t)(item - (uint64_t)lo_ * total);
+        const uint32_t e = item - (uint32_t)lo_ * total;
         // instance holding entry e: last inst with pre[inst] <= e
         int a = 0, z = n_inst;
         while (z - a > 1) {
@@ -212,7 +215,12 @@ hipError_t launch_copy(const spc_shape& s, const int32_t* load_pos, const int32_
   const int vrow = vk + s.v_dim * eb / 16;
   const ByteLayout hb{hl.s_b * eb, hl.s_layer * eb, hl.s_head * eb, hl.s_row * eb, hl.s_kv * eb};
   const ByteLayout db{dl.s_b * eb, dl.s_layer * eb, dl.s_head * eb, dl.s_row * eb, dl.s_kv * eb};
-  copy_kernel<<<dim3(kCopyBlocks), kCopyThreads, 0, st>>>(
+  static const int blocks = [] {
+    const char* e = getenv("SPC_COPY_BLOCKS");
+    const int v = e ? atoi(e) : 0;
+    return v > 0 && v <= 65535 ? v : kCopyBlocksDefault;
+  }();
+  copy_kernel<<<dim3(blocks), kCopyThreads, 0, st>>>(
       load_pos, load_slot, load_count, static_cast<const char*>(host_dev_ptr), hb, static_cast<char*>(dev_kv), db,
       s.batch * s.n_groups, s.n_groups, s.budget, s.max_len, layer_begin, layer_end - layer_begin, vk, vrow);
   return hipGetLastError();

@@ -21,12 +21,15 @@ hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const
 
 // ---- stage 2: group max + Top-K
 constexpr int kTopkLdsKeys = 32768;    // lengths up to this keep their keys in LDS
+constexpr int kKeyChunk = 2048;        // positions per workgroup of the key / first-digit kernel
+size_t topk_ws_bytes(const spc_shape& s);
 hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
-                       int32_t* sel_count, hipStream_t st);
+                       int32_t* sel_count, void* ws, hipStream_t st);
 
 // ---- stage 3: elastic plan / copy / reset
 constexpr int kPlanMaxBudget = 8192;
 constexpr int kCopyMaxInstances = 4096;
+constexpr int kCopyBlocksDefault = 32;   // workgroups of the gather (override: SPC_COPY_BLOCKS)
 hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
                        uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
                        hipStream_t st);
@@ -37,7 +40,6 @@ hipError_t launch_reset(const spc_shape& s, int batch_begin, int batch_end, int3
                         uint32_t* resident_bm, hipStream_t st);
 
 // ---- stage 4: sparse decode attention
-constexpr int kAttnRowsPerSplit = 128;
 size_t attn_ws_bytes(const spc_shape& s);
 bool attn_supported(const spc_shape& s);
 hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql, const void* kv,

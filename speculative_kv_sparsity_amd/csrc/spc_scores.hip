@@ -167,7 +167,18 @@ __global__ __launch_bounds__(kThreads) void scores_normalize_kernel(float* __res
   const float inv = 1.f / s;
   float* pr = probs + (size_t)bh * max_len;
   const int j1 = min(j0 + kNormChunk, n);
-  for (int j = j0 + threadIdx.x; j < j1; j += kThreads) pr[j] = __expf(pr[j] - m) * inv;
+  constexpr int kPer = kNormChunk / kThreads;
+  float x[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = j0 + threadIdx.x + u * kThreads;
+    x[u] = j < j1 ? pr[j] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = j0 + threadIdx.x + u * kThreads;
+    if (j < j1) pr[j] = __expf(x[u] - m) * inv;
+  }
 }
 
 template <int DT, int D>

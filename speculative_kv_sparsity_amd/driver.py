@@ -57,6 +57,8 @@ class SparseDecoder:
         self.out = torch.zeros((B, p.n_layers, Hq, p.v_dim), dtype=torch.float32, device=dev)
         self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
                                      dtype=torch.uint8, device=dev)
+        self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
+                                   dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
                                    dtype=torch.uint8, device=dev)
         self.q_l = api.q_layout(Hq * d, 0, d)   # the same query serves every layer
@@ -73,9 +75,16 @@ class SparseDecoder:
         api.spc_elastic_reset(self.shape, batch_index, self.slot_pos, self.resident_bm, stream=self.main)
 
     # --- the four stages --------------------------------------------------------------
-    def select(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
+    def scores(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
         api.spc_retrieval_scores(self.shape, q, self.dlm_k, lengths, self.probs, ws=self.ws_scores, stream=self.main)
-        api.spc_group_max_topk(self.shape, self.probs, lengths, self.sel_idx, self.sel_count, stream=self.main)
+
+    def topk(self, lengths: torch.Tensor) -> None:
+        api.spc_group_max_topk(self.shape, self.probs, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk,
+                               stream=self.main)
+
+    def select(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
+        self.scores(q, lengths)
+        self.topk(lengths)
 
     def plan(self) -> None:
         api.spc_elastic_update(self.shape, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm,
@@ -94,15 +103,43 @@ class SparseDecoder:
                                    api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn, stream=self.main)
 
     # --- one step -----------------------------------------------------------------------
-    def step(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
-        """q: device [B][H_q][d]; lengths: device int32 [B].  Asynchronous."""
-        self.select(q, lengths)
+    def step(self, q: torch.Tensor, lengths: torch.Tensor, timer: Optional["StageTimer"] = None) -> None:
+        """q: device [B][H_q][d]; lengths: device int32 [B].  Asynchronous.
+
+        ``timer`` (optional) brackets every stage call with events on the
+        stream the stage runs on."""
+        mark = timer.mark if timer is not None else (lambda name, stream: None)
+        mark("scores", self.main)
+        self.scores(q, lengths)
+        mark("topk", self.main)
+        self.topk(lengths)
+        mark("plan", self.main)
         self.plan()
+        mark("plan_end", self.main)
         self.ev_plan.record(self.main)
         self.copy.wait_event(self.ev_plan)
         for c in range(len(self.chunks)):
+            mark(f"copy{c}", self.copy)
             self.copy_chunk(c)
+            mark(f"copy{c}_end", self.copy)
             self.ev_copy[c].record(self.copy)
         for c in range(len(self.chunks)):
             self.main.wait_event(self.ev_copy[c])
+            mark(f"attn{c}", self.main)
             self.attend_chunk(q, c)
+            mark(f"attn{c}_end", self.main)
+
+
+class StageTimer:
+    """Events recorded around each stage call of a step, on that stage's stream."""
+
+    def __init__(self):
+        self.events = {}
+
+    def mark(self, name: str, stream) -> None:
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        self.events[name] = ev
+
+    def ms(self, a: str, b: str) -> float:
+        return self.events[a].elapsed_time(self.events[b])
