@@ -147,14 +147,26 @@ __device__ __forceinline__ float sum_across_rows8(float v) {
   return add_xor32(v);
 }
 
-// Inclusive scan of a uint32 over the wave.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  // bound_ctrl off and old = 0: lanes without a source lane read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Inclusive scan of a uint32 over the wave: DPP row shifts scan each 16-lane
+// row, then the three lower row totals are broadcast with readlane.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  x += dpp_u<0x111>(x);   // row_shr:1
+  x += dpp_u<0x112>(x);   // row_shr:2
+  x += dpp_u<0x114>(x);   // row_shr:4
+  x += dpp_u<0x118>(x);   // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  if (lane >= 16) x += r0;
+  if (lane >= 32) x += r1;
+  if (lane >= 48) x += r2;
   return x;
 }
 
@@ -168,14 +180,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* smem, 
   const uint32_t incl = wave_incl_scan(v);
   if (lane == kWave - 1) smem[wid] = incl;
   __syncthreads();
-  if (wid == 0) {
-    uint32_t w = lane < nw ? smem[lane] : 0u;
-    w = wave_incl_scan(w);
-    if (lane < nw) smem[lane] = w;
+  uint32_t base = 0u, tot = 0u;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t t = smem[w];
+    base += w < wid ? t : 0u;
+    tot += t;
   }
-  __syncthreads();
-  const uint32_t base = wid ? smem[wid - 1] : 0u;
-  total = smem[nw - 1];
+  total = tot;
   __syncthreads();
   return base + incl - v;
 }

@@ -21,7 +21,7 @@ hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const
 
 // ---- stage 2: group max + Top-K
 constexpr int kTopkLdsKeys = 32768;    // lengths up to this keep their keys in LDS
-constexpr int kKeyChunk = 2048;        // positions per workgroup of the key / first-digit kernel
+constexpr int kKeyChunk = 1024;        // positions per workgroup of the key / first-digit kernel
 size_t topk_ws_bytes(const spc_shape& s);
 hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
                        int32_t* sel_count, void* ws, hipStream_t st);

@@ -31,9 +31,6 @@ namespace {
 constexpr int kKeyThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kBins1 = 256;                       // first digit: key bits 31..24
-constexpr int kPadded = kTopkLdsKeys + kTopkLdsKeys / 32;
-
-__device__ __forceinline__ int pidx(int j) { return j + (j >> 5); }
 
 // Order-preserving map from fp32 bits to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -115,6 +112,13 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int need,
   __syncthreads();
 }
 
+// LDS layout of staged keys: 4-key vector v lives in vector slot v ^ ((v >> 3) & 7),
+// so 16-byte reads are free of bank conflicts both when lanes take consecutive
+// vectors and when each lane walks its own contiguous run of 8 vectors.
+__device__ __forceinline__ int vslot(int v) { return v ^ ((v >> 3) & 7); }
+
+// Radix passes 2 and 3 plus the ordered compaction, shared by both key sources.
+// key_vec(v) returns keys 4v..4v+3 (entries >= n are ignored).
 template <bool IN_LDS>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t* __restrict__ keys,
                                                                   const uint32_t* __restrict__ chist,
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
                                                                   int32_t* __restrict__ sel_idx,
                                                                   int32_t* __restrict__ sel_count, int n_groups,
                                                                   int max_len, int budget, int nchunk) {
-  __shared__ uint32_t skeys[IN_LDS ? kPadded : 1];
+  __shared__ uint4 skeys[IN_LDS ? kTopkLdsKeys / 4 : 1];
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t scan_smem[16];
   __shared__ uint32_t bcast[2];
@@ -139,29 +143,37 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
     return;
   }
   const uint32_t* kin = keys + (size_t)inst * max_len;
+  const int nv = (n + 3) / 4;                          // key vectors (the last may be partial)
+  const bool aligned = (max_len % 4) == 0;             // rows of the key buffer start 16-byte aligned
   if (IN_LDS) {
-    // 16-byte loads, all of a thread's issued before its LDS stores (max_len % 4 == 0 keeps rows aligned)
     constexpr int kVecPerThread = kTopkLdsKeys / 4 / kSelThreads;
-    const int n4 = (max_len % 4 == 0) ? n / 4 : 0;
     uint4 v[kVecPerThread];
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
       const int i4 = tid + u * kSelThreads;
-      if (i4 < n4) v[u] = reinterpret_cast<const uint4*>(kin)[i4];
+      if (i4 < nv) {
+        if (aligned && 4 * i4 + 3 < n) {
+          v[u] = reinterpret_cast<const uint4*>(kin)[i4];
+        } else {
+          const int j = 4 * i4;
+          v[u] = make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u,
+                            j + 3 < n ? kin[j + 3] : 0u);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
       const int i4 = tid + u * kSelThreads;
-      if (i4 < n4) {
-        const int j = 4 * i4;
-        skeys[pidx(j)] = v[u].x;
-        skeys[pidx(j + 1)] = v[u].y;
-        skeys[pidx(j + 2)] = v[u].z;
-        skeys[pidx(j + 3)] = v[u].w;
-      }
+      if (i4 < nv) skeys[vslot(i4)] = v[u];
     }
-    for (int j = 4 * n4 + tid; j < n; j += kSelThreads) skeys[pidx(j)] = kin[j];
   }
+  auto key_vec = [&](int v) -> uint4 {
+    if (IN_LDS) return skeys[vslot(v)];
+    const int j = 4 * v;
+    if (aligned && j + 3 < n) return reinterpret_cast<const uint4*>(kin)[v];
+    return make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u, j + 3 < n ? kin[j + 3] : 0u);
+  };
+
   // first digit from the chunk histograms: thread t sums bin t % 256 over the
   // chunks c = t / 256 (mod 4), eight independent loads at a time
   const int nch = (n + kKeyChunk - 1) / kKeyChunk;
@@ -184,53 +196,263 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
     atomicAdd(&hist[bin], s);
   }
   __syncthreads();
-  auto key_at = [&](int j) -> uint32_t { return IN_LDS ? skeys[pidx(j)] : kin[j]; };
 
   int need = K;
   find_bin(hist, kBins1, need, scan_smem, bcast);
   uint32_t prefix = bcast[0] << 24;
   uint32_t pmask = 0xFF000000u;
   need -= (int)bcast[1];
+  bool whole = (int)hist[bcast[0]] == need;       // every key of the bin is taken: T is resolved
   __syncthreads();
 #pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 2 && !whole; ++pass) {
     const int shift = pass == 0 ? 12 : 0;
     for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
     __syncthreads();
-    for (int j = tid; j < n; j += kSelThreads) {
-      const uint32_t key = key_at(j);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 4095u], 1u);
+    for (int v = tid; v < nv; v += kSelThreads) {
+      const uint4 kv = key_vec(v);
+      const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * v + e < n && (k4[e] & pmask) == prefix) atomicAdd(&hist[(k4[e] >> shift) & 4095u], 1u);
     }
     __syncthreads();
     find_bin(hist, 4096, need, scan_smem, bcast);
     prefix |= bcast[0] << shift;
     pmask |= 4095u << shift;
     need -= (int)bcast[1];
+    whole = (int)hist[bcast[0]] == need;
     __syncthreads();
   }
-  const uint32_t T = prefix;   // the K-th largest key; `need` copies of it are taken
-
-  const int C = (n + kSelThreads - 1) / kSelThreads;
-  const int j0 = min(tid * C, n), j1 = min(j0 + C, n);
+  // Selected: masked key > prefix, plus the first `need` (in index order) with
+  // masked key == prefix.  When all 32 bits are resolved those keys are equal
+  // and the lower indices win; otherwise every one of them is taken.
+  // Thread t owns the contiguous vectors [t*C4, t*C4 + C4); flags are kept as
+  // bit masks of 32 keys so the keys are swept once.
+  const int C4 = (nv + kSelThreads - 1) / kSelThreads;
+  const int v0 = min(tid * C4, nv), v1 = min(v0 + C4, nv);
   uint32_t gt = 0u, eq = 0u;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = key_at(j);
-    gt += key > T;
-    eq += key == T;
-  }
+  int ee = 0, eq_before = 0, gt_before = 0, take_eq = 0;
   uint32_t tot;
-  const uint32_t eq_before = block_excl_scan(eq, scan_smem, tot);
-  const int take_eq = max(0, min((int)eq, need - (int)eq_before));
-  const uint32_t base = block_excl_scan(gt + (uint32_t)take_eq, scan_smem, tot);
-  int o = (int)base, e = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = key_at(j);
-    bool take = key > T;
-    if (key == T) {
-      take = e < take_eq;
-      ++e;
+  if (C4 <= 8) {
+    uint32_t gtm = 0u, eqm = 0u;
+    for (int v = v0; v < v1; ++v) {
+      const uint4 kv = key_vec(v);
+      const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bit = 4 * (v - v0) + e;
+        const uint32_t mk = k4[e] & pmask;
+        const bool valid = 4 * v + e < n;
+        gtm |= (uint32_t)(valid && mk > prefix) << bit;
+        eqm |= (uint32_t)(valid && mk == prefix) << bit;
+      }
     }
-    if (take && o < K) out[o++] = j;
+    gt = __popc(gtm);
+    eq = __popc(eqm);
+    if (n < 65536) {
+      const uint32_t before = block_excl_scan((eq << 16) | gt, scan_smem, tot);
+      eq_before = (int)(before >> 16);
+      gt_before = (int)(before & 0xFFFFu);
+    } else {
+      eq_before = (int)block_excl_scan(eq, scan_smem, tot);
+      gt_before = (int)block_excl_scan(gt, scan_smem, tot);
+    }
+    take_eq = max(0, min((int)eq, need - eq_before));
+    // drop the equal keys beyond take_eq, then write the set bits in index order
+    uint32_t keep_eq = eqm;
+    for (int drop = (int)eq - take_eq; drop > 0; --drop) keep_eq &= ~(0x80000000u >> __clz(keep_eq));
+    uint32_t m = gtm | keep_eq;
+    int o = gt_before + min(eq_before, need);
+    const int jbase = 4 * v0;
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      if (o < K) out[o++] = jbase + bit;
+    }
+  } else {
+    for (int v = v0; v < v1; ++v) {
+      const uint4 kv = key_vec(v);
+      const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t mk = k4[e] & pmask;
+        const bool valid = 4 * v + e < n;
+        gt += valid && mk > prefix;
+        eq += valid && mk == prefix;
+      }
+    }
+    eq_before = (int)block_excl_scan(eq, scan_smem, tot);
+    gt_before = (int)block_excl_scan(gt, scan_smem, tot);
+    take_eq = max(0, min((int)eq, need - eq_before));
+    int o = gt_before + min(eq_before, need);
+    for (int v = v0; v < v1; ++v) {
+      const uint4 kv = key_vec(v);
+      const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * v + e;
+        if (j >= n) continue;
+        const uint32_t mk = k4[e] & pmask;
+        bool take = mk > prefix;
+        if (mk == prefix) {
+          take = ee < take_eq;
+          ++ee;
+        }
+        if (take && o < K) out[o++] = j;
+      }
+    }
+  }
+  if (tid == 0) sel_count[inst] = K;
+}
+
+// Rows of at most 32768 keys (staged in LDS, 32 keys per thread): one sweep over
+// each thread's contiguous keys records, as bit masks, the keys whose first
+// digit is above the threshold digit (always selected) and those equal to it
+// (candidates), and histograms the candidates' second digit.  Every later step
+// touches only the candidates.
+__global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint32_t* __restrict__ keys,
+                                                                      const uint32_t* __restrict__ chist,
+                                                                      const int32_t* __restrict__ lengths,
+                                                                      int32_t* __restrict__ sel_idx,
+                                                                      int32_t* __restrict__ sel_count,
+                                                                      int n_groups, int max_len, int budget,
+                                                                      int nchunk) {
+  __shared__ uint4 skeys[kTopkLdsKeys / 4];
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t scan_smem[16];
+  __shared__ uint32_t bcast[2];
+  constexpr int kVecPerThread = kTopkLdsKeys / 4 / kSelThreads;   // 8 vectors = 32 keys
+
+  const int inst = blockIdx.x;
+  const int b = inst / n_groups;
+  const int n = clamp_len(lengths, b, max_len);
+  const int K = budget;
+  const int tid = threadIdx.x;
+  int32_t* out = sel_idx + (size_t)inst * K;
+  if (n <= K) {
+    for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
+    if (tid == 0) sel_count[inst] = n;
+    return;
+  }
+  const uint32_t* kin = keys + (size_t)inst * max_len;
+  const int nv = (n + 3) / 4;
+  const bool aligned = (max_len % 4) == 0;
+
+  // issue the key loads (strided, coalesced) and the chunk-histogram loads together
+  uint4 v[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int i4 = tid + u * kSelThreads;
+    if (i4 < nv) {
+      if (aligned && 4 * i4 + 3 < n) {
+        v[u] = reinterpret_cast<const uint4*>(kin)[i4];
+      } else {
+        const int j = 4 * i4;
+        v[u] = make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u,
+                          j + 3 < n ? kin[j + 3] : 0u);
+      }
+    }
+  }
+  const int nch = (n + kKeyChunk - 1) / kKeyChunk;
+  const int hbin = tid & (kBins1 - 1), c0 = tid >> 8;
+  uint32_t hs = 0u;
+  {
+    const uint32_t* ch = chist + (size_t)inst * nchunk * kBins1 + hbin;
+    for (int cb = c0; cb < nch; cb += 32) {
+      uint32_t hv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = cb + 4 * u;
+        hv[u] = c < nch ? ch[(size_t)c * kBins1] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hs += hv[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int i4 = tid + u * kSelThreads;
+    if (i4 < nv) skeys[vslot(i4)] = v[u];
+  }
+  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
+  __syncthreads();
+  atomicAdd(&hist[hbin], hs);
+  __syncthreads();
+
+  int need = K;
+  find_bin(hist, kBins1, need, scan_smem, bcast);
+  const uint32_t d1 = bcast[0];
+  need -= (int)bcast[1];
+  __syncthreads();
+  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
+  __syncthreads();
+
+  // one sweep over the thread's contiguous 32 keys
+  const int v0 = tid * kVecPerThread;
+  uint32_t gtm = 0u, cm = 0u;
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int vv = v0 + u;
+    if (vv < nv) {
+      const uint4 kv = skeys[vslot(vv)];
+      const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = 4 * vv + e < n;
+        const uint32_t top = k4[e] >> 24;
+        gtm |= (uint32_t)(valid && top > d1) << (4 * u + e);
+        if (valid && top == d1) {
+          cm |= 1u << (4 * u + e);
+          atomicAdd(&hist[(k4[e] >> 12) & 4095u], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  auto cand_key = [&](int bit) -> uint32_t {
+    const uint4 kv = skeys[vslot(v0 + (bit >> 2))];
+    const int e = bit & 3;
+    return e == 0 ? kv.x : (e == 1 ? kv.y : (e == 2 ? kv.z : kv.w));
+  };
+  find_bin(hist, 4096, need, scan_smem, bcast);
+  uint32_t prefix = (d1 << 24) | (bcast[0] << 12);
+  uint32_t pmask = 0xFFFFF000u;
+  need -= (int)bcast[1];
+  const bool whole = (int)hist[bcast[0]] == need;
+  __syncthreads();
+  if (!whole) {
+    for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t m = cm; m; m &= m - 1) {
+      const uint32_t key = cand_key(__ffs(m) - 1);
+      if ((key & pmask) == prefix) atomicAdd(&hist[key & 4095u], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, 4096, need, scan_smem, bcast);
+    prefix |= bcast[0];
+    pmask = 0xFFFFFFFFu;
+    need -= (int)bcast[1];
+    __syncthreads();
+  }
+  // resolve the candidates: masked key > prefix -> selected; == prefix -> tie at T
+  uint32_t eqm = 0u;
+  for (uint32_t m = cm; m; m &= m - 1) {
+    const int bit = __ffs(m) - 1;
+    const uint32_t mk = cand_key(bit) & pmask;
+    if (mk > prefix) gtm |= 1u << bit;
+    else if (mk == prefix) eqm |= 1u << bit;
+  }
+  const uint32_t gt = __popc(gtm), eq = __popc(eqm);
+  uint32_t tot;
+  const uint32_t before = block_excl_scan((eq << 16) | gt, scan_smem, tot);   // n <= 32768 < 2^16
+  const int eq_before = (int)(before >> 16), gt_before = (int)(before & 0xFFFFu);
+  const int take_eq = max(0, min((int)eq, need - eq_before));
+  uint32_t keep_eq = eqm;
+  for (int drop = (int)eq - take_eq; drop > 0; --drop) keep_eq &= ~(0x80000000u >> __clz(keep_eq));
+  int o = gt_before + min(eq_before, need);
+  for (uint32_t m = gtm | keep_eq; m; m &= m - 1) {
+    if (o < K) out[o++] = 4 * v0 + __ffs(m) - 1;
   }
   if (tid == 0) sel_count[inst] = K;
 }
@@ -254,8 +476,8 @@ hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* le
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (s.max_len <= kTopkLdsKeys)
-    topk_select_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(keys, chist, lengths, sel_idx, sel_count,
-                                                                 s.n_groups, s.max_len, s.budget, nchunk);
+    topk_select_lds_kernel<<<dim3(inst), kSelThreads, 0, st>>>(keys, chist, lengths, sel_idx, sel_count,
+                                                               s.n_groups, s.max_len, s.budget, nchunk);
   else
     topk_select_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(keys, chist, lengths, sel_idx, sel_count,
                                                                   s.n_groups, s.max_len, s.budget, nchunk);

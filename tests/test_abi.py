@@ -87,6 +87,6 @@ def test_workspace_sizes():
     assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(s)) == 2 * 32 * 128 * 8
     # one (max, sum) pair and one v_dim vector per head, layer and split of 128 rows
     assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s)) == 2 * 32 * 32 * 16 * (128 * 4 + 8)
-    # keys (one uint32 per position) + 256-bin histograms per 2048-position chunk
-    assert lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s)) == 2 * 8 * (32768 * 4 + 16 * 256 * 4)
+    # keys (one uint32 per position) + 256-bin histograms per 1024-position chunk
+    assert lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s)) == 2 * 8 * (32768 * 4 + 32 * 256 * 4)
     assert lib.spc_workspace_size(L.SPC_CALL_ELASTIC, ctypes.byref(s)) == 0

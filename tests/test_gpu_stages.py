@@ -320,3 +320,13 @@ def test_full_budget_reproduces_dense_attention():
             ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[:, None, :], K_, V_, enable_gqa=True,
                                                  scale=p.scale)[:, 0, :].numpy()
             assert np.max(np.abs(got[b, layer] - ref)) <= ATTN_DERIVED
+
+
+def test_topk_exact_long_rows_and_large_budget():
+    """Rows beyond 2^16 positions with a budget of 9000 (counts beyond 16 bits) and heavy ties."""
+    B, Hq, G, L, K = 1, 2, 1, 70000, 9000
+    rng = np.random.default_rng(7)
+    vals = rng.choice(np.asarray([0.0, 0.5, 0.75, 1.0], dtype=np.float32), size=(B, Hq, L), p=[0.6, 0.3, 0.05, 0.05])
+    shape = api.make_shape(B, Hq, G, G, 128, 128, L, K, 1, "bf16", 1.0)
+    sel_idx, sel_count = _topk_gpu(shape, torch.from_numpy(vals).cuda(), [L])
+    _assert_sel_equal(sel_idx, sel_count, _oracle_topk(vals.astype(np.float64), [L], G, K), K)
