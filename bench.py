@@ -10,9 +10,12 @@ default workload is the Llama3.1-8B-shaped 32K step (batch 1, 32 layers,
 memory).  Inputs are resident (HBM / pinned host) before timing starts.
 
 Prints one JSON line: steps/s from a clean timed pass (events only at its two
-ends), per-stage times from a second, instrumented pass (events around every
-stage call on its own stream), the rooflines of the attention, scoring and
-elastic-copy kernels, and the CPU oracle timed on a bounded sample.
+ends); per-stage times inside steps from a second, instrumented pass (events
+around every stage call on its own stream); per-call kernel times from a third,
+isolated phase (each stage call launched back to back, events only at the ends
+of the run, on the stream the call uses), which the rooflines of the attention,
+scoring and elastic-copy kernels use; and the CPU oracle timed on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -38,11 +41,40 @@ def parse():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--config", default="b1_32k")
-    ap.add_argument("--layer-chunks", type=int, default=4)
+    ap.add_argument("--layer-chunks", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--iso-reps", type=int, default=30, help="launches per stage in the isolated phase")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with three 256 MiB device-to-device copies (counter calibration)")
     return ap.parse_args()
+
+
+def measured_traffic(workload: str, layer_chunks: int):
+    """HBM traffic per launch from the committed counter summary, while the kernels are unchanged.
+
+    profiles/hbm_traffic_<workload>.md carries the scaled FETCH_SIZE / WRITE_SIZE bytes per launch
+    of each stage call and the hashes of the sources they were taken with; any mismatch gives None.
+    """
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return {}
+    data = json.loads(m.group(1))
+    if data.get("workload") != workload or data.get("layer_chunks") != layer_chunks:
+        return {}
+    out = {}
+    csrc = os.path.join(ROOT, "speculative_kv_sparsity_amd", "csrc")
+    for call, rec in data["calls"].items():
+        ok = all(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16] == h
+                 for f, h in rec["sources"].items())
+        out[call] = rec["read_bytes"] + rec["write_bytes"] if ok else None
+    return out
 
 
 def cpu_baseline(p, w, t0, budget_s):
@@ -125,6 +157,54 @@ def main():
         sel_rows.append(int(dec.sel_count.sum().item()))
     avg = {k: float(np.mean(v)) for k, v in stage.items()}
 
+    # isolated phase: each stage call launched back to back, captured once into a
+    # HIP graph so that host launch overhead does not enter the measured time
+    from speculative_kv_sparsity_amd import api
+
+    def iso(call, reps):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            call(st)
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(reps):
+                    call(st)
+            with torch.cuda.stream(st):        # replay is enqueued on the current stream
+                g.replay()
+                torch.cuda.synchronize()
+                a.record(st)
+                g.replay()
+                z.record(st)
+        except Exception:          # capture refused: time eager launches instead
+            torch.cuda.synchronize()
+            a.record(st)
+            for _ in range(reps):
+                call(st)
+            z.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / reps
+
+    tq, tl = qs[Wm + 2 * K_ - 1], lens[Wm + 2 * K_ - 1]
+    R = args.iso_reps
+    c0a, c0z = dec.chunks[0]
+    iso_ms = {
+        "scores": iso(lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs, ws=dec.ws_scores,
+                                                          stream=st), R),
+        "topk": iso(lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel_idx, dec.sel_count,
+                                                      ws=dec.ws_topk, stream=st), R),
+        "attn": iso(lambda st: api.spc_sparse_decode_attn(dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos,
+                                                          None, api.SPC_ROWS_SLOTS, c0a, c0z, dec.out,
+                                                          ws=dec.ws_attn, stream=st), R),
+        "copy": iso(lambda st: api.spc_elastic_update(dec.shape, None, None, None, None, dec.load_pos, dec.load_slot,
+                                                      dec.load_count, dec.host_kv, dec.host_l, dec.dev_kv, dec.dev_l,
+                                                      c0a, c0z, flags=api.SPC_COPY, plan_stream=st, copy_stream=st),
+                    max(5, R // 3)),   # rewrites the same slots
+    }
+
     eb = p.elem_bytes
     lay_per_chunk = [z - a for a, z in dec.chunks]
     B, Hkv, Hq, d, K, L = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget, p.max_len
@@ -136,10 +216,12 @@ def main():
     copy_bytes = float(np.mean(loaded_rows)) * lay_per_chunk[0] * row                        # host reads per chunk
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
 
-    def roof(bound, nbytes, ms, peak, kernel, calls):
+    traffic = measured_traffic(p.name, nch)
+
+    def roof(bound, nbytes, ms, peak, kernel, calls, call):
         ach = nbytes / (ms * 1e-3) / 1e9
         return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "GB/s",
-                "frac": round(ach / peak, 4), "traffic": None, "kernel": kernel,
+                "frac": round(ach / peak, 4), "traffic": traffic.get(call), "kernel": kernel,
                 "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 2), "launches_per_step": calls}
 
     result = {
@@ -158,17 +240,24 @@ def main():
         "config": {"workload": f"{p.name}: Llama3.1-8B-shaped decode step" if p.name == "b1_32k" else p.name,
                    "batch": B, "layers": p.n_layers, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "cached_tokens": L, "kv_budget": K, "layer_chunks": nch, "parallelism": "single GPU"},
-        "roofline": roof("hbm", attn_bytes, avg["attn"], HBM_PEAK_GBS,
-                         "attn_split_kernel + attn_combine_kernel (sparse decode attention)", nch),
-        "roofline_scores": roof("hbm", score_bytes, avg["scores"], HBM_PEAK_GBS,
-                                "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1),
-        "roofline_host_link": roof("host_link", copy_bytes, avg["copy"], HOST_LINK_PEAK_GBS,
-                                   "copy_kernel (elastic host->HBM gather)", nch),
-        "stage_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS,
+                         "attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K)", nch, "attn"),
+        "roofline_scores": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS,
+                                "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1, "scores"),
+        "roofline_host_link": roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS,
+                                   "copy_kernel (elastic host->HBM gather)", nch, "copy"),
+        "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
         "elastic": {"rows_loaded_per_step": float(np.mean(loaded_rows)), "rows_selected_per_step": float(np.mean(sel_rows)),
                     "transfer_fraction_vs_full_reload": round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
                     "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * p.n_layers * row)},
     }
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, w, Wm, args.cpu_seconds)
     print(json.dumps(result), flush=True)

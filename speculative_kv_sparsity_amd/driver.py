@@ -32,7 +32,7 @@ class SparseDecoder:
     host_kv: pinned host [B][layers][H_kv][L][2][d]  full target K/V store
     """
 
-    def __init__(self, p: Preset, dlm_k: torch.Tensor, host_kv: torch.Tensor, layer_chunks: int = 4,
+    def __init__(self, p: Preset, dlm_k: torch.Tensor, host_kv: torch.Tensor, layer_chunks: int = 2,
                  device: Optional[torch.device] = None):
         assert p.kind in ("gqa", "mha", "mqa"), "MLA uses MlaDecoder"
         self.p = p
