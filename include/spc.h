@@ -119,7 +119,9 @@ size_t spc_workspace_size(int which_call, const spc_shape* s);
  * (SpeContext blog section 2, AttentionWeight formula; blog section 5 and paper
  * summary sections 4.2-4.3: only the Q/K path of the distilled model is kept,
  * head-level weights.)
- *   q        device [B][H_q][head_dim], dtype s->dtype (MLA: absorbed query, see spc_mla_absorb_q)
+ *   q        device [B][H_q][head_dim], dtype s->dtype.  MLA shapes (head_dim 576): the float32
+ *            absorbed query [B][H_q][576] written by spc_mla_absorb_q, scored on MFMA against
+ *            the bf16 latent cache (n_kv_heads 1, H_q a multiple of 16, at most 128)
  *   k        device [B][H_kv][max_len][head_dim], dtype s->dtype
  *   lengths  device [B] int32
  *   probs    device [B][H_q][max_len] float32 out; entries j >= lengths[b] are left untouched
@@ -191,7 +193,9 @@ int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos
  *   out[b][l][i] = sum_r softmax_r(scale * q_l[b][i] . K[r]) V[r]
  * over the rows r of group i / (H_q/n_groups) (see row modes above), for every
  * layer l in [layer_begin, layer_end).
- *   q, q_l   device queries, dtype s->dtype, strides q_l (elements)
+ *   q, q_l   device queries, dtype s->dtype, strides q_l (elements).  MLA shapes (head_dim 576):
+ *            the float32 absorbed query, strides in float32 elements; kv is the latent
+ *            cache with s_kv = 0 (V = the first 512 elements of each latent row)
  *   kv, kv_l device K/V store, dtype s->dtype (slots, or a full cache for GATHER)
  *   rows, row_count  see SPC_ROWS_*; row_count is ignored for SLOTS
  *   out      device [B][n_layers][H_q][v_dim] float32; only layers in range are written
@@ -201,6 +205,31 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
                            const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count,
                            int rows_mode, int32_t layer_begin, int32_t layer_end, float* out, void* ws,
                            size_t ws_bytes, void* stream);
+
+/*
+ * MLA helpers (SpeContext blog section 5, last paragraph; paper summary section
+ * 4.3: MLA keeps a low-dimensional latent per position, retrieval stays
+ * head-level, and only the selected latent rows are expanded).  The per-head
+ * up-projections are absorbed into the query and the output, which equals
+ * expanding the selected rows in real arithmetic:
+ *   q_h . (W_UK[h] c_j || r_j) = (W_UK[h]^T q_nope_h || q_rope_h) . (c_j || r_j)
+ *   sum_j w_j W_UV[h] c_j      = W_UV[h] (sum_j w_j c_j)
+ * Shapes: head_dim 576 (latent 512 + rope 64), v_dim 512, n_kv_heads 1,
+ * n_groups = n_q_heads, dtype bf16, batch <= 16.
+ *
+ * spc_mla_absorb_q: q_abs[b][h][0:512) = W_UK[h]^T q_nope[b][h], q_abs[b][h][512:576) = q_rope[b][h].
+ *   w_uk   device bf16 [H][nope_dim][512]     q_nope device bf16 [B][H][nope_dim]
+ *   q_rope device bf16 [B][H][64]             q_abs  device float32 [B][H][576] out
+ */
+int spc_mla_absorb_q(const spc_shape* s, int32_t nope_dim, const void* w_uk, const void* q_nope,
+                     const void* q_rope, float* q_abs, void* stream);
+
+/* spc_mla_out_proj: out[b][h][0:dv) = W_UV[h] o_lat[b][layer][h] (float32).
+ *   w_uv   device bf16 [H][dv][512]
+ *   o_lat  device float32 [B][n_layers][H][512], as written by spc_sparse_decode_attn
+ *   out    device float32 [B][H][dv] out */
+int spc_mla_out_proj(const spc_shape* s, int32_t dv, const void* w_uv, const float* o_lat, int32_t layer,
+                     float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_SCORES, SPC_CALL_TOPK, SPC_
 __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version", "spc_workspace_size",
            "spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_elastic_reset",
            "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
-           "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN"]
+           "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "spc_mla_absorb_q", "spc_mla_out_proj"]
 
 
 class SpcError(RuntimeError):
@@ -126,8 +126,25 @@ def spc_elastic_reset(shape: SpcShape, batch_index: int, slot_pos, resident_bm, 
 def spc_sparse_decode_attn(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvLayout, rows, row_count,
                            rows_mode: int, layer_begin: int, layer_end: int, out, ws=None, stream=None) -> None:
     _dev(out, "out")
+    for t, n in ((q, "q"), (kv, "kv"), (rows, "rows")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a device tensor")
     ws = _workspace(SPC_CALL_ATTN, shape, out.device) if ws is None else ws
     _check(L.lib().spc_sparse_decode_attn(
         ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
         int(rows_mode), int(layer_begin), int(layer_end), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def spc_mla_absorb_q(shape: SpcShape, nope_dim: int, w_uk, q_nope, q_rope, q_abs, stream=None) -> None:
+    for t, n in ((w_uk, "w_uk"), (q_nope, "q_nope"), (q_rope, "q_rope"), (q_abs, "q_abs")):
+        _dev(t, n)
+    _check(L.lib().spc_mla_absorb_q(ctypes.byref(shape), int(nope_dim), _ptr(w_uk), _ptr(q_nope), _ptr(q_rope),
+                                    _ptr(q_abs), _stream(stream)))
+
+
+def spc_mla_out_proj(shape: SpcShape, dv: int, w_uv, o_lat, layer: int, out, stream=None) -> None:
+    for t, n in ((w_uv, "w_uv"), (o_lat, "o_lat"), (out, "out")):
+        _dev(t, n)
+    _check(L.lib().spc_mla_out_proj(ctypes.byref(shape), int(dv), _ptr(w_uv), _ptr(o_lat), int(layer), _ptr(out),
+                                    _stream(stream)))

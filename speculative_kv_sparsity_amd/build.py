@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["spc_api.cpp", "spc_scores.hip", "spc_topk.hip", "spc_elastic.hip", "spc_attn.hip"]
+SOURCES = ["spc_api.cpp", "spc_scores.hip", "spc_topk.hip", "spc_elastic.hip", "spc_attn.hip", "spc_mla.hip"]
 ARCH = os.environ.get("SPC_OFFLOAD_ARCH", "gfx950")
 
 

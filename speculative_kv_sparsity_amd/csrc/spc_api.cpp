@@ -212,8 +212,9 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
   if (s->head_dim == 576 && kv_l->s_kv != 0)
     return fail(SPC_ERR_UNSUPPORTED, "head_dim 576 reads V from the latent row itself (s_kv must be 0)");
   const int eb = elem_bytes(s);
+  const int qeb = spc::mla_shape(*s) ? 4 : eb;   // MLA: float32 absorbed query
   if (!aligned16(q) || !aligned16(kv)) return fail(SPC_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
-  if ((q_l->s_b * eb) % 16 || (q_l->s_layer * eb) % 16 || (q_l->s_head * eb) % 16)
+  if ((q_l->s_b * qeb) % 16 || (q_l->s_layer * qeb) % 16 || (q_l->s_head * qeb) % 16)
     return fail(SPC_ERR_INVALID_ARG, "query strides must be multiples of 16 bytes");
   if ((kv_l->s_b * eb) % 16 || (kv_l->s_layer * eb) % 16 || (kv_l->s_head * eb) % 16 || (kv_l->s_row * eb) % 16 ||
       (kv_l->s_kv * eb) % 16)
@@ -225,6 +226,45 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
   const hipError_t e = spc::launch_attn(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin, layer_end,
                                         out, ws, as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "sparse decode attention launch");
+}
+
+}  // extern "C"
+
+namespace {
+int check_mla(const spc_shape* s) {
+  if (int e = check_shape(s)) return e;
+  if (!spc::mla_shape(*s) || s->v_dim != spc::kMlaLatent || s->n_kv_heads != 1 || s->dtype != SPC_BF16)
+    return fail(SPC_ERR_UNSUPPORTED, "MLA helpers need head_dim 576, v_dim 512, one latent head, bf16");
+  if (s->batch > spc::kMlaMaxBatch) return fail(SPC_ERR_UNSUPPORTED, "MLA helpers support batch <= %d", spc::kMlaMaxBatch);
+  return SPC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int spc_mla_absorb_q(const spc_shape* s, int32_t nope_dim, const void* w_uk, const void* q_nope,
+                     const void* q_rope, float* q_abs, void* stream) {
+  if (int e = check_mla(s)) return e;
+  if (!w_uk || !q_nope || !q_rope || !q_abs) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (nope_dim < 1 || nope_dim > 1024) return fail(SPC_ERR_INVALID_ARG, "nope_dim %d outside [1, 1024]", nope_dim);
+  if (!aligned16(q_abs)) return fail(SPC_ERR_INVALID_ARG, "q_abs must be 16-byte aligned");
+  const hipError_t e = spc::launch_mla_absorb(s->batch, s->n_q_heads, nope_dim, w_uk, q_nope, q_rope, q_abs,
+                                              as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "MLA query absorption launch");
+}
+
+int spc_mla_out_proj(const spc_shape* s, int32_t dv, const void* w_uv, const float* o_lat, int32_t layer,
+                     float* out, void* stream) {
+  if (int e = check_mla(s)) return e;
+  if (!w_uv || !o_lat || !out) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (dv < 1 || dv > 4096) return fail(SPC_ERR_INVALID_ARG, "dv %d outside [1, 4096]", dv);
+  if (layer < 0 || layer >= s->n_layers) return fail(SPC_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, s->n_layers);
+  if (!aligned16(w_uv) || !aligned16(o_lat)) return fail(SPC_ERR_INVALID_ARG, "w_uv and o_lat must be 16-byte aligned");
+  const int64_t b_stride = (int64_t)s->n_layers * s->n_q_heads * spc::kMlaLatent;
+  const hipError_t e = spc::launch_mla_out_proj(s->batch, s->n_q_heads, dv, w_uv,
+                                                o_lat + (size_t)layer * s->n_q_heads * spc::kMlaLatent, b_stride, out,
+                                                as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "MLA output projection launch");
 }
 
 }  // extern "C"

@@ -247,7 +247,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   }
 }
 
-// MLA latent rows: V is the first DV elements of the K row; one head per group.
+// MLA latent rows: V is the first DV elements of the K row; one head per group; the
+// query is the float32 absorbed query (q_l strides in float32 elements).
 template <int D, int DV, int NI>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
@@ -297,17 +298,28 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
       for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16(kr + (p + 8 * c) * 16);
     }
   }
-  Vec16 qv[CPLK];
-  const char* qh = q + b * ql.b + layer * ql.layer + (int64_t)head * ql.head;
+  // float32 absorbed query: the 8 elements paired with chunk c of the row
+  float qv[CPLK][EPC];
+  const float* qh = reinterpret_cast<const float*>(q + b * ql.b + layer * ql.layer + (int64_t)head * ql.head);
 #pragma unroll
-  for (int c = 0; c < CPLK; ++c) qv[c] = ld16(qh + (p + 8 * c) * 16);
+  for (int c = 0; c < CPLK; ++c) {
+    const float4 a0 = *reinterpret_cast<const float4*>(qh + 8 * (p + 8 * c));
+    const float4 a1 = *reinterpret_cast<const float4*>(qh + 8 * (p + 8 * c) + 4);
+    qv[c][0] = a0.x; qv[c][1] = a0.y; qv[c][2] = a0.z; qv[c][3] = a0.w;
+    qv[c][4] = a1.x; qv[c][5] = a1.y; qv[c][6] = a1.z; qv[c][7] = a1.w;
+  }
   float lg[NI];
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
     float a = 0.f;
     if (row[it] >= 0) {
 #pragma unroll
-      for (int c = 0; c < CPLK; ++c) a = dot16<SPC_BF16>(kc[it][c], qv[c], a);
+      for (int c = 0; c < CPLK; ++c) {
+        float x[EPC];
+        widen16<SPC_BF16>(kc[it][c], x);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) a = fmaf(x[e], qv[c][e], a);
+      }
     }
     a = sum8(a);
     lg[it] = row[it] >= 0 ? a * scale : -INFINITY;
@@ -484,7 +496,8 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
   const size_t n_inst = (size_t)s.batch * n_lay * s.n_groups;
   SplitArgs a;
   a.q = static_cast<const char*>(q);
-  a.ql = QL{qlay.s_b * eb, qlay.s_layer * eb, qlay.s_head * eb};
+  const int qeb = mla_shape(s) ? 4 : eb;          // MLA: float32 absorbed query
+  a.ql = QL{qlay.s_b * qeb, qlay.s_layer * qeb, qlay.s_head * qeb};
   a.kv = static_cast<const char*>(kv);
   a.kl = KL{klay.s_b * eb, klay.s_layer * eb, klay.s_head * eb, klay.s_row * eb, klay.s_kv * eb};
   a.rows = rows;

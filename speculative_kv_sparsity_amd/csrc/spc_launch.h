@@ -18,6 +18,21 @@ size_t scores_ws_bytes(const spc_shape& s);
 bool scores_supported(const spc_shape& s);
 hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* probs,
                          void* ws, hipStream_t st);
+// rewrites logits as probabilities from per-tile (max, sum exp) partials [B*Hq][ntiles]
+hipError_t launch_scores_normalize(const spc_shape& s, float* probs, const float2* part, const int32_t* lengths,
+                                   int ntiles, hipStream_t st);
+
+// ---- MLA (latent 512 + rope 64, one shared latent KV head)
+constexpr int kMlaLatent = 512;
+constexpr int kMlaRope = 64;
+constexpr int kMlaMaxBatch = 16;
+bool mla_shape(const spc_shape& s);   // head_dim 576: the MLA layout
+hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void* q_nope, const void* q_rope,
+                             float* q_abs, hipStream_t st);
+hipError_t launch_mla_scores(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
+                             float* probs, void* ws, hipStream_t st);
+hipError_t launch_mla_out_proj(int B, int H, int dv, const void* w_uv, const float* o_lat, int64_t lat_b_stride,
+                               float* out, hipStream_t st);
 
 // ---- stage 2: group max + Top-K
 constexpr int kTopkLdsKeys = 32768;    // lengths up to this keep their keys in LDS

@@ -204,7 +204,7 @@ hipError_t launch_logits_hc(int HC, dim3 grid, hipStream_t st, const char* q, co
 
 int heads_per_chunk(const spc_shape& s) {
   const int per_kv = s.n_q_heads / s.n_kv_heads;
-  const int cap = s.head_dim > 256 ? 2 : 8;   // register budget for the query chunks
+  const int cap = 8;                          // register budget for the query chunks
   int hc = 1;
   while (hc < per_kv && hc < cap) hc <<= 1;
   return hc;
@@ -212,9 +212,20 @@ int heads_per_chunk(const spc_shape& s) {
 
 }  // namespace
 
+bool mla_shape(const spc_shape& s) { return s.head_dim == kMlaLatent + kMlaRope; }
+
 bool scores_supported(const spc_shape& s) {
+  if (mla_shape(s))   // MFMA path: one latent head shared by 16..128 query heads, bf16 latent
+    return s.dtype == SPC_BF16 && s.n_kv_heads == 1 && s.n_q_heads % 16 == 0 && s.n_q_heads <= 128;
   if (s.dtype == SPC_F32) return s.head_dim == 128 || s.head_dim == 64;
-  return s.head_dim == 64 || s.head_dim == 128 || s.head_dim == 256 || s.head_dim == 576;
+  return s.head_dim == 64 || s.head_dim == 128 || s.head_dim == 256;
+}
+
+hipError_t launch_scores_normalize(const spc_shape& s, float* probs, const float2* part, const int32_t* lengths,
+                                   int ntiles, hipStream_t st) {
+  const dim3 g2((s.max_len + kNormChunk - 1) / kNormChunk, s.batch * s.n_q_heads);
+  scores_normalize_kernel<<<g2, kThreads, 0, st>>>(probs, part, lengths, s.n_q_heads, s.max_len, ntiles);
+  return hipGetLastError();
 }
 
 size_t scores_ws_bytes(const spc_shape& s) {
@@ -224,6 +235,7 @@ size_t scores_ws_bytes(const spc_shape& s) {
 
 hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* probs,
                          void* ws, hipStream_t st) {
+  if (mla_shape(s)) return launch_mla_scores(s, static_cast<const float*>(q), k, lengths, probs, ws, st);
   const int per_kv = s.n_q_heads / s.n_kv_heads;
   const int HC = heads_per_chunk(s);
   const int nchunk = (per_kv + HC - 1) / HC;
@@ -250,16 +262,13 @@ hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const
       SPC_D(64)
       SPC_D(128)
       SPC_D(256)
-      SPC_D(576)
 #undef SPC_D
       default:
         break;
     }
   }
   if (e != hipSuccess) return e;
-  const dim3 g2((s.max_len + kNormChunk - 1) / kNormChunk, s.batch * s.n_q_heads);
-  scores_normalize_kernel<<<g2, kThreads, 0, st>>>(probs, part, lengths, s.n_q_heads, s.max_len, ntiles);
-  return hipGetLastError();
+  return launch_scores_normalize(s, probs, part, lengths, ntiles, st);
 }
 
 }  // namespace spc

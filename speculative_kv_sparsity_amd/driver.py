@@ -143,3 +143,55 @@ class StageTimer:
 
     def ms(self, a: str, b: str) -> float:
         return self.events[a].elapsed_time(self.events[b])
+
+
+class MlaDecoder:
+    """The MLA variant of the step: one shared latent head (512 latent + 64 rope dims) in HBM.
+
+    Per step: absorbed query -> head-level scores over the latent cache (MFMA) -> per-head
+    Top-K -> elastic plan (the resident-set bookkeeping of each head; the latent stays in
+    HBM, so there is nothing to copy) -> attention over the selected latent rows -> output
+    projection.  latent: device [B][L][576]; w_uk, w_uv: device [H][dv][512].
+    """
+
+    def __init__(self, p: Preset, latent: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor):
+        assert p.kind == "mla"
+        self.p = p
+        dev = latent.device
+        B, H, L, K = p.batch, p.n_q_heads, p.max_len, p.budget
+        self.shape = api.make_shape(B, H, 1, H, p.head_dim, p.v_dim, L, K, 1, p.dtype, p.scale)
+        self.latent, self.w_uk, self.w_uv = latent, w_uk, w_uv
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.q_abs = torch.empty((B, H, p.head_dim), **f32)
+        self.probs = torch.empty((B, H, L), **f32)
+        self.sel_idx = torch.empty((B, H, K), **i32)
+        self.sel_count = torch.empty((B, H), **i32)
+        self.slot_pos = torch.empty((B, H, K), **i32)
+        self.resident_bm = torch.empty((B, H, (L + 31) // 32), **i32)
+        self.load_pos = torch.empty((B, H, K), **i32)
+        self.load_slot = torch.empty((B, H, K), **i32)
+        self.load_count = torch.empty((B, H), **i32)
+        self.o_lat = torch.zeros((B, 1, H, p.latent_dim), **f32)
+        self.out = torch.zeros((B, H, p.nope_dim), **f32)
+        self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
+                                     dtype=torch.uint8, device=dev)
+        self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
+                                   dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
+                                   dtype=torch.uint8, device=dev)
+        self.q_l = api.q_layout(H * p.head_dim, 0, p.head_dim)          # float32 elements
+        self.lat_l = api.SpcKvLayout(L * p.head_dim, 0, 0, p.head_dim, 0)  # V = first 512 dims of the row
+        self.main = torch.cuda.current_stream(dev)
+        api.spc_elastic_reset(self.shape, -1, self.slot_pos, self.resident_bm, stream=self.main)
+
+    def step(self, q_nope: torch.Tensor, q_rope: torch.Tensor, lengths: torch.Tensor) -> None:
+        s, st = self.shape, self.main
+        api.spc_mla_absorb_q(s, self.p.nope_dim, self.w_uk, q_nope, q_rope, self.q_abs, stream=st)
+        api.spc_retrieval_scores(s, self.q_abs, self.latent, lengths, self.probs, ws=self.ws_scores, stream=st)
+        api.spc_group_max_topk(s, self.probs, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk, stream=st)
+        api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
+                               self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)
+        api.spc_sparse_decode_attn(s, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx, self.sel_count,
+                                   api.SPC_ROWS_GATHER, 0, 1, self.o_lat, ws=self.ws_attn, stream=st)
+        api.spc_mla_out_proj(s, self.p.nope_dim, self.w_uv, self.o_lat, 0, self.out, stream=st)

@@ -1,0 +1,92 @@
+"""MLA variant: head-level retrieval over the latent cache, per-head Top-K, attention over the
+selected latent rows, against the oracle's literal expansion of only the selected rows."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import spc_oracle as O
+from speculative_kv_sparsity_amd import workload as W
+from speculative_kv_sparsity_amd.driver import MlaDecoder
+from tests.gpu_util import (ATTN_DERIVED, ATTN_MAX_ABS, PROBS_RTOL, check_topk_tolerance, dev_lengths, raw,
+                            sel_lists)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(t):
+    return O.to_f64(raw(t), "bf16")
+
+
+def _check_steps(p, w, steps, lengths_override=None, heads=None, batches=None):
+    dec = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+    C = p.latent_dim
+    w_uk, w_uv = _bf(w.w_uk), _bf(w.w_uv)
+    lat_all = [_bf(w.latent[b]) for b in range(p.batch)]
+    heads = list(range(p.n_q_heads)) if heads is None else heads
+    batches = list(range(p.batch)) if batches is None else batches
+    prev = None
+    overl = []
+    for t in range(steps):
+        lengths = list(w.lengths[t]) if lengths_override is None else lengths_override
+        qn, qr = w.q_nope[t].contiguous(), w.q_rope[t].contiguous()
+        dec.step(qn, qr, dev_lengths(lengths))
+        torch.cuda.synchronize()
+        qn64, qr64 = _bf(qn), _bf(qr)
+        probs = dec.probs.cpu().numpy().astype(np.float64)
+        gsel = sel_lists(dec.sel_idx, dec.sel_count)
+        # Top-K bit-exact on the GPU's own float32 scores, every head
+        for b in range(p.batch):
+            n = int(lengths[b])
+            for h in range(p.n_q_heads):
+                ref = O.topk_select(np.nan_to_num(probs[b, h]), n, p.budget)
+                np.testing.assert_array_equal(gsel[b][h], ref)
+        # scores and selection against the literal-expansion oracle, sampled heads
+        for b in batches:
+            n = int(lengths[b])
+            if n == 0:
+                assert all(len(gsel[b][h]) == 0 for h in heads)
+                assert np.all(dec.out.cpu().numpy()[b] == 0)
+                continue
+            lat, rope = lat_all[b][:, :C], lat_all[b][:, C:]
+            ref_p = O.mla_retrieval_scores(qn64[b:b + 1], qr64[b:b + 1], lat[None], rope[None], w_uk, [n], p.scale,
+                                           heads=heads)
+            for h in heads:
+                rp = ref_p[(0, h)]
+                np.testing.assert_allclose(probs[b, h, :n], rp, rtol=PROBS_RTOL, atol=0)
+                ref_sel = O.topk_select(rp, n, p.budget)
+                check_topk_tolerance([[gsel[b][h]]], [[ref_sel]], rp[None, None, :], p.budget)
+                # attention + output projection over the GPU's selection, rows expanded literally
+                ref_o = O.mla_sparse_attention(qn64[b, h], qr64[b, h], lat, rope, w_uk, w_uv, gsel[b][h], h, p.scale)
+                err = float(np.max(np.abs(dec.out.cpu().numpy()[b, h].astype(np.float64) - ref_o)))
+                assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, (t, b, h, err)
+        # the per-head plan keeps the resident set equal to the selection
+        sp = dec.slot_pos.cpu().numpy()
+        for b in range(p.batch):
+            for h in range(p.n_q_heads):
+                assert set(int(x) for x in sp[b, h] if x >= 0) == set(gsel[b][h].tolist())
+        if prev is not None:
+            overl.append(np.mean([O.overlap(prev[b][h], gsel[b][h]) for b in range(p.batch)
+                                  for h in range(p.n_q_heads) if len(gsel[b][h])]))
+        prev = gsel
+    return overl
+
+
+def test_mla_small_ragged_all_heads():
+    p = W.PRESETS["mla_32k"].with_(batch=3, n_q_heads=16, max_len=1000, budget=96)
+    w = W.generate(p, device="cuda", seed=5, steps=3)
+    _check_steps(p, w, 3, lengths_override=[1000, 613, 0])
+
+
+def test_mla_budget_covers_everything_and_tail_tile():
+    """n <= K selects every position; a length that is not a multiple of the 16-row MFMA block."""
+    p = W.PRESETS["mla_32k"].with_(batch=2, n_q_heads=32, max_len=300, budget=300)
+    w = W.generate(p, device="cuda", seed=6, steps=1)
+    _check_steps(p, w, 1, lengths_override=[300, 77])
+
+
+def test_mla_32k_full_shape_sampled_heads():
+    """4 sequences, 128 heads, 32768 latent rows, budget 2048; oracle checks on sampled heads."""
+    p = W.PRESETS["mla_32k"]
+    w = W.generate(p, device="cuda", seed=0, steps=2)
+    overl = _check_steps(p, w, 2, heads=[0, 37, 127], batches=[0, 3])
+    assert overl and overl[0] > 0.3
