@@ -35,31 +35,64 @@ constexpr int kLdsRow = kMlaD + 8;                 // padded row (elements): spr
 constexpr int kScoreThreads = 512;                 // 8 waves x 16 heads
 static_assert(kMlaD % 32 == 0, "k-steps of 32");
 
+// One workgroup per head.  Lane l owns latent dims 8l..8l+7 (one 16-byte chunk of
+// every W_UK row); wave w takes the rows n = w, w+4, ...; sequences go four at a
+// time; the four waves' partial sums are added through LDS.
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const uint16_t* __restrict__ w_uk,
                                                          const uint16_t* __restrict__ q_nope,
                                                          const uint16_t* __restrict__ q_rope,
                                                          float* __restrict__ q_abs, int B, int H, int dn) {
+  static_assert(kMlaLatent == 8 * kWave, "one 16-byte chunk of the latent per lane");
   const int h = blockIdx.x;
-  extern __shared__ float sq[];                    // [B][dn] query of this head, widened
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  extern __shared__ float smem[];
+  float* sq = smem;                                 // [B][dn] query of this head, widened
+  float* red = smem + B * dn;                       // [4 waves][4 sequences][512]
   for (int i = threadIdx.x; i < B * dn; i += blockDim.x) {
     const int b = i / dn, n = i - (i / dn) * dn;
     sq[i] = __uint_as_float((uint32_t)q_nope[((size_t)b * H + h) * dn + n] << 16);
   }
   __syncthreads();
-  const uint16_t* w = w_uk + (size_t)h * dn * kMlaLatent;
-  for (int k = threadIdx.x; k < kMlaLatent; k += blockDim.x) {
-    float acc[kMlaMaxBatch];
+  const uint16_t* w = w_uk + (size_t)h * dn * kMlaLatent + 8 * lane;
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    float acc[4][8];
 #pragma unroll
-    for (int b = 0; b < kMlaMaxBatch; ++b) acc[b] = 0.f;
-    for (int n = 0; n < dn; ++n) {
-      const float wv = __uint_as_float((uint32_t)w[(size_t)n * kMlaLatent + k] << 16);
+    for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-      for (int b = 0; b < kMlaMaxBatch; ++b)
-        if (b < B) acc[b] = fmaf(wv, sq[b * dn + n], acc[b]);
+      for (int e = 0; e < 8; ++e) acc[bb][e] = 0.f;
+    for (int n0 = wid; n0 < dn; n0 += 32) {
+      Vec16 wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (n0 + 4 * u < dn) wv[u] = ld16(w + (size_t)(n0 + 4 * u) * kMlaLatent);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int n = n0 + 4 * u;
+        if (n >= dn) break;
+        float x[8];
+        widen16<SPC_BF16>(wv[u], x);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const float qv = b0 + bb < B ? sq[(b0 + bb) * dn + n] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[bb][e] = fmaf(x[e], qv, acc[bb][e]);
+        }
+      }
     }
 #pragma unroll
-    for (int b = 0; b < kMlaMaxBatch; ++b)
-      if (b < B) q_abs[((size_t)b * H + h) * kMlaD + k] = acc[b];
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(wid * 4 + bb) * kMlaLatent + 8 * lane + e] = acc[bb][e];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 4 * kMlaLatent; i += blockDim.x) {
+      const int bb = i / kMlaLatent, k = i - (i / kMlaLatent) * kMlaLatent;
+      if (b0 + bb < B) {
+        const float v = red[(0 * 4 + bb) * kMlaLatent + k] + red[(1 * 4 + bb) * kMlaLatent + k] +
+                        red[(2 * 4 + bb) * kMlaLatent + k] + red[(3 * 4 + bb) * kMlaLatent + k];
+        q_abs[((size_t)(b0 + bb) * H + h) * kMlaD + k] = v;
+      }
+    }
+    __syncthreads();
   }
   for (int i = threadIdx.x; i < B * kMlaRope; i += blockDim.x) {
     const int b = i / kMlaRope, r = i - (i / kMlaRope) * kMlaRope;
@@ -181,35 +214,49 @@ __global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* 
   }
 }
 
-// One workgroup per head; wave w handles output rows w, w+4, ...; a lane holds 8
-// contiguous latent dims of the row.
+// One workgroup per head; two lanes per output row, each summing 256 contiguous
+// latent dims (eight 16-byte loads in flight); o_lat of the head sits in LDS.
 __global__ __launch_bounds__(256) void mla_out_proj_kernel(const uint16_t* __restrict__ w_uv,
                                                            const float* __restrict__ o_lat, int64_t lat_b_stride,
                                                            float* __restrict__ out, int B, int H, int dv) {
   const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  static_assert(kMlaLatent == 8 * kWave, "one 16-byte chunk of the latent per lane");
-  float ol[kMlaMaxBatch][8];
-#pragma unroll
-  for (int b = 0; b < kMlaMaxBatch; ++b) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ol[b][e] = 0.f;
-    if (b < B) {
-      const float* src = o_lat + (size_t)b * lat_b_stride + (size_t)h * kMlaLatent + 8 * lane;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ol[b][e] = src[e];
-    }
+  extern __shared__ float sol[];                    // [B][512]
+  for (int i = threadIdx.x; i < B * kMlaLatent; i += blockDim.x) {
+    const int b = i / kMlaLatent, k = i - (i / kMlaLatent) * kMlaLatent;
+    sol[i] = o_lat[(size_t)b * lat_b_stride + (size_t)h * kMlaLatent + k];
   }
-  for (int r = wid; r < dv; r += 4) {
-    const Vec16 wv = ld16(w_uv + ((size_t)h * dv + r) * kMlaLatent + 8 * lane);
-    float x[8];
-    widen16<SPC_BF16>(wv, x);
-    for (int b = 0; b < B; ++b) {
-      float a = 0.f;
+  __syncthreads();
+  const int half = threadIdx.x & 1;
+  constexpr int kHalf = kMlaLatent / 2;             // 256 dims per lane
+  for (int r0 = 0; r0 < dv; r0 += blockDim.x / 2) {
+    const int r = r0 + (threadIdx.x >> 1);
+    const bool ok = r < dv;
+    const uint16_t* wr = w_uv + ((size_t)h * dv + (ok ? r : 0)) * kMlaLatent + kHalf * half;
+    for (int b0 = 0; b0 < B; b0 += 4) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < kHalf / 8; c0 += 8) {
+        Vec16 wv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a = fmaf(x[e], ol[b][e], a);
-      a = wave_sum(a);
-      if (lane == 0) out[((size_t)b * H + h) * dv + r] = a;
+        for (int u = 0; u < 8; ++u) wv[u] = ld16(wr + 8 * (c0 + u));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float x[8];
+          widen16<SPC_BF16>(wv[u], x);
+          const int k = kHalf * half + 8 * (c0 + u);
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            if (b0 + bb >= B) break;
+            const float* o = sol + (b0 + bb) * kMlaLatent + k;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[bb] = fmaf(x[e], o[e], acc[bb]);
+          }
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const float t = acc[bb] + __shfl_xor(acc[bb], 1, kWave);
+        if (ok && half == 0 && b0 + bb < B) out[((size_t)(b0 + bb) * H + h) * dv + r] = t;
+      }
     }
   }
 }
@@ -218,7 +265,7 @@ __global__ __launch_bounds__(256) void mla_out_proj_kernel(const uint16_t* __res
 
 hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void* q_nope, const void* q_rope,
                              float* q_abs, hipStream_t st) {
-  mla_absorb_kernel<<<dim3(H), 256, (size_t)B * dn * sizeof(float), st>>>(
+  mla_absorb_kernel<<<dim3(H), 256, ((size_t)B * dn + 4 * 4 * kMlaLatent) * sizeof(float), st>>>(
       static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
       q_abs, B, H, dn);
   return hipGetLastError();
@@ -237,7 +284,7 @@ hipError_t launch_mla_scores(const spc_shape& s, const float* q_abs, const void*
 
 hipError_t launch_mla_out_proj(int B, int H, int dv, const void* w_uv, const float* o_lat, int64_t lat_b_stride,
                                float* out, hipStream_t st) {
-  mla_out_proj_kernel<<<dim3(H), 256, 0, st>>>(static_cast<const uint16_t*>(w_uv), o_lat, lat_b_stride, out, B, H,
+  mla_out_proj_kernel<<<dim3(H), 256, (size_t)B * kMlaLatent * sizeof(float), st>>>(static_cast<const uint16_t*>(w_uv), o_lat, lat_b_stride, out, B, H,
                                                 dv);
   return hipGetLastError();
 }
