@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps 60] [--warmup 4] [--config b1_32k]
 
 A step is one pass of the whole path over one batch of synthetic input:
-retrieval scores -> group max / Top-K -> elastic plan -> elastic copy (side
-stream, per layer chunk) -> sparse decode attention (per layer chunk).  The
+retrieval scores -> group max / Top-K -> elastic plan -> elastic copy (per
+layer chunk) -> sparse decode attention (per layer chunk, overlapping the
+copies of the later chunks on a second stream).  The
 default workload is the Llama3.1-8B-shaped 32K step (batch 1, 32 layers,
 32 q-heads / 8 KV heads, d=128, bf16, budget 2048, target K/V in pinned host
 memory).  Inputs are resident (HBM / pinned host) before timing starts.
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--config", default="b1_32k")
     ap.add_argument("--layer-chunks", type=int, default=2)
+    ap.add_argument("--tail-layers", type=int, default=None,
+                    help="layers in the last chunk (default n_layers // 8)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -120,7 +123,7 @@ def main():
     K_, Wm = args.steps, args.warmup
     total = Wm + 2 * K_
     w = W.generate(p, device="cuda", seed=args.seed, steps=total, pin_host=True)
-    dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=args.layer_chunks)
+    dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=args.layer_chunks, tail_layers=args.tail_layers)
     lens = torch.as_tensor(w.lengths, device="cuda")
     qs = w.q.contiguous()
     torch.cuda.synchronize()
@@ -198,7 +201,7 @@ def main():
                                                       ws=dec.ws_topk, stream=st), R),
         "attn": iso(lambda st: api.spc_sparse_decode_attn(dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos,
                                                           None, api.SPC_ROWS_SLOTS, c0a, c0z, dec.out,
-                                                          ws=dec.ws_attn, stream=st), R),
+                                                          ws=dec.ws_attn[0], stream=st), R),
         "copy": iso(lambda st: api.spc_elastic_update(dec.shape, None, None, None, None, dec.load_pos, dec.load_slot,
                                                       dec.load_count, dec.host_kv, dec.host_l, dec.dev_kv, dec.dev_l,
                                                       c0a, c0z, flags=api.SPC_COPY, plan_stream=st, copy_stream=st),
@@ -239,7 +242,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{p.name}: Llama3.1-8B-shaped decode step" if p.name == "b1_32k" else p.name,
                    "batch": B, "layers": p.n_layers, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
-                   "cached_tokens": L, "kv_budget": K, "layer_chunks": nch, "parallelism": "single GPU"},
+                   "cached_tokens": L, "kv_budget": K, "layer_chunks": nch,
+                   "chunk_layers": [z - a for a, z in dec.chunks], "parallelism": "single GPU"},
         "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS,
                          "attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K)", nch, "attn"),
         "roofline_scores": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS,

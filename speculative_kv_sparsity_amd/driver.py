@@ -2,21 +2,23 @@
 
 SpeContext's dataflow (blog section 4; paper summary section 5.1): the
 retrieval head runs first on the step's input, its Top-K selection drives the
-elastic load of the missing K/V rows on a second stream, and the target
-model's attention consumes the resident sparse KV.  Here:
+elastic load of the missing K/V rows, and the target model's attention
+consumes the resident sparse KV while later layers are still loading.  Here:
 
-  main stream : scores -> group max / Top-K -> plan --ev_plan-->
-  copy stream :                                  wait ev_plan -> copy(layer chunk c) -> ev_copy[c]
-  main stream :                                  wait ev_copy[c] -> attention(layer chunk c)
+  main stream : scores -> group max / Top-K -> plan -> copy(chunk 0) -ev_copy[0]-> copy(chunk 1) ... copy(last)
+                -> attention(last chunk) -> wait ev_attn
+  side stream :                   wait ev_copy[c] -> attention(chunk c) ... -> ev_attn   (every chunk but the last)
 
-so the copy of chunk c+1 overlaps the attention of chunk c.  The next step's
-scores are stream-ordered after this step's last attention (the next query
-depends on this step's output), and the next plan, which frees slots, is
-ordered after every attention that read them.
+The copy is on the critical path, so it runs on the stream of the stages it
+depends on and starts without a cross-stream hand-off; the attention of the
+earlier layer chunks overlaps the remaining copies on the side stream.  The
+last chunk is the short one (its attention is the only compute left after the
+last copy).  The next step's scores are ordered after every attention of this
+step (the next query depends on this step's output), and so is the next plan,
+which frees slots those attentions read.
 """
 from __future__ import annotations
 
-import math
 from typing import List, Optional
 
 import torch
@@ -33,7 +35,7 @@ class SparseDecoder:
     """
 
     def __init__(self, p: Preset, dlm_k: torch.Tensor, host_kv: torch.Tensor, layer_chunks: int = 2,
-                 device: Optional[torch.device] = None):
+                 tail_layers: Optional[int] = None, device: Optional[torch.device] = None):
         assert p.kind in ("gqa", "mha", "mqa"), "MLA uses MlaDecoder"
         self.p = p
         dev = device or dlm_k.device
@@ -59,16 +61,15 @@ class SparseDecoder:
                                      dtype=torch.uint8, device=dev)
         self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
                                    dtype=torch.uint8, device=dev)
-        self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
-                                   dtype=torch.uint8, device=dev)
         self.q_l = api.q_layout(Hq * d, 0, d)   # the same query serves every layer
-        n = max(1, min(layer_chunks, p.n_layers))
-        step = math.ceil(p.n_layers / n)
-        self.chunks: List[tuple] = [(a, min(a + step, p.n_layers)) for a in range(0, p.n_layers, step)]
+        self.chunks: List[tuple] = layer_chunk_bounds(p.n_layers, layer_chunks, tail_layers)
+        # one attention workspace per layer chunk: chunks run concurrently on two streams
+        self.ws_attn = [torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
+                                    dtype=torch.uint8, device=dev) for _ in self.chunks]
         self.main = torch.cuda.current_stream(dev)
-        self.copy = torch.cuda.Stream(device=dev)
-        self.ev_plan = torch.cuda.Event()
+        self.side = torch.cuda.Stream(device=dev)
         self.ev_copy = [torch.cuda.Event() for _ in self.chunks]
+        self.ev_attn = torch.cuda.Event()
         self.reset()
 
     def reset(self, batch_index: int = -1) -> None:
@@ -95,12 +96,13 @@ class SparseDecoder:
         a, z = self.chunks[c]
         api.spc_elastic_update(self.shape, None, None, None, None, self.load_pos, self.load_slot, self.load_count,
                                self.host_kv, self.host_l, self.dev_kv, self.dev_l, a, z, flags=api.SPC_COPY,
-                               plan_stream=self.copy, copy_stream=self.copy)
+                               plan_stream=self.main, copy_stream=self.main)
 
-    def attend_chunk(self, q: torch.Tensor, c: int) -> None:
+    def attend_chunk(self, q: torch.Tensor, c: int, stream=None) -> None:
         a, z = self.chunks[c]
         api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.dev_kv, self.dev_l, self.slot_pos, None,
-                                   api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn, stream=self.main)
+                                   api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn[c],
+                                   stream=self.main if stream is None else stream)
 
     # --- one step -----------------------------------------------------------------------
     def step(self, q: torch.Tensor, lengths: torch.Tensor, timer: Optional["StageTimer"] = None) -> None:
@@ -116,18 +118,41 @@ class SparseDecoder:
         mark("plan", self.main)
         self.plan()
         mark("plan_end", self.main)
-        self.ev_plan.record(self.main)
-        self.copy.wait_event(self.ev_plan)
+        last = len(self.chunks) - 1
         for c in range(len(self.chunks)):
-            mark(f"copy{c}", self.copy)
+            mark(f"copy{c}", self.main)
             self.copy_chunk(c)
-            mark(f"copy{c}_end", self.copy)
-            self.ev_copy[c].record(self.copy)
-        for c in range(len(self.chunks)):
-            self.main.wait_event(self.ev_copy[c])
-            mark(f"attn{c}", self.main)
-            self.attend_chunk(q, c)
-            mark(f"attn{c}_end", self.main)
+            mark(f"copy{c}_end", self.main)
+            if c < last:
+                self.ev_copy[c].record(self.main)
+                self.side.wait_event(self.ev_copy[c])
+                mark(f"attn{c}", self.side)
+                self.attend_chunk(q, c, self.side)
+                mark(f"attn{c}_end", self.side)
+        mark(f"attn{last}", self.main)
+        self.attend_chunk(q, last)
+        mark(f"attn{last}_end", self.main)
+        if last > 0:
+            self.ev_attn.record(self.side)
+            self.main.wait_event(self.ev_attn)
+
+
+def layer_chunk_bounds(n_layers: int, n_chunks: int, tail_layers: Optional[int] = None) -> List[tuple]:
+    """Layer ranges [a, z) of the copy/attention pipeline.
+
+    The last chunk holds ``tail_layers`` layers (default n_layers // 8, at least
+    one): its attention is the only work left once the last copy ends, and its
+    copy must outlast the attention of the chunks before it.  The other layers
+    are split evenly over the first n_chunks - 1 chunks."""
+    n = max(1, min(n_chunks, n_layers))
+    if n == 1:
+        return [(0, n_layers)]
+    tail = max(1, n_layers // 8) if tail_layers is None else tail_layers
+    tail = max(1, min(tail, n_layers - (n - 1)))
+    head = n_layers - tail
+    step = -(-head // (n - 1))
+    out = [(a, min(a + step, head)) for a in range(0, head, step)]
+    return out + [(head, n_layers)]
 
 
 class StageTimer:

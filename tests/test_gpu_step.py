@@ -15,6 +15,21 @@ pytestmark = pytest.mark.gpu
 def _run_and_check(p, steps, layer_chunks=4, seed=0, delay_cycles=0, check_layers=None):
     w = W.generate(p, device="cuda", seed=seed, steps=steps, pin_host=True)
     dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=layer_chunks)
+    if delay_cycles:
+        # hold back every copy (main stream) and every side-stream attention by a spin, so a
+        # missing wait between them shows up as a wrong output in this or the next step
+        copy_chunk, attend_chunk = dec.copy_chunk, dec.attend_chunk
+
+        def slow_copy(c):
+            torch.cuda._sleep(delay_cycles)
+            copy_chunk(c)
+
+        def slow_attend(q, c, stream=None):
+            with torch.cuda.stream(stream if stream is not None else dec.main):
+                torch.cuda._sleep(delay_cycles)
+            attend_chunk(q, c, stream)
+
+        dec.copy_chunk, dec.attend_chunk = slow_copy, slow_attend
     ora = OracleDecoder(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.budget, p.scale, p.dtype)
     lens_dev = dev_lengths(w.lengths)
     k_raw, kv_raw = raw(w.dlm_k), raw(w.host_kv)
@@ -23,18 +38,7 @@ def _run_and_check(p, steps, layer_chunks=4, seed=0, delay_cycles=0, check_layer
     prev = None
     for t in range(steps):
         q = w.q[t].contiguous()
-        if delay_cycles:
-            # same ordering as SparseDecoder.step, with the side stream held back by a spin
-            dec.select(q, lens_dev[t]); dec.plan()
-            dec.ev_plan.record(dec.main); dec.copy.wait_event(dec.ev_plan)
-            with torch.cuda.stream(dec.copy):
-                torch.cuda._sleep(delay_cycles)
-            for c in range(len(dec.chunks)):
-                dec.copy_chunk(c); dec.ev_copy[c].record(dec.copy)
-            for c in range(len(dec.chunks)):
-                dec.main.wait_event(dec.ev_copy[c]); dec.attend_chunk(q, c)
-        else:
-            dec.step(q, lens_dev[t])
+        dec.step(q, lens_dev[t])
         torch.cuda.synchronize()
         lengths = w.lengths[t]
         # selection against the fp64 oracle chain (near-ties only)
@@ -78,7 +82,8 @@ def test_gqa_multi_layer_chunks_and_ragged_batch():
 
 
 def test_side_stream_delay_does_not_change_results():
-    """Hazard test: the copy stream is held back each step; events must keep outputs identical."""
+    """Hazard test: every copy and every side-stream attention is held back by a spin each step;
+    the events between the streams must keep the outputs identical."""
     p = W.PRESETS["b1_32k"].with_(max_len=4096, budget=512, n_layers=8)
     a, _ = _run_and_check(p, steps=4, layer_chunks=4, seed=3)
     b, _ = _run_and_check(p, steps=4, layer_chunks=4, seed=3, delay_cycles=2_000_000)
