@@ -1,6 +1,7 @@
 """Benchmark of the sparse-KV decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps 60] [--warmup 4] [--config b1_32k]
+                    (--config tiny | b1_32k | b16_grow | mha_64k | mla_32k)
 
 A step is one pass of the whole path over one batch of synthetic input:
 retrieval scores -> group max / Top-K -> elastic plan -> elastic copy (per
@@ -9,6 +10,10 @@ copies of the later chunks on a second stream).  The
 default workload is the Llama3.1-8B-shaped 32K step (batch 1, 32 layers,
 32 q-heads / 8 KV heads, d=128, bf16, budget 2048, target K/V in pinned host
 memory).  Inputs are resident (HBM / pinned host) before timing starts.
+The other configurations run the same way; the MLA one runs its own step
+(absorbed query -> scores over the latent cache -> per-head Top-K -> plan ->
+attention over the selected latent rows -> output projection; the latent
+stays in HBM, so nothing is copied).
 
 Prints one JSON line: steps/s from a clean timed pass (events only at its two
 ends); per-stage times inside steps from a second, instrumented pass (events
@@ -34,6 +39,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 HOST_LINK_PEAK_GBS = 63.0      # PCIe Gen5 x16 per direction: 32 GT/s x 16 x 128/130 / 8
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+WORKLOADS = {
+    "tiny": "tiny: 1 sequence, 1 layer, 32 q-heads / 8 KV heads, d=128, fp32, 4096 cached tokens, budget 256",
+    "b1_32k": "b1_32k: Llama3.1-8B-shaped decode step",
+    "b16_grow": "b16_grow: batch 16 reasoning growth, 32 layers, ragged lengths growing to 16384, budget 1024",
+    "mha_64k": "mha_64k: MHA 32 q-heads = 32 KV heads, 65536 cached tokens, batch 2, budget 4096, 1 layer",
+    "mla_32k": "mla_32k: MLA 128 heads, latent 512 + rope 64, 32768 cached tokens, batch 4, budget 2048",
+}
 
 
 def parse():
@@ -46,6 +60,9 @@ def parse():
     ap.add_argument("--tail-layers", type=int, default=None,
                     help="layers in the last chunk (default n_layers // 8)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--t0", type=int, default=None,
+                    help="first step of the measured window in the length schedule (default 0; batch-16 "
+                         "growth: the last steps, where every sequence has reached 16384)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iso-reps", type=int, default=30, help="launches per stage in the isolated phase")
@@ -78,6 +95,46 @@ def measured_traffic(workload: str, layer_chunks: int):
                  for f, h in rec["sources"].items())
         out[call] = rec["read_bytes"] + rec["write_bytes"] if ok else None
     return out
+
+
+def iso(torch, call, reps):
+    """Average time of one call: `reps` launches captured once into a HIP graph (host launch
+    overhead out of the bracket), replayed between two events on the stream the calls use."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        call(st)
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(reps):
+                call(st)
+        with torch.cuda.stream(st):        # replay is enqueued on the current stream
+            g.replay()
+            torch.cuda.synchronize()
+            a.record(st)
+            g.replay()
+            z.record(st)
+    except Exception:          # capture refused: time eager launches instead
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(reps):
+            call(st)
+        z.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(z) / reps
+
+
+def roof(bound, amount, ms, peak, unit, kernel, calls, traffic=None):
+    """Roofline record of one call: `amount` algorithmic bytes (GB/s units) or flops (TFLOP/s)."""
+    scale = 1e9 if unit == "GB/s" else 1e12
+    ach = amount / (ms * 1e-3) / scale
+    rec = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+           "traffic": traffic, "kernel": kernel, "avg_launch_us": round(ms * 1e3, 2), "launches_per_step": calls}
+    rec["bytes_per_launch" if unit == "GB/s" else "flop_per_launch"] = int(amount)
+    return rec
 
 
 def cpu_baseline(p, w, t0, budget_s):
@@ -116,19 +173,48 @@ def main():
     import torch
 
     from speculative_kv_sparsity_amd import workload as W
-    from speculative_kv_sparsity_amd.driver import SparseDecoder, StageTimer
 
     torch.cuda.set_device(0)
     p = W.PRESETS[args.config]
+    result = bench_mla(args, p, torch, W) if p.kind == "mla" else bench_gqa(args, p, torch, W)
+    print(json.dumps(result), flush=True)
+
+
+def _header(args, p, ms_per_step, config):
+    return {
+        "metric": "sparse decode steps/s (score+TopK+elastic load+attn) and % HBM peak at 32K",
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": config,
+    }
+
+
+def bench_gqa(args, p, torch, W):
+    from speculative_kv_sparsity_amd import api
+    from speculative_kv_sparsity_amd.driver import SparseDecoder, StageTimer
+
     K_, Wm = args.steps, args.warmup
     total = Wm + 2 * K_
-    w = W.generate(p, device="cuda", seed=args.seed, steps=total, pin_host=True)
+    t0 = args.t0
+    if t0 is None:
+        t0 = p.steps - total if p.name == "b16_grow" else 0
+    t0 = max(0, min(t0, p.steps - total)) if p.steps >= total else 0
+    w = W.generate(p, device="cuda", seed=args.seed, steps=max(total, t0 + total), pin_host=True)
     dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=args.layer_chunks, tail_layers=args.tail_layers)
     lens = torch.as_tensor(w.lengths, device="cuda")
     qs = w.q.contiguous()
     torch.cuda.synchronize()
 
-    for t in range(Wm):                          # step 0 is the cold full-budget load
+    for t in range(t0, t0 + Wm):                 # the first step is the cold full-budget load
         dec.step(qs[t], lens[t])
     torch.cuda.synchronize()
 
@@ -136,7 +222,7 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(dec.main)
-    for t in range(Wm, Wm + K_):
+    for t in range(t0 + Wm, t0 + Wm + K_):
         dec.step(qs[t], lens[t])
     e1.record(dec.main)
     torch.cuda.synchronize()
@@ -146,7 +232,7 @@ def main():
     stage = {k: [] for k in ("scores", "topk", "plan", "copy", "attn")}
     loaded_rows, sel_rows = [], []
     nch = len(dec.chunks)
-    for t in range(Wm + K_, Wm + 2 * K_):
+    for t in range(t0 + Wm + K_, t0 + total):
         tm = StageTimer()
         dec.step(qs[t], lens[t], timer=tm)
         torch.cuda.synchronize()
@@ -160,102 +246,59 @@ def main():
         sel_rows.append(int(dec.sel_count.sum().item()))
     avg = {k: float(np.mean(v)) for k, v in stage.items()}
 
-    # isolated phase: each stage call launched back to back, captured once into a
-    # HIP graph so that host launch overhead does not enter the measured time
-    from speculative_kv_sparsity_amd import api
-
-    def iso(call, reps):
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            call(st)
-        torch.cuda.synchronize()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        try:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=st):
-                for _ in range(reps):
-                    call(st)
-            with torch.cuda.stream(st):        # replay is enqueued on the current stream
-                g.replay()
-                torch.cuda.synchronize()
-                a.record(st)
-                g.replay()
-                z.record(st)
-        except Exception:          # capture refused: time eager launches instead
-            torch.cuda.synchronize()
-            a.record(st)
-            for _ in range(reps):
-                call(st)
-            z.record(st)
-        torch.cuda.synchronize()
-        return a.elapsed_time(z) / reps
-
-    tq, tl = qs[Wm + 2 * K_ - 1], lens[Wm + 2 * K_ - 1]
+    # isolated phase: each stage call launched back to back
+    tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
     R = args.iso_reps
     c0a, c0z = dec.chunks[0]
     iso_ms = {
-        "scores": iso(lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs, ws=dec.ws_scores,
-                                                          stream=st), R),
-        "topk": iso(lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel_idx, dec.sel_count,
-                                                      ws=dec.ws_topk, stream=st), R),
-        "attn": iso(lambda st: api.spc_sparse_decode_attn(dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos,
-                                                          None, api.SPC_ROWS_SLOTS, c0a, c0z, dec.out,
-                                                          ws=dec.ws_attn[0], stream=st), R),
-        "copy": iso(lambda st: api.spc_elastic_update(dec.shape, None, None, None, None, dec.load_pos, dec.load_slot,
-                                                      dec.load_count, dec.host_kv, dec.host_l, dec.dev_kv, dec.dev_l,
-                                                      c0a, c0z, flags=api.SPC_COPY, plan_stream=st, copy_stream=st),
+        "scores": iso(torch, lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs,
+                                                                 ws=dec.ws_scores, stream=st), R),
+        "topk": iso(torch, lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel_idx, dec.sel_count,
+                                                             ws=dec.ws_topk, stream=st), R),
+        "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l,
+                                                                 dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
+                                                                 dec.out, ws=dec.ws_attn[0], stream=st), R),
+        "copy": iso(torch, lambda st: api.spc_elastic_update(dec.shape, None, None, None, None, dec.load_pos,
+                                                             dec.load_slot, dec.load_count, dec.host_kv, dec.host_l,
+                                                             dec.dev_kv, dec.dev_l, c0a, c0z, flags=api.SPC_COPY,
+                                                             plan_stream=st, copy_stream=st),
                     max(5, R // 3)),   # rewrites the same slots
     }
 
     eb = p.elem_bytes
-    lay_per_chunk = [z - a for a, z in dec.chunks]
-    B, Hkv, Hq, d, K, L = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget, p.max_len
-    n_valid = float(np.mean(w.lengths[Wm + K_:Wm + 2 * K_].sum(axis=1)))
+    lay0 = c0z - c0a
+    B, Hkv, Hq, d, K = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget
+    n_valid = float(np.mean(w.lengths[t0 + Wm + K_:t0 + total].sum(axis=1)))
     row = 2 * d * eb                                             # one K||V row
     # algorithmic bytes per call (one launch of the stage)
-    attn_bytes = B * lay_per_chunk[0] * Hkv * K * row + B * lay_per_chunk[0] * Hq * d * 4   # K/V read + out write
-    score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4                                  # keys read + probs write
-    copy_bytes = float(np.mean(loaded_rows)) * lay_per_chunk[0] * row                        # host reads per chunk
+    attn_bytes = B * lay0 * Hkv * K * row + B * lay0 * Hq * d * 4        # K/V read + out write
+    score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4              # keys read + probs write
+    copy_bytes = float(np.mean(loaded_rows)) * lay0 * row                # host reads per chunk
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
 
     traffic = measured_traffic(p.name, nch)
-
-    def roof(bound, nbytes, ms, peak, kernel, calls, call):
-        ach = nbytes / (ms * 1e-3) / 1e9
-        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "GB/s",
-                "frac": round(ach / peak, 4), "traffic": traffic.get(call), "kernel": kernel,
-                "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 2), "launches_per_step": calls}
-
-    result = {
-        "metric": "sparse decode steps/s (score+TopK+elastic load+attn) and % HBM peak at 32K",
-        "value": round(1e3 / ms_per_step, 2),
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": K_,
-        "warmup": Wm,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": p.dtype,
-        "data": "synthetic",
-        "config": {"workload": f"{p.name}: Llama3.1-8B-shaped decode step" if p.name == "b1_32k" else p.name,
-                   "batch": B, "layers": p.n_layers, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
-                   "cached_tokens": L, "kv_budget": K, "layer_chunks": nch,
-                   "chunk_layers": [z - a for a, z in dec.chunks], "parallelism": "single GPU"},
-        "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS,
-                         "attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K)", nch, "attn"),
-        "roofline_scores": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS,
-                                "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1, "scores"),
-        "roofline_host_link": roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS,
-                                   "copy_kernel (elastic host->HBM gather)", nch, "copy"),
+    config = {"workload": WORKLOADS.get(p.name, p.name), "batch": B, "layers": p.n_layers, "q_heads": Hq,
+              "kv_heads": Hkv, "head_dim": d, "cached_tokens": p.max_len,
+              "mean_length": round(n_valid / B, 1), "first_step": t0, "kv_budget": K, "layer_chunks": nch,
+              "chunk_layers": [z - a for a, z in dec.chunks], "parallelism": "single GPU"}
+    result = _header(args, p, ms_per_step, config)
+    result.update({
+        "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                         "attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K)", nch,
+                         traffic.get("attn")),
+        "roofline_scores": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
+                                "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1,
+                                traffic.get("scores")),
+        "roofline_host_link": roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
+                                   "copy_kernel (elastic host->HBM gather)", nch, traffic.get("copy")),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
-        "elastic": {"rows_loaded_per_step": float(np.mean(loaded_rows)), "rows_selected_per_step": float(np.mean(sel_rows)),
-                    "transfer_fraction_vs_full_reload": round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
+        "elastic": {"rows_loaded_per_step": float(np.mean(loaded_rows)),
+                    "rows_selected_per_step": float(np.mean(sel_rows)),
+                    "transfer_fraction_vs_full_reload":
+                        round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
                     "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * p.n_layers * row)},
-    }
+    })
     if args.calibrate_copy:
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -263,8 +306,126 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, w, Wm, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+        result["cpu_baseline"] = cpu_baseline(p, w, t0 + Wm, args.cpu_seconds)
+    return result
+
+
+def bench_mla(args, p, torch, W):
+    from speculative_kv_sparsity_amd import api
+    from speculative_kv_sparsity_amd.driver import MlaDecoder, StageTimer
+
+    K_, Wm = args.steps, args.warmup
+    total = Wm + 2 * K_
+    w = W.generate(p, device="cuda", seed=args.seed, steps=total)
+    dec = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+    lens = torch.as_tensor(w.lengths, device="cuda")
+    qn, qr = w.q_nope.contiguous(), w.q_rope.contiguous()
+    torch.cuda.synchronize()
+    for t in range(Wm):
+        dec.step(qn[t], qr[t], lens[t])
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(dec.main)
+    for t in range(Wm, Wm + K_):
+        dec.step(qn[t], qr[t], lens[t])
+    e1.record(dec.main)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / K_
+
+    names = ("absorb", "scores", "topk", "plan", "attn", "out_proj", "end")
+    stage = {k: [] for k in names[:-1]}
+    churn, sel_rows = [], []
+    for t in range(Wm + K_, total):
+        tm = StageTimer()
+        dec.step(qn[t], qr[t], lens[t], timer=tm)
+        torch.cuda.synchronize()
+        for a, z in zip(names[:-1], names[1:]):
+            stage[a].append(tm.ms(a, z))
+        churn.append(int(dec.load_count.sum().item()))
+        sel_rows.append(int(dec.sel_count.sum().item()))
+    avg = {k: float(np.mean(v)) for k, v in stage.items()}
+
+    tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
+    R = args.iso_reps
+    s = dec.shape
+    iso_ms = {
+        "absorb": iso(torch, lambda st: api.spc_mla_absorb_q(s, p.nope_dim, dec.w_uk, tq, tr, dec.q_abs,
+                                                             stream=st), R),
+        "scores": iso(torch, lambda st: api.spc_retrieval_scores(s, dec.q_abs, dec.latent, tl, dec.probs,
+                                                                 ws=dec.ws_scores, stream=st), R),
+        "topk": iso(torch, lambda st: api.spc_group_max_topk(s, dec.probs, tl, dec.sel_idx, dec.sel_count,
+                                                             ws=dec.ws_topk, stream=st), R),
+        "attn": iso(torch, lambda st: dec.attend(st), R),
+        "out_proj": iso(torch, lambda st: api.spc_mla_out_proj(s, p.nope_dim, dec.w_uv, dec.o_lat, 0, dec.out,
+                                                               stream=st), R),
+    }
+    B, H, L, D = p.batch, p.n_q_heads, p.max_len, p.head_dim
+    n_valid = float(np.mean(w.lengths[Wm + K_:total].sum(axis=1)))
+    sel = float(np.mean(sel_rows))
+    row = D * p.elem_bytes                                      # one latent row: 512 latent + 64 rope dims
+    attn_bytes = sel * row + B * H * p.latent_dim * 4            # each head's selected rows + o_lat writes
+    score_flop = 2.0 * n_valid * H * D                           # every head against every valid latent row
+    score_bytes = n_valid * row + n_valid * H * 4               # latent read once + probs write
+    config = {"workload": WORKLOADS["mla_32k"] if p.name == "mla_32k" else p.name, "batch": B, "layers": 1,
+              "q_heads": H, "latent_dim": p.latent_dim, "rope_dim": p.rope_dim, "nope_dim": p.nope_dim,
+              "cached_tokens": L, "kv_budget": p.budget, "parallelism": "single GPU"}
+    result = _header(args, p, ms_per_step, config)
+    result.update({
+        "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                         "attn_split_latent_kernel + attn_combine_kernel (per-head gather of the selected latent "
+                         "rows; the 151 MB latent cache is re-read from the last-level cache)", 1),
+        "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+                                "mla_scores_kernel + scores_normalize_kernel (bf16 MFMA, fp32 query as a "
+                                "hi/lo bf16 pair: 2 MFMAs per product)", 1),
+        "roofline_scores_hbm": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
+                                    "mla_scores_kernel + scores_normalize_kernel", 1),
+        "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
+        "elastic": {"rows_selected_per_step": sel, "rows_changed_per_step": float(np.mean(churn)),
+                    "resident_churn": round(float(np.mean(churn)) / sel, 4) if sel else None,
+                    "host_link_bytes_per_step": 0},
+    })
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_mla(p, w, Wm, args.cpu_seconds)
+    return result
+
+
+def cpu_baseline_mla(p, w, t, budget_s):
+    """The CPU oracle's MLA step (literal expansion of the keys and of the selected rows), timed
+    per (sequence, head) on a bounded sample and scaled to whole steps of all heads and sequences."""
+    from oracle import spc_oracle as O
+    from speculative_kv_sparsity_amd.workload import to_numpy_raw
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    C = p.latent_dim
+    lat = O.to_f64(to_numpy_raw(w.latent), "bf16")
+    w_uk = O.to_f64(to_numpy_raw(w.w_uk), "bf16")
+    w_uv = O.to_f64(to_numpy_raw(w.w_uv), "bf16")
+    qn = O.to_f64(to_numpy_raw(w.q_nope[t]), "bf16")
+    qr = O.to_f64(to_numpy_raw(w.q_rope[t]), "bf16")
+    n_done, start = 0, time.perf_counter()
+    b = 0
+    h = 0
+    while True:
+        n = int(w.lengths[t][b])
+        probs = O.mla_retrieval_scores(qn[b:b + 1], qr[b:b + 1], lat[b:b + 1, :, :C], lat[b:b + 1, :, C:], w_uk,
+                                       [n], p.scale, heads=[h])[(0, h)]
+        sel = O.topk_select(probs, n, p.budget)
+        O.mla_sparse_attention(qn[b, h], qr[b, h], lat[b, :, :C], lat[b, :, C:], w_uk, w_uv, sel, h, p.scale)
+        n_done += 1
+        h = (h + 1) % p.n_q_heads
+        if time.perf_counter() - start >= budget_s:
+            break
+    el = time.perf_counter() - start
+    per_step = el / n_done * p.batch * p.n_q_heads
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_done} (sequence 0, head) scoring + Top-K + attention evaluations of one step "
+                      f"(fp64 NumPy, keys expanded literally), {el:.1f} s, scaled by "
+                      f"{p.batch} x {p.n_q_heads} to whole steps"}
 
 
 if __name__ == "__main__":

@@ -210,13 +210,28 @@ class MlaDecoder:
         self.main = torch.cuda.current_stream(dev)
         api.spc_elastic_reset(self.shape, -1, self.slot_pos, self.resident_bm, stream=self.main)
 
-    def step(self, q_nope: torch.Tensor, q_rope: torch.Tensor, lengths: torch.Tensor) -> None:
+    def step(self, q_nope: torch.Tensor, q_rope: torch.Tensor, lengths: torch.Tensor,
+             timer: Optional["StageTimer"] = None) -> None:
+        """q_nope: device [B][H][dn]; q_rope: device [B][H][R]; lengths: device int32 [B].  Asynchronous."""
+        mark = timer.mark if timer is not None else (lambda name, stream: None)
         s, st = self.shape, self.main
+        mark("absorb", st)
         api.spc_mla_absorb_q(s, self.p.nope_dim, self.w_uk, q_nope, q_rope, self.q_abs, stream=st)
+        mark("scores", st)
         api.spc_retrieval_scores(s, self.q_abs, self.latent, lengths, self.probs, ws=self.ws_scores, stream=st)
+        mark("topk", st)
         api.spc_group_max_topk(s, self.probs, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk, stream=st)
+        mark("plan", st)
         api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
                                self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)
-        api.spc_sparse_decode_attn(s, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx, self.sel_count,
-                                   api.SPC_ROWS_GATHER, 0, 1, self.o_lat, ws=self.ws_attn, stream=st)
+        mark("attn", st)
+        self.attend()
+        mark("out_proj", st)
         api.spc_mla_out_proj(s, self.p.nope_dim, self.w_uv, self.o_lat, 0, self.out, stream=st)
+        mark("end", st)
+
+    def attend(self, stream=None) -> None:
+        """Attention of every head over its selected latent rows (gathered by position)."""
+        api.spc_sparse_decode_attn(self.shape, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx,
+                                   self.sel_count, api.SPC_ROWS_GATHER, 0, 1, self.o_lat, ws=self.ws_attn,
+                                   stream=self.main if stream is None else stream)
