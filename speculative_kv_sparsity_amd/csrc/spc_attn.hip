@@ -31,6 +31,8 @@ namespace spc {
 namespace {
 
 constexpr int kThreads = 256;                 // 4 waves
+constexpr int kLatentTilesSmall = 4;          // MLA: 16-row tiles per wave and split (few instances)
+constexpr int kLatentTilesLarge = 16;         // (enough instances x splits to fill the chip)
 
 struct QL { int64_t b, layer, head; };        // byte strides
 struct KL { int64_t b, layer, head, row, kv; };
@@ -249,18 +251,30 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 
 // MLA latent rows: V is the first DV elements of the K row; one head per group; the
 // query is the float32 absorbed query (q_l strides in float32 elements).
-template <int D, int DV, int NI>
+//
+// The per-row work is a GEMV on both sides (576 dims against the query, 512 dims
+// into the output), so the kernel keeps it on packed bf16 dot products:
+//   logits: the float32 query is held as a bf16 pair (hi + lo, ~16 mantissa bits);
+//     v_dot2_f32_bf16 of a packed pair of latent elements with the hi and with the
+//     lo pair gives two MACs per instruction with no widening of the row.
+//   output: the two rows a lane holds in a tile are interleaved per element with
+//     v_perm_b32 (row0[d], row1[d]), and dot2 against the pair of their weights
+//     (again hi + lo bf16) adds both rows' contributions to dims d at once.
+// Each wave walks T tiles of 16 rows (8 lanes per row, 2 rows per lane) with an
+// online softmax, so the 8-lane-group reduction and the cross-wave merge are paid
+// once per 64 T rows instead of once per 16.
+template <int D, int DV, int T>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
     int n_lay, int nsplit, int nhc, int max_rows, float scale, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
-  constexpr int EB = 2, EPC = 8;
-  constexpr int CPLK = D * EB / 16 / 8;
-  constexpr int CPLV = DV * EB / 16 / 8;
-  constexpr int RPW = 8 * NI, RPS = 4 * RPW;
+  constexpr int EB = 2;
+  constexpr int CPLK = D * EB / 16 / 8;              // 16-byte chunks per lane of a row (9)
+  constexpr int CPLV = DV * EB / 16 / 8;             // of them in the value part (8)
+  constexpr int RPT = 16;                            // rows per wave tile (8 lanes per row, 2 rows per lane)
+  constexpr int RPS = 4 * RPT * T;
   static_assert(CPLV <= CPLK && D * EB % 128 == 0 && DV * EB % 128 == 0, "latent row layout");
-
   const int split = blockIdx.x;
   const int inst = blockIdx.y;
   const int r = inst % n_groups;
@@ -272,11 +286,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   const int head = r * (Hq / n_groups);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int p = lane & 7, rr = lane >> 3;
-
   __shared__ int32_t sRow[RPS];
   __shared__ float s_m[4], s_l[4];
   __shared__ float red[4][DV];
-
   const int32_t* rl = rows + ((size_t)b * n_groups + r) * K;
   int cnt = K;
   if (mode == SPC_ROWS_GATHER) {
@@ -287,91 +299,109 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   for (int i = tid; i < RPS; i += kThreads) sRow[i] = split_row(rl, i0 + i, cnt, mode, max_rows);
   __syncthreads();
   const char* kbase = kv + b * kl.b + layer * kl.layer + (int64_t)kvh * kl.head;
-  int32_t row[NI];
-  Vec16 kc[NI][CPLK];
-#pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    row[it] = sRow[wid * RPW + it * 8 + rr];
-    if (row[it] >= 0) {
-      const char* kr = kbase + (int64_t)row[it] * kl.row;
-#pragma unroll
-      for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16(kr + (p + 8 * c) * 16);
-    }
-  }
-  // float32 absorbed query: the 8 elements paired with chunk c of the row
-  float qv[CPLK][EPC];
+
+  // query chunk p + 8c as hi / lo bf16 pairs
+  uint32_t qhi[CPLK][4], qlo[CPLK][4];
   const float* qh = reinterpret_cast<const float*>(q + b * ql.b + layer * ql.layer + (int64_t)head * ql.head);
 #pragma unroll
   for (int c = 0; c < CPLK; ++c) {
     const float4 a0 = *reinterpret_cast<const float4*>(qh + 8 * (p + 8 * c));
     const float4 a1 = *reinterpret_cast<const float4*>(qh + 8 * (p + 8 * c) + 4);
-    qv[c][0] = a0.x; qv[c][1] = a0.y; qv[c][2] = a0.z; qv[c][3] = a0.w;
-    qv[c][4] = a1.x; qv[c][5] = a1.y; qv[c][6] = a1.z; qv[c][7] = a1.w;
-  }
-  float lg[NI];
+    const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    float a = 0.f;
-    if (row[it] >= 0) {
+    for (int w = 0; w < 4; ++w) {
+      qhi[c][w] = pack_bf16_hi(x[2 * w], x[2 * w + 1]);
+      qlo[c][w] = pack_bf16_lo(x[2 * w], x[2 * w + 1], qhi[c][w]);
+    }
+  }
+  float M = -INFINITY, lsum = 0.f;
+  float acc[CPLV * 8];
+#pragma unroll
+  for (int e = 0; e < CPLV * 8; ++e) acc[e] = 0.f;
+
+#pragma unroll 1
+  for (int t = 0; t < T; ++t) {
+    const int base = (t * 4 + wid) * RPT;
+    int32_t row[2];
+    Vec16 kc[2][CPLK];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      row[j] = sRow[base + 8 * j + rr];
+      const char* kr = kbase + (int64_t)(row[j] >= 0 ? row[j] : 0) * kl.row;
 #pragma unroll
       for (int c = 0; c < CPLK; ++c) {
-        float x[EPC];
-        widen16<SPC_BF16>(kc[it][c], x);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) a = fmaf(x[e], qv[c][e], a);
+        if (row[j] >= 0) {
+          kc[j][c] = ld16(kr + (p + 8 * c) * 16);
+        } else {
+          kc[j][c].w[0] = kc[j][c].w[1] = kc[j][c].w[2] = kc[j][c].w[3] = 0u;   // weight 0 must not meet NaN
+        }
       }
     }
-    a = sum8(a);
-    lg[it] = row[it] >= 0 ? a * scale : -INFINITY;
-  }
-  float m = -INFINITY;
+    float lg[2];
 #pragma unroll
-  for (int it = 0; it < NI; ++it) m = fmaxf(m, lg[it]);
-  const float mw = max_across_rows8(m);
-  float sum = 0.f;
+    for (int j = 0; j < 2; ++j) {
+      float a = 0.f;
 #pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    lg[it] = lg[it] == -INFINITY ? 0.f : __expf(lg[it] - mw);
-    sum += lg[it];
-  }
-  const float lw = sum_across_rows8(sum);
-  float acc[CPLV * EPC];
+      for (int c = 0; c < CPLK; ++c)
 #pragma unroll
-  for (int e = 0; e < CPLV * EPC; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    if (row[it] >= 0) {
-#pragma unroll
-      for (int c = 0; c < CPLV; ++c) {
-        float x[EPC];
-        widen16<SPC_BF16>(kc[it][c], x);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[c * EPC + e] = fmaf(lg[it], x[e], acc[c * EPC + e]);
-      }
+        for (int w = 0; w < 4; ++w) {
+          a = dot2_bf16(kc[j][c].w[w], qhi[c][w], a);
+          a = dot2_bf16(kc[j][c].w[w], qlo[c][w], a);
+        }
+      a = sum8(a);
+      lg[j] = row[j] >= 0 ? a * scale : -INFINITY;
     }
-  }
+    // online softmax: the wave's running max, rescaling the accumulators when it grows
+    const float mt = max_across_rows8(fmaxf(lg[0], lg[1]));
+    if (mt > M) {                                     // wave-uniform
+      const float alpha = M == -INFINITY ? 0.f : __expf(M - mt);
+      lsum *= alpha;
 #pragma unroll
-  for (int e = 0; e < CPLV * EPC; ++e) acc[e] = sum_across_rows8(acc[e]);
-  if (lane == 0) { s_m[wid] = mw; s_l[wid] = lw; }
+      for (int e = 0; e < CPLV * 8; ++e) acc[e] *= alpha;
+      M = mt;
+    }
+    const float w0 = lg[0] == -INFINITY ? 0.f : __expf(lg[0] - M);
+    const float w1 = lg[1] == -INFINITY ? 0.f : __expf(lg[1] - M);
+    lsum += w0 + w1;
+    const uint32_t whi = pack_bf16_hi(w0, w1);
+    const uint32_t wlo = pack_bf16_lo(w0, w1, whi);
+#pragma unroll
+    for (int c = 0; c < CPLV; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // (row0[2w], row1[2w]) and (row0[2w+1], row1[2w+1]) of chunk c
+        const uint32_t pl = __builtin_amdgcn_perm(kc[1][c].w[w], kc[0][c].w[w], 0x05040100u);
+        const uint32_t ph = __builtin_amdgcn_perm(kc[1][c].w[w], kc[0][c].w[w], 0x07060302u);
+        float& a0 = acc[c * 8 + 2 * w];
+        float& a1 = acc[c * 8 + 2 * w + 1];
+        a0 = dot2_bf16(pl, wlo, dot2_bf16(pl, whi, a0));
+        a1 = dot2_bf16(ph, wlo, dot2_bf16(ph, whi, a1));
+      }
+  }
+  // wave totals (the 8 lanes that share p hold different rows), then the cross-wave merge
+  const float lw = sum_across_rows8(lsum);
+#pragma unroll
+  for (int e = 0; e < CPLV * 8; ++e) acc[e] = sum_across_rows8(acc[e]);
+  if (lane == 0) { s_m[wid] = M; s_l[wid] = lw; }
   __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  const float fw = mw == -INFINITY ? 0.f : __expf(mw - M);
+  const float MM = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const float fw = M == -INFINITY ? 0.f : __expf(M - MM);
   if (rr == 0) {
 #pragma unroll
     for (int c = 0; c < CPLV; ++c)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) red[wid][(p + 8 * c) * EPC + e] = acc[c * EPC + e] * fw;
+      for (int e = 0; e < 8; ++e) red[wid][(p + 8 * c) * 8 + e] = acc[c * 8 + e] * fw;
   }
   __syncthreads();
   const size_t pbase = (size_t)inst * nsplit + split;
   for (int d = tid; d < DV; d += kThreads) part_o[pbase * DV + d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
   if (tid == 0) {
     float L = 0.f;
-    if (M != -INFINITY) {
+    if (MM != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) L += s_m[w] == -INFINITY ? 0.f : s_l[w] * __expf(s_m[w] - M);
+      for (int w = 0; w < 4; ++w) L += s_m[w] == -INFINITY ? 0.f : s_l[w] * __expf(s_m[w] - MM);
     }
-    part_ml[pbase] = make_float2(M, L);
+    part_ml[pbase] = make_float2(MM, L);
   }
 }
 
@@ -443,8 +473,17 @@ int head_chunk(const spc_shape& s) {
 }
 
 // rows per split = 4 waves x 8 rows x NI of the instantiation launched below
-// (NI = 4, or 2 where registers are tight: 8 heads per workgroup, MLA rows)
-int rows_per_split(const spc_shape& s) { return (s.head_dim > 256 || head_chunk(s) >= 8) ? 64 : 128; }
+// (NI = 4, or 2 where registers are tight: 8 heads per workgroup); MLA latent rows:
+// 4 waves x 4 or 16 tiles of 16 rows (16 once the launch has >= 1024 workgroups)
+int latent_tiles(const spc_shape& s) {
+  constexpr int kLarge = 4 * 16 * kLatentTilesLarge;
+  const long wgs = (long)s.batch * s.n_layers * s.n_q_heads * ((s.budget + kLarge - 1) / kLarge);
+  return wgs >= 1024 ? kLatentTilesLarge : kLatentTilesSmall;
+}
+int rows_per_split(const spc_shape& s) {
+  if (s.head_dim > 256) return 4 * 16 * latent_tiles(s);
+  return head_chunk(s) >= 8 ? 64 : 128;
+}
 
 struct SplitArgs {
   const char* q; QL ql; const char* kv; KL kl; const int32_t* rows; const int32_t* row_count; int mode;
@@ -519,9 +558,14 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
   } else if (s.head_dim == 64) {
     e = launch_split_gqc<SPC_BF16, 64>(gqc, s, grid, st, a);
   } else if (s.head_dim == 576 && gqc == 1) {
-    attn_split_latent_kernel<576, 512, 2><<<grid, kThreads, 0, st>>>(
-        a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
-        a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
+    if (latent_tiles(s) == kLatentTilesLarge)
+      attn_split_latent_kernel<576, 512, kLatentTilesLarge><<<grid, kThreads, 0, st>>>(
+          a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
+          a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
+    else
+      attn_split_latent_kernel<576, 512, kLatentTilesSmall><<<grid, kThreads, 0, st>>>(
+          a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
+          a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;

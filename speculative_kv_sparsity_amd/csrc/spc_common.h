@@ -40,6 +40,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
+// Round-to-nearest-even bf16 of a float, as the upper 16 bits of a word.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// Packed bf16 pair (lo = a, hi = b) of two floats, and of their rounding remainders:
+// a ~= hi.lo + lo.lo and b ~= hi.hi + lo.hi to ~16 mantissa bits (finite inputs).
+__device__ __forceinline__ uint32_t pack_bf16_hi(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+__device__ __forceinline__ uint32_t pack_bf16_lo(float a, float b, uint32_t hi) {
+  return bf16_bits(a - bf_lo(hi)) | (bf16_bits(b - bf_hi(hi)) << 16);
+}
 // Dot product of two 16-byte chunks (8 bf16 or 4 fp32), accumulated into c.
 template <int DT>
 __device__ __forceinline__ float dot16(const Vec16& a, const Vec16& b, float c);
