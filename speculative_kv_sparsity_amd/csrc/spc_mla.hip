@@ -12,8 +12,8 @@
 // mla_absorb_kernel    q_abs[b][h] = (W_UK^h^T q_nope[b][h]) || q_rope[b][h], float32.
 // mla_scores_kernel    logits[b][h][j] = scale * q_abs[b][h] . latent[b][j] for all 128
 //   heads at once: a dense [heads x 576] x [576 x positions] contraction on MFMA
-//   (v_mfma_f32_16x16x32_bf16).  Each of 8 waves owns 16 heads; a tile of latent
-//   rows is staged in LDS and shared by the waves.  The float32 query is split
+//   (v_mfma_f32_16x16x32_bf16).  Each of 4 waves owns 16 heads; a tile of latent
+//   rows is staged in LDS (double-buffered) and shared by the waves.  The float32 query is split
 //   into bf16 hi + lo parts (two MFMA passes), which keeps ~16 mantissa bits of
 //   the query while the latent rows are bf16 already.  Per-tile (max, sum exp)
 //   partials feed the shared normalize kernel of the scores stage.
@@ -30,9 +30,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMlaD = kMlaLatent + kMlaRope;      // 576 scored dims
 constexpr int kKSteps = kMlaD / 32;                // MFMA k-steps of 32
-constexpr int kSub = 64;                           // latent rows staged in LDS at a time
+constexpr int kSub = 32;                           // latent rows per LDS buffer
 constexpr int kLdsRow = kMlaD + 8;                 // padded row (elements): spreads rows over banks
-constexpr int kScoreThreads = 512;                 // 8 waves x 16 heads
+constexpr int kScoreThreads = 256;                 // 4 waves x 16 heads
 static_assert(kMlaD % 32 == 0, "k-steps of 32");
 
 // One workgroup per head.  Lane l owns latent dims 8l..8l+7 (one 16-byte chunk of
@@ -114,25 +114,38 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
   m = M;
 }
 
-__global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* __restrict__ q_abs,
+// Workgroup = (sequence, kScoreTile positions, 64 heads): 4 waves x 16 heads, two
+// workgroups per CU.  The tile is staged 32 rows at a time through two LDS
+// buffers, so one barrier per sub-tile separates the MFMAs on one buffer from the
+// staging of the next sub-tile into the other.  The two workgroups
+// of the 128 heads of one tile get block ids 8 apart, which the dispatcher's
+// round-robin over the 8 XCDs places on the same XCD, so the second reads the
+// tile from that L2.
+__global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const float* __restrict__ q_abs,
                                                                    const uint16_t* __restrict__ lat,
                                                                    const int32_t* __restrict__ lengths,
                                                                    float* __restrict__ probs,
                                                                    float2* __restrict__ part, int H, int max_len,
-                                                                   int ntiles, float scale) {
-  __shared__ uint16_t sl[kSub * kLdsRow];
-  const int b = blockIdx.y, tile = blockIdx.x;
+                                                                   int ntiles, int nhg, float scale) {
+  __shared__ uint16_t sl[2][kSub * kLdsRow];
+  // block id -> (tile, head group): groups of 8 * nhg ids hold 8 tiles x nhg head groups
+  const int id = blockIdx.x;
+  const int grp = id / (8 * nhg), in = id - grp * 8 * nhg;
+  const int hg = in / 8, tile = grp * 8 + (in & 7);
+  const int b = blockIdx.y;
+  if (tile >= ntiles) return;
   const int n = clamp_len(lengths, b, max_len);
   const int row0 = tile * kScoreTile;
   if (row0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nw = H / 16;                           // waves that own heads
+  const int hbase = hg * 64 + 16 * wid;              // first head of this wave
+  const bool active = hbase < H;
   const int kc = lane >> 4, col = lane & 15;
 
-  // this lane's query fragments (head 16*wid + col, k-chunk kc of every k-step), hi and lo parts
-  bf16x8_t ahi[kKSteps], alo[kKSteps];
-  if (wid < nw) {
-    const float* qa = q_abs + ((size_t)b * H + 16 * wid + col) * kMlaD;
+  // this lane's query fragments (head hbase + col, k-chunk kc of every k-step), hi and lo parts
+  bf16x8_t ahi[kKSteps], alo[kKSteps];   // 144 VGPRs: the budget that fixes 2 workgroups per CU
+  if (active) {
+    const float* qa = q_abs + ((size_t)b * H + hbase + col) * kMlaD;
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) {
       const float4 x0 = *reinterpret_cast<const float4*>(qa + 32 * s + 8 * kc);
@@ -151,14 +164,13 @@ __global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* 
   for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
 
   constexpr int kChunks = kMlaD * 2 / 16;          // 16-byte chunks per latent row
+  constexpr int kPer = kSub * kChunks / kScoreThreads;
+  static_assert(kSub * kChunks % kScoreThreads == 0, "sub-tile load split");
   const uint16_t* lb = lat + (size_t)b * max_len * kMlaD;
-#pragma unroll 1
-  for (int sub = 0; sub < kScoreTile / kSub; ++sub) {
+  const int nsub = min(kScoreTile, n - row0 + kSub - 1) / kSub;   // sub-tiles with valid rows
+  uint4 v[kPer];
+  auto load = [&](int sub) {
     const int p_sub = row0 + sub * kSub;
-    if (p_sub >= n) break;
-    __syncthreads();                               // previous sub-tile fully consumed
-    constexpr int kPer = kSub * kChunks / kScoreThreads;
-    uint4 v[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + u * kScoreThreads;
@@ -166,20 +178,29 @@ __global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* 
       v[u] = p_sub + r < n ? *reinterpret_cast<const uint4*>(lb + (size_t)(p_sub + r) * kMlaD + 8 * ch)
                            : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + u * kScoreThreads;
       const int r = c / kChunks, ch = c - (c / kChunks) * kChunks;
-      *reinterpret_cast<uint4*>(&sl[r * kLdsRow + 8 * ch]) = v[u];
+      *reinterpret_cast<uint4*>(&sl[buf][r * kLdsRow + 8 * ch]) = v[u];
     }
-    __syncthreads();
-    if (wid < nw) {
+  };
+  load(0);
+  stage(0);
+  __syncthreads();
 #pragma unroll 1
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int buf = sub & 1;
+
+    if (active) {
+      const int p_sub = row0 + sub * kSub;
+#pragma unroll
       for (int blk = 0; blk < kSub / 16; ++blk) {
         const int p0 = p_sub + 16 * blk;
-        if (p0 >= n) break;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* srow = &sl[(16 * blk + col) * kLdsRow + 8 * kc];
+        const uint16_t* srow = &sl[buf][(16 * blk + col) * kLdsRow + 8 * kc];
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
           const bf16x8_t bfrag = *reinterpret_cast<const bf16x8_t*>(srow + 32 * s);
@@ -190,7 +211,7 @@ __global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* 
         if (pos < n) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int h = 16 * wid + 4 * kc + i;
+            const int h = hbase + 4 * kc + i;
             const float l = acc[i] * scale;
             probs[((size_t)b * H + h) * max_len + pos] = l;
             online_ms(m_run[i], s_run[i], l);
@@ -198,8 +219,10 @@ __global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* 
         }
       }
     }
+    if (sub + 1 < nsub) { load(sub + 1); stage(buf ^ 1); }
+    __syncthreads();
   }
-  if (wid < nw) {
+  if (active) {
     // merge (max, sum) over the 16 lanes of each row group (the tile's positions)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -209,7 +232,7 @@ __global__ __launch_bounds__(kScoreThreads) void mla_scores_kernel(const float* 
         const float s2 = __shfl_xor(s_run[i], o, kWave);
         merge_ms(m_run[i], s_run[i], m2, s2);
       }
-      if (col == 0) part[((size_t)b * H + 16 * wid + 4 * kc + i) * ntiles + tile] = make_float2(m_run[i], s_run[i]);
+      if (col == 0) part[((size_t)b * H + hbase + 4 * kc + i) * ntiles + tile] = make_float2(m_run[i], s_run[i]);
     }
   }
 }
@@ -275,8 +298,11 @@ hipError_t launch_mla_scores(const spc_shape& s, const float* q_abs, const void*
                              float* probs, void* ws, hipStream_t st) {
   const int ntiles = (s.max_len + kScoreTile - 1) / kScoreTile;
   float2* part = static_cast<float2*>(ws);
-  mla_scores_kernel<<<dim3(ntiles, s.batch), kScoreThreads, 0, st>>>(
-      q_abs, static_cast<const uint16_t*>(latent), lengths, probs, part, s.n_q_heads, s.max_len, ntiles, s.scale);
+  const int nhg = (s.n_q_heads + 63) / 64;         // head groups of 64
+  const int ngrp = (ntiles + 7) / 8;
+  mla_scores_kernel<<<dim3(ngrp * 8 * nhg, s.batch), kScoreThreads, 0, st>>>(
+      q_abs, static_cast<const uint16_t*>(latent), lengths, probs, part, s.n_q_heads, s.max_len, ntiles, nhg,
+      s.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_scores_normalize(s, probs, part, lengths, ntiles, st);
