@@ -12,7 +12,9 @@
 //
 // topk_keys_kernel    many workgroups per (b, g), kKeyChunk positions each:
 //   takes the group max while reading the heads' rows once, writes the keys to
-//   the workspace and the chunk's histogram of the top 8 key bits.
+//   the workspace and the chunk's histogram of the top 8 key bits.  With one
+//   head per group (MHA, MLA) the keys are not written: the select kernel maps
+//   the probabilities to keys as it loads them.
 // topk_select_kernel  one 1024-thread workgroup per (b, g): sums the chunk
 //   histograms (first digit), runs the two remaining 12-bit passes with LDS
 //   histograms over the keys that still match the prefix, and compacts every j
@@ -36,6 +38,13 @@ constexpr int kBins1 = 256;                       // first digit: key bits 31..2
 __device__ __forceinline__ uint32_t order_key(float v) {
   const uint32_t u = __float_as_uint(v);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Keys of 4 loaded words: the words themselves, or (RAW) the keys of 4 fp32 values.
+template <bool RAW>
+__device__ __forceinline__ uint4 to_keys(uint4 w) {
+  if (!RAW) return w;
+  return make_uint4(order_key(__uint_as_float(w.x)), order_key(__uint_as_float(w.y)), order_key(__uint_as_float(w.z)),
+                    order_key(__uint_as_float(w.w)));
 }
 
 __global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __restrict__ probs,
@@ -77,7 +86,7 @@ __global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __r
     const int j = j0 + threadIdx.x + u * kKeyThreads;
     if (j < j1) {
       const uint32_t key = order_key(v[u]);
-      kout[j] = key;
+      if (Gq > 1) kout[j] = key;      // one head per group: the select kernel keys the probabilities itself
       atomicAdd(&h[key >> 24], 1u);
     }
   }
@@ -119,7 +128,7 @@ __device__ __forceinline__ int vslot(int v) { return v ^ ((v >> 3) & 7); }
 
 // Radix passes 2 and 3 plus the ordered compaction, shared by both key sources.
 // key_vec(v) returns keys 4v..4v+3 (entries >= n are ignored).
-template <bool IN_LDS>
+template <bool IN_LDS, bool RAW>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t* __restrict__ keys,
                                                                   const uint32_t* __restrict__ chist,
                                                                   const int32_t* __restrict__ lengths,
@@ -164,14 +173,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
       const int i4 = tid + u * kSelThreads;
-      if (i4 < nv) skeys[vslot(i4)] = v[u];
+      if (i4 < nv) skeys[vslot(i4)] = to_keys<RAW>(v[u]);
     }
   }
   auto key_vec = [&](int v) -> uint4 {
     if (IN_LDS) return skeys[vslot(v)];
     const int j = 4 * v;
-    if (aligned && j + 3 < n) return reinterpret_cast<const uint4*>(kin)[v];
-    return make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u, j + 3 < n ? kin[j + 3] : 0u);
+    if (aligned && j + 3 < n) return to_keys<RAW>(reinterpret_cast<const uint4*>(kin)[v]);
+    return to_keys<RAW>(
+        make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u, j + 3 < n ? kin[j + 3] : 0u));
   };
 
   // first digit from the chunk histograms: thread t sums bin t % 256 over the
@@ -311,6 +321,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
 // digit is above the threshold digit (always selected) and those equal to it
 // (candidates), and histograms the candidates' second digit.  Every later step
 // touches only the candidates.
+template <bool RAW>
 __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint32_t* __restrict__ keys,
                                                                       const uint32_t* __restrict__ chist,
                                                                       const int32_t* __restrict__ lengths,
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
     const int i4 = tid + u * kSelThreads;
-    if (i4 < nv) skeys[vslot(i4)] = v[u];
+    if (i4 < nv) skeys[vslot(i4)] = to_keys<RAW>(v[u]);
   }
   for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
@@ -475,12 +486,25 @@ hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* le
                                                                s.n_groups, s.max_len, s.budget, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (s.max_len <= kTopkLdsKeys)
-    topk_select_lds_kernel<<<dim3(inst), kSelThreads, 0, st>>>(keys, chist, lengths, sel_idx, sel_count,
-                                                               s.n_groups, s.max_len, s.budget, nchunk);
-  else
-    topk_select_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(keys, chist, lengths, sel_idx, sel_count,
-                                                                  s.n_groups, s.max_len, s.budget, nchunk);
+  // one head per group: the keys are the probabilities' own order keys, taken on load
+  const bool raw = s.n_q_heads == s.n_groups;
+  const uint32_t* kin = raw ? reinterpret_cast<const uint32_t*>(probs) : keys;
+  if (s.max_len <= kTopkLdsKeys) {
+    if (raw)
+      topk_select_lds_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                       s.n_groups, s.max_len, s.budget, nchunk);
+    else
+      topk_select_lds_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                        s.n_groups, s.max_len, s.budget, nchunk);
+  } else {
+    if (raw)
+      topk_select_kernel<false, true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                          s.n_groups, s.max_len, s.budget, nchunk);
+    else
+      topk_select_kernel<false, false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
+                                                                           sel_count, s.n_groups, s.max_len,
+                                                                           s.budget, nchunk);
+  }
   return hipGetLastError();
 }
 
