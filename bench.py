@@ -46,7 +46,7 @@ WORKLOADS = {
     "b1_32k": "b1_32k: Llama3.1-8B-shaped decode step",
     "b16_grow": "b16_grow: batch 16 reasoning growth, 32 layers, ragged lengths growing to 16384, budget 1024",
     "mha_64k": "mha_64k: MHA 32 q-heads = 32 KV heads, 65536 cached tokens, batch 2, budget 4096, 1 layer",
-    "mla_32k": "mla_32k: MLA 128 heads, latent 512 + rope 64, 32768 cached tokens, batch 4, budget 2048",
+    "mla_32k": "mla_32k: MLA 128 heads, latent 512 + rope 64, 32768 cached tokens, batch 4, budget 2048, 1 layer",
 }
 
 
@@ -135,6 +135,15 @@ def roof(bound, amount, ms, peak, unit, kernel, calls, traffic=None):
            "traffic": traffic, "kernel": kernel, "avg_launch_us": round(ms * 1e3, 2), "launches_per_step": calls}
     rec["bytes_per_launch" if unit == "GB/s" else "flop_per_launch"] = int(amount)
     return rec
+
+
+def calibration_copies(torch):
+    """Three 256 MiB device-to-device copies: the known-size reference of the counter passes."""
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(p, w, t0, budget_s):
@@ -300,11 +309,7 @@ def bench_gqa(args, p, torch, W):
                     "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * p.n_layers * row)},
     })
     if args.calibrate_copy:
-        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copies(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, w, t0 + Wm, args.cpu_seconds)
     return result
@@ -367,6 +372,7 @@ def bench_mla(args, p, torch, W):
     attn_bytes = sel * row + B * H * p.latent_dim * 4            # each head's selected rows + o_lat writes
     score_flop = 2.0 * n_valid * H * D                           # every head against every valid latent row
     score_bytes = n_valid * row + n_valid * H * 4               # latent read once + probs write
+    traffic = measured_traffic(p.name, 1)
     config = {"workload": WORKLOADS["mla_32k"] if p.name == "mla_32k" else p.name, "batch": B, "layers": 1,
               "q_heads": H, "latent_dim": p.latent_dim, "rope_dim": p.rope_dim, "nope_dim": p.nope_dim,
               "cached_tokens": L, "kv_budget": p.budget, "parallelism": "single GPU"}
@@ -374,18 +380,20 @@ def bench_mla(args, p, torch, W):
     result.update({
         "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
                          "attn_split_latent_kernel + attn_combine_kernel (per-head gather of the selected latent "
-                         "rows; the 151 MB latent cache is re-read from the last-level cache)", 1),
+                         "rows; the 151 MB latent cache is re-read from the last-level cache)", 1, traffic.get("attn")),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                 "mla_scores_kernel + scores_normalize_kernel (bf16 MFMA, fp32 query as a "
                                 "hi/lo bf16 pair: 2 MFMAs per product)", 1),
         "roofline_scores_hbm": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                    "mla_scores_kernel + scores_normalize_kernel", 1),
+                                    "mla_scores_kernel + scores_normalize_kernel", 1, traffic.get("scores")),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
         "elastic": {"rows_selected_per_step": sel, "rows_changed_per_step": float(np.mean(churn)),
                     "resident_churn": round(float(np.mean(churn)) / sel, 4) if sel else None,
                     "host_link_bytes_per_step": 0},
     })
+    if args.calibrate_copy:
+        calibration_copies(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_mla(p, w, Wm, args.cpu_seconds)
     return result
