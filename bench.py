@@ -340,7 +340,7 @@ def bench_mla(args, p, torch, W):
 
     names = ("absorb", "scores", "topk", "plan", "attn", "out_proj", "end")
     stage = {k: [] for k in names[:-1]}
-    churn, sel_rows = [], []
+    churn, sel_rows, union_rows = [], [], []
     for t in range(Wm + K_, total):
         tm = StageTimer()
         dec.step(qn[t], qr[t], lens[t], timer=tm)
@@ -349,6 +349,8 @@ def bench_mla(args, p, torch, W):
             stage[a].append(tm.ms(a, z))
         churn.append(int(dec.load_count.sum().item()))
         sel_rows.append(int(dec.sel_count.sum().item()))
+        # distinct latent rows selected by any head of a sequence: what the attention must read at least once
+        union_rows.append(sum(int(torch.unique(x[x >= 0]).numel()) for x in dec.sel_idx))
     avg = {k: float(np.mean(v)) for k, v in stage.items()}
 
     tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
@@ -368,8 +370,10 @@ def bench_mla(args, p, torch, W):
     B, H, L, D = p.batch, p.n_q_heads, p.max_len, p.head_dim
     n_valid = float(np.mean(w.lengths[Wm + K_:total].sum(axis=1)))
     sel = float(np.mean(sel_rows))
+    union = float(np.mean(union_rows))
     row = D * p.elem_bytes                                      # one latent row: 512 latent + 64 rope dims
-    attn_bytes = sel * row + B * H * p.latent_dim * 4            # each head's selected rows + o_lat writes
+    attn_bytes = union * row + B * H * p.latent_dim * 4          # every selected row once + o_lat writes
+    gathered = sel * row                                         # each head's own gather (L2 / last-level cache)
     score_flop = 2.0 * n_valid * H * D                           # every head against every valid latent row
     score_bytes = n_valid * row + n_valid * H * 4               # latent read once + probs write
     traffic = measured_traffic(p.name, 1)
@@ -378,9 +382,11 @@ def bench_mla(args, p, torch, W):
               "cached_tokens": L, "kv_budget": p.budget, "parallelism": "single GPU"}
     result = _header(args, p, ms_per_step, config)
     result.update({
-        "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
-                         "attn_split_latent_kernel + attn_combine_kernel (per-head gather of the selected latent "
-                         "rows; the 151 MB latent cache is re-read from the last-level cache)", 1, traffic.get("attn")),
+        "roofline": dict(roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                              "attn_split_latent_kernel + attn_combine_kernel (each head gathers its selected latent "
+                              "rows; a row selected by several heads is counted once here)", 1, traffic.get("attn")),
+                         gathered_bytes_per_launch=int(gathered),
+                         gathered_GBs=round(gathered / (iso_ms["attn"] * 1e-3) / 1e9, 1)),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                 "mla_scores_kernel + scores_normalize_kernel (bf16 MFMA, fp32 query as a "
                                 "hi/lo bf16 pair: 2 MFMAs per product)", 1),
@@ -388,7 +394,8 @@ def bench_mla(args, p, torch, W):
                                     "mla_scores_kernel + scores_normalize_kernel", 1, traffic.get("scores")),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
-        "elastic": {"rows_selected_per_step": sel, "rows_changed_per_step": float(np.mean(churn)),
+        "elastic": {"rows_selected_per_step": sel, "distinct_rows_per_step": union,
+                    "rows_changed_per_step": float(np.mean(churn)),
                     "resident_churn": round(float(np.mean(churn)) / sel, 4) if sel else None,
                     "host_link_bytes_per_step": 0},
     })
