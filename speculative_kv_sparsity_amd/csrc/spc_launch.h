@@ -44,7 +44,7 @@ hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* le
 // ---- stage 3: elastic plan / copy / reset
 constexpr int kPlanMaxBudget = 8192;
 constexpr int kCopyMaxInstances = 4096;
-constexpr int kCopyBlocksDefault = 32;   // workgroups of the gather (override: SPC_COPY_BLOCKS)
+constexpr int kCopyBlocksDefault = 48;   // workgroups of the gather (override: SPC_COPY_BLOCKS)
 hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
                        uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
                        hipStream_t st);
