@@ -146,6 +146,17 @@ __global__ __launch_bounds__(kThreads) void scores_normalize_kernel(float* __res
   const int j0 = blockIdx.x * kNormChunk;
   if (j0 >= n) return;
   const int nt = (n + kScoreTile - 1) / kScoreTile;
+  // this workgroup's logits are loaded first: they do not depend on the head's (max, sum), so
+  // both round trips overlap
+  float* pr = probs + (size_t)bh * max_len;
+  const int j1 = min(j0 + kNormChunk, n);
+  constexpr int kPer = kNormChunk / kThreads;
+  float x[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = j0 + threadIdx.x + u * kThreads;
+    x[u] = j < j1 ? pr[j] : 0.f;
+  }
   float m = -INFINITY, s = 0.f;
   for (int t = threadIdx.x; t < nt; t += kThreads) {
     const float2 v = part[(size_t)bh * ntiles + t];
@@ -165,15 +176,6 @@ __global__ __launch_bounds__(kThreads) void scores_normalize_kernel(float* __res
 #pragma unroll
   for (int w = 1; w < 4; ++w) combine_ms(m, s, sm[w], ss[w]);
   const float inv = 1.f / s;
-  float* pr = probs + (size_t)bh * max_len;
-  const int j1 = min(j0 + kNormChunk, n);
-  constexpr int kPer = kNormChunk / kThreads;
-  float x[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int j = j0 + threadIdx.x + u * kThreads;
-    x[u] = j < j1 ? pr[j] : 0.f;
-  }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int j = j0 + threadIdx.x + u * kThreads;
