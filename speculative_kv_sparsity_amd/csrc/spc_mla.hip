@@ -114,7 +114,7 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
   m = M;
 }
 
-// Workgroup = (sequence, kScoreTile positions, 64 heads): 4 waves x 16 heads, two
+// Workgroup = (sequence, kMlaScoreTile positions, 64 heads): 4 waves x 16 heads, two
 // workgroups per CU.  The tile is staged 32 rows at a time through two LDS
 // buffers, so one barrier per sub-tile separates the MFMAs on one buffer from the
 // staging of the next sub-tile into the other.  The two workgroups
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
   const int b = blockIdx.y;
   if (tile >= ntiles) return;
   const int n = clamp_len(lengths, b, max_len);
-  const int row0 = tile * kScoreTile;
+  const int row0 = tile * kMlaScoreTile;
   if (row0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int hbase = hg * 64 + 16 * wid;              // first head of this wave
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
   constexpr int kPer = kSub * kChunks / kScoreThreads;
   static_assert(kSub * kChunks % kScoreThreads == 0, "sub-tile load split");
   const uint16_t* lb = lat + (size_t)b * max_len * kMlaD;
-  const int nsub = min(kScoreTile, n - row0 + kSub - 1) / kSub;   // sub-tiles with valid rows
+  const int nsub = min(kMlaScoreTile, n - row0 + kSub - 1) / kSub;   // sub-tiles with valid rows
   uint4 v[kPer];
   auto load = [&](int sub) {
     const int p_sub = row0 + sub * kSub;
@@ -296,7 +296,7 @@ hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void*
 
 hipError_t launch_mla_scores(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
                              float* probs, void* ws, hipStream_t st) {
-  const int ntiles = (s.max_len + kScoreTile - 1) / kScoreTile;
+  const int ntiles = (s.max_len + kMlaScoreTile - 1) / kMlaScoreTile;
   float2* part = static_cast<float2*>(ws);
   const int nhg = (s.n_q_heads + 63) / 64;         // head groups of 64
   const int ngrp = (ntiles + 7) / 8;

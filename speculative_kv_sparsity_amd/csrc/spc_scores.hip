@@ -11,8 +11,9 @@
 //       8 lanes cooperate on a row: lane p holds the 16-byte chunks p, p+8, ...
 //       so one wave load instruction covers 8 rows x 128 contiguous bytes (full
 //       cache lines).  bf16 dot products use v_dot2_f32_bf16 on packed pairs
-//       (no widening), the 8-lane sum uses DPP.  The logits go to `probs`; the
-//       tile's per-head (max, sum exp) go to the workspace.
+//       (no widening), the 8-lane sum uses DPP.  The tile's logits are
+//       gathered per head in LDS and written to `probs` as whole 16-byte
+//       vectors; the tile's per-head (max, sum exp) go to the workspace.
 //   scores_normalize_kernel combines the tile partials of a head into
 //       (max, sum) and rewrites its logits in place as exp(l - max) / sum.
 #include "spc_common.h"
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
     }
 
   const char* kb = k + ((size_t)b * Hkv + g) * (size_t)max_len * RB;
-  float* pb = probs + ((size_t)b * Hq + h0 + (p < nh ? p : 0)) * (size_t)max_len;
+  __shared__ __align__(16) float slg[HC][kScoreTile];   // the tile's logits per head, for coalesced writes
   float lg[kIters];
 
 #pragma unroll
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
       mine *= scale;
       const bool ok = row < n && p < nh;
       lg[u0 + u] = ok ? mine : -INFINITY;
-      if (ok) pb[row] = mine;
+      if (p < HC) slg[p][row - row0] = mine;
     }
   }
 
@@ -114,6 +115,20 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
   m = max_across_rows8(m);
   if (rr == 0) s_m[wid][p] = m;
   __syncthreads();
+  // logits of the valid rows: 16-byte stores where four rows are valid and the row start is aligned
+  {
+    const int nrow = min(kScoreTile, n - row0);
+    const bool vec = (max_len & 3) == 0;
+    for (int i = threadIdx.x; i < nh * (kScoreTile / 4); i += kThreads) {
+      const int h = i / (kScoreTile / 4), r4 = 4 * (i - h * (kScoreTile / 4));
+      float* dst = probs + ((size_t)b * Hq + h0 + h) * (size_t)max_len + row0 + r4;
+      if (vec && r4 + 3 < nrow) {
+        *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(&slg[h][r4]);
+      } else {
+        for (int e = 0; e < 4 && r4 + e < nrow; ++e) dst[e] = slg[h][r4 + e];
+      }
+    }
+  }
   const float M = fmaxf(fmaxf(s_m[0][p], s_m[1][p]), fmaxf(s_m[2][p], s_m[3][p]));
   float sum = 0.f;
   if (M != -INFINITY) {
@@ -139,13 +154,13 @@ __device__ __forceinline__ void combine_ms(float& m, float& s, float m2, float s
 __global__ __launch_bounds__(kThreads) void scores_normalize_kernel(float* __restrict__ probs,
                                                                     const float2* __restrict__ part,
                                                                     const int32_t* __restrict__ lengths, int Hq,
-                                                                    int max_len, int ntiles) {
+                                                                    int max_len, int ntiles, int tile) {
   const int bh = blockIdx.y;
   const int b = bh / Hq;
   const int n = clamp_len(lengths, b, max_len);
   const int j0 = blockIdx.x * kNormChunk;
   if (j0 >= n) return;
-  const int nt = (n + kScoreTile - 1) / kScoreTile;
+  const int nt = (n + tile - 1) / tile;
   // this workgroup's logits are loaded first: they do not depend on the head's (max, sum), so
   // both round trips overlap
   float* pr = probs + (size_t)bh * max_len;
@@ -223,15 +238,18 @@ bool scores_supported(const spc_shape& s) {
   return s.head_dim == 64 || s.head_dim == 128 || s.head_dim == 256;
 }
 
+int score_tile(const spc_shape& s) { return mla_shape(s) ? kMlaScoreTile : kScoreTile; }
+
 hipError_t launch_scores_normalize(const spc_shape& s, float* probs, const float2* part, const int32_t* lengths,
                                    int ntiles, hipStream_t st) {
   const dim3 g2((s.max_len + kNormChunk - 1) / kNormChunk, s.batch * s.n_q_heads);
-  scores_normalize_kernel<<<g2, kThreads, 0, st>>>(probs, part, lengths, s.n_q_heads, s.max_len, ntiles);
+  scores_normalize_kernel<<<g2, kThreads, 0, st>>>(probs, part, lengths, s.n_q_heads, s.max_len, ntiles,
+                                                   score_tile(s));
   return hipGetLastError();
 }
 
 size_t scores_ws_bytes(const spc_shape& s) {
-  const size_t ntiles = (size_t)(s.max_len + kScoreTile - 1) / kScoreTile;
+  const size_t ntiles = (size_t)(s.max_len + score_tile(s) - 1) / score_tile(s);
   return (size_t)s.batch * s.n_q_heads * ntiles * sizeof(float2);
 }
 

@@ -84,9 +84,19 @@ def test_null_pointers_and_small_workspace_rejected():
 def test_workspace_sizes():
     lib = L.lib()
     s = _shape(batch=2, max_len=32768, budget=2048, n_layers=32)
-    assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(s)) == 2 * 32 * 128 * 8
+    # one (max, sum) pair per head and tile of 128 positions (MLA scoring: tiles of 256)
+    assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(s)) == 2 * 32 * 256 * 8
     # one (max, sum) pair and one v_dim vector per head, layer and split of 128 rows
     assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s)) == 2 * 32 * 32 * 16 * (128 * 4 + 8)
     # keys (one uint32 per position) + 256-bin histograms per 1024-position chunk
     assert lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s)) == 2 * 8 * (32768 * 4 + 32 * 256 * 4)
     assert lib.spc_workspace_size(L.SPC_CALL_ELASTIC, ctypes.byref(s)) == 0
+    # MLA: 4 sequences, 128 heads over one shared latent head (576 scored dims, 512 value dims)
+    m = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+               budget=2048, scale=192 ** -0.5)
+    assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(m)) == 4 * 128 * 128 * 8
+    # 1024-row splits once the launch has >= 1024 workgroups (4 x 128 x 2 here)
+    assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(m)) == 4 * 128 * 2 * (512 * 4 + 8)
+    small = _shape(batch=1, n_q_heads=16, n_kv_heads=1, n_groups=16, head_dim=576, v_dim=512, max_len=4096,
+                   budget=512, scale=192 ** -0.5)
+    assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(small)) == 16 * 2 * (512 * 4 + 8)   # 256-row splits
