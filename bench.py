@@ -209,7 +209,7 @@ def _header(args, p, ms_per_step, config):
 
 def bench_gqa(args, p, torch, W):
     from speculative_kv_sparsity_amd import api
-    from speculative_kv_sparsity_amd.driver import SparseDecoder, StageTimer
+    from speculative_kv_sparsity_amd.driver import RetrievalHead, SparseDecoder, StageTimer
 
     K_, Wm = args.steps, args.warmup
     total = Wm + 2 * K_
@@ -273,6 +273,12 @@ def bench_gqa(args, p, torch, W):
                                                              plan_stream=st, copy_stream=st),
                     max(5, R // 3)),   # rewrites the same slots
     }
+    # the retrieval head's front end (upstream of the step): new tokens -> query, key appended
+    fw = W.generate_front(p, device="cuda", seed=args.seed, steps=1)
+    head = RetrievalHead(dec.shape, fw)
+    q_front = torch.empty((p.batch, p.n_q_heads, p.head_dim), dtype=p.torch_dtype, device="cuda")
+    tok = torch.as_tensor(fw.tokens[0], device="cuda")
+    iso_ms["front"] = iso(torch, lambda st: head(tok, tl, q_front, dec.dlm_k, stream=st), R)
 
     eb = p.elem_bytes
     lay0 = c0z - c0a
@@ -283,6 +289,7 @@ def bench_gqa(args, p, torch, W):
     attn_bytes = B * lay0 * Hkv * K * row + B * lay0 * Hq * d * 4        # K/V read + out write
     score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4              # keys read + probs write
     copy_bytes = float(np.mean(loaded_rows)) * lay0 * row                # host reads per chunk
+    front_bytes = ((Hq + Hkv) * d * fw.hidden + B * fw.hidden + fw.hidden + B * (Hq + Hkv) * d) * eb
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
 
     traffic = measured_traffic(p.name, nch)
@@ -300,6 +307,10 @@ def bench_gqa(args, p, torch, W):
                                 traffic.get("scores")),
         "roofline_host_link": roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
                                    "copy_kernel (elastic host->HBM gather)", nch, traffic.get("copy")),
+        "roofline_front_end": roof("hbm", front_bytes, iso_ms["front"], HBM_PEAK_GBS, "GB/s",
+                                   "front_gemv_kernel + front_finish_kernel (retrieval-head front end: embedding, "
+                                   f"input norm, Q/K projection of hidden {fw.hidden}, YaRN rotary, key append; "
+                                   "upstream of the step, not in value)", 1, traffic.get("front")),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
         "elastic": {"rows_loaded_per_step": float(np.mean(loaded_rows)),

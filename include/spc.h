@@ -92,7 +92,21 @@ typedef struct spc_q_layout {
 } spc_q_layout;
 
 /* which_call for spc_workspace_size */
-enum { SPC_CALL_SCORES = 1, SPC_CALL_TOPK = 2, SPC_CALL_ELASTIC = 3, SPC_CALL_ATTN = 4 };
+enum { SPC_CALL_SCORES = 1, SPC_CALL_TOPK = 2, SPC_CALL_ELASTIC = 3, SPC_CALL_ATTN = 4, SPC_CALL_FRONT = 5 };
+
+/* Rotary position embedding of the retrieval head (spc_retrieval_head_qk): frequencies
+ * theta_i = base^(-2i/d) on the dimension pairs (i, i + d/2), extended by YaRN when
+ * factor > 1 (Peng et al. 2023, "NTK-by-parts"): with r_i = orig_max_pos * theta_i / (2 pi)
+ * rotations over the trained context and ramp = clamp((r_i - beta_slow) / (beta_fast -
+ * beta_slow), 0, 1), theta'_i = ramp * theta_i + (1 - ramp) * theta_i / factor, and q and k
+ * are both multiplied by 0.1 ln(factor) + 1. */
+typedef struct spc_rope {
+  float base;            /* rotary base */
+  float factor;          /* YaRN context scale; <= 1 gives plain rotary embedding */
+  int32_t orig_max_pos;  /* context length the frequencies were trained for (> 0) */
+  float beta_fast;       /* ramp end (rotations), > beta_slow */
+  float beta_slow;       /* ramp start (rotations) */
+} spc_rope;
 
 /* flags of spc_elastic_update */
 enum { SPC_PLAN = 1u, SPC_COPY = 2u };
@@ -111,6 +125,33 @@ const char* spc_last_error(void);
 
 /* Bytes of scratch the call needs for this shape (0 if none). */
 size_t spc_workspace_size(int which_call, const spc_shape* s);
+
+/*
+ * Retrieval-head front end, upstream of stage 1 (SpeContext blog section 5 "C1":
+ * the retrieval head keeps the distilled model's embedding and Query/Key
+ * projections; paper summary section 4.1: EAGLE-3's single decoder layer, its 2K
+ * context extended with training-free YaRN; section 4.3).  For each sequence b
+ * with new token t = tokens[b] at position p = positions[b]:
+ *   x = emb[t];  x^ = gamma * x / sqrt(mean(x^2) + eps)       (the layer's input norm)
+ *   q = rope_p(W_q x^) -> q_out[b]                            [H_q][head_dim]
+ *   k = rope_p(W_k x^) -> dlm_k[b][g][p] for 0 <= p < max_len [H_kv][head_dim]
+ * rope_p rotates the pairs (i, i + head_dim/2) by p * theta'_i (see spc_rope).  Results
+ * are rounded to s->dtype (bf16: nearest even); accumulation is float32, the rotation
+ * angle is reduced in double precision.  The new key becomes a candidate of stage 1
+ * once lengths[b] > p (the next step of a growing sequence).
+ *   hidden     multiple of 1024, <= 16384          vocab  rows of emb (>= 1)
+ *   tokens, positions  device int32 [B]; a token outside [0, vocab) gives zero q and k
+ *   emb    device [vocab][hidden]       gamma device [hidden]
+ *   wq     device [H_q * head_dim][hidden]   wk device [H_kv * head_dim][hidden]
+ *          (row h * head_dim + i produces dimension i of head h); all s->dtype
+ *   q_out  device [B][H_q][head_dim] s->dtype        dlm_k device [B][H_kv][max_len][head_dim] (in/out)
+ *   ws     spc_workspace_size(SPC_CALL_FRONT, s) bytes (float32 partial sums)
+ * Supported: batch <= 16, head_dim 64 or 128, dtype bf16 or f32.
+ */
+int spc_retrieval_head_qk(const spc_shape* s, int32_t hidden, int64_t vocab, const spc_rope* rope, float eps,
+                          const int32_t* tokens, const int32_t* positions, const void* emb, const void* gamma,
+                          const void* wq, const void* wk, void* q_out, void* dlm_k, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Stage 1 - retrieval scores.  The retrieval head's attention weights of one

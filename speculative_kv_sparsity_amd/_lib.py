@@ -24,6 +24,7 @@ SPC_CALL_SCORES = 1
 SPC_CALL_TOPK = 2
 SPC_CALL_ELASTIC = 3
 SPC_CALL_ATTN = 4
+SPC_CALL_FRONT = 5
 
 SPC_PLAN = 1
 SPC_COPY = 2
@@ -42,6 +43,11 @@ class SpcShape(ctypes.Structure):
 class SpcKvLayout(ctypes.Structure):
     _fields_ = [("s_b", ctypes.c_int64), ("s_layer", ctypes.c_int64), ("s_head", ctypes.c_int64),
                 ("s_row", ctypes.c_int64), ("s_kv", ctypes.c_int64)]
+
+
+class SpcRope(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_float), ("factor", ctypes.c_float), ("orig_max_pos", ctypes.c_int32),
+                ("beta_fast", ctypes.c_float), ("beta_slow", ctypes.c_float)]
 
 
 class SpcQLayout(ctypes.Structure):
@@ -68,6 +74,8 @@ SIGNATURES = {
                                     ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _P, _SZ, _P]),
     "spc_mla_absorb_q": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P, _P, _P]),
     "spc_mla_out_proj": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _I32, _P, _P]),
+    "spc_retrieval_head_qk": (_I, [ctypes.POINTER(SpcShape), _I32, ctypes.c_int64, ctypes.POINTER(SpcRope),
+                                   ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

@@ -12,13 +12,14 @@ from typing import Optional
 import torch
 
 from . import _lib as L
-from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_SCORES, SPC_CALL_TOPK, SPC_COPY, SPC_F32, SPC_PLAN, SPC_ROWS_GATHER,
-                   SPC_ROWS_SLOTS, SpcKvLayout, SpcQLayout, SpcShape)
+from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_FRONT, SPC_CALL_SCORES, SPC_CALL_TOPK, SPC_COPY, SPC_F32,
+                   SPC_PLAN, SPC_ROWS_GATHER, SPC_ROWS_SLOTS, SpcKvLayout, SpcQLayout, SpcRope, SpcShape)
 
 __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version", "spc_workspace_size",
            "spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_elastic_reset",
            "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
-           "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "spc_mla_absorb_q", "spc_mla_out_proj"]
+           "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "SPC_CALL_FRONT", "spc_mla_absorb_q",
+           "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk"]
 
 
 class SpcError(RuntimeError):
@@ -148,3 +149,20 @@ def spc_mla_out_proj(shape: SpcShape, dv: int, w_uv, o_lat, layer: int, out, str
         _dev(t, n)
     _check(L.lib().spc_mla_out_proj(ctypes.byref(shape), int(dv), _ptr(w_uv), _ptr(o_lat), int(layer), _ptr(out),
                                     _stream(stream)))
+
+
+def rope_params(base: float, factor: float = 1.0, orig_max_pos: int = 2048, beta_fast: float = 32.0,
+                beta_slow: float = 1.0) -> SpcRope:
+    return SpcRope(float(base), float(factor), int(orig_max_pos), float(beta_fast), float(beta_slow))
+
+
+def spc_retrieval_head_qk(shape: SpcShape, hidden: int, rope: SpcRope, eps: float, tokens, positions, emb, gamma,
+                          wq, wk, q_out, dlm_k, ws=None, stream=None) -> None:
+    for t, n in ((tokens, "tokens"), (positions, "positions"), (emb, "emb"), (gamma, "gamma"), (wq, "wq"),
+                 (wk, "wk"), (q_out, "q_out"), (dlm_k, "dlm_k")):
+        _dev(t, n)
+    ws = _workspace(SPC_CALL_FRONT, shape, q_out.device) if ws is None else ws
+    _check(L.lib().spc_retrieval_head_qk(ctypes.byref(shape), int(hidden), int(emb.shape[0]), ctypes.byref(rope),
+                                         float(eps), _ptr(tokens), _ptr(positions), _ptr(emb), _ptr(gamma), _ptr(wq),
+                                         _ptr(wk), _ptr(q_out), _ptr(dlm_k), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)))

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["spc_api.cpp", "spc_scores.hip", "spc_topk.hip", "spc_elastic.hip", "spc_attn.hip", "spc_mla.hip"]
+SOURCES = ["spc_api.cpp", "spc_scores.hip", "spc_topk.hip", "spc_elastic.hip", "spc_attn.hip", "spc_mla.hip",
+           "spc_front.hip"]
 ARCH = os.environ.get("SPC_OFFLOAD_ARCH", "gfx950")
 
 

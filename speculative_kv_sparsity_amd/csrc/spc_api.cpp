@@ -86,6 +86,7 @@ size_t spc_workspace_size(int which_call, const spc_shape* s) {
     case SPC_CALL_SCORES: return spc::scores_ws_bytes(*s);
     case SPC_CALL_TOPK: return spc::topk_ws_bytes(*s);
     case SPC_CALL_ATTN: return spc::attn_ws_bytes(*s);
+    case SPC_CALL_FRONT: return spc::front_ws_bytes(*s);
     default: return 0;
   }
 }
@@ -265,6 +266,38 @@ int spc_mla_out_proj(const spc_shape* s, int32_t dv, const void* w_uv, const flo
                                                 o_lat + (size_t)layer * s->n_q_heads * spc::kMlaLatent, b_stride, out,
                                                 as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "MLA output projection launch");
+}
+
+int spc_retrieval_head_qk(const spc_shape* s, int32_t hidden, int64_t vocab, const spc_rope* rope, float eps,
+                          const int32_t* tokens, const int32_t* positions, const void* emb, const void* gamma,
+                          const void* wq, const void* wk, void* q_out, void* dlm_k, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!rope || !tokens || !positions || !emb || !gamma || !wq || !wk || !q_out || !dlm_k)
+    return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (s->batch > spc::kFrontMaxBatch)
+    return fail(SPC_ERR_UNSUPPORTED, "batch %d > %d for the front end", s->batch, spc::kFrontMaxBatch);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SPC_ERR_UNSUPPORTED, "front end head_dim %d (64 or 128 built)", s->head_dim);
+  if (hidden < spc::kFrontSlice || hidden % spc::kFrontSlice != 0 || hidden > spc::kFrontSlice * spc::kFrontMaxSlices)
+    return fail(SPC_ERR_INVALID_ARG, "hidden %d must be a multiple of %d, at most %d", hidden, spc::kFrontSlice,
+                spc::kFrontSlice * spc::kFrontMaxSlices);
+  if (vocab < 1) return fail(SPC_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (!(eps >= 0.f)) return fail(SPC_ERR_INVALID_ARG, "eps must be >= 0");
+  if (!(rope->base > 1.f) || !(rope->factor > 0.f) || rope->orig_max_pos < 1)
+    return fail(SPC_ERR_INVALID_ARG, "rope: base > 1, factor > 0 and orig_max_pos >= 1 required");
+  if (rope->factor > 1.f && !(rope->beta_fast > rope->beta_slow))
+    return fail(SPC_ERR_INVALID_ARG, "rope: beta_fast must exceed beta_slow");
+  if (!aligned16(wq) || !aligned16(wk) || !aligned4(emb) || !aligned4(gamma) || !aligned16(q_out) ||
+      !aligned16(dlm_k))
+    return fail(SPC_ERR_INVALID_ARG, "wq, wk, q_out and dlm_k must be 16-byte aligned (emb, gamma 4-byte)");
+  const size_t need = spc::front_ws_bytes(*s);
+  if (ws_bytes < need || !ws)
+    return fail(SPC_ERR_WORKSPACE, "front end needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = spc::launch_front(*s, hidden, vocab, *rope, eps, tokens, positions, emb, gamma, wq, wk, q_out,
+                                         dlm_k, ws, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "retrieval head front end launch");
 }
 
 }  // extern "C"

@@ -56,6 +56,16 @@ hipError_t launch_copy(const spc_shape& s, const int32_t* load_pos, const int32_
 hipError_t launch_reset(const spc_shape& s, int batch_begin, int batch_end, int32_t* slot_pos,
                         uint32_t* resident_bm, hipStream_t st);
 
+// ---- retrieval-head front end (token -> stage-1 query, DLM key append)
+constexpr int kFrontSlice = 1024;      // hidden elements per GEMV workgroup slice
+constexpr int kFrontMaxSlices = 16;    // hidden <= 16384
+constexpr int kFrontMaxBatch = 16;
+constexpr int kFrontMaxHeadDim = 128;
+size_t front_ws_bytes(const spc_shape& s);
+hipError_t launch_front(const spc_shape& s, int hidden, int64_t vocab, const spc_rope& rope, float eps,
+                        const int32_t* tokens, const int32_t* positions, const void* emb, const void* gamma,
+                        const void* wq, const void* wk, void* q_out, void* dlm_k, void* ws, hipStream_t st);
+
 // ---- stage 4: sparse decode attention
 size_t attn_ws_bytes(const spc_shape& s);
 bool attn_supported(const spc_shape& s);

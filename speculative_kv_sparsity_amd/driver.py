@@ -24,7 +24,25 @@ from typing import List, Optional
 import torch
 
 from . import api
-from .workload import Preset
+from .workload import FrontWeights, Preset
+
+
+class RetrievalHead:
+    """The retrieval head's front end: the new token of each sequence -> the stage-1 query; its key
+    is appended to the DLM key cache at the token's position (SpeContext blog section 5 "C1")."""
+
+    def __init__(self, shape, fw: FrontWeights):
+        self.shape = shape
+        self.fw = fw
+        self.rope = api.rope_params(fw.rope_base, fw.rope_factor, fw.rope_orig)
+        self.ws = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_FRONT, shape)), dtype=torch.uint8,
+                              device=fw.emb.device)
+
+    def __call__(self, tokens: torch.Tensor, positions: torch.Tensor, q_out: torch.Tensor, dlm_k: torch.Tensor,
+                 stream=None) -> None:
+        fw = self.fw
+        api.spc_retrieval_head_qk(self.shape, fw.hidden, self.rope, fw.eps, tokens, positions, fw.emb, fw.gamma,
+                                  fw.wq, fw.wk, q_out, dlm_k, ws=self.ws, stream=stream)
 
 
 class SparseDecoder:
@@ -105,6 +123,20 @@ class SparseDecoder:
                                    stream=self.main if stream is None else stream)
 
     # --- one step -----------------------------------------------------------------------
+    def step_tokens(self, head: RetrievalHead, tokens: torch.Tensor, lengths: torch.Tensor,
+                    timer: Optional["StageTimer"] = None) -> torch.Tensor:
+        """The step from the new tokens: the front end writes the query (and appends each token's
+        key at position lengths[b], a candidate from the next step on), then the four stages.
+        Returns the query buffer."""
+        if not hasattr(self, "q_front"):
+            p = self.p
+            self.q_front = torch.empty((p.batch, p.n_q_heads, p.head_dim), dtype=p.torch_dtype, device=self.device)
+        mark = timer.mark if timer is not None else (lambda name, stream: None)
+        mark("front", self.main)
+        head(tokens, lengths, self.q_front, self.dlm_k, stream=self.main)
+        self.step(self.q_front, lengths, timer)
+        return self.q_front
+
     def step(self, q: torch.Tensor, lengths: torch.Tensor, timer: Optional["StageTimer"] = None) -> None:
         """q: device [B][H_q][d]; lengths: device int32 [B].  Asynchronous.
 

@@ -232,6 +232,44 @@ def _generate_mla(p: Preset, device, seed: int, steps: int) -> Workload:
                     q_nope=q_nope, q_rope=q_rope, boosted=boosted)
 
 
+@dataclass
+class FrontWeights:
+    """Synthetic retrieval-head front end: embedding table, input-norm gain, Q/K projections,
+    rotary parameters.  Random weights: they exercise the path, they carry no meaning."""
+    emb: torch.Tensor        # [vocab][hidden]
+    gamma: torch.Tensor      # [hidden]
+    wq: torch.Tensor         # [H_q * d][hidden]
+    wk: torch.Tensor         # [H_kv * d][hidden]
+    hidden: int
+    eps: float
+    rope_base: float
+    rope_factor: float
+    rope_orig: int
+    tokens: np.ndarray       # [steps][B] int32 token ids of the decode steps
+
+
+def generate_front(p: Preset | str, device="cpu", seed: int = 0, steps: int = 8, vocab: int = 128256,
+                   hidden: int = 4096, rope_base: float = 500000.0, rope_orig: int = 2048,
+                   eps: float = 1e-5) -> FrontWeights:
+    """Front-end weights in the workload's element type.  Embedding rows ~ N(0, 0.02^2) (the scale
+    cancels in the input norm), gain ~ 1 + N(0, 0.1^2), projections ~ N(0, 1/hidden).  The rotary
+    context scale is max(1, L_max / rope_orig): the distilled model's 2K context extended to the
+    workload's length."""
+    if isinstance(p, str):
+        p = PRESETS[p]
+    dt = p.torch_dtype
+    device = torch.device(device)
+    g = _gen(device, seed, "front")
+    emb = (0.02 * torch.randn((vocab, hidden), generator=g, device=device)).to(dt)
+    gamma = (1.0 + 0.1 * torch.randn((hidden,), generator=g, device=device)).to(dt)
+    wq = (torch.randn((p.n_q_heads * p.head_dim, hidden), generator=g, device=device) / math.sqrt(hidden)).to(dt)
+    wk = (torch.randn((p.n_kv_heads * p.head_dim, hidden), generator=g, device=device) / math.sqrt(hidden)).to(dt)
+    rng = np.random.default_rng(_subseed(seed, "tokens"))
+    tokens = rng.integers(0, vocab, size=(steps, p.batch), dtype=np.int64).astype(np.int32)
+    return FrontWeights(emb, gamma, wq, wk, hidden, eps, rope_base, max(1.0, p.max_len / rope_orig), rope_orig,
+                        tokens)
+
+
 # ----------------------------------------------------------------------------
 # NumPy views for the oracle (raw bits for bf16, float32 otherwise)
 # ----------------------------------------------------------------------------

@@ -100,3 +100,31 @@ def test_workspace_sizes():
     small = _shape(batch=1, n_q_heads=16, n_kv_heads=1, n_groups=16, head_dim=576, v_dim=512, max_len=4096,
                    budget=512, scale=192 ** -0.5)
     assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(small)) == 16 * 2 * (512 * 4 + 8)   # 256-row splits
+
+
+def test_front_end_host_validation():
+    """spc_retrieval_head_qk rejects bad sizes before launching (pointers are never dereferenced)."""
+    lib = L.lib()
+    s = _shape()
+    rope = L.SpcRope(500000.0, 16.0, 2048, 32.0, 1.0)
+    p = ctypes.c_void_p(256)
+    ws_ok = lib.spc_workspace_size(L.SPC_CALL_FRONT, ctypes.byref(s))
+    # one (max) float32 partial per slice, sequence and output row, plus the per-slice sums of squares
+    assert ws_ok == 16 * 16 * ((32 + 8) * 128 + 1) * 4
+
+    def call(shape=s, hidden=4096, vocab=1000, r=rope, eps=1e-5, ptr=p, ws_bytes=ws_ok):
+        return lib.spc_retrieval_head_qk(ctypes.byref(shape), hidden, vocab, ctypes.byref(r), eps, ptr, ptr, ptr, ptr,
+                                         ptr, ptr, ptr, ptr, ptr, ws_bytes, None)
+
+    assert call(hidden=4000) == L.SPC_ERR_INVALID_ARG          # not a multiple of 1024
+    assert call(hidden=32768) == L.SPC_ERR_INVALID_ARG         # above 16384
+    assert call(vocab=0) == L.SPC_ERR_INVALID_ARG
+    assert call(eps=-1.0) == L.SPC_ERR_INVALID_ARG
+    assert call(r=L.SpcRope(500000.0, 16.0, 2048, 1.0, 32.0)) == L.SPC_ERR_INVALID_ARG   # beta_fast <= beta_slow
+    assert call(r=L.SpcRope(0.5, 1.0, 2048, 32.0, 1.0)) == L.SPC_ERR_INVALID_ARG         # base <= 1
+    assert call(shape=_shape(batch=17)) == L.SPC_ERR_UNSUPPORTED
+    assert call(shape=_shape(head_dim=96, v_dim=96)) == L.SPC_ERR_UNSUPPORTED
+    assert call(ptr=None) == L.SPC_ERR_INVALID_ARG
+    assert call(ptr=ctypes.c_void_p(258)) == L.SPC_ERR_INVALID_ARG                      # misaligned
+    assert call(ws_bytes=ws_ok - 1) == L.SPC_ERR_WORKSPACE
+    assert b"workspace" in lib.spc_last_error()

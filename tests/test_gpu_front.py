@@ -1,0 +1,142 @@
+"""Retrieval-head front end on the GPU against the fp64 oracle: the stage-1 query, the appended
+DLM key, the cache rows it must not touch, and the step driven from tokens."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import OracleDecoder
+from oracle import front as F
+from oracle import spc_oracle as O
+from speculative_kv_sparsity_amd import api
+from speculative_kv_sparsity_amd import workload as W
+from speculative_kv_sparsity_amd.driver import RetrievalHead, SparseDecoder
+from tests.gpu_util import (ATTN_DERIVED, ATTN_MAX_ABS, check_topk_tolerance, dev_lengths, raw, sel_lists,
+                            shape_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def _f64(t):
+    return O.to_f64(raw(t), "bf16" if t.dtype == torch.bfloat16 else "f32")
+
+
+def _close(got, ref, dtype):
+    """bf16 results: within half a bf16 ulp of the fp64 value (plus fp32 accumulation); fp32: 1e-5."""
+    scale = float(np.max(np.abs(ref))) or 1.0
+    if dtype == "bf16":
+        tol = 2.0 ** -8 * np.abs(ref) + 1e-6 * scale
+    else:
+        tol = 1e-5 * scale + 1e-6 * np.abs(ref)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (int(bad.sum()), float(np.max(np.abs(got - ref))), scale)
+
+
+def _run_front(p, fw, tokens, positions, seed=0):
+    shape = shape_of(p)
+    dev = fw.emb.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    dlm_k = torch.randn((p.batch, p.n_kv_heads, p.max_len, p.head_dim), generator=g, device=dev).to(p.torch_dtype)
+    before = raw(dlm_k).copy()
+    q_out = torch.zeros((p.batch, p.n_q_heads, p.head_dim), dtype=p.torch_dtype, device=dev)
+    head = RetrievalHead(shape, fw)
+    head(dev_lengths(tokens), dev_lengths(positions), q_out, dlm_k)
+    torch.cuda.synchronize()
+    # the oracle reads only the embedding rows of the tokens used (the full table can be 1 GB)
+    vocab = fw.emb.shape[0]
+    used = sorted({t for t in tokens if 0 <= t < vocab})
+    sub = _f64(fw.emb[torch.as_tensor(used, dtype=torch.long, device=fw.emb.device)]) if used else np.zeros((0, 1))
+    sub_tokens = [used.index(t) if 0 <= t < vocab else -1 for t in tokens]
+    q_ref, k_ref = F.retrieval_head_qk(sub_tokens, positions, sub, _f64(fw.gamma), _f64(fw.wq), _f64(fw.wk),
+                                       p.n_q_heads, p.n_kv_heads, p.head_dim, fw.eps, fw.rope_base, fw.rope_factor,
+                                       fw.rope_orig)
+    _close(_f64(q_out), q_ref, p.dtype)
+    after = raw(dlm_k)
+    for b, pos in enumerate(positions):
+        if 0 <= pos < p.max_len:
+            _close(_f64(dlm_k[b, :, pos]), k_ref[b], p.dtype)
+            after[b, :, pos] = before[b, :, pos]
+    np.testing.assert_array_equal(after, before)          # no other row of the cache moved
+    return q_out, q_ref
+
+
+@pytest.mark.parametrize("dtype,d,factor", [("bf16", 128, 4.0), ("f32", 128, 1.0), ("bf16", 64, 16.0)])
+def test_front_matches_oracle(dtype, d, factor):
+    p = W.PRESETS["tiny"].with_(batch=4, n_q_heads=8, n_kv_heads=2, head_dim=d, v_dim=d, max_len=256,
+                                budget=32, dtype=dtype)
+    fw = W.generate_front(p, device="cuda", seed=1, vocab=300, hidden=2048, rope_orig=64)
+    fw.rope_factor = factor
+    # an in-range token at position 0, a token outside the vocabulary, a position past the cache,
+    # and a large position (YaRN's interpolated low frequencies matter there)
+    q, _ = _run_front(p, fw, tokens=[5, -1, 299, 17], positions=[0, 100, 256, 60000])
+    assert np.all(_f64(q[1]) == 0)
+
+
+def test_front_full_size_llama8b_shape():
+    """hidden 4096, vocabulary 128256 (1 GB embedding table), 32 q-heads / 8 KV heads, YaRN to 32K."""
+    p = W.PRESETS["b1_32k"].with_(batch=2, n_layers=1)
+    fw = W.generate_front(p, device="cuda", seed=2)
+    assert fw.rope_factor == 16.0
+    _run_front(p, fw, tokens=[int(fw.tokens[0, 0]), 128255], positions=[32767, 20000])
+
+
+def test_front_batch16():
+    p = W.PRESETS["b16_grow"].with_(n_layers=1, max_len=4096)
+    fw = W.generate_front(p, device="cuda", seed=3, vocab=1000, hidden=4096)
+    rng = np.random.default_rng(4)
+    _run_front(p, fw, tokens=rng.integers(0, 1000, 16).tolist(), positions=rng.integers(0, 4096, 16).tolist())
+
+
+def test_front_rejects_bad_hidden_and_batch():
+    p = W.PRESETS["tiny"].with_(dtype="bf16")
+    fw = W.generate_front(p, device="cuda", seed=5, vocab=10, hidden=1024)
+    q = torch.zeros((1, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, p.n_kv_heads, p.max_len, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    t = dev_lengths([1])
+    rope = api.rope_params(fw.rope_base, fw.rope_factor, fw.rope_orig)
+    with pytest.raises(api.SpcError):
+        api.spc_retrieval_head_qk(shape_of(p), 1000, rope, fw.eps, t, t, fw.emb, fw.gamma, fw.wq, fw.wk, q, k)
+    with pytest.raises(api.SpcError):
+        api.spc_retrieval_head_qk(shape_of(p.with_(batch=17)), 1024, rope, fw.eps, t, t, fw.emb, fw.gamma, fw.wq,
+                                  fw.wk, q, k)
+
+
+def test_step_from_tokens_growth():
+    """Growing sequences driven from tokens: each step's query comes from the front end and its key
+    joins the cache at the current length, so it is a candidate of the next step.  Every step is
+    checked against the oracle fed the GPU's query and key cache (stage by stage)."""
+    p = W.PRESETS["b16_grow"].with_(batch=3, n_layers=4, max_len=3000, budget=256, start_len=1000,
+                                    offset_max=1500)
+    steps = 4
+    w = W.generate(p, device="cuda", seed=6, steps=steps, pin_host=True)
+    fw = W.generate_front(p, device="cuda", seed=6, steps=steps, vocab=5000, hidden=2048)
+    dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=2)
+    head = RetrievalHead(dec.shape, fw)
+    ora = OracleDecoder(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.budget, p.scale, p.dtype)
+    kv_raw = raw(w.host_kv)
+    lens_dev = dev_lengths(w.lengths)
+    for t in range(steps):
+        k_before = raw(dec.dlm_k).copy()
+        q = dec.step_tokens(head, dev_lengths(fw.tokens[t]), lens_dev[t])
+        torch.cuda.synchronize()
+        lengths = w.lengths[t]
+        # the appended keys sit at the current lengths, outside this step's candidates
+        k_now = raw(dec.dlm_k)
+        for b in range(p.batch):
+            n = int(lengths[b])
+            np.testing.assert_array_equal(k_now[b, :, :n], k_before[b, :, :n])
+        probs, ref_sel = ora.select(raw(q), k_now, lengths)
+        gsel = sel_lists(dec.sel_idx, dec.sel_count)
+        check_topk_tolerance(gsel, ref_sel, O.group_scores(probs, p.n_groups), p.budget)
+        ora.plan(gsel)
+        sp = dec.slot_pos.cpu().numpy()
+        for b in range(p.batch):
+            for g in range(p.n_groups):
+                np.testing.assert_array_equal(sp[b, g], ora.slot_pos[b][g])
+        ref = ora.attend(raw(q), kv_raw, gsel, list(range(p.n_layers)))
+        err = float(np.max(np.abs(dec.out.cpu().numpy().astype(np.float64) - ref)))
+        assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, (t, err)
+        # this step's new keys were written at the current lengths (the synthetic rows there are replaced)
+        for b in range(p.batch):
+            n = int(lengths[b])
+            assert not np.array_equal(k_now[b, :, n], k_before[b, :, n])
