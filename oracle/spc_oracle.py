@@ -342,3 +342,54 @@ def kv_cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, elem_bytes: in
 def default_scale(head_dim: int) -> float:
     """1/sqrt(d), the scale of the AttentionWeight formula."""
     return 1.0 / math.sqrt(head_dim)
+
+
+# ----------------------------------------------------------------------------
+# Adaptive memory management: per-layer offload thresholds
+# (blog section 7 "C3"; paper summary sections 6.1-6.2.1)
+# ----------------------------------------------------------------------------
+
+INT32_MAX = 2 ** 31 - 1
+
+
+def memory_bytes(seq_len: int, n_offloaded: int, fixed_bytes: int, token_bytes: int, n_layers: int, batch: int,
+                 n_kv_heads: int, head_dim: int, v_dim: int, budget: int, elem_bytes: int) -> int:
+    """GPU memory at sequence length L with the last c layers offloaded: everything independent of L,
+    the per-position state outside the target KV, the full K/V of the layers kept on the GPU, and the
+    budget-sized working set of each offloaded layer (the pages' four inputs: the model's weights and
+    layers, KV heads and head dimension, the requests and the KV budget)."""
+    per_layer_token = batch * n_kv_heads * (head_dim + v_dim) * elem_bytes
+    return (fixed_bytes + seq_len * token_bytes + (n_layers - n_offloaded) * seq_len * per_layer_token
+            + n_offloaded * budget * per_layer_token)
+
+
+def offload_thresholds(gpu_bytes: int, **model) -> List[int]:
+    """threshold[c] for c = 0..n_layers: the first sequence length at which c offloaded layers no
+    longer fit in gpu_bytes (0: not even an empty cache fits; INT32_MAX: never within int32).
+    Found by bisection on the plain memory sum."""
+    out = []
+    for c in range(model["n_layers"] + 1):
+        if memory_bytes(0, c, **model) > gpu_bytes:
+            out.append(0)
+            continue
+        if memory_bytes(INT32_MAX - 1, c, **model) <= gpu_bytes:
+            out.append(INT32_MAX)
+            continue
+        lo, hi = 0, INT32_MAX - 1            # fits at lo, not at hi
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if memory_bytes(mid, c, **model) <= gpu_bytes:
+                lo = mid
+            else:
+                hi = mid
+        out.append(hi)
+    return out
+
+
+def offloaded_layers(seq_len: int, thresholds: Sequence[int], n_offloaded: int = 0) -> int:
+    """The pages' runtime loop: while the length reaches the threshold of the current count,
+    offload one more layer (the last one still on the GPU)."""
+    c = n_offloaded
+    while c < len(thresholds) - 1 and seq_len >= thresholds[c]:
+        c += 1
+    return c

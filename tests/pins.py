@@ -318,3 +318,31 @@ def check_kv_cache_size(kv_cache_bytes):
     for pt in ex["points"]:
         gb = kv_cache_bytes(m["n_layers"], m["n_kv_heads"], m["head_dim"], m["elem_bytes"], pt["seq_len"]) / 2 ** 30
         assert abs(gb - pt["approx_gb"]) <= ex["rel_tolerance"] * pt["approx_gb"]
+
+
+# ----------------------------------------------------------------------------- adaptive offloading (C3)
+
+def check_offload_golden(offload_thresholds, offloaded_layers):
+    g = json.load(open(os.path.join(GOLDEN, "offload_thresholds.json")))
+    th = offload_thresholds(g["gpu_bytes"], **g["model"])
+    assert list(th) == g["thresholds"]
+    for L, c in g["offloaded_at"]:
+        assert offloaded_layers(L, th) == c, (L, c)
+
+
+def check_offload_invariants(offload_thresholds, memory_bytes):
+    """Each finite threshold t is the first length that does not fit: L = t - 1 fits, t does not."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        model = dict(fixed_bytes=int(rng.integers(0, 10 ** 10)), token_bytes=int(rng.integers(0, 10 ** 5)),
+                     n_layers=int(rng.integers(1, 40)), batch=int(rng.integers(1, 17)),
+                     n_kv_heads=int(rng.integers(1, 9)), head_dim=128, v_dim=128,
+                     budget=int(rng.integers(1, 4097)), elem_bytes=2)
+        gpu = int(rng.integers(10 ** 9, 3 * 10 ** 11))
+        th = offload_thresholds(gpu, **model)
+        assert len(th) == model["n_layers"] + 1
+        for c, t in enumerate(th):
+            if t == 0:
+                assert memory_bytes(0, c, **model) > gpu
+            elif t < 2 ** 31 - 1:
+                assert memory_bytes(t - 1, c, **model) <= gpu < memory_bytes(t, c, **model)

@@ -147,3 +147,21 @@ def test_pins_catch_mla_mistakes():
 
 def test_pins_catch_size_mistakes():
     _fails(pins.check_kv_cache_size, lambda l, h, d, e, s, b=1: l * h * d * e * s * b)   # forgot K and V
+
+
+def test_pins_catch_offload_mistakes():
+    def last_fitting(gpu, **m):            # the last length that fits instead of the first that does not
+        return [t - 1 if 0 < t < 2 ** 31 - 1 else t for t in O.offload_thresholds(gpu, **m)]
+
+    def no_working_set(L, c, **m):         # offloaded layers keep nothing on the GPU
+        per = m["batch"] * m["n_kv_heads"] * (m["head_dim"] + m["v_dim"]) * m["elem_bytes"]
+        return m["fixed_bytes"] + L * m["token_bytes"] + (m["n_layers"] - c) * L * per
+
+    def strict_loop(L, th, c=0):           # offloads only once the length passes the threshold
+        while c < len(th) - 1 and L > th[c]:
+            c += 1
+        return c
+
+    _fails(pins.check_offload_golden, last_fitting, O.offloaded_layers)
+    _fails(pins.check_offload_golden, O.offload_thresholds, strict_loop)
+    _fails(pins.check_offload_invariants, O.offload_thresholds, no_working_set)

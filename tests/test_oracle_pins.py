@@ -85,3 +85,11 @@ def test_bf16_widening_exact():
     assert vals[2] == 3.140625                      # 0x4049: 1.5703125 * 2
     assert vals[4] == (2 - 2 ** -7) * 2.0 ** 127    # largest finite bf16
     assert vals[5] == 2.0 ** -133                   # smallest subnormal bf16
+
+
+def test_offload_thresholds_worked_instance():
+    pins.check_offload_golden(O.offload_thresholds, O.offloaded_layers)
+
+
+def test_offload_thresholds_are_first_lengths_that_do_not_fit():
+    pins.check_offload_invariants(O.offload_thresholds, O.memory_bytes)
