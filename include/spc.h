@@ -228,6 +228,30 @@ int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos
                       void* stream);
 
 /*
+ * Adaptive memory management (SpeContext blog section 7 "C3"; paper summary
+ * sections 6.1-6.2.1): layers are offloaded to host memory one at a time, the
+ * last layer still on the GPU first, as the sequence grows; an offloaded layer
+ * keeps only its budget-sized working set (the slots of stage 3) on the GPU.
+ * The memory model, with c layers offloaded at sequence length L:
+ *   bytes(L, c) = fixed_bytes + L * token_bytes
+ *               + (n_layers - c) * L * layer_token + c * budget * layer_token,
+ *   layer_token = batch * n_kv_heads * (head_dim + v_dim) * elem_bytes.
+ * spc_offload_thresholds writes threshold[c], c = 0..n_layers: the first length at
+ * which c offloaded layers no longer fit in gpu_bytes (0 if not even an empty
+ * cache fits, INT32_MAX if every int32 length fits).  The runtime rule is the
+ * pages' loop: while seq_len >= threshold[c] and c < n_layers, offload one more.
+ * Host-only arithmetic (no GPU); all sizes >= 0, n_layers, batch, heads >= 1.
+ */
+typedef struct spc_mem_model {
+  int64_t gpu_bytes;    /* GPU memory the model may use */
+  int64_t fixed_bytes;  /* everything independent of the length: weights, workspaces */
+  int64_t token_bytes;  /* per cached position outside the target K/V (DLM keys, probabilities, ...) */
+  int32_t n_layers, batch, n_kv_heads, head_dim, v_dim, budget, elem_bytes;
+} spc_mem_model;
+
+int spc_offload_thresholds(const spc_mem_model* m, int32_t* threshold /* [n_layers + 1] */);
+
+/*
  * Stage 4 - sparse decode attention over the resident sparse KV only
  * (blog section 4 pseudocode, llm.forward(..., sparse_kv=resident_kv); the
  * AttentionWeight formula of blog section 2):

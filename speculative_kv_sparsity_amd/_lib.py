@@ -50,6 +50,13 @@ class SpcRope(ctypes.Structure):
                 ("beta_fast", ctypes.c_float), ("beta_slow", ctypes.c_float)]
 
 
+class SpcMemModel(ctypes.Structure):
+    _fields_ = [("gpu_bytes", ctypes.c_int64), ("fixed_bytes", ctypes.c_int64), ("token_bytes", ctypes.c_int64),
+                ("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32)]
+
+
 class SpcQLayout(ctypes.Structure):
     _fields_ = [("s_b", ctypes.c_int64), ("s_layer", ctypes.c_int64), ("s_head", ctypes.c_int64)]
 
@@ -74,6 +81,7 @@ SIGNATURES = {
                                     ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _P, _SZ, _P]),
     "spc_mla_absorb_q": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P, _P, _P]),
     "spc_mla_out_proj": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _I32, _P, _P]),
+    "spc_offload_thresholds": (_I, [ctypes.POINTER(SpcMemModel), ctypes.POINTER(ctypes.c_int32)]),
     "spc_retrieval_head_qk": (_I, [ctypes.POINTER(SpcShape), _I32, ctypes.c_int64, ctypes.POINTER(SpcRope),
                                    ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }

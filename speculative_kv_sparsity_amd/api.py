@@ -13,13 +13,14 @@ import torch
 
 from . import _lib as L
 from ._lib import (SPC_BF16, SPC_CALL_ATTN, SPC_CALL_FRONT, SPC_CALL_SCORES, SPC_CALL_TOPK, SPC_COPY, SPC_F32,
-                   SPC_PLAN, SPC_ROWS_GATHER, SPC_ROWS_SLOTS, SpcKvLayout, SpcQLayout, SpcRope, SpcShape)
+                   SPC_PLAN, SPC_ROWS_GATHER, SPC_ROWS_SLOTS, SpcKvLayout, SpcMemModel, SpcQLayout, SpcRope,
+                   SpcShape)
 
 __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version", "spc_workspace_size",
            "spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_elastic_reset",
            "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
            "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "SPC_CALL_FRONT", "spc_mla_absorb_q",
-           "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk"]
+           "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds"]
 
 
 class SpcError(RuntimeError):
@@ -166,3 +167,13 @@ def spc_retrieval_head_qk(shape: SpcShape, hidden: int, rope: SpcRope, eps: floa
                                          float(eps), _ptr(tokens), _ptr(positions), _ptr(emb), _ptr(gamma), _ptr(wq),
                                          _ptr(wk), _ptr(q_out), _ptr(dlm_k), _ptr(ws), ws.numel() * ws.element_size(),
                                          _stream(stream)))
+
+
+def spc_offload_thresholds(gpu_bytes: int, fixed_bytes: int, token_bytes: int, n_layers: int, batch: int,
+                           n_kv_heads: int, head_dim: int, v_dim: int, budget: int, elem_bytes: int) -> list:
+    """threshold[c], c = 0..n_layers (host arithmetic in the library; see include/spc.h)."""
+    m = SpcMemModel(int(gpu_bytes), int(fixed_bytes), int(token_bytes), int(n_layers), int(batch), int(n_kv_heads),
+                    int(head_dim), int(v_dim), int(budget), int(elem_bytes))
+    out = (ctypes.c_int32 * (int(n_layers) + 1))()
+    _check(L.lib().spc_offload_thresholds(ctypes.byref(m), out))
+    return list(out)

@@ -300,4 +300,28 @@ int spc_retrieval_head_qk(const spc_shape* s, int32_t hidden, int64_t vocab, con
   return e == hipSuccess ? ok() : hip_fail(e, "retrieval head front end launch");
 }
 
+int spc_offload_thresholds(const spc_mem_model* m, int32_t* threshold) {
+  if (!m || !threshold) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (m->gpu_bytes < 0 || m->fixed_bytes < 0 || m->token_bytes < 0 || m->n_layers < 1 || m->batch < 1 ||
+      m->n_kv_heads < 1 || m->head_dim < 0 || m->v_dim < 0 || m->budget < 0 || m->elem_bytes < 1)
+    return fail(SPC_ERR_INVALID_ARG, "memory model sizes must be >= 0 (layers, batch, heads, element bytes >= 1)");
+  // exact integer arithmetic in 128 bits: bytes(L, c) = A_c + L * S_c
+  const __int128 layer_token = (__int128)m->batch * m->n_kv_heads * (m->head_dim + m->v_dim) * m->elem_bytes;
+  const __int128 M = m->gpu_bytes;
+  const int64_t kMax = 2147483647;
+  for (int c = 0; c <= m->n_layers; ++c) {
+    const __int128 A = (__int128)m->fixed_bytes + (__int128)c * m->budget * layer_token;
+    const __int128 S = (__int128)m->token_bytes + (__int128)(m->n_layers - c) * layer_token;
+    if (A > M) {
+      threshold[c] = 0;
+    } else if (S == 0) {
+      threshold[c] = (int32_t)kMax;
+    } else {
+      const __int128 last_fit = (M - A) / S;           // the largest L with A + L S <= M
+      threshold[c] = last_fit >= kMax - 1 ? (int32_t)kMax : (int32_t)(last_fit + 1);
+    }
+  }
+  return ok();
+}
+
 }  // extern "C"

@@ -128,3 +128,27 @@ def test_front_end_host_validation():
     assert call(ptr=ctypes.c_void_p(258)) == L.SPC_ERR_INVALID_ARG                      # misaligned
     assert call(ws_bytes=ws_ok - 1) == L.SPC_ERR_WORKSPACE
     assert b"workspace" in lib.spc_last_error()
+
+
+def test_offload_thresholds_match_the_oracle():
+    """Host arithmetic in the library (no GPU): bit-exact against the oracle's bisection."""
+    import json
+    import numpy as np
+
+    from oracle import spc_oracle as O
+    from speculative_kv_sparsity_amd import api
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "offload_thresholds.json")))
+    assert api.spc_offload_thresholds(g["gpu_bytes"], **g["model"]) == g["thresholds"]
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        model = dict(fixed_bytes=int(rng.integers(0, 10 ** 11)), token_bytes=int(rng.integers(0, 10 ** 6)),
+                     n_layers=int(rng.integers(1, 81)), batch=int(rng.integers(1, 65)),
+                     n_kv_heads=int(rng.integers(1, 33)), head_dim=int(rng.choice([64, 128, 576])),
+                     v_dim=int(rng.choice([0, 64, 128, 512])), budget=int(rng.integers(0, 8193)),
+                     elem_bytes=int(rng.choice([1, 2, 4])))
+        gpu = int(rng.integers(0, 3 * 10 ** 11))
+        assert api.spc_offload_thresholds(gpu, **model) == O.offload_thresholds(gpu, **model), (gpu, model)
+    lib = L.lib()
+    bad = L.SpcMemModel(-1, 0, 0, 1, 1, 1, 1, 1, 1, 1)
+    out = (ctypes.c_int32 * 2)()
+    assert lib.spc_offload_thresholds(ctypes.byref(bad), out) == L.SPC_ERR_INVALID_ARG
