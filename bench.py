@@ -60,6 +60,11 @@ def parse():
     ap.add_argument("--tail-layers", type=int, default=None,
                     help="layers in the last chunk (default n_layers // 8)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--hbm-gb", type=float, default=None,
+                    help="adaptive offloading: GPU memory (GB) for the model; layers whose full K/V fits stay on "
+                         "the GPU (default: every layer offloaded, the K/V store in pinned host memory)")
+    ap.add_argument("--weights-gb", type=float, default=16.0,
+                    help="target-model weights counted against --hbm-gb (8B parameters in bf16)")
     ap.add_argument("--t0", type=int, default=None,
                     help="first step of the measured window in the length schedule (default 0; batch-16 "
                          "growth: the last steps, where every sequence has reached 16384)")
@@ -218,13 +223,27 @@ def bench_gqa(args, p, torch, W):
         t0 = p.steps - total if p.name == "b16_grow" else 0
     t0 = max(0, min(t0, p.steps - total)) if p.steps >= total else 0
     w = W.generate(p, device="cuda", seed=args.seed, steps=max(total, t0 + total), pin_host=True)
-    dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=args.layer_chunks, tail_layers=args.tail_layers)
+    thresholds = None
+    if args.hbm_gb is not None:
+        # memory model: weights; per position the DLM key, the probabilities and the Top-K key of every
+        # head; per layer and position the target K and V (the four inputs the pages name)
+        thresholds = api.spc_offload_thresholds(
+            int(args.hbm_gb * 1e9), int(args.weights_gb * 1e9),
+            p.batch * (p.n_kv_heads * p.head_dim * p.elem_bytes + p.n_q_heads * 4 + p.n_groups * 4), p.n_layers,
+            p.batch, p.n_kv_heads, p.head_dim, p.v_dim, p.budget, p.elem_bytes)
+    dec = SparseDecoder(p, w.dlm_k, w.host_kv, layer_chunks=args.layer_chunks, tail_layers=args.tail_layers,
+                        thresholds=thresholds)
+    seq_len = [int(x) for x in w.lengths.max(axis=1)]
+
+    def step(t, timer=None):
+        dec.offload_for(seq_len[t])
+        dec.step(qs[t], lens[t], timer)
     lens = torch.as_tensor(w.lengths, device="cuda")
     qs = w.q.contiguous()
     torch.cuda.synchronize()
 
     for t in range(t0, t0 + Wm):                 # the first step is the cold full-budget load
-        dec.step(qs[t], lens[t])
+        step(t)
     torch.cuda.synchronize()
 
     # clean timed pass
@@ -232,47 +251,53 @@ def bench_gqa(args, p, torch, W):
     torch.cuda.synchronize()
     e0.record(dec.main)
     for t in range(t0 + Wm, t0 + Wm + K_):
-        dec.step(qs[t], lens[t])
+        step(t)
     e1.record(dec.main)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / K_
 
     # instrumented pass: per-stage event times and the rows actually moved
-    stage = {k: [] for k in ("scores", "topk", "plan", "copy", "attn")}
+    stage = {k: [] for k in ("scores", "topk", "plan", "copy", "attn", "attn_resident")}
     loaded_rows, sel_rows = [], []
     nch = len(dec.chunks)
     for t in range(t0 + Wm + K_, t0 + total):
         tm = StageTimer()
-        dec.step(qs[t], lens[t], timer=tm)
+        step(t, tm)
         torch.cuda.synchronize()
         stage["scores"].append(tm.ms("scores", "topk"))
         stage["topk"].append(tm.ms("topk", "plan"))
         stage["plan"].append(tm.ms("plan", "plan_end"))
-        for c in range(nch):
+        for c in range(len(dec.chunks)):
             stage["copy"].append(tm.ms(f"copy{c}", f"copy{c}_end"))
             stage["attn"].append(tm.ms(f"attn{c}", f"attn{c}_end"))
+        if dec.n_res:
+            stage["attn_resident"].append(tm.ms("attn_res", "attn_res_end"))
         loaded_rows.append(int(dec.load_count.sum().item()))
         sel_rows.append(int(dec.sel_count.sum().item()))
-    avg = {k: float(np.mean(v)) for k, v in stage.items()}
+    avg = {k: float(np.mean(v)) for k, v in stage.items() if v}
+    nch = len(dec.chunks)
 
     # isolated phase: each stage call launched back to back
     tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
     R = args.iso_reps
-    c0a, c0z = dec.chunks[0]
     iso_ms = {
         "scores": iso(torch, lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs,
                                                                  ws=dec.ws_scores, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel_idx, dec.sel_count,
                                                              ws=dec.ws_topk, stream=st), R),
-        "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l,
-                                                                 dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
-                                                                 dec.out, ws=dec.ws_attn[0], stream=st), R),
-        "copy": iso(torch, lambda st: api.spc_elastic_update(dec.shape, None, None, None, None, dec.load_pos,
-                                                             dec.load_slot, dec.load_count, dec.host_kv, dec.host_l,
-                                                             dec.dev_kv, dec.dev_l, c0a, c0z, flags=api.SPC_COPY,
-                                                             plan_stream=st, copy_stream=st),
-                    max(5, R // 3)),   # rewrites the same slots
     }
+    if nch:
+        c0a, c0z = dec.chunks[0]
+        iso_ms["attn"] = iso(torch, lambda st: api.spc_sparse_decode_attn(
+            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
+            dec.out, ws=dec.ws_attn[0], stream=st), R)
+        iso_ms["copy"] = iso(torch, lambda st: api.spc_elastic_update(
+            dec.shape, None, None, None, None, dec.load_pos, dec.load_slot, dec.load_count, dec.host_kv, dec.host_l,
+            dec.dev_kv, dec.dev_l, c0a, c0z, flags=api.SPC_COPY, plan_stream=st, copy_stream=st),
+            max(5, R // 3))   # rewrites the same slots
+    else:                     # every layer on the GPU: the gather from the full cache is the attention
+        c0a, c0z = 0, dec.n_res
+        iso_ms["attn"] = iso(torch, lambda st: dec.attend_resident(tq, st), R)
     # the retrieval head's front end (upstream of the step): new tokens -> query, key appended
     fw = W.generate_front(p, device="cuda", seed=args.seed, steps=1)
     head = RetrievalHead(dec.shape, fw)
@@ -285,40 +310,46 @@ def bench_gqa(args, p, torch, W):
     B, Hkv, Hq, d, K = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget
     n_valid = float(np.mean(w.lengths[t0 + Wm + K_:t0 + total].sum(axis=1)))
     row = 2 * d * eb                                             # one K||V row
+    sel_per_group = float(np.mean(sel_rows)) / (B * p.n_groups)
     # algorithmic bytes per call (one launch of the stage)
-    attn_bytes = B * lay0 * Hkv * K * row + B * lay0 * Hq * d * 4        # K/V read + out write
+    attn_bytes = B * lay0 * Hkv * sel_per_group * row + B * lay0 * Hq * d * 4   # K/V read + out write
     score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4              # keys read + probs write
-    copy_bytes = float(np.mean(loaded_rows)) * lay0 * row                # host reads per chunk
     front_bytes = ((Hq + Hkv) * d * fw.hidden + B * fw.hidden + fw.hidden + B * (Hq + Hkv) * d) * eb
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
+    off = p.n_layers - dec.n_res                                 # offloaded layers at the end of the run
 
-    traffic = measured_traffic(p.name, nch)
+    traffic = measured_traffic(p.name, nch) if thresholds is None else {}
     config = {"workload": WORKLOADS.get(p.name, p.name), "batch": B, "layers": p.n_layers, "q_heads": Hq,
               "kv_heads": Hkv, "head_dim": d, "cached_tokens": p.max_len,
               "mean_length": round(n_valid / B, 1), "first_step": t0, "kv_budget": K, "layer_chunks": nch,
               "chunk_layers": [z - a for a, z in dec.chunks], "parallelism": "single GPU"}
+    if thresholds is not None:
+        config.update({"hbm_gb": args.hbm_gb, "weights_gb": args.weights_gb, "offloaded_layers": off,
+                       "offload_thresholds": thresholds})
     result = _header(args, p, ms_per_step, config)
-    result.update({
-        "roofline": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
-                         "attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K)", nch,
-                         traffic.get("attn")),
-        "roofline_scores": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1,
-                                traffic.get("scores")),
-        "roofline_host_link": roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
-                                   "copy_kernel (elastic host->HBM gather)", nch, traffic.get("copy")),
-        "roofline_front_end": roof("hbm", front_bytes, iso_ms["front"], HBM_PEAK_GBS, "GB/s",
-                                   "front_gemv_kernel + front_finish_kernel (retrieval-head front end: embedding, "
-                                   f"input norm, Q/K projection of hidden {fw.hidden}, YaRN rotary, key append; "
-                                   "upstream of the step, not in value)", 1, traffic.get("front")),
-        "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
-        "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
-        "elastic": {"rows_loaded_per_step": float(np.mean(loaded_rows)),
-                    "rows_selected_per_step": float(np.mean(sel_rows)),
-                    "transfer_fraction_vs_full_reload":
-                        round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
-                    "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * p.n_layers * row)},
-    })
+    attn_kernel = ("attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K" +
+                   (", slots of the offloaded layers)" if nch else
+                    ", selected rows gathered from the GPU-resident full cache)"))
+    result["roofline"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s", attn_kernel,
+                              max(nch, 1), traffic.get("attn"))
+    result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
+                                     "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1,
+                                     traffic.get("scores"))
+    if nch:
+        copy_bytes = float(np.mean(loaded_rows)) * lay0 * row            # host reads per chunk
+        result["roofline_host_link"] = roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
+                                            "copy_kernel (elastic host->HBM gather)", nch, traffic.get("copy"))
+    result["roofline_front_end"] = roof("hbm", front_bytes, iso_ms["front"], HBM_PEAK_GBS, "GB/s",
+                                        "front_gemv_kernel + front_finish_kernel (retrieval-head front end: "
+                                        f"embedding, input norm, Q/K projection of hidden {fw.hidden}, YaRN rotary, "
+                                        "key append; upstream of the step, not in value)", 1, traffic.get("front"))
+    result["stage_us_in_step"] = {k: round(v * 1e3, 2) for k, v in avg.items()}
+    result["call_us_isolated"] = {k: round(v * 1e3, 2) for k, v in iso_ms.items()}
+    result["elastic"] = {"rows_loaded_per_step": float(np.mean(loaded_rows)),
+                         "rows_selected_per_step": float(np.mean(sel_rows)),
+                         "transfer_fraction_vs_full_reload":
+                             round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
+                         "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * off * row)}
     if args.calibrate_copy:
         calibration_copies(torch)
     if not args.no_cpu_baseline:

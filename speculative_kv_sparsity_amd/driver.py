@@ -50,10 +50,18 @@ class SparseDecoder:
 
     dlm_k:   device [B][H_kv][L][d]  retrieval-head key cache
     host_kv: pinned host [B][layers][H_kv][L][2][d]  full target K/V store
+
+    ``thresholds`` (optional, from ``api.spc_offload_thresholds``) turns on adaptive offloading
+    (SpeContext blog section 7 "C3"; paper summary section 6.2): the decoder starts with every
+    layer's full K/V on the GPU and offloads the last layer still there each time the sequence
+    length reaches the next threshold (``offload_for``).  GPU-resident layers attend over the
+    selected positions gathered from their full cache; offloaded layers use the elastic slots.
+    Without thresholds every layer is offloaded from the start (the host-resident workloads).
     """
 
     def __init__(self, p: Preset, dlm_k: torch.Tensor, host_kv: torch.Tensor, layer_chunks: int = 2,
-                 tail_layers: Optional[int] = None, device: Optional[torch.device] = None):
+                 tail_layers: Optional[int] = None, device: Optional[torch.device] = None,
+                 thresholds: Optional[List[int]] = None):
         assert p.kind in ("gqa", "mha", "mqa"), "MLA uses MlaDecoder"
         self.p = p
         dev = device or dlm_k.device
@@ -80,18 +88,62 @@ class SparseDecoder:
         self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
                                    dtype=torch.uint8, device=dev)
         self.q_l = api.q_layout(Hq * d, 0, d)   # the same query serves every layer
-        self.chunks: List[tuple] = layer_chunk_bounds(p.n_layers, layer_chunks, tail_layers)
-        # one attention workspace per layer chunk: chunks run concurrently on two streams
-        self.ws_attn = [torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
-                                    dtype=torch.uint8, device=dev) for _ in self.chunks]
+        self.layer_chunks, self.tail_layers = layer_chunks, tail_layers
+        self.thresholds = list(thresholds) if thresholds is not None else None
+        if self.thresholds is None:
+            self.n_off = p.n_layers
+            self.full_kv = None
+        else:
+            # every layer's full K/V on the GPU to start with (the prefill's cache)
+            self.n_off = 0
+            self.full_kv = torch.empty((B, p.n_layers, Hkv, L, 2, d), dtype=p.torch_dtype, device=dev)
+            self.full_kv.copy_(host_kv)
+            self.full_l = api.kv_layout(self.full_kv)
+            # a full reload of an offloaded layer: every slot x from host row slot_pos[x]
+            self.all_slots = torch.arange(K, dtype=torch.int32, device=dev).repeat(B, G, 1).contiguous()
+            self.all_count = torch.full((B, G), K, **i32)
         self.main = torch.cuda.current_stream(dev)
         self.side = torch.cuda.Stream(device=dev)
-        self.ev_copy = [torch.cuda.Event() for _ in self.chunks]
+        self.ev_sel = torch.cuda.Event()
         self.ev_attn = torch.cuda.Event()
+        self._layout()
         self.reset()
+
+    def _layout(self) -> None:
+        """Layer chunks of the offloaded layers [n_res, n_layers) and the events / workspaces they need."""
+        p = self.p
+        self.n_res = p.n_layers - self.n_off
+        self.chunks: List[tuple] = []
+        if self.n_off:
+            self.chunks = [(self.n_res + a, self.n_res + z)
+                           for a, z in layer_chunk_bounds(self.n_off, self.layer_chunks, self.tail_layers)]
+        self.ev_copy = [torch.cuda.Event() for _ in self.chunks]
+        # one attention workspace per call that may run concurrently: the resident layers + each chunk
+        n_ws = len(self.chunks) + 1
+        if not hasattr(self, "ws_attn") or len(self.ws_attn) < n_ws:
+            self.ws_attn = [torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
+                                        dtype=torch.uint8, device=self.device) for _ in range(n_ws)]
 
     def reset(self, batch_index: int = -1) -> None:
         api.spc_elastic_reset(self.shape, batch_index, self.slot_pos, self.resident_bm, stream=self.main)
+
+    def offload_for(self, seq_len: int) -> int:
+        """The pages' rule: while seq_len reaches the threshold of the current count, offload the last
+        layer still on the GPU.  A newly offloaded layer's slots are filled with the rows of the
+        current resident set (the next plan then loads only what changes).  Returns the count."""
+        if self.thresholds is None:
+            return self.n_off
+        c = self.n_off
+        while c < self.p.n_layers and seq_len >= self.thresholds[c]:
+            c += 1
+        if c > self.n_off:
+            a, z = self.p.n_layers - c, self.p.n_layers - self.n_off
+            api.spc_elastic_update(self.shape, None, None, None, None, self.slot_pos, self.all_slots, self.all_count,
+                                   self.host_kv, self.host_l, self.dev_kv, self.dev_l, a, z, flags=api.SPC_COPY,
+                                   plan_stream=self.main, copy_stream=self.main)
+            self.n_off = c
+            self._layout()
+        return self.n_off
 
     # --- the four stages --------------------------------------------------------------
     def scores(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
@@ -119,7 +171,13 @@ class SparseDecoder:
     def attend_chunk(self, q: torch.Tensor, c: int, stream=None) -> None:
         a, z = self.chunks[c]
         api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.dev_kv, self.dev_l, self.slot_pos, None,
-                                   api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn[c],
+                                   api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn[c + 1],
+                                   stream=self.main if stream is None else stream)
+
+    def attend_resident(self, q: torch.Tensor, stream=None) -> None:
+        """Layers still on the GPU: the selected positions gathered from their full cache."""
+        api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.full_kv, self.full_l, self.sel_idx, self.sel_count,
+                                   api.SPC_ROWS_GATHER, 0, self.n_res, self.out, ws=self.ws_attn[0],
                                    stream=self.main if stream is None else stream)
 
     # --- one step -----------------------------------------------------------------------
@@ -150,6 +208,19 @@ class SparseDecoder:
         mark("plan", self.main)
         self.plan()
         mark("plan_end", self.main)
+        side_used = False
+        if self.n_res:
+            if self.chunks:                       # overlap the resident layers with the copies
+                self.ev_sel.record(self.main)
+                self.side.wait_event(self.ev_sel)
+                mark("attn_res", self.side)
+                self.attend_resident(q, self.side)
+                mark("attn_res_end", self.side)
+                side_used = True
+            else:
+                mark("attn_res", self.main)
+                self.attend_resident(q)
+                mark("attn_res_end", self.main)
         last = len(self.chunks) - 1
         for c in range(len(self.chunks)):
             mark(f"copy{c}", self.main)
@@ -161,10 +232,12 @@ class SparseDecoder:
                 mark(f"attn{c}", self.side)
                 self.attend_chunk(q, c, self.side)
                 mark(f"attn{c}_end", self.side)
-        mark(f"attn{last}", self.main)
-        self.attend_chunk(q, last)
-        mark(f"attn{last}_end", self.main)
-        if last > 0:
+                side_used = True
+        if self.chunks:
+            mark(f"attn{last}", self.main)
+            self.attend_chunk(q, last)
+            mark(f"attn{last}_end", self.main)
+        if side_used:
             self.ev_attn.record(self.side)
             self.main.wait_event(self.ev_attn)
 

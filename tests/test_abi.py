@@ -152,3 +152,22 @@ def test_offload_thresholds_match_the_oracle():
     bad = L.SpcMemModel(-1, 0, 0, 1, 1, 1, 1, 1, 1, 1)
     out = (ctypes.c_int32 * 2)()
     assert lib.spc_offload_thresholds(ctypes.byref(bad), out) == L.SPC_ERR_INVALID_ARG
+
+
+def test_thresholds_from_the_memory_model():
+    """The library's thresholds for the 32K step's shapes on a GPU budget that holds about 20 of the 32
+    layers' full K/V at 32K: the count of offloaded layers follows the pages' loop."""
+    from oracle import spc_oracle as O
+    from speculative_kv_sparsity_amd import api
+    from speculative_kv_sparsity_amd import workload as W
+    p = W.PRESETS["b1_32k"]
+    per_layer_32k = p.batch * p.n_kv_heads * (p.head_dim + p.v_dim) * 2 * p.max_len
+    model = dict(fixed_bytes=16 * 10 ** 9, token_bytes=p.n_kv_heads * p.head_dim * 2 + p.n_q_heads * 4,
+                 n_layers=p.n_layers, batch=p.batch, n_kv_heads=p.n_kv_heads, head_dim=p.head_dim, v_dim=p.v_dim,
+                 budget=p.budget, elem_bytes=2)
+    gpu = 16 * 10 ** 9 + 20 * per_layer_32k
+    th = api.spc_offload_thresholds(gpu, **model)
+    assert th == O.offload_thresholds(gpu, **model)
+    c = O.offloaded_layers(p.max_len, th)
+    assert 12 <= c <= 16
+    assert O.memory_bytes(p.max_len, c, **model) <= gpu < O.memory_bytes(p.max_len, c - 1, **model)
