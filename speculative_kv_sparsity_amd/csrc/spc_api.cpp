@@ -214,7 +214,8 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
     return fail(SPC_ERR_UNSUPPORTED, "head_dim 576 reads V from the latent row itself (s_kv must be 0)");
   const int eb = elem_bytes(s);
   const int qeb = spc::mla_shape(*s) ? 4 : eb;   // MLA: float32 absorbed query
-  if (!aligned16(q) || !aligned16(kv)) return fail(SPC_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out))
+    return fail(SPC_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned");
   if ((q_l->s_b * qeb) % 16 || (q_l->s_layer * qeb) % 16 || (q_l->s_head * qeb) % 16)
     return fail(SPC_ERR_INVALID_ARG, "query strides must be multiples of 16 bytes");
   if ((kv_l->s_b * eb) % 16 || (kv_l->s_layer * eb) % 16 || (kv_l->s_head * eb) % 16 || (kv_l->s_row * eb) % 16 ||

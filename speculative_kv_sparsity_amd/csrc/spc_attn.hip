@@ -22,7 +22,7 @@
 // attn_split_latent_kernel  the same for MLA latent rows, where V is the first
 //   v_dim elements of the K row (read once, used twice) and one head per group.
 // attn_combine_kernel  merges the splits of every head with their log-sum-exp
-//   weights into the float32 output.
+//   weights into the float32 output, 4 dims per thread.
 #include "spc_common.h"
 #include "spc_launch.h"
 
@@ -406,19 +406,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
 }
 
 constexpr int kCombineChunk = 16;
-
-// One thread per (instance, head chunk, head, dim); the split partials are read
-// 16 at a time (all loads of a chunk issued together) and merged online.
+// One thread per (instance, head chunk, head, 4 consecutive dims): the split
+// weights (max, sum) of the head are read once for its 4 dims, the partial
+// outputs as 16-byte vectors, 16 splits at a time (all loads of a chunk issued
+// together), merged online.
 template <int GQC>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml,
                                                            float* __restrict__ out, int DV, int Hq, int n_layers,
                                                            int n_groups, int layer_begin, int n_lay, int nsplit,
-                                                           int nhc, int64_t n_out) {
+                                                           int nhc, int64_t n_out4) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_out) return;
-  const int d = (int)(t % DV);
-  const int64_t ih = t / DV;                 // ((inst * nhc + hcix) * GQC + h)
+  if (t >= n_out4) return;
+  const int DV4 = DV / 4;
+  const int d4 = (int)(t % DV4);
+  const int64_t ih = t / DV4;                // ((inst * nhc + hcix) * GQC + h)
   const int h = (int)(ih % GQC);
   const int64_t ic = ih / GQC;               // inst * nhc + hcix
   const int hcix = (int)(ic % nhc);
@@ -429,18 +431,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int b = bl / n_lay;
   const int head = r * (Hq / n_groups) + hcix * GQC + h;
   const size_t pb = (size_t)ic * nsplit;
-  float M = -INFINITY, L = 0.f, acc = 0.f;
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < nsplit; s0 += kCombineChunk) {
     float2 ml[kCombineChunk];
-    float po[kCombineChunk];
+    float4 po[kCombineChunk];
 #pragma unroll
     for (int i = 0; i < kCombineChunk; ++i) {
       if (s0 + i < nsplit) {
         ml[i] = part_ml[(pb + s0 + i) * GQC + h];
-        po[i] = part_o[((pb + s0 + i) * GQC + h) * DV + d];
+        po[i] = reinterpret_cast<const float4*>(part_o + ((pb + s0 + i) * GQC + h) * DV)[d4];
       } else {
         ml[i] = make_float2(-INFINITY, 0.f);
-        po[i] = 0.f;
+        po[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     float Mc = M;
@@ -450,18 +453,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     if (Mc == -INFINITY) continue;
     const float rescale = M == -INFINITY ? 0.f : __expf(M - Mc);
     L *= rescale;
-    acc *= rescale;
+    acc.x *= rescale; acc.y *= rescale; acc.z *= rescale; acc.w *= rescale;
 #pragma unroll
     for (int i = 0; i < kCombineChunk; ++i) {
       if (ml[i].y > 0.f) {
         const float w = __expf(ml[i].x - Mc);
         L += ml[i].y * w;
-        acc += po[i] * w;
+        acc.x += po[i].x * w; acc.y += po[i].y * w; acc.z += po[i].z * w; acc.w += po[i].w * w;
       }
     }
     M = Mc;
   }
-  out[(((size_t)b * n_layers + layer_begin + lo) * Hq + head) * DV + d] = L > 0.f ? acc / L : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  reinterpret_cast<float4*>(out + (((size_t)b * n_layers + layer_begin + lo) * Hq + head) * DV)[d4] =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 int head_chunk(const spc_shape& s) {
@@ -569,13 +574,13 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  const int64_t n_out = (int64_t)n_inst * nhc * gqc * s.v_dim;
-  const dim3 g2((unsigned)((n_out + 255) / 256));
+  const int64_t n_out4 = (int64_t)n_inst * nhc * gqc * (s.v_dim / 4);
+  const dim3 g2((unsigned)((n_out4 + 255) / 256));
   switch (gqc) {
 #define SPC_CASE(N)                                                                                         \
   case N:                                                                                                   \
     attn_combine_kernel<N><<<g2, 256, 0, st>>>(a.part_o, a.part_ml, out, s.v_dim, s.n_q_heads, s.n_layers, \
-                                               s.n_groups, layer_begin, n_lay, nsplit, nhc, n_out);         \
+                                               s.n_groups, layer_begin, n_lay, nsplit, nhc, n_out4);        \
     break;
     SPC_CASE(1)
     SPC_CASE(2)
