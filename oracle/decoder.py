@@ -85,3 +85,30 @@ class OracleDecoder:
                      for b in range(self.B)]
         self.prev_sel = sel
         return dict(probs=probs, sel=sel, plans=plans, out=out, overlap=stats)
+
+
+class LagOneOracleDecoder(OracleDecoder):
+    """The pipelined loop of the blog's section 4: at step t the retrieval head's selection S_t+1
+    (from token t) is loaded while the target model attends over S_t, the selection made at the
+    previous step.  The first step has no previous selection: it attends over its own (the
+    pipeline's warm-up, which the blog's pseudocode omits).  The slots form a pool of ``pool``
+    entries per (b, group) (the union of two selections must fit)."""
+
+    def __init__(self, batch, n_q_heads, n_kv_heads, n_groups, head_dim, budget, scale, dtype, pool: int):
+        super().__init__(batch, n_q_heads, n_kv_heads, n_groups, head_dim, budget, scale, dtype)
+        self.slot_pos = [[np.full(pool, -1, dtype=np.int64) for _ in range(n_groups)] for _ in range(batch)]
+        self.current: Optional[List[List[np.ndarray]]] = None
+
+    def plan_lag1(self, nxt: List[List[np.ndarray]]):
+        """O4 of the pipelined loop; returns (plans[b][r] = (to_load, load_slot, attend_slots), current)."""
+        cur = nxt if self.current is None else self.current
+        plans = []
+        for b in range(self.B):
+            row = []
+            for r in range(self.G):
+                to_load, load_slot, new, attend = O.elastic_plan_lag1(cur[b][r], nxt[b][r], self.slot_pos[b][r])
+                self.slot_pos[b][r] = new
+                row.append((to_load, load_slot, attend))
+            plans.append(row)
+        self.current = nxt
+        return plans, cur

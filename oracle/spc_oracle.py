@@ -199,6 +199,37 @@ def elastic_plan(selected: Sequence[int], slot_pos: Sequence[int]) -> Tuple[np.n
             np.asarray(new, dtype=np.int64))
 
 
+def elastic_plan_lag1(current: Sequence[int], nxt: Sequence[int], slot_pos: Sequence[int]
+                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """The elastic plan of the pipelined loop (blog section 4: "the retrieval head predicts the
+    positions of the next round while the target model uses the sparse KV prepared last round").
+
+    current: S_t, the selection the target model attends over in this step (loaded last round);
+    nxt:     S_t+1, the selection the retrieval head just made for the next step;
+    slot_pos: the pool's slot map before the step (-1 = empty).
+    A slot may be overwritten only if its position is in neither selection: the current one is
+    being read by this step's attention, the next one will be (paper summary section 5.4 tracks
+    the prior, current and resident selections).  Returns (to_load, load_slot, new_slot_pos,
+    attend_slots): to_load = sorted(S_t+1 - resident) into the ascending free slots, leftover free
+    slots emptied, and the ascending slots holding S_t after the update.
+    """
+    keep = set(int(p) for p in current) | set(int(p) for p in nxt)
+    slots = [int(p) for p in slot_pos]
+    resident = set(p for p in slots if p != -1)
+    to_load = sorted(set(int(p) for p in nxt) - resident)
+    free = sorted(x for x in range(len(slots)) if slots[x] == -1 or slots[x] not in keep)
+    assert len(to_load) <= len(free), "pool exceeded: more positions to load than free slots"
+    new = list(slots)
+    for i, pos in enumerate(to_load):
+        new[free[i]] = pos
+    for x in free[len(to_load):]:
+        new[x] = -1
+    cur = set(int(p) for p in current)
+    attend = sorted(x for x in range(len(new)) if new[x] in cur)
+    return (np.asarray(to_load, dtype=np.int64), np.asarray(free[:len(to_load)], dtype=np.int64),
+            np.asarray(new, dtype=np.int64), np.asarray(attend, dtype=np.int64))
+
+
 # ----------------------------------------------------------------------------
 # O5: elastic copy
 # ----------------------------------------------------------------------------

@@ -346,3 +346,56 @@ def check_offload_invariants(offload_thresholds, memory_bytes):
                 assert memory_bytes(0, c, **model) > gpu
             elif t < 2 ** 31 - 1:
                 assert memory_bytes(t - 1, c, **model) <= gpu < memory_bytes(t, c, **model)
+
+
+# ----------------------------------------------------------------------------- pipelined loop (lag 1)
+
+def check_plan_lag1_worked_example(elastic_plan_lag1):
+    g = json.load(open(os.path.join(GOLDEN, "elastic_lag1_example.json")))
+    for st in g["steps"]:
+        to_load, load_slot, new, attend = elastic_plan_lag1(st["current"], st["next"], st["slot_pos"])
+        assert list(to_load) == st["to_load"] and list(load_slot) == st["load_slot"]
+        assert list(new) == st["new_slot_pos"] and list(attend) == st["attend_slots"]
+
+
+def check_plan_lag1_reduces_to_lag0(elastic_plan_lag1, elastic_plan):
+    """With the same selection as current and next the pipelined plan is the plan of the blog's loop."""
+    rng = np.random.default_rng(21)
+    K, L = 16, 60
+    slots = np.full(K, -1)
+    for _ in range(20):
+        S = np.sort(rng.choice(L, size=int(rng.integers(0, K + 1)), replace=False))
+        a = elastic_plan(S, slots)
+        b = elastic_plan_lag1(S, S, slots)
+        for x, y in zip(a, b[:3]):
+            np.testing.assert_array_equal(x, y)
+        slots = a[2]
+        np.testing.assert_array_equal(np.sort(slots[b[3]]), S)
+
+
+def check_plan_lag1_invariants(elastic_plan_lag1):
+    """Over random correlated sequences with a pool of twice the budget: the pool holds exactly the
+    union of current and next; the current selection's slots never move while it is attended; loads
+    go to slots that held neither selection; the attended slots hold exactly the current selection."""
+    rng = np.random.default_rng(22)
+    K, L = 12, 50
+    slots = np.full(2 * K, -1)
+    nxt = np.sort(rng.choice(L, size=K, replace=False))
+    cur = nxt
+    for _ in range(40):
+        before = np.array(slots)
+        to_load, load_slot, new, attend = elastic_plan_lag1(cur, nxt, before)
+        U = set(cur.tolist()) | set(nxt.tolist())
+        assert set(p for p in new.tolist() if p >= 0) == U
+        for x, p in enumerate(before.tolist()):
+            if p in set(cur.tolist()):
+                assert new[x] == p
+        assert not (set(to_load.tolist()) & set(p for p in before.tolist() if p >= 0))
+        for x in load_slot.tolist():
+            assert before[x] == -1 or before[x] not in U
+        assert sorted(new[attend].tolist()) == sorted(cur.tolist())
+        slots = new
+        cur = nxt
+        keep = rng.choice(cur, size=int(rng.integers(K // 2, K + 1)), replace=False)
+        fresh = rng.choice(np.setdiff1d(np.arange(L), keep), size=K - len(keep), replace=False)
+        nxt = np.sort(np.concatenate([keep, fresh]))

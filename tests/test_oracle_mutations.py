@@ -165,3 +165,17 @@ def test_pins_catch_offload_mistakes():
     _fails(pins.check_offload_golden, last_fitting, O.offloaded_layers)
     _fails(pins.check_offload_golden, O.offload_thresholds, strict_loop)
     _fails(pins.check_offload_invariants, O.offload_thresholds, no_working_set)
+
+
+def test_pins_catch_lag1_plan_mistakes():
+    def frees_current(cur, nxt, slots):          # reuses the slots the current step still reads
+        return O.elastic_plan_lag1(nxt, nxt, slots)
+
+    def attend_before_update(cur, nxt, slots):   # attended slots taken from the map before the loads
+        a, b, new, _ = O.elastic_plan_lag1(cur, nxt, slots)
+        c = set(int(p) for p in cur)
+        return a, b, new, np.asarray([x for x, p in enumerate(slots) if p in c], dtype=np.int64)
+
+    _fails(pins.check_plan_lag1_worked_example, frees_current)
+    _fails(pins.check_plan_lag1_invariants, frees_current)
+    _fails(pins.check_plan_lag1_reduces_to_lag0, attend_before_update, O.elastic_plan)

@@ -93,3 +93,15 @@ def test_offload_thresholds_worked_instance():
 
 def test_offload_thresholds_are_first_lengths_that_do_not_fit():
     pins.check_offload_invariants(O.offload_thresholds, O.memory_bytes)
+
+
+def test_plan_lag1_worked_example():
+    pins.check_plan_lag1_worked_example(O.elastic_plan_lag1)
+
+
+def test_plan_lag1_reduces_to_the_blog_loop_plan():
+    pins.check_plan_lag1_reduces_to_lag0(O.elastic_plan_lag1, O.elastic_plan)
+
+
+def test_plan_lag1_invariants():
+    pins.check_plan_lag1_invariants(O.elastic_plan_lag1)
