@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--hbm-gb", type=float, default=None,
                     help="adaptive offloading: GPU memory (GB) for the model; layers whose full K/V fits stay on "
                          "the GPU (default: every layer offloaded, the K/V store in pinned host memory)")
+    ap.add_argument("--lag", type=int, default=0, choices=(0, 1),
+                    help="1: the pipelined loop (the step attends over the previous step's selection while the "
+                         "next one loads)")
     ap.add_argument("--weights-gb", type=float, default=16.0,
                     help="target-model weights counted against --hbm-gb (8B parameters in bf16)")
     ap.add_argument("--t0", type=int, default=None,
@@ -190,7 +193,12 @@ def main():
 
     torch.cuda.set_device(0)
     p = W.PRESETS[args.config]
-    result = bench_mla(args, p, torch, W) if p.kind == "mla" else bench_gqa(args, p, torch, W)
+    if p.kind == "mla":
+        result = bench_mla(args, p, torch, W)
+    elif args.lag == 1:
+        result = bench_lag1(args, p, torch, W)
+    else:
+        result = bench_gqa(args, p, torch, W)
     print(json.dumps(result), flush=True)
 
 
@@ -354,6 +362,95 @@ def bench_gqa(args, p, torch, W):
         calibration_copies(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, w, t0 + Wm, args.cpu_seconds)
+    return result
+
+
+def bench_lag1(args, p, torch, W):
+    """The pipelined loop: step t's copy loads step t+1's rows while step t attends over the rows
+    loaded for it one step earlier."""
+    from speculative_kv_sparsity_amd import api
+    from speculative_kv_sparsity_amd.driver import LagOneDecoder, StageTimer
+
+    K_, Wm = args.steps, args.warmup
+    total = Wm + 2 * K_
+    t0 = args.t0
+    if t0 is None:
+        t0 = p.steps - total if p.name == "b16_grow" else 0
+    t0 = max(0, min(t0, p.steps - total)) if p.steps >= total else 0
+    w = W.generate(p, device="cuda", seed=args.seed, steps=max(total, t0 + total), pin_host=True)
+    dec = LagOneDecoder(p, w.dlm_k, w.host_kv)
+    lens = torch.as_tensor(w.lengths, device="cuda")
+    qs = w.q.contiguous()
+    torch.cuda.synchronize()
+    for t in range(t0, t0 + Wm):
+        dec.step(qs[t], lens[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(dec.main)
+    for t in range(t0 + Wm, t0 + Wm + K_):
+        dec.step(qs[t], lens[t])
+    e1.record(dec.main)
+    dec.side.synchronize()
+    torch.cuda.synchronize()
+    # the last step's copy (of the rows of a step not run) is outside the bracket; it overlapped the
+    # attention of that step, as every copy overlaps the next step's work
+    ms_per_step = e0.elapsed_time(e1) / K_
+    stage = {k: [] for k in ("scores", "topk", "plan", "copy", "attn")}
+    loaded, sel_rows = [], []
+    for t in range(t0 + Wm + K_, t0 + total):
+        nx = dec.t % 2
+        tm = StageTimer()
+        dec.step(qs[t], lens[t], timer=tm)
+        torch.cuda.synchronize()
+        for a, z in (("scores", "topk"), ("topk", "plan"), ("plan", "plan_end"), ("copy", "copy_end"),
+                     ("attn", "attn_end")):
+            stage[a].append(tm.ms(a, z))
+        loaded.append(int(dec.load_count[nx].sum().item()))
+        sel_rows.append(int(dec.cnt[nx].sum().item()))
+    avg = {k: float(np.mean(v)) for k, v in stage.items()}
+    tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
+    R = args.iso_reps
+    nx = (dec.t - 1) % 2
+    iso_ms = {
+        "scores": iso(torch, lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs,
+                                                                 ws=dec.ws_scores, stream=st), R),
+        "topk": iso(torch, lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel[nx], dec.cnt[nx],
+                                                             ws=dec.ws_topk, stream=st), R),
+        "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
+            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
+            0, p.n_layers, dec.out, ws=dec.ws_attn, stream=st), R),
+        "copy": iso(torch, lambda st: api.spc_elastic_update(
+            dec.pool_shape, None, None, None, None, dec.load_pos[nx], dec.load_slot[nx], dec.load_count[nx],
+            dec.host_kv, dec.host_l, dec.dev_kv, dec.dev_l, 0, p.n_layers, flags=api.SPC_COPY, plan_stream=st,
+            copy_stream=st), max(5, R // 3)),
+    }
+    eb = p.elem_bytes
+    B, Hkv, Hq, d, K = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget
+    n_valid = float(np.mean(w.lengths[t0 + Wm + K_:t0 + total].sum(axis=1)))
+    row = 2 * d * eb
+    sel_per_group = float(np.mean(sel_rows)) / (B * p.n_groups)
+    attn_bytes = B * p.n_layers * Hkv * sel_per_group * row + B * p.n_layers * Hq * d * 4
+    score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4
+    copy_bytes = float(np.mean(loaded)) * p.n_layers * row
+    config = {"workload": WORKLOADS.get(p.name, p.name), "batch": B, "layers": p.n_layers, "q_heads": Hq,
+              "kv_heads": Hkv, "head_dim": d, "cached_tokens": p.max_len, "mean_length": round(n_valid / B, 1),
+              "first_step": t0, "kv_budget": K, "pipeline": "lag 1 (attention over the previous step's selection)",
+              "slot_pool": dec.P, "parallelism": "single GPU"}
+    result = _header(args, p, ms_per_step, config)
+    result["roofline"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                              "attn_split_kernel + attn_combine_kernel (the pool's rows of the current selection, "
+                              "gathered)", 1)
+    result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
+                                     "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1)
+    result["roofline_host_link"] = roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
+                                        "copy_kernel (elastic host->HBM gather, every layer in one launch)", 1)
+    result["stage_us_in_step"] = {k: round(v * 1e3, 2) for k, v in avg.items()}
+    result["call_us_isolated"] = {k: round(v * 1e3, 2) for k, v in iso_ms.items()}
+    result["elastic"] = {"rows_loaded_per_step": float(np.mean(loaded)),
+                         "rows_selected_per_step": float(np.mean(sel_rows)),
+                         "transfer_fraction_vs_full_reload": round(float(np.mean(loaded)) / float(np.mean(sel_rows)),
+                                                                   4),
+                         "host_link_bytes_per_step": int(copy_bytes)}
     return result
 
 

@@ -228,6 +228,33 @@ int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos
                       void* stream);
 
 /*
+ * Stage 3 for the pipelined loop of the SpeContext blog's section 4 (the
+ * retrieval head predicts the positions of the next round while the target
+ * model attends over the sparse KV prepared in the last one; paper summary
+ * section 5.4: prior, current and resident selections).  Per (b, group):
+ *   keep       = slots whose position is in cur or next (cur is being attended
+ *                in this step, next will be);
+ *   to_load    = next - resident, ascending, into the ascending remaining slots;
+ *                leftover remaining slots become empty (-1);
+ *   attend_rows = the ascending slots that hold cur after the update, followed by -1;
+ *                attend_count = |cur| (the row list of spc_sparse_decode_attn in
+ *                SPC_ROWS_GATHER mode over the pool).
+ *   s        shape whose budget is the pool size P (>= 2 * sel_budget, <= 8192)
+ *   sel_cur, cur_count, sel_next, next_count  device int32 [B][G][sel_budget], [B][G]
+ *   slot_pos device int32 [B][G][P], resident_bm [B][G][ceil(max_len/32)]: state, in/out
+ *   load_pos, load_slot [B][G][P], load_count [B][G]: out (input of spc_elastic_update SPC_COPY
+ *            with the same pool shape)
+ *   attend_rows [B][G][sel_budget], attend_count [B][G]: out
+ * The copy that follows may run concurrently with this step's attention over
+ * attend_rows (they touch different slots); it must follow the previous step's
+ * attention, whose rows it may reuse.
+ */
+int spc_elastic_plan_lag1(const spc_shape* s, int32_t sel_budget, const int32_t* sel_cur, const int32_t* cur_count,
+                          const int32_t* sel_next, const int32_t* next_count, int32_t* slot_pos,
+                          uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                          int32_t* attend_rows, int32_t* attend_count, void* stream);
+
+/*
  * Adaptive memory management (SpeContext blog section 7 "C3"; paper summary
  * sections 6.1-6.2.1): layers are offloaded to host memory one at a time, the
  * last layer still on the GPU first, as the sequence grows; an offloaded layer

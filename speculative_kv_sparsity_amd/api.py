@@ -20,7 +20,8 @@ __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version",
            "spc_retrieval_scores", "spc_group_max_topk", "spc_elastic_update", "spc_elastic_reset",
            "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
            "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "SPC_CALL_FRONT", "spc_mla_absorb_q",
-           "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds"]
+           "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds",
+           "spc_elastic_plan_lag1"]
 
 
 class SpcError(RuntimeError):
@@ -177,3 +178,16 @@ def spc_offload_thresholds(gpu_bytes: int, fixed_bytes: int, token_bytes: int, n
     out = (ctypes.c_int32 * (int(n_layers) + 1))()
     _check(L.lib().spc_offload_thresholds(ctypes.byref(m), out))
     return list(out)
+
+
+def spc_elastic_plan_lag1(pool_shape: SpcShape, sel_budget: int, sel_cur, cur_count, sel_next, next_count, slot_pos,
+                          resident_bm, load_pos, load_slot, load_count, attend_rows, attend_count, stream=None) -> None:
+    for t, n in ((sel_cur, "sel_cur"), (cur_count, "cur_count"), (sel_next, "sel_next"), (next_count, "next_count"),
+                 (slot_pos, "slot_pos"), (resident_bm, "resident_bm"), (load_pos, "load_pos"),
+                 (load_slot, "load_slot"), (load_count, "load_count"), (attend_rows, "attend_rows"),
+                 (attend_count, "attend_count")):
+        _dev(t, n)
+    _check(L.lib().spc_elastic_plan_lag1(ctypes.byref(pool_shape), int(sel_budget), _ptr(sel_cur), _ptr(cur_count),
+                                         _ptr(sel_next), _ptr(next_count), _ptr(slot_pos), _ptr(resident_bm),
+                                         _ptr(load_pos), _ptr(load_slot), _ptr(load_count), _ptr(attend_rows),
+                                         _ptr(attend_count), _stream(stream)))

@@ -325,4 +325,25 @@ int spc_offload_thresholds(const spc_mem_model* m, int32_t* threshold) {
   return ok();
 }
 
+int spc_elastic_plan_lag1(const spc_shape* s, int32_t sel_budget, const int32_t* sel_cur, const int32_t* cur_count,
+                          const int32_t* sel_next, const int32_t* next_count, int32_t* slot_pos,
+                          uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                          int32_t* attend_rows, int32_t* attend_count, void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!sel_cur || !cur_count || !sel_next || !next_count || !slot_pos || !resident_bm || !load_pos || !load_slot ||
+      !load_count || !attend_rows || !attend_count)
+    return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (sel_budget < 1 || (int64_t)s->budget < 2 * (int64_t)sel_budget)
+    return fail(SPC_ERR_INVALID_ARG, "pool (shape budget %d) must hold two selections of %d", s->budget, sel_budget);
+  if (s->budget > spc::kPlanMaxBudget)
+    return fail(SPC_ERR_UNSUPPORTED, "pool %d exceeds the plan kernel's %d", s->budget, spc::kPlanMaxBudget);
+  if (3 * sel_budget + 2 * s->budget > spc::kPlanLag1MaxWords)
+    return fail(SPC_ERR_UNSUPPORTED, "pool %d and selections of %d exceed the plan kernel's LDS", s->budget,
+                sel_budget);
+  const hipError_t e = spc::launch_plan_lag1(*s, sel_budget, sel_cur, cur_count, sel_next, next_count, slot_pos,
+                                             resident_bm, load_pos, load_slot, load_count, attend_rows, attend_count,
+                                             as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "pipelined elastic plan launch");
+}
+
 }  // extern "C"

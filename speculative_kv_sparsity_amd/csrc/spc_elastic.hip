@@ -11,6 +11,7 @@
 //   ordered compactions (block scans over contiguous ranges) give the freed
 //   slots and the positions to load, both ascending; the i-th position goes to
 //   the i-th freed slot.  Slot map and bitmap are then updated in place.
+// plan_lag1_kernel  the same for the pipelined loop (see below).
 // copy_kernel  a grid-stride gather over (layer, instance, entry, 16-byte
 //   vector): every lane reads 16 bytes of a K||V row straight from pinned,
 //   device-mapped host memory over the host link and writes them into the
@@ -113,6 +114,100 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   if (tid == 0) load_count[inst] = (int32_t)nl;
 }
 
+// The plan of the pipelined loop: the target model attends over the current
+// selection C (loaded last round) while the next selection N is loaded, so a
+// slot of the pool (P >= 2 K slots) is reusable only if its position is in
+// neither; the new positions are N - resident.  Also writes the ascending slots
+// that hold C (the rows the attention of this step gathers).  Same block scans
+// and in-place update as plan_kernel.
+__global__ __launch_bounds__(kPlanThreads) void plan_lag1_kernel(
+    const int32_t* __restrict__ sel_cur, const int32_t* __restrict__ cur_count,
+    const int32_t* __restrict__ sel_next, const int32_t* __restrict__ next_count, int32_t* __restrict__ slot_pos,
+    uint32_t* __restrict__ resident_bm, int32_t* __restrict__ load_pos, int32_t* __restrict__ load_slot,
+    int32_t* __restrict__ load_count, int32_t* __restrict__ attend_rows, int32_t* __restrict__ attend_count, int Ks,
+    int P, int bm_words) {
+  extern __shared__ int32_t lds[];
+  int32_t* sN = lds;              // next selection [Ks], ascending
+  int32_t* sC = sN + Ks;          // current selection [Ks], ascending
+  int32_t* sL = sC + Ks;          // positions to load [Ks]
+  int32_t* sF = sL + Ks;          // reusable slots [P]
+  int32_t* sP = sF + P;           // the pool's slot map [P]
+  __shared__ uint32_t scan_smem[16];
+
+  const int inst = blockIdx.x;
+  const int tid = threadIdx.x;
+  int cn = next_count[inst], cc = cur_count[inst];
+  cn = cn < 0 ? 0 : (cn > Ks ? Ks : cn);
+  cc = cc < 0 ? 0 : (cc > Ks ? Ks : cc);
+  int32_t* sp = slot_pos + (size_t)inst * P;
+  uint32_t* bm = resident_bm + (size_t)inst * bm_words;
+  for (int i = tid; i < cn; i += kPlanThreads) sN[i] = sel_next[(size_t)inst * Ks + i];
+  for (int i = tid; i < cc; i += kPlanThreads) sC[i] = sel_cur[(size_t)inst * Ks + i];
+  for (int x = tid; x < P; x += kPlanThreads) sP[x] = sp[x];
+  __syncthreads();
+
+  const int Cx = (P + kPlanThreads - 1) / kPlanThreads;
+  const int x0 = min(tid * Cx, P), x1 = min(x0 + Cx, P);
+  uint32_t fmask = 0u, nf_loc = 0u;
+  for (int x = x0; x < x1; ++x) {
+    const int32_t pos = sP[x];
+    const bool keep = pos >= 0 && (sorted_contains(sN, cn, pos) || sorted_contains(sC, cc, pos));
+    if (!keep) { fmask |= 1u << (x - x0); ++nf_loc; }
+  }
+  const int Ci = (cn + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(tid * Ci, cn), i1 = min(i0 + Ci, cn);
+  uint32_t lmask = 0u, nl_loc = 0u;
+  const int32_t pos_end = bm_words * 32;
+  for (int i = i0; i < i1; ++i) {
+    const int32_t j = sN[i];
+    if (j < 0 || j >= pos_end) continue;
+    if (!((bm[j >> 5] >> (j & 31)) & 1u)) { lmask |= 1u << (i - i0); ++nl_loc; }
+  }
+  uint32_t nf, nl;
+  uint32_t fo = block_excl_scan(nf_loc, scan_smem, nf);
+  uint32_t lo = block_excl_scan(nl_loc, scan_smem, nl);
+  for (int x = x0; x < x1; ++x)
+    if (fmask >> (x - x0) & 1u) sF[fo++] = x;
+  for (int i = i0; i < i1; ++i)
+    if (lmask >> (i - i0) & 1u) sL[lo++] = sN[i];
+  __syncthreads();
+  // the host guarantees P >= 2 Ks, so nl <= nf
+  for (int i = tid; i < (int)nf; i += kPlanThreads) {
+    const int x = sF[i];
+    const int32_t old = sP[x];
+    if (old >= 0 && old < pos_end) atomicAnd(&bm[old >> 5], ~(1u << (old & 31)));
+    int32_t nw = -1;
+    if (i < (int)nl) {
+      nw = sL[i];
+      atomicOr(&bm[nw >> 5], 1u << (nw & 31));
+    }
+    sp[x] = nw;
+    sP[x] = nw;
+  }
+  int32_t* lp = load_pos + (size_t)inst * P;
+  int32_t* ls = load_slot + (size_t)inst * P;
+  for (int i = tid; i < P; i += kPlanThreads) {
+    const bool v = i < (int)nl;
+    lp[i] = v ? sL[i] : -1;
+    ls[i] = v ? sF[i] : -1;
+  }
+  if (tid == 0) load_count[inst] = (int32_t)nl;
+  __syncthreads();
+  // the slots holding the current selection, ascending
+  uint32_t amask = 0u, na_loc = 0u;
+  for (int x = x0; x < x1; ++x) {
+    const int32_t pos = sP[x];
+    if (pos >= 0 && sorted_contains(sC, cc, pos)) { amask |= 1u << (x - x0); ++na_loc; }
+  }
+  uint32_t na;
+  uint32_t ao = block_excl_scan(na_loc, scan_smem, na);
+  int32_t* ar = attend_rows + (size_t)inst * Ks;
+  for (int x = x0; x < x1; ++x)
+    if ((amask >> (x - x0) & 1u) && ao < (uint32_t)Ks) ar[ao++] = x;
+  for (int i = (int)na + tid; i < Ks; i += kPlanThreads) ar[i] = -1;
+  if (tid == 0) attend_count[inst] = (int32_t)(na < (uint32_t)Ks ? na : (uint32_t)Ks);
+}
+
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 8;
 
@@ -204,6 +299,18 @@ hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t
   plan_kernel<<<dim3(s.batch * s.n_groups), kPlanThreads, 0, st>>>(sel_idx, sel_count, slot_pos, resident_bm,
                                                                    load_pos, load_slot, load_count, s.budget,
                                                                    bm_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_lag1(const spc_shape& s, int sel_budget, const int32_t* sel_cur, const int32_t* cur_count,
+                            const int32_t* sel_next, const int32_t* next_count, int32_t* slot_pos,
+                            uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                            int32_t* attend_rows, int32_t* attend_count, hipStream_t st) {
+  const int bm_words = (s.max_len + 31) / 32;
+  const size_t lds = (size_t)(3 * sel_budget + 2 * s.budget) * sizeof(int32_t);
+  plan_lag1_kernel<<<dim3(s.batch * s.n_groups), kPlanThreads, lds, st>>>(
+      sel_cur, cur_count, sel_next, next_count, slot_pos, resident_bm, load_pos, load_slot, load_count, attend_rows,
+      attend_count, sel_budget, s.budget, bm_words);
   return hipGetLastError();
 }
 

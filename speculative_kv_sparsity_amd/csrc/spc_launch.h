@@ -45,11 +45,16 @@ hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* le
 
 // ---- stage 3: elastic plan / copy / reset
 constexpr int kPlanMaxBudget = 8192;
+constexpr int kPlanLag1MaxWords = 16384;   // 3 selections' + 2 pools' int32 in 64 KB of LDS
 constexpr int kCopyMaxInstances = 4096;
 constexpr int kCopyBlocksDefault = 48;   // workgroups of the gather (override: SPC_COPY_BLOCKS)
 hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t* sel_count, int32_t* slot_pos,
                        uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
                        hipStream_t st);
+hipError_t launch_plan_lag1(const spc_shape& s, int sel_budget, const int32_t* sel_cur, const int32_t* cur_count,
+                            const int32_t* sel_next, const int32_t* next_count, int32_t* slot_pos,
+                            uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                            int32_t* attend_rows, int32_t* attend_count, hipStream_t st);
 hipError_t launch_copy(const spc_shape& s, const int32_t* load_pos, const int32_t* load_slot,
                        const int32_t* load_count, const void* host_dev_ptr, const spc_kv_layout& hl, void* dev_kv,
                        const spc_kv_layout& dl, int layer_begin, int layer_end, hipStream_t st);

@@ -242,6 +242,94 @@ class SparseDecoder:
             self.main.wait_event(self.ev_attn)
 
 
+class LagOneDecoder:
+    """The pipelined loop of the SpeContext blog's section 4: at step t the retrieval head selects
+    the positions of step t+1 and their missing rows are copied on the side stream, while the
+    target model attends over the selection made at step t-1 (loaded by the previous copy).
+
+      main : scores(t) -> Top-K(t) -> plan(cur=S_t, next=S_t+1) -ev_plan-> wait ev_copy(t-1) -> attention(S_t)
+      side :                                  wait ev_plan -> copy(S_t+1 - resident) -> ev_copy(t)
+
+    The slots form a pool of ``pool`` (default 2K) rows per (b, group): a slot is reused only if it
+    holds neither selection, so the copy of step t never touches the rows the attention of step t
+    reads, and it starts after the attention of step t-1 (stream order on main).  In steady state the
+    copies run back to back and everything else overlaps them.  The first step has no previous
+    selection and attends over its own, after its copy (warm-up).
+    """
+
+    def __init__(self, p: Preset, dlm_k: torch.Tensor, host_kv: torch.Tensor, pool: Optional[int] = None):
+        assert p.kind in ("gqa", "mha", "mqa")
+        self.p = p
+        dev = dlm_k.device
+        self.device = dev
+        B, Hq, Hkv, G, d, L, K = p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.max_len, p.budget
+        P = 2 * K if pool is None else pool
+        self.P = P
+        self.shape = api.make_shape(B, Hq, Hkv, G, d, p.v_dim, L, K, p.n_layers, p.dtype, p.scale)
+        self.pool_shape = api.make_shape(B, Hq, Hkv, G, d, p.v_dim, L, P, p.n_layers, p.dtype, p.scale)
+        self.dlm_k, self.host_kv = dlm_k, host_kv
+        self.host_l = api.kv_layout(host_kv)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.probs = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.sel = [torch.empty((B, G, K), **i32) for _ in range(2)]
+        self.cnt = [torch.empty((B, G), **i32) for _ in range(2)]
+        self.slot_pos = torch.empty((B, G, P), **i32)
+        self.resident_bm = torch.empty((B, G, (L + 31) // 32), **i32)
+        self.load_pos = [torch.empty((B, G, P), **i32) for _ in range(2)]
+        self.load_slot = [torch.empty((B, G, P), **i32) for _ in range(2)]
+        self.load_count = [torch.zeros((B, G), **i32) for _ in range(2)]
+        self.attend_rows = torch.empty((B, G, K), **i32)
+        self.attend_count = torch.empty((B, G), **i32)
+        self.dev_kv = torch.zeros((B, p.n_layers, Hkv, P, 2, d), dtype=p.torch_dtype, device=dev)
+        self.dev_l = api.kv_layout(self.dev_kv)
+        self.out = torch.zeros((B, p.n_layers, Hq, p.v_dim), dtype=torch.float32, device=dev)
+        self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
+                                     dtype=torch.uint8, device=dev)
+        self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
+                                   dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
+                                   dtype=torch.uint8, device=dev)
+        self.q_l = api.q_layout(Hq * d, 0, d)
+        self.main = torch.cuda.current_stream(dev)
+        self.side = torch.cuda.Stream(device=dev)
+        self.ev_plan = torch.cuda.Event()
+        self.ev_copy = [torch.cuda.Event() for _ in range(2)]
+        self.t = 0
+        api.spc_elastic_reset(self.pool_shape, -1, self.slot_pos, self.resident_bm, stream=self.main)
+
+    def step(self, q: torch.Tensor, lengths: torch.Tensor, timer: Optional["StageTimer"] = None) -> None:
+        mark = timer.mark if timer is not None else (lambda name, stream: None)
+        nx = self.t % 2
+        cur = nx if self.t == 0 else 1 - nx
+        mark("scores", self.main)
+        api.spc_retrieval_scores(self.shape, q, self.dlm_k, lengths, self.probs, ws=self.ws_scores, stream=self.main)
+        mark("topk", self.main)
+        api.spc_group_max_topk(self.shape, self.probs, lengths, self.sel[nx], self.cnt[nx], ws=self.ws_topk,
+                               stream=self.main)
+        mark("plan", self.main)
+        api.spc_elastic_plan_lag1(self.pool_shape, self.p.budget, self.sel[cur], self.cnt[cur], self.sel[nx],
+                                  self.cnt[nx], self.slot_pos, self.resident_bm, self.load_pos[nx],
+                                  self.load_slot[nx], self.load_count[nx], self.attend_rows, self.attend_count,
+                                  stream=self.main)
+        mark("plan_end", self.main)
+        self.ev_plan.record(self.main)
+        self.side.wait_event(self.ev_plan)
+        mark("copy", self.side)
+        api.spc_elastic_update(self.pool_shape, None, None, None, None, self.load_pos[nx], self.load_slot[nx],
+                               self.load_count[nx], self.host_kv, self.host_l, self.dev_kv, self.dev_l, 0,
+                               self.p.n_layers, flags=api.SPC_COPY, plan_stream=self.side, copy_stream=self.side)
+        mark("copy_end", self.side)
+        self.ev_copy[nx].record(self.side)
+        # this step attends over S_t, loaded by the previous step's copy (the warm-up step by its own)
+        self.main.wait_event(self.ev_copy[nx if self.t == 0 else cur])
+        mark("attn", self.main)
+        api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.dev_kv, self.dev_l, self.attend_rows,
+                                   self.attend_count, api.SPC_ROWS_GATHER, 0, self.p.n_layers, self.out,
+                                   ws=self.ws_attn, stream=self.main)
+        mark("attn_end", self.main)
+        self.t += 1
+
+
 def layer_chunk_bounds(n_layers: int, n_chunks: int, tail_layers: Optional[int] = None) -> List[tuple]:
     """Layer ranges [a, z) of the copy/attention pipeline.
 
