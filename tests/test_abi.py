@@ -171,3 +171,19 @@ def test_thresholds_from_the_memory_model():
     c = O.offloaded_layers(p.max_len, th)
     assert 12 <= c <= 16
     assert O.memory_bytes(p.max_len, c, **model) <= gpu < O.memory_bytes(p.max_len, c - 1, **model)
+
+
+def test_lag1_plan_host_validation():
+    """spc_elastic_plan_lag1 needs a pool of at least two selections and rejects NULLs before launching."""
+    lib = L.lib()
+    p = ctypes.c_void_p(256)
+    args = [p] * 12
+    pool = _shape(budget=512)
+    assert lib.spc_elastic_plan_lag1(ctypes.byref(pool), 300, *args, None) == L.SPC_ERR_INVALID_ARG   # 512 < 600
+    assert lib.spc_elastic_plan_lag1(ctypes.byref(pool), 0, *args, None) == L.SPC_ERR_INVALID_ARG
+    big = _shape(max_len=65536, budget=9000)
+    assert lib.spc_elastic_plan_lag1(ctypes.byref(big), 4000, *args, None) == L.SPC_ERR_UNSUPPORTED
+    lds = _shape(max_len=65536, budget=8000)
+    assert lib.spc_elastic_plan_lag1(ctypes.byref(lds), 4000, *args, None) == L.SPC_ERR_UNSUPPORTED   # LDS words
+    bad = [p] * 11 + [None]
+    assert lib.spc_elastic_plan_lag1(ctypes.byref(pool), 256, *bad, None) == L.SPC_ERR_INVALID_ARG
