@@ -174,16 +174,22 @@ def test_thresholds_from_the_memory_model():
 
 
 def test_lag1_plan_host_validation():
-    """spc_elastic_plan_lag1 needs a pool of at least two selections and rejects NULLs before launching."""
+    """spc_elastic_plan_lag1 needs a pool of at least two selections and rejects NULLs before launching
+    (every call here fails validation: the fake pointers are never dereferenced)."""
     lib = L.lib()
     p = ctypes.c_void_p(256)
-    args = [p] * 12
+    ptrs = [p] * 11                       # sel_cur ... attend_count
     pool = _shape(budget=512)
-    assert lib.spc_elastic_plan_lag1(ctypes.byref(pool), 300, *args, None) == L.SPC_ERR_INVALID_ARG   # 512 < 600
-    assert lib.spc_elastic_plan_lag1(ctypes.byref(pool), 0, *args, None) == L.SPC_ERR_INVALID_ARG
-    big = _shape(max_len=65536, budget=9000)
-    assert lib.spc_elastic_plan_lag1(ctypes.byref(big), 4000, *args, None) == L.SPC_ERR_UNSUPPORTED
-    lds = _shape(max_len=65536, budget=8000)
-    assert lib.spc_elastic_plan_lag1(ctypes.byref(lds), 4000, *args, None) == L.SPC_ERR_UNSUPPORTED   # LDS words
-    bad = [p] * 11 + [None]
-    assert lib.spc_elastic_plan_lag1(ctypes.byref(pool), 256, *bad, None) == L.SPC_ERR_INVALID_ARG
+
+    def call(shape, sel_budget, pointers=ptrs):
+        assert len(pointers) == 11
+        return lib.spc_elastic_plan_lag1(ctypes.byref(shape), sel_budget, *pointers, None)
+
+    assert call(pool, 300) == L.SPC_ERR_INVALID_ARG            # 512 < 2 * 300
+    assert call(pool, 0) == L.SPC_ERR_INVALID_ARG
+    assert call(_shape(max_len=65536, budget=9000), 4000) == L.SPC_ERR_UNSUPPORTED
+    assert call(_shape(max_len=65536, budget=8000), 4000) == L.SPC_ERR_UNSUPPORTED   # LDS words
+    for i in range(11):
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(pool, 256, bad) == L.SPC_ERR_INVALID_ARG
