@@ -145,6 +145,15 @@ def roof(bound, amount, ms, peak, unit, kernel, calls, traffic=None):
     return rec
 
 
+def probs_call(torch, api, shape, q, k, lengths):
+    """A launcher of the probability form of stage 1 (spc_retrieval_scores: logits, then the
+    normalize pass), with its own output and workspace.  The step ranks the log-domain form; this
+    one is measured beside it."""
+    probs = torch.empty((shape.batch, shape.n_q_heads, shape.max_len), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, shape)), dtype=torch.uint8, device="cuda")
+    return lambda st: api.spc_retrieval_scores(shape, q, k, lengths, probs, ws=ws, stream=st)
+
+
 def calibration_copies(torch):
     """Three 256 MiB device-to-device copies: the known-size reference of the counter passes."""
     src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
@@ -289,10 +298,12 @@ def bench_gqa(args, p, torch, W):
     tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
     R = args.iso_reps
     iso_ms = {
-        "scores": iso(torch, lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs,
-                                                                 ws=dec.ws_scores, stream=st), R),
-        "topk": iso(torch, lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel_idx, dec.sel_count,
-                                                             ws=dec.ws_topk, stream=st), R),
+        "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dec.dlm_k, tl, dec.logits,
+                                                                 dec.tile_stats, stream=st), R),
+        "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
+                                                                    dec.sel_idx, dec.sel_count, ws=dec.ws_topk,
+                                                                    stream=st), R),
+        "scores_probs": iso(torch, probs_call(torch, api, dec.shape, tq, dec.dlm_k, tl), R),
     }
     if nch:
         c0a, c0z = dec.chunks[0]
@@ -321,7 +332,7 @@ def bench_gqa(args, p, torch, W):
     sel_per_group = float(np.mean(sel_rows)) / (B * p.n_groups)
     # algorithmic bytes per call (one launch of the stage)
     attn_bytes = B * lay0 * Hkv * sel_per_group * row + B * lay0 * Hq * d * 4   # K/V read + out write
-    score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4              # keys read + probs write
+    score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4              # keys read + logits (probs) write
     front_bytes = ((Hq + Hkv) * d * fw.hidden + B * fw.hidden + fw.hidden + B * (Hq + Hkv) * d) * eb
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
     off = p.n_layers - dec.n_res                                 # offloaded layers at the end of the run
@@ -341,8 +352,12 @@ def bench_gqa(args, p, torch, W):
     result["roofline"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s", attn_kernel,
                               max(nch, 1), traffic.get("attn"))
     result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                     "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1,
-                                     traffic.get("scores"))
+                                     "scores_logits_kernel (stage 1 as the step runs it: logits and per-tile "
+                                     "max / sum exp in one pass over the DLM keys)", 1, traffic.get("scores"))
+    result["roofline_scores_probs"] = roof("hbm", score_bytes, iso_ms["scores_probs"], HBM_PEAK_GBS, "GB/s",
+                                           "scores_logits_kernel + scores_normalize_kernel (spc_retrieval_scores: "
+                                           "the probabilities written; not on the step's path)", 0,
+                                           traffic.get("scores_probs"))
     if nch:
         copy_bytes = float(np.mean(loaded_rows)) * lay0 * row            # host reads per chunk
         result["roofline_host_link"] = roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
@@ -412,10 +427,11 @@ def bench_lag1(args, p, torch, W):
     R = args.iso_reps
     nx = (dec.t - 1) % 2
     iso_ms = {
-        "scores": iso(torch, lambda st: api.spc_retrieval_scores(dec.shape, tq, dec.dlm_k, tl, dec.probs,
-                                                                 ws=dec.ws_scores, stream=st), R),
-        "topk": iso(torch, lambda st: api.spc_group_max_topk(dec.shape, dec.probs, tl, dec.sel[nx], dec.cnt[nx],
-                                                             ws=dec.ws_topk, stream=st), R),
+        "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dec.dlm_k, tl, dec.logits,
+                                                                 dec.tile_stats, stream=st), R),
+        "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
+                                                                    dec.sel[nx], dec.cnt[nx], ws=dec.ws_topk,
+                                                                    stream=st), R),
         "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
             dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
             0, p.n_layers, dec.out, ws=dec.ws_attn, stream=st), R),
@@ -441,7 +457,7 @@ def bench_lag1(args, p, torch, W):
                               "attn_split_kernel + attn_combine_kernel (the pool's rows of the current selection, "
                               "gathered)", 1)
     result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                     "scores_logits_kernel + scores_normalize_kernel (retrieval scores)", 1)
+                                     "scores_logits_kernel (logits and per-tile max / sum exp, one pass)", 1)
     result["roofline_host_link"] = roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
                                         "copy_kernel (elastic host->HBM gather, every layer in one launch)", 1)
     result["stage_us_in_step"] = {k: round(v * 1e3, 2) for k, v in avg.items()}
@@ -498,10 +514,11 @@ def bench_mla(args, p, torch, W):
     iso_ms = {
         "absorb": iso(torch, lambda st: api.spc_mla_absorb_q(s, p.nope_dim, dec.w_uk, tq, tr, dec.q_abs,
                                                              stream=st), R),
-        "scores": iso(torch, lambda st: api.spc_retrieval_scores(s, dec.q_abs, dec.latent, tl, dec.probs,
-                                                                 ws=dec.ws_scores, stream=st), R),
-        "topk": iso(torch, lambda st: api.spc_group_max_topk(s, dec.probs, tl, dec.sel_idx, dec.sel_count,
-                                                             ws=dec.ws_topk, stream=st), R),
+        "scores": iso(torch, lambda st: api.spc_retrieval_logits(s, dec.q_abs, dec.latent, tl, dec.logits,
+                                                                 dec.tile_stats, stream=st), R),
+        "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(s, dec.logits, None, tl, dec.sel_idx,
+                                                                    dec.sel_count, ws=dec.ws_topk, stream=st), R),
+        "scores_probs": iso(torch, probs_call(torch, api, s, dec.q_abs, dec.latent, tl), R),
         "attn": iso(torch, lambda st: dec.attend(st), R),
         "out_proj": iso(torch, lambda st: api.spc_mla_out_proj(s, p.nope_dim, dec.w_uv, dec.o_lat, 0, dec.out,
                                                                stream=st), R),
@@ -514,7 +531,7 @@ def bench_mla(args, p, torch, W):
     attn_bytes = union * row + B * H * p.latent_dim * 4          # every selected row once + o_lat writes
     gathered = sel * row                                         # each head's own gather (L2 / last-level cache)
     score_flop = 2.0 * n_valid * H * D                           # every head against every valid latent row
-    score_bytes = n_valid * row + n_valid * H * 4               # latent read once + probs write
+    score_bytes = n_valid * row + n_valid * H * 4               # latent read once + logits (probs) write
     traffic = measured_traffic(p.name, 1)
     config = {"workload": WORKLOADS["mla_32k"] if p.name == "mla_32k" else p.name, "batch": B, "layers": 1,
               "q_heads": H, "latent_dim": p.latent_dim, "rope_dim": p.rope_dim, "nope_dim": p.nope_dim,
@@ -527,10 +544,14 @@ def bench_mla(args, p, torch, W):
                          gathered_bytes_per_launch=int(gathered),
                          gathered_GBs=round(gathered / (iso_ms["attn"] * 1e-3) / 1e9, 1)),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                                "mla_scores_kernel + scores_normalize_kernel (bf16 MFMA, fp32 query as a "
-                                "hi/lo bf16 pair: 2 MFMAs per product)", 1),
+                                "mla_scores_kernel (logits and per-tile max / sum exp; bf16 MFMA, fp32 query as "
+                                "a hi/lo bf16 pair: 2 MFMAs per product)", 1),
         "roofline_scores_hbm": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                    "mla_scores_kernel + scores_normalize_kernel", 1, traffic.get("scores")),
+                                    "mla_scores_kernel", 1, traffic.get("scores")),
+        "roofline_scores_probs": roof("hbm", score_bytes, iso_ms["scores_probs"], HBM_PEAK_GBS, "GB/s",
+                                      "mla_scores_kernel + scores_normalize_kernel (spc_retrieval_scores: the "
+                                      "probabilities written; not on the step's path)", 0,
+                                      traffic.get("scores_probs")),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
         "elastic": {"rows_selected_per_step": sel, "distinct_rows_per_step": union,

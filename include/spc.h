@@ -173,6 +173,31 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
                          float* probs, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stage 1 in log-domain form, for a caller that only ranks the weights (stage 2):
+ * the same softmax as spc_retrieval_scores, kept as the logits plus what
+ * normalises them, in one pass over the key cache (the probabilities are never
+ * written).
+ *   logits[b][i][j]     = scale * q[b][i] . k[b][i / (H_q/H_kv)][j],   j < lengths[b]
+ *   tile_stats[b][i][t] = (m, s) with m = max and s = sum of exp(logit - m) over the
+ *                         positions j < lengths[b] of tile t = [t T, (t+1) T),
+ *                         T = spc_score_tile(s); tiles t >= ceil(lengths[b] / T) are
+ *                         left untouched
+ * so that probs[b][i][j] = exp(logits[b][i][j] - lse[b][i]) with lse the
+ * log-sum-exp of the head's tile pairs (SpeContext blog section 2, AttentionWeight
+ * formula; the same inputs and supported shapes as spc_retrieval_scores).
+ *   logits      device [B][H_q][max_len] float32 out; entries j >= lengths[b] untouched
+ *   tile_stats  device float32 pairs [B][H_q][ceil(max_len / T)] out, 8-byte aligned,
+ *               spc_tile_stats_size(s) bytes
+ */
+int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths,
+                         float* logits, float* tile_stats, void* stream);
+
+/* Positions per tile of the stage-1 statistics (128; MLA shapes 256), 0 for an invalid shape. */
+int spc_score_tile(const spc_shape* s);
+/* Bytes of spc_retrieval_logits' tile_stats for the shape, 0 for an invalid shape. */
+size_t spc_tile_stats_size(const spc_shape* s);
+
+/*
  * Stage 2 - group max and Top-K.
  *   v[b][g][j] = max over the query heads i of group g of probs[b][i][j]
  *   S[b][g]    = the first min(K, n) positions j < n = lengths[b] ordered by
@@ -188,6 +213,24 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
  */
 int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
                        int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 2 on the log-domain form of spc_retrieval_logits: the selection of
+ * spc_group_max_topk, ranked by
+ *   v[b][g][j] = exp( max over the query heads i of group g of (logits[b][i][j] - lse[b][i]) )
+ * which is the group max of the probabilities (exp is increasing, so it commutes
+ * with the max); lse[b][i] is the log-sum-exp of the head's tile pairs, formed here.
+ * With one query head per group (MHA, MLA) the logits themselves are ranked (the
+ * same order as the head's probabilities, without exp rounding) and tile_stats
+ * may be NULL; otherwise it is required.
+ *   logits, tile_stats  as written by spc_retrieval_logits for the same shape
+ *   sel_idx, sel_count, ws  as for spc_group_max_topk (same workspace size)
+ * At most 64 query heads per group.  The selection is exact on the float32 values v
+ * (as in the probability form, values below float32's range tie at zero).
+ */
+int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats,
+                              const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * Stage 3 - elastic loading (blog section 4 pseudocode: to_load = selected -

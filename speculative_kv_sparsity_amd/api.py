@@ -21,7 +21,8 @@ __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version",
            "spc_sparse_decode_attn", "SPC_PLAN", "SPC_COPY", "SPC_ROWS_SLOTS", "SPC_ROWS_GATHER",
            "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "SPC_CALL_FRONT", "spc_mla_absorb_q",
            "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds",
-           "spc_elastic_plan_lag1"]
+           "spc_elastic_plan_lag1", "spc_retrieval_logits", "spc_group_max_topk_logits", "spc_score_tile",
+           "spc_tile_stats_size", "tile_stats_shape"]
 
 
 class SpcError(RuntimeError):
@@ -108,6 +109,41 @@ def spc_group_max_topk(shape: SpcShape, probs, lengths, sel_idx, sel_count, ws=N
     ws = _workspace(SPC_CALL_TOPK, shape, probs.device) if ws is None else ws
     _check(L.lib().spc_group_max_topk(ctypes.byref(shape), _ptr(probs), _ptr(lengths), _ptr(sel_idx),
                                       _ptr(sel_count), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spc_score_tile(shape: SpcShape) -> int:
+    return int(L.lib().spc_score_tile(ctypes.byref(shape)))
+
+
+def spc_tile_stats_size(shape: SpcShape) -> int:
+    return int(L.lib().spc_tile_stats_size(ctypes.byref(shape)))
+
+
+def tile_stats_shape(shape: SpcShape) -> tuple:
+    """[B][H_q][n_tiles][2] float32 of spc_retrieval_logits' tile statistics."""
+    T = spc_score_tile(shape)
+    return (shape.batch, shape.n_q_heads, (shape.max_len + T - 1) // T, 2)
+
+
+def spc_retrieval_logits(shape: SpcShape, q, k, lengths, logits, tile_stats, stream=None) -> None:
+    for t, n in ((q, "q"), (k, "k"), (lengths, "lengths"), (logits, "logits"), (tile_stats, "tile_stats")):
+        _dev(t, n)
+    if tile_stats.numel() * tile_stats.element_size() < spc_tile_stats_size(shape):
+        raise ValueError("tile_stats is smaller than spc_tile_stats_size(shape)")
+    _check(L.lib().spc_retrieval_logits(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(lengths), _ptr(logits),
+                                        _ptr(tile_stats), _stream(stream)))
+
+
+def spc_group_max_topk_logits(shape: SpcShape, logits, tile_stats, lengths, sel_idx, sel_count, ws=None,
+                              stream=None) -> None:
+    for t, n in ((logits, "logits"), (lengths, "lengths"), (sel_idx, "sel_idx"), (sel_count, "sel_count")):
+        _dev(t, n)
+    if tile_stats is not None:
+        _dev(tile_stats, "tile_stats")
+    ws = _workspace(SPC_CALL_TOPK, shape, logits.device) if ws is None else ws
+    _check(L.lib().spc_group_max_topk_logits(ctypes.byref(shape), _ptr(logits), _ptr(tile_stats), _ptr(lengths),
+                                             _ptr(sel_idx), _ptr(sel_count), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spc_elastic_update(shape: SpcShape, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,

@@ -91,6 +91,10 @@ size_t spc_workspace_size(int which_call, const spc_shape* s) {
   }
 }
 
+int spc_score_tile(const spc_shape* s) { return check_shape(s) == SPC_OK ? spc::score_tile(*s) : 0; }
+
+size_t spc_tile_stats_size(const spc_shape* s) { return check_shape(s) == SPC_OK ? spc::scores_ws_bytes(*s) : 0; }
+
 int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const int32_t* lengths, float* probs,
                          void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_shape(s)) return e;
@@ -107,6 +111,47 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
   return e == hipSuccess ? ok() : hip_fail(e, "retrieval scores launch");
 }
 
+int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths, float* logits,
+                         float* tile_stats, void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!q || !k || !lengths || !logits || !tile_stats)
+    return fail(SPC_ERR_INVALID_ARG, "NULL q, k, lengths, logits or tile_stats");
+  if (!spc::scores_supported(*s))
+    return fail(SPC_ERR_UNSUPPORTED, "retrieval logits: head_dim %d with dtype %d", s->head_dim, s->dtype);
+  if (!aligned16(q) || !aligned16(k)) return fail(SPC_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (!aligned4(logits) || !aligned4(lengths)) return fail(SPC_ERR_INVALID_ARG, "logits/lengths misaligned");
+  if ((reinterpret_cast<uintptr_t>(tile_stats) & 7u) != 0)
+    return fail(SPC_ERR_INVALID_ARG, "tile_stats must be 8-byte aligned");
+  const hipError_t e = spc::launch_logits(*s, q, k, lengths, logits, reinterpret_cast<float2*>(tile_stats),
+                                          as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "retrieval logits launch");
+}
+
+int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats,
+                              const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!logits || !lengths || !sel_idx || !sel_count)
+    return fail(SPC_ERR_INVALID_ARG, "NULL logits, lengths, sel_idx or sel_count");
+  const int gq = s->n_q_heads / s->n_groups;
+  if (gq > 1 && !tile_stats)
+    return fail(SPC_ERR_INVALID_ARG, "tile_stats are needed with %d query heads per group", gq);
+  if (gq > spc::kMaxGroupHeads)
+    return fail(SPC_ERR_UNSUPPORTED, "%d query heads per group exceed %d", gq, spc::kMaxGroupHeads);
+  if (!aligned4(logits) || !aligned4(sel_idx) || !aligned4(sel_count) || !aligned4(lengths))
+    return fail(SPC_ERR_INVALID_ARG, "misaligned int32/float buffer");
+  if ((reinterpret_cast<uintptr_t>(tile_stats) & 7u) != 0)
+    return fail(SPC_ERR_INVALID_ARG, "tile_stats must be 8-byte aligned");
+  const size_t need = spc::topk_ws_bytes(*s);
+  if (ws_bytes < need || !ws)
+    return fail(SPC_ERR_WORKSPACE, "group max / top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const float2* st = gq > 1 ? reinterpret_cast<const float2*>(tile_stats) : nullptr;
+  const hipError_t e = spc::launch_topk(*s, logits, st, spc::score_tile(*s), lengths, sel_idx, sel_count, ws,
+                                        as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "group max / top-k (logits) launch");
+}
+
 int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
                        int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_shape(s)) return e;
@@ -118,7 +163,7 @@ int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* le
   if (ws_bytes < need || !ws)
     return fail(SPC_ERR_WORKSPACE, "group max / top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
   if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  const hipError_t e = spc::launch_topk(*s, probs, lengths, sel_idx, sel_count, ws, as_stream(stream));
+  const hipError_t e = spc::launch_topk(*s, probs, nullptr, 0, lengths, sel_idx, sel_count, ws, as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "group max / top-k launch");
 }
 

@@ -19,6 +19,9 @@ size_t scores_ws_bytes(const spc_shape& s);
 bool scores_supported(const spc_shape& s);
 hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* probs,
                          void* ws, hipStream_t st);
+// one pass: logits and their per-tile (max, sum exp) stats [B*Hq][ceil(max_len/score_tile)]
+hipError_t launch_logits(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* logits,
+                         float2* stats, hipStream_t st);
 // rewrites logits as probabilities from per-tile (max, sum exp) partials [B*Hq][ntiles]
 int score_tile(const spc_shape& s);    // positions per (max, sum) partial of the scores workspace
 hipError_t launch_scores_normalize(const spc_shape& s, float* probs, const float2* part, const int32_t* lengths,
@@ -31,17 +34,20 @@ constexpr int kMlaMaxBatch = 16;
 bool mla_shape(const spc_shape& s);   // head_dim 576: the MLA layout
 hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void* q_nope, const void* q_rope,
                              float* q_abs, hipStream_t st);
-hipError_t launch_mla_scores(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
-                             float* probs, void* ws, hipStream_t st);
+hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
+                             float* logits, float2* stats, hipStream_t st);
 hipError_t launch_mla_out_proj(int B, int H, int dv, const void* w_uv, const float* o_lat, int64_t lat_b_stride,
                                float* out, hipStream_t st);
 
 // ---- stage 2: group max + Top-K
 constexpr int kTopkLdsKeys = 32768;    // lengths up to this keep their keys in LDS
 constexpr int kKeyChunk = 1024;        // positions per workgroup of the key / first-digit kernel
+constexpr int kMaxGroupHeads = 64;     // query heads per group of the log-domain ranking
 size_t topk_ws_bytes(const spc_shape& s);
-hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
-                       int32_t* sel_count, void* ws, hipStream_t st);
+// scores: probabilities (stats NULL) or logits with per-tile (max, sum exp) stats of
+// stat_tile positions [B*Hq][ceil(max_len/stat_tile)] (NULL allowed with one head per group)
+hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
+                       const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, hipStream_t st);
 
 // ---- stage 3: elastic plan / copy / reset
 constexpr int kPlanMaxBudget = 8192;

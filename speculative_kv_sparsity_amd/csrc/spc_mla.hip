@@ -294,18 +294,15 @@ hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void*
   return hipGetLastError();
 }
 
-hipError_t launch_mla_scores(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
-                             float* probs, void* ws, hipStream_t st) {
+hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
+                             float* logits, float2* stats, hipStream_t st) {
   const int ntiles = (s.max_len + kMlaScoreTile - 1) / kMlaScoreTile;
-  float2* part = static_cast<float2*>(ws);
   const int nhg = (s.n_q_heads + 63) / 64;         // head groups of 64
   const int ngrp = (ntiles + 7) / 8;
   mla_scores_kernel<<<dim3(ngrp * 8 * nhg, s.batch), kScoreThreads, 0, st>>>(
-      q_abs, static_cast<const uint16_t*>(latent), lengths, probs, part, s.n_q_heads, s.max_len, ntiles, nhg,
+      q_abs, static_cast<const uint16_t*>(latent), lengths, logits, stats, s.n_q_heads, s.max_len, ntiles, nhg,
       s.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_scores_normalize(s, probs, part, lengths, ntiles, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_mla_out_proj(int B, int H, int dv, const void* w_uv, const float* o_lat, int64_t lat_b_stride,

@@ -12,10 +12,12 @@
 //       so one wave load instruction covers 8 rows x 128 contiguous bytes (full
 //       cache lines).  bf16 dot products use v_dot2_f32_bf16 on packed pairs
 //       (no widening), the 8-lane sum uses DPP.  The tile's logits are
-//       gathered per head in LDS and written to `probs` as whole 16-byte
-//       vectors; the tile's per-head (max, sum exp) go to the workspace.
+//       gathered per head in LDS and written as whole 16-byte vectors; the
+//       tile's per-head (max, sum exp) go to the tile stats.
 //   scores_normalize_kernel combines the tile partials of a head into
 //       (max, sum) and rewrites its logits in place as exp(l - max) / sum.
+// The log-domain form (logits + tile stats, no normalize pass) is what the
+// ranking of stage 2 needs; the probabilities are the second kernel's work.
 #include "spc_common.h"
 #include "spc_launch.h"
 
@@ -253,31 +255,30 @@ size_t scores_ws_bytes(const spc_shape& s) {
   return (size_t)s.batch * s.n_q_heads * ntiles * sizeof(float2);
 }
 
-hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* probs,
-                         void* ws, hipStream_t st) {
-  if (mla_shape(s)) return launch_mla_scores(s, static_cast<const float*>(q), k, lengths, probs, ws, st);
+hipError_t launch_logits(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* logits,
+                         float2* part, hipStream_t st) {
+  if (mla_shape(s)) return launch_mla_logits(s, static_cast<const float*>(q), k, lengths, logits, part, st);
   const int per_kv = s.n_q_heads / s.n_kv_heads;
   const int HC = heads_per_chunk(s);
   const int nchunk = (per_kv + HC - 1) / HC;
   const int ntiles = (s.max_len + kScoreTile - 1) / kScoreTile;
-  float2* part = static_cast<float2*>(ws);
   const dim3 g1(ntiles, s.batch * s.n_kv_heads * nchunk);
   const char* qc = static_cast<const char*>(q);
   const char* kc = static_cast<const char*>(k);
   hipError_t e = hipErrorInvalidValue;
   if (s.dtype == SPC_F32) {
     if (s.head_dim == 128)
-      e = launch_logits_hc<SPC_F32, 128>(HC, g1, st, qc, kc, lengths, probs, part, s.n_q_heads, s.n_kv_heads,
+      e = launch_logits_hc<SPC_F32, 128>(HC, g1, st, qc, kc, lengths, logits, part, s.n_q_heads, s.n_kv_heads,
                                          s.max_len, nchunk, ntiles, s.scale);
     else if (s.head_dim == 64)
-      e = launch_logits_hc<SPC_F32, 64>(HC, g1, st, qc, kc, lengths, probs, part, s.n_q_heads, s.n_kv_heads,
+      e = launch_logits_hc<SPC_F32, 64>(HC, g1, st, qc, kc, lengths, logits, part, s.n_q_heads, s.n_kv_heads,
                                         s.max_len, nchunk, ntiles, s.scale);
   } else {
     switch (s.head_dim) {
-#define SPC_D(DIM)                                                                                            \
-  case DIM:                                                                                                   \
-    e = launch_logits_hc<SPC_BF16, DIM>(HC, g1, st, qc, kc, lengths, probs, part, s.n_q_heads, s.n_kv_heads, \
-                                        s.max_len, nchunk, ntiles, s.scale);                                  \
+#define SPC_D(DIM)                                                                                             \
+  case DIM:                                                                                                    \
+    e = launch_logits_hc<SPC_BF16, DIM>(HC, g1, st, qc, kc, lengths, logits, part, s.n_q_heads, s.n_kv_heads, \
+                                        s.max_len, nchunk, ntiles, s.scale);                                   \
     break;
       SPC_D(64)
       SPC_D(128)
@@ -287,7 +288,15 @@ hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const
         break;
     }
   }
+  return e;
+}
+
+hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* probs,
+                         void* ws, hipStream_t st) {
+  float2* part = static_cast<float2*>(ws);
+  const hipError_t e = launch_logits(s, q, k, lengths, probs, part, st);
   if (e != hipSuccess) return e;
+  const int ntiles = (s.max_len + score_tile(s) - 1) / score_tile(s);
   return launch_scores_normalize(s, probs, part, lengths, ntiles, st);
 }
 

@@ -10,6 +10,12 @@
 // Each fp32 value becomes an order-preserving uint32 key; the K-th largest key
 // T is found by radix select over 8 + 12 + 12 bits.
 //
+// The scores may also arrive in log-domain form (logits plus each head's
+// per-tile max and sum of exp): the group max is then taken over
+// logit - log-sum-exp and exponentiated, which is the group max of the
+// probabilities (exp is increasing), so the probabilities need never be
+// written.  With one head per group the logits are ranked as they are.
+//
 // topk_keys_kernel    many workgroups per (b, g), kKeyChunk positions each:
 //   takes the group max while reading the heads' rows once, writes the keys to
 //   the workspace and the chunk's histogram of the top 8 key bits.  With one
@@ -47,11 +53,30 @@ __device__ __forceinline__ uint4 to_keys(uint4 w) {
                     order_key(__uint_as_float(w.w)));
 }
 
-__global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __restrict__ probs,
+// Online merge of two (max, sum exp(x - max)) pairs.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = (m == -INFINITY ? 0.f : s * __expf(m - M)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - M));
+  m = M;
+}
+
+// LOGITS: `scores` are logits and, with several heads per group, `stats` holds
+// each head's per-tile (max, sum exp) [B*Hq][ntiles] over tiles of `tile`
+// positions.  The group max is then taken over l - lse of every head and keyed
+// as exp of it: exp is increasing, so that is the group max of the
+// probabilities exp(l - lse), formed here instead of stored.  (Keying the
+// log-probabilities themselves would rank the same, but they crowd into one or
+// two values of the first radix digit - sign and high exponent bits - and the
+// select would then carry the whole row as candidates.)
+template <bool LOGITS>
+__global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __restrict__ scores,
+                                                                const float2* __restrict__ stats,
                                                                 const int32_t* __restrict__ lengths,
                                                                 uint32_t* __restrict__ keys,
                                                                 uint32_t* __restrict__ chist, int Hq, int n_groups,
-                                                                int max_len, int budget, int nchunk) {
+                                                                int max_len, int budget, int nchunk, int ntiles,
+                                                                int tile) {
   const int inst = blockIdx.y;
   const int c = blockIdx.x;
   const int b = inst / n_groups;
@@ -61,11 +86,11 @@ __global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __r
   if (n <= budget || j0 >= n) return;
   const int j1 = min(j0 + kKeyChunk, n);
   const int Gq = Hq / n_groups;
-  const float* pb = probs + ((size_t)b * Hq + (size_t)g * Gq) * max_len;
+  const float* pb = scores + ((size_t)b * Hq + (size_t)g * Gq) * max_len;
   uint32_t* kout = keys + (size_t)inst * max_len;
   __shared__ uint32_t h[kBins1];
+  __shared__ float s_lse[kMaxGroupHeads];
   h[threadIdx.x] = 0u;
-  __syncthreads();
   constexpr int kPer = kKeyChunk / kKeyThreads;       // positions per thread
   float v[kPer];
 #pragma unroll
@@ -73,20 +98,53 @@ __global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __r
     const int j = j0 + threadIdx.x + u * kKeyThreads;
     v[u] = j < j1 ? pb[j] : 0.f;
   }
+  const bool lse = LOGITS && Gq > 1;
+  if (lse) {
+    // log-sum-exp of every head of the group from its tile pairs (one wave per head)
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nt = (n + tile - 1) / tile;
+    for (int hh = wid; hh < Gq; hh += kKeyThreads / 64) {
+      const float2* st = stats + ((size_t)b * Hq + (size_t)g * Gq + hh) * ntiles;
+      float m = -INFINITY, sm = 0.f;
+      for (int t0 = 0; t0 < nt; t0 += 4 * 64) {
+        float2 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = t0 + lane + 64 * u;
+          x[u] = t < nt ? st[t] : make_float2(-INFINITY, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) merge_ms(m, sm, x[u].x, x[u].y);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, kWave);
+        const float s2 = __shfl_xor(sm, o, kWave);
+        merge_ms(m, sm, m2, s2);
+      }
+      if (lane == 0) s_lse[hh] = m + __logf(sm);
+    }
+  }
+  __syncthreads();
+  if (lse) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) v[u] -= s_lse[0];
+  }
   for (int hh = 1; hh < Gq; ++hh) {
     const float* ph = pb + (size_t)hh * max_len;
+    const float off = lse ? s_lse[hh] : 0.f;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int j = j0 + threadIdx.x + u * kKeyThreads;
-      if (j < j1) v[u] = fmaxf(v[u], ph[j]);
+      if (j < j1) v[u] = fmaxf(v[u], ph[j] - off);
     }
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int j = j0 + threadIdx.x + u * kKeyThreads;
     if (j < j1) {
-      const uint32_t key = order_key(v[u]);
-      if (Gq > 1) kout[j] = key;      // one head per group: the select kernel keys the probabilities itself
+      const uint32_t key = order_key(lse ? __expf(v[u]) : v[u]);
+      if (Gq > 1) kout[j] = key;      // one head per group: the select kernel keys the scores itself
       atomicAdd(&h[key >> 24], 1u);
     }
   }
@@ -476,19 +534,25 @@ size_t topk_ws_bytes(const spc_shape& s) {
   return inst * (size_t)s.max_len * sizeof(uint32_t) + inst * nchunk * kBins1 * sizeof(uint32_t);
 }
 
-hipError_t launch_topk(const spc_shape& s, const float* probs, const int32_t* lengths, int32_t* sel_idx,
-                       int32_t* sel_count, void* ws, hipStream_t st) {
+hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
+                       const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, hipStream_t st) {
   const int inst = s.batch * s.n_groups;
   const int nchunk = (s.max_len + kKeyChunk - 1) / kKeyChunk;
+  const int ntiles = stat_tile > 0 ? (s.max_len + stat_tile - 1) / stat_tile : 0;
   uint32_t* keys = static_cast<uint32_t*>(ws);
   uint32_t* chist = keys + (size_t)inst * s.max_len;
-  topk_keys_kernel<<<dim3(nchunk, inst), kKeyThreads, 0, st>>>(probs, lengths, keys, chist, s.n_q_heads,
-                                                               s.n_groups, s.max_len, s.budget, nchunk);
+  const dim3 kg(nchunk, inst);
+  if (stats)
+    topk_keys_kernel<true><<<kg, kKeyThreads, 0, st>>>(scores, stats, lengths, keys, chist, s.n_q_heads, s.n_groups,
+                                                       s.max_len, s.budget, nchunk, ntiles, stat_tile);
+  else
+    topk_keys_kernel<false><<<kg, kKeyThreads, 0, st>>>(scores, nullptr, lengths, keys, chist, s.n_q_heads,
+                                                        s.n_groups, s.max_len, s.budget, nchunk, 0, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one head per group: the keys are the probabilities' own order keys, taken on load
+  // one head per group: the keys are the scores' own order keys, taken on load
   const bool raw = s.n_q_heads == s.n_groups;
-  const uint32_t* kin = raw ? reinterpret_cast<const uint32_t*>(probs) : keys;
+  const uint32_t* kin = raw ? reinterpret_cast<const uint32_t*>(scores) : keys;
   if (s.max_len <= kTopkLdsKeys) {
     if (raw)
       topk_select_lds_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,

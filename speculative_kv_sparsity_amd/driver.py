@@ -72,7 +72,9 @@ class SparseDecoder:
         self.host_kv = host_kv
         self.host_l = api.kv_layout(host_kv)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.probs = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        # stage 1 in log-domain form: logits + per-tile (max, sum exp); stage 2 ranks them directly
+        self.logits = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.tile_stats = torch.empty(api.tile_stats_shape(self.shape), dtype=torch.float32, device=dev)
         self.sel_idx = torch.empty((B, G, K), **i32)
         self.sel_count = torch.empty((B, G), **i32)
         self.slot_pos = torch.empty((B, G, K), **i32)
@@ -83,8 +85,6 @@ class SparseDecoder:
         self.dev_kv = torch.zeros((B, p.n_layers, Hkv, K, 2, d), dtype=p.torch_dtype, device=dev)
         self.dev_l = api.kv_layout(self.dev_kv)
         self.out = torch.zeros((B, p.n_layers, Hq, p.v_dim), dtype=torch.float32, device=dev)
-        self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
-                                     dtype=torch.uint8, device=dev)
         self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
                                    dtype=torch.uint8, device=dev)
         self.q_l = api.q_layout(Hq * d, 0, d)   # the same query serves every layer
@@ -147,11 +147,11 @@ class SparseDecoder:
 
     # --- the four stages --------------------------------------------------------------
     def scores(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
-        api.spc_retrieval_scores(self.shape, q, self.dlm_k, lengths, self.probs, ws=self.ws_scores, stream=self.main)
+        api.spc_retrieval_logits(self.shape, q, self.dlm_k, lengths, self.logits, self.tile_stats, stream=self.main)
 
     def topk(self, lengths: torch.Tensor) -> None:
-        api.spc_group_max_topk(self.shape, self.probs, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk,
-                               stream=self.main)
+        api.spc_group_max_topk_logits(self.shape, self.logits, self.tile_stats, lengths, self.sel_idx,
+                                      self.sel_count, ws=self.ws_topk, stream=self.main)
 
     def select(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
         self.scores(q, lengths)
@@ -270,7 +270,9 @@ class LagOneDecoder:
         self.dlm_k, self.host_kv = dlm_k, host_kv
         self.host_l = api.kv_layout(host_kv)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.probs = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        # stage 1 in log-domain form: logits + per-tile (max, sum exp); stage 2 ranks them directly
+        self.logits = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.tile_stats = torch.empty(api.tile_stats_shape(self.shape), dtype=torch.float32, device=dev)
         self.sel = [torch.empty((B, G, K), **i32) for _ in range(2)]
         self.cnt = [torch.empty((B, G), **i32) for _ in range(2)]
         self.slot_pos = torch.empty((B, G, P), **i32)
@@ -283,8 +285,6 @@ class LagOneDecoder:
         self.dev_kv = torch.zeros((B, p.n_layers, Hkv, P, 2, d), dtype=p.torch_dtype, device=dev)
         self.dev_l = api.kv_layout(self.dev_kv)
         self.out = torch.zeros((B, p.n_layers, Hq, p.v_dim), dtype=torch.float32, device=dev)
-        self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
-                                     dtype=torch.uint8, device=dev)
         self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
                                    dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
@@ -302,10 +302,10 @@ class LagOneDecoder:
         nx = self.t % 2
         cur = nx if self.t == 0 else 1 - nx
         mark("scores", self.main)
-        api.spc_retrieval_scores(self.shape, q, self.dlm_k, lengths, self.probs, ws=self.ws_scores, stream=self.main)
+        api.spc_retrieval_logits(self.shape, q, self.dlm_k, lengths, self.logits, self.tile_stats, stream=self.main)
         mark("topk", self.main)
-        api.spc_group_max_topk(self.shape, self.probs, lengths, self.sel[nx], self.cnt[nx], ws=self.ws_topk,
-                               stream=self.main)
+        api.spc_group_max_topk_logits(self.shape, self.logits, self.tile_stats, lengths, self.sel[nx],
+                                      self.cnt[nx], ws=self.ws_topk, stream=self.main)
         mark("plan", self.main)
         api.spc_elastic_plan_lag1(self.pool_shape, self.p.budget, self.sel[cur], self.cnt[cur], self.sel[nx],
                                   self.cnt[nx], self.slot_pos, self.resident_bm, self.load_pos[nx],
@@ -382,7 +382,8 @@ class MlaDecoder:
         f32 = dict(dtype=torch.float32, device=dev)
         i32 = dict(dtype=torch.int32, device=dev)
         self.q_abs = torch.empty((B, H, p.head_dim), **f32)
-        self.probs = torch.empty((B, H, L), **f32)
+        self.logits = torch.empty((B, H, L), **f32)
+        self.tile_stats = torch.empty(api.tile_stats_shape(self.shape), **f32)
         self.sel_idx = torch.empty((B, H, K), **i32)
         self.sel_count = torch.empty((B, H), **i32)
         self.slot_pos = torch.empty((B, H, K), **i32)
@@ -392,8 +393,6 @@ class MlaDecoder:
         self.load_count = torch.empty((B, H), **i32)
         self.o_lat = torch.zeros((B, 1, H, p.latent_dim), **f32)
         self.out = torch.zeros((B, H, p.nope_dim), **f32)
-        self.ws_scores = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, self.shape)),
-                                     dtype=torch.uint8, device=dev)
         self.ws_topk = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_TOPK, self.shape)),
                                    dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.shape)),
@@ -411,9 +410,10 @@ class MlaDecoder:
         mark("absorb", st)
         api.spc_mla_absorb_q(s, self.p.nope_dim, self.w_uk, q_nope, q_rope, self.q_abs, stream=st)
         mark("scores", st)
-        api.spc_retrieval_scores(s, self.q_abs, self.latent, lengths, self.probs, ws=self.ws_scores, stream=st)
+        api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.tile_stats, stream=st)
         mark("topk", st)
-        api.spc_group_max_topk(s, self.probs, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk, stream=st)
+        api.spc_group_max_topk_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk,
+                                      stream=st)
         mark("plan", st)
         api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
                                self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)

@@ -193,3 +193,36 @@ def test_lag1_plan_host_validation():
         bad = list(ptrs)
         bad[i] = None
         assert call(pool, 256, bad) == L.SPC_ERR_INVALID_ARG
+
+
+def test_log_domain_scoring_sizes_and_validation():
+    """spc_retrieval_logits / spc_group_max_topk_logits: tile sizes, the stats buffer size, and
+    rejection before launch (every call here fails validation: the fake pointers are never used)."""
+    lib = L.lib()
+    s = _shape(batch=2, max_len=1000)
+    assert lib.spc_score_tile(ctypes.byref(s)) == 128
+    assert lib.spc_tile_stats_size(ctypes.byref(s)) == 2 * 32 * 8 * 8          # ceil(1000 / 128) = 8 tiles
+    mla = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                 budget=2048, scale=192 ** -0.5)
+    assert lib.spc_score_tile(ctypes.byref(mla)) == 256
+    assert lib.spc_tile_stats_size(ctypes.byref(mla)) == 4 * 128 * 128 * 8
+    assert lib.spc_score_tile(ctypes.byref(_shape(budget=0))) == 0
+    p = ctypes.c_void_p(256)
+    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, None, None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, ctypes.c_void_p(260), None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_retrieval_logits(ctypes.byref(_shape(head_dim=96)), p, p, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
+    need = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s))
+    # four heads per group: the tile stats are required
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, None, p, p, p, p, need, None) == L.SPC_ERR_INVALID_ARG
+    assert b"tile_stats" in lib.spc_last_error()
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, p, p, p, p, p, need - 1, None) == L.SPC_ERR_WORKSPACE
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, ctypes.c_void_p(260), p, p, p, p, need,
+                                         None) == L.SPC_ERR_INVALID_ARG
+    wide = _shape(n_q_heads=128, n_kv_heads=1, n_groups=1)                      # 128 heads in one group
+    assert lib.spc_group_max_topk_logits(ctypes.byref(wide), p, p, p, p, p, p, 1 << 40,
+                                         None) == L.SPC_ERR_UNSUPPORTED
+    # one head per group: NULL stats are accepted (checked here with a workspace too small)
+    mha = _shape(n_q_heads=8, n_kv_heads=8, n_groups=8)
+    need_mha = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(mha))
+    assert lib.spc_group_max_topk_logits(ctypes.byref(mha), p, None, p, p, p, p, need_mha - 1,
+                                         None) == L.SPC_ERR_WORKSPACE

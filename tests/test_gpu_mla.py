@@ -5,6 +5,7 @@ import pytest
 import torch
 
 from oracle import spc_oracle as O
+from speculative_kv_sparsity_amd import api
 from speculative_kv_sparsity_amd import workload as W
 from speculative_kv_sparsity_amd.driver import MlaDecoder
 from tests.gpu_util import (ATTN_DERIVED, ATTN_MAX_ABS, PROBS_RTOL, check_topk_tolerance, dev_lengths, raw,
@@ -19,6 +20,7 @@ def _bf(t):
 
 def _check_steps(p, w, steps, lengths_override=None, heads=None, batches=None):
     dec = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+    T = api.spc_score_tile(dec.shape)
     C = p.latent_dim
     w_uk, w_uv = _bf(w.w_uk), _bf(w.w_uv)
     lat_all = [_bf(w.latent[b]) for b in range(p.batch)]
@@ -32,13 +34,14 @@ def _check_steps(p, w, steps, lengths_override=None, heads=None, batches=None):
         dec.step(qn, qr, dev_lengths(lengths))
         torch.cuda.synchronize()
         qn64, qr64 = _bf(qn), _bf(qr)
-        probs = dec.probs.cpu().numpy().astype(np.float64)
+        logits = dec.logits.cpu().numpy().astype(np.float64)
+        stats = dec.tile_stats.cpu().numpy().astype(np.float64)
         gsel = sel_lists(dec.sel_idx, dec.sel_count)
-        # Top-K bit-exact on the GPU's own float32 scores, every head
+        # Top-K bit-exact on the GPU's own float32 logits (one head per group: ranked as they are)
         for b in range(p.batch):
             n = int(lengths[b])
             for h in range(p.n_q_heads):
-                ref = O.topk_select(np.nan_to_num(probs[b, h]), n, p.budget)
+                ref = O.topk_select(np.nan_to_num(logits[b, h], nan=-np.inf), n, p.budget)
                 np.testing.assert_array_equal(gsel[b][h], ref)
         # scores and selection against the literal-expansion oracle, sampled heads
         for b in batches:
@@ -50,9 +53,13 @@ def _check_steps(p, w, steps, lengths_override=None, heads=None, batches=None):
             lat, rope = lat_all[b][:, :C], lat_all[b][:, C:]
             ref_p = O.mla_retrieval_scores(qn64[b:b + 1], qr64[b:b + 1], lat[None], rope[None], w_uk, [n], p.scale,
                                            heads=heads)
+            nt = (n + T - 1) // T
             for h in heads:
                 rp = ref_p[(0, h)]
-                np.testing.assert_allclose(probs[b, h, :n], rp, rtol=PROBS_RTOL, atol=0)
+                # the probabilities exp(logit - lse), lse from the head's tile pairs
+                m, sm = stats[b, h, :nt, 0], stats[b, h, :nt, 1]
+                lse = np.max(m) + np.log(np.sum(sm * np.exp(m - np.max(m))))
+                np.testing.assert_allclose(np.exp(logits[b, h, :n] - lse), rp, rtol=PROBS_RTOL, atol=0)
                 ref_sel = O.topk_select(rp, n, p.budget)
                 check_topk_tolerance([[gsel[b][h]]], [[ref_sel]], rp[None, None, :], p.budget)
                 # attention + output projection over the GPU's selection, rows expanded literally

@@ -89,6 +89,150 @@ def test_topk_exact_on_gpu_scores_and_tolerant_vs_oracle_chain(name, p, lengths)
     check_topk_tolerance(sel_lists(sel_idx, sel_count), ref_sel, ref_grp, p.budget)
 
 
+# --------------------------------------------------------------- log-domain form of stages 1-2
+
+
+def _logits(p, w, lengths):
+    shape = shape_of(p)
+    nan = float("nan")
+    logits = torch.full((p.batch, p.n_q_heads, p.max_len), nan, device="cuda")
+    stats = torch.full(api.tile_stats_shape(shape), nan, device="cuda")
+    api.spc_retrieval_logits(shape, w.q[0].contiguous(), w.dlm_k, dev_lengths(lengths), logits, stats)
+    torch.cuda.synchronize()
+    return shape, logits, stats
+
+
+def _lse(stats_bh, nt):
+    """log-sum-exp of a head from its first nt tile pairs, in float64."""
+    m, s = stats_bh[:nt, 0].astype(np.float64), stats_bh[:nt, 1].astype(np.float64)
+    M = np.max(m)
+    return M + np.log(np.sum(s * np.exp(m - M)))
+
+
+@pytest.mark.parametrize("name,p,lengths", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_logits_and_tile_stats_give_the_oracle_probabilities(name, p, lengths):
+    w = W.generate(p, device="cuda", seed=11, steps=1)
+    lengths = list(w.lengths[0]) if lengths is None else lengths
+    shape, logits, stats = _logits(p, w, lengths)
+    T = api.spc_score_tile(shape)
+    ref = O.retrieval_scores(f64(w.q[0], p.dtype), f64(w.dlm_k, p.dtype), lengths, p.scale)
+    lg = logits.cpu().numpy()
+    st = stats.cpu().numpy()
+    for b, n in enumerate(lengths):
+        assert np.all(np.isnan(lg[b, :, n:]))              # positions past the length are not written
+        nt = (n + T - 1) // T
+        assert np.all(np.isnan(st[b, :, nt:]))             # nor the tiles past it
+        if n == 0:
+            continue
+        for i in range(p.n_q_heads):
+            x = lg[b, i, :n].astype(np.float64)
+            # each tile pair is the exact max and the sum of exp over the tile's own logits
+            for t in range(nt):
+                seg = x[t * T:min(n, (t + 1) * T)]
+                assert st[b, i, t, 0] == np.max(seg)
+                np.testing.assert_allclose(st[b, i, t, 1], np.sum(np.exp(seg - np.max(seg))), rtol=1e-5)
+            # exp(logit - lse) are the oracle's probabilities
+            pr = np.exp(x - _lse(st[b, i], nt))
+            np.testing.assert_allclose(pr, ref[b, i, :n], rtol=PROBS_RTOL, atol=0)
+
+
+def _topk_logits_gpu(shape, logits, stats, lengths):
+    B, G, K = shape.batch, shape.n_groups, shape.budget
+    sel_idx = torch.full((B, G, K), -7, dtype=torch.int32, device="cuda")
+    sel_count = torch.full((B, G), -7, dtype=torch.int32, device="cuda")
+    api.spc_group_max_topk_logits(shape, logits, stats, dev_lengths(lengths), sel_idx, sel_count)
+    torch.cuda.synchronize()
+    return sel_idx, sel_count
+
+
+@pytest.mark.parametrize("name,p,lengths", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_topk_on_logits_matches_the_oracle_chain(name, p, lengths):
+    w = W.generate(p, device="cuda", seed=12, steps=1)
+    lengths = list(w.lengths[0]) if lengths is None else lengths
+    shape, logits, stats = _logits(p, w, lengths)
+    sel_idx, sel_count = _topk_logits_gpu(shape, logits, stats, lengths)
+    if p.n_groups == p.n_q_heads:
+        # one head per group: the GPU's float32 logits are ranked as they are (bit-exact)
+        gl = np.nan_to_num(logits.cpu().numpy().astype(np.float64), nan=-np.inf)
+        _assert_sel_equal(sel_idx, sel_count, _oracle_topk(gl, lengths, p.n_groups, p.budget), p.budget)
+    ref_probs = O.retrieval_scores(f64(w.q[0], p.dtype), f64(w.dlm_k, p.dtype), lengths, p.scale)
+    ref_grp = O.group_scores(ref_probs, p.n_groups)
+    ref_sel = O.select_all(ref_grp, lengths, p.budget)
+    check_topk_tolerance(sel_lists(sel_idx, sel_count), ref_sel, ref_grp, p.budget)
+    # the probability path on the same inputs agrees with it up to the same near-ties
+    _, probs = _scores(p, w, lengths)
+    ps, pc = _topk_gpu(shape, probs, lengths)
+    check_topk_tolerance(sel_lists(sel_idx, sel_count), sel_lists(ps, pc), ref_grp, p.budget)
+
+
+def _host_stats(vals, T):
+    """float32 tile pairs (max, sum exp) of given logits [B][H][L] (test input construction)."""
+    B, H, L = vals.shape
+    nt = (L + T - 1) // T
+    st = np.zeros((B, H, nt, 2), dtype=np.float32)
+    for t in range(nt):
+        seg = vals[:, :, t * T:(t + 1) * T].astype(np.float64)
+        m = seg.max(axis=2)
+        st[:, :, t, 0] = m
+        st[:, :, t, 1] = np.exp(seg - m[..., None]).sum(axis=2)
+    return st
+
+
+LOGIT_TIE_CASES = [
+    # (B, Hq, G, L, K, lengths, value pool or None, same pool for every head)
+    (1, 4, 1, 3000, 64, [3000], [0.125], True),                     # all equal: lowest indices win
+    (2, 8, 2, 5000, 300, [5000, 4097], [-3.0, 0.0, 2.5], True),     # heavy ties inside each head
+    (1, 2, 2, 40000, 2048, [40000], None, False),                   # keys streamed from global memory
+    (1, 6, 2, 33000, 5000, [33000], None, False),                   # 3 heads per group, LDS limit crossed
+    (3, 2, 1, 2000, 100, [100, 101, 0], None, False),               # n = K, n = K + 1, n = 0
+    (2, 4, 4, 1500, 1, [1500, 7], [-1.0, 4.0], True),               # K = 1, one head per group
+]
+
+
+@pytest.mark.parametrize("case", LOGIT_TIE_CASES, ids=[f"ltie{i}" for i in range(len(LOGIT_TIE_CASES))])
+def test_topk_on_logits_with_ties_and_edges(case):
+    B, Hq, G, L, K, lengths, pool, shared = case
+    rng = np.random.default_rng(7)
+    if pool is None:
+        vals = (4.0 * rng.standard_normal((B, Hq, L))).astype(np.float32)
+    else:
+        vals = rng.choice(np.asarray(pool, dtype=np.float32), size=(B, Hq, L))
+        if shared:                       # every head of a group sees the same values: equal lse
+            vals[:] = vals[:, :1]
+    for b, n in enumerate(lengths):
+        vals[b, :, n:] = np.nan                                # never read
+    shape = api.make_shape(B, Hq, G, G, 128, 128, L, K, 1, "bf16", 1.0)
+    T = api.spc_score_tile(shape)
+    stats = np.zeros((B, Hq, (L + T - 1) // T, 2), dtype=np.float32)
+    for b, n in enumerate(lengths):
+        if n:
+            stats[b:b + 1, :, :(n + T - 1) // T] = _host_stats(vals[b:b + 1, :, :n], T)
+    sel_idx, sel_count = _topk_logits_gpu(shape, torch.from_numpy(vals).cuda(),
+                                          torch.from_numpy(stats).cuda() if Hq > G else None, lengths)
+    # fp64 reference: the probabilities exp(l - lse) of the same logits, group max, Top-K
+    probs = np.zeros((B, Hq, L))
+    for b, n in enumerate(lengths):
+        if n:
+            x = vals[b, :, :n].astype(np.float64)
+            m = x.max(axis=1, keepdims=True)
+            probs[b, :, :n] = np.exp(x - m) / np.exp(x - m).sum(axis=1, keepdims=True)
+    grp = O.group_scores(probs, G)
+    ref = O.select_all(grp, lengths, K)
+    if shared or Hq == G:
+        _assert_sel_equal(sel_idx, sel_count, ref, K)          # ties are exact in both domains
+    else:
+        check_topk_tolerance(sel_lists(sel_idx, sel_count), ref, grp, K)
+
+
+def test_topk_logits_rejects_missing_stats():
+    shape = api.make_shape(1, 8, 2, 2, 128, 128, 1000, 64, 1, "bf16", 1.0)
+    lg = torch.zeros((1, 8, 1000), device="cuda")
+    sel = torch.zeros((1, 2, 64), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(api.SpcError):
+        api.spc_group_max_topk_logits(shape, lg, None, dev_lengths([1000]), sel, cnt)
+
+
 TIE_CASES = [
     # (B, Hq, G, L, K, lengths, value pool or None)
     (2, 8, 2, 5000, 300, [5000, 4097], [0.0, 0.25, 0.5]),          # heavy ties across radix passes
