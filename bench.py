@@ -310,6 +310,9 @@ def bench_gqa(args, p, torch, W):
         iso_ms["attn"] = iso(torch, lambda st: api.spc_sparse_decode_attn(
             dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
             dec.out, ws=dec.ws_attn[0], stream=st), R)
+        iso_ms["attn_partial"] = iso(torch, lambda st: api.spc_attn_partial(
+            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
+            dec.ws_attn[0], stream=st), R)
         iso_ms["copy"] = iso(torch, lambda st: api.spc_elastic_update(
             dec.shape, None, None, None, None, dec.load_pos, dec.load_slot, dec.load_count, dec.host_kv, dec.host_l,
             dec.dev_kv, dec.dev_l, c0a, c0z, flags=api.SPC_COPY, plan_stream=st, copy_stream=st),
@@ -317,6 +320,9 @@ def bench_gqa(args, p, torch, W):
     else:                     # every layer on the GPU: the gather from the full cache is the attention
         c0a, c0z = 0, dec.n_res
         iso_ms["attn"] = iso(torch, lambda st: dec.attend_resident(tq, st), R)
+        iso_ms["attn_partial"] = iso(torch, lambda st: api.spc_attn_partial(
+            dec.shape, tq, dec.q_l, dec.full_kv, dec.full_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0,
+            dec.n_res, dec.ws_attn[0], stream=st), R)
     # the retrieval head's front end (upstream of the step): new tokens -> query, key appended
     fw = W.generate_front(p, device="cuda", seed=args.seed, steps=1)
     head = RetrievalHead(dec.shape, fw)
@@ -331,7 +337,8 @@ def bench_gqa(args, p, torch, W):
     row = 2 * d * eb                                             # one K||V row
     sel_per_group = float(np.mean(sel_rows)) / (B * p.n_groups)
     # algorithmic bytes per call (one launch of the stage)
-    attn_bytes = B * lay0 * Hkv * sel_per_group * row + B * lay0 * Hq * d * 4   # K/V read + out write
+    kv_bytes = B * lay0 * Hkv * sel_per_group * row                         # K/V rows read (split kernel)
+    attn_bytes = kv_bytes + B * lay0 * Hq * d * 4                             # + out write (the whole call)
     score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4              # keys read + logits (probs) write
     front_bytes = ((Hq + Hkv) * d * fw.hidden + B * fw.hidden + fw.hidden + B * (Hq + Hkv) * d) * eb
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
@@ -346,11 +353,14 @@ def bench_gqa(args, p, torch, W):
         config.update({"hbm_gb": args.hbm_gb, "weights_gb": args.weights_gb, "offloaded_layers": off,
                        "offload_thresholds": thresholds})
     result = _header(args, p, ms_per_step, config)
-    attn_kernel = ("attn_split_kernel + attn_combine_kernel (sparse decode attention, split-K" +
-                   (", slots of the offloaded layers)" if nch else
-                    ", selected rows gathered from the GPU-resident full cache)"))
-    result["roofline"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s", attn_kernel,
-                              max(nch, 1), traffic.get("attn"))
+    rows_of = (", slots of the offloaded layers" if nch else
+               ", selected rows gathered from the GPU-resident full cache")
+    result["roofline"] = roof("hbm", kv_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
+                              "attn_split_kernel (the dominant kernel: split-K partial attention" + rows_of +
+                              "; timed alone through spc_attn_partial)", max(nch, 1), traffic.get("attn_partial"))
+    result["roofline_attn_call"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                                        "attn_split_kernel + attn_combine_kernel (spc_sparse_decode_attn: the "
+                                        "whole stage-4 call" + rows_of + ")", max(nch, 1), traffic.get("attn"))
     result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
                                      "scores_logits_kernel (stage 1 as the step runs it: logits and per-tile "
                                      "max / sum exp in one pass over the DLM keys)", 1, traffic.get("scores"))
@@ -435,6 +445,9 @@ def bench_lag1(args, p, torch, W):
         "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
             dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
             0, p.n_layers, dec.out, ws=dec.ws_attn, stream=st), R),
+        "attn_partial": iso(torch, lambda st: api.spc_attn_partial(
+            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
+            0, p.n_layers, dec.ws_attn, stream=st), R),
         "copy": iso(torch, lambda st: api.spc_elastic_update(
             dec.pool_shape, None, None, None, None, dec.load_pos[nx], dec.load_slot[nx], dec.load_count[nx],
             dec.host_kv, dec.host_l, dec.dev_kv, dec.dev_l, 0, p.n_layers, flags=api.SPC_COPY, plan_stream=st,
@@ -445,7 +458,8 @@ def bench_lag1(args, p, torch, W):
     n_valid = float(np.mean(w.lengths[t0 + Wm + K_:t0 + total].sum(axis=1)))
     row = 2 * d * eb
     sel_per_group = float(np.mean(sel_rows)) / (B * p.n_groups)
-    attn_bytes = B * p.n_layers * Hkv * sel_per_group * row + B * p.n_layers * Hq * d * 4
+    kv_bytes = B * p.n_layers * Hkv * sel_per_group * row
+    attn_bytes = kv_bytes + B * p.n_layers * Hq * d * 4
     score_bytes = n_valid * Hkv * d * eb + n_valid * Hq * 4
     copy_bytes = float(np.mean(loaded)) * p.n_layers * row
     config = {"workload": WORKLOADS.get(p.name, p.name), "batch": B, "layers": p.n_layers, "q_heads": Hq,
@@ -453,9 +467,11 @@ def bench_lag1(args, p, torch, W):
               "first_step": t0, "kv_budget": K, "pipeline": "lag 1 (attention over the previous step's selection)",
               "slot_pool": dec.P, "parallelism": "single GPU"}
     result = _header(args, p, ms_per_step, config)
-    result["roofline"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
-                              "attn_split_kernel + attn_combine_kernel (the pool's rows of the current selection, "
-                              "gathered)", 1)
+    result["roofline"] = roof("hbm", kv_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
+                              "attn_split_kernel (the dominant kernel: the pool's rows of the current selection, "
+                              "gathered; timed alone through spc_attn_partial)", 1)
+    result["roofline_attn_call"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                                        "attn_split_kernel + attn_combine_kernel (the whole stage-4 call)", 1)
     result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
                                      "scores_logits_kernel (logits and per-tile max / sum exp, one pass)", 1)
     result["roofline_host_link"] = roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
@@ -520,6 +536,9 @@ def bench_mla(args, p, torch, W):
                                                                     dec.sel_count, ws=dec.ws_topk, stream=st), R),
         "scores_probs": iso(torch, probs_call(torch, api, s, dec.q_abs, dec.latent, tl), R),
         "attn": iso(torch, lambda st: dec.attend(st), R),
+        "attn_partial": iso(torch, lambda st: api.spc_attn_partial(
+            s, dec.q_abs, dec.q_l, dec.latent, dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0, 1,
+            dec.ws_attn, stream=st), R),
         "out_proj": iso(torch, lambda st: api.spc_mla_out_proj(s, p.nope_dim, dec.w_uv, dec.o_lat, 0, dec.out,
                                                                stream=st), R),
     }
@@ -528,7 +547,8 @@ def bench_mla(args, p, torch, W):
     sel = float(np.mean(sel_rows))
     union = float(np.mean(union_rows))
     row = D * p.elem_bytes                                      # one latent row: 512 latent + 64 rope dims
-    attn_bytes = union * row + B * H * p.latent_dim * 4          # every selected row once + o_lat writes
+    lat_bytes = union * row                                      # every selected row once (split kernel)
+    attn_bytes = lat_bytes + B * H * p.latent_dim * 4            # + o_lat writes (the whole call)
     gathered = sel * row                                         # each head's own gather (L2 / last-level cache)
     score_flop = 2.0 * n_valid * H * D                           # every head against every valid latent row
     score_bytes = n_valid * row + n_valid * H * 4               # latent read once + logits (probs) write
@@ -538,11 +558,15 @@ def bench_mla(args, p, torch, W):
               "cached_tokens": L, "kv_budget": p.budget, "parallelism": "single GPU"}
     result = _header(args, p, ms_per_step, config)
     result.update({
-        "roofline": dict(roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
-                              "attn_split_latent_kernel + attn_combine_kernel (each head gathers its selected latent "
-                              "rows; a row selected by several heads is counted once here)", 1, traffic.get("attn")),
+        "roofline": dict(roof("hbm", lat_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
+                              "attn_split_latent_kernel (the dominant kernel, timed alone through spc_attn_partial: "
+                              "each head gathers its selected latent rows; a row selected by several heads is "
+                              "counted once here)", 1, traffic.get("attn_partial")),
                          gathered_bytes_per_launch=int(gathered),
-                         gathered_GBs=round(gathered / (iso_ms["attn"] * 1e-3) / 1e9, 1)),
+                         gathered_GBs=round(gathered / (iso_ms["attn_partial"] * 1e-3) / 1e9, 1)),
+        "roofline_attn_call": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                                   "attn_split_latent_kernel + attn_combine_kernel (the whole stage-4 call)", 1,
+                                   traffic.get("attn")),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                 "mla_scores_kernel (logits and per-tile max / sum exp; bf16 MFMA, fp32 query as "
                                 "a hi/lo bf16 pair: 2 MFMAs per product)", 1),

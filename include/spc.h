@@ -342,6 +342,24 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
                            size_t ws_bytes, void* stream);
 
 /*
+ * The two halves of spc_sparse_decode_attn (split-K), for a caller that runs them
+ * apart (the merge on another stream, or later) or times them:
+ *   spc_attn_partial  attends every split of the rows and leaves, in ws, each split's
+ *                     unnormalised output and (max, sum of exp) per head, in the
+ *                     library's own layout; same arguments as spc_sparse_decode_attn
+ *                     without `out`
+ *   spc_attn_merge    combines those splits with their log-sum-exp weights into `out`
+ *                     for the same shape and layer range; ws is only read
+ * spc_attn_partial followed by spc_attn_merge on one stream (or ordered by an event)
+ * gives exactly the output of spc_sparse_decode_attn.
+ */
+int spc_attn_partial(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                     const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
+                     int32_t layer_begin, int32_t layer_end, void* ws, size_t ws_bytes, void* stream);
+int spc_attn_merge(const spc_shape* s, int32_t layer_begin, int32_t layer_end, const void* ws, size_t ws_bytes,
+                   float* out, void* stream);
+
+/*
  * MLA helpers (SpeContext blog section 5, last paragraph; paper summary section
  * 4.3: MLA keeps a low-dimensional latent per position, retrieval stays
  * head-level, and only the selected latent rows are expanded).  The per-head

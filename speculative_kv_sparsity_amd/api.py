@@ -22,7 +22,7 @@ __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version",
            "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "SPC_CALL_FRONT", "spc_mla_absorb_q",
            "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds",
            "spc_elastic_plan_lag1", "spc_retrieval_logits", "spc_group_max_topk_logits", "spc_score_tile",
-           "spc_tile_stats_size", "tile_stats_shape"]
+           "spc_tile_stats_size", "tile_stats_shape", "spc_attn_partial", "spc_attn_merge"]
 
 
 class SpcError(RuntimeError):
@@ -173,6 +173,25 @@ def spc_sparse_decode_attn(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvL
         ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
         int(rows_mode), int(layer_begin), int(layer_end), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def spc_attn_partial(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvLayout, rows, row_count, rows_mode: int,
+                     layer_begin: int, layer_end: int, ws, stream=None) -> None:
+    """The split half of spc_sparse_decode_attn: per-split partials into ws (kept for spc_attn_merge)."""
+    for t, n in ((q, "q"), (kv, "kv"), (rows, "rows"), (ws, "ws")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a device tensor")
+    _check(L.lib().spc_attn_partial(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
+        int(rows_mode), int(layer_begin), int(layer_end), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spc_attn_merge(shape: SpcShape, layer_begin: int, layer_end: int, ws, out, stream=None) -> None:
+    """The merge half of spc_sparse_decode_attn: the partials in ws -> out."""
+    _dev(out, "out")
+    _dev(ws, "ws")
+    _check(L.lib().spc_attn_merge(ctypes.byref(shape), int(layer_begin), int(layer_end), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _ptr(out), _stream(stream)))
 
 
 def spc_mla_absorb_q(shape: SpcShape, nope_dim: int, w_uk, q_nope, q_rope, q_abs, stream=None) -> None:

@@ -241,12 +241,15 @@ int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos
   return e == hipSuccess ? ok() : hip_fail(e, "elastic reset launch");
 }
 
-int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
-                           const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
-                           int32_t layer_begin, int32_t layer_end, float* out, void* ws, size_t ws_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+// Arguments of the partial half (and of the whole call, which adds `out`).
+int check_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv, const spc_kv_layout* kv_l,
+               const int32_t* rows, const int32_t* row_count, int rows_mode, int32_t layer_begin, int32_t layer_end,
+               void* ws, size_t ws_bytes) {
   if (int e = check_shape(s)) return e;
-  if (!q || !q_l || !kv || !kv_l || !rows || !out) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (!q || !q_l || !kv || !kv_l || !rows) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
   if (rows_mode != SPC_ROWS_SLOTS && rows_mode != SPC_ROWS_GATHER)
     return fail(SPC_ERR_INVALID_ARG, "rows_mode %d", rows_mode);
   if (rows_mode == SPC_ROWS_GATHER && !row_count) return fail(SPC_ERR_INVALID_ARG, "GATHER needs row_count");
@@ -255,12 +258,14 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
   if (!spc::attn_supported(*s))
     return fail(SPC_ERR_UNSUPPORTED, "attention: head_dim %d / v_dim %d with dtype %d", s->head_dim, s->v_dim,
                 s->dtype);
+  if (spc::attn_splits(*s) > spc::kCombineMaxSplits)
+    return fail(SPC_ERR_UNSUPPORTED, "attention: budget %d needs more than %d row splits", s->budget,
+                spc::kCombineMaxSplits);
   if (s->head_dim == 576 && kv_l->s_kv != 0)
     return fail(SPC_ERR_UNSUPPORTED, "head_dim 576 reads V from the latent row itself (s_kv must be 0)");
   const int eb = elem_bytes(s);
   const int qeb = spc::mla_shape(*s) ? 4 : eb;   // MLA: float32 absorbed query
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(out))
-    return fail(SPC_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(kv)) return fail(SPC_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
   if ((q_l->s_b * qeb) % 16 || (q_l->s_layer * qeb) % 16 || (q_l->s_head * qeb) % 16)
     return fail(SPC_ERR_INVALID_ARG, "query strides must be multiples of 16 bytes");
   if ((kv_l->s_b * eb) % 16 || (kv_l->s_layer * eb) % 16 || (kv_l->s_head * eb) % 16 || (kv_l->s_row * eb) % 16 ||
@@ -270,9 +275,52 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
   if (ws_bytes < need || !ws)
     return fail(SPC_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
   if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return SPC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                           const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
+                           int32_t layer_begin, int32_t layer_end, float* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws, ws_bytes))
+    return e;
+  if (!out || !aligned16(out)) return fail(SPC_ERR_INVALID_ARG, "out must be a 16-byte aligned device pointer");
   const hipError_t e = spc::launch_attn(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin, layer_end,
                                         out, ws, as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "sparse decode attention launch");
+}
+
+int spc_attn_partial(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                     const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
+                     int32_t layer_begin, int32_t layer_end, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws, ws_bytes))
+    return e;
+  const hipError_t e = spc::launch_attn_partial(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin,
+                                                layer_end, ws, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "partial attention launch");
+}
+
+int spc_attn_merge(const spc_shape* s, int32_t layer_begin, int32_t layer_end, const void* ws, size_t ws_bytes,
+                   float* out, void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (!ws || !out) return fail(SPC_ERR_INVALID_ARG, "NULL ws or out");
+  if (layer_begin < 0 || layer_end > s->n_layers || layer_begin >= layer_end)
+    return fail(SPC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end, s->n_layers);
+  if (!spc::attn_supported(*s))
+    return fail(SPC_ERR_UNSUPPORTED, "attention: head_dim %d / v_dim %d with dtype %d", s->head_dim, s->v_dim,
+                s->dtype);
+  if (spc::attn_splits(*s) > spc::kCombineMaxSplits)
+    return fail(SPC_ERR_UNSUPPORTED, "attention: budget %d needs more than %d row splits", s->budget,
+                spc::kCombineMaxSplits);
+  if (ws_bytes < spc::attn_ws_bytes(*s))
+    return fail(SPC_ERR_WORKSPACE, "attention merge reads %zu workspace bytes, got %zu", spc::attn_ws_bytes(*s),
+                ws_bytes);
+  if (!aligned16(ws) || !aligned16(out)) return fail(SPC_ERR_INVALID_ARG, "ws and out must be 16-byte aligned");
+  const hipError_t e = spc::launch_attn_merge(*s, layer_begin, layer_end, ws, out, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "attention merge launch");
 }
 
 }  // extern "C"

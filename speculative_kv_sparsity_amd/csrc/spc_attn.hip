@@ -22,7 +22,7 @@
 // attn_split_latent_kernel  the same for MLA latent rows, where V is the first
 //   v_dim elements of the K row (read once, used twice) and one head per group.
 // attn_combine_kernel  merges the splits of every head with their log-sum-exp
-//   weights into the float32 output, 4 dims per thread.
+//   weights into the float32 output (one workgroup per head).
 #include "spc_common.h"
 #include "spc_launch.h"
 
@@ -405,68 +405,98 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   }
 }
 
-constexpr int kCombineChunk = 16;
-// One thread per (instance, head chunk, head, 4 consecutive dims): the split
-// weights (max, sum) of the head are read once for its 4 dims, the partial
-// outputs as 16-byte vectors, 16 splits at a time (all loads of a chunk issued
-// together), merged online.
+// One workgroup per head: every thread first issues the loads of its
+// partial-output vectors (4 dims, every (256 / (DV/4))-th split), then wave 0
+// turns the splits' (max, sum) into weights exp(m_s - M) and 1 / L in LDS, and
+// each thread folds its splits; the split groups are summed through LDS.  The
+// partial loads do not wait for the weights, so the whole merge costs about one
+// memory round trip.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineRegs = 8;           // partial vectors a thread keeps in flight per round
 template <int GQC>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml,
-                                                           float* __restrict__ out, int DV, int Hq, int n_layers,
-                                                           int n_groups, int layer_begin, int n_lay, int nsplit,
-                                                           int nhc, int64_t n_out4) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_out4) return;
-  const int DV4 = DV / 4;
-  const int d4 = (int)(t % DV4);
-  const int64_t ih = t / DV4;                // ((inst * nhc + hcix) * GQC + h)
-  const int h = (int)(ih % GQC);
-  const int64_t ic = ih / GQC;               // inst * nhc + hcix
-  const int hcix = (int)(ic % nhc);
-  const int inst = (int)(ic / nhc);
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                                       const float2* __restrict__ part_ml,
+                                                                       float* __restrict__ out, int DV, int Hq,
+                                                                       int n_layers, int n_groups, int layer_begin,
+                                                                       int n_lay, int nsplit, int nhc) {
+  __shared__ float s_w[kCombineMaxSplits];
+  __shared__ float s_l[kCombineMaxSplits];
+  __shared__ float s_inv;
+  __shared__ float4 s_acc[kCombineThreads];
+  const int ih = blockIdx.x;                 // ((inst * nhc + hcix) * GQC + h)
+  const int h = ih % GQC;
+  const int ic = ih / GQC;                   // inst * nhc + hcix
+  const int hcix = ic % nhc;
+  const int inst = ic / nhc;
   const int r = inst % n_groups;
   const int bl = inst / n_groups;
   const int lo = bl % n_lay;
   const int b = bl / n_lay;
   const int head = r * (Hq / n_groups) + hcix * GQC + h;
   const size_t pb = (size_t)ic * nsplit;
-  float M = -INFINITY, L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < nsplit; s0 += kCombineChunk) {
-    float2 ml[kCombineChunk];
-    float4 po[kCombineChunk];
+  const int tid = threadIdx.x;
+  const int DV4 = DV / 4;
+  const int ngrp = kCombineThreads / DV4;    // split groups (DV4 divides 256)
+  const int d4 = tid % DV4, sg = tid / DV4;
+  const float4* po = reinterpret_cast<const float4*>(part_o);
+  // this thread's first round of partial vectors, issued before the weights exist
+  float4 x[kCombineRegs];
 #pragma unroll
-    for (int i = 0; i < kCombineChunk; ++i) {
-      if (s0 + i < nsplit) {
-        ml[i] = part_ml[(pb + s0 + i) * GQC + h];
-        po[i] = reinterpret_cast<const float4*>(part_o + ((pb + s0 + i) * GQC + h) * DV)[d4];
-      } else {
-        ml[i] = make_float2(-INFINITY, 0.f);
-        po[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-    float Mc = M;
-#pragma unroll
-    for (int i = 0; i < kCombineChunk; ++i)
-      if (ml[i].y > 0.f) Mc = fmaxf(Mc, ml[i].x);
-    if (Mc == -INFINITY) continue;
-    const float rescale = M == -INFINITY ? 0.f : __expf(M - Mc);
-    L *= rescale;
-    acc.x *= rescale; acc.y *= rescale; acc.z *= rescale; acc.w *= rescale;
-#pragma unroll
-    for (int i = 0; i < kCombineChunk; ++i) {
-      if (ml[i].y > 0.f) {
-        const float w = __expf(ml[i].x - Mc);
-        L += ml[i].y * w;
-        acc.x += po[i].x * w; acc.y += po[i].y * w; acc.z += po[i].z * w; acc.w += po[i].w * w;
-      }
-    }
-    M = Mc;
+  for (int u = 0; u < kCombineRegs; ++u) {
+    const int sp = sg + u * ngrp;
+    x[u] = sp < nsplit ? po[((pb + sp) * GQC + h) * DV4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  reinterpret_cast<float4*>(out + (((size_t)b * n_layers + layer_begin + lo) * Hq + head) * DV)[d4] =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (tid < kWave) {
+    // (max, sum) of every split: the split's max goes to s_w, its sum to s_l, one load each
+    float M = -INFINITY;
+    for (int sp = tid; sp < nsplit; sp += kWave) {
+      const float2 ml = part_ml[(pb + sp) * GQC + h];
+      s_w[sp] = ml.y > 0.f ? ml.x : -INFINITY;
+      s_l[sp] = ml.y;
+      M = fmaxf(M, s_w[sp]);
+    }
+    M = wave_max(M);
+    float L = 0.f;
+    for (int sp = tid; sp < nsplit; sp += kWave) {     // each lane rereads only its own entries
+      const float w = s_w[sp] == -INFINITY ? 0.f : __expf(s_w[sp] - M);
+      s_w[sp] = w;
+      L += s_l[sp] * w;
+    }
+    L = wave_sum(L);
+    if (tid == 0) s_inv = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineRegs * ngrp) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kCombineRegs; ++u) {
+        const int sp = s0 + sg + u * ngrp;
+        x[u] = sp < nsplit ? po[((pb + sp) * GQC + h) * DV4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineRegs; ++u) {
+      const int sp = s0 + sg + u * ngrp;
+      const float w = sp < nsplit ? s_w[sp] : 0.f;
+      if (w > 0.f) {                         // a split without rows contributes nothing
+        acc.x = fmaf(w, x[u].x, acc.x); acc.y = fmaf(w, x[u].y, acc.y);
+        acc.z = fmaf(w, x[u].z, acc.z); acc.w = fmaf(w, x[u].w, acc.w);
+      }
+    }
+  }
+  s_acc[tid] = acc;
+  __syncthreads();
+  if (tid < DV4) {
+    float4 t = s_acc[tid];
+    for (int g = 1; g < ngrp; ++g) {
+      const float4 v = s_acc[g * DV4 + tid];
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+    }
+    const float inv = s_inv;
+    reinterpret_cast<float4*>(out + (((size_t)b * n_layers + layer_begin + lo) * Hq + head) * DV)[tid] =
+        make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
 }
 
 int head_chunk(const spc_shape& s) {
@@ -522,22 +552,42 @@ bool attn_supported(const spc_shape& s) {
   return (s.head_dim == 128 && s.v_dim == 128) || (s.head_dim == 64 && s.v_dim == 64);
 }
 
+int attn_splits(const spc_shape& s) { return (s.budget + rows_per_split(s) - 1) / rows_per_split(s); }
+
 size_t attn_ws_bytes(const spc_shape& s) {
   const size_t nsplit = (size_t)(s.budget + rows_per_split(s) - 1) / rows_per_split(s);
   const size_t heads = (size_t)s.batch * s.n_layers * s.n_q_heads;   // one partial per head per split
   return heads * nsplit * ((size_t)s.v_dim * sizeof(float) + sizeof(float2));
 }
 
-hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
-                       const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
-                       int layer_begin, int layer_end, float* out, void* ws, hipStream_t st) {
+namespace {
+
+struct AttnGeom {
+  int n_lay, nsplit, gqc, nhc;
+  size_t n_inst;
+  float* part_o;
+  float2* part_ml;
+};
+
+AttnGeom attn_geom(const spc_shape& s, int layer_begin, int layer_end, void* ws) {
+  AttnGeom g;
+  g.n_lay = layer_end - layer_begin;
+  g.nsplit = attn_splits(s);
+  g.gqc = head_chunk(s);
+  g.nhc = s.n_q_heads / s.n_groups / g.gqc;
+  g.n_inst = (size_t)s.batch * g.n_lay * s.n_groups;
+  g.part_o = static_cast<float*>(ws);
+  g.part_ml = reinterpret_cast<float2*>(g.part_o + g.n_inst * g.nhc * g.nsplit * g.gqc * s.v_dim);
+  return g;
+}
+
+}  // namespace
+
+hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
+                               const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
+                               int layer_begin, int layer_end, void* ws, hipStream_t st) {
   const int eb = s.dtype == SPC_BF16 ? 2 : 4;
-  const int n_lay = layer_end - layer_begin;
-  const int rps = rows_per_split(s);
-  const int nsplit = (s.budget + rps - 1) / rps;
-  const int gqc = head_chunk(s);
-  const int nhc = s.n_q_heads / s.n_groups / gqc;
-  const size_t n_inst = (size_t)s.batch * n_lay * s.n_groups;
+  const AttnGeom g = attn_geom(s, layer_begin, layer_end, ws);
   SplitArgs a;
   a.q = static_cast<const char*>(q);
   const int qeb = mla_shape(s) ? 4 : eb;          // MLA: float32 absorbed query
@@ -548,13 +598,14 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
   a.row_count = row_count;
   a.mode = mode;
   a.layer_begin = layer_begin;
-  a.n_lay = n_lay;
-  a.nsplit = nsplit;
-  a.nhc = nhc;
+  a.n_lay = g.n_lay;
+  a.nsplit = g.nsplit;
+  a.nhc = g.nhc;
   a.max_rows = mode == SPC_ROWS_SLOTS ? s.budget : s.max_len;
-  a.part_o = static_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float2*>(a.part_o + n_inst * nhc * nsplit * gqc * s.v_dim);
-  const dim3 grid(nsplit, (unsigned)n_inst, nhc);
+  a.part_o = g.part_o;
+  a.part_ml = g.part_ml;
+  const int gqc = g.gqc;
+  const dim3 grid(g.nsplit, (unsigned)g.n_inst, g.nhc);
   hipError_t e = hipErrorInvalidValue;
   if (s.dtype == SPC_F32) {
     e = launch_split_gqc<SPC_F32, 128>(gqc, s, grid, st, a);
@@ -573,14 +624,19 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
           a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
     e = hipGetLastError();
   }
-  if (e != hipSuccess) return e;
-  const int64_t n_out4 = (int64_t)n_inst * nhc * gqc * (s.v_dim / 4);
-  const dim3 g2((unsigned)((n_out4 + 255) / 256));
-  switch (gqc) {
+  return e;
+}
+
+hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end, const void* ws, float* out,
+                             hipStream_t st) {
+  const AttnGeom g = attn_geom(s, layer_begin, layer_end, const_cast<void*>(ws));
+  const dim3 g2((unsigned)(g.n_inst * g.nhc * g.gqc));
+  switch (g.gqc) {
 #define SPC_CASE(N)                                                                                         \
   case N:                                                                                                   \
-    attn_combine_kernel<N><<<g2, 256, 0, st>>>(a.part_o, a.part_ml, out, s.v_dim, s.n_q_heads, s.n_layers, \
-                                               s.n_groups, layer_begin, n_lay, nsplit, nhc, n_out4);        \
+    attn_combine_kernel<N><<<g2, kCombineThreads, 0, st>>>(g.part_o, g.part_ml, out, s.v_dim, s.n_q_heads,   \
+                                                           s.n_layers, s.n_groups, layer_begin, g.n_lay,     \
+                                                           g.nsplit, g.nhc);                                 \
     break;
     SPC_CASE(1)
     SPC_CASE(2)
@@ -591,6 +647,15 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
+                       const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
+                       int layer_begin, int layer_end, float* out, void* ws, hipStream_t st) {
+  const hipError_t e = launch_attn_partial(s, q, qlay, kv, klay, rows, row_count, mode, layer_begin, layer_end, ws,
+                                           st);
+  if (e != hipSuccess) return e;
+  return launch_attn_merge(s, layer_begin, layer_end, ws, out, st);
 }
 
 }  // namespace spc

@@ -78,10 +78,18 @@ hipError_t launch_front(const spc_shape& s, int hidden, int64_t vocab, const spc
                         const void* wq, const void* wk, void* q_out, void* dlm_k, void* ws, hipStream_t st);
 
 // ---- stage 4: sparse decode attention
+constexpr int kCombineMaxSplits = 1024;  // splits per head the combine merges
 size_t attn_ws_bytes(const spc_shape& s);
 bool attn_supported(const spc_shape& s);
+int attn_splits(const spc_shape& s);     // row splits per (instance, head)
 hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql, const void* kv,
                        const spc_kv_layout& kl, const int32_t* rows, const int32_t* row_count, int mode,
                        int layer_begin, int layer_end, float* out, void* ws, hipStream_t st);
+// the two halves of launch_attn: the split kernel (partials into ws) and the merge
+hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_layout& ql, const void* kv,
+                               const spc_kv_layout& kl, const int32_t* rows, const int32_t* row_count, int mode,
+                               int layer_begin, int layer_end, void* ws, hipStream_t st);
+hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end, const void* ws, float* out,
+                             hipStream_t st);
 
 }  // namespace spc

@@ -226,3 +226,24 @@ def test_log_domain_scoring_sizes_and_validation():
     need_mha = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(mha))
     assert lib.spc_group_max_topk_logits(ctypes.byref(mha), p, None, p, p, p, p, need_mha - 1,
                                          None) == L.SPC_ERR_WORKSPACE
+
+
+def test_attention_halves_validation():
+    """spc_attn_partial / spc_attn_merge reject bad arguments before launching (fake pointers unused)."""
+    lib = L.lib()
+    s = _shape(n_layers=4)
+    p = ctypes.c_void_p(256)
+    need = lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s))
+    assert need > 0
+    ql = L.SpcQLayout(32 * 128, 0, 128)
+    kl = L.SpcKvLayout(0, 0, 0, 256, 128)
+    assert lib.spc_attn_partial(ctypes.byref(s), p, ctypes.byref(ql), p, ctypes.byref(kl), None, None,
+                                L.SPC_ROWS_SLOTS, 0, 4, p, need, None) == L.SPC_ERR_INVALID_ARG      # rows
+    assert lib.spc_attn_partial(ctypes.byref(s), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                L.SPC_ROWS_SLOTS, 0, 4, p, need - 1, None) == L.SPC_ERR_WORKSPACE
+    assert lib.spc_attn_merge(ctypes.byref(s), 0, 4, None, need, p, None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_attn_merge(ctypes.byref(s), 0, 4, p, need - 1, p, None) == L.SPC_ERR_WORKSPACE
+    assert lib.spc_attn_merge(ctypes.byref(s), 2, 5, p, need, p, None) == L.SPC_ERR_INVALID_ARG    # layers
+    assert lib.spc_attn_merge(ctypes.byref(s), 0, 4, p, need, ctypes.c_void_p(264), None) == L.SPC_ERR_INVALID_ARG
+    big = _shape(max_len=1 << 20, budget=200000)                                  # > 1024 splits
+    assert lib.spc_attn_merge(ctypes.byref(big), 0, 1, p, 1 << 40, p, None) == L.SPC_ERR_UNSUPPORTED

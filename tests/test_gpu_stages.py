@@ -390,8 +390,18 @@ def test_copy_rejects_unpinned_host_memory():
 # ------------------------------------------------------------------------------ attention
 
 
-def _attn_case(p, lengths, mode, seed=21):
-    """Selections from the GPU scores + Top-K, K/V placed by plan + copy (SLOTS) or a full cache (GATHER)."""
+def _attend(shape, q, ql, kv, rows, counts, mode, NL, out, halves):
+    if not halves:
+        api.spc_sparse_decode_attn(shape, q, ql, kv, api.kv_layout(kv), rows, counts, mode, 0, NL, out)
+        return
+    ws = torch.empty(api.spc_workspace_size(api.SPC_CALL_ATTN, shape), dtype=torch.uint8, device="cuda")
+    api.spc_attn_partial(shape, q, ql, kv, api.kv_layout(kv), rows, counts, mode, 0, NL, ws)
+    api.spc_attn_merge(shape, 0, NL, ws, out)
+
+
+def _attn_case(p, lengths, mode, seed=21, halves=False):
+    """Selections from the GPU scores + Top-K, K/V placed by plan + copy (SLOTS) or a full cache (GATHER);
+    halves: the attention as spc_attn_partial + spc_attn_merge."""
     w = W.generate(p, device="cuda", seed=seed, steps=1, pin_host=True)
     shape, probs = _scores(p, w, lengths)
     sel_idx, sel_count = _topk_gpu(shape, probs, lengths)
@@ -408,10 +418,10 @@ def _attn_case(p, lengths, mode, seed=21):
         api.spc_elastic_update(shape, sel_idx, sel_count, slot_pos, bm, lp, ls, lc, w.host_kv,
                                api.kv_layout(w.host_kv), dev, api.kv_layout(dev), 0, NL,
                                flags=api.SPC_PLAN | api.SPC_COPY)
-        api.spc_sparse_decode_attn(shape, q, ql, dev, api.kv_layout(dev), slot_pos, None, mode, 0, NL, out)
+        _attend(shape, q, ql, dev, slot_pos, None, mode, NL, out, halves)
     else:
         full = w.host_kv.cuda()
-        api.spc_sparse_decode_attn(shape, q, ql, full, api.kv_layout(full), sel_idx, sel_count, mode, 0, NL, out)
+        _attend(shape, q, ql, full, sel_idx, sel_count, mode, NL, out, halves)
     torch.cuda.synchronize()
     return w, sel_lists(sel_idx, sel_count), out.cpu().numpy().astype(np.float64)
 
@@ -446,6 +456,14 @@ def test_attention_matches_oracle(name, p, lengths, mode):
     for b, n in enumerate(lengths):
         if n == 0:
             assert np.all(got[b] == 0)
+
+
+@pytest.mark.parametrize("name,p,lengths,mode", [ATTN_CASES[i] for i in (0, 1, 2, 3)],
+                         ids=[ATTN_CASES[i][0] for i in (0, 1, 2, 3)])
+def test_partial_then_merge_equals_the_whole_call(name, p, lengths, mode):
+    _, _, whole = _attn_case(p, lengths, mode)
+    _, _, halves = _attn_case(p, lengths, mode, halves=True)
+    np.testing.assert_array_equal(halves, whole)
 
 
 def test_full_budget_reproduces_dense_attention():
