@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--lag", type=int, default=0, choices=(0, 1),
                     help="1: the pipelined loop (the step attends over the previous step's selection while the "
                          "next one loads)")
+    ap.add_argument("--mla-literal", action="store_true",
+                    help="MLA: the literal form (each head expands its newly loaded rows into its own K/V slots) "
+                         "instead of the absorbed one")
     ap.add_argument("--weights-gb", type=float, default=16.0,
                     help="target-model weights counted against --hbm-gb (8B parameters in bf16)")
     ap.add_argument("--t0", type=int, default=None,
@@ -203,7 +206,7 @@ def main():
     torch.cuda.set_device(0)
     p = W.PRESETS[args.config]
     if p.kind == "mla":
-        result = bench_mla(args, p, torch, W)
+        result = bench_mla_literal(args, p, torch, W) if args.mla_literal else bench_mla(args, p, torch, W)
     elif args.lag == 1:
         result = bench_lag1(args, p, torch, W)
     else:
@@ -585,6 +588,102 @@ def bench_mla(args, p, torch, W):
     })
     if args.calibrate_copy:
         calibration_copies(torch)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_mla(p, w, Wm, args.cpu_seconds)
+    return result
+
+
+def bench_mla_literal(args, p, torch, W):
+    """The MLA step in the literal form: per-head K/V slots, only the rows a head newly loads
+    expanded (MFMA), attention over the slots; the absorbed step is timed beside it."""
+    from speculative_kv_sparsity_amd import api
+    from speculative_kv_sparsity_amd.driver import MlaDecoder, MlaLiteralDecoder, StageTimer
+
+    K_, Wm = args.steps, args.warmup
+    total = Wm + 2 * K_
+    w = W.generate(p, device="cuda", seed=args.seed, steps=total)
+    dec = MlaLiteralDecoder(p, w.latent, w.w_uk, w.w_uv)
+    lens = torch.as_tensor(w.lengths, device="cuda")
+    qn, qr = w.q_nope.contiguous(), w.q_rope.contiguous()
+    torch.cuda.synchronize()
+    for t in range(Wm):
+        dec.step(qn[t], qr[t], lens[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(dec.main)
+    for t in range(Wm, Wm + K_):
+        dec.step(qn[t], qr[t], lens[t])
+    e1.record(dec.main)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / K_
+
+    names = ("absorb", "scores", "topk", "plan", "expand", "attn", "end")
+    stage = {k: [] for k in names[:-1]}
+    loaded, sel_rows = [], []
+    for t in range(Wm + K_, total):
+        tm = StageTimer()
+        dec.step(qn[t], qr[t], lens[t], timer=tm)
+        torch.cuda.synchronize()
+        for a, z in zip(names[:-1], names[1:]):
+            stage[a].append(tm.ms(a, z))
+        loaded.append(int(dec.load_count.sum().item()))
+        sel_rows.append(int(dec.sel_count.sum().item()))
+    avg = {k: float(np.mean(v)) for k, v in stage.items()}
+
+    tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
+    R = args.iso_reps
+    xs = dec.exp_shape
+    iso_ms = {
+        "expand": iso(torch, lambda st: dec.expand(tq, tr, st), R),
+        "attn": iso(torch, lambda st: dec.attend(st), R),
+        "attn_partial": iso(torch, lambda st: api.spc_attn_partial(
+            xs, dec.q_exp, dec.exp_q_l, dec.kv_exp, dec.exp_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, 0, 1,
+            dec.ws_exp_attn, stream=st), R),
+    }
+    # the absorbed step on the same inputs, for comparison
+    ab = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+    for t in range(Wm):
+        ab.step(qn[t], qr[t], lens[t])
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(ab.main)
+    for t in range(Wm, Wm + K_):
+        ab.step(qn[t], qr[t], lens[t])
+    a1.record(ab.main)
+    torch.cuda.synchronize()
+    absorbed_ms = a0.elapsed_time(a1) / K_
+
+    B, H, L = p.batch, p.n_q_heads, p.max_len
+    sel = float(np.mean(sel_rows))
+    rows_new = float(np.mean(loaded))
+    dn, dr, dv, C = p.nope_dim, p.rope_dim, w.w_uv.shape[1], p.latent_dim
+    row_exp = (dn + dr + dv) * p.elem_bytes                       # one expanded K||V slot row
+    kv_bytes = sel * row_exp                                       # every selected slot read once
+    exp_flop = 2.0 * rows_new * C * (dn + dv)                      # K and V up-projection of the new rows
+    exp_bytes = rows_new * (2 * (C + dr) * p.elem_bytes + row_exp) + 2 * H * dn * C * p.elem_bytes
+    config = {"workload": "mla_32k, literal expansion: " + WORKLOADS["mla_32k"] if p.name == "mla_32k" else p.name,
+              "batch": B, "layers": 1, "q_heads": H, "latent_dim": C, "rope_dim": dr, "nope_dim": dn,
+              "cached_tokens": L, "kv_budget": p.budget, "form": "literal (per-head expanded K/V slots)",
+              "parallelism": "single GPU"}
+    result = _header(args, p, ms_per_step, config)
+    result.update({
+        "roofline": roof("hbm", kv_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
+                         "attn_split_kernel<bf16, 192, 128> (the dominant kernel: every head over its expanded "
+                         "slots, timed alone through spc_attn_partial)", 1),
+        "roofline_attn_call": roof("hbm", kv_bytes + B * H * dv * 4, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
+                                   "attn_split_kernel + attn_combine_kernel (the whole stage-4 call)", 1),
+        "roofline_expand": roof("mfma", exp_flop, iso_ms["expand"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+                                "mla_expand_kernel (the newly loaded rows of every head up-projected to K and V "
+                                "on bf16 MFMA)", 1),
+        "roofline_expand_hbm": roof("hbm", exp_bytes, iso_ms["expand"], HBM_PEAK_GBS, "GB/s",
+                                    "mla_expand_kernel (latent rows read by both halves + slot rows written + "
+                                    "W_UK and W_UV)", 1),
+        "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
+        "absorbed_form": {"ms_per_step": round(absorbed_ms, 4), "steps_per_s": round(1e3 / absorbed_ms, 2)},
+        "elastic": {"rows_selected_per_step": sel, "rows_expanded_per_step": rows_new,
+                    "expanded_fraction": round(rows_new / sel, 4) if sel else None, "host_link_bytes_per_step": 0},
+    })
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_mla(p, w, Wm, args.cpu_seconds)
     return result

@@ -384,6 +384,35 @@ int spc_mla_absorb_q(const spc_shape* s, int32_t nope_dim, const void* w_uk, con
 int spc_mla_out_proj(const spc_shape* s, int32_t dv, const void* w_uv, const float* o_lat, int32_t layer,
                      float* out, void* stream);
 
+/*
+ * MLA in the literal form (SpeContext blog section 5, last paragraph; paper summary
+ * section 4.3, MLA bullet: only the selected latent rows are expanded, 512 ->
+ * 128 x 128 K/V up-projection, before sparse attention): each head keeps its own
+ * K/V slots, and a step expands only the rows the head newly loads (the load
+ * lists of spc_elastic_update's plan for this shape), the rows it keeps stay
+ * expanded from earlier steps:
+ *   kv_exp[b][h][slot][0:128)   = bf16( W_UK[h] c_pos )      (nope part of the key)
+ *   kv_exp[b][h][slot][128:192) = r_pos                      (rotary dims, copied)
+ *   kv_exp[b][h][slot][192:320) = bf16( W_UV[h] c_pos )      (value)
+ * for every (pos, slot) = (load_pos[b][h][i], load_slot[b][h][i]), i < load_count[b][h];
+ * float32 accumulation on MFMA, rounded to nearest even.  With q_exp given,
+ * q_exp[b][h] = q_nope[b][h] || q_rope[b][h] (bf16, [B][H][192]) as well: the head's
+ * query against these keys.  Attention then runs with spc_sparse_decode_attn on
+ * the shape (n_kv_heads = n_groups = H, head_dim 192, v_dim 128) over kv_exp as
+ * slots (row stride 320 elements, V at offset 192); its output is the head's output
+ * directly (no output projection).
+ *   s          the MLA shape (head_dim 576, v_dim 512, n_kv_heads 1, n_groups = H, bf16,
+ *              batch <= 16); budget = slots per head
+ *   nope_dim, v_head_dim  128 each (the supported per-head dims)
+ *   latent     device bf16 [B][max_len][576];  w_uk, w_uv device bf16 [H][128][512]
+ *   load_pos, load_slot, load_count  device int32 [B][H][budget], [B][H] (plan output)
+ *   kv_exp     device bf16 [B][H][budget][320]: only the listed slots are written
+ *   q_nope, q_rope, q_exp  device bf16 [B][H][128], [B][H][64], [B][H][192], or all NULL
+ */
+int spc_mla_expand(const spc_shape* s, int32_t nope_dim, int32_t v_head_dim, const void* latent, const void* w_uk,
+                   const void* w_uv, const void* q_nope, const void* q_rope, const int32_t* load_pos,
+                   const int32_t* load_slot, const int32_t* load_count, void* kv_exp, void* q_exp, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

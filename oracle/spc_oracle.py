@@ -288,6 +288,34 @@ def sparse_decode_layer(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 # ----------------------------------------------------------------------------
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (8 significant bits), ties to even,
+    returned as float64.  For finite values in bf16's normal range: x = m 2^e with
+    0.5 <= |m| < 1 (frexp); the 8 significant bits are m 2^8 rounded half to even."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def mla_expand_rows(latent_rows: np.ndarray, rope_rows: np.ndarray, W_UK_h: np.ndarray, W_UV_h: np.ndarray,
+                    stored: str | None = None) -> Tuple[np.ndarray, np.ndarray]:
+    """One head's literal expansion of latent rows (SpeContext blog section 5, last
+    paragraph; paper summary section 4.3, MLA bullet: 512 -> 128 x 128 K/V up-projection):
+    K[j] = (W_UK_h c_j) || r_j and V[j] = W_UV_h c_j.
+
+    latent_rows: [n][C]; rope_rows: [n][R]; W_UK_h: [dn][C]; W_UV_h: [dv][C].
+    stored="bf16": the up-projected parts are rounded to bf16 (nearest, ties to even) as a
+    bf16 K/V cache holds them; the rotary dims are cache values already.  Returns (K, V).
+    """
+    Kn = np.asarray(latent_rows, dtype=np.float64) @ np.asarray(W_UK_h, dtype=np.float64).T
+    V = np.asarray(latent_rows, dtype=np.float64) @ np.asarray(W_UV_h, dtype=np.float64).T
+    if stored == "bf16":
+        Kn, V = round_bf16(Kn), round_bf16(V)
+    elif stored is not None:
+        raise ValueError(stored)
+    return np.concatenate([Kn, np.asarray(rope_rows, dtype=np.float64)], axis=1), V
+
+
 def mla_expand_keys(latent: np.ndarray, rope: np.ndarray, W_UK: np.ndarray) -> np.ndarray:
     """Per-head keys of the given latent rows: K_h[j] = (W_UK[h] c_j) || r_j.
 
@@ -328,19 +356,19 @@ def mla_retrieval_scores(q_nope: np.ndarray, q_rope: np.ndarray, latent: np.ndar
 
 def mla_sparse_attention(q_nope: np.ndarray, q_rope: np.ndarray, latent: np.ndarray,
                          rope: np.ndarray, W_UK: np.ndarray, W_UV: np.ndarray,
-                         positions: Sequence[int], h: int, scale: float) -> np.ndarray:
+                         positions: Sequence[int], h: int, scale: float,
+                         stored: str | None = None) -> np.ndarray:
     """One MLA head over its selected latent rows, expanding ONLY those rows.
 
-    K_h[j] = (W_UK[h] c_j) || r_j,  V_h[j] = W_UV[h] c_j, for j in positions;
+    K_h[j] = (W_UK[h] c_j) || r_j,  V_h[j] = W_UV[h] c_j, for j in positions
+    (mla_expand_rows; stored="bf16" rounds them as a bf16 cache of expanded rows holds them);
     then out = softmax(scale * q . K_h[j]) weighted sum of V_h[j].
     q_nope: [dn]; q_rope: [R]; latent: [L][C]; rope: [L][R]; W_UK, W_UV: [H][d][C].
     """
     pos = np.asarray(list(positions), dtype=np.int64)
     if pos.size == 0:
         return np.zeros(W_UV.shape[1], dtype=np.float64)
-    c = latent[pos]
-    K = np.concatenate([c @ W_UK[h].T, rope[pos]], axis=1)
-    V = c @ W_UV[h].T
+    K, V = mla_expand_rows(latent[pos], rope[pos], W_UK[h], W_UV[h], stored)
     q = np.concatenate([q_nope, q_rope])
     w = softmax((K @ q) * scale)
     return w @ V

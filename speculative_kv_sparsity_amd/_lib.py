@@ -86,6 +86,7 @@ SIGNATURES = {
     "spc_attn_partial": (_I, [ctypes.POINTER(SpcShape), _P, ctypes.POINTER(SpcQLayout), _P,
                               ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _SZ, _P]),
     "spc_attn_merge": (_I, [ctypes.POINTER(SpcShape), _I32, _I32, _P, _SZ, _P, _P]),
+    "spc_mla_expand": (_I, [ctypes.POINTER(SpcShape), _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "spc_mla_absorb_q": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P, _P, _P]),
     "spc_mla_out_proj": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _I32, _P, _P]),
     "spc_elastic_plan_lag1": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),

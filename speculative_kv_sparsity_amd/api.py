@@ -22,7 +22,8 @@ __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version",
            "SPC_CALL_SCORES", "SPC_CALL_TOPK", "SPC_CALL_ATTN", "SPC_CALL_FRONT", "spc_mla_absorb_q",
            "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds",
            "spc_elastic_plan_lag1", "spc_retrieval_logits", "spc_group_max_topk_logits", "spc_score_tile",
-           "spc_tile_stats_size", "tile_stats_shape", "spc_attn_partial", "spc_attn_merge"]
+           "spc_tile_stats_size", "tile_stats_shape", "spc_attn_partial", "spc_attn_merge",
+           "spc_mla_expand"]
 
 
 class SpcError(RuntimeError):
@@ -192,6 +193,20 @@ def spc_attn_merge(shape: SpcShape, layer_begin: int, layer_end: int, ws, out, s
     _dev(ws, "ws")
     _check(L.lib().spc_attn_merge(ctypes.byref(shape), int(layer_begin), int(layer_end), _ptr(ws),
                                   ws.numel() * ws.element_size(), _ptr(out), _stream(stream)))
+
+
+def spc_mla_expand(shape: SpcShape, nope_dim: int, v_head_dim: int, latent, w_uk, w_uv, load_pos, load_slot,
+                   load_count, kv_exp, q_nope=None, q_rope=None, q_exp=None, stream=None) -> None:
+    """Literal MLA: the newly loaded rows of every head expanded into its K/V slots (and the joined query)."""
+    for t, n in ((latent, "latent"), (w_uk, "w_uk"), (w_uv, "w_uv"), (load_pos, "load_pos"), (load_slot, "load_slot"),
+                 (load_count, "load_count"), (kv_exp, "kv_exp")):
+        _dev(t, n)
+    for t, n in ((q_nope, "q_nope"), (q_rope, "q_rope"), (q_exp, "q_exp")):
+        if t is not None:
+            _dev(t, n)
+    _check(L.lib().spc_mla_expand(ctypes.byref(shape), int(nope_dim), int(v_head_dim), _ptr(latent), _ptr(w_uk),
+                                  _ptr(w_uv), _ptr(q_nope), _ptr(q_rope), _ptr(load_pos), _ptr(load_slot),
+                                  _ptr(load_count), _ptr(kv_exp), _ptr(q_exp), _stream(stream)))
 
 
 def spc_mla_absorb_q(shape: SpcShape, nope_dim: int, w_uk, q_nope, q_rope, q_abs, stream=None) -> None:

@@ -439,4 +439,30 @@ int spc_elastic_plan_lag1(const spc_shape* s, int32_t sel_budget, const int32_t*
   return e == hipSuccess ? ok() : hip_fail(e, "pipelined elastic plan launch");
 }
 
+int spc_mla_expand(const spc_shape* s, int32_t nope_dim, int32_t v_head_dim, const void* latent, const void* w_uk,
+                   const void* w_uv, const void* q_nope, const void* q_rope, const int32_t* load_pos,
+                   const int32_t* load_slot, const int32_t* load_count, void* kv_exp, void* q_exp, void* stream) {
+  if (int e = check_mla(s)) return e;
+  if (nope_dim != spc::kMlaExpandDims || v_head_dim != spc::kMlaExpandDims)
+    return fail(SPC_ERR_UNSUPPORTED, "literal expansion supports nope and value head dims of %d (got %d, %d)",
+                spc::kMlaExpandDims, nope_dim, v_head_dim);
+  if (s->n_groups != s->n_q_heads)
+    return fail(SPC_ERR_INVALID_ARG, "literal expansion needs one selection group per head");
+  if (!latent || !w_uk || !w_uv || !load_pos || !load_slot || !load_count || !kv_exp)
+    return fail(SPC_ERR_INVALID_ARG, "NULL latent, weights, load lists or kv_exp");
+  const bool with_q = q_exp != nullptr;
+  if (with_q != (q_nope != nullptr) || with_q != (q_rope != nullptr))
+    return fail(SPC_ERR_INVALID_ARG, "q_nope, q_rope and q_exp must be all given or all NULL");
+  if (!aligned16(latent) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv_exp))
+    return fail(SPC_ERR_INVALID_ARG, "latent, weights and kv_exp must be 16-byte aligned");
+  if (!aligned4(load_pos) || !aligned4(load_slot) || !aligned4(load_count))
+    return fail(SPC_ERR_INVALID_ARG, "misaligned load lists");
+  if (with_q && ((reinterpret_cast<uintptr_t>(q_nope) | reinterpret_cast<uintptr_t>(q_rope) |
+                  reinterpret_cast<uintptr_t>(q_exp)) & 1u))
+    return fail(SPC_ERR_INVALID_ARG, "misaligned bf16 query buffers");
+  const hipError_t e = spc::launch_mla_expand(*s, latent, w_uk, w_uv, q_nope, q_rope, load_pos, load_slot,
+                                              load_count, kv_exp, q_exp, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "MLA literal expansion launch");
+}
+
 }  // extern "C"

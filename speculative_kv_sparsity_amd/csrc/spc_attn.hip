@@ -76,8 +76,8 @@ __device__ __forceinline__ int32_t split_row(const int32_t* rl, int idx, int cnt
   return mode == SPC_ROWS_SLOTS ? (v >= 0 ? idx : -1) : (v >= 0 && v < max_rows ? v : -1);
 }
 
-// NI: K iterations of 8 rows per wave (rows per wave = 8 NI).
-template <int DT, int D, int GQC, int NI>
+// NI: K iterations of 8 rows per wave (rows per wave = 8 NI).  D: key width, DV: value width.
+template <int DT, int D, int DV, int GQC, int NI>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
@@ -87,10 +87,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   constexpr int CPLK = D * EB / 16 / 8;              // K: 16-byte chunks per lane
   constexpr int RPW = 8 * NI;                        // rows per wave
   constexpr int RPS = 4 * RPW;                       // rows per split
-  constexpr int EPL = D / 32;                        // V: dims per lane
+  constexpr int EPL = DV / 32;                       // V: dims per lane
   constexpr int VB = EPL * EB;                       // V: bytes per lane and row
   constexpr int NV = RPW / 2;                        // V: rows per lane
-  static_assert(D * EB % 128 == 0 && D % 32 == 0, "row layout");
+  static_assert(D * EB % 128 == 0 && DV % 32 == 0, "row layout");
 
   const int split = blockIdx.x;
   const int hcix = blockIdx.z;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   __shared__ int32_t sRow[RPS];
   __shared__ float sW[4][RPW][GQC];
   __shared__ float s_m[4][GQC], s_l[4][GQC];
-  __shared__ float red[4][GQC][D];
+  __shared__ float red[4][GQC][DV];
 
   const int32_t* rl = rows + ((size_t)b * n_groups + r) * K;
   int cnt = K;
@@ -233,9 +233,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   }
   __syncthreads();
   const size_t pbase = ((size_t)inst * nhc + hcix) * nsplit + split;
-  for (int t = tid; t < GQC * D; t += kThreads) {
-    const int h = t / D, d = t - (t / D) * D;
-    part_o[(pbase * GQC + h) * D + d] = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
+  for (int t = tid; t < GQC * DV; t += kThreads) {
+    const int h = t / DV, d = t - (t / DV) * DV;
+    part_o[(pbase * GQC + h) * DV + d] = red[0][h][d] + red[1][h][d] + red[2][h][d] + red[3][h][d];
   }
   if (tid < GQC) {
     const int h = tid;
@@ -525,21 +525,21 @@ struct SplitArgs {
   int layer_begin, n_lay, nsplit, nhc, max_rows; float* part_o; float2* part_ml;
 };
 
-template <int DT, int D, int GQC, int NI>
+template <int DT, int D, int DV, int GQC, int NI>
 hipError_t launch_split(const spc_shape& s, dim3 grid, hipStream_t st, const SplitArgs& a) {
-  attn_split_kernel<DT, D, GQC, NI><<<grid, kThreads, 0, st>>>(
+  attn_split_kernel<DT, D, DV, GQC, NI><<<grid, kThreads, 0, st>>>(
       a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
       a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
   return hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int D, int DV = D>
 hipError_t launch_split_gqc(int gqc, const spc_shape& s, dim3 grid, hipStream_t st, const SplitArgs& a) {
   switch (gqc) {
-    case 1: return launch_split<DT, D, 1, 4>(s, grid, st, a);
-    case 2: return launch_split<DT, D, 2, 4>(s, grid, st, a);
-    case 4: return launch_split<DT, D, 4, 4>(s, grid, st, a);
-    case 8: return launch_split<DT, D, 8, 2>(s, grid, st, a);
+    case 1: return launch_split<DT, D, DV, 1, 4>(s, grid, st, a);
+    case 2: return launch_split<DT, D, DV, 2, 4>(s, grid, st, a);
+    case 4: return launch_split<DT, D, DV, 4, 4>(s, grid, st, a);
+    case 8: return launch_split<DT, D, DV, 8, 2>(s, grid, st, a);
     default: return hipErrorInvalidValue;
   }
 }
@@ -549,6 +549,7 @@ hipError_t launch_split_gqc(int gqc, const spc_shape& s, dim3 grid, hipStream_t 
 bool attn_supported(const spc_shape& s) {
   if (s.dtype == SPC_F32) return s.head_dim == 128 && s.v_dim == 128;
   if (s.head_dim == 576) return s.v_dim == 512 && head_chunk(s) == 1;   // MLA latent: one head per group
+  if (s.head_dim == 192) return s.v_dim == 128;   // MLA rows expanded per head: nope 128 + rope 64 keys
   return (s.head_dim == 128 && s.v_dim == 128) || (s.head_dim == 64 && s.v_dim == 64);
 }
 
@@ -613,6 +614,8 @@ hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_la
     e = launch_split_gqc<SPC_BF16, 128>(gqc, s, grid, st, a);
   } else if (s.head_dim == 64) {
     e = launch_split_gqc<SPC_BF16, 64>(gqc, s, grid, st, a);
+  } else if (s.head_dim == 192) {
+    e = launch_split_gqc<SPC_BF16, 192, 128>(gqc, s, grid, st, a);
   } else if (s.head_dim == 576 && gqc == 1) {
     if (latent_tiles(s) == kLatentTilesLarge)
       attn_split_latent_kernel<576, 512, kLatentTilesLarge><<<grid, kThreads, 0, st>>>(

@@ -36,6 +36,11 @@ hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void*
                              float* q_abs, hipStream_t st);
 hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
                              float* logits, float2* stats, hipStream_t st);
+constexpr int kMlaExpandDims = 128;   // per-head nope / value dims of the literal expansion
+hipError_t launch_mla_expand(const spc_shape& s, const void* latent, const void* w_uk, const void* w_uv,
+                             const void* q_nope, const void* q_rope, const int32_t* load_pos,
+                             const int32_t* load_slot, const int32_t* load_count, void* kv_exp, void* q_exp,
+                             hipStream_t st);
 hipError_t launch_mla_out_proj(int B, int H, int dv, const void* w_uv, const float* o_lat, int64_t lat_b_stride,
                                float* out, hipStream_t st);
 

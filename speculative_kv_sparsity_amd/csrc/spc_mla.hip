@@ -18,6 +18,11 @@
 //   the query while the latent rows are bf16 already.  Per-tile (max, sum exp)
 //   partials feed the shared normalize kernel of the scores stage.
 // mla_out_proj_kernel  out[b][h] = W_UV^h o_lat[b][h] (float32 result).
+// mla_expand_kernel    the literal form instead of the absorbed one: the rows a
+//   head newly loads are expanded into that head's K/V slots, K = W_UK^h c || r
+//   and V = W_UV^h c in bf16 (dense [128 x 512] x [512 x rows] on MFMA), and the
+//   head's query is joined as q_nope || q_rope; attention then runs over the
+//   slots like any other head.
 #include "spc_common.h"
 #include "spc_launch.h"
 
@@ -294,6 +299,167 @@ hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void*
   return hipGetLastError();
 }
 
+// One workgroup per (head, half): half 0 expands K (W_UK, and copies the rotary
+// dims), half 1 expands V (W_UV).  The half's weights W^h [128 x 512] sit in LDS
+// (rows padded to 1040 bytes: the 16 rows of an MFMA fragment fall on distinct
+// banks).  The head's newly loaded rows of every sequence are taken 256 at a
+// time, 64 per wave in four blocks of 16; each lane loads its row's latent chunk
+// of a k-step straight into the MFMA B fragment, seven steps ahead of the 32
+// MFMAs that use it.  C^T [dims x rows] = W [dims x 512] x
+// latent^T [512 x rows]: a lane ends with 4 consecutive dims of one row, rounded
+// to bf16 and stored as 8 bytes.  The two halves of a head get block ids 8
+// apart, which puts them on the same XCD, where the second finds the rows in L2.
+constexpr int kExpDims = 128;                     // nope and value dims per head
+constexpr int kExpWRow = kMlaLatent + 8;          // padded LDS row of W (elements)
+constexpr int kExpThreads = 256;
+constexpr int kExpOut = kExpDims + kMlaRope + kExpDims;   // slot row: K nope || rope || V
+constexpr int kExpKSteps = kMlaLatent / 32;
+constexpr int kExpAhead = 7;                      // k-steps of latent fragments in flight
+
+__global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
+    const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv,
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope, const int32_t* __restrict__ load_pos,
+    const int32_t* __restrict__ load_slot, const int32_t* __restrict__ load_count, uint16_t* __restrict__ kv,
+    uint16_t* __restrict__ q_exp, int B, int H, int max_len, int K) {
+  __shared__ __align__(16) uint16_t sw[kExpDims * kExpWRow];
+  __shared__ int s_pref[kMlaMaxBatch + 1];
+  const int id = blockIdx.x;
+  const int grp = id >> 4, in = id & 15;
+  const int half = in >> 3, h = grp * 8 + (in & 7);
+  if (h >= H) return;
+  const int tid = threadIdx.x;
+  const uint16_t* w = (half ? w_uv : w_uk) + (size_t)h * kExpDims * kMlaLatent;
+  // the half's weights into LDS, 16 loads per thread in flight at a time
+  constexpr int kWChunks = kExpDims * kMlaLatent / 8;
+  constexpr int kWPer = kWChunks / kExpThreads;
+  constexpr int kWBatch = 16;
+  static_assert(kWChunks % kExpThreads == 0 && kWPer % kWBatch == 0, "weight staging split");
+#pragma unroll
+  for (int u0 = 0; u0 < kWPer; u0 += kWBatch) {
+    uint4 t[kWBatch];
+#pragma unroll
+    for (int u = 0; u < kWBatch; ++u) {
+      const int c = tid + (u0 + u) * kExpThreads;
+      const int r = c / (kMlaLatent / 8), ch = c - r * (kMlaLatent / 8);
+      t[u] = *reinterpret_cast<const uint4*>(w + (size_t)r * kMlaLatent + 8 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < kWBatch; ++u) {
+      const int c = tid + (u0 + u) * kExpThreads;
+      const int r = c / (kMlaLatent / 8), ch = c - r * (kMlaLatent / 8);
+      *reinterpret_cast<uint4*>(&sw[r * kExpWRow + 8 * ch]) = t[u];
+    }
+  }
+  if (tid == 0) {
+    int acc = 0;
+    for (int b = 0; b < B; ++b) {
+      s_pref[b] = acc;
+      const int c = load_count[(size_t)b * H + h];
+      acc += c < 0 ? 0 : (c > K ? K : c);
+    }
+    s_pref[B] = acc;
+  }
+  if (half == 0 && q_exp != nullptr) {             // the head's query against the expanded keys
+    for (int i = tid; i < B * (kExpDims + kMlaRope); i += kExpThreads) {
+      const int b = i / (kExpDims + kMlaRope), d = i - b * (kExpDims + kMlaRope);
+      q_exp[((size_t)b * H + h) * (kExpDims + kMlaRope) + d] =
+          d < kExpDims ? q_nope[((size_t)b * H + h) * kExpDims + d]
+                       : q_rope[((size_t)b * H + h) * kMlaRope + (d - kExpDims)];
+    }
+  }
+  __syncthreads();
+  const int R = s_pref[B];
+  const int lane = tid & 63, wid = tid >> 6, col = lane & 15, kc = lane >> 4;
+  const int off = half ? kExpDims + kMlaRope : 0;
+  int pref[kMlaMaxBatch];
+#pragma unroll
+  for (int j = 0; j < kMlaMaxBatch; ++j) pref[j] = j < B ? s_pref[j] : R;
+  // the load-list entries of this lane's four rows of a pass, found without a data-dependent loop
+  // and loaded together; a pass's entries are loaded during the previous pass's MFMAs
+  int npos[4], nslot[4], nb[4];
+  auto list_load = [&](int r0) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int rr = r0 + 64 * wid + 16 * rb + col;
+      int b = 0;
+#pragma unroll
+      for (int j = 1; j < kMlaMaxBatch; ++j) b += rr >= pref[j];
+      const bool in = rr < R;
+      const size_t li = in ? ((size_t)b * H + h) * K + (rr - pref[b]) : 0;
+      nb[rb] = in ? b : -1;
+      npos[rb] = load_pos[li];
+      nslot[rb] = load_slot[li];
+    }
+  };
+  list_load(0);
+  for (int r0 = 0; r0 < R; r0 += 4 * 64) {
+    if (r0 + 64 * wid >= R) break;                 // wave-uniform: no rows left for this wave
+    const uint16_t* rowp[4];
+    uint16_t* dst[4];
+    bool ok[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int b = nb[rb], pos = npos[rb], slot = nslot[rb];
+      ok[rb] = b >= 0 && pos >= 0 && pos < max_len && slot >= 0 && slot < K;
+      rowp[rb] = ok[rb] ? lat + ((size_t)b * max_len + pos) * (kMlaLatent + kMlaRope) : lat;
+      dst[rb] = ok[rb] ? kv + (((size_t)b * H + h) * K + slot) * kExpOut : kv;
+    }
+    f32x4_t acc[4][kExpDims / 16];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int db = 0; db < kExpDims / 16; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the gathered latent fragments of kExpAhead k-steps are in flight ahead of the MFMAs that use
+    // them (a ring of registers; a gather from a random row costs far more than one step's MFMAs)
+    bf16x8_t ring[kExpAhead + 1][4];
+    auto load_b = [&](int s, bf16x8_t* bf) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (ok[rb]) {
+          bf[rb] = *reinterpret_cast<const bf16x8_t*>(rowp[rb] + 32 * s + 8 * kc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bf[rb][e] = (__bf16)0.f;
+        }
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < kExpAhead; ++s) load_b(s, ring[s]);
+    if (r0 + 4 * 64 < R) list_load(r0 + 4 * 64);   // the next pass's entries, behind this pass's MFMAs
+#pragma unroll
+    for (int s = 0; s < kExpKSteps; ++s) {
+      if (s + kExpAhead < kExpKSteps) load_b(s + kExpAhead, ring[(s + kExpAhead) % (kExpAhead + 1)]);
+      const bf16x8_t* bcur = ring[s % (kExpAhead + 1)];
+      bf16x8_t a[kExpDims / 16];
+#pragma unroll
+      for (int db = 0; db < kExpDims / 16; ++db)
+        a[db] = *reinterpret_cast<const bf16x8_t*>(&sw[(16 * db + col) * kExpWRow + 32 * s + 8 * kc]);
+#pragma unroll
+      for (int db = 0; db < kExpDims / 16; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[db], bcur[rb], acc[rb][db], 0, 0, 0);
+    }
+    // lane (col, kc): dims 16 db + 4 kc .. + 3 of row `col` of each block
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (!ok[rb]) continue;
+#pragma unroll
+      for (int db = 0; db < kExpDims / 16; ++db) {
+        const uint2 v = make_uint2(bf16_bits(acc[rb][db][0]) | (bf16_bits(acc[rb][db][1]) << 16),
+                                   bf16_bits(acc[rb][db][2]) | (bf16_bits(acc[rb][db][3]) << 16));
+        *reinterpret_cast<uint2*>(dst[rb] + off + 16 * db + 4 * kc) = v;
+      }
+      if (half == 0) {                             // the rotary dims of the row, copied as they are
+        *reinterpret_cast<uint4*>(dst[rb] + kExpDims + 8 * kc) =
+            *reinterpret_cast<const uint4*>(rowp[rb] + kMlaLatent + 8 * kc);
+        *reinterpret_cast<uint4*>(dst[rb] + kExpDims + 8 * (kc + 4)) =
+            *reinterpret_cast<const uint4*>(rowp[rb] + kMlaLatent + 8 * (kc + 4));
+      }
+    }
+  }
+}
+
 hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
                              float* logits, float2* stats, hipStream_t st) {
   const int ntiles = (s.max_len + kMlaScoreTile - 1) / kMlaScoreTile;
@@ -302,6 +468,18 @@ hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void*
   mla_scores_kernel<<<dim3(ngrp * 8 * nhg, s.batch), kScoreThreads, 0, st>>>(
       q_abs, static_cast<const uint16_t*>(latent), lengths, logits, stats, s.n_q_heads, s.max_len, ntiles, nhg,
       s.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_expand(const spc_shape& s, const void* latent, const void* w_uk, const void* w_uv,
+                             const void* q_nope, const void* q_rope, const int32_t* load_pos,
+                             const int32_t* load_slot, const int32_t* load_count, void* kv_exp, void* q_exp,
+                             hipStream_t st) {
+  const int ngrp = (s.n_q_heads + 7) / 8;
+  mla_expand_kernel<<<dim3(ngrp * 16), kExpThreads, 0, st>>>(
+      static_cast<const uint16_t*>(latent), static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
+      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), load_pos, load_slot, load_count,
+      static_cast<uint16_t*>(kv_exp), static_cast<uint16_t*>(q_exp), s.batch, s.n_q_heads, s.max_len, s.budget);
   return hipGetLastError();
 }
 

@@ -428,3 +428,61 @@ class MlaDecoder:
         api.spc_sparse_decode_attn(self.shape, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx,
                                    self.sel_count, api.SPC_ROWS_GATHER, 0, 1, self.o_lat, ws=self.ws_attn,
                                    stream=self.main if stream is None else stream)
+
+
+class MlaLiteralDecoder(MlaDecoder):
+    """The MLA step in the literal form: each head keeps its own expanded K/V slots.
+
+    Per step: absorbed query -> head-level scores over the latent cache -> per-head Top-K ->
+    elastic plan -> the rows each head newly loads expanded into its slots, K = W_UK c || r and
+    V = W_UV c in bf16 (spc_mla_expand, MFMA), with the head's query joined as q_nope || q_rope
+    -> attention of every head over its slots (head_dim 192, v_dim 128).  Rows a head keeps are
+    not expanded again.  The output is the heads' attention output itself, [B][1][H][dv].
+    """
+
+    def __init__(self, p: Preset, latent: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor):
+        super().__init__(p, latent, w_uk, w_uv)
+        B, H, L, K = p.batch, p.n_q_heads, p.max_len, p.budget
+        dn, R, dv = p.nope_dim, p.rope_dim, w_uv.shape[1]
+        dev = latent.device
+        self.row = dn + R + dv
+        self.kv_exp = torch.zeros((B, H, K, self.row), dtype=torch.bfloat16, device=dev)
+        self.q_exp = torch.empty((B, H, dn + R), dtype=torch.bfloat16, device=dev)
+        self.exp_shape = api.make_shape(B, H, H, H, dn + R, dv, L, K, 1, p.dtype, p.scale)
+        self.exp_l = api.SpcKvLayout(H * K * self.row, 0, K * self.row, self.row, dn + R)
+        self.exp_q_l = api.q_layout(H * (dn + R), 0, dn + R)
+        self.out = torch.zeros((B, 1, H, dv), dtype=torch.float32, device=dev)
+        self.ws_exp_attn = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_ATTN, self.exp_shape)),
+                                       dtype=torch.uint8, device=dev)
+
+    def step(self, q_nope: torch.Tensor, q_rope: torch.Tensor, lengths: torch.Tensor,
+             timer: Optional["StageTimer"] = None) -> None:
+        """q_nope: device [B][H][dn]; q_rope: device [B][H][R]; lengths: device int32 [B].  Asynchronous."""
+        mark = timer.mark if timer is not None else (lambda name, stream: None)
+        s, st = self.shape, self.main
+        mark("absorb", st)
+        api.spc_mla_absorb_q(s, self.p.nope_dim, self.w_uk, q_nope, q_rope, self.q_abs, stream=st)
+        mark("scores", st)
+        api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.tile_stats, stream=st)
+        mark("topk", st)
+        api.spc_group_max_topk_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk,
+                                      stream=st)
+        mark("plan", st)
+        api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
+                               self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)
+        mark("expand", st)
+        self.expand(q_nope, q_rope, st)
+        mark("attn", st)
+        self.attend(st)
+        mark("end", st)
+
+    def expand(self, q_nope: torch.Tensor, q_rope: torch.Tensor, stream=None) -> None:
+        api.spc_mla_expand(self.shape, self.p.nope_dim, self.w_uv.shape[1], self.latent, self.w_uk, self.w_uv,
+                           self.load_pos, self.load_slot, self.load_count, self.kv_exp, q_nope, q_rope, self.q_exp,
+                           stream=self.main if stream is None else stream)
+
+    def attend(self, stream=None) -> None:
+        """Every head over its expanded slots (slot x attended iff it holds a position)."""
+        api.spc_sparse_decode_attn(self.exp_shape, self.q_exp, self.exp_q_l, self.kv_exp, self.exp_l, self.slot_pos,
+                                   None, api.SPC_ROWS_SLOTS, 0, 1, self.out, ws=self.ws_exp_attn,
+                                   stream=self.main if stream is None else stream)

@@ -310,6 +310,52 @@ def check_mla_literal_vs_absorbed(mla_sparse_attention, mla_retrieval_scores):
         np.testing.assert_allclose(probs[(0, h)], ref, rtol=1e-10, atol=1e-14)
 
 
+def check_round_bf16(round_bf16, to_bf16_bits):
+    """Nearest bf16 with ties to even (8 significant bits): halfway cases by hand, and agreement
+    with an independent bit-level rounding on float32 inputs (where rounding through float32 is
+    exact, so the two must agree)."""
+    u = 2.0 ** -7                                            # bf16 spacing on [1, 2)
+    cases = [(1.0 + u / 2, 1.0),                             # halfway, even below
+             (1.0 + 3 * u / 2, 1.0 + 2 * u),                 # halfway, even above
+             (1.0 + u / 2 + 2.0 ** -20, 1.0 + u),            # just above halfway
+             (-(1.0 + u / 2), -1.0), (3.0, 3.0), (0.0, 0.0),
+             (255.0, 255.0), (257.0, 256.0), (259.0, 260.0),  # integers: 8 significant bits
+             (2.0 ** -30 * (1 + 3 * u / 2), 2.0 ** -30 * (1 + 2 * u))]
+    for x, want in cases:
+        assert float(round_bf16(np.float64(x))) == want, (x, float(round_bf16(np.float64(x))), want)
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = (to_bf16_bits(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64)), ref)
+
+
+def check_mla_expand_exact(mla_expand_rows):
+    """Integer latent rows and sparse integer weights: every up-projected value is an integer of
+    at most 8 significant bits, so the bf16-stored expansion is exact and equals a brute-force
+    integer sum; K takes W_UK, V takes W_UV, the rotary dims are copied."""
+    rng = np.random.default_rng(22)
+    n, C, dn, dv, R = 7, 64, 6, 5, 4
+    lat = rng.integers(-3, 4, (n, C))
+    rope = rng.integers(-9, 10, (n, R)) / 8.0
+    W_UK = np.zeros((dn, C), dtype=np.int64)
+    W_UV = np.zeros((dv, C), dtype=np.int64)
+    for W in (W_UK, W_UV):
+        for r in range(W.shape[0]):
+            cols = rng.choice(C, 5, replace=False)
+            W[r, cols] = rng.integers(-3, 4, 5)
+    K, V = mla_expand_rows(lat.astype(np.float64), rope, W_UK.astype(np.float64), W_UV.astype(np.float64), "bf16")
+    for j in range(n):
+        for r in range(dn):
+            assert K[j, r] == sum(int(lat[j, c]) * int(W_UK[r, c]) for c in range(C))
+        for r in range(dv):
+            assert V[j, r] == sum(int(lat[j, c]) * int(W_UV[r, c]) for c in range(C))
+        np.testing.assert_array_equal(K[j, dn:], rope[j])
+    # rounding applies to the projections only: a value needing 9 bits rounds to 8
+    K1, _ = mla_expand_rows(np.array([[257.0] + [0.0] * (C - 1)]), np.zeros((1, R)),
+                            np.eye(dn, C), np.eye(dv, C), "bf16")
+    assert K1[0, 0] == 256.0
+
+
 # ----------------------------------------------------------------------------- sizes
 
 def check_kv_cache_size(kv_cache_bytes):

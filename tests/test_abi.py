@@ -247,3 +247,27 @@ def test_attention_halves_validation():
     assert lib.spc_attn_merge(ctypes.byref(s), 0, 4, p, need, ctypes.c_void_p(264), None) == L.SPC_ERR_INVALID_ARG
     big = _shape(max_len=1 << 20, budget=200000)                                  # > 1024 splits
     assert lib.spc_attn_merge(ctypes.byref(big), 0, 1, p, 1 << 40, p, None) == L.SPC_ERR_UNSUPPORTED
+
+
+def test_mla_expand_validation():
+    """spc_mla_expand rejects what it does not support before launching (fake pointers unused)."""
+    lib = L.lib()
+    mla = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                 budget=2048, scale=192 ** -0.5)
+    p = ctypes.c_void_p(256)
+    args = [p] * 7                                   # latent, w_uk, w_uv, q_nope, q_rope, load_pos, load_slot
+    assert lib.spc_mla_expand(ctypes.byref(mla), 96, 128, *args, p, p, p, None) == L.SPC_ERR_UNSUPPORTED  # nope 96
+    assert lib.spc_mla_expand(ctypes.byref(mla), 128, 128, None, *args[1:], p, p, p, None) == L.SPC_ERR_INVALID_ARG
+    # the query triple is all or nothing
+    assert lib.spc_mla_expand(ctypes.byref(mla), 128, 128, p, p, p, None, p, p, p, p, p, p, None) \
+        == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_mla_expand(ctypes.byref(mla), 128, 128, ctypes.c_void_p(264), *args[1:], p, p, p, None) \
+        == L.SPC_ERR_INVALID_ARG                                                               # latent alignment
+    gqa = _shape()
+    assert lib.spc_mla_expand(ctypes.byref(gqa), 128, 128, *args, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
+    big = _shape(batch=17, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                 budget=2048)
+    assert lib.spc_mla_expand(ctypes.byref(big), 128, 128, *args, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
+    one_group = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=1, head_dim=576, v_dim=512,
+                       max_len=32768, budget=2048)
+    assert lib.spc_mla_expand(ctypes.byref(one_group), 128, 128, *args, p, p, p, None) == L.SPC_ERR_INVALID_ARG

@@ -179,3 +179,38 @@ def test_pins_catch_lag1_plan_mistakes():
     _fails(pins.check_plan_lag1_worked_example, frees_current)
     _fails(pins.check_plan_lag1_invariants, frees_current)
     _fails(pins.check_plan_lag1_reduces_to_lag0, attend_before_update, O.elastic_plan)
+
+
+def test_pins_catch_bf16_and_expansion_mistakes():
+    from oracle.front import to_bf16_bits
+
+    def half_up(x):                                   # ties away from zero instead of to even
+        m, e = np.frexp(np.asarray(x, dtype=np.float64))
+        return np.ldexp(np.sign(m) * np.floor(np.abs(m) * 256.0 + 0.5), e - 8)
+
+    def truncate(x):
+        m, e = np.frexp(np.asarray(x, dtype=np.float64))
+        return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+    def seven_bits(x):
+        m, e = np.frexp(np.asarray(x, dtype=np.float64))
+        return np.ldexp(np.rint(m * 128.0), e - 7)
+
+    _fails(pins.check_round_bf16, half_up, to_bf16_bits)
+    _fails(pins.check_round_bf16, truncate, to_bf16_bits)
+    _fails(pins.check_round_bf16, seven_bits, to_bf16_bits)
+
+    def swapped(lat, rope, W_UK_h, W_UV_h, stored=None):
+        return O.mla_expand_rows(lat, rope, W_UV_h[:W_UK_h.shape[0]] if W_UV_h.shape[0] >= W_UK_h.shape[0]
+                                 else np.resize(W_UV_h, W_UK_h.shape), W_UK_h[:W_UV_h.shape[0]], stored)
+
+    def transposed_rows(lat, rope, W_UK_h, W_UV_h, stored=None):
+        K, V = O.mla_expand_rows(lat, rope, W_UK_h, W_UV_h, stored)
+        return K, V[::-1]                                # rows of V misassigned
+
+    def no_rounding(lat, rope, W_UK_h, W_UV_h, stored=None):
+        return O.mla_expand_rows(lat, rope, W_UK_h, W_UV_h, None)
+
+    _fails(pins.check_mla_expand_exact, swapped)
+    _fails(pins.check_mla_expand_exact, transposed_rows)
+    _fails(pins.check_mla_expand_exact, no_rounding)

@@ -73,6 +73,15 @@ def test_mla_literal_expansion_matches_absorbed_form():
     pins.check_mla_literal_vs_absorbed(O.mla_sparse_attention, O.mla_retrieval_scores)
 
 
+def test_bf16_rounding_ties_to_even():
+    from oracle.front import to_bf16_bits
+    pins.check_round_bf16(O.round_bf16, to_bf16_bits)
+
+
+def test_mla_expansion_stored_in_bf16_is_exact_on_integers():
+    pins.check_mla_expand_exact(O.mla_expand_rows)
+
+
 def test_kv_cache_size_matches_pages():
     pins.check_kv_cache_size(O.kv_cache_bytes)
 
