@@ -299,6 +299,8 @@ hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void*
   return hipGetLastError();
 }
 
+namespace {
+
 // One workgroup per (head, half): half 0 expands K (W_UK, and copies the rotary
 // dims), half 1 expands V (W_UV).  The half's weights W^h [128 x 512] sit in LDS
 // (rows padded to 1040 bytes: the 16 rows of an MFMA fragment fall on distinct
@@ -459,6 +461,8 @@ __global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
     }
   }
 }
+
+}  // namespace
 
 hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
                              float* logits, float2* stats, hipStream_t st) {
