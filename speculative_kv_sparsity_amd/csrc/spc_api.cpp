@@ -37,6 +37,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int elem_bytes(const spc_shape* s) { return s->dtype == SPC_BF16 ? 2 : 4; }
 
+constexpr int kMaxGridY = 65535;      // workgroups in the second and third grid dimensions
+
 int check_shape(const spc_shape* s) {
   if (!s) return fail(SPC_ERR_INVALID_ARG, "shape is NULL");
   if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_groups < 1)
@@ -55,6 +57,10 @@ int check_shape(const spc_shape* s) {
   if (s->dtype != SPC_F32 && s->dtype != SPC_BF16) return fail(SPC_ERR_UNSUPPORTED, "dtype %d", s->dtype);
   if (s->head_dim < 1 || s->v_dim < 1) return fail(SPC_ERR_INVALID_ARG, "head_dim and v_dim must be >= 1");
   if (!(s->scale > 0.f)) return fail(SPC_ERR_INVALID_ARG, "scale must be > 0");
+  // (sequence, query head) and (sequence, group) instances index the second grid dimension
+  if ((long long)s->batch * s->n_q_heads > kMaxGridY)
+    return fail(SPC_ERR_UNSUPPORTED, "batch * n_q_heads = %lld exceeds %d", (long long)s->batch * s->n_q_heads,
+                kMaxGridY);
   return SPC_OK;
 }
 
@@ -261,6 +267,9 @@ int check_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const
   if (spc::attn_splits(*s) > spc::kCombineMaxSplits)
     return fail(SPC_ERR_UNSUPPORTED, "attention: budget %d needs more than %d row splits", s->budget,
                 spc::kCombineMaxSplits);
+  if ((long long)s->batch * (layer_end - layer_begin) * s->n_groups > kMaxGridY)
+    return fail(SPC_ERR_UNSUPPORTED, "attention: batch * layers * n_groups exceeds %d (split the layer range)",
+                kMaxGridY);
   if (s->head_dim == 576 && kv_l->s_kv != 0)
     return fail(SPC_ERR_UNSUPPORTED, "head_dim 576 reads V from the latent row itself (s_kv must be 0)");
   const int eb = elem_bytes(s);

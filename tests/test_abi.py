@@ -271,3 +271,19 @@ def test_mla_expand_validation():
     one_group = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=1, head_dim=576, v_dim=512,
                        max_len=32768, budget=2048)
     assert lib.spc_mla_expand(ctypes.byref(one_group), 128, 128, *args, p, p, p, None) == L.SPC_ERR_INVALID_ARG
+
+
+def test_grid_limits_are_checked_before_launch():
+    """Instance counts that would not fit the second grid dimension are rejected, not launched."""
+    lib = L.lib()
+    p = ctypes.c_void_p(256)
+    wide = _shape(batch=1024, n_q_heads=128, n_kv_heads=8, n_groups=8)           # 131072 (sequence, head) pairs
+    assert lib.spc_retrieval_scores(ctypes.byref(wide), p, p, p, p, p, 1 << 40, None) == L.SPC_ERR_UNSUPPORTED
+    assert b"n_q_heads" in lib.spc_last_error()
+    s = _shape(batch=64, n_q_heads=32, n_kv_heads=32, n_groups=32, n_layers=64)   # 64 * 64 * 32 instances
+    ql = L.SpcQLayout(32 * 128, 0, 128)
+    kl = L.SpcKvLayout(0, 0, 0, 256, 128)
+    ws = lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s))
+    assert lib.spc_sparse_decode_attn(ctypes.byref(s), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                      L.SPC_ROWS_SLOTS, 0, 64, p, p, ws, None) == L.SPC_ERR_UNSUPPORTED
+    assert b"layer range" in lib.spc_last_error()
