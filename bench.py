@@ -660,7 +660,7 @@ def bench_mla_literal(args, p, torch, W):
     row_exp = (dn + dr + dv) * p.elem_bytes                       # one expanded K||V slot row
     kv_bytes = sel * row_exp                                       # every selected slot read once
     exp_flop = 2.0 * rows_new * C * (dn + dv)                      # K and V up-projection of the new rows
-    exp_bytes = rows_new * (2 * (C + dr) * p.elem_bytes + row_exp) + 2 * H * dn * C * p.elem_bytes
+    exp_bytes = rows_new * ((C + dr) * p.elem_bytes + row_exp) + 2 * H * dn * C * p.elem_bytes
     config = {"workload": "mla_32k, literal expansion: " + WORKLOADS["mla_32k"] if p.name == "mla_32k" else p.name,
               "batch": B, "layers": 1, "q_heads": H, "latent_dim": C, "rope_dim": dr, "nope_dim": dn,
               "cached_tokens": L, "kv_budget": p.budget, "form": "literal (per-head expanded K/V slots)",
@@ -676,8 +676,8 @@ def bench_mla_literal(args, p, torch, W):
                                 "mla_expand_kernel (the newly loaded rows of every head up-projected to K and V "
                                 "on bf16 MFMA)", 1),
         "roofline_expand_hbm": roof("hbm", exp_bytes, iso_ms["expand"], HBM_PEAK_GBS, "GB/s",
-                                    "mla_expand_kernel (latent rows read by both halves + slot rows written + "
-                                    "W_UK and W_UV)", 1),
+                                    "mla_expand_kernel (each new latent row read once + its K||V slot row "
+                                    "written + W_UK and W_UV)", 1),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
         "absorbed_form": {"ms_per_step": round(absorbed_ms, 4), "steps_per_s": round(1e3 / absorbed_ms, 2)},

@@ -301,56 +301,55 @@ hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void*
 
 namespace {
 
-// One workgroup per (head, half): half 0 expands K (W_UK, and copies the rotary
-// dims), half 1 expands V (W_UV).  The half's weights W^h [128 x 512] sit in LDS
-// (rows padded to 1040 bytes: the 16 rows of an MFMA fragment fall on distinct
-// banks).  The head's newly loaded rows of every sequence are taken 256 at a
-// time, 64 per wave in four blocks of 16; each lane loads its row's latent chunk
-// of a k-step straight into the MFMA B fragment, seven steps ahead of the 32
-// MFMAs that use it.  C^T [dims x rows] = W [dims x 512] x
-// latent^T [512 x rows]: a lane ends with 4 consecutive dims of one row, rounded
-// to bf16 and stored as 8 bytes.  The two halves of a head get block ids 8
-// apart, which puts them on the same XCD, where the second finds the rows in L2.
+// One workgroup per (head, part): the head's newly loaded rows of every sequence
+// are taken 64 per pass, part p taking passes p, p + 2, ...  Eight waves: wave
+// w < 4 owns key dims [32 w, 32 w + 32) (W_UK), wave w >= 4 the same value dims
+// (W_UV), and keeps those weight rows in registers as MFMA A fragments for the
+// whole kernel (16 k-steps x 2 blocks of 16 dims).  A pass's latent rows go from
+// memory straight into LDS (global_load_lds_dwordx4: lane l of a wave load lands
+// 16 l bytes past the wave's LDS base), double-buffered: the next pass is in
+// flight while this pass's MFMAs read the current one, and no registers hold it.
+// Every wave reads the rows as B fragments, so each gathered row is read from
+// memory once and yields its K and its V.  The load-list entries of a pass are
+// fetched into registers two passes ahead.
+// C^T [dims x rows] = W [dims x 512] x latent^T [512 x rows] on
+// v_mfma_f32_16x16x32_bf16; a lane ends with 4 consecutive dims of one row,
+// rounded to bf16 (nearest even) and stored as 8 bytes.
 constexpr int kExpDims = 128;                     // nope and value dims per head
-constexpr int kExpWRow = kMlaLatent + 8;          // padded LDS row of W (elements)
-constexpr int kExpThreads = 256;
 constexpr int kExpOut = kExpDims + kMlaRope + kExpDims;   // slot row: K nope || rope || V
 constexpr int kExpKSteps = kMlaLatent / 32;
-constexpr int kExpAhead = 7;                      // k-steps of latent fragments in flight
+constexpr int kExpThreads = 512;                  // 8 waves: 4 on K, 4 on V
+constexpr int kExpRows = 64;                      // rows per pass
+constexpr int kExpRowChunks = kMlaLatent / 8 + 1; // 16-byte chunks per padded LDS row (one pad chunk)
+constexpr int kExpLRow = kExpRowChunks * 8;       // padded LDS row (elements): fragment rows on distinct banks
+constexpr int kExpChunks = kExpRows * kExpRowChunks;
+constexpr int kExpLoads = (kExpChunks + kWave - 1) / kWave;   // wave loads of 64 chunks per pass
+constexpr int kExpBuf = kExpLoads * kWave * 8;    // LDS elements of a pass buffer
 
 __global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv,
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope, const int32_t* __restrict__ load_pos,
     const int32_t* __restrict__ load_slot, const int32_t* __restrict__ load_count, uint16_t* __restrict__ kv,
     uint16_t* __restrict__ q_exp, int B, int H, int max_len, int K) {
-  __shared__ __align__(16) uint16_t sw[kExpDims * kExpWRow];
+  __shared__ __align__(16) uint16_t sa[kExpBuf];
+  __shared__ __align__(16) uint16_t sb[kExpBuf];
   __shared__ int s_pref[kMlaMaxBatch + 1];
-  const int id = blockIdx.x;
-  const int grp = id >> 4, in = id & 15;
-  const int half = in >> 3, h = grp * 8 + (in & 7);
+  __shared__ int s_b[2][kExpRows];                 // sequence of a pass row, or -1
+  __shared__ int s_pos[2][kExpRows];
+  __shared__ int s_slot[2][kExpRows];
+  const int h = blockIdx.x >> 1, part = blockIdx.x & 1;
   if (h >= H) return;
-  const int tid = threadIdx.x;
-  const uint16_t* w = (half ? w_uv : w_uk) + (size_t)h * kExpDims * kMlaLatent;
-  // the half's weights into LDS, 16 loads per thread in flight at a time
-  constexpr int kWChunks = kExpDims * kMlaLatent / 8;
-  constexpr int kWPer = kWChunks / kExpThreads;
-  constexpr int kWBatch = 16;
-  static_assert(kWChunks % kExpThreads == 0 && kWPer % kWBatch == 0, "weight staging split");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, col = lane & 15, kc = lane >> 4;
+  const bool isv = wid >= 4;
+  const int d0 = 32 * (wid & 3);
+  bf16x8_t a[2][kExpKSteps];                      // this wave's weight rows, for the whole kernel
+  {
+    const uint16_t* w = (isv ? w_uv : w_uk) + ((size_t)h * kExpDims + d0) * kMlaLatent;
 #pragma unroll
-  for (int u0 = 0; u0 < kWPer; u0 += kWBatch) {
-    uint4 t[kWBatch];
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int u = 0; u < kWBatch; ++u) {
-      const int c = tid + (u0 + u) * kExpThreads;
-      const int r = c / (kMlaLatent / 8), ch = c - r * (kMlaLatent / 8);
-      t[u] = *reinterpret_cast<const uint4*>(w + (size_t)r * kMlaLatent + 8 * ch);
-    }
-#pragma unroll
-    for (int u = 0; u < kWBatch; ++u) {
-      const int c = tid + (u0 + u) * kExpThreads;
-      const int r = c / (kMlaLatent / 8), ch = c - r * (kMlaLatent / 8);
-      *reinterpret_cast<uint4*>(&sw[r * kExpWRow + 8 * ch]) = t[u];
-    }
+      for (int s = 0; s < kExpKSteps; ++s)
+        a[db][s] = *reinterpret_cast<const bf16x8_t*>(w + (size_t)(16 * db + col) * kMlaLatent + 32 * s + 8 * kc);
   }
   if (tid == 0) {
     int acc = 0;
@@ -361,7 +360,7 @@ __global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
     }
     s_pref[B] = acc;
   }
-  if (half == 0 && q_exp != nullptr) {             // the head's query against the expanded keys
+  if (part == 0 && q_exp != nullptr) {             // the head's query against the expanded keys
     for (int i = tid; i < B * (kExpDims + kMlaRope); i += kExpThreads) {
       const int b = i / (kExpDims + kMlaRope), d = i - b * (kExpDims + kMlaRope);
       q_exp[((size_t)b * H + h) * (kExpDims + kMlaRope) + d] =
@@ -371,94 +370,110 @@ __global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
   }
   __syncthreads();
   const int R = s_pref[B];
-  const int lane = tid & 63, wid = tid >> 6, col = lane & 15, kc = lane >> 4;
-  const int off = half ? kExpDims + kMlaRope : 0;
-  int pref[kMlaMaxBatch];
-#pragma unroll
-  for (int j = 0; j < kMlaMaxBatch; ++j) pref[j] = j < B ? s_pref[j] : R;
-  // the load-list entries of this lane's four rows of a pass, found without a data-dependent loop
-  // and loaded together; a pass's entries are loaded during the previous pass's MFMAs
-  int npos[4], nslot[4], nb[4];
-  auto list_load = [&](int r0) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int rr = r0 + 64 * wid + 16 * rb + col;
-      int b = 0;
-#pragma unroll
-      for (int j = 1; j < kMlaMaxBatch; ++j) b += rr >= pref[j];
-      const bool in = rr < R;
-      const size_t li = in ? ((size_t)b * H + h) * K + (rr - pref[b]) : 0;
-      nb[rb] = in ? b : -1;
-      npos[rb] = load_pos[li];
-      nslot[rb] = load_slot[li];
+  const int npass = (R + kExpRows - 1) / kExpRows;
+  int p = part;
+  if (p >= npass) return;                          // uniform: no barrier follows for this workgroup
+
+  // a pass's load-list entries: fetched by 64 threads into registers, published to LDS later
+  int e_b = -1, e_pos = 0, e_slot = 0;
+  auto fetch = [&](int pass) {
+    e_b = -1;
+    if (tid < kExpRows) {
+      const int rr = pass * kExpRows + tid;
+      if (rr < R) {
+        int b = 0;
+        for (int j = 1; j < B; ++j) b += rr >= s_pref[j];
+        const size_t li = ((size_t)b * H + h) * K + (rr - s_pref[b]);
+        e_pos = load_pos[li];
+        e_slot = load_slot[li];
+        e_b = b;
+      }
     }
   };
-  list_load(0);
-  for (int r0 = 0; r0 < R; r0 += 4 * 64) {
-    if (r0 + 64 * wid >= R) break;                 // wave-uniform: no rows left for this wave
-    const uint16_t* rowp[4];
-    uint16_t* dst[4];
-    bool ok[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int b = nb[rb], pos = npos[rb], slot = nslot[rb];
-      ok[rb] = b >= 0 && pos >= 0 && pos < max_len && slot >= 0 && slot < K;
-      rowp[rb] = ok[rb] ? lat + ((size_t)b * max_len + pos) * (kMlaLatent + kMlaRope) : lat;
-      dst[rb] = ok[rb] ? kv + (((size_t)b * H + h) * K + slot) * kExpOut : kv;
+  auto publish = [&](int buf) {
+    if (tid < kExpRows) {
+      const bool ok = e_b >= 0 && e_pos >= 0 && e_pos < max_len && e_slot >= 0 && e_slot < K;
+      s_b[buf][tid] = ok ? e_b : -1;
+      s_pos[buf][tid] = ok ? e_pos : 0;
+      s_slot[buf][tid] = ok ? e_slot : 0;
     }
-    f32x4_t acc[4][kExpDims / 16];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int db = 0; db < kExpDims / 16; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // the gathered latent fragments of kExpAhead k-steps are in flight ahead of the MFMAs that use
-    // them (a ring of registers; a gather from a random row costs far more than one step's MFMAs)
-    bf16x8_t ring[kExpAhead + 1][4];
-    auto load_b = [&](int s, bf16x8_t* bf) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (ok[rb]) {
-          bf[rb] = *reinterpret_cast<const bf16x8_t*>(rowp[rb] + 32 * s + 8 * kc);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bf[rb][e] = (__bf16)0.f;
-        }
+  };
+  // the rows of the entries in s_*[buf] -> LDS (pad chunks and empty rows load latent row 0)
+  auto dma = [&](int buf, uint16_t* dst) {
+    for (int i = wid; i < kExpLoads; i += kExpThreads / kWave) {
+      const int k = kWave * i + lane;
+      const int r = k / kExpRowChunks, ch = k - r * kExpRowChunks;
+      const uint16_t* src = lat;
+      if (k < kExpChunks && ch < kMlaLatent / 8) {
+        const int b = s_b[buf][r];
+        if (b >= 0) src = lat + ((size_t)b * max_len + s_pos[buf][r]) * (kMlaLatent + kMlaRope) + 8 * ch;
       }
-    };
+      __builtin_amdgcn_global_load_lds(src, dst + 8 * kWave * i, 16, 0, 0);
+    }
+  };
+  auto pass_body = [&](int buf, const uint16_t* rows) {
+    f32x4_t acc[4][2];
 #pragma unroll
-    for (int s = 0; s < kExpAhead; ++s) load_b(s, ring[s]);
-    if (r0 + 4 * 64 < R) list_load(r0 + 4 * 64);   // the next pass's entries, behind this pass's MFMAs
+    for (int rb = 0; rb < 4; ++rb) { acc[rb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f}; acc[rb][1] = acc[rb][0]; }
 #pragma unroll
     for (int s = 0; s < kExpKSteps; ++s) {
-      if (s + kExpAhead < kExpKSteps) load_b(s + kExpAhead, ring[(s + kExpAhead) % (kExpAhead + 1)]);
-      const bf16x8_t* bcur = ring[s % (kExpAhead + 1)];
-      bf16x8_t a[kExpDims / 16];
 #pragma unroll
-      for (int db = 0; db < kExpDims / 16; ++db)
-        a[db] = *reinterpret_cast<const bf16x8_t*>(&sw[(16 * db + col) * kExpWRow + 32 * s + 8 * kc]);
-#pragma unroll
-      for (int db = 0; db < kExpDims / 16; ++db)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[db], bcur[rb], acc[rb][db], 0, 0, 0);
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(rows + (16 * rb + col) * kExpLRow + 32 * s + 8 * kc);
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][s], bf, acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][s], bf, acc[rb][1], 0, 0, 0);
+      }
     }
-    // lane (col, kc): dims 16 db + 4 kc .. + 3 of row `col` of each block
+    // lane (col, kc): dims d0 + 16 db + 4 kc .. + 3 of row 16 rb + col
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      if (!ok[rb]) continue;
+      const int row = 16 * rb + col;
+      const int b = s_b[buf][row];
+      if (b < 0) continue;
+      uint16_t* dst = kv + (((size_t)b * H + h) * K + s_slot[buf][row]) * kExpOut;
 #pragma unroll
-      for (int db = 0; db < kExpDims / 16; ++db) {
-        const uint2 v = make_uint2(bf16_bits(acc[rb][db][0]) | (bf16_bits(acc[rb][db][1]) << 16),
-                                   bf16_bits(acc[rb][db][2]) | (bf16_bits(acc[rb][db][3]) << 16));
-        *reinterpret_cast<uint2*>(dst[rb] + off + 16 * db + 4 * kc) = v;
+      for (int db = 0; db < 2; ++db) {
+        const uint2 w2 = make_uint2(bf16_bits(acc[rb][db][0]) | (bf16_bits(acc[rb][db][1]) << 16),
+                                    bf16_bits(acc[rb][db][2]) | (bf16_bits(acc[rb][db][3]) << 16));
+        *reinterpret_cast<uint2*>(dst + (isv ? kExpDims + kMlaRope : 0) + d0 + 16 * db + 4 * kc) = w2;
       }
-      if (half == 0) {                             // the rotary dims of the row, copied as they are
-        *reinterpret_cast<uint4*>(dst[rb] + kExpDims + 8 * kc) =
-            *reinterpret_cast<const uint4*>(rowp[rb] + kMlaLatent + 8 * kc);
-        *reinterpret_cast<uint4*>(dst[rb] + kExpDims + 8 * (kc + 4)) =
-            *reinterpret_cast<const uint4*>(rowp[rb] + kMlaLatent + 8 * (kc + 4));
+      if (!isv && rb == (wid & 3)) {               // the rotary dims of the row, copied as they are
+        const uint16_t* src = lat + ((size_t)b * max_len + s_pos[buf][row]) * (kMlaLatent + kMlaRope) + kMlaLatent;
+        *reinterpret_cast<uint4*>(dst + kExpDims + 8 * kc) = *reinterpret_cast<const uint4*>(src + 8 * kc);
+        *reinterpret_cast<uint4*>(dst + kExpDims + 8 * (kc + 4)) = *reinterpret_cast<const uint4*>(src + 8 * (kc + 4));
       }
     }
+  };
+
+  fetch(p);
+  publish(0);
+  if (p + 2 < npass) fetch(p + 2);
+  __syncthreads();
+  dma(0, sa);
+  publish(1);                                      // entries of pass p + 2 (unused if there is none)
+  __syncthreads();                                 // pass p's rows are in sa
+#pragma unroll 1
+  for (;;) {
+    // even step: rows of pass p in sa (entries s_*[0]); pass p + 2 (entries s_*[1]) -> sb
+    bool more = p + 2 < npass;
+    if (more) dma(1, sb);
+    if (p + 4 < npass) fetch(p + 4);
+    pass_body(0, sa);
+    __syncthreads();                               // sb loaded; sa and s_*[0] free
+    if (!more) break;
+    publish(0);                                    // entries of pass p + 4
+    __syncthreads();
+    p += 2;
+    // odd step: rows of pass p in sb (entries s_*[1]); pass p + 2 (entries s_*[0]) -> sa
+    more = p + 2 < npass;
+    if (more) dma(0, sa);
+    if (p + 4 < npass) fetch(p + 4);
+    pass_body(1, sb);
+    __syncthreads();
+    if (!more) break;
+    publish(1);
+    __syncthreads();
+    p += 2;
   }
 }
 
@@ -479,8 +494,7 @@ hipError_t launch_mla_expand(const spc_shape& s, const void* latent, const void*
                              const void* q_nope, const void* q_rope, const int32_t* load_pos,
                              const int32_t* load_slot, const int32_t* load_count, void* kv_exp, void* q_exp,
                              hipStream_t st) {
-  const int ngrp = (s.n_q_heads + 7) / 8;
-  mla_expand_kernel<<<dim3(ngrp * 16), kExpThreads, 0, st>>>(
+  mla_expand_kernel<<<dim3(2 * s.n_q_heads), kExpThreads, 0, st>>>(
       static_cast<const uint16_t*>(latent), static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
       static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), load_pos, load_slot, load_count,
       static_cast<uint16_t*>(kv_exp), static_cast<uint16_t*>(q_exp), s.batch, s.n_q_heads, s.max_len, s.budget);
