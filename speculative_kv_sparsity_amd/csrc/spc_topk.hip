@@ -457,33 +457,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
 
-  // one sweep over the thread's contiguous 32 keys
+  // one sweep over the thread's contiguous 32 keys, which then stay in registers: the later
+  // passes over the candidates are unrolled, predicated loops with no LDS traffic and no
+  // per-lane trip counts
+  constexpr int kKeysPerThread = 4 * kVecPerThread;
   const int v0 = tid * kVecPerThread;
+  uint32_t kr[kKeysPerThread];
   uint32_t gtm = 0u, cm = 0u;
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
     const int vv = v0 + u;
-    if (vv < nv) {
-      const uint4 kv = skeys[vslot(vv)];
-      const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+    const uint4 kv = vv < nv ? skeys[vslot(vv)] : make_uint4(0u, 0u, 0u, 0u);
+    kr[4 * u] = kv.x; kr[4 * u + 1] = kv.y; kr[4 * u + 2] = kv.z; kr[4 * u + 3] = kv.w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = 4 * vv + e < n;
-        const uint32_t top = k4[e] >> 24;
-        gtm |= (uint32_t)(valid && top > d1) << (4 * u + e);
-        if (valid && top == d1) {
-          cm |= 1u << (4 * u + e);
-          atomicAdd(&hist[(k4[e] >> 12) & 4095u], 1u);
-        }
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = 4 * vv + e < n;
+      const uint32_t top = kr[4 * u + e] >> 24;
+      gtm |= (uint32_t)(valid && top > d1) << (4 * u + e);
+      if (valid && top == d1) {
+        cm |= 1u << (4 * u + e);
+        atomicAdd(&hist[(kr[4 * u + e] >> 12) & 4095u], 1u);
       }
     }
   }
   __syncthreads();
-  auto cand_key = [&](int bit) -> uint32_t {
-    const uint4 kv = skeys[vslot(v0 + (bit >> 2))];
-    const int e = bit & 3;
-    return e == 0 ? kv.x : (e == 1 ? kv.y : (e == 2 ? kv.z : kv.w));
-  };
   find_bin(hist, 4096, need, scan_smem, bcast);
   uint32_t prefix = (d1 << 24) | (bcast[0] << 12);
   uint32_t pmask = 0xFFFFF000u;
@@ -493,10 +490,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   if (!whole) {
     for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
     __syncthreads();
-    for (uint32_t m = cm; m; m &= m - 1) {
-      const uint32_t key = cand_key(__ffs(m) - 1);
-      if ((key & pmask) == prefix) atomicAdd(&hist[key & 4095u], 1u);
-    }
+#pragma unroll
+    for (int e = 0; e < kKeysPerThread; ++e)
+      if (((cm >> e) & 1u) && (kr[e] & pmask) == prefix) atomicAdd(&hist[kr[e] & 4095u], 1u);
     __syncthreads();
     find_bin(hist, 4096, need, scan_smem, bcast);
     prefix |= bcast[0];
@@ -506,11 +502,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   }
   // resolve the candidates: masked key > prefix -> selected; == prefix -> tie at T
   uint32_t eqm = 0u;
-  for (uint32_t m = cm; m; m &= m - 1) {
-    const int bit = __ffs(m) - 1;
-    const uint32_t mk = cand_key(bit) & pmask;
-    if (mk > prefix) gtm |= 1u << bit;
-    else if (mk == prefix) eqm |= 1u << bit;
+#pragma unroll
+  for (int e = 0; e < kKeysPerThread; ++e) {
+    const uint32_t mk = kr[e] & pmask;
+    const bool c = (cm >> e) & 1u;
+    gtm |= (uint32_t)(c && mk > prefix) << e;
+    eqm |= (uint32_t)(c && mk == prefix) << e;
   }
   const uint32_t gt = __popc(gtm), eq = __popc(eqm);
   uint32_t tot;
