@@ -22,7 +22,9 @@
 //   head per group (MHA, MLA) the keys are not written: the select kernel maps
 //   the probabilities to keys as it loads them.
 // topk_select_kernel  one 1024-thread workgroup per (b, g): sums the chunk
-//   histograms (first digit), runs the two remaining 12-bit passes with LDS
+//   histograms (first digit; with one head per group and rows that fit LDS the
+//   select counts it from its staged keys and no keys pass runs), runs the two
+//   remaining 12-bit passes with LDS
 //   histograms over the keys that still match the prefix, and compacts every j
 //   with key > T plus the lowest-index `need` ones with key == T, ascending,
 //   with two block scans over per-thread contiguous index ranges.  For
@@ -423,10 +425,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
       }
     }
   }
-  const int nch = (n + kKeyChunk - 1) / kKeyChunk;
   const int hbin = tid & (kBins1 - 1), c0 = tid >> 8;
   uint32_t hs = 0u;
-  {
+  if (!RAW) {                                       // first digit: the chunk histograms of the keys kernel
+    const int nch = (n + kKeyChunk - 1) / kKeyChunk;
     const uint32_t* ch = chist + (size_t)inst * nchunk * kBins1 + hbin;
     for (int cb = c0; cb < nch; cb += 32) {
       uint32_t hv[8];
@@ -439,14 +441,29 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
       for (int u = 0; u < 8; ++u) hs += hv[u];
     }
   }
+  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
     const int i4 = tid + u * kSelThreads;
-    if (i4 < nv) skeys[vslot(i4)] = to_keys<RAW>(v[u]);
+    if (i4 < nv) {
+      v[u] = to_keys<RAW>(v[u]);
+      skeys[vslot(i4)] = v[u];
+    }
   }
-  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
-  atomicAdd(&hist[hbin], hs);
+  if (RAW) {
+    // one head per group: no keys pass ran; the first digit is counted here from the staged keys
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const int i4 = tid + u * kSelThreads;
+      const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i4 < nv && 4 * i4 + e < n) atomicAdd(&hist[k4[e] >> 24], 1u);
+    }
+  } else {
+    atomicAdd(&hist[hbin], hs);
+  }
   __syncthreads();
 
   int need = K;
@@ -539,16 +556,20 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
   uint32_t* keys = static_cast<uint32_t*>(ws);
   uint32_t* chist = keys + (size_t)inst * s.max_len;
   const dim3 kg(nchunk, inst);
-  if (stats)
-    topk_keys_kernel<true><<<kg, kKeyThreads, 0, st>>>(scores, stats, lengths, keys, chist, s.n_q_heads, s.n_groups,
-                                                       s.max_len, s.budget, nchunk, ntiles, stat_tile);
-  else
-    topk_keys_kernel<false><<<kg, kKeyThreads, 0, st>>>(scores, nullptr, lengths, keys, chist, s.n_q_heads,
-                                                        s.n_groups, s.max_len, s.budget, nchunk, 0, 1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // one head per group: the keys are the scores' own order keys, taken on load
+  // one head per group with rows that fit LDS: the select keys the scores and counts the first
+  // digit itself, so no keys pass runs
   const bool raw = s.n_q_heads == s.n_groups;
+  if (!(raw && s.max_len <= kTopkLdsKeys)) {
+    if (stats)
+      topk_keys_kernel<true><<<kg, kKeyThreads, 0, st>>>(scores, stats, lengths, keys, chist, s.n_q_heads,
+                                                         s.n_groups, s.max_len, s.budget, nchunk, ntiles, stat_tile);
+    else
+      topk_keys_kernel<false><<<kg, kKeyThreads, 0, st>>>(scores, nullptr, lengths, keys, chist, s.n_q_heads,
+                                                          s.n_groups, s.max_len, s.budget, nchunk, 0, 1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // one head per group: the keys are the scores' own order keys, taken on load
   const uint32_t* kin = raw ? reinterpret_cast<const uint32_t*>(scores) : keys;
   if (s.max_len <= kTopkLdsKeys) {
     if (raw)
