@@ -18,6 +18,7 @@
 //   a wave sum per (row, sequence) (DPP and permlane swaps, no LDS) gives the
 //   slice's partial dot product.
 //   Row-block 0 of each slice also writes the slice's sum of x^2.
+// front_mfma_kernel    the same pass on MFMA for bf16 with more than 4 sequences.
 // front_finish_kernel  one workgroup per (head, sequence), one thread per
 //   rotary pair (i, i + d/2): sums the slice partials, scales by 1/rms, rotates
 //   by position * theta'_i (angle reduced in double precision: positions reach
@@ -119,6 +120,107 @@ __global__ __launch_bounds__(kThreads) void front_gemv_kernel(const int32_t* __r
   }
 }
 
+// bf16 with more than 4 sequences: the projection is a dense [rows x hidden] x
+// [hidden x 16 sequences] product, so it runs on MFMA (v_mfma_f32_16x16x32_bf16):
+// C^T[row][seq] = W[row][k] (gamma x)[seq][k].  A fragments are 16 contiguous bytes
+// of a weight row, straight from memory (each weight read once); B fragments come
+// from LDS, where gamma * x of the slice sits as a bf16 pair hi + lo (the product of
+// two bf16 values has at most 16 significant bits, so hi + lo holds it exactly and
+// the MFMAs add exact products in float32, as the GEMV does).  One wave per 16
+// rows, four per workgroup; a lane ends with 4 consecutive rows of one sequence and
+// writes them as one 16-byte vector into the same partial layout as the GEMV.
+constexpr int kMfmaBatch = 16;
+constexpr int kFrontKSteps = kFrontSlice / 32;
+constexpr int kFrontAhead = 8;                    // k-steps of weight fragments in flight
+
+__global__ __launch_bounds__(kThreads) void front_mfma_kernel(const int32_t* __restrict__ tokens,
+                                                              const uint16_t* __restrict__ emb, int64_t vocab,
+                                                              const uint16_t* __restrict__ gamma,
+                                                              const uint16_t* __restrict__ wq,
+                                                              const uint16_t* __restrict__ wk, int rows_q,
+                                                              int rows_total, int hidden, int B,
+                                                              float* __restrict__ part, float* __restrict__ rms_part) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) uint16_t xh[kMfmaBatch][kFrontSlice + 8];   // gamma * x, bf16 high part
+  __shared__ __align__(16) uint16_t xl[kMfmaBatch][kFrontSlice + 8];   // and the remainder
+  __shared__ float s_sq[kMfmaBatch][4];
+  const int slice = blockIdx.y;
+  const int k0 = slice * kFrontSlice;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, col = lane & 15, kc = lane >> 4;
+  const int row = blockIdx.x * 64 + wid * 16 + col;           // this lane's weight row (A fragment row)
+  const bool rok = row < rows_total;
+  const uint16_t* wr = !rok ? wq : (row < rows_q ? wq + (size_t)row * hidden : wk + (size_t)(row - rows_q) * hidden);
+  wr += k0 + 8 * kc;
+  // the first k-steps' weight fragments go out before anything else
+  bf16x8_t ring[kFrontAhead + 1];
+  auto load_a = [&](int s, bf16x8_t& a) {
+    if (rok) {
+      a = *reinterpret_cast<const bf16x8_t*>(wr + 32 * s);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = (__bf16)0.f;
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kFrontAhead; ++s) load_a(s, ring[s]);
+  // gamma * x of every sequence over the slice (hi + lo), and the slice's sum of x^2: thread t
+  // takes the 16-byte chunk t % 128 of sequence 2 i + t / 128 in round i (all loads issued first)
+  constexpr int kChunksPerSlice = kFrontSlice / 8;
+  constexpr int kRounds = kMfmaBatch * kChunksPerSlice / kThreads;
+  static_assert(kThreads % kChunksPerSlice == 0 && kRounds * kThreads == kMfmaBatch * kChunksPerSlice,
+                "setup split");
+  const int ch = tid % kChunksPerSlice, sub = tid / kChunksPerSlice;
+  const uint4 gv = *reinterpret_cast<const uint4*>(gamma + k0 + 8 * ch);
+  uint4 xv[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int b = (kThreads / kChunksPerSlice) * i + sub;
+    const int t = b < B ? tokens[b] : -1;
+    xv[i] = t >= 0 && (int64_t)t < vocab ? *reinterpret_cast<const uint4*>(emb + (size_t)t * hidden + k0 + 8 * ch)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int b = (kThreads / kChunksPerSlice) * i + sub;
+    const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+    uint32_t hw[4], lw[4];
+    float sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = bf_lo(xw[j]), x1 = bf_hi(xw[j]);
+      const float p0 = bf_lo(gw[j]) * x0, p1 = bf_hi(gw[j]) * x1;
+      hw[j] = pack_bf16_hi(p0, p1);
+      lw[j] = pack_bf16_lo(p0, p1, hw[j]);
+      sq = fmaf(x0, x0, fmaf(x1, x1, sq));
+    }
+    *reinterpret_cast<uint4*>(&xh[b][8 * ch]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *reinterpret_cast<uint4*>(&xl[b][8 * ch]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    sq = wave_sum(sq);
+    if (lane == 0) s_sq[b][wid % (kChunksPerSlice / kWave)] = sq;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < B) rms_part[(size_t)slice * kFrontMaxBatch + tid] = s_sq[tid][0] + s_sq[tid][1];
+  f32x4_t acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kFrontKSteps; ++s) {
+    if (s + kFrontAhead < kFrontKSteps) load_a(s + kFrontAhead, ring[(s + kFrontAhead) % (kFrontAhead + 1)]);
+    const bf16x8_t a = ring[s % (kFrontAhead + 1)];
+    const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&xh[col][32 * s + 8 * kc]);
+    const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&xl[col][32 * s + 8 * kc]);
+    acc_h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc_h, 0, 0, 0);
+    acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc_l, 0, 0, 0);
+  }
+  // lane (col, kc): rows blockIdx.x * 64 + wid * 16 + 4 kc .. + 3 of sequence col
+  const int r0 = blockIdx.x * 64 + wid * 16 + 4 * kc;
+  if (col < B && r0 < rows_total) {
+    float* dst = part + ((size_t)slice * kFrontMaxBatch + col) * rows_total + r0;
+    *reinterpret_cast<float4*>(dst) =
+        make_float4(acc_h[0] + acc_l[0], acc_h[1] + acc_l[1], acc_h[2] + acc_l[2], acc_h[3] + acc_l[3]);
+  }
+}
+
 struct RopeFreqs {
   double theta[kFrontMaxHeadDim / 2];
 };
@@ -190,6 +292,13 @@ hipError_t launch_front(const spc_shape& s, int hidden, int64_t vocab, const spc
   const char* q = static_cast<const char*>(wq);
   const char* k = static_cast<const char*>(wk);
   const size_t lds = (size_t)s.batch * kFrontSlice * sizeof(float);
+  if (s.dtype == SPC_BF16 && s.batch > 4) {
+    const dim3 gm((rows_total + 63) / 64, nslice);
+    front_mfma_kernel<<<gm, kThreads, 0, st>>>(tokens, static_cast<const uint16_t*>(emb), vocab,
+                                               static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(wq),
+                                               static_cast<const uint16_t*>(wk), rows_q, rows_total, hidden, s.batch,
+                                               part, rms_part);
+  } else {
 #define SPC_GEMV(DT_, RPW_)                                                                             \
   front_gemv_kernel<DT_, RPW_><<<g1, kThreads, lds, st>>>(tokens, e, vocab, g, q, k, rows_q, rows_total, hidden, \
                                                           s.batch, part, rms_part)
@@ -199,6 +308,7 @@ hipError_t launch_front(const spc_shape& s, int hidden, int64_t vocab, const spc
     if (rpw == 4) SPC_GEMV(SPC_F32, 4); else SPC_GEMV(SPC_F32, 8);
   }
 #undef SPC_GEMV
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // rotary frequencies in double precision, extended by YaRN's "NTK-by-parts" when factor > 1

@@ -87,6 +87,15 @@ def test_front_batch16():
     _run_front(p, fw, tokens=rng.integers(0, 1000, 16).tolist(), positions=rng.integers(0, 4096, 16).tolist())
 
 
+def test_front_partial_batch_on_the_matrix_path():
+    """7 sequences (more than 4: the MFMA projection; fewer than its 16 columns), one token outside
+    the vocabulary, positions past the cache and at 0."""
+    p = W.PRESETS["b16_grow"].with_(batch=7, n_layers=1, max_len=4096)
+    fw = W.generate_front(p, device="cuda", seed=9, vocab=3000, hidden=2048)
+    q, _ = _run_front(p, fw, tokens=[11, 2999, -5, 0, 1500, 7, 2048], positions=[0, 4095, 17, 4096, 9000, 3, 100])
+    assert np.all(_f64(q[2]) == 0)
+
+
 def test_front_rejects_bad_hidden_and_batch():
     p = W.PRESETS["tiny"].with_(dtype="bf16")
     fw = W.generate_front(p, device="cuda", seed=5, vocab=10, hidden=1024)
