@@ -299,6 +299,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   for (int i = tid; i < RPS; i += kThreads) sRow[i] = split_row(rl, i0 + i, cnt, mode, max_rows);
   __syncthreads();
   const char* kbase = kv + b * kl.b + layer * kl.layer + (int64_t)kvh * kl.head;
+  // a buffer resource over the head's rows (the host keeps them under 2 GiB)
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(kbase), (short)0, (int)((int64_t)max_rows * kl.row), kBufferRsrcWord3);
 
   // query chunk p + 8c as hi / lo bf16 pairs
   uint32_t qhi[CPLK][4], qlo[CPLK][4];
@@ -327,15 +330,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       row[j] = sRow[base + 8 * j + rr];
-      const char* kr = kbase + (int64_t)(row[j] >= 0 ? row[j] : 0) * kl.row;
+      // a padding row's offset lies past the resource and reads zeros: its weight 0 must not meet NaN
+      const uint32_t off = row[j] >= 0 ? (uint32_t)row[j] * (uint32_t)kl.row + 16u * p : kBufferOutOfRange;
 #pragma unroll
-      for (int c = 0; c < CPLK; ++c) {
-        if (row[j] >= 0) {
-          kc[j][c] = ld16(kr + (p + 8 * c) * 16);
-        } else {
-          kc[j][c].w[0] = kc[j][c].w[1] = kc[j][c].w[2] = kc[j][c].w[3] = 0u;   // weight 0 must not meet NaN
-        }
-      }
+      for (int c = 0; c < CPLK; ++c) kc[j][c] = ld16_buffer(krs, off + 128u * c);
     }
     float lg[2];
 #pragma unroll

@@ -24,6 +24,19 @@ __device__ __forceinline__ Vec16 ld16(const void* p) {
   return r;
 }
 
+// Buffer-resource loads (raw, stride 0): an offset at or past the resource's byte count reads
+// zeros, which turns a padding row's load into zeros with no branch.  Word 3 of the resource
+// for gfx9-family parts: 32-bit data format, no swizzle.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // past any range the host allows (< 2 GiB)
+__device__ __forceinline__ Vec16 ld16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  Vec16 o;
+  o.w[0] = (uint32_t)v.x; o.w[1] = (uint32_t)v.y; o.w[2] = (uint32_t)v.z; o.w[3] = (uint32_t)v.w;
+  return o;
+}
+
 __device__ __forceinline__ void st16(void* p, const Vec16& r) {
   *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
 }
@@ -130,12 +143,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Max / sum over lanes that share (lane & 7): the 8 lanes l, l+8, ..., l+56.
-__device__ __forceinline__ float max_across_rows8(float v) {
-  v = fmaxf(v, __shfl_xor(v, 8, kWave));
-  v = fmaxf(v, __shfl_xor(v, 16, kWave));
-  v = fmaxf(v, __shfl_xor(v, 32, kWave));
-  return v;
-}
 
 constexpr int kDppRowRor8 = 0x128;      // lane i <- lane (i+8) mod 16 within each 16-lane row
 
@@ -150,6 +157,23 @@ __device__ __forceinline__ float add_xor16(float v) {
 __device__ __forceinline__ float add_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// max over the 8 lanes that share lane & 7 (l ^ 8 by DPP, l ^ 16 and l ^ 32 by permlane swaps)
+__device__ __forceinline__ float max_across_rows8(float v) {
+  v = fmaxf(v, dpp_f<kDppRowRor8>(v));
+  v = max_xor16(v);
+  return max_xor32(v);
 }
 
 __device__ __forceinline__ float sum_across_rows8(float v) {

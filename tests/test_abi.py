@@ -247,6 +247,17 @@ def test_attention_halves_validation():
     assert lib.spc_attn_merge(ctypes.byref(s), 0, 4, p, need, ctypes.c_void_p(264), None) == L.SPC_ERR_INVALID_ARG
     big = _shape(max_len=1 << 20, budget=200000)                                  # > 1024 splits
     assert lib.spc_attn_merge(ctypes.byref(big), 0, 1, p, 1 << 40, p, None) == L.SPC_ERR_UNSUPPORTED
+    # MLA latent rows are read through a 32-bit range: one head's rows must stay under 2 GiB,
+    # and a row stride below the 576 scored elements is refused
+    for max_len, row, ok in ((1 << 20, 576, True), (1 << 21, 576, False), (4096, 512, False)):
+        mla = _shape(batch=1, n_q_heads=16, n_kv_heads=1, n_groups=16, head_dim=576, v_dim=512, max_len=max_len,
+                     budget=2048, scale=192 ** -0.5)
+        need_m = lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(mla))
+        mql = L.SpcQLayout(16 * 576, 0, 576)
+        mkl = L.SpcKvLayout(max_len * row, 0, 0, row, 0)
+        rc = lib.spc_attn_partial(ctypes.byref(mla), p, ctypes.byref(mql), p, ctypes.byref(mkl), p, p,
+                                  L.SPC_ROWS_GATHER, 0, 1, p, need_m - 1, None)
+        assert rc == (L.SPC_ERR_WORKSPACE if ok else L.SPC_ERR_UNSUPPORTED), (max_len, row, rc)
 
 
 def test_mla_expand_validation():
