@@ -44,7 +44,7 @@ constexpr int kBins1 = 256;                       // first digit: key bits 31..2
 
 // Order-preserving map from fp32 bits to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float v) {
-  const uint32_t u = __float_as_uint(v);
+  const uint32_t u = __float_as_uint(v + 0.0f);   // -0 + 0 = +0: the two zeros are one value (a tie)
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 // Keys of 4 loaded words: the words themselves, or (RAW) the keys of 4 fp32 values.
@@ -394,6 +394,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   __shared__ uint32_t scan_smem[16];
   __shared__ uint32_t bcast[2];
   constexpr int kVecPerThread = kTopkLdsKeys / 4 / kSelThreads;   // 8 vectors = 32 keys
+  // digits of the order key: raw float32 keys take 12 + 12 + 8 bits (the top 12 bits -- sign,
+  // exponent and 3 mantissa bits -- spread logits over many bins, so the first histogram's LDS
+  // atomics rarely collide); keys of the keys pass take 8 (its chunk histograms) + 12 + 12
+  constexpr int S1 = RAW ? 20 : 24;                // first digit: bits 31..S1
+  constexpr int S2 = S1 - 12;                      // second digit: 12 bits S1-1..S2; third: S2-1..0
 
   const int inst = blockIdx.x;
   const int b = inst / n_groups;
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
       const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (i4 < nv && 4 * i4 + e < n) atomicAdd(&hist[k4[e] >> 24], 1u);
+        if (i4 < nv && 4 * i4 + e < n) atomicAdd(&hist[k4[e] >> S1], 1u);
     }
   } else {
     atomicAdd(&hist[hbin], hs);
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   __syncthreads();
 
   int need = K;
-  find_bin(hist, kBins1, need, scan_smem, bcast);
+  find_bin(hist, 1 << (32 - S1), need, scan_smem, bcast);
   const uint32_t d1 = bcast[0];
   need -= (int)bcast[1];
   __syncthreads();
@@ -489,18 +494,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool valid = 4 * vv + e < n;
-      const uint32_t top = kr[4 * u + e] >> 24;
+      const uint32_t top = kr[4 * u + e] >> S1;
       gtm |= (uint32_t)(valid && top > d1) << (4 * u + e);
       if (valid && top == d1) {
         cm |= 1u << (4 * u + e);
-        atomicAdd(&hist[(kr[4 * u + e] >> 12) & 4095u], 1u);
+        atomicAdd(&hist[(kr[4 * u + e] >> S2) & 4095u], 1u);
       }
     }
   }
   __syncthreads();
   find_bin(hist, 4096, need, scan_smem, bcast);
-  uint32_t prefix = (d1 << 24) | (bcast[0] << 12);
-  uint32_t pmask = 0xFFFFF000u;
+  uint32_t prefix = (d1 << S1) | (bcast[0] << S2);
+  uint32_t pmask = ~((1u << S2) - 1u);
   need -= (int)bcast[1];
   const bool whole = (int)hist[bcast[0]] == need;
   __syncthreads();
@@ -509,9 +514,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < kKeysPerThread; ++e)
-      if (((cm >> e) & 1u) && (kr[e] & pmask) == prefix) atomicAdd(&hist[kr[e] & 4095u], 1u);
+      if (((cm >> e) & 1u) && (kr[e] & pmask) == prefix) atomicAdd(&hist[kr[e] & ((1u << S2) - 1u)], 1u);
     __syncthreads();
-    find_bin(hist, 4096, need, scan_smem, bcast);
+    find_bin(hist, 1 << S2, need, scan_smem, bcast);
     prefix |= bcast[0];
     pmask = 0xFFFFFFFFu;
     need -= (int)bcast[1];

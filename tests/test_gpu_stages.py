@@ -186,6 +186,12 @@ LOGIT_TIE_CASES = [
     (1, 6, 2, 33000, 5000, [33000], None, False),                   # 3 heads per group, LDS limit crossed
     (3, 2, 1, 2000, 100, [100, 101, 0], None, False),               # n = K, n = K + 1, n = 0
     (2, 4, 4, 1500, 1, [1500, 7], [-1.0, 4.0], True),               # K = 1, one head per group
+    # one head per group at the LDS size limit: 64 values one ulp apart (the top 24 bits of every
+    # key agree, so the last radix digit decides), and the boundary inside a tie group
+    (2, 4, 4, 32768, 2000, [32768, 20001], list(np.float32(1.0) + np.arange(64, dtype=np.float32)
+                                                 * np.float32(2.0 ** -23)), False),
+    # -0.0 and +0.0 are one value: ties broken by the lower index
+    (1, 2, 2, 30000, 2048, [30000], [-0.0, 0.0, -1.0], False),
 ]
 
 
