@@ -11,6 +11,8 @@
 //   ordered compactions (block scans over contiguous ranges) give the freed
 //   slots and the positions to load, both ascending; the i-th position goes to
 //   the i-th freed slot.  Slot map and bitmap are then updated in place.
+// plan_bm_kernel  the same where a bitmap of S fits LDS (below): bit tests instead of
+//   the binary search, and the resident bitmap rewritten from it.
 // plan_lag1_kernel  the same for the pipelined loop (see below).
 // copy_kernel  a grid-stride gather over (layer, instance, entry, 16-byte
 //   vector): every lane reads 16 bytes of a K||V row straight from pinned,
@@ -112,6 +114,93 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     ls[i] = v ? sF[i] : -1;
   }
   if (tid == 0) load_count[inst] = (int32_t)nl;
+}
+
+// The plan when a bitmap of the new selection fits LDS (the common case): a slot is
+// kept iff its position's bit is set (one LDS read instead of a binary search), and
+// since every position of S is resident after the step, the resident bitmap is
+// rewritten whole from that bitmap (coalesced stores, no atomics).  Slot map entries
+// and selection entries are read into registers (CPT contiguous ones per thread);
+// one block scan of packed 16-bit counts orders both compactions.
+template <int CPT>
+__global__ __launch_bounds__(kPlanThreads) void plan_bm_kernel(const int32_t* __restrict__ sel_idx,
+                                                               const int32_t* __restrict__ sel_count,
+                                                               int32_t* __restrict__ slot_pos,
+                                                               uint32_t* __restrict__ resident_bm,
+                                                               int32_t* __restrict__ load_pos,
+                                                               int32_t* __restrict__ load_slot,
+                                                               int32_t* __restrict__ load_count, int K, int bm_words) {
+  extern __shared__ int32_t lds[];
+  int32_t* sL = lds;                                       // positions to load, ascending [K]
+  int32_t* sF = sL + K;                                    // freed slots, ascending [K]
+  uint32_t* sB = reinterpret_cast<uint32_t*>(sF + K);      // bitmap of S [bm_words]
+  __shared__ uint32_t scan_smem[16];
+
+  const int inst = blockIdx.x;
+  const int tid = threadIdx.x;
+  int c = sel_count[inst];
+  c = c < 0 ? 0 : (c > K ? K : c);
+  const int32_t* S = sel_idx + (size_t)inst * K;
+  int32_t* sp = slot_pos + (size_t)inst * K;
+  uint32_t* bm = resident_bm + (size_t)inst * bm_words;
+  const int32_t pos_end = bm_words * 32;                   // positions outside [0, pos_end) are never loaded
+
+  const int Cx = (K + kPlanThreads - 1) / kPlanThreads;   // <= CPT
+  const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
+  const int Ci = (c + kPlanThreads - 1) / kPlanThreads;   // <= Cx
+  const int i0 = min(tid * Ci, c), i1 = min(i0 + Ci, c);
+  int32_t pos[CPT], sel[CPT];
+  uint32_t oldw[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    pos[u] = x0 + u < x1 ? sp[x0 + u] : -1;
+    sel[u] = i0 + u < i1 ? S[i0 + u] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {                          // resident before the step (outside: never loaded)
+    const int32_t j = sel[u];
+    oldw[u] = j >= 0 && j < pos_end ? bm[j >> 5] : 0xFFFFFFFFu;
+  }
+  for (int w = tid; w < bm_words; w += kPlanThreads) sB[w] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int32_t j = sel[u];
+    if (j >= 0 && j < pos_end) atomicOr(&sB[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  uint32_t fmask = 0u, lmask = 0u, nf_loc = 0u, nl_loc = 0u;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int32_t q = pos[u];
+    const bool keep = q >= 0 && q < pos_end && ((sB[q >> 5] >> (q & 31)) & 1u);
+    if (x0 + u < x1 && !keep) { fmask |= 1u << u; ++nf_loc; }
+    const int32_t j = sel[u];
+    if (i0 + u < i1 && !((oldw[u] >> (j & 31)) & 1u)) { lmask |= 1u << u; ++nl_loc; }
+  }
+  uint32_t tot;
+  const uint32_t before = block_excl_scan(nf_loc | (nl_loc << 16), scan_smem, tot);   // counts <= K < 2^16
+  uint32_t fo = before & 0xFFFFu, lo = before >> 16;
+  const int nf = (int)(tot & 0xFFFFu), nl = (int)(tot >> 16);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    if ((fmask >> u) & 1u) sF[fo++] = x0 + u;
+    if ((lmask >> u) & 1u) sL[lo++] = sel[u];
+  }
+  __syncthreads();
+
+  // apply: the i-th position to load goes to the i-th freed slot, the rest empty; the
+  // resident set becomes S
+  for (int i = tid; i < nf; i += kPlanThreads) sp[sF[i]] = i < nl ? sL[i] : -1;
+  for (int w = tid; w < bm_words; w += kPlanThreads) bm[w] = sB[w];
+  int32_t* lp = load_pos + (size_t)inst * K;
+  int32_t* ls = load_slot + (size_t)inst * K;
+  for (int i = tid; i < K; i += kPlanThreads) {
+    const bool v = i < nl;
+    lp[i] = v ? sL[i] : -1;
+    ls[i] = v ? sF[i] : -1;
+  }
+  if (tid == 0) load_count[inst] = nl;
 }
 
 // The plan of the pipelined loop: the target model attends over the current
@@ -296,9 +385,26 @@ hipError_t launch_plan(const spc_shape& s, const int32_t* sel_idx, const int32_t
                        uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
                        hipStream_t st) {
   const int bm_words = (s.max_len + 31) / 32;
-  plan_kernel<<<dim3(s.batch * s.n_groups), kPlanThreads, 0, st>>>(sel_idx, sel_count, slot_pos, resident_bm,
-                                                                   load_pos, load_slot, load_count, s.budget,
-                                                                   bm_words);
+  const dim3 grid(s.batch * s.n_groups);
+  const size_t lds = (size_t)(2 * s.budget + bm_words) * sizeof(int32_t);
+  const int cpt = (s.budget + kPlanThreads - 1) / kPlanThreads;
+  if (lds <= kPlanBmLdsBytes) {
+    switch (cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8) {
+#define SPC_CASE(N)                                                                                           \
+  case N:                                                                                                     \
+    plan_bm_kernel<N><<<grid, kPlanThreads, lds, st>>>(sel_idx, sel_count, slot_pos, resident_bm, load_pos,   \
+                                                       load_slot, load_count, s.budget, bm_words);            \
+    break;
+      SPC_CASE(1)
+      SPC_CASE(2)
+      SPC_CASE(4)
+      SPC_CASE(8)
+#undef SPC_CASE
+    }
+  } else {
+    plan_kernel<<<grid, kPlanThreads, 0, st>>>(sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,
+                                               load_count, s.budget, bm_words);
+  }
   return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
 
 // ---- stage 3: elastic plan / copy / reset
 constexpr int kPlanMaxBudget = 8192;
+constexpr size_t kPlanBmLdsBytes = 65536;  // the bitmap plan: two K-lists + the bitmap of S in LDS
 constexpr int kPlanLag1MaxWords = 16384;   // 3 selections' + 2 pools' int32 in 64 KB of LDS
 constexpr int kCopyMaxInstances = 4096;
 constexpr int kCopyBlocksDefault = 48;   // workgroups of the gather (override: SPC_COPY_BLOCKS)

@@ -290,7 +290,10 @@ def _random_selection_sequence(rng, B, G, L, K, steps):
     return seqs
 
 
-@pytest.mark.parametrize("B,G,L,K", [(2, 3, 5000, 300), (1, 8, 32768, 2048), (1, 1, 9000, 8192), (3, 2, 50, 1)])
+# bitmap plan with 1, 2, 4 and 8 entries per thread; the binary-search plan where the lists and the
+# bitmap of S outgrow 64 KB of LDS (budget 8192; a 2^20-position cache)
+@pytest.mark.parametrize("B,G,L,K", [(2, 3, 5000, 300), (1, 8, 32768, 2048), (1, 2, 65536, 4096), (1, 1, 40000, 6000),
+                                     (1, 1, 9000, 8192), (1, 2, 1 << 20, 1024), (3, 2, 50, 1)])
 def test_plan_bit_exact_over_steps(B, G, L, K):
     rng = np.random.default_rng(B * 1000 + K)
     shape = api.make_shape(B, G, G, G, 128, 128, L, K, 1, "bf16", 1.0)
