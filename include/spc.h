@@ -330,9 +330,11 @@ int spc_offload_thresholds(const spc_mem_model* m, int32_t* threshold /* [n_laye
  * layer l in [layer_begin, layer_end).
  *   q, q_l   device queries, dtype s->dtype, strides q_l (elements).  MLA shapes (head_dim 576):
  *            the float32 absorbed query, strides in float32 elements; kv is the latent
- *            cache with s_kv = 0 (V = the first 512 elements of each latent row), a row
- *            stride of at least 576, and the rows of one head under 2 GiB (SPC_ERR_UNSUPPORTED)
- *   kv, kv_l device K/V store, dtype s->dtype (slots, or a full cache for GATHER)
+ *            cache with s_kv = 0 (V = the first 512 elements of each latent row)
+ *   kv, kv_l device K/V store, dtype s->dtype (slots, or a full cache for GATHER).  The row
+ *            stride s_row must be at least head_dim and v_dim, and the rows of one (sequence,
+ *            layer, head) -- budget rows for SLOTS, max_len for GATHER -- must span under
+ *            2 GiB (they are read through 32-bit ranges); otherwise SPC_ERR_UNSUPPORTED
  *   rows, row_count  see SPC_ROWS_*; row_count is ignored for SLOTS
  *   out      device [B][n_layers][H_q][v_dim] float32; only layers in range are written
  * A group with no rows writes zeros.  Accumulation is float32.

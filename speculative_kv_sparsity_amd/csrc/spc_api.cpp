@@ -273,11 +273,11 @@ int check_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const
   if (s->head_dim == 576 && kv_l->s_kv != 0)
     return fail(SPC_ERR_UNSUPPORTED, "head_dim 576 reads V from the latent row itself (s_kv must be 0)");
   const int eb = elem_bytes(s);
-  if (s->head_dim == 576) {                 // the latent rows of one head are read through a 32-bit range
+  {                                         // one head's rows are read through 32-bit buffer ranges
     const long long span = (long long)(rows_mode == SPC_ROWS_SLOTS ? s->budget : s->max_len) * kv_l->s_row * eb;
-    if (kv_l->s_row < s->head_dim || span >= (1LL << 31))
-      return fail(SPC_ERR_UNSUPPORTED, "head_dim 576: rows of one head span %lld bytes (row stride %lld; limit 2 GiB)",
-                  span, (long long)kv_l->s_row);
+    if (kv_l->s_row < s->head_dim || kv_l->s_row < s->v_dim || span >= (1LL << 31))
+      return fail(SPC_ERR_UNSUPPORTED, "attention: the rows of one head span %lld bytes with row stride %lld "
+                  "(the stride must cover a key and a value row; limit 2 GiB)", span, (long long)kv_l->s_row);
   }
   const int qeb = spc::mla_shape(*s) ? 4 : eb;   // MLA: float32 absorbed query
   if (!aligned16(q) || !aligned16(kv)) return fail(SPC_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");

@@ -37,24 +37,27 @@ constexpr int kLatentTilesLarge = 16;         // (enough instances x splits to f
 struct QL { int64_t b, layer, head; };        // byte strides
 struct KL { int64_t b, layer, head, row, kv; };
 
-// Loads of 4, 8 or 16 bytes for the V layout.
+// Loads of 4, 8 or 16 bytes for the V layout, through a buffer resource (zeros past its range).
 template <int BYTES> struct VLoad;
 template <> struct VLoad<4> {
   uint32_t w[1];
-  __device__ __forceinline__ void load(const char* p) { w[0] = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void load_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  }
 };
 template <> struct VLoad<8> {
   uint32_t w[2];
-  __device__ __forceinline__ void load(const char* p) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
+  __device__ __forceinline__ void load_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    w[0] = (uint32_t)v.x; w[1] = (uint32_t)v.y;
   }
 };
 template <> struct VLoad<16> {
   uint32_t w[4];
-  __device__ __forceinline__ void load(const char* p) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  __device__ __forceinline__ void load_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const Vec16 v = ld16_buffer(r, off);
+    w[0] = v.w[0]; w[1] = v.w[1]; w[2] = v.w[2]; w[3] = v.w[3];
   }
 };
 
@@ -124,24 +127,29 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   __syncthreads();
 
   const char* kbase = kv + b * kl.b + layer * kl.layer + (int64_t)kvh * kl.head;
+  // buffer resources over the head's key rows and value rows (the host keeps each under 2 GiB):
+  // a padding row's offset lies past the range and reads zeros, with no branch
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(kbase), (short)0, (int)((int64_t)max_rows * kl.row), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(kbase + kl.kv), (short)0, (int)((int64_t)max_rows * kl.row), kBufferRsrcWord3);
   const int wrow = wid * RPW;                        // first row of this wave within the split
   int32_t rowk[NI];
   Vec16 kc[NI][CPLK];
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
     rowk[it] = sRow[wrow + it * 8 + rr];
-    if (rowk[it] >= 0) {
-      const char* kr = kbase + (int64_t)rowk[it] * kl.row;
+    const uint32_t off = rowk[it] >= 0 ? (uint32_t)rowk[it] * (uint32_t)kl.row + 16u * p : kBufferOutOfRange;
 #pragma unroll
-      for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16(kr + (p + 8 * c) * 16);
-    }
+    for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16_buffer(krs, off + 128u * c);
   }
   int32_t rowv[NV];
   VLoad<VB> vv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     rowv[i] = sRow[wrow + 2 * i + half];
-    if (rowv[i] >= 0) vv[i].load(kbase + (int64_t)rowv[i] * kl.row + kl.kv + vl * VB);
+    const uint32_t off = rowv[i] >= 0 ? (uint32_t)rowv[i] * (uint32_t)kl.row + vl * VB : kBufferOutOfRange;
+    vv[i].load_buffer(vrs, off);
   }
   Vec16 qv[GQC][CPLK];
 #pragma unroll

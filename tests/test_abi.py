@@ -247,8 +247,8 @@ def test_attention_halves_validation():
     assert lib.spc_attn_merge(ctypes.byref(s), 0, 4, p, need, ctypes.c_void_p(264), None) == L.SPC_ERR_INVALID_ARG
     big = _shape(max_len=1 << 20, budget=200000)                                  # > 1024 splits
     assert lib.spc_attn_merge(ctypes.byref(big), 0, 1, p, 1 << 40, p, None) == L.SPC_ERR_UNSUPPORTED
-    # MLA latent rows are read through a 32-bit range: one head's rows must stay under 2 GiB,
-    # and a row stride below the 576 scored elements is refused
+    # rows are read through 32-bit ranges: one head's rows must stay under 2 GiB, and a row stride
+    # below the key or value width is refused (MLA latent rows here; the GQA case below)
     for max_len, row, ok in ((1 << 20, 576, True), (1 << 21, 576, False), (4096, 512, False)):
         mla = _shape(batch=1, n_q_heads=16, n_kv_heads=1, n_groups=16, head_dim=576, v_dim=512, max_len=max_len,
                      budget=2048, scale=192 ** -0.5)
@@ -257,6 +257,14 @@ def test_attention_halves_validation():
         mkl = L.SpcKvLayout(max_len * row, 0, 0, row, 0)
         rc = lib.spc_attn_partial(ctypes.byref(mla), p, ctypes.byref(mql), p, ctypes.byref(mkl), p, p,
                                   L.SPC_ROWS_GATHER, 0, 1, p, need_m - 1, None)
+        assert rc == (L.SPC_ERR_WORKSPACE if ok else L.SPC_ERR_UNSUPPORTED), (max_len, row, rc)
+    for max_len, row, ok in ((1 << 21, 256, True), (1 << 22, 128, True), (1 << 23, 128, False), (1 << 22, 256, False),
+                             (4096, 96, False)):
+        g = _shape(max_len=max_len, budget=2048)
+        need_g = lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(g))
+        gkl = L.SpcKvLayout(0, 0, 0, row, row // 2 if row == 256 else 0)
+        rc = lib.spc_attn_partial(ctypes.byref(g), p, ctypes.byref(ql), p, ctypes.byref(gkl), p, p,
+                                  L.SPC_ROWS_GATHER, 0, 1, p, need_g - 1, None)
         assert rc == (L.SPC_ERR_WORKSPACE if ok else L.SPC_ERR_UNSUPPORTED), (max_len, row, rc)
 
 
