@@ -8,7 +8,10 @@
 // attn_split_kernel  split-K: one workgroup per (b, layer, group, head chunk,
 //   split of 64 or 128 rows).  The GQC query heads of the chunk share every
 //   K/V row read.  Every lane issues ALL of its K and V loads up front, so a
-//   workgroup has its whole tile in flight at once.
+//   workgroup has its whole tile in flight at once.  The loads go through
+//   buffer resources over the head's rows: a padding row (empty slot, past the
+//   count) gets an offset past the range and reads zeros, so no load waits
+//   behind a branch.
 //     K: 8 lanes per row (lane p holds the 16-byte chunks p, p+8, ...; one wave
 //        load covers 8 rows x 128 contiguous bytes); v_dot2_f32_bf16 on packed
 //        pairs and DPP 8-lane sums give every lane of the group the logits.

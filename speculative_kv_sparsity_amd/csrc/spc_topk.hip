@@ -7,8 +7,11 @@
 //     (blog section 2: at most K positions per head per round; the lower index
 //      wins a tie)
 //
-// Each fp32 value becomes an order-preserving uint32 key; the K-th largest key
-// T is found by radix select over 8 + 12 + 12 bits.
+// Each fp32 value becomes an order-preserving uint32 key (-0 and +0 are one
+// value); the K-th largest key T is found by radix select over 8 + 12 + 12 bits,
+// or, for raw logits staged in LDS, 12 + 12 + 8 bits (a 12-bit first digit --
+// sign, exponent and three mantissa bits -- spreads logits over many bins, so
+// the first histogram's LDS atomics rarely collide).
 //
 // The scores may also arrive in log-domain form (logits plus each head's
 // per-tile max and sum of exp): the group max is then taken over
@@ -24,7 +27,7 @@
 // topk_select_kernel  one 1024-thread workgroup per (b, g): sums the chunk
 //   histograms (first digit; with one head per group and rows that fit LDS the
 //   select counts it from its staged keys and no keys pass runs), runs the two
-//   remaining 12-bit passes with LDS
+//   remaining passes with LDS
 //   histograms over the keys that still match the prefix, and compacts every j
 //   with key > T plus the lowest-index `need` ones with key == T, ascending,
 //   with two block scans over per-thread contiguous index ranges.  For
