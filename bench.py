@@ -26,6 +26,8 @@ sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
+import itertools
 import json
 import os
 import sys
@@ -39,6 +41,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 HOST_LINK_PEAK_GBS = 63.0      # PCIe Gen5 x16 per direction: 32 GT/s x 16 x 128/130 / 8
+LLC_BYTES = 256 << 20          # MI355X last-level cache (Infinity Cache)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 WORKLOADS = {
@@ -148,13 +151,25 @@ def roof(bound, amount, ms, peak, unit, kernel, calls, traffic=None):
     return rec
 
 
+def rotation(*ts, min_bytes=2 * LLC_BYTES):
+    """A function that hands out, call by call in turn, copies of the given device tensors, with
+    enough copies that one round touches min_bytes.  An isolated call replayed over them reads its
+    inputs from HBM, as in a step (the step's other traffic has pushed them out of the last-level
+    cache by their next use), instead of from the cache a replay of one buffer would hit."""
+    size = sum(t.numel() * t.element_size() for t in ts)
+    n = max(2, -(-min_bytes // size))
+    it = itertools.cycle([ts] + [tuple(t.clone() for t in ts) for _ in range(n - 1)])
+    return lambda: next(it)
+
+
 def probs_call(torch, api, shape, q, k, lengths):
     """A launcher of the probability form of stage 1 (spc_retrieval_scores: logits, then the
-    normalize pass), with its own output and workspace.  The step ranks the log-domain form; this
-    one is measured beside it."""
+    normalize pass), with its own output and workspace, over rotating copies of the keys.  The step
+    ranks the log-domain form; this one is measured beside it."""
     probs = torch.empty((shape.batch, shape.n_q_heads, shape.max_len), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, shape)), dtype=torch.uint8, device="cuda")
-    return lambda st: api.spc_retrieval_scores(shape, q, k, lengths, probs, ws=ws, stream=st)
+    kr = rotation(k)
+    return lambda st: api.spc_retrieval_scores(shape, q, kr()[0], lengths, probs, ws=ws, stream=st)
 
 
 def calibration_copies(torch):
@@ -276,32 +291,37 @@ def bench_gqa(args, p, torch, W):
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / K_
 
-    # instrumented pass: per-stage event times and the rows actually moved
-    stage = {k: [] for k in ("scores", "topk", "plan", "copy", "attn", "attn_resident")}
-    loaded_rows, sel_rows = [], []
-    nch = len(dec.chunks)
-    for t in range(t0 + Wm + K_, t0 + total):
+    # instrumented pass: K more steps, launched back to back like the timed ones (no synchronize
+    # between steps), with events around every stage call and inside each attention call at its
+    # merge; the rows moved are summed on the device and read at the end
+    timers = []
+    moved = torch.zeros((K_, 2), dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    for i, t in enumerate(range(t0 + Wm + K_, t0 + total)):
         tm = StageTimer()
         step(t, tm)
-        torch.cuda.synchronize()
-        stage["scores"].append(tm.ms("scores", "topk"))
-        stage["topk"].append(tm.ms("topk", "plan"))
-        stage["plan"].append(tm.ms("plan", "plan_end"))
-        for c in range(len(dec.chunks)):
-            stage["copy"].append(tm.ms(f"copy{c}", f"copy{c}_end"))
-            stage["attn"].append(tm.ms(f"attn{c}", f"attn{c}_end"))
-        if dec.n_res:
-            stage["attn_resident"].append(tm.ms("attn_res", "attn_res_end"))
-        loaded_rows.append(int(dec.load_count.sum().item()))
-        sel_rows.append(int(dec.sel_count.sum().item()))
-    avg = {k: float(np.mean(v)) for k, v in stage.items() if v}
+        moved[i, 0] = dec.load_count.sum()
+        moved[i, 1] = dec.sel_count.sum()
+        timers.append(tm)
+    torch.cuda.synchronize()
     nch = len(dec.chunks)
+    loaded_rows, sel_rows = moved[:, 0].tolist(), moved[:, 1].tolist()
+    spans = {"scores": ("scores", "topk"), "topk": ("topk", "plan"), "plan": ("plan", "plan_end")}
+    for c in range(nch):
+        spans.update({f"copy{c}": (f"copy{c}", f"copy{c}_end"), f"attn{c}": (f"attn{c}", f"attn{c}_end"),
+                      f"attn{c}_split": (f"attn{c}", f"attn{c}_merge")})
+    if dec.n_res:
+        spans.update({"attn_resident": ("attn_res", "attn_res_end"), "attn_resident_split": ("attn_res",
+                                                                                              "attn_res_merge")})
+    avg = {k: float(np.mean([tm.ms(a, z) for tm in timers])) for k, (a, z) in spans.items()}
 
-    # isolated phase: each stage call launched back to back
+    # isolated phase: each stage call launched back to back, the HBM-bound ones over rotating copies
+    # of their inputs (cold in the last-level cache, as in a step)
     tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
     R = args.iso_reps
+    dk = rotation(dec.dlm_k)
     iso_ms = {
-        "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dec.dlm_k, tl, dec.logits,
+        "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dk()[0], tl, dec.logits,
                                                                  dec.tile_stats, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
                                                                     dec.sel_idx, dec.sel_count, ws=dec.ws_topk,
@@ -310,11 +330,12 @@ def bench_gqa(args, p, torch, W):
     }
     if nch:
         c0a, c0z = dec.chunks[0]
+        kv = rotation(dec.dev_kv)
         iso_ms["attn"] = iso(torch, lambda st: api.spc_sparse_decode_attn(
-            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
+            dec.shape, tq, dec.q_l, kv()[0], dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
             dec.out, ws=dec.ws_attn[0], stream=st), R)
         iso_ms["attn_partial"] = iso(torch, lambda st: api.spc_attn_partial(
-            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
+            dec.shape, tq, dec.q_l, kv()[0], dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
             dec.ws_attn[0], stream=st), R)
         iso_ms["copy"] = iso(torch, lambda st: api.spc_elastic_update(
             dec.shape, None, None, None, None, dec.load_pos, dec.load_slot, dec.load_count, dec.host_kv, dec.host_l,
@@ -322,16 +343,22 @@ def bench_gqa(args, p, torch, W):
             max(5, R // 3))   # rewrites the same slots
     else:                     # every layer on the GPU: the gather from the full cache is the attention
         c0a, c0z = 0, dec.n_res
-        iso_ms["attn"] = iso(torch, lambda st: dec.attend_resident(tq, st), R)
+        fk = rotation(dec.full_kv)
+        iso_ms["attn"] = iso(torch, lambda st: api.spc_sparse_decode_attn(
+            dec.shape, tq, dec.q_l, fk()[0], dec.full_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0,
+            dec.n_res, dec.out, ws=dec.ws_attn[0], stream=st), R)
         iso_ms["attn_partial"] = iso(torch, lambda st: api.spc_attn_partial(
-            dec.shape, tq, dec.q_l, dec.full_kv, dec.full_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0,
+            dec.shape, tq, dec.q_l, fk()[0], dec.full_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0,
             dec.n_res, dec.ws_attn[0], stream=st), R)
     # the retrieval head's front end (upstream of the step): new tokens -> query, key appended
     fw = W.generate_front(p, device="cuda", seed=args.seed, steps=1)
-    head = RetrievalHead(dec.shape, fw)
+    heads = rotation(fw.wq, fw.wk)
+    heads = [RetrievalHead(dec.shape, dataclasses.replace(fw, wq=wq, wk=wk))
+             for wq, wk in (heads() for _ in range(max(2, -(-2 * LLC_BYTES // (fw.wq.nbytes + fw.wk.nbytes)))))]
+    head = itertools.cycle(heads)
     q_front = torch.empty((p.batch, p.n_q_heads, p.head_dim), dtype=p.torch_dtype, device="cuda")
     tok = torch.as_tensor(fw.tokens[0], device="cuda")
-    iso_ms["front"] = iso(torch, lambda st: head(tok, tl, q_front, dec.dlm_k, stream=st), R)
+    iso_ms["front"] = iso(torch, lambda st: next(head)(tok, tl, q_front, dec.dlm_k, stream=st), R)
 
     eb = p.elem_bytes
     lay0 = c0z - c0a
@@ -358,15 +385,18 @@ def bench_gqa(args, p, torch, W):
     result = _header(args, p, ms_per_step, config)
     rows_of = (", slots of the offloaded layers" if nch else
                ", selected rows gathered from the GPU-resident full cache")
+    cold = "; isolated launches over rotating copies of its inputs, cold in the last-level cache as in a step"
     result["roofline"] = roof("hbm", kv_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
                               "attn_split_kernel (the dominant kernel: split-K partial attention" + rows_of +
-                              "; timed alone through spc_attn_partial)", max(nch, 1), traffic.get("attn_partial"))
+                              ", first layer chunk, timed alone through spc_attn_partial" + cold + ")", max(nch, 1),
+                              traffic.get("attn_partial"))
     result["roofline_attn_call"] = roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
                                         "attn_split_kernel + attn_combine_kernel (spc_sparse_decode_attn: the "
-                                        "whole stage-4 call" + rows_of + ")", max(nch, 1), traffic.get("attn"))
+                                        "whole stage-4 call" + rows_of + cold + ")", max(nch, 1), traffic.get("attn"))
     result["roofline_scores"] = roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
                                      "scores_logits_kernel (stage 1 as the step runs it: logits and per-tile "
-                                     "max / sum exp in one pass over the DLM keys)", 1, traffic.get("scores"))
+                                     "max / sum exp in one pass over the DLM keys" + cold + ")", 1,
+                                     traffic.get("scores"))
     result["roofline_scores_probs"] = roof("hbm", score_bytes, iso_ms["scores_probs"], HBM_PEAK_GBS, "GB/s",
                                            "scores_logits_kernel + scores_normalize_kernel (spc_retrieval_scores: "
                                            "the probabilities written; not on the step's path)", 0,
@@ -374,7 +404,8 @@ def bench_gqa(args, p, torch, W):
     if nch:
         copy_bytes = float(np.mean(loaded_rows)) * lay0 * row            # host reads per chunk
         result["roofline_host_link"] = roof("host_link", copy_bytes, iso_ms["copy"], HOST_LINK_PEAK_GBS, "GB/s",
-                                            "copy_kernel (elastic host->HBM gather)", nch, traffic.get("copy"))
+                                            "copy_kernel (elastic host->HBM gather, first layer chunk)", nch,
+                                            traffic.get("copy"))
     result["roofline_front_end"] = roof("hbm", front_bytes, iso_ms["front"], HBM_PEAK_GBS, "GB/s",
                                         "front_gemv_kernel + front_finish_kernel (retrieval-head front end: "
                                         f"embedding, input norm, Q/K projection of hidden {fw.hidden}, YaRN rotary, "
@@ -439,17 +470,18 @@ def bench_lag1(args, p, torch, W):
     tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
     R = args.iso_reps
     nx = (dec.t - 1) % 2
+    dk, kv = rotation(dec.dlm_k), rotation(dec.dev_kv)
     iso_ms = {
-        "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dec.dlm_k, tl, dec.logits,
+        "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dk()[0], tl, dec.logits,
                                                                  dec.tile_stats, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
                                                                     dec.sel[nx], dec.cnt[nx], ws=dec.ws_topk,
                                                                     stream=st), R),
         "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
-            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
+            dec.shape, tq, dec.q_l, kv()[0], dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
             0, p.n_layers, dec.out, ws=dec.ws_attn, stream=st), R),
         "attn_partial": iso(torch, lambda st: api.spc_attn_partial(
-            dec.shape, tq, dec.q_l, dec.dev_kv, dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
+            dec.shape, tq, dec.q_l, kv()[0], dec.dev_l, dec.attend_rows, dec.attend_count, api.SPC_ROWS_GATHER,
             0, p.n_layers, dec.ws_attn, stream=st), R),
         "copy": iso(torch, lambda st: api.spc_elastic_update(
             dec.pool_shape, None, None, None, None, dec.load_pos[nx], dec.load_slot[nx], dec.load_count[nx],
@@ -512,37 +544,49 @@ def bench_mla(args, p, torch, W):
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / K_
 
+    # instrumented pass: K more steps launched back to back (no synchronize between steps), events
+    # around every stage call and at the attention's merge; counts summed on the device
     names = ("absorb", "scores", "topk", "plan", "attn", "out_proj", "end")
-    stage = {k: [] for k in names[:-1]}
-    churn, sel_rows, union_rows = [], [], []
-    for t in range(Wm + K_, total):
+    timers = []
+    moved = torch.zeros((K_, 3), dtype=torch.int64, device="cuda")
+    mark = torch.zeros((p.batch, p.max_len + 1), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for i, t in enumerate(range(Wm + K_, total)):
         tm = StageTimer()
         dec.step(qn[t], qr[t], lens[t], timer=tm)
-        torch.cuda.synchronize()
-        for a, z in zip(names[:-1], names[1:]):
-            stage[a].append(tm.ms(a, z))
-        churn.append(int(dec.load_count.sum().item()))
-        sel_rows.append(int(dec.sel_count.sum().item()))
+        moved[i, 0] = dec.load_count.sum()
+        moved[i, 1] = dec.sel_count.sum()
         # distinct latent rows selected by any head of a sequence: what the attention must read at least once
-        union_rows.append(sum(int(torch.unique(x[x >= 0]).numel()) for x in dec.sel_idx))
-    avg = {k: float(np.mean(v)) for k, v in stage.items()}
+        idx = torch.where(dec.sel_idx >= 0, dec.sel_idx, p.max_len).reshape(p.batch, -1).long()
+        mark.zero_()
+        mark.scatter_(1, idx, 1)
+        moved[i, 2] = mark[:, :p.max_len].sum()
+        timers.append(tm)
+    torch.cuda.synchronize()
+    churn, sel_rows, union_rows = (moved[:, j].tolist() for j in range(3))
+    spans = dict(zip(names[:-1], zip(names[:-1], names[1:])))
+    spans["attn_split"] = ("attn", "attn_merge")
+    avg = {k: float(np.mean([tm.ms(a, z) for tm in timers])) for k, (a, z) in spans.items()}
 
     tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
     R = args.iso_reps
     s = dec.shape
+    uk, uv, lat = rotation(dec.w_uk), rotation(dec.w_uv), rotation(dec.latent)
     iso_ms = {
-        "absorb": iso(torch, lambda st: api.spc_mla_absorb_q(s, p.nope_dim, dec.w_uk, tq, tr, dec.q_abs,
+        "absorb": iso(torch, lambda st: api.spc_mla_absorb_q(s, p.nope_dim, uk()[0], tq, tr, dec.q_abs,
                                                              stream=st), R),
-        "scores": iso(torch, lambda st: api.spc_retrieval_logits(s, dec.q_abs, dec.latent, tl, dec.logits,
+        "scores": iso(torch, lambda st: api.spc_retrieval_logits(s, dec.q_abs, lat()[0], tl, dec.logits,
                                                                  dec.tile_stats, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(s, dec.logits, None, tl, dec.sel_idx,
                                                                     dec.sel_count, ws=dec.ws_topk, stream=st), R),
         "scores_probs": iso(torch, probs_call(torch, api, s, dec.q_abs, dec.latent, tl), R),
-        "attn": iso(torch, lambda st: dec.attend(st), R),
+        "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
+            s, dec.q_abs, dec.q_l, lat()[0], dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0, 1,
+            dec.o_lat, ws=dec.ws_attn, stream=st), R),
         "attn_partial": iso(torch, lambda st: api.spc_attn_partial(
-            s, dec.q_abs, dec.q_l, dec.latent, dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0, 1,
+            s, dec.q_abs, dec.q_l, lat()[0], dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0, 1,
             dec.ws_attn, stream=st), R),
-        "out_proj": iso(torch, lambda st: api.spc_mla_out_proj(s, p.nope_dim, dec.w_uv, dec.o_lat, 0, dec.out,
+        "out_proj": iso(torch, lambda st: api.spc_mla_out_proj(s, p.nope_dim, uv()[0], dec.o_lat, 0, dec.out,
                                                                stream=st), R),
     }
     B, H, L, D = p.batch, p.n_q_heads, p.max_len, p.head_dim
@@ -562,9 +606,10 @@ def bench_mla(args, p, torch, W):
     result = _header(args, p, ms_per_step, config)
     result.update({
         "roofline": dict(roof("hbm", lat_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
-                              "attn_split_latent_kernel (the dominant kernel, timed alone through spc_attn_partial: "
-                              "each head gathers its selected latent rows; a row selected by several heads is "
-                              "counted once here)", 1, traffic.get("attn_partial")),
+                              "attn_split_latent_kernel (the dominant kernel, timed alone through spc_attn_partial "
+                              "over rotating copies of the latent cache: each head gathers its selected latent "
+                              "rows; a row selected by several heads is counted once here)", 1,
+                              traffic.get("attn_partial")),
                          gathered_bytes_per_launch=int(gathered),
                          gathered_GBs=round(gathered / (iso_ms["attn_partial"] * 1e-3) / 1e9, 1)),
         "roofline_attn_call": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
@@ -572,9 +617,10 @@ def bench_mla(args, p, torch, W):
                                    traffic.get("attn")),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                 "mla_scores_kernel (logits and per-tile max / sum exp; bf16 MFMA, fp32 query as "
-                                "a hi/lo bf16 pair: 2 MFMAs per product)", 1),
+                                "a hi/lo bf16 pair: 2 MFMAs per product; rotating copies of the latent cache)", 1),
         "roofline_scores_hbm": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                    "mla_scores_kernel", 1, traffic.get("scores")),
+                                    "mla_scores_kernel (rotating copies of the latent cache)", 1,
+                                    traffic.get("scores")),
         "roofline_scores_probs": roof("hbm", score_bytes, iso_ms["scores_probs"], HBM_PEAK_GBS, "GB/s",
                                       "mla_scores_kernel + scores_normalize_kernel (spc_retrieval_scores: the "
                                       "probabilities written; not on the step's path)", 0,

@@ -168,17 +168,27 @@ class SparseDecoder:
                                self.host_kv, self.host_l, self.dev_kv, self.dev_l, a, z, flags=api.SPC_COPY,
                                plan_stream=self.main, copy_stream=self.main)
 
-    def attend_chunk(self, q: torch.Tensor, c: int, stream=None) -> None:
-        a, z = self.chunks[c]
-        api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.dev_kv, self.dev_l, self.slot_pos, None,
-                                   api.SPC_ROWS_SLOTS, a, z, self.out, ws=self.ws_attn[c + 1],
-                                   stream=self.main if stream is None else stream)
+    def _attend(self, q, kv, kv_l, rows, count, mode, a, z, ws, stream, mark, name) -> None:
+        """One attention call; with `mark`, the same two kernels as two calls (split, then merge) with
+        an event between them, so the split kernel's own time can be read."""
+        st = self.main if stream is None else stream
+        if mark is None:
+            api.spc_sparse_decode_attn(self.shape, q, self.q_l, kv, kv_l, rows, count, mode, a, z, self.out, ws=ws,
+                                       stream=st)
+        else:
+            api.spc_attn_partial(self.shape, q, self.q_l, kv, kv_l, rows, count, mode, a, z, ws, stream=st)
+            mark(name + "_merge", st)
+            api.spc_attn_merge(self.shape, a, z, ws, self.out, stream=st)
 
-    def attend_resident(self, q: torch.Tensor, stream=None) -> None:
+    def attend_chunk(self, q: torch.Tensor, c: int, stream=None, mark=None) -> None:
+        a, z = self.chunks[c]
+        self._attend(q, self.dev_kv, self.dev_l, self.slot_pos, None, api.SPC_ROWS_SLOTS, a, z, self.ws_attn[c + 1],
+                     stream, mark, f"attn{c}")
+
+    def attend_resident(self, q: torch.Tensor, stream=None, mark=None) -> None:
         """Layers still on the GPU: the selected positions gathered from their full cache."""
-        api.spc_sparse_decode_attn(self.shape, q, self.q_l, self.full_kv, self.full_l, self.sel_idx, self.sel_count,
-                                   api.SPC_ROWS_GATHER, 0, self.n_res, self.out, ws=self.ws_attn[0],
-                                   stream=self.main if stream is None else stream)
+        self._attend(q, self.full_kv, self.full_l, self.sel_idx, self.sel_count, api.SPC_ROWS_GATHER, 0, self.n_res,
+                     self.ws_attn[0], stream, mark, "attn_res")
 
     # --- one step -----------------------------------------------------------------------
     def step_tokens(self, head: RetrievalHead, tokens: torch.Tensor, lengths: torch.Tensor,
@@ -199,8 +209,9 @@ class SparseDecoder:
         """q: device [B][H_q][d]; lengths: device int32 [B].  Asynchronous.
 
         ``timer`` (optional) brackets every stage call with events on the
-        stream the stage runs on."""
+        stream the stage runs on, and splits each attention call at its merge."""
         mark = timer.mark if timer is not None else (lambda name, stream: None)
+        split = timer.mark if timer is not None else None
         mark("scores", self.main)
         self.scores(q, lengths)
         mark("topk", self.main)
@@ -214,12 +225,12 @@ class SparseDecoder:
                 self.ev_sel.record(self.main)
                 self.side.wait_event(self.ev_sel)
                 mark("attn_res", self.side)
-                self.attend_resident(q, self.side)
+                self.attend_resident(q, self.side, split)
                 mark("attn_res_end", self.side)
                 side_used = True
             else:
                 mark("attn_res", self.main)
-                self.attend_resident(q)
+                self.attend_resident(q, mark=split)
                 mark("attn_res_end", self.main)
         last = len(self.chunks) - 1
         for c in range(len(self.chunks)):
@@ -230,12 +241,12 @@ class SparseDecoder:
                 self.ev_copy[c].record(self.main)
                 self.side.wait_event(self.ev_copy[c])
                 mark(f"attn{c}", self.side)
-                self.attend_chunk(q, c, self.side)
+                self.attend_chunk(q, c, self.side, split)
                 mark(f"attn{c}_end", self.side)
                 side_used = True
         if self.chunks:
             mark(f"attn{last}", self.main)
-            self.attend_chunk(q, last)
+            self.attend_chunk(q, last, mark=split)
             mark(f"attn{last}_end", self.main)
         if side_used:
             self.ev_attn.record(self.side)
@@ -418,16 +429,23 @@ class MlaDecoder:
         api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
                                self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)
         mark("attn", st)
-        self.attend()
+        self.attend(mark=timer.mark if timer is not None else None)
         mark("out_proj", st)
         api.spc_mla_out_proj(s, self.p.nope_dim, self.w_uv, self.o_lat, 0, self.out, stream=st)
         mark("end", st)
 
-    def attend(self, stream=None) -> None:
-        """Attention of every head over its selected latent rows (gathered by position)."""
-        api.spc_sparse_decode_attn(self.shape, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx,
-                                   self.sel_count, api.SPC_ROWS_GATHER, 0, 1, self.o_lat, ws=self.ws_attn,
-                                   stream=self.main if stream is None else stream)
+    def attend(self, stream=None, mark=None) -> None:
+        """Attention of every head over its selected latent rows (gathered by position); with `mark`,
+        as its split and merge halves with an event "attn_merge" between them."""
+        st = self.main if stream is None else stream
+        args = (self.shape, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx, self.sel_count,
+                api.SPC_ROWS_GATHER, 0, 1)
+        if mark is None:
+            api.spc_sparse_decode_attn(*args, self.o_lat, ws=self.ws_attn, stream=st)
+        else:
+            api.spc_attn_partial(*args, self.ws_attn, stream=st)
+            mark("attn_merge", st)
+            api.spc_attn_merge(self.shape, 0, 1, self.ws_attn, self.o_lat, stream=st)
 
 
 class MlaLiteralDecoder(MlaDecoder):

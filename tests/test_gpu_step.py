@@ -24,10 +24,10 @@ def _run_and_check(p, steps, layer_chunks=4, seed=0, delay_cycles=0, check_layer
             torch.cuda._sleep(delay_cycles)
             copy_chunk(c)
 
-        def slow_attend(q, c, stream=None):
+        def slow_attend(q, c, stream=None, mark=None):
             with torch.cuda.stream(stream if stream is not None else dec.main):
                 torch.cuda._sleep(delay_cycles)
-            attend_chunk(q, c, stream)
+            attend_chunk(q, c, stream, mark)
 
         dec.copy_chunk, dec.attend_chunk = slow_copy, slow_attend
     ora = OracleDecoder(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.budget, p.scale, p.dtype)
