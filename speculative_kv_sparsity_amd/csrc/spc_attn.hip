@@ -11,7 +11,7 @@
 //   workgroup has its whole tile in flight at once.  The loads go through
 //   buffer resources over the head's rows: a padding row (empty slot, past the
 //   count) gets an offset past the range and reads zeros, so no load waits
-//   behind a branch.
+//   behind a branch.  They are nontemporal (each row is read once per step).
 //     K: 8 lanes per row (lane p holds the 16-byte chunks p, p+8, ...; one wave
 //        load covers 8 rows x 128 contiguous bytes); v_dot2_f32_bf16 on packed
 //        pairs and DPP 8-lane sums give every lane of the group the logits.
@@ -40,26 +40,27 @@ constexpr int kLatentTilesLarge = 16;         // (enough instances x splits to f
 struct QL { int64_t b, layer, head; };        // byte strides
 struct KL { int64_t b, layer, head, row, kv; };
 
-// Loads of 4, 8 or 16 bytes for the V layout, through a buffer resource (zeros past its range).
+// Loads of 4, 8 or 16 bytes for the V layout, through a buffer resource (zeros past its range),
+// nontemporal: the split kernel reads each slot row once per step.
 template <int BYTES> struct VLoad;
 template <> struct VLoad<4> {
   uint32_t w[1];
   __device__ __forceinline__ void load_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kLoadNontemporal);
   }
 };
 template <> struct VLoad<8> {
   uint32_t w[2];
   __device__ __forceinline__ void load_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     typedef int v2i __attribute__((ext_vector_type(2)));
-    const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLoadNontemporal);
     w[0] = (uint32_t)v.x; w[1] = (uint32_t)v.y;
   }
 };
 template <> struct VLoad<16> {
   uint32_t w[4];
   __device__ __forceinline__ void load_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const Vec16 v = ld16_buffer(r, off);
+    const Vec16 v = ld16_buffer<kLoadNontemporal>(r, off);
     w[0] = v.w[0]; w[1] = v.w[1]; w[2] = v.w[2]; w[3] = v.w[3];
   }
 };
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     rowk[it] = sRow[wrow + it * 8 + rr];
     const uint32_t off = rowk[it] >= 0 ? (uint32_t)rowk[it] * (uint32_t)kl.row + 16u * p : kBufferOutOfRange;
 #pragma unroll
-    for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16_buffer(krs, off + 128u * c);
+    for (int c = 0; c < CPLK; ++c) kc[it][c] = ld16_buffer<kLoadNontemporal>(krs, off + 128u * c);
   }
   int32_t rowv[NV];
   VLoad<VB> vv[NV];

@@ -29,9 +29,12 @@ __device__ __forceinline__ Vec16 ld16(const void* p) {
 // for gfx9-family parts: 32-bit data format, no swizzle.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // past any range the host allows (< 2 GiB)
+// AUX: the load's cache-policy bits (2: nontemporal, for data read once).
+constexpr int kLoadNontemporal = 2;
+template <int AUX = 0>
 __device__ __forceinline__ Vec16 ld16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef int v4i __attribute__((ext_vector_type(4)));
-  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
   Vec16 o;
   o.w[0] = (uint32_t)v.x; o.w[1] = (uint32_t)v.y; o.w[2] = (uint32_t)v.z; o.w[3] = (uint32_t)v.w;
   return o;

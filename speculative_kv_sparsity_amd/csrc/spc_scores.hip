@@ -69,6 +69,11 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
     }
 
   const char* kb = k + ((size_t)b * Hkv + g) * (size_t)max_len * RB;
+  // the sequence's n key rows through a buffer resource (under 2 GiB, checked on the host): rows
+  // past the length read zeros with no branch; the loads are marked nontemporal (each key row is
+  // read once per step, so it need not stay in the caches)
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb), (short)0, n * RB, kBufferRsrcWord3);
   __shared__ __align__(16) float slg[HC][kScoreTile];   // the tile's logits per head, for coalesced writes
   float lg[kIters];
 
@@ -78,10 +83,9 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int row = row0 + (u0 + u) * kRowsPerIter + wid * 8 + rr;
-      if (row < n) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) kv[u][c] = ld16(kb + (size_t)row * RB + (p + 8 * c) * 16);
-      }
+      for (int c = 0; c < CPL; ++c)
+        kv[u][c] = ld16_buffer<kLoadNontemporal>(krs, (uint32_t)(row * RB + (p + 8 * c) * 16));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -236,6 +240,9 @@ bool mla_shape(const spc_shape& s) { return s.head_dim == kMlaLatent + kMlaRope;
 bool scores_supported(const spc_shape& s) {
   if (mla_shape(s))   // MFMA path: one latent head shared by 16..128 query heads, bf16 latent
     return s.dtype == SPC_BF16 && s.n_kv_heads == 1 && s.n_q_heads % 16 == 0 && s.n_q_heads <= 128;
+  // one KV head's keys of a sequence are read through a 32-bit buffer range: under 2 GiB
+  const long long span = (long long)s.max_len * s.head_dim * (s.dtype == SPC_F32 ? 4 : 2);
+  if (span >= (1LL << 31)) return false;
   if (s.dtype == SPC_F32) return s.head_dim == 128 || s.head_dim == 64;
   return s.head_dim == 64 || s.head_dim == 128 || s.head_dim == 256;
 }

@@ -211,6 +211,9 @@ def test_log_domain_scoring_sizes_and_validation():
     assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, None, None) == L.SPC_ERR_INVALID_ARG
     assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, ctypes.c_void_p(260), None) == L.SPC_ERR_INVALID_ARG
     assert lib.spc_retrieval_logits(ctypes.byref(_shape(head_dim=96)), p, p, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
+    # one KV head's keys are read through a 32-bit range: 2^23 bf16 rows of 128 reach 2 GiB
+    assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 23)), p, p, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
+    assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 22)), p, p, p, p, None, None) == L.SPC_ERR_INVALID_ARG
     need = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s))
     # four heads per group: the tile stats are required
     assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, None, p, p, p, p, need, None) == L.SPC_ERR_INVALID_ARG
