@@ -151,6 +151,12 @@ def roof(bound, amount, ms, peak, unit, kernel, calls, traffic=None):
     return rec
 
 
+def resident(*ts):
+    """rotation()'s counterpart for inputs that a step keeps in the last-level cache: always the same
+    tensors."""
+    return lambda: ts
+
+
 def rotation(*ts, min_bytes=2 * LLC_BYTES):
     """A function that hands out, call by call in turn, copies of the given device tensors, with
     enough copies that one round touches min_bytes.  An isolated call replayed over them reads its
@@ -162,13 +168,13 @@ def rotation(*ts, min_bytes=2 * LLC_BYTES):
     return lambda: next(it)
 
 
-def probs_call(torch, api, shape, q, k, lengths):
+def probs_call(torch, api, shape, q, k, lengths, inputs=rotation):
     """A launcher of the probability form of stage 1 (spc_retrieval_scores: logits, then the
-    normalize pass), with its own output and workspace, over rotating copies of the keys.  The step
-    ranks the log-domain form; this one is measured beside it."""
+    normalize pass), with its own output and workspace, over rotating (or resident) copies of the
+    keys.  The step ranks the log-domain form; this one is measured beside it."""
     probs = torch.empty((shape.batch, shape.n_q_heads, shape.max_len), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(16, api.spc_workspace_size(api.SPC_CALL_SCORES, shape)), dtype=torch.uint8, device="cuda")
-    kr = rotation(k)
+    kr = inputs(k)
     return lambda st: api.spc_retrieval_scores(shape, q, kr()[0], lengths, probs, ws=ws, stream=st)
 
 
@@ -315,22 +321,29 @@ def bench_gqa(args, p, torch, W):
                                                                                               "attn_res_merge")})
     avg = {k: float(np.mean([tm.ms(a, z) for tm in timers])) for k, (a, z) in spans.items()}
 
-    # isolated phase: each stage call launched back to back, the HBM-bound ones over rotating copies
-    # of their inputs (cold in the last-level cache, as in a step)
+    # isolated phase: each stage call launched back to back.  Where one step moves more than the
+    # last-level cache holds (keys, logits, every layer's selected K/V rows, the rows copied in), a
+    # stage's inputs are gone from the cache by its next use, so the HBM-bound calls are replayed over
+    # rotating copies of their inputs; a smaller step keeps them resident and replays the same ones
     tq, tl = qs[t0 + total - 1], lens[t0 + total - 1]
     R = args.iso_reps
-    dk = rotation(dec.dlm_k)
+    n_step = float(np.mean(w.lengths[t0 + Wm + K_:t0 + total].sum(axis=1)))
+    step_bytes = (n_step * (p.n_kv_heads * p.head_dim * p.elem_bytes + p.n_q_heads * 4)
+                  + float(np.mean(sel_rows)) * p.n_layers * 2 * p.head_dim * p.elem_bytes
+                  + float(np.mean(loaded_rows)) * (p.n_layers - dec.n_res) * 2 * p.head_dim * p.elem_bytes)
+    inputs = rotation if step_bytes > LLC_BYTES else resident
+    dk = inputs(dec.dlm_k)
     iso_ms = {
         "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dk()[0], tl, dec.logits,
                                                                  dec.tile_stats, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
                                                                     dec.sel_idx, dec.sel_count, ws=dec.ws_topk,
                                                                     stream=st), R),
-        "scores_probs": iso(torch, probs_call(torch, api, dec.shape, tq, dec.dlm_k, tl), R),
+        "scores_probs": iso(torch, probs_call(torch, api, dec.shape, tq, dec.dlm_k, tl, inputs), R),
     }
     if nch:
         c0a, c0z = dec.chunks[0]
-        kv = rotation(dec.dev_kv)
+        kv = inputs(dec.dev_kv)
         iso_ms["attn"] = iso(torch, lambda st: api.spc_sparse_decode_attn(
             dec.shape, tq, dec.q_l, kv()[0], dec.dev_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, c0a, c0z,
             dec.out, ws=dec.ws_attn[0], stream=st), R)
@@ -343,7 +356,7 @@ def bench_gqa(args, p, torch, W):
             max(5, R // 3))   # rewrites the same slots
     else:                     # every layer on the GPU: the gather from the full cache is the attention
         c0a, c0z = 0, dec.n_res
-        fk = rotation(dec.full_kv)
+        fk = inputs(dec.full_kv)
         iso_ms["attn"] = iso(torch, lambda st: api.spc_sparse_decode_attn(
             dec.shape, tq, dec.q_l, fk()[0], dec.full_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0,
             dec.n_res, dec.out, ws=dec.ws_attn[0], stream=st), R)
@@ -352,9 +365,9 @@ def bench_gqa(args, p, torch, W):
             dec.n_res, dec.ws_attn[0], stream=st), R)
     # the retrieval head's front end (upstream of the step): new tokens -> query, key appended
     fw = W.generate_front(p, device="cuda", seed=args.seed, steps=1)
-    heads = rotation(fw.wq, fw.wk)
-    heads = [RetrievalHead(dec.shape, dataclasses.replace(fw, wq=wq, wk=wk))
-             for wq, wk in (heads() for _ in range(max(2, -(-2 * LLC_BYTES // (fw.wq.nbytes + fw.wk.nbytes)))))]
+    heads = inputs(fw.wq, fw.wk)
+    ncopy = max(2, -(-2 * LLC_BYTES // (fw.wq.nbytes + fw.wk.nbytes))) if inputs is rotation else 1
+    heads = [RetrievalHead(dec.shape, dataclasses.replace(fw, wq=wq, wk=wk)) for wq, wk in (heads() for _ in range(ncopy))]
     head = itertools.cycle(heads)
     q_front = torch.empty((p.batch, p.n_q_heads, p.head_dim), dtype=p.torch_dtype, device="cuda")
     tok = torch.as_tensor(fw.tokens[0], device="cuda")
@@ -385,7 +398,8 @@ def bench_gqa(args, p, torch, W):
     result = _header(args, p, ms_per_step, config)
     rows_of = (", slots of the offloaded layers" if nch else
                ", selected rows gathered from the GPU-resident full cache")
-    cold = "; isolated launches over rotating copies of its inputs, cold in the last-level cache as in a step"
+    cold = ("; isolated launches over rotating copies of its inputs, cold in the last-level cache as in a step"
+            if inputs is rotation else "")
     result["roofline"] = roof("hbm", kv_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
                               "attn_split_kernel (the dominant kernel: split-K partial attention" + rows_of +
                               ", first layer chunk, timed alone through spc_attn_partial" + cold + ")", max(nch, 1),
@@ -412,6 +426,8 @@ def bench_gqa(args, p, torch, W):
                                         "key append; upstream of the step, not in value)", 1, traffic.get("front"))
     result["stage_us_in_step"] = {k: round(v * 1e3, 2) for k, v in avg.items()}
     result["call_us_isolated"] = {k: round(v * 1e3, 2) for k, v in iso_ms.items()}
+    result["isolated_inputs"] = {"step_bytes": int(step_bytes), "last_level_cache_bytes": LLC_BYTES,
+                                 "replayed_over": "rotating copies" if inputs is rotation else "the same buffers"}
     result["elastic"] = {"rows_loaded_per_step": float(np.mean(loaded_rows)),
                          "rows_selected_per_step": float(np.mean(sel_rows)),
                          "transfer_fraction_vs_full_reload":
@@ -571,7 +587,15 @@ def bench_mla(args, p, torch, W):
     tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
     R = args.iso_reps
     s = dec.shape
-    uk, uv, lat = rotation(dec.w_uk), rotation(dec.w_uv), rotation(dec.latent)
+    # what one step moves: the latent rows, the logits and the two up-projections.  At 32K that is
+    # about 250 MB, which the 256 MB last-level cache holds from one step to the next (the kernels'
+    # durations inside the timed steps match warm replays), so the isolated calls replay resident
+    # inputs; a larger working set gets rotating copies, cold like the GQA steps
+    n_step = float(np.mean(w.lengths[Wm + K_:total].sum(axis=1)))
+    step_bytes = (n_step * p.head_dim * p.elem_bytes + n_step * p.n_q_heads * 4 + dec.w_uk.nbytes
+                  + dec.w_uv.nbytes)
+    inputs = rotation if step_bytes > LLC_BYTES else resident
+    uk, uv, lat = inputs(dec.w_uk), inputs(dec.w_uv), inputs(dec.latent)
     iso_ms = {
         "absorb": iso(torch, lambda st: api.spc_mla_absorb_q(s, p.nope_dim, uk()[0], tq, tr, dec.q_abs,
                                                              stream=st), R),
@@ -579,7 +603,7 @@ def bench_mla(args, p, torch, W):
                                                                  dec.tile_stats, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(s, dec.logits, None, tl, dec.sel_idx,
                                                                     dec.sel_count, ws=dec.ws_topk, stream=st), R),
-        "scores_probs": iso(torch, probs_call(torch, api, s, dec.q_abs, dec.latent, tl), R),
+        "scores_probs": iso(torch, probs_call(torch, api, s, dec.q_abs, dec.latent, tl, inputs), R),
         "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
             s, dec.q_abs, dec.q_l, lat()[0], dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0, 1,
             dec.o_lat, ws=dec.ws_attn, stream=st), R),
@@ -606,9 +630,9 @@ def bench_mla(args, p, torch, W):
     result = _header(args, p, ms_per_step, config)
     result.update({
         "roofline": dict(roof("hbm", lat_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
-                              "attn_split_latent_kernel (the dominant kernel, timed alone through spc_attn_partial "
-                              "over rotating copies of the latent cache: each head gathers its selected latent "
-                              "rows; a row selected by several heads is counted once here)", 1,
+                              "attn_split_latent_kernel (the dominant kernel, timed alone through spc_attn_partial: "
+                              "each head gathers its selected latent rows; a row selected by several heads is "
+                              "counted once here)", 1,
                               traffic.get("attn_partial")),
                          gathered_bytes_per_launch=int(gathered),
                          gathered_GBs=round(gathered / (iso_ms["attn_partial"] * 1e-3) / 1e9, 1)),
@@ -617,16 +641,17 @@ def bench_mla(args, p, torch, W):
                                    traffic.get("attn")),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                 "mla_scores_kernel (logits and per-tile max / sum exp; bf16 MFMA, fp32 query as "
-                                "a hi/lo bf16 pair: 2 MFMAs per product; rotating copies of the latent cache)", 1),
+                                "a hi/lo bf16 pair: 2 MFMAs per product)", 1),
         "roofline_scores_hbm": roof("hbm", score_bytes, iso_ms["scores"], HBM_PEAK_GBS, "GB/s",
-                                    "mla_scores_kernel (rotating copies of the latent cache)", 1,
-                                    traffic.get("scores")),
+                                    "mla_scores_kernel", 1, traffic.get("scores")),
         "roofline_scores_probs": roof("hbm", score_bytes, iso_ms["scores_probs"], HBM_PEAK_GBS, "GB/s",
                                       "mla_scores_kernel + scores_normalize_kernel (spc_retrieval_scores: the "
                                       "probabilities written; not on the step's path)", 0,
                                       traffic.get("scores_probs")),
         "stage_us_in_step": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "call_us_isolated": {k: round(v * 1e3, 2) for k, v in iso_ms.items()},
+        "isolated_inputs": {"step_bytes": int(step_bytes), "last_level_cache_bytes": LLC_BYTES,
+                            "replayed_over": "rotating copies" if inputs is rotation else "the same buffers"},
         "elastic": {"rows_selected_per_step": sel, "distinct_rows_per_step": union,
                     "rows_changed_per_step": float(np.mean(churn)),
                     "resident_churn": round(float(np.mean(churn)) / sel, 4) if sel else None,
@@ -679,11 +704,24 @@ def bench_mla_literal(args, p, torch, W):
     tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
     R = args.iso_reps
     xs = dec.exp_shape
+    # one step reads every head's expanded slots (671 MB at 32K), past the last-level cache: the
+    # attention calls are replayed over rotating copies of the slot store, the expansion over rotating
+    # copies of the latent cache and the up-projections
+    kx = rotation(dec.kv_exp)
+    lx = rotation(dec.latent, dec.w_uk, dec.w_uv)
+
+    def expand(st):
+        lat, uk, uv = lx()
+        api.spc_mla_expand(dec.shape, p.nope_dim, uv.shape[1], lat, uk, uv, dec.load_pos, dec.load_slot,
+                           dec.load_count, kx()[0], tq, tr, dec.q_exp, stream=st)
+
     iso_ms = {
-        "expand": iso(torch, lambda st: dec.expand(tq, tr, st), R),
-        "attn": iso(torch, lambda st: dec.attend(st), R),
+        "expand": iso(torch, expand, R),
+        "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
+            xs, dec.q_exp, dec.exp_q_l, kx()[0], dec.exp_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, 0, 1, dec.out,
+            ws=dec.ws_exp_attn, stream=st), R),
         "attn_partial": iso(torch, lambda st: api.spc_attn_partial(
-            xs, dec.q_exp, dec.exp_q_l, dec.kv_exp, dec.exp_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, 0, 1,
+            xs, dec.q_exp, dec.exp_q_l, kx()[0], dec.exp_l, dec.slot_pos, None, api.SPC_ROWS_SLOTS, 0, 1,
             dec.ws_exp_attn, stream=st), R),
     }
     # the absorbed step on the same inputs, for comparison
