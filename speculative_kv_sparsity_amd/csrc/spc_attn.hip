@@ -279,7 +279,7 @@ template <int D, int DV, int T>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
-    int n_lay, int nsplit, int nhc, int max_rows, float scale, float* __restrict__ part_o,
+    int n_lay, int nsplit, int /*nhc: one head per group*/, int max_rows, float scale, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
   constexpr int EB = 2;
   constexpr int CPLK = D * EB / 16 / 8;              // 16-byte chunks per lane of a row (9)

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
   sum = sum_across_rows8(sum);
   if (rr == 0) s_s[wid][p] = sum;
   __syncthreads();
-  if (threadIdx.x < nh) {
+  if ((int)threadIdx.x < nh) {
     const float S = s_s[0][p] + s_s[1][p] + s_s[2][p] + s_s[3][p];
     part[((size_t)b * Hq + h0 + p) * ntiles + blockIdx.x] = make_float2(M, S);
   }
