@@ -201,7 +201,7 @@ size_t spc_tile_stats_size(const spc_shape* s);
  * Stage 2 - group max and Top-K.
  *   v[b][g][j] = max over the query heads i of group g of probs[b][i][j]
  *   S[b][g]    = the first min(K, n) positions j < n = lengths[b] ordered by
- *                (v desc, j asc): the lower index wins a tie
+ *                (v desc, j asc): the lower index wins a tie (-0.0 and +0.0 are equal values)
  * (blog section 5, GQA element-wise max then per-group Top-K, MQA one group,
  * MHA per head; blog section 2, the KV budget K; paper summary section 4.3.)
  *   probs      device [B][H_q][max_len] float32 (as written by stage 1)
