@@ -159,6 +159,9 @@ def check_topk_edge_cases(topk_select):
     assert list(topk_select(np.arange(5.0), 5, 9)) == [0, 1, 2, 3, 4]         # K >= n: everything
     assert len(topk_select(np.arange(5.0), 0, 3)) == 0                         # n = 0: nothing
     assert list(topk_select(np.array([0.1, 0.9, 0.5, 0.9]), 3, 2)) == [1, 2]   # only j < n counts
+    # -0.0 and +0.0 are one value: a tie, broken by the lower index (not +0 above -0)
+    assert list(topk_select(np.array([0.0, -0.0, -0.0, 0.0]), 4, 2)) == [0, 1]
+    assert list(topk_select(np.array([-1.0, -0.0, 0.0, -2.0]), 4, 1)) == [1]
 
 
 # ----------------------------------------------------------------------------- O4 plan
