@@ -73,10 +73,16 @@ def test_pins_catch_topk_mistakes():
     def ignores_length(s, n, k):
         return O.topk_select(s, len(s), k)[:min(k, n)] if n > 0 else np.zeros(0, dtype=np.int64)
 
+    def signed_zeros_apart(s, n, k):       # ranks +0.0 above -0.0, as a key made of the float's bits would
+        x = np.asarray(s, dtype=np.float64)
+        x = np.where((x == 0) & np.signbit(x), -1e-300, x)
+        return O.topk_select(x, n, k)
+
     for bad in (high_index_wins, ascending_scores, unsorted_output):
         _fails(pins.check_topk_bruteforce, bad)
         _fails(pins.check_topk_python_sorted, bad)
     _fails(pins.check_topk_edge_cases, ignores_length)
+    _fails(pins.check_topk_edge_cases, signed_zeros_apart)
 
 
 def test_pins_catch_plan_mistakes():
