@@ -80,6 +80,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iso-reps", type=int, default=30, help="launches per stage in the isolated phase")
+    ap.add_argument("--kv-heads-per-gpu", type=int, default=None,
+                    help="GQA/MHA: run one tensor-parallel shard of the workload, with this many KV heads (and "
+                         "their query heads) of the model's; every stage is independent per KV head, so a shard "
+                         "is the whole per-GPU path of a multi-GPU step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with three 256 MiB device-to-device copies (counter calibration)")
     return ap.parse_args()
@@ -226,6 +230,14 @@ def main():
 
     torch.cuda.set_device(0)
     p = W.PRESETS[args.config]
+    if args.kv_heads_per_gpu is not None:
+        if p.kind not in ("gqa", "mha") or not 0 < args.kv_heads_per_gpu <= p.n_kv_heads or \
+                p.n_kv_heads % args.kv_heads_per_gpu:
+            print(f"--kv-heads-per-gpu must divide the {p.n_kv_heads} KV heads of a GQA/MHA workload",
+                  file=sys.stderr)
+            sys.exit(2)
+        g = p.n_q_heads // p.n_kv_heads
+        p = p.with_(n_kv_heads=args.kv_heads_per_gpu, n_q_heads=g * args.kv_heads_per_gpu)
     if p.kind == "mla":
         result = bench_mla_literal(args, p, torch, W) if args.mla_literal else bench_mla(args, p, torch, W)
     elif args.lag == 1:
@@ -387,7 +399,8 @@ def bench_gqa(args, p, torch, W):
     full_reload = float(np.mean(sel_rows)) * p.n_layers * row
     off = p.n_layers - dec.n_res                                 # offloaded layers at the end of the run
 
-    traffic = measured_traffic(p.name, nch) if thresholds is None else {}
+    shard = args.kv_heads_per_gpu is not None
+    traffic = measured_traffic(p.name, nch) if thresholds is None and not shard else {}
     config = {"workload": WORKLOADS.get(p.name, p.name), "batch": B, "layers": p.n_layers, "q_heads": Hq,
               "kv_heads": Hkv, "head_dim": d, "cached_tokens": p.max_len,
               "mean_length": round(n_valid / B, 1), "first_step": t0, "kv_budget": K, "layer_chunks": nch,
@@ -395,6 +408,10 @@ def bench_gqa(args, p, torch, W):
     if thresholds is not None:
         config.update({"hbm_gb": args.hbm_gb, "weights_gb": args.weights_gb, "offloaded_layers": off,
                        "offload_thresholds": thresholds})
+    if shard:
+        full = W.PRESETS[p.name].n_kv_heads
+        config["parallelism"] = (f"one of {full // p.n_kv_heads} tensor-parallel shards over KV heads "
+                                 f"({p.n_kv_heads} of {full} per GPU), single GPU")
     result = _header(args, p, ms_per_step, config)
     rows_of = (", slots of the offloaded layers" if nch else
                ", selected rows gathered from the GPU-resident full cache")
