@@ -32,7 +32,7 @@ notation, with no blocking, fusion or reordering:
   O7  statistics            adjacent-step overlap, bytes moved vs full reload
       (blog section 6; paper summary sections 1 and 5.3)
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * lower index wins a tie in the Top-K;
   * the i-th ascending position to load goes to the i-th ascending freed slot;
   * a sequence with n <= K valid positions selects all n; n = 0 selects none
@@ -201,10 +201,11 @@ def elastic_plan(selected: Sequence[int], slot_pos: Sequence[int]) -> Tuple[np.n
 
 def elastic_plan_lag1(current: Sequence[int], nxt: Sequence[int], slot_pos: Sequence[int]
                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
-    """The elastic plan of the pipelined loop (blog section 4: "the retrieval head predicts the
-    positions of the next round while the target model uses the sparse KV prepared last round").
+    """The elastic plan of the pipelined loop (blog section 4: while the target model attends over
+    the sparse KV loaded in the previous iteration, the retrieval head already selects the positions
+    for the following one).
 
-    current: S_t, the selection the target model attends over in this step (loaded last round);
+    current: S_t, the selection the target model attends over in this step (loaded in the previous one);
     nxt:     S_t+1, the selection the retrieval head just made for the next step;
     slot_pos: the pool's slot map before the step (-1 = empty).
     A slot may be overwritten only if its position is in neither selection: the current one is

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bm_kernel(const int32_t* __
 }
 
 // The plan of the pipelined loop: the target model attends over the current
-// selection C (loaded last round) while the next selection N is loaded, so a
+// selection C (loaded in the previous step) while the next selection N is loaded, so a
 // slot of the pool (P >= 2 K slots) is reusable only if its position is in
 // neither; the new positions are N - resident.  Also writes the ascending slots
 // that hold C (the rows the attention of this step gathers).  Same block scans

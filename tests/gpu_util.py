@@ -8,7 +8,7 @@ from oracle import spc_oracle as O
 from speculative_kv_sparsity_amd import api
 from speculative_kv_sparsity_amd.workload import Preset, to_numpy_raw
 
-# Bars of the path (the benchmark spec): attention max-abs 1e-2 for bf16 inputs with
+# Parity bars of the path: attention max-abs 1e-2 for bf16 inputs with
 # fp32 accumulation; a Top-K mismatch only where the oracle score is within
 # 1e-3 (relative) of the K-th score; indices / load lists / slot maps exact.
 ATTN_MAX_ABS = 1e-2
