@@ -233,10 +233,10 @@ int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const flo
                               size_t ws_bytes, void* stream);
 
 /*
- * Stage 3 - elastic loading (blog section 4 pseudocode: to_load = selected -
- * resident_kv_indices, async_prefetch(kv_cache[to_load]); blog section 6
- * worked example {1,8,21,35} -> {1,8,21,50} loads only 50, in place of 35;
- * paper summary section 5.4: fixed budget, in place).
+ * Stage 3 - elastic loading (blog section 4 pseudocode: the positions to load
+ * are the new selection minus the resident ones, fetched asynchronously; blog
+ * section 6 worked example {1,8,21,35} -> {1,8,21,50} loads only 50, in place
+ * of 35; paper summary section 5.4: fixed budget, in place).
  *
  * State, per (b, g), owned by the caller and initialised by spc_elastic_reset:
  *   slot_pos     device [B][n_groups][budget] int32: position held by slot x, or -1

@@ -21,7 +21,7 @@ notation, with no blocking, fusion or reordering:
       (blog section 4 pseudocode; blog section 6 worked example
        {1,8,21,35} -> {1,8,21,50}; paper summary section 5.4 / Figure 7)
   O5  elastic copy          host row -> device slot for every (pos, slot) pair
-      (blog section 4, async_prefetch(kv_cache[to_load]))
+      (blog section 4 pseudocode: only the rows to load are prefetched)
   O6  sparse attention      softmax(q K_S^T / sqrt(d)) V_S over the selected
       positions only, read from the host store BY POSITION
       (blog section 4 pseudocode llm.forward(..., sparse_kv=resident_kv);

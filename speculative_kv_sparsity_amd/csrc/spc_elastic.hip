@@ -1,7 +1,7 @@
 // Stage 3 - elastic loading: plan (set difference, in-place slot reuse) and copy.
 //
-// The SpeContext blog's section 4 loop computes to_load = selected -
-// resident_kv_indices and prefetches only kv_cache[to_load]; its section 6
+// The SpeContext blog's section 4 loop takes the positions to load as the new
+// selection minus the resident ones and prefetches only those rows; its section 6
 // worked example ({1,8,21,35} -> {1,8,21,50}) loads only 50, into the place of
 // 35; the paper summary's section 5.4 keeps the budget fixed and loads in place.
 //
