@@ -274,7 +274,8 @@ int spc_elastic_reset(const spc_shape* s, int32_t batch_index, int32_t* slot_pos
  * Stage 3 for the pipelined loop of the SpeContext blog's section 4 (while the
  * target model attends over the sparse KV loaded in the previous iteration,
  * the retrieval head already selects the positions for the following one;
- * paper summary section 5.4: prior, current and resident selections).  Per (b, group):
+ * paper summary section 5.4: three sets, the previous selection, the current one
+ * and the resident one).  Per (b, group):
  *   keep       = slots whose position is in cur or next (cur is being attended
  *                in this step, next will be);
  *   to_load    = next - resident, ascending, into the ascending remaining slots;

@@ -209,8 +209,8 @@ def elastic_plan_lag1(current: Sequence[int], nxt: Sequence[int], slot_pos: Sequ
     nxt:     S_t+1, the selection the retrieval head just made for the next step;
     slot_pos: the pool's slot map before the step (-1 = empty).
     A slot may be overwritten only if its position is in neither selection: the current one is
-    being read by this step's attention, the next one will be (paper summary section 5.4 tracks
-    the prior, current and resident selections).  Returns (to_load, load_slot, new_slot_pos,
+    being read by this step's attention, the next one will be (paper summary section 5.4 keeps three
+    sets: the previous selection, the current one and what is resident).  Returns (to_load, load_slot, new_slot_pos,
     attend_slots): to_load = sorted(S_t+1 - resident) into the ascending free slots, leftover free
     slots emptied, and the ascending slots holding S_t after the update.
     """
