@@ -84,6 +84,9 @@ def parse():
                     help="GQA/MHA: run one tensor-parallel shard of the workload, with this many KV heads (and "
                          "their query heads) of the model's; every stage is independent per KV head, so a shard "
                          "is the whole per-GPU path of a multi-GPU step")
+    ap.add_argument("--budget-sweep", default=None,
+                    help="comma-separated KV budgets: per budget, one layer's prefetch (a full reload and the "
+                         "elastic load of a steady step) against one layer's sparse attention")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with three 256 MiB device-to-device copies (counter calibration)")
     return ap.parse_args()
@@ -238,7 +241,9 @@ def main():
             sys.exit(2)
         g = p.n_q_heads // p.n_kv_heads
         p = p.with_(n_kv_heads=args.kv_heads_per_gpu, n_q_heads=g * args.kv_heads_per_gpu)
-    if p.kind == "mla":
+    if args.budget_sweep:
+        result = bench_budget_sweep(args, p, torch, W)
+    elif p.kind == "mla":
         result = bench_mla_literal(args, p, torch, W) if args.mla_literal else bench_mla(args, p, torch, W)
     elif args.lag == 1:
         result = bench_lag1(args, p, torch, W)
@@ -455,6 +460,54 @@ def bench_gqa(args, p, torch, W):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, w, t0 + Wm, args.cpu_seconds)
     return result
+
+
+def bench_budget_sweep(args, p, torch, W):
+    """Per KV budget: the time to prefetch one layer's selected rows (all of them, as on the cold first
+    step, and the elastic load of a steady step) against one layer's sparse attention over them.
+    The copy and the attention of all layers run as one chunk and are divided by the layer count."""
+    from speculative_kv_sparsity_amd import api
+    from speculative_kv_sparsity_amd.driver import SparseDecoder, StageTimer
+
+    budgets = [int(x) for x in args.budget_sweep.split(",")]
+    if p.kind not in ("gqa", "mha") or any(not 0 < k <= p.max_len for k in budgets):
+        print("--budget-sweep takes budgets in (0, max_len] of a GQA/MHA workload", file=sys.stderr)
+        sys.exit(2)
+    steps = 8
+    w = W.generate(p, device="cuda", seed=args.seed, steps=steps, pin_host=True)
+    lens = torch.as_tensor(w.lengths, device="cuda")
+    qs = w.q.contiguous()
+    L, row = p.n_layers, 2 * p.head_dim * p.elem_bytes
+    rows = []
+    for K in budgets:
+        pk = p.with_(budget=K)
+        dec = SparseDecoder(pk, w.dlm_k, w.host_kv, layer_chunks=1)
+        times = []
+        moved = []
+        for t in range(steps):
+            tm = StageTimer()
+            dec.step(qs[t], lens[t], tm)
+            torch.cuda.synchronize()
+            times.append((tm.ms("copy0", "copy0_end"), tm.ms("attn0", "attn0_merge")))
+            moved.append(int(dec.load_count.sum().item()))
+        cold_copy = times[0][0] / L
+        warm = times[2:]
+        el_copy = float(np.mean([c for c, _ in warm])) / L
+        attn = float(np.mean([a for _, a in warm])) / L
+        full_bytes = moved[0] * row                               # every selected row of one layer
+        el_bytes = float(np.mean(moved[2:])) * row
+        rows.append({"budget": K, "full_reload_us_per_layer": round(cold_copy * 1e3, 2),
+                     "full_reload_MB_per_layer": round(full_bytes / 1e6, 3),
+                     "elastic_us_per_layer": round(el_copy * 1e3, 2),
+                     "elastic_MB_per_layer": round(el_bytes / 1e6, 3),
+                     "attention_us_per_layer": round(attn * 1e3, 2)})
+        del dec
+        torch.cuda.empty_cache()
+    config = {"workload": WORKLOADS.get(p.name, p.name), "batch": p.batch, "layers": L, "q_heads": p.n_q_heads,
+              "kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "cached_tokens": p.max_len,
+              "budgets": budgets, "parallelism": "single GPU"}
+    return {"mode": "budget sweep (one layer's prefetch against one layer's sparse attention)",
+            "data": "synthetic", "config": config, "budget_sweep": rows}
 
 
 def bench_lag1(args, p, torch, W):
