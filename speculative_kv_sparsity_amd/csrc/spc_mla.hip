@@ -40,39 +40,47 @@ constexpr int kLdsRow = kMlaD + 8;                 // padded row (elements): spr
 constexpr int kScoreThreads = 256;                 // 4 waves x 16 heads
 static_assert(kMlaD % 32 == 0, "k-steps of 32");
 
-// One workgroup per head.  Lane l owns latent dims 8l..8l+7 (one 16-byte chunk of
-// every W_UK row); wave w takes the rows n = w, w+4, ...; sequences go four at a
-// time; the four waves' partial sums are added through LDS.
+// Workgroup = (quarter of the 512 latent dims, head), so a head's 128 KB of W_UK
+// is read by four workgroups.  Lane (g, c) of 16 row groups x 16 chunks holds the
+// 16-byte chunk c of the quarter in rows g, g + 16, ...; a lane issues all its row
+// loads of a pass (eight rows, every row of a 128-row W_UK) together, and each wave
+// load covers 4 rows x 256 contiguous bytes.  Sequences go four at a time; the row
+// groups' partial sums meet in LDS.
+constexpr int kAbsorbParts = 4;
+constexpr int kAbsorbDims = kMlaLatent / kAbsorbParts;   // latent dims per workgroup
+constexpr int kAbsorbGroups = 16;                        // row groups (256 threads / 16 chunks)
+constexpr int kAbsorbRows = 8;                           // rows per lane per pass
+static_assert(kAbsorbDims == 8 * 16, "16 chunks of 8 dims per quarter");
+
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const uint16_t* __restrict__ w_uk,
                                                          const uint16_t* __restrict__ q_nope,
                                                          const uint16_t* __restrict__ q_rope,
                                                          float* __restrict__ q_abs, int B, int H, int dn) {
-  static_assert(kMlaLatent == 8 * kWave, "one 16-byte chunk of the latent per lane");
-  const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, c = tid & 15, g = tid >> 4;
   extern __shared__ float smem[];
   float* sq = smem;                                 // [B][dn] query of this head, widened
-  float* red = smem + B * dn;                       // [4 waves][4 sequences][512]
-  for (int i = threadIdx.x; i < B * dn; i += blockDim.x) {
+  float* red = smem + B * dn;                       // [16 row groups][4 sequences][128 dims]
+  for (int i = tid; i < B * dn; i += blockDim.x) {
     const int b = i / dn, n = i - (i / dn) * dn;
     sq[i] = __uint_as_float((uint32_t)q_nope[((size_t)b * H + h) * dn + n] << 16);
   }
   __syncthreads();
-  const uint16_t* w = w_uk + (size_t)h * dn * kMlaLatent + 8 * lane;
+  const uint16_t* w = w_uk + (size_t)h * dn * kMlaLatent + part * kAbsorbDims + 8 * c;
   for (int b0 = 0; b0 < B; b0 += 4) {
     float acc[4][8];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[bb][e] = 0.f;
-    for (int n0 = wid; n0 < dn; n0 += 32) {
-      Vec16 wv[8];
+    for (int n0 = g; n0 < dn; n0 += kAbsorbGroups * kAbsorbRows) {
+      Vec16 wv[kAbsorbRows];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (n0 + 4 * u < dn) wv[u] = ld16(w + (size_t)(n0 + 4 * u) * kMlaLatent);
+      for (int u = 0; u < kAbsorbRows; ++u)
+        if (n0 + kAbsorbGroups * u < dn) wv[u] = ld16(w + (size_t)(n0 + kAbsorbGroups * u) * kMlaLatent);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int n = n0 + 4 * u;
+      for (int u = 0; u < kAbsorbRows; ++u) {
+        const int n = n0 + kAbsorbGroups * u;
         if (n >= dn) break;
         float x[8];
         widen16<SPC_BF16>(wv[u], x);
@@ -87,22 +95,25 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const uint16_t* __restr
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[(wid * 4 + bb) * kMlaLatent + 8 * lane + e] = acc[bb][e];
+      for (int e = 0; e < 8; ++e) red[(g * 4 + bb) * kAbsorbDims + 8 * c + e] = acc[bb][e];
     __syncthreads();
-    for (int i = threadIdx.x; i < 4 * kMlaLatent; i += blockDim.x) {
-      const int bb = i / kMlaLatent, k = i - (i / kMlaLatent) * kMlaLatent;
+    for (int i = tid; i < 4 * kAbsorbDims; i += blockDim.x) {
+      const int bb = i / kAbsorbDims, k = i - bb * kAbsorbDims;
       if (b0 + bb < B) {
-        const float v = red[(0 * 4 + bb) * kMlaLatent + k] + red[(1 * 4 + bb) * kMlaLatent + k] +
-                        red[(2 * 4 + bb) * kMlaLatent + k] + red[(3 * 4 + bb) * kMlaLatent + k];
-        q_abs[((size_t)(b0 + bb) * H + h) * kMlaD + k] = v;
+        float v = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < kAbsorbGroups; ++gg) v += red[(gg * 4 + bb) * kAbsorbDims + k];
+        q_abs[((size_t)(b0 + bb) * H + h) * kMlaD + part * kAbsorbDims + k] = v;
       }
     }
     __syncthreads();
   }
-  for (int i = threadIdx.x; i < B * kMlaRope; i += blockDim.x) {
-    const int b = i / kMlaRope, r = i - (i / kMlaRope) * kMlaRope;
-    q_abs[((size_t)b * H + h) * kMlaD + kMlaLatent + r] =
-        __uint_as_float((uint32_t)q_rope[((size_t)b * H + h) * kMlaRope + r] << 16);
+  if (part == 0) {
+    for (int i = tid; i < B * kMlaRope; i += blockDim.x) {
+      const int b = i / kMlaRope, r = i - (i / kMlaRope) * kMlaRope;
+      q_abs[((size_t)b * H + h) * kMlaD + kMlaLatent + r] =
+          __uint_as_float((uint32_t)q_rope[((size_t)b * H + h) * kMlaRope + r] << 16);
+    }
   }
 }
 
@@ -242,49 +253,52 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
   }
 }
 
-// One workgroup per head; two lanes per output row, each summing 256 contiguous
-// latent dims (eight 16-byte loads in flight); o_lat of the head sits in LDS.
+// Workgroup = (32 output rows, head), so a head's 128 KB of W_UV is read by
+// four workgroups.  Eight lanes per row: lane p holds the 16-byte chunks p, p + 8,
+// ..., p + 56 of the row (64 latent dims), all eight loads issued together, and
+// each wave load covers 8 rows x 128 contiguous bytes.  o_lat of the head sits in
+// LDS; the eight lanes' sums meet by butterfly shuffles.
+constexpr int kOutRows = 32;                      // output rows per workgroup
 __global__ __launch_bounds__(256) void mla_out_proj_kernel(const uint16_t* __restrict__ w_uv,
                                                            const float* __restrict__ o_lat, int64_t lat_b_stride,
                                                            float* __restrict__ out, int B, int H, int dv) {
-  const int h = blockIdx.x;
+  const int h = blockIdx.y;
   extern __shared__ float sol[];                    // [B][512]
   for (int i = threadIdx.x; i < B * kMlaLatent; i += blockDim.x) {
     const int b = i / kMlaLatent, k = i - (i / kMlaLatent) * kMlaLatent;
     sol[i] = o_lat[(size_t)b * lat_b_stride + (size_t)h * kMlaLatent + k];
   }
+  const int p = threadIdx.x & 7;
+  const int r = blockIdx.x * kOutRows + (threadIdx.x >> 3);
+  const bool ok = r < dv;
+  const uint16_t* wr = w_uv + ((size_t)h * dv + (ok ? r : 0)) * kMlaLatent;
+  constexpr int kChunks = kMlaLatent / 8 / 8;       // 16-byte chunks per lane (8)
+  Vec16 wv[kChunks];
+#pragma unroll
+  for (int u = 0; u < kChunks; ++u) wv[u] = ld16(wr + 8 * (p + 8 * u));
   __syncthreads();
-  const int half = threadIdx.x & 1;
-  constexpr int kHalf = kMlaLatent / 2;             // 256 dims per lane
-  for (int r0 = 0; r0 < dv; r0 += blockDim.x / 2) {
-    const int r = r0 + (threadIdx.x >> 1);
-    const bool ok = r < dv;
-    const uint16_t* wr = w_uv + ((size_t)h * dv + (ok ? r : 0)) * kMlaLatent + kHalf * half;
-    for (int b0 = 0; b0 < B; b0 += 4) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < kHalf / 8; c0 += 8) {
-        Vec16 wv[8];
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) wv[u] = ld16(wr + 8 * (c0 + u));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float x[8];
-          widen16<SPC_BF16>(wv[u], x);
-          const int k = kHalf * half + 8 * (c0 + u);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            if (b0 + bb >= B) break;
-            const float* o = sol + (b0 + bb) * kMlaLatent + k;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[bb] = fmaf(x[e], o[e], acc[bb]);
-          }
-        }
-      }
+    for (int u = 0; u < kChunks; ++u) {
+      float x[8];
+      widen16<SPC_BF16>(wv[u], x);
+      const int k = 8 * (p + 8 * u);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const float t = acc[bb] + __shfl_xor(acc[bb], 1, kWave);
-        if (ok && half == 0 && b0 + bb < B) out[((size_t)(b0 + bb) * H + h) * dv + r] = t;
+        if (b0 + bb >= B) break;
+        const float* o = sol + (b0 + bb) * kMlaLatent + k;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[bb] = fmaf(x[e], o[e], acc[bb]);
       }
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      float t = acc[bb];
+      t += __shfl_xor(t, 1, kWave);
+      t += __shfl_xor(t, 2, kWave);
+      t += __shfl_xor(t, 4, kWave);
+      if (ok && p == 0 && b0 + bb < B) out[((size_t)(b0 + bb) * H + h) * dv + r] = t;
     }
   }
 }
@@ -293,7 +307,8 @@ __global__ __launch_bounds__(256) void mla_out_proj_kernel(const uint16_t* __res
 
 hipError_t launch_mla_absorb(int B, int H, int dn, const void* w_uk, const void* q_nope, const void* q_rope,
                              float* q_abs, hipStream_t st) {
-  mla_absorb_kernel<<<dim3(H), 256, ((size_t)B * dn + 4 * 4 * kMlaLatent) * sizeof(float), st>>>(
+  mla_absorb_kernel<<<dim3(kAbsorbParts, H), 256,
+                      ((size_t)B * dn + (size_t)kAbsorbGroups * 4 * kAbsorbDims) * sizeof(float), st>>>(
       static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
       q_abs, B, H, dn);
   return hipGetLastError();
@@ -503,8 +518,8 @@ hipError_t launch_mla_expand(const spc_shape& s, const void* latent, const void*
 
 hipError_t launch_mla_out_proj(int B, int H, int dv, const void* w_uv, const float* o_lat, int64_t lat_b_stride,
                                float* out, hipStream_t st) {
-  mla_out_proj_kernel<<<dim3(H), 256, (size_t)B * kMlaLatent * sizeof(float), st>>>(static_cast<const uint16_t*>(w_uv), o_lat, lat_b_stride, out, B, H,
-                                                dv);
+  mla_out_proj_kernel<<<dim3((dv + kOutRows - 1) / kOutRows, H), 256, (size_t)B * kMlaLatent * sizeof(float), st>>>(
+      static_cast<const uint16_t*>(w_uv), o_lat, lat_b_stride, out, B, H, dv);
   return hipGetLastError();
 }
 

@@ -97,3 +97,45 @@ def test_mla_32k_full_shape_sampled_heads():
     w = W.generate(p, device="cuda", seed=0, steps=2)
     overl = _check_steps(p, w, 2, heads=[0, 37, 127], batches=[0, 3])
     assert overl and overl[0] > 0.3
+
+
+@pytest.mark.parametrize("B,H,dn,dv,n_layers,layer", [(1, 3, 128, 128, 1, 0), (5, 8, 100, 77, 3, 2),
+                                                       (16, 2, 33, 300, 2, 1), (4, 128, 128, 128, 1, 0)])
+def test_mla_helpers_match_literal_up_projections(B, H, dn, dv, n_layers, layer):
+    """spc_mla_absorb_q and spc_mla_out_proj against the oracle's literal expansion.  The
+    absorbed query dotted with a latent row c || r equals q_nope . (W_UK c) + q_rope . r, so the
+    unit rows e_k give every entry; the output projection of o_lat equals the value part of the
+    expansion of o_lat taken as a latent row, W_UV o_lat.  Odd nope and value widths, a batch of
+    16 and four row groups of output rows with a ragged tail."""
+    C, R = 512, 64
+    gen = torch.Generator().manual_seed(7 * B + dn + dv)
+    w_uk = (torch.randn(H, dn, C, generator=gen) * 0.05).to(torch.bfloat16)
+    w_uv = (torch.randn(H, dv, C, generator=gen) * 0.05).to(torch.bfloat16)
+    q_nope = torch.randn(B, H, dn, generator=gen).to(torch.bfloat16)
+    q_rope = torch.randn(B, H, R, generator=gen).to(torch.bfloat16)
+    o_lat = torch.randn(B, n_layers, H, C, generator=gen)
+    shape = api.make_shape(B, H, 1, H, C + R, C, 64, 8, n_layers, "bf16", (128 + R) ** -0.5)
+    dev = torch.device("cuda")
+    q_abs = torch.full((B, H, C + R), float("nan"), device=dev)
+    out = torch.full((B, H, dv), float("nan"), device=dev)
+    api.spc_mla_absorb_q(shape, dn, w_uk.to(dev), q_nope.to(dev), q_rope.to(dev), q_abs)
+    api.spc_mla_out_proj(shape, dv, w_uv.to(dev), o_lat.to(dev), layer, out)
+    torch.cuda.synchronize()
+    qa, got = q_abs.cpu().numpy().astype(np.float64), out.cpu().numpy().astype(np.float64)
+    wuk, wuv = _bf(w_uk), _bf(w_uv)
+    qn, qr = _bf(q_nope), _bf(q_rope)
+    eye = np.eye(C)
+    for h in range(H):
+        # keys of the unit latent rows (rope 0), then q_nope . K[k]: entry k of W_UK^T q_nope
+        keys = O.mla_expand_keys(eye, np.zeros((C, R)), wuk[h:h + 1])[0][:, :dn]
+        for b in range(B):
+            ref_q = keys @ qn[b, h]
+            # fp32 accumulation: at most dn fused multiply-adds and 16 partial sums, each rounding
+            # by at most 2^-24 of the running magnitude, bounded by the sum of |terms|
+            bound = (dn + 32) * 2.0 ** -24 * (np.abs(keys) @ np.abs(qn[b, h]))
+            assert np.all(np.abs(qa[b, h, :C] - ref_q) <= bound), (b, h)
+            np.testing.assert_array_equal(qa[b, h, C:], qr[b, h])       # the rope part widened exactly
+            _, V = O.mla_expand_rows(o_lat[b, layer, h].numpy()[None].astype(np.float64), np.zeros((1, R)),
+                                     wuk[h], wuv[h])
+            bound = (C + 32) * 2.0 ** -24 * (np.abs(wuv[h]) @ np.abs(o_lat[b, layer, h].numpy().astype(np.float64)))
+            assert np.all(np.abs(got[b, h] - V[0]) <= bound), (b, h)
