@@ -192,7 +192,8 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
 int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths,
                          float* logits, float* tile_stats, void* stream);
 
-/* Positions per tile of the stage-1 statistics (128; MLA shapes 256), 0 for an invalid shape. */
+/* Positions per tile of the stage-1 statistics, 0 for an invalid shape: 128; MLA shapes 512 when
+ * batch x ceil(H_q / 64) x ceil(max_len / 512) >= 512 (two scoring workgroups per CU), else 256. */
 int spc_score_tile(const spc_shape* s);
 /* Bytes of spc_retrieval_logits' tile_stats for the shape, 0 for an invalid shape. */
 size_t spc_tile_stats_size(const spc_shape* s);

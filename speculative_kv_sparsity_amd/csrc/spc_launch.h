@@ -14,6 +14,7 @@ namespace spc {
 // ---- stage 1: scores
 constexpr int kScoreTile = 128;        // positions per workgroup of the logits kernel
 constexpr int kMlaScoreTile = 256;     // positions per workgroup of the MLA scoring kernel
+constexpr int kMlaScoreTileLarge = 512;   // the same when the grid still gives every CU two workgroups
 constexpr int kNormChunk = 2048;       // positions per workgroup of the normalize kernel
 size_t scores_ws_bytes(const spc_shape& s);
 bool scores_supported(const spc_shape& s);
@@ -23,6 +24,7 @@ hipError_t launch_scores(const spc_shape& s, const void* q, const void* k, const
 hipError_t launch_logits(const spc_shape& s, const void* q, const void* k, const int32_t* lengths, float* logits,
                          float2* stats, hipStream_t st);
 // rewrites logits as probabilities from per-tile (max, sum exp) partials [B*Hq][ntiles]
+int mla_score_tile(const spc_shape& s);   // kMlaScoreTile or kMlaScoreTileLarge
 int score_tile(const spc_shape& s);    // positions per (max, sum) partial of the scores workspace
 hipError_t launch_scores_normalize(const spc_shape& s, float* probs, const float2* part, const int32_t* lengths,
                                    int ntiles, hipStream_t st);

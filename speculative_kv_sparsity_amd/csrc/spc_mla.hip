@@ -130,7 +130,7 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
   m = M;
 }
 
-// Workgroup = (sequence, kMlaScoreTile positions, 64 heads): 4 waves x 16 heads, two
+// Workgroup = (sequence, tile of 256 or 512 positions, 64 heads): 4 waves x 16 heads, two
 // workgroups per CU.  The tile is staged 32 rows at a time through two LDS
 // buffers, so one barrier per sub-tile separates the MFMAs on one buffer from the
 // staging of the next sub-tile into the other.  The two workgroups
@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
                                                                    const int32_t* __restrict__ lengths,
                                                                    float* __restrict__ probs,
                                                                    float2* __restrict__ part, int H, int max_len,
-                                                                   int ntiles, int nhg, float scale) {
+                                                                   int ntiles, int nhg, int tile_len,
+                                                                   float scale) {
   __shared__ uint16_t sl[2][kSub * kLdsRow];
   // block id -> (tile, head group): groups of 8 * nhg ids hold 8 tiles x nhg head groups
   const int id = blockIdx.x;
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
   const int b = blockIdx.y;
   if (tile >= ntiles) return;
   const int n = clamp_len(lengths, b, max_len);
-  const int row0 = tile * kMlaScoreTile;
+  const int row0 = tile * tile_len;
   if (row0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int hbase = hg * 64 + 16 * wid;              // first head of this wave
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
   constexpr int kPer = kSub * kChunks / kScoreThreads;
   static_assert(kSub * kChunks % kScoreThreads == 0, "sub-tile load split");
   const uint16_t* lb = lat + (size_t)b * max_len * kMlaD;
-  const int nsub = min(kMlaScoreTile, n - row0 + kSub - 1) / kSub;   // sub-tiles with valid rows
+  const int nsub = min(tile_len, n - row0 + kSub - 1) / kSub;   // sub-tiles with valid rows
   uint4 v[kPer];
   auto load = [&](int sub) {
     const int p_sub = row0 + sub * kSub;
@@ -494,13 +495,22 @@ __global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
 
 }  // namespace
 
+// 512-position tiles halve the workgroups and the query-fragment setup per position; they are
+// taken when the grid still holds two workgroups for each of the 256 CUs
+int mla_score_tile(const spc_shape& s) {
+  const long nhg = (s.n_q_heads + 63) / 64;
+  const long wgs = (long)s.batch * nhg * ((s.max_len + kMlaScoreTileLarge - 1) / kMlaScoreTileLarge);
+  return wgs >= 512 ? kMlaScoreTileLarge : kMlaScoreTile;
+}
+
 hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
                              float* logits, float2* stats, hipStream_t st) {
-  const int ntiles = (s.max_len + kMlaScoreTile - 1) / kMlaScoreTile;
+  const int tl = mla_score_tile(s);
+  const int ntiles = (s.max_len + tl - 1) / tl;
   const int nhg = (s.n_q_heads + 63) / 64;         // head groups of 64
   const int ngrp = (ntiles + 7) / 8;
   mla_scores_kernel<<<dim3(ngrp * 8 * nhg, s.batch), kScoreThreads, 0, st>>>(
-      q_abs, static_cast<const uint16_t*>(latent), lengths, logits, stats, s.n_q_heads, s.max_len, ntiles, nhg,
+      q_abs, static_cast<const uint16_t*>(latent), lengths, logits, stats, s.n_q_heads, s.max_len, ntiles, nhg, tl,
       s.scale);
   return hipGetLastError();
 }

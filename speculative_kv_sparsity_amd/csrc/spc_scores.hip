@@ -247,7 +247,7 @@ bool scores_supported(const spc_shape& s) {
   return s.head_dim == 64 || s.head_dim == 128 || s.head_dim == 256;
 }
 
-int score_tile(const spc_shape& s) { return mla_shape(s) ? kMlaScoreTile : kScoreTile; }
+int score_tile(const spc_shape& s) { return mla_shape(s) ? mla_score_tile(s) : kScoreTile; }
 
 hipError_t launch_scores_normalize(const spc_shape& s, float* probs, const float2* part, const int32_t* lengths,
                                    int ntiles, hipStream_t st) {

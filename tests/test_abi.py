@@ -84,7 +84,7 @@ def test_null_pointers_and_small_workspace_rejected():
 def test_workspace_sizes():
     lib = L.lib()
     s = _shape(batch=2, max_len=32768, budget=2048, n_layers=32)
-    # one (max, sum) pair per head and tile of 128 positions (MLA scoring: tiles of 256)
+    # one (max, sum) pair per head and tile of 128 positions (MLA scoring: tiles of 256 or 512)
     assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(s)) == 2 * 32 * 256 * 8
     # one (max, sum) pair and one v_dim vector per head, layer and split of 128 rows
     assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s)) == 2 * 32 * 32 * 16 * (128 * 4 + 8)
@@ -94,7 +94,7 @@ def test_workspace_sizes():
     # MLA: 4 sequences, 128 heads over one shared latent head (576 scored dims, 512 value dims)
     m = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
                budget=2048, scale=192 ** -0.5)
-    assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(m)) == 4 * 128 * 128 * 8
+    assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(m)) == 4 * 128 * 64 * 8   # tiles of 512
     # 1024-row splits once the launch has >= 1024 workgroups (4 x 128 x 2 here)
     assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(m)) == 4 * 128 * 2 * (512 * 4 + 8)
     small = _shape(batch=1, n_q_heads=16, n_kv_heads=1, n_groups=16, head_dim=576, v_dim=512, max_len=4096,
@@ -204,8 +204,13 @@ def test_log_domain_scoring_sizes_and_validation():
     assert lib.spc_tile_stats_size(ctypes.byref(s)) == 2 * 32 * 8 * 8          # ceil(1000 / 128) = 8 tiles
     mla = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
                  budget=2048, scale=192 ** -0.5)
-    assert lib.spc_score_tile(ctypes.byref(mla)) == 256
-    assert lib.spc_tile_stats_size(ctypes.byref(mla)) == 4 * 128 * 128 * 8
+    # 4 sequences x 2 head groups x 64 tiles of 512 = 512 scoring workgroups: the large tile
+    assert lib.spc_score_tile(ctypes.byref(mla)) == 512
+    assert lib.spc_tile_stats_size(ctypes.byref(mla)) == 4 * 128 * 64 * 8
+    mla1 = _shape(batch=1, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                  budget=2048, scale=192 ** -0.5)
+    assert lib.spc_score_tile(ctypes.byref(mla1)) == 256                      # 128 workgroups of 512: too few
+    assert lib.spc_tile_stats_size(ctypes.byref(mla1)) == 128 * 128 * 8
     assert lib.spc_score_tile(ctypes.byref(_shape(budget=0))) == 0
     p = ctypes.c_void_p(256)
     assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, None, None) == L.SPC_ERR_INVALID_ARG
