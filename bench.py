@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--config", default="b1_32k")
+    ap.add_argument("--retrieval", default="head", choices=("head", "batch"),
+                    help="head: one selection per KV head (GQA group; the path as built); batch: one selection "
+                         "per sequence shared by every head (the comparison the pages draw)")
     ap.add_argument("--layer-chunks", type=int, default=2)
     ap.add_argument("--tail-layers", type=int, default=None,
                     help="layers in the last chunk (default n_layers // 8)")
@@ -118,9 +121,19 @@ def measured_traffic(workload: str, layer_chunks: int):
     return out
 
 
+ISO_WARM_MS = 10.0      # back-to-back replays before the timed ones (steady clocks, see iso())
+ISO_TIMED_REPLAYS = 3
+
+
 def iso(torch, call, reps):
     """Average time of one call: `reps` launches captured once into a HIP graph (host launch
-    overhead out of the bracket), replayed between two events on the stream the calls use."""
+    overhead out of the bracket), replayed between two events on the stream the calls use.
+
+    The timed replays follow at least ISO_WARM_MS of back-to-back replays of the same graph, with no
+    idle gap in between: after the PCIe-bound copies of the steps the part needs a few milliseconds
+    of HBM-bound work before its clocks settle (the 32K attention kernel reads 44-45 us in its first
+    replay and 42 us from the fifth on, over the same rotating inputs), and a serving loop runs these
+    kernels back to back."""
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(st):
@@ -133,19 +146,27 @@ def iso(torch, call, reps):
             for _ in range(reps):
                 call(st)
         with torch.cuda.stream(st):        # replay is enqueued on the current stream
-            g.replay()
-            torch.cuda.synchronize()
             a.record(st)
             g.replay()
             z.record(st)
+            torch.cuda.synchronize()
+            n_warm = max(2, int(np.ceil(ISO_WARM_MS / max(a.elapsed_time(z), 1e-3))))
+            for _ in range(n_warm):
+                g.replay()
+            a.record(st)
+            for _ in range(ISO_TIMED_REPLAYS):
+                g.replay()
+            z.record(st)
+        n = reps * ISO_TIMED_REPLAYS
     except Exception:          # capture refused: time eager launches instead
         torch.cuda.synchronize()
         a.record(st)
         for _ in range(reps):
             call(st)
         z.record(st)
+        n = reps
     torch.cuda.synchronize()
-    return a.elapsed_time(z) / reps
+    return a.elapsed_time(z) / n
 
 
 def roof(bound, amount, ms, peak, unit, kernel, calls, traffic=None):
@@ -194,6 +215,32 @@ def calibration_copies(torch):
     torch.cuda.synchronize()
 
 
+def selection_coverage(torch, p, q, dlm_k, host_kv, lengths, sel_idx, sel_count):
+    """How much attention weight the step's selection covers, averaged over (sequence, query head):
+    of the retrieval head's own weights, and of layer 0's target weights (dense softmax over every
+    cached position, the same query).  A statistic of the run, computed after the timed passes with
+    plain tensor operations; the pages compare it between head-level and batch-level selection."""
+    B, Hq, Hkv, d = p.batch, p.n_q_heads, p.n_kv_heads, p.head_dim
+    per_kv, per_g = Hq // Hkv, Hq // p.n_groups
+    lens = lengths.tolist()
+    sel, cnt = sel_idx.cpu(), sel_count.cpu()
+    out = {"retrieval_head": [], "target_layer0": []}
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        qb = q[b].float()
+        for name, keys in (("retrieval_head", dlm_k[b, :, :n].float()),
+                           ("target_layer0", host_kv[b, 0, :, :n, 0].to("cuda").float())):
+            kh = keys.repeat_interleave(per_kv, dim=0).contiguous()             # [Hq][n][d] float32
+            wts = torch.softmax(torch.bmm(kh, qb[:, :, None].contiguous())[:, :, 0] * p.scale, dim=-1)
+            for i in range(Hq):
+                g = i // per_g
+                idx = sel[b, g, :int(cnt[b, g])].long().to("cuda")
+                out[name].append(float(wts[i, idx].sum()))
+    return {k: round(float(np.mean(v)), 4) for k, v in out.items()}
+
+
 def cpu_baseline(p, w, t0, budget_s):
     """The CPU oracle (as it stands) on a bounded sample of the same workload."""
     from oracle import OracleDecoder
@@ -203,6 +250,10 @@ def cpu_baseline(p, w, t0, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
     dec = OracleDecoder(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.budget, p.scale, p.dtype)
     k = to_numpy_raw(w.dlm_k)
     kv = to_numpy_raw(w.host_kv)
@@ -217,8 +268,10 @@ def cpu_baseline(p, w, t0, budget_s):
             break
     el = time.perf_counter() - start
     return {"value": n / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "nproc": usable, "host_cpus": os.cpu_count(),
             "sample": f"{n} consecutive decode steps of the same workload (all {p.n_layers} layers, "
-                      f"fp64 NumPy), {el:.1f} s"}
+                      f"fp64 NumPy), {el:.1f} s; cores = the BLAS threads the oracle ran with, nproc = the "
+                      f"CPUs this process may use"}
 
 
 def main():
@@ -241,6 +294,11 @@ def main():
             sys.exit(2)
         g = p.n_q_heads // p.n_kv_heads
         p = p.with_(n_kv_heads=args.kv_heads_per_gpu, n_q_heads=g * args.kv_heads_per_gpu)
+    if args.retrieval == "batch":
+        if p.kind not in ("gqa", "mha"):
+            print("--retrieval batch applies to GQA/MHA workloads", file=sys.stderr)
+            sys.exit(2)
+        p = p.with_(kind="mqa")          # one group over every query head of a sequence
     if args.budget_sweep:
         result = bench_budget_sweep(args, p, torch, W)
     elif p.kind == "mla":
@@ -410,6 +468,8 @@ def bench_gqa(args, p, torch, W):
               "kv_heads": Hkv, "head_dim": d, "cached_tokens": p.max_len,
               "mean_length": round(n_valid / B, 1), "first_step": t0, "kv_budget": K, "layer_chunks": nch,
               "chunk_layers": [z - a for a, z in dec.chunks], "parallelism": "single GPU"}
+    if p.kind == "mqa":
+        config["retrieval"] = "batch-level: one selection per sequence shared by all query heads"
     if thresholds is not None:
         config.update({"hbm_gb": args.hbm_gb, "weights_gb": args.weights_gb, "offloaded_layers": off,
                        "offload_thresholds": thresholds})
@@ -454,7 +514,11 @@ def bench_gqa(args, p, torch, W):
                          "rows_selected_per_step": float(np.mean(sel_rows)),
                          "transfer_fraction_vs_full_reload":
                              round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
+                         "adjacent_overlap": round(1.0 - float(np.mean(loaded_rows)) / float(np.mean(sel_rows)), 4),
                          "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * off * row)}
+    result["retrieval"] = {"level": "head" if p.kind != "mqa" else "batch", "groups": p.n_groups,
+                           "coverage": selection_coverage(torch, p, tq, dec.dlm_k, w.host_kv, tl, dec.sel_idx,
+                                                          dec.sel_count)}
     if args.calibrate_copy:
         calibration_copies(torch)
     if not args.no_cpu_baseline:
@@ -853,6 +917,10 @@ def cpu_baseline_mla(p, w, t, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
     C = p.latent_dim
     lat = O.to_f64(to_numpy_raw(w.latent), "bf16")
     w_uk = O.to_f64(to_numpy_raw(w.w_uk), "bf16")
@@ -875,6 +943,7 @@ def cpu_baseline_mla(p, w, t, budget_s):
     el = time.perf_counter() - start
     per_step = el / n_done * p.batch * p.n_q_heads
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "nproc": usable, "host_cpus": os.cpu_count(),
             "sample": f"{n_done} (sequence 0, head) scoring + Top-K + attention evaluations of one step "
                       f"(fp64 NumPy, keys expanded literally), {el:.1f} s, scaled by "
                       f"{p.batch} x {p.n_q_heads} to whole steps"}

@@ -35,7 +35,13 @@
  *     belongs to selection group i / (n_q_heads / n_groups) (consecutive
  *     heads share).  GQA: n_groups = n_kv_heads; MQA: n_groups = 1;
  *     MHA: n_groups = n_q_heads = n_kv_heads; MLA (one shared latent KV
- *     head): n_kv_heads = 1, n_groups = n_q_heads.
+ *     head): n_kv_heads = 1, n_groups = n_q_heads.  One of n_groups and
+ *     n_kv_heads divides the other: a group lies within one KV head, or a KV
+ *     head within one group.  The second case includes the batch-level
+ *     selection the SpeContext blog (section 5, "C1") and the paper summary
+ *     (section 4.2) set against head-level retrieval: n_groups = 1 over several
+ *     KV heads, one selection shared by every head of the sequence, ranked by
+ *     the element-wise max over all of its query heads.
  */
 #ifndef SPC_H
 #define SPC_H
@@ -47,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPC_ABI_VERSION 1
+#define SPC_ABI_VERSION 2
 
 typedef enum spc_status {
   SPC_OK = 0,
@@ -187,10 +193,10 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
  * formula; the same inputs and supported shapes as spc_retrieval_scores).
  *   logits      device [B][H_q][max_len] float32 out; entries j >= lengths[b] untouched
  *   tile_stats  device float32 pairs [B][H_q][ceil(max_len / T)] out, 8-byte aligned,
- *               spc_tile_stats_size(s) bytes
+ *               tile_stats_bytes >= spc_tile_stats_size(s) (else SPC_ERR_INVALID_ARG)
  */
 int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths,
-                         float* logits, float* tile_stats, void* stream);
+                         float* logits, float* tile_stats, size_t tile_stats_bytes, void* stream);
 
 /* Positions per tile of the stage-1 statistics, 0 for an invalid shape: 128; MLA shapes 512 when
  * batch x ceil(H_q / 64) x ceil(max_len / 512) >= 512 (two scoring workgroups per CU), else 256. */
@@ -224,14 +230,16 @@ int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* le
  * With one query head per group (MHA, MLA) the logits themselves are ranked (the
  * same order as the head's probabilities, without exp rounding) and tile_stats
  * may be NULL; otherwise it is required.
- *   logits, tile_stats  as written by spc_retrieval_logits for the same shape
+ *   logits, tile_stats  as written by spc_retrieval_logits for the same shape; tile_stats_bytes
+ *               is the size of the tile_stats buffer, at least spc_tile_stats_size(s) when the
+ *               stats are required (else SPC_ERR_INVALID_ARG), ignored when they are not
  *   sel_idx, sel_count, ws  as for spc_group_max_topk (same workspace size)
  * At most 64 query heads per group.  The selection is exact on the float32 values v
  * (as in the probability form, values below float32's range tie at zero).
  */
 int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats,
-                              const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws,
-                              size_t ws_bytes, void* stream);
+                              size_t tile_stats_bytes, const int32_t* lengths, int32_t* sel_idx,
+                              int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Stage 3 - elastic loading (blog section 4 pseudocode: the positions to load
@@ -251,11 +259,12 @@ int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const flo
  *   follows.  Kept positions never move.  Entries after load_count are -1.
  *   load_pos, load_slot: device [B][n_groups][budget] int32; load_count [B][n_groups].
  * SPC_COPY (on copy_stream, reading the load lists): for every layer l in
- *   [layer_begin, layer_end) and i < load_count[b][g]:
- *     dev_kv  K,V row load_slot[i] of (b, l, g)  <-  host_kv K,V row load_pos[i] of (b, l, g)
+ *   [layer_begin, layer_end), KV head h and i < load_count[b][g], g = h / (n_kv_heads / n_groups):
+ *     dev_kv  K,V row load_slot[b][g][i] of (b, l, h)  <-  host_kv K,V row load_pos[b][g][i] of (b, l, h)
+ *   (GQA: g = h.  n_groups must divide n_kv_heads: the device store has one slot row per
+ *   (KV head, slot), and every KV head of a group holds the group's selection.)
  *   host_kv must be pinned host memory mapped for the device (hipHostMalloc,
  *   torch pin_memory=True); the device reads it directly over the host link.
- *   Requires n_groups == n_kv_heads.
  * With both flags, the plan runs on plan_stream and the copy on copy_stream;
  * the caller orders copy_stream after plan_stream (e.g. with an event) when they
  * differ.  Run SPC_PLAN exactly once per step: a repeated plan is empty.

@@ -62,6 +62,10 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -129,10 +133,8 @@ def tile_stats_shape(shape: SpcShape) -> tuple:
 def spc_retrieval_logits(shape: SpcShape, q, k, lengths, logits, tile_stats, stream=None) -> None:
     for t, n in ((q, "q"), (k, "k"), (lengths, "lengths"), (logits, "logits"), (tile_stats, "tile_stats")):
         _dev(t, n)
-    if tile_stats.numel() * tile_stats.element_size() < spc_tile_stats_size(shape):
-        raise ValueError("tile_stats is smaller than spc_tile_stats_size(shape)")
     _check(L.lib().spc_retrieval_logits(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(lengths), _ptr(logits),
-                                        _ptr(tile_stats), _stream(stream)))
+                                        _ptr(tile_stats), _nbytes(tile_stats), _stream(stream)))
 
 
 def spc_group_max_topk_logits(shape: SpcShape, logits, tile_stats, lengths, sel_idx, sel_count, ws=None,
@@ -142,9 +144,9 @@ def spc_group_max_topk_logits(shape: SpcShape, logits, tile_stats, lengths, sel_
     if tile_stats is not None:
         _dev(tile_stats, "tile_stats")
     ws = _workspace(SPC_CALL_TOPK, shape, logits.device) if ws is None else ws
-    _check(L.lib().spc_group_max_topk_logits(ctypes.byref(shape), _ptr(logits), _ptr(tile_stats), _ptr(lengths),
-                                             _ptr(sel_idx), _ptr(sel_count), _ptr(ws),
-                                             ws.numel() * ws.element_size(), _stream(stream)))
+    _check(L.lib().spc_group_max_topk_logits(ctypes.byref(shape), _ptr(logits), _ptr(tile_stats),
+                                             _nbytes(tile_stats), _ptr(lengths), _ptr(sel_idx), _ptr(sel_count),
+                                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spc_elastic_update(shape: SpcShape, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,

@@ -47,8 +47,10 @@ int check_shape(const spc_shape* s) {
     return fail(SPC_ERR_INVALID_ARG, "n_q_heads (%d) %% n_kv_heads (%d) != 0", s->n_q_heads, s->n_kv_heads);
   if (s->n_q_heads % s->n_groups != 0)
     return fail(SPC_ERR_INVALID_ARG, "n_q_heads (%d) %% n_groups (%d) != 0", s->n_q_heads, s->n_groups);
-  if (s->n_groups % s->n_kv_heads != 0)
-    return fail(SPC_ERR_INVALID_ARG, "n_groups (%d) must be a multiple of n_kv_heads (%d)", s->n_groups,
+  // each group lies within one KV head (GQA, MHA, MLA), or each KV head within one group (one
+  // selection shared by the heads of several KV heads, e.g. all of them)
+  if (s->n_groups % s->n_kv_heads != 0 && s->n_kv_heads % s->n_groups != 0)
+    return fail(SPC_ERR_INVALID_ARG, "n_groups (%d) and n_kv_heads (%d): neither divides the other", s->n_groups,
                 s->n_kv_heads);
   if (s->max_len < 1) return fail(SPC_ERR_INVALID_ARG, "max_len must be >= 1");
   if (s->budget < 1 || s->budget > s->max_len)
@@ -118,7 +120,7 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
 }
 
 int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths, float* logits,
-                         float* tile_stats, void* stream) {
+                         float* tile_stats, size_t tile_stats_bytes, void* stream) {
   if (int e = check_shape(s)) return e;
   if (!q || !k || !lengths || !logits || !tile_stats)
     return fail(SPC_ERR_INVALID_ARG, "NULL q, k, lengths, logits or tile_stats");
@@ -128,14 +130,17 @@ int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const
   if (!aligned4(logits) || !aligned4(lengths)) return fail(SPC_ERR_INVALID_ARG, "logits/lengths misaligned");
   if ((reinterpret_cast<uintptr_t>(tile_stats) & 7u) != 0)
     return fail(SPC_ERR_INVALID_ARG, "tile_stats must be 8-byte aligned");
+  if (tile_stats_bytes < spc::scores_ws_bytes(*s))
+    return fail(SPC_ERR_INVALID_ARG, "tile_stats holds %zu bytes, the shape needs %zu", tile_stats_bytes,
+                spc::scores_ws_bytes(*s));
   const hipError_t e = spc::launch_logits(*s, q, k, lengths, logits, reinterpret_cast<float2*>(tile_stats),
                                           as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "retrieval logits launch");
 }
 
 int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats,
-                              const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              size_t tile_stats_bytes, const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count,
+                              void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_shape(s)) return e;
   if (!logits || !lengths || !sel_idx || !sel_count)
     return fail(SPC_ERR_INVALID_ARG, "NULL logits, lengths, sel_idx or sel_count");
@@ -148,6 +153,9 @@ int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const flo
     return fail(SPC_ERR_INVALID_ARG, "misaligned int32/float buffer");
   if ((reinterpret_cast<uintptr_t>(tile_stats) & 7u) != 0)
     return fail(SPC_ERR_INVALID_ARG, "tile_stats must be 8-byte aligned");
+  if (gq > 1 && tile_stats_bytes < spc::scores_ws_bytes(*s))
+    return fail(SPC_ERR_INVALID_ARG, "tile_stats holds %zu bytes, the shape needs %zu", tile_stats_bytes,
+                spc::scores_ws_bytes(*s));
   const size_t need = spc::topk_ws_bytes(*s);
   if (ws_bytes < need || !ws)
     return fail(SPC_ERR_WORKSPACE, "group max / top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -192,15 +200,16 @@ int spc_elastic_update(const spc_shape* s, const int32_t* sel_idx, const int32_t
   if (flags & SPC_COPY) {
     if (!host_kv || !host_l || !dev_kv || !dev_l)
       return fail(SPC_ERR_INVALID_ARG, "copy needs host_kv, host layout, dev_kv and device layout");
-    if (s->n_groups != s->n_kv_heads)
-      return fail(SPC_ERR_UNSUPPORTED, "copy needs one selection group per KV head (n_groups == n_kv_heads)");
+    if (s->n_kv_heads % s->n_groups != 0)
+      return fail(SPC_ERR_UNSUPPORTED, "copy needs every KV head inside one selection group (n_kv_heads %% n_groups "
+                  "== 0; %d KV heads, %d groups)", s->n_kv_heads, s->n_groups);
     if ((long long)s->batch * s->n_groups > spc::kCopyMaxInstances)
       return fail(SPC_ERR_UNSUPPORTED, "batch * n_groups exceeds %d", spc::kCopyMaxInstances);
     if (layer_begin < 0 || layer_end > s->n_layers || layer_begin >= layer_end)
       return fail(SPC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
                   s->n_layers);
     const int eb = elem_bytes(s);
-    const double vecs = (double)s->batch * s->n_groups * s->budget * (layer_end - layer_begin) *
+    const double vecs = (double)s->batch * s->n_kv_heads * s->budget * (layer_end - layer_begin) *
                         ((double)(s->head_dim + s->v_dim) * eb / 16.0);
     if (vecs >= 4294967296.0)
       return fail(SPC_ERR_UNSUPPORTED, "copy of %.0f 16-byte vectors exceeds one launch; split the layer range",

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   const int layer = layer_begin + lo;
   const int GQ = Hq / n_groups;
   const int h0 = r * GQ + hcix * GQC;
-  const int kvh = (r * GQ) / (Hq / Hkv);
+  const int kvh = h0 / (Hq / Hkv);                   // the chunk's heads share one KV head
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int p = lane & 7, rr = lane >> 3;
@@ -509,11 +509,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const flo
   }
 }
 
+// Query heads per workgroup: they must share both the selection group and the KV head, so the
+// chunk divides the smaller of the two head counts (one divides the other).
 int head_chunk(const spc_shape& s) {
-  const int GQ = s.n_q_heads / s.n_groups;
-  if (GQ % 8 == 0) return 8;
-  if (GQ % 4 == 0) return 4;
-  if (GQ % 2 == 0) return 2;
+  const int GQ = s.n_q_heads / s.n_groups, per_kv = s.n_q_heads / s.n_kv_heads;
+  const int g = GQ < per_kv ? GQ : per_kv;
+  if (g % 8 == 0) return 8;
+  if (g % 4 == 0) return 4;
+  if (g % 2 == 0) return 2;
   return 1;
 }
 

@@ -14,8 +14,9 @@
 // plan_bm_kernel  the same where a bitmap of S fits LDS (below): bit tests instead of
 //   the binary search, and the resident bitmap rewritten from it.
 // plan_lag1_kernel  the same for the pipelined loop (see below).
-// copy_kernel  a grid-stride gather over (layer, instance, entry, 16-byte
-//   vector): every lane reads 16 bytes of a K||V row straight from pinned,
+// copy_kernel  a grid-stride gather over (layer, KV head of the group, instance,
+//   entry, 16-byte vector): every KV head of a selection group takes the group's
+//   load lists; every lane reads 16 bytes of a K||V row straight from pinned,
 //   device-mapped host memory over the host link and writes them into the
 //   row's slot in HBM.  Consecutive lanes cover consecutive bytes of a row, so
 //   each wave reads whole rows; each lane keeps several reads in flight.
@@ -309,8 +310,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const int32_t* __res
                                                             const int32_t* __restrict__ load_count,
                                                             const char* __restrict__ host, ByteLayout hl,
                                                             char* __restrict__ dev, ByteLayout dl, int n_inst,
-                                                            int n_groups, int K, int max_len, int layer_begin,
-                                                            int n_lay, int vk, int vrow) {
+                                                            int n_groups, int hpg, int K, int max_len,
+                                                            int layer_begin, int n_lay, int vk, int vrow) {
   __shared__ uint32_t pre[kCopyMaxInstances + 1];
   __shared__ uint32_t scan_smem[16];
   // prefix sums of the load counts over instances
@@ -329,9 +330,10 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const int32_t* __res
   }
   if (threadIdx.x == 0) pre[n_inst] = carry;
   __syncthreads();
-  // 32-bit vector ids: the host checks n_inst * K * n_lay * vrow < 2^32
+  // 32-bit vector ids: the host checks n_inst * hpg * K * n_lay * vrow < 2^32
   const uint32_t total = carry;
-  const uint32_t nvec = total * (uint32_t)n_lay * (uint32_t)vrow;
+  const uint32_t per_layer = total * (uint32_t)hpg;       // (KV head of the group, entry) pairs
+  const uint32_t nvec = per_layer * (uint32_t)n_lay * (uint32_t)vrow;
   const uint32_t stride = gridDim.x * kCopyThreads;
 
   for (uint32_t v0 = blockIdx.x * kCopyThreads + threadIdx.x; v0 < nvec; v0 += stride * kCopyUnroll) {
@@ -344,8 +346,10 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const int32_t* __res
       if (vid < nvec) {
         const uint32_t item = vid / (uint32_t)vrow;
         const int v = (int)(vid - item * (uint32_t)vrow);
-        const int lo_ = (int)(item / total);
-        const uint32_t e = item - (uint32_t)lo_ * total;
+        const int lo_ = (int)(item / per_layer);
+        const uint32_t he = item - (uint32_t)lo_ * per_layer;
+        const int hh = (int)(he / total);
+        const uint32_t e = he - (uint32_t)hh * total;
         // instance holding entry e: last inst with pre[inst] <= e
         int a = 0, z = n_inst;
         while (z - a > 1) {
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const int32_t* __res
         }
         const int inst = a;
         const int i = (int)(e - pre[inst]);
-        const int b = inst / n_groups, g = inst - (inst / n_groups) * n_groups;
+        const int b = inst / n_groups, g = (inst - (inst / n_groups) * n_groups) * hpg + hh;   // KV head
         const int layer = layer_begin + lo_;
         const int32_t pos = load_pos[(size_t)inst * K + i];
         const int32_t slot = load_slot[(size_t)inst * K + i];
@@ -435,7 +439,8 @@ hipError_t launch_copy(const spc_shape& s, const int32_t* load_pos, const int32_
   }();
   copy_kernel<<<dim3(blocks), kCopyThreads, 0, st>>>(
       load_pos, load_slot, load_count, static_cast<const char*>(host_dev_ptr), hb, static_cast<char*>(dev_kv), db,
-      s.batch * s.n_groups, s.n_groups, s.budget, s.max_len, layer_begin, layer_end - layer_begin, vk, vrow);
+      s.batch * s.n_groups, s.n_groups, s.n_kv_heads / s.n_groups, s.budget, s.max_len, layer_begin,
+      layer_end - layer_begin, vk, vrow);
   return hipGetLastError();
 }
 

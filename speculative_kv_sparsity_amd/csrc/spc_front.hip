@@ -303,7 +303,7 @@ hipError_t launch_front(const spc_shape& s, int hidden, int64_t vocab, const spc
   front_gemv_kernel<DT_, RPW_><<<g1, kThreads, lds, st>>>(tokens, e, vocab, g, q, k, rows_q, rows_total, hidden, \
                                                           s.batch, part, rms_part)
   if (s.dtype == SPC_BF16) {
-    if (rpw == 4) SPC_GEMV(SPC_BF16, 4); else SPC_GEMV(SPC_BF16, 8);
+    SPC_GEMV(SPC_BF16, 4);            // bf16 beyond 4 sequences takes the MFMA kernel above
   } else {
     if (rpw == 4) SPC_GEMV(SPC_F32, 4); else SPC_GEMV(SPC_F32, 8);
   }

@@ -189,16 +189,16 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int need,
 // vectors and when each lane walks its own contiguous run of 8 vectors.
 __device__ __forceinline__ int vslot(int v) { return v ^ ((v >> 3) & 7); }
 
-// Radix passes 2 and 3 plus the ordered compaction, shared by both key sources.
-// key_vec(v) returns keys 4v..4v+3 (entries >= n are ignored).
-template <bool IN_LDS, bool RAW>
+// Rows longer than the LDS stage (streamed): radix passes 2 and 3 over the keys
+// read from the workspace or the scores (L2) in every pass, plus the ordered
+// compaction.  key_vec(v) returns keys 4v..4v+3 (entries >= n are ignored).
+template <bool RAW>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t* __restrict__ keys,
                                                                   const uint32_t* __restrict__ chist,
                                                                   const int32_t* __restrict__ lengths,
                                                                   int32_t* __restrict__ sel_idx,
                                                                   int32_t* __restrict__ sel_count, int n_groups,
                                                                   int max_len, int budget, int nchunk) {
-  __shared__ uint4 skeys[IN_LDS ? kTopkLdsKeys / 4 : 1];
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t scan_smem[16];
   __shared__ uint32_t bcast[2];
@@ -217,30 +217,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
   const uint32_t* kin = keys + (size_t)inst * max_len;
   const int nv = (n + 3) / 4;                          // key vectors (the last may be partial)
   const bool aligned = (max_len % 4) == 0;             // rows of the key buffer start 16-byte aligned
-  if (IN_LDS) {
-    constexpr int kVecPerThread = kTopkLdsKeys / 4 / kSelThreads;
-    uint4 v[kVecPerThread];
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) {
-      const int i4 = tid + u * kSelThreads;
-      if (i4 < nv) {
-        if (aligned && 4 * i4 + 3 < n) {
-          v[u] = reinterpret_cast<const uint4*>(kin)[i4];
-        } else {
-          const int j = 4 * i4;
-          v[u] = make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u,
-                            j + 3 < n ? kin[j + 3] : 0u);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) {
-      const int i4 = tid + u * kSelThreads;
-      if (i4 < nv) skeys[vslot(i4)] = to_keys<RAW>(v[u]);
-    }
-  }
   auto key_vec = [&](int v) -> uint4 {
-    if (IN_LDS) return skeys[vslot(v)];
     const int j = 4 * v;
     if (aligned && j + 3 < n) return to_keys<RAW>(reinterpret_cast<const uint4*>(kin)[v]);
     return to_keys<RAW>(
@@ -588,10 +565,10 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
                                                                         s.n_groups, s.max_len, s.budget, nchunk);
   } else {
     if (raw)
-      topk_select_kernel<false, true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+      topk_select_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
                                                                           s.n_groups, s.max_len, s.budget, nchunk);
     else
-      topk_select_kernel<false, false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
+      topk_select_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
                                                                            sel_count, s.n_groups, s.max_len,
                                                                            s.budget, nchunk);
   }

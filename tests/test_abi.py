@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     lib = L.lib()
-    assert lib.spc_abi_version() == 1
+    assert lib.spc_abi_version() == 2
     assert lib.spc_status_string(0) == b"ok"
     assert b"workspace" in lib.spc_status_string(L.SPC_ERR_WORKSPACE)
 
@@ -45,7 +45,8 @@ def _shape(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(n_q_heads=30), dict(n_groups=3), dict(budget=0), dict(budget=5000),
-                                 dict(batch=0), dict(scale=0.0), dict(dtype=7), dict(n_groups=4)])
+                                 dict(batch=0), dict(scale=0.0), dict(dtype=7),
+                                 dict(n_q_heads=48, n_kv_heads=16, n_groups=12)])
 def test_invalid_shapes_are_rejected_before_launch(bad):
     lib = L.lib()
     s = _shape(**bad)
@@ -213,26 +214,37 @@ def test_log_domain_scoring_sizes_and_validation():
     assert lib.spc_tile_stats_size(ctypes.byref(mla1)) == 128 * 128 * 8
     assert lib.spc_score_tile(ctypes.byref(_shape(budget=0))) == 0
     p = ctypes.c_void_p(256)
-    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, None, None) == L.SPC_ERR_INVALID_ARG
-    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, ctypes.c_void_p(260), None) == L.SPC_ERR_INVALID_ARG
-    assert lib.spc_retrieval_logits(ctypes.byref(_shape(head_dim=96)), p, p, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
-    # one KV head's keys are read through a 32-bit range: 2^23 bf16 rows of 128 reach 2 GiB
-    assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 23)), p, p, p, p, p, None) == L.SPC_ERR_UNSUPPORTED
-    assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 22)), p, p, p, p, None, None) == L.SPC_ERR_INVALID_ARG
-    need = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s))
-    # four heads per group: the tile stats are required
-    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, None, p, p, p, p, need, None) == L.SPC_ERR_INVALID_ARG
+    ts = lib.spc_tile_stats_size(ctypes.byref(s))
+    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, None, ts, None) == L.SPC_ERR_INVALID_ARG
+    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, ctypes.c_void_p(260), ts,
+                                    None) == L.SPC_ERR_INVALID_ARG
+    # a tile_stats buffer smaller than the shape needs is rejected by the library itself
+    assert lib.spc_retrieval_logits(ctypes.byref(s), p, p, p, p, p, ts - 8, None) == L.SPC_ERR_INVALID_ARG
     assert b"tile_stats" in lib.spc_last_error()
-    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, p, p, p, p, p, need - 1, None) == L.SPC_ERR_WORKSPACE
-    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, ctypes.c_void_p(260), p, p, p, p, need,
+    assert lib.spc_retrieval_logits(ctypes.byref(_shape(head_dim=96)), p, p, p, p, p, 1 << 40,
+                                    None) == L.SPC_ERR_UNSUPPORTED
+    # one KV head's keys are read through a 32-bit range: 2^23 bf16 rows of 128 reach 2 GiB
+    assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 23)), p, p, p, p, p, 1 << 40,
+                                    None) == L.SPC_ERR_UNSUPPORTED
+    assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 22)), p, p, p, p, None, 1 << 40,
+                                    None) == L.SPC_ERR_INVALID_ARG
+    need = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s))
+    # four heads per group: the tile stats are required, and their size is checked
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, None, 0, p, p, p, p, need, None) == L.SPC_ERR_INVALID_ARG
+    assert b"tile_stats" in lib.spc_last_error()
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, p, ts - 8, p, p, p, p, need,
+                                         None) == L.SPC_ERR_INVALID_ARG
+    assert b"tile_stats" in lib.spc_last_error()
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, p, ts, p, p, p, p, need - 1, None) == L.SPC_ERR_WORKSPACE
+    assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, ctypes.c_void_p(260), ts, p, p, p, p, need,
                                          None) == L.SPC_ERR_INVALID_ARG
     wide = _shape(n_q_heads=128, n_kv_heads=1, n_groups=1)                      # 128 heads in one group
-    assert lib.spc_group_max_topk_logits(ctypes.byref(wide), p, p, p, p, p, p, 1 << 40,
+    assert lib.spc_group_max_topk_logits(ctypes.byref(wide), p, p, 1 << 40, p, p, p, p, 1 << 40,
                                          None) == L.SPC_ERR_UNSUPPORTED
-    # one head per group: NULL stats are accepted (checked here with a workspace too small)
+    # one head per group: NULL stats of size 0 are accepted (checked here with a workspace too small)
     mha = _shape(n_q_heads=8, n_kv_heads=8, n_groups=8)
     need_mha = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(mha))
-    assert lib.spc_group_max_topk_logits(ctypes.byref(mha), p, None, p, p, p, p, need_mha - 1,
+    assert lib.spc_group_max_topk_logits(ctypes.byref(mha), p, None, 0, p, p, p, p, need_mha - 1,
                                          None) == L.SPC_ERR_WORKSPACE
 
 
@@ -314,3 +326,26 @@ def test_grid_limits_are_checked_before_launch():
     assert lib.spc_sparse_decode_attn(ctypes.byref(s), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
                                       L.SPC_ROWS_SLOTS, 0, 64, p, p, ws, None) == L.SPC_ERR_UNSUPPORTED
     assert b"layer range" in lib.spc_last_error()
+
+
+def test_group_and_kv_head_counts():
+    """One of n_groups and n_kv_heads must divide the other: a group inside one KV head (GQA, MHA,
+    MLA) or KV heads inside one group (one selection shared by all heads, or by pairs of KV heads).
+    The copy needs every KV head inside one group.  Only validation runs (fake pointers)."""
+    lib = L.lib()
+    p = ctypes.c_void_p(256)
+    for g in (1, 2, 4, 8, 16, 32):
+        s = _shape(n_groups=g)
+        assert lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s)) > 0, g
+        assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(s)) > 0, g
+    assert lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(_shape(n_q_heads=48, n_kv_heads=16,
+                                                                       n_groups=12))) == 0
+    lay = L.SpcKvLayout(0, 0, 0, 256, 128)
+    for g, want in ((16, L.SPC_ERR_UNSUPPORTED), (32, L.SPC_ERR_UNSUPPORTED)):
+        st = lib.spc_elastic_update(ctypes.byref(_shape(n_groups=g)), None, None, None, None, p, p, p, p,
+                                    ctypes.byref(lay), p, ctypes.byref(lay), 0, 1, L.SPC_COPY, None, None)
+        assert st == want and b"KV head" in lib.spc_last_error()
+    # one selection for every KV head passes the group check (and fails later, on the unpinned host pointer)
+    st = lib.spc_elastic_update(ctypes.byref(_shape(n_groups=1)), None, None, None, None, p, p, p, p,
+                                ctypes.byref(lay), p, ctypes.byref(lay), 0, 1, L.SPC_COPY, None, None)
+    assert st == L.SPC_ERR_NOT_MAPPED

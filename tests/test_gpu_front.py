@@ -96,6 +96,20 @@ def test_front_partial_batch_on_the_matrix_path():
     assert np.all(_f64(q[2]) == 0)
 
 
+def test_front_f32_beyond_four_sequences():
+    """float32 with more than 4 sequences: the vector kernel with 8 rows per wave (the bf16 form of
+    that batch takes the matrix path), one token outside the vocabulary, a position past the cache."""
+    p = W.PRESETS["tiny"].with_(batch=11, n_q_heads=8, n_kv_heads=2, max_len=512, budget=32, dtype="f32")
+    fw = W.generate_front(p, device="cuda", seed=12, vocab=700, hidden=3072, rope_orig=128)
+    fw.rope_factor = 4.0
+    rng = np.random.default_rng(13)
+    tokens = rng.integers(0, 700, 11).tolist()
+    positions = rng.integers(0, 512, 11).tolist()
+    tokens[4], positions[7] = 700, 512
+    q, _ = _run_front(p, fw, tokens=tokens, positions=positions)
+    assert np.all(_f64(q[4]) == 0)
+
+
 def test_front_rejects_bad_hidden_and_batch():
     p = W.PRESETS["tiny"].with_(dtype="bf16")
     fw = W.generate_front(p, device="cuda", seed=5, vocab=10, hidden=1024)

@@ -99,6 +99,26 @@ def test_mla_32k_full_shape_sampled_heads():
     assert overl and overl[0] > 0.3
 
 
+def test_mla_32k_full_shape_all_heads_of_one_sequence():
+    """Every one of the 128 heads of sequence 2 at the full 4 x 128 x 32768 shape: scores, selection and
+    attention with the output projection against the oracle's literal expansion."""
+    p = W.PRESETS["mla_32k"]
+    w = W.generate(p, device="cuda", seed=3, steps=1)
+    _check_steps(p, w, 1, batches=[2])
+
+
+def test_mla_512_position_tiles_with_ragged_lengths():
+    """The shape that scores on 512-position tiles (4 sequences x 2 head halves x 64 tiles), with
+    lengths that end inside a tile, inside its first 16-row block, and at zero: logits, tile stats
+    and Top-K against the oracle."""
+    p = W.PRESETS["mla_32k"]
+    w = W.generate(p, device="cuda", seed=4, steps=1)
+    dec_shape = api.make_shape(p.batch, p.n_q_heads, 1, p.n_q_heads, p.head_dim, p.v_dim, p.max_len, p.budget, 1,
+                               p.dtype, p.scale)
+    assert api.spc_score_tile(dec_shape) == 512
+    _check_steps(p, w, 1, lengths_override=[32768, 30001, 17, 0], heads=[0, 63, 64, 127], batches=[0, 1, 2, 3])
+
+
 @pytest.mark.parametrize("B,H,dn,dv,n_layers,layer", [(1, 3, 128, 128, 1, 0), (5, 8, 100, 77, 3, 2),
                                                        (16, 2, 33, 300, 2, 1), (4, 128, 128, 128, 1, 0)])
 def test_mla_helpers_match_literal_up_projections(B, H, dn, dv, n_layers, layer):

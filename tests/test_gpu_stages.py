@@ -33,6 +33,9 @@ SCORE_CASES = [
     ("mqa", GQA_SMALL.with_(kind="mqa", n_q_heads=8, n_kv_heads=1, max_len=600), [600, 599]),
     ("heads_per_kv_16", GQA_SMALL.with_(n_q_heads=32, n_kv_heads=2, max_len=513), [513, 257]),
     ("d64", GQA_SMALL.with_(head_dim=64, v_dim=64, max_len=300), [300, 3]),
+    # batch-level retrieval: one selection per sequence over the heads of every KV head
+    ("batch_level", GQA_SMALL.with_(kind="mqa"), [1000, 517]),
+    ("batch_level_32_heads", GQA_SMALL.with_(kind="mqa", n_q_heads=32, n_kv_heads=8, max_len=1500), [1500, 1001]),
 ]
 
 
@@ -344,14 +347,17 @@ def _pinned_kv(rng, B, NL, H, L, d, dtype):
     return t
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_copy_moves_exactly_the_loaded_rows(dtype):
+@pytest.mark.parametrize("dtype,G,H", [(torch.bfloat16, 3, 3), (torch.float32, 3, 3), (torch.bfloat16, 1, 4),
+                                       (torch.bfloat16, 2, 4)])
+def test_copy_moves_exactly_the_loaded_rows(dtype, G, H):
+    """G selection groups over H KV heads: every KV head takes the load lists of its group
+    h // (H / G) (G = H: one group per KV head; G = 1: one selection for every head)."""
     rng = np.random.default_rng(5)
-    B, G, NL, L, K, d = 2, 3, 4, 700, 64, 128
+    B, NL, L, K, d = 2, 4, 700, 64, 128
     dt = "bf16" if dtype == torch.bfloat16 else "f32"
-    shape = api.make_shape(B, G, G, G, d, d, L, K, NL, dt, 1.0)
-    host = _pinned_kv(rng, B, NL, G, L, d, dtype)
-    dev = torch.zeros((B, NL, G, K, 2, d), dtype=dtype, device="cuda")
+    shape = api.make_shape(B, H, H, G, d, d, L, K, NL, dt, 1.0)
+    host = _pinned_kv(rng, B, NL, H, L, d, dtype)
+    dev = torch.zeros((B, NL, H, K, 2, d), dtype=dtype, device="cuda")
     i32 = dict(dtype=torch.int32, device="cuda")
     slot_pos, bm = torch.empty((B, G, K), **i32), torch.empty((B, G, (L + 31) // 32), **i32)
     lp, ls, lc = torch.empty((B, G, K), **i32), torch.empty((B, G, K), **i32), torch.empty((B, G), **i32)
@@ -371,16 +377,18 @@ def test_copy_moves_exactly_the_loaded_rows(dtype):
         # layers outside [1, 3) untouched
         np.testing.assert_array_equal(draw[:, [0, 3]], braw[:, [0, 3]])
         for b in range(B):
-            for g in range(G):
+            for h in range(H):
+                g = h // (H // G)
                 for layer in (1, 2):
-                    ref = braw[b, layer, g].copy()
-                    O.elastic_copy(hraw[b, layer, g], ref, lpn[b, g, :lcn[b, g]], lsn[b, g, :lcn[b, g]])
-                    np.testing.assert_array_equal(draw[b, layer, g], ref)
+                    ref = braw[b, layer, h].copy()
+                    O.elastic_copy(hraw[b, layer, h], ref, lpn[b, g, :lcn[b, g]], lsn[b, g, :lcn[b, g]])
+                    np.testing.assert_array_equal(draw[b, layer, h], ref)
         # copies of every step leave the slots of layers 1-2 holding exactly their positions
         for b in range(B):
-            for g in range(G):
+            for h in range(H):
+                g = h // (H // G)
                 for x in np.nonzero(sp[b, g] >= 0)[0]:
-                    np.testing.assert_array_equal(draw[b, 1:3, g, x], hraw[b, 1:3, g, sp[b, g, x]])
+                    np.testing.assert_array_equal(draw[b, 1:3, h, x], hraw[b, 1:3, h, sp[b, g, x]])
 
 
 def test_copy_rejects_unpinned_host_memory():
@@ -453,6 +461,11 @@ ATTN_CASES = [
     ("d64_slots", GQA_SMALL.with_(head_dim=64, v_dim=64, max_len=300), [300, 299], api.SPC_ROWS_SLOTS),
     ("budget1", GQA_SMALL.with_(budget=1), [1000, 5], api.SPC_ROWS_SLOTS),
     ("split_tail", GQA_SMALL.with_(budget=333, max_len=2000), [2000, 1999], api.SPC_ROWS_SLOTS),
+    # batch-level retrieval: the heads of every KV head attend over one shared selection
+    ("batch_level_slots", GQA_SMALL.with_(kind="mqa"), [1000, 517], api.SPC_ROWS_SLOTS),
+    ("batch_level_gather", GQA_SMALL.with_(kind="mqa"), [1000, 0], api.SPC_ROWS_GATHER),
+    ("batch_level_32_heads_slots", GQA_SMALL.with_(kind="mqa", n_q_heads=32, n_kv_heads=8, max_len=1500),
+     [1500, 1001], api.SPC_ROWS_SLOTS),
 ]
 
 
