@@ -356,6 +356,26 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
                            size_t ws_bytes, void* stream);
 
 /*
+ * spc_sparse_decode_attn without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, checks, kernels and output as spc_sparse_decode_attn, with the split-K
+ * partials kept in a scratch array of 64 MiB that the library holds on each GPU it runs on until
+ * the process ends.  The call allocates and frees nothing.
+ *   - A layer range whose partials, batch x layers x H_q x splits x (v_dim + 2) x 4 bytes (splits =
+ *     ceil(budget / 128), or / 64 with 8 query heads per workgroup), exceed 64 MiB is rejected with
+ *     SPC_ERR_WORKSPACE before anything launches: split the layer range.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (on different
+ *     streams, or from different threads) race and corrupt each other's outputs; order them.
+ *   - The array keeps the last call's partials; no part of it needs to start at zero (every split
+ *     writes all of its partials before the merge reads them).
+ *   - The first call on a device resolves the array's device address (SPC_ERR_HIP if that fails).
+ */
+int spc_sparse_decode_attn_noalloc(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                                   const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count,
+                                   int rows_mode, int32_t layer_begin, int32_t layer_end, float* out,
+                                   void* stream);
+
+/*
  * The two halves of spc_sparse_decode_attn (split-K), for a caller that runs them
  * apart (the merge on another stream, or later) or times them:
  *   spc_attn_partial  attends every split of the rows and leaves, in ws, each split's

@@ -83,6 +83,8 @@ SIGNATURES = {
     "spc_elastic_reset": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P]),
     "spc_sparse_decode_attn": (_I, [ctypes.POINTER(SpcShape), _P, ctypes.POINTER(SpcQLayout), _P,
                                     ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _P, _SZ, _P]),
+    "spc_sparse_decode_attn_noalloc": (_I, [ctypes.POINTER(SpcShape), _P, ctypes.POINTER(SpcQLayout), _P,
+                                            ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _P]),
     "spc_attn_partial": (_I, [ctypes.POINTER(SpcShape), _P, ctypes.POINTER(SpcQLayout), _P,
                               ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _SZ, _P]),
     "spc_attn_merge": (_I, [ctypes.POINTER(SpcShape), _I32, _I32, _P, _SZ, _P, _P]),

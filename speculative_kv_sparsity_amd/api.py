@@ -23,7 +23,7 @@ __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version",
            "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds",
            "spc_elastic_plan_lag1", "spc_retrieval_logits", "spc_group_max_topk_logits", "spc_score_tile",
            "spc_tile_stats_size", "tile_stats_shape", "spc_attn_partial", "spc_attn_merge",
-           "spc_mla_expand"]
+           "spc_mla_expand", "spc_sparse_decode_attn_noalloc"]
 
 
 class SpcError(RuntimeError):
@@ -176,6 +176,18 @@ def spc_sparse_decode_attn(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvL
         ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
         int(rows_mode), int(layer_begin), int(layer_end), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def spc_sparse_decode_attn_noalloc(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvLayout, rows, row_count,
+                                   rows_mode: int, layer_begin: int, layer_end: int, out, stream=None) -> None:
+    """spc_sparse_decode_attn with its partials in the library's scratch array (no workspace)."""
+    _dev(out, "out")
+    for t, n in ((q, "q"), (kv, "kv"), (rows, "rows")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a device tensor")
+    _check(L.lib().spc_sparse_decode_attn_noalloc(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
+        int(rows_mode), int(layer_begin), int(layer_end), _ptr(out), _stream(stream)))
 
 
 def spc_attn_partial(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvLayout, rows, row_count, rows_mode: int,

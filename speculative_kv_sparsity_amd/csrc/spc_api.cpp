@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/spc.h"
@@ -67,6 +68,40 @@ int check_shape(const spc_shape* s) {
 }
 
 hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
+
+}  // namespace
+
+// Scratch of spc_sparse_decode_attn_noalloc: the split-K partials of one call live in this array,
+// which the HIP runtime places in each GPU's memory when it loads the library's code there and
+// keeps until the process ends.  Host code never passes its name to a kernel (in host code the name
+// is a stand-in, not a device address): scratch_address() resolves the device address, once per
+// device, and every launch uses that.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];       // device address of `scratch` per device, resolved on first use
+
+// The device address of `scratch` on the current device (hipGetSymbolAddress with that device current,
+// checked, kept per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPC_OK;
+}
 
 }  // namespace
 
@@ -262,7 +297,7 @@ namespace {
 // Arguments of the partial half (and of the whole call, which adds `out`).
 int check_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv, const spc_kv_layout* kv_l,
                const int32_t* rows, const int32_t* row_count, int rows_mode, int32_t layer_begin, int32_t layer_end,
-               void* ws, size_t ws_bytes) {
+               void* ws, size_t ws_bytes, size_t need) {
   if (int e = check_shape(s)) return e;
   if (!q || !q_l || !kv || !kv_l || !rows) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
   if (rows_mode != SPC_ROWS_SLOTS && rows_mode != SPC_ROWS_GATHER)
@@ -295,7 +330,6 @@ int check_attn(const spc_shape* s, const void* q, const spc_q_layout* q_l, const
   if ((kv_l->s_b * eb) % 16 || (kv_l->s_layer * eb) % 16 || (kv_l->s_head * eb) % 16 || (kv_l->s_row * eb) % 16 ||
       (kv_l->s_kv * eb) % 16)
     return fail(SPC_ERR_INVALID_ARG, "K/V strides must be multiples of 16 bytes");
-  const size_t need = spc::attn_ws_bytes(*s);
   if (ws_bytes < need || !ws)
     return fail(SPC_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
   if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -309,7 +343,8 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
                            const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
                            int32_t layer_begin, int32_t layer_end, float* out, void* ws, size_t ws_bytes,
                            void* stream) {
-  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws, ws_bytes))
+  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws, ws_bytes,
+                            spc::attn_ws_bytes(*s)))
     return e;
   if (!out || !aligned16(out)) return fail(SPC_ERR_INVALID_ARG, "out must be a 16-byte aligned device pointer");
   const hipError_t e = spc::launch_attn(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin, layer_end,
@@ -317,10 +352,37 @@ int spc_sparse_decode_attn(const spc_shape* s, const void* q, const spc_q_layout
   return e == hipSuccess ? ok() : hip_fail(e, "sparse decode attention launch");
 }
 
+int spc_sparse_decode_attn_noalloc(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                                   const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count,
+                                   int rows_mode, int32_t layer_begin, int32_t layer_end, float* out, void* stream) {
+  if (int e = check_shape(s)) return e;
+  if (layer_begin < 0 || layer_end > s->n_layers || layer_begin >= layer_end)
+    return fail(SPC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end, s->n_layers);
+  if (!spc::attn_supported(*s))
+    return fail(SPC_ERR_UNSUPPORTED, "attention: head_dim %d / v_dim %d with dtype %d", s->head_dim, s->v_dim,
+                s->dtype);
+  const size_t need = spc::attn_ws_bytes_layers(*s, layer_end - layer_begin);
+  if (need > kNoAllocScratchBytes)
+    return fail(SPC_ERR_WORKSPACE, "the allocation-free attention needs %zu bytes of scratch for %d layers, its "
+                "array holds %zu: split the layer range, or call spc_sparse_decode_attn with a workspace", need,
+                layer_end - layer_begin, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (int e = scratch_address(&ws)) return e;
+  // the partials of this layer range only (the launch lays them out for [layer_begin, layer_end))
+  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws,
+                         kNoAllocScratchBytes, need))
+    return e;
+  if (!out || !aligned16(out)) return fail(SPC_ERR_INVALID_ARG, "out must be a 16-byte aligned device pointer");
+  const hipError_t e = spc::launch_attn(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin, layer_end,
+                                        out, ws, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "sparse decode attention (allocation-free) launch");
+}
+
 int spc_attn_partial(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
                      const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
                      int32_t layer_begin, int32_t layer_end, void* ws, size_t ws_bytes, void* stream) {
-  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws, ws_bytes))
+  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer_begin, layer_end, ws, ws_bytes,
+                            spc::attn_ws_bytes(*s)))
     return e;
   const hipError_t e = spc::launch_attn_partial(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer_begin,
                                                 layer_end, ws, as_stream(stream));

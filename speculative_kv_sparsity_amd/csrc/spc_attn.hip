@@ -568,11 +568,13 @@ bool attn_supported(const spc_shape& s) {
 
 int attn_splits(const spc_shape& s) { return (s.budget + rows_per_split(s) - 1) / rows_per_split(s); }
 
-size_t attn_ws_bytes(const spc_shape& s) {
+size_t attn_ws_bytes_layers(const spc_shape& s, int n_lay) {
   const size_t nsplit = (size_t)(s.budget + rows_per_split(s) - 1) / rows_per_split(s);
-  const size_t heads = (size_t)s.batch * s.n_layers * s.n_q_heads;   // one partial per head per split
+  const size_t heads = (size_t)s.batch * n_lay * s.n_q_heads;        // one partial per head per split
   return heads * nsplit * ((size_t)s.v_dim * sizeof(float) + sizeof(float2));
 }
+
+size_t attn_ws_bytes(const spc_shape& s) { return attn_ws_bytes_layers(s, s.n_layers); }
 
 namespace {
 

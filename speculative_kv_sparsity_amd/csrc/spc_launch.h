@@ -97,6 +97,7 @@ hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& ql
 hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_layout& ql, const void* kv,
                                const spc_kv_layout& kl, const int32_t* rows, const int32_t* row_count, int mode,
                                int layer_begin, int layer_end, void* ws, hipStream_t st);
+size_t attn_ws_bytes_layers(const spc_shape& s, int n_lay);   // the partials of n_lay layers of one call
 hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end, const void* ws, float* out,
                              hipStream_t st);
 

@@ -248,6 +248,21 @@ def test_log_domain_scoring_sizes_and_validation():
                                          None) == L.SPC_ERR_WORKSPACE
 
 
+def test_noalloc_attention_rejects_partials_beyond_its_scratch():
+    """The allocation-free attention holds the partials of one call in a 64 MiB array: a layer range
+    needing more is rejected before anything launches; a bad layer range too (fake pointers unused)."""
+    lib = L.lib()
+    p = ctypes.c_void_p(256)
+    ql, kl = L.SpcQLayout(4096, 0, 128), L.SpcKvLayout(0, 0, 0, 256, 128)
+    big = _shape(batch=16, n_layers=32, max_len=32768, budget=2048)    # 16 x 32 x 32 x 16 x 520 B = 136 MB
+    st = lib.spc_sparse_decode_attn_noalloc(ctypes.byref(big), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                            L.SPC_ROWS_SLOTS, 0, 32, p, None)
+    assert st == L.SPC_ERR_WORKSPACE and b"split the layer range" in lib.spc_last_error()
+    st = lib.spc_sparse_decode_attn_noalloc(ctypes.byref(big), p, ctypes.byref(ql), p, ctypes.byref(kl), p, None,
+                                            L.SPC_ROWS_SLOTS, 3, 2, p, None)
+    assert st == L.SPC_ERR_INVALID_ARG
+
+
 def test_attention_halves_validation():
     """spc_attn_partial / spc_attn_merge reject bad arguments before launching (fake pointers unused)."""
     lib = L.lib()
