@@ -196,6 +196,16 @@ def rotation(*ts, min_bytes=2 * LLC_BYTES):
     return lambda: next(it)
 
 
+def topk_plan_call(api, shape, logits, tile_stats, lengths, dec):
+    """A launcher of the fused Top-K + plan call on copies of the decoder's selection, state and plan
+    buffers (a replay must not change the decoder's own load lists, which the copy's timing reads)."""
+    sel, cnt = dec.sel_idx.clone(), dec.sel_count.clone()
+    sp, bm = dec.slot_pos.clone(), dec.resident_bm.clone()
+    lp, ls, lc = dec.load_pos.clone(), dec.load_slot.clone(), dec.load_count.clone()
+    return lambda st: api.spc_group_max_topk_plan_logits(shape, logits, tile_stats, lengths, sel, cnt, sp, bm, lp,
+                                                         ls, lc, ws=dec.ws_topk, stream=st)
+
+
 def probs_call(torch, api, shape, q, k, lengths, inputs=rotation):
     """A launcher of the probability form of stage 1 (spc_retrieval_scores: logits, then the
     normalize pass), with its own output and workspace, over rotating (or resident) copies of the
@@ -386,8 +396,11 @@ def bench_gqa(args, p, torch, W):
         timers.append(tm)
     torch.cuda.synchronize()
     nch = len(dec.chunks)
-    loaded_rows, sel_rows = moved[:, 0].tolist(), moved[:, 1].tolist()
-    spans = {"scores": ("scores", "topk"), "topk": ("topk", "plan"), "plan": ("plan", "plan_end")}
+    # rows per KV head: a group spanning several KV heads (batch-level retrieval) loads and holds its
+    # selected rows in every one of them
+    hpg = max(1, p.n_kv_heads // p.n_groups)
+    loaded_rows, sel_rows = [x * hpg for x in moved[:, 0].tolist()], [x * hpg for x in moved[:, 1].tolist()]
+    spans = {"scores": ("scores", "topk"), "topk_plan": ("topk", "plan_end")}
     for c in range(nch):
         spans.update({f"copy{c}": (f"copy{c}", f"copy{c}_end"), f"attn{c}": (f"attn{c}", f"attn{c}_end"),
                       f"attn{c}_split": (f"attn{c}", f"attn{c}_merge")})
@@ -414,6 +427,7 @@ def bench_gqa(args, p, torch, W):
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
                                                                     dec.sel_idx, dec.sel_count, ws=dec.ws_topk,
                                                                     stream=st), R),
+        "topk_plan": iso(torch, topk_plan_call(api, dec.shape, dec.logits, dec.tile_stats, tl, dec), R),
         "scores_probs": iso(torch, probs_call(torch, api, dec.shape, tq, dec.dlm_k, tl, inputs), R),
     }
     if nch:
@@ -453,7 +467,7 @@ def bench_gqa(args, p, torch, W):
     B, Hkv, Hq, d, K = p.batch, p.n_kv_heads, p.n_q_heads, p.head_dim, p.budget
     n_valid = float(np.mean(w.lengths[t0 + Wm + K_:t0 + total].sum(axis=1)))
     row = 2 * d * eb                                             # one K||V row
-    sel_per_group = float(np.mean(sel_rows)) / (B * p.n_groups)
+    sel_per_group = float(np.mean(sel_rows)) / (B * p.n_kv_heads)       # rows per (sequence, KV head)
     # algorithmic bytes per call (one launch of the stage)
     kv_bytes = B * lay0 * Hkv * sel_per_group * row                         # K/V rows read (split kernel)
     attn_bytes = kv_bytes + B * lay0 * Hq * d * 4                             # + out write (the whole call)
@@ -515,6 +529,7 @@ def bench_gqa(args, p, torch, W):
                          "transfer_fraction_vs_full_reload":
                              round(float(np.mean(loaded_rows)) * p.n_layers * row / full_reload, 4),
                          "adjacent_overlap": round(1.0 - float(np.mean(loaded_rows)) / float(np.mean(sel_rows)), 4),
+                         "rows_counted_per": "(sequence, layer, KV head)",
                          "host_link_bytes_per_step": int(float(np.mean(loaded_rows)) * off * row)}
     result["retrieval"] = {"level": "head" if p.kind != "mqa" else "batch", "groups": p.n_groups,
                            "coverage": selection_coverage(torch, p, tq, dec.dlm_k, w.host_kv, tl, dec.sel_idx,
@@ -696,7 +711,7 @@ def bench_mla(args, p, torch, W):
 
     # instrumented pass: K more steps launched back to back (no synchronize between steps), events
     # around every stage call and at the attention's merge; counts summed on the device
-    names = ("absorb", "scores", "topk", "plan", "attn", "out_proj", "end")
+    names = ("absorb", "scores", "topk", "attn", "out_proj", "end")
     timers = []
     moved = torch.zeros((K_, 3), dtype=torch.int64, device="cuda")
     mark = torch.zeros((p.batch, p.max_len + 1), dtype=torch.int32, device="cuda")
@@ -737,6 +752,7 @@ def bench_mla(args, p, torch, W):
                                                                  dec.tile_stats, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(s, dec.logits, None, tl, dec.sel_idx,
                                                                     dec.sel_count, ws=dec.ws_topk, stream=st), R),
+        "topk_plan": iso(torch, topk_plan_call(api, s, dec.logits, None, tl, dec), R),
         "scores_probs": iso(torch, probs_call(torch, api, s, dec.q_abs, dec.latent, tl, inputs), R),
         "attn": iso(torch, lambda st: api.spc_sparse_decode_attn(
             s, dec.q_abs, dec.q_l, lat()[0], dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0, 1,
@@ -822,7 +838,7 @@ def bench_mla_literal(args, p, torch, W):
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / K_
 
-    names = ("absorb", "scores", "topk", "plan", "expand", "attn", "end")
+    names = ("absorb", "scores", "topk", "expand", "attn", "end")
     stage = {k: [] for k in names[:-1]}
     loaded, sel_rows = [], []
     for t in range(Wm + K_, total):

@@ -242,6 +242,25 @@ int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const flo
                               int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stage 2 and the plan of stage 3 in one call, as the step runs them: the selection of
+ * spc_group_max_topk_logits, then the SPC_PLAN half of spc_elastic_update on it (blog section 4: the
+ * retrieval head's Top-K, then to_load = selected - resident).  Where the selection, the plan's two
+ * lists and a bitmap of the selection fit 64 KB of LDS (budget + max(4096, 2 budget + ceil(max_len/32))
+ * words) and the two-phase select applies, the plan runs at the end of the Top-K's last kernel while
+ * the selection is still in LDS; otherwise the plan is its own launch.  The outputs are exactly those
+ * of the two calls.
+ *   logits, tile_stats, tile_stats_bytes, lengths, sel_idx, sel_count, ws, ws_bytes
+ *              as for spc_group_max_topk_logits (same workspace size)
+ *   slot_pos, resident_bm, load_pos, load_slot, load_count
+ *              as for spc_elastic_update (state in/out, plan out); budget <= 8192
+ */
+int spc_group_max_topk_plan_logits(const spc_shape* s, const float* logits, const float* tile_stats,
+                                   size_t tile_stats_bytes, const int32_t* lengths, int32_t* sel_idx,
+                                   int32_t* sel_count, int32_t* slot_pos, uint32_t* resident_bm,
+                                   int32_t* load_pos, int32_t* load_slot, int32_t* load_count, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Stage 3 - elastic loading (blog section 4 pseudocode: the positions to load
  * are the new selection minus the resident ones, fetched asynchronously; blog
  * section 6 worked example {1,8,21,35} -> {1,8,21,50} loads only 50, in place

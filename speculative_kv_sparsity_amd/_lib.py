@@ -77,6 +77,8 @@ SIGNATURES = {
     "spc_score_tile": (_I, [ctypes.POINTER(SpcShape)]),
     "spc_tile_stats_size": (_SZ, [ctypes.POINTER(SpcShape)]),
     "spc_group_max_topk_logits": (_I, [ctypes.POINTER(SpcShape), _P, _P, _SZ, _P, _P, _P, _P, _SZ, _P]),
+    "spc_group_max_topk_plan_logits": (_I, [ctypes.POINTER(SpcShape), _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _SZ, _P]),
     "spc_elastic_update": (_I, [ctypes.POINTER(SpcShape), _P, _P, _P, _P, _P, _P, _P, _P,
                                 ctypes.POINTER(SpcKvLayout), _P, ctypes.POINTER(SpcKvLayout), _I32, _I32,
                                 ctypes.c_uint, _P, _P]),

@@ -23,7 +23,7 @@ __all__ = ["SpcError", "make_shape", "kv_layout", "q_layout", "spc_abi_version",
            "spc_mla_out_proj", "rope_params", "spc_retrieval_head_qk", "spc_offload_thresholds",
            "spc_elastic_plan_lag1", "spc_retrieval_logits", "spc_group_max_topk_logits", "spc_score_tile",
            "spc_tile_stats_size", "tile_stats_shape", "spc_attn_partial", "spc_attn_merge",
-           "spc_mla_expand", "spc_sparse_decode_attn_noalloc"]
+           "spc_mla_expand", "spc_sparse_decode_attn_noalloc", "spc_group_max_topk_plan_logits"]
 
 
 class SpcError(RuntimeError):
@@ -147,6 +147,22 @@ def spc_group_max_topk_logits(shape: SpcShape, logits, tile_stats, lengths, sel_
     _check(L.lib().spc_group_max_topk_logits(ctypes.byref(shape), _ptr(logits), _ptr(tile_stats),
                                              _nbytes(tile_stats), _ptr(lengths), _ptr(sel_idx), _ptr(sel_count),
                                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spc_group_max_topk_plan_logits(shape: SpcShape, logits, tile_stats, lengths, sel_idx, sel_count, slot_pos,
+                                   resident_bm, load_pos, load_slot, load_count, ws=None, stream=None) -> None:
+    """spc_group_max_topk_logits followed by the SPC_PLAN half of spc_elastic_update, in one call."""
+    for t, n in ((logits, "logits"), (lengths, "lengths"), (sel_idx, "sel_idx"), (sel_count, "sel_count"),
+                 (slot_pos, "slot_pos"), (resident_bm, "resident_bm"), (load_pos, "load_pos"),
+                 (load_slot, "load_slot"), (load_count, "load_count")):
+        _dev(t, n)
+    if tile_stats is not None:
+        _dev(tile_stats, "tile_stats")
+    ws = _workspace(SPC_CALL_TOPK, shape, logits.device) if ws is None else ws
+    _check(L.lib().spc_group_max_topk_plan_logits(
+        ctypes.byref(shape), _ptr(logits), _ptr(tile_stats), _nbytes(tile_stats), _ptr(lengths), _ptr(sel_idx),
+        _ptr(sel_count), _ptr(slot_pos), _ptr(resident_bm), _ptr(load_pos), _ptr(load_slot), _ptr(load_count),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spc_elastic_update(shape: SpcShape, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot,

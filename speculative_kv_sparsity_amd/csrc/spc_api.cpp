@@ -173,9 +173,10 @@ int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const
   return e == hipSuccess ? ok() : hip_fail(e, "retrieval logits launch");
 }
 
-int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats,
-                              size_t tile_stats_bytes, const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count,
-                              void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// Arguments of stage 2 on the log-domain form (spc_group_max_topk_logits and the fused call).
+int check_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats, size_t tile_stats_bytes,
+                      const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, size_t ws_bytes) {
   if (int e = check_shape(s)) return e;
   if (!logits || !lengths || !sel_idx || !sel_count)
     return fail(SPC_ERR_INVALID_ARG, "NULL logits, lengths, sel_idx or sel_count");
@@ -195,10 +196,49 @@ int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const flo
   if (ws_bytes < need || !ws)
     return fail(SPC_ERR_WORKSPACE, "group max / top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
   if (!aligned16(ws)) return fail(SPC_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return SPC_OK;
+}
+}  // namespace
+
+int spc_group_max_topk_logits(const spc_shape* s, const float* logits, const float* tile_stats,
+                              size_t tile_stats_bytes, const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_topk_logits(s, logits, tile_stats, tile_stats_bytes, lengths, sel_idx, sel_count, ws, ws_bytes))
+    return e;
+  const int gq = s->n_q_heads / s->n_groups;
   const float2* st = gq > 1 ? reinterpret_cast<const float2*>(tile_stats) : nullptr;
   const hipError_t e = spc::launch_topk(*s, logits, st, spc::score_tile(*s), lengths, sel_idx, sel_count, ws,
                                         as_stream(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "group max / top-k (logits) launch");
+}
+
+int spc_group_max_topk_plan_logits(const spc_shape* s, const float* logits, const float* tile_stats,
+                                   size_t tile_stats_bytes, const int32_t* lengths, int32_t* sel_idx,
+                                   int32_t* sel_count, int32_t* slot_pos, uint32_t* resident_bm, int32_t* load_pos,
+                                   int32_t* load_slot, int32_t* load_count, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (int e = check_topk_logits(s, logits, tile_stats, tile_stats_bytes, lengths, sel_idx, sel_count, ws, ws_bytes))
+    return e;
+  if (!slot_pos || !resident_bm || !load_pos || !load_slot || !load_count)
+    return fail(SPC_ERR_INVALID_ARG, "the plan needs slot_pos, resident_bm, load_pos, load_slot and load_count");
+  if (!aligned4(slot_pos) || !aligned4(resident_bm) || !aligned4(load_pos) || !aligned4(load_slot) ||
+      !aligned4(load_count))
+    return fail(SPC_ERR_INVALID_ARG, "misaligned plan buffer");
+  if (s->budget > spc::kPlanMaxBudget)
+    return fail(SPC_ERR_UNSUPPORTED, "budget %d exceeds the plan kernel's %d", s->budget, spc::kPlanMaxBudget);
+  const int gq = s->n_q_heads / s->n_groups;
+  const float2* st = gq > 1 ? reinterpret_cast<const float2*>(tile_stats) : nullptr;
+  hipError_t e;
+  if (spc::select_plan_fused(*s)) {
+    e = spc::launch_select_plan(*s, logits, st, spc::score_tile(*s), lengths, sel_idx, sel_count, slot_pos,
+                                resident_bm, load_pos, load_slot, load_count, ws, as_stream(stream));
+  } else {
+    e = spc::launch_topk(*s, logits, st, spc::score_tile(*s), lengths, sel_idx, sel_count, ws, as_stream(stream));
+    if (e == hipSuccess)
+      e = spc::launch_plan(*s, sel_idx, sel_count, slot_pos, resident_bm, load_pos, load_slot, load_count,
+                           as_stream(stream));
+  }
+  return e == hipSuccess ? ok() : hip_fail(e, "group max / top-k + plan launch");
 }
 
 int spc_group_max_topk(const spc_shape* s, const float* probs, const int32_t* lengths, int32_t* sel_idx,

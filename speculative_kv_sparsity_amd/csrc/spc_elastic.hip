@@ -24,12 +24,11 @@
 
 #include "spc_common.h"
 #include "spc_launch.h"
+#include "spc_plan.h"
 
 namespace spc {
 
 namespace {
-
-constexpr int kPlanThreads = 1024;
 
 __device__ __forceinline__ bool sorted_contains(const int32_t* a, int n, int32_t v) {
   int lo = 0, hi = n;
@@ -122,7 +121,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 // since every position of S is resident after the step, the resident bitmap is
 // rewritten whole from that bitmap (coalesced stores, no atomics).  Slot map entries
 // and selection entries are read into registers (CPT contiguous ones per thread);
-// one block scan of packed 16-bit counts orders both compactions.
+// one block scan of packed 16-bit counts orders both compactions (plan_bitmap).
 template <int CPT>
 __global__ __launch_bounds__(kPlanThreads) void plan_bm_kernel(const int32_t* __restrict__ sel_idx,
                                                                const int32_t* __restrict__ sel_count,
@@ -136,72 +135,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_bm_kernel(const int32_t* __
   int32_t* sF = sL + K;                                    // freed slots, ascending [K]
   uint32_t* sB = reinterpret_cast<uint32_t*>(sF + K);      // bitmap of S [bm_words]
   __shared__ uint32_t scan_smem[16];
-
   const int inst = blockIdx.x;
-  const int tid = threadIdx.x;
   int c = sel_count[inst];
   c = c < 0 ? 0 : (c > K ? K : c);
-  const int32_t* S = sel_idx + (size_t)inst * K;
-  int32_t* sp = slot_pos + (size_t)inst * K;
-  uint32_t* bm = resident_bm + (size_t)inst * bm_words;
-  const int32_t pos_end = bm_words * 32;                   // positions outside [0, pos_end) are never loaded
-
-  const int Cx = (K + kPlanThreads - 1) / kPlanThreads;   // <= CPT
-  const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
-  const int Ci = (c + kPlanThreads - 1) / kPlanThreads;   // <= Cx
-  const int i0 = min(tid * Ci, c), i1 = min(i0 + Ci, c);
-  int32_t pos[CPT], sel[CPT];
-  uint32_t oldw[CPT];
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    pos[u] = x0 + u < x1 ? sp[x0 + u] : -1;
-    sel[u] = i0 + u < i1 ? S[i0 + u] : -1;
-  }
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {                          // resident before the step (outside: never loaded)
-    const int32_t j = sel[u];
-    oldw[u] = j >= 0 && j < pos_end ? bm[j >> 5] : 0xFFFFFFFFu;
-  }
-  for (int w = tid; w < bm_words; w += kPlanThreads) sB[w] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    const int32_t j = sel[u];
-    if (j >= 0 && j < pos_end) atomicOr(&sB[j >> 5], 1u << (j & 31));
-  }
-  __syncthreads();
-  uint32_t fmask = 0u, lmask = 0u, nf_loc = 0u, nl_loc = 0u;
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    const int32_t q = pos[u];
-    const bool keep = q >= 0 && q < pos_end && ((sB[q >> 5] >> (q & 31)) & 1u);
-    if (x0 + u < x1 && !keep) { fmask |= 1u << u; ++nf_loc; }
-    const int32_t j = sel[u];
-    if (i0 + u < i1 && !((oldw[u] >> (j & 31)) & 1u)) { lmask |= 1u << u; ++nl_loc; }
-  }
-  uint32_t tot;
-  const uint32_t before = block_excl_scan(nf_loc | (nl_loc << 16), scan_smem, tot);   // counts <= K < 2^16
-  uint32_t fo = before & 0xFFFFu, lo = before >> 16;
-  const int nf = (int)(tot & 0xFFFFu), nl = (int)(tot >> 16);
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    if ((fmask >> u) & 1u) sF[fo++] = x0 + u;
-    if ((lmask >> u) & 1u) sL[lo++] = sel[u];
-  }
-  __syncthreads();
-
-  // apply: the i-th position to load goes to the i-th freed slot, the rest empty; the
-  // resident set becomes S
-  for (int i = tid; i < nf; i += kPlanThreads) sp[sF[i]] = i < nl ? sL[i] : -1;
-  for (int w = tid; w < bm_words; w += kPlanThreads) bm[w] = sB[w];
-  int32_t* lp = load_pos + (size_t)inst * K;
-  int32_t* ls = load_slot + (size_t)inst * K;
-  for (int i = tid; i < K; i += kPlanThreads) {
-    const bool v = i < nl;
-    lp[i] = v ? sL[i] : -1;
-    ls[i] = v ? sF[i] : -1;
-  }
-  if (tid == 0) load_count[inst] = nl;
+  plan_bitmap<CPT>(sel_idx + (size_t)inst * K, c, slot_pos + (size_t)inst * K, resident_bm + (size_t)inst * bm_words,
+                   load_pos + (size_t)inst * K, load_slot + (size_t)inst * K, load_count + inst, K, bm_words, sL, sF,
+                   sB, scan_smem);
 }
 
 // The plan of the pipelined loop: the target model attends over the current

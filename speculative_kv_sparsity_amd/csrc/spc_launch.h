@@ -55,6 +55,13 @@ size_t topk_ws_bytes(const spc_shape& s);
 // stat_tile positions [B*Hq][ceil(max_len/stat_tile)] (NULL allowed with one head per group)
 hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
                        const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, hipStream_t st);
+// stage 2 and the elastic plan in one launch sequence (the plan inside the Top-K's last kernel) where
+// select_plan_fused(s); same workspace as launch_topk
+bool select_plan_fused(const spc_shape& s);
+hipError_t launch_select_plan(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
+                              const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, int32_t* slot_pos,
+                              uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                              void* ws, hipStream_t st);
 
 // ---- stage 3: elastic plan / copy / reset
 constexpr int kPlanMaxBudget = 8192;

@@ -33,9 +33,11 @@
 //   with two block scans over per-thread contiguous index ranges.  For
 //   n <= 32768 the keys are staged in LDS (one pad word per 32 keys keeps the
 //   contiguous-range sweeps free of bank conflicts); longer rows are read from
-//   the workspace (L2) in every pass.
+//   the workspace (L2) in every pass.  The LDS form can end with the elastic
+//   plan of its instance (spc_plan.h), so the selection is never re-read.
 #include "spc_common.h"
 #include "spc_launch.h"
+#include "spc_plan.h"
 
 namespace spc {
 
@@ -44,6 +46,7 @@ namespace {
 constexpr int kKeyThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kBins1 = 256;                       // first digit: key bits 31..24
+static_assert(kSelThreads == kPlanThreads, "the fused plan runs on the select's workgroup");
 
 // Order-preserving map from fp32 bits to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -361,14 +364,27 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
 // digit is above the threshold digit (always selected) and those equal to it
 // (candidates), and histograms the candidates' second digit.  Every later step
 // touches only the candidates.
-template <bool RAW>
+//
+// With CPT > 0 the kernel also makes the instance's elastic plan: thread t's 32 keys are positions
+// [32t, 32t + 32), so its selection mask is word t of the selection's bitmap, and the plan
+// (plan_words) runs on those words with the keys' LDS, no longer read, holding its lists.
+struct PlanBufs {
+  int32_t* slot_pos;
+  uint32_t* resident_bm;
+  int32_t* load_pos;
+  int32_t* load_slot;
+  int32_t* load_count;
+  int bm_words;
+};
+
+template <bool RAW, int CPT>
 __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint32_t* __restrict__ keys,
                                                                       const uint32_t* __restrict__ chist,
                                                                       const int32_t* __restrict__ lengths,
                                                                       int32_t* __restrict__ sel_idx,
                                                                       int32_t* __restrict__ sel_count,
                                                                       int n_groups, int max_len, int budget,
-                                                                      int nchunk) {
+                                                                      int nchunk, PlanBufs pb) {
   __shared__ uint4 skeys[kTopkLdsKeys / 4];
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t scan_smem[16];
@@ -386,9 +402,33 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   const int K = budget;
   const int tid = threadIdx.x;
   int32_t* out = sel_idx + (size_t)inst * K;
+  constexpr bool kPlan = CPT > 0;
+  constexpr int kP = kPlan ? CPT : 1;
+  // the plan's inputs, loaded first so that their latency hides behind the select
+  uint32_t oldw = 0u;
+  int32_t pos[kP];
+  int32_t* sp = pb.slot_pos + (size_t)inst * K;
+  uint32_t* bm = pb.resident_bm + (size_t)inst * pb.bm_words;
+  if (kPlan) {
+    const int Cx = (K + kSelThreads - 1) / kSelThreads;
+    const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
+#pragma unroll
+    for (int u = 0; u < kP; ++u) pos[u] = x0 + u < x1 ? sp[x0 + u] : -1;
+    if (tid < pb.bm_words) oldw = bm[tid];
+  }
+  auto plan = [&](uint32_t selw) {
+    int32_t* sL = reinterpret_cast<int32_t*>(skeys);
+    plan_words<kP>(selw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
+                   pb.load_count + inst, K, pb.bm_words, sL, sL + K, reinterpret_cast<uint32_t*>(sL + 2 * K),
+                   scan_smem);
+  };
   if (n <= K) {
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
     if (tid == 0) sel_count[inst] = n;
+    if (kPlan) {
+      const int r = n - 32 * tid;                  // this thread's word: positions [32 tid, 32 tid + 32)
+      plan(r >= 32 ? 0xFFFFFFFFu : r > 0 ? (1u << r) - 1u : 0u);
+    }
     return;
   }
   const uint32_t* kin = keys + (size_t)inst * max_len;
@@ -519,10 +559,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   uint32_t keep_eq = eqm;
   for (int drop = (int)eq - take_eq; drop > 0; --drop) keep_eq &= ~(0x80000000u >> __clz(keep_eq));
   int o = gt_before + min(eq_before, need);
-  for (uint32_t m = gtm | keep_eq; m; m &= m - 1) {
+  const uint32_t selw = gtm | keep_eq;
+  for (uint32_t m = selw; m; m &= m - 1) {
     if (o < K) out[o++] = 4 * v0 + __ffs(m) - 1;
   }
   if (tid == 0) sel_count[inst] = K;
+  if (kPlan) plan(selw);
 }
 
 }  // namespace
@@ -533,44 +575,99 @@ size_t topk_ws_bytes(const spc_shape& s) {
   return inst * (size_t)s.max_len * sizeof(uint32_t) + inst * nchunk * kBins1 * sizeof(uint32_t);
 }
 
-hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
-                       const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, hipStream_t st) {
+namespace {
+
+// The keys pass (group max, first-digit histograms), unless one head per group with rows that fit
+// LDS lets the select key the scores and count the first digit itself.  *kin: the keys the select
+// reads (with one head per group, the scores' own words, keyed on load).
+hipError_t launch_keys(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
+                       const int32_t* lengths, void* ws, hipStream_t st, const uint32_t** kin, uint32_t** chist) {
   const int inst = s.batch * s.n_groups;
   const int nchunk = (s.max_len + kKeyChunk - 1) / kKeyChunk;
   const int ntiles = stat_tile > 0 ? (s.max_len + stat_tile - 1) / stat_tile : 0;
   uint32_t* keys = static_cast<uint32_t*>(ws);
-  uint32_t* chist = keys + (size_t)inst * s.max_len;
-  const dim3 kg(nchunk, inst);
-  // one head per group with rows that fit LDS: the select keys the scores and counts the first
-  // digit itself, so no keys pass runs
+  *chist = keys + (size_t)inst * s.max_len;
   const bool raw = s.n_q_heads == s.n_groups;
-  if (!(raw && s.max_len <= kTopkLdsKeys)) {
-    if (stats)
-      topk_keys_kernel<true><<<kg, kKeyThreads, 0, st>>>(scores, stats, lengths, keys, chist, s.n_q_heads,
-                                                         s.n_groups, s.max_len, s.budget, nchunk, ntiles, stat_tile);
-    else
-      topk_keys_kernel<false><<<kg, kKeyThreads, 0, st>>>(scores, nullptr, lengths, keys, chist, s.n_q_heads,
-                                                          s.n_groups, s.max_len, s.budget, nchunk, 0, 1);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // one head per group: the keys are the scores' own order keys, taken on load
-  const uint32_t* kin = raw ? reinterpret_cast<const uint32_t*>(scores) : keys;
+  *kin = raw ? reinterpret_cast<const uint32_t*>(scores) : keys;
+  if (raw && s.max_len <= kTopkLdsKeys) return hipSuccess;
+  const dim3 kg(nchunk, inst);
+  if (stats)
+    topk_keys_kernel<true><<<kg, kKeyThreads, 0, st>>>(scores, stats, lengths, keys, *chist, s.n_q_heads,
+                                                       s.n_groups, s.max_len, s.budget, nchunk, ntiles, stat_tile);
+  else
+    topk_keys_kernel<false><<<kg, kKeyThreads, 0, st>>>(scores, nullptr, lengths, keys, *chist, s.n_q_heads,
+                                                        s.n_groups, s.max_len, s.budget, nchunk, 0, 1);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
+                       const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, void* ws, hipStream_t st) {
+  const int inst = s.batch * s.n_groups;
+  const int nchunk = (s.max_len + kKeyChunk - 1) / kKeyChunk;
+  const uint32_t* kin;
+  uint32_t* chist;
+  const hipError_t e = launch_keys(s, scores, stats, stat_tile, lengths, ws, st, &kin, &chist);
+  if (e != hipSuccess) return e;
+  const bool raw = s.n_q_heads == s.n_groups;
+  const PlanBufs none{};
   if (s.max_len <= kTopkLdsKeys) {
     if (raw)
-      topk_select_lds_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
-                                                                       s.n_groups, s.max_len, s.budget, nchunk);
+      topk_select_lds_kernel<true, 0><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                          s.n_groups, s.max_len, s.budget, nchunk,
+                                                                          none);
     else
-      topk_select_lds_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
-                                                                        s.n_groups, s.max_len, s.budget, nchunk);
+      topk_select_lds_kernel<false, 0><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
+                                                                           sel_count, s.n_groups, s.max_len,
+                                                                           s.budget, nchunk, none);
   } else {
     if (raw)
       topk_select_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
-                                                                          s.n_groups, s.max_len, s.budget, nchunk);
+                                                                   s.n_groups, s.max_len, s.budget, nchunk);
     else
-      topk_select_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
-                                                                           sel_count, s.n_groups, s.max_len,
-                                                                           s.budget, nchunk);
+      topk_select_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                    s.n_groups, s.max_len, s.budget, nchunk);
+  }
+  return hipGetLastError();
+}
+
+bool select_plan_fused(const spc_shape& s) {
+  // the plan's lists (2 K words) and the bitmap (<= 1024 words) fit the keys' LDS
+  return s.max_len <= kTopkLdsKeys && s.budget <= kPlanMaxBudget && 2 * s.budget + 1024 <= kTopkLdsKeys;
+}
+
+hipError_t launch_select_plan(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
+                              const int32_t* lengths, int32_t* sel_idx, int32_t* sel_count, int32_t* slot_pos,
+                              uint32_t* resident_bm, int32_t* load_pos, int32_t* load_slot, int32_t* load_count,
+                              void* ws, hipStream_t st) {
+  if (!select_plan_fused(s)) return hipErrorInvalidValue;
+  const int inst = s.batch * s.n_groups;
+  const int nchunk = (s.max_len + kKeyChunk - 1) / kKeyChunk;
+  const uint32_t* kin;
+  uint32_t* chist;
+  const hipError_t e = launch_keys(s, scores, stats, stat_tile, lengths, ws, st, &kin, &chist);
+  if (e != hipSuccess) return e;
+  const bool raw = s.n_q_heads == s.n_groups;
+  const PlanBufs pb{slot_pos, resident_bm, load_pos, load_slot, load_count, (s.max_len + 31) / 32};
+  const int cpt = (s.budget + kSelThreads - 1) / kSelThreads;
+  switch ((cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8) * (raw ? -1 : 1)) {
+#define SPC_CASE(N)                                                                                           \
+  case N:                                                                                                     \
+    topk_select_lds_kernel<false, N><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,        \
+                                                                         sel_count, s.n_groups, s.max_len,    \
+                                                                         s.budget, nchunk, pb);               \
+    break;                                                                                                    \
+  case -N:                                                                                                    \
+    topk_select_lds_kernel<true, N><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,         \
+                                                                        sel_count, s.n_groups, s.max_len,     \
+                                                                        s.budget, nchunk, pb);                \
+    break;
+    SPC_CASE(1)
+    SPC_CASE(2)
+    SPC_CASE(4)
+    SPC_CASE(8)
+#undef SPC_CASE
   }
   return hipGetLastError();
 }

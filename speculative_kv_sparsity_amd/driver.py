@@ -162,6 +162,12 @@ class SparseDecoder:
                                self.load_pos, self.load_slot, self.load_count, flags=api.SPC_PLAN,
                                plan_stream=self.main)
 
+    def topk_plan(self, lengths: torch.Tensor) -> None:
+        """Top-K and the elastic plan in one call (the plan at the end of the Top-K's last kernel)."""
+        api.spc_group_max_topk_plan_logits(self.shape, self.logits, self.tile_stats, lengths, self.sel_idx,
+                                           self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
+                                           self.load_slot, self.load_count, ws=self.ws_topk, stream=self.main)
+
     def copy_chunk(self, c: int) -> None:
         a, z = self.chunks[c]
         api.spc_elastic_update(self.shape, None, None, None, None, self.load_pos, self.load_slot, self.load_count,
@@ -215,9 +221,7 @@ class SparseDecoder:
         mark("scores", self.main)
         self.scores(q, lengths)
         mark("topk", self.main)
-        self.topk(lengths)
-        mark("plan", self.main)
-        self.plan()
+        self.topk_plan(lengths)
         mark("plan_end", self.main)
         side_used = False
         if self.n_res:
@@ -423,11 +427,9 @@ class MlaDecoder:
         mark("scores", st)
         api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.tile_stats, stream=st)
         mark("topk", st)
-        api.spc_group_max_topk_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk,
-                                      stream=st)
-        mark("plan", st)
-        api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
-                               self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)
+        api.spc_group_max_topk_plan_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count,
+                                           self.slot_pos, self.resident_bm, self.load_pos, self.load_slot,
+                                           self.load_count, ws=self.ws_topk, stream=st)
         mark("attn", st)
         self.attend(mark=timer.mark if timer is not None else None)
         mark("out_proj", st)
@@ -483,11 +485,9 @@ class MlaLiteralDecoder(MlaDecoder):
         mark("scores", st)
         api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.tile_stats, stream=st)
         mark("topk", st)
-        api.spc_group_max_topk_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count, ws=self.ws_topk,
-                                      stream=st)
-        mark("plan", st)
-        api.spc_elastic_update(s, self.sel_idx, self.sel_count, self.slot_pos, self.resident_bm, self.load_pos,
-                               self.load_slot, self.load_count, flags=api.SPC_PLAN, plan_stream=st)
+        api.spc_group_max_topk_plan_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count,
+                                           self.slot_pos, self.resident_bm, self.load_pos, self.load_slot,
+                                           self.load_count, ws=self.ws_topk, stream=st)
         mark("expand", st)
         self.expand(q_nope, q_rope, st)
         mark("attn", st)

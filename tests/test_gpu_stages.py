@@ -95,12 +95,12 @@ def test_topk_exact_on_gpu_scores_and_tolerant_vs_oracle_chain(name, p, lengths)
 # --------------------------------------------------------------- log-domain form of stages 1-2
 
 
-def _logits(p, w, lengths):
+def _logits(p, w, lengths, t=0):
     shape = shape_of(p)
     nan = float("nan")
     logits = torch.full((p.batch, p.n_q_heads, p.max_len), nan, device="cuda")
     stats = torch.full(api.tile_stats_shape(shape), nan, device="cuda")
-    api.spc_retrieval_logits(shape, w.q[0].contiguous(), w.dlm_k, dev_lengths(lengths), logits, stats)
+    api.spc_retrieval_logits(shape, w.q[t].contiguous(), w.dlm_k, dev_lengths(lengths), logits, stats)
     torch.cuda.synchronize()
     return shape, logits, stats
 
@@ -514,3 +514,66 @@ def test_topk_exact_long_rows_and_large_budget():
     shape = api.make_shape(B, Hq, G, G, 128, 128, L, K, 1, "bf16", 1.0)
     sel_idx, sel_count = _topk_gpu(shape, torch.from_numpy(vals).cuda(), [L])
     _assert_sel_equal(sel_idx, sel_count, _oracle_topk(vals.astype(np.float64), [L], G, K), K)
+
+
+# ------------------------------------------------------------------------------ Top-K + plan in one call
+
+
+FUSED_CASES = [
+    # (name, preset, lengths per step): the plan inside the LDS select's workgroup (rows of at most
+    # 32768 positions) with several heads per group and with one (raw logits, 2 KB per thread of plan
+    # lists at budget 4096), a batch with a short and an empty sequence and a row length that is no
+    # multiple of 32, budget 8192 (8 slots per thread) with sequences at, below and just above the
+    # budget; and two where the plan runs as its own launch after the select: MHA at 64K and budget
+    # 8192 at 40000 positions
+    ("gqa_32k", W.PRESETS["b1_32k"].with_(n_layers=1), None),
+    ("mha_32k_raw", W.PRESETS["mha_64k"].with_(max_len=32768, batch=1), None),
+    ("ragged", GQA_SMALL.with_(batch=3, max_len=3000, budget=256), [[3000, 100, 0], [3000, 257, 0], [2999, 300, 5]]),
+    ("budget_8192_lds", GQA_SMALL.with_(batch=3, n_q_heads=4, n_kv_heads=2, max_len=20000, budget=8192),
+     [[20000, 5000, 8192], [19999, 8192, 8193], [20000, 8193, 12000]]),
+    ("mha_64k", W.PRESETS["mha_64k"], None),
+    ("budget_8192", GQA_SMALL.with_(batch=1, n_q_heads=4, n_kv_heads=2, max_len=40000, budget=8192), None),
+]
+
+
+@pytest.mark.parametrize("name,p,lens", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_topk_and_plan_in_one_call_equal_the_two_calls(name, p, lens):
+    steps = 3
+    w = W.generate(p, device="cuda", seed=31, steps=steps)
+    shape = shape_of(p)
+    B, G, K, L = p.batch, p.n_groups, p.budget, p.max_len
+    i32 = dict(dtype=torch.int32, device="cuda")
+
+    def state():
+        st = dict(sel=torch.full((B, G, K), -7, **i32), cnt=torch.full((B, G), -7, **i32),
+                  sp=torch.empty((B, G, K), **i32), bm=torch.empty((B, G, (L + 31) // 32), **i32),
+                  lp=torch.full((B, G, K), -7, **i32), ls=torch.full((B, G, K), -7, **i32),
+                  lc=torch.full((B, G), -7, **i32))
+        api.spc_elastic_reset(shape, -1, st["sp"], st["bm"])
+        return st
+
+    two, one = state(), state()
+    ref_slots = [[np.full(K, -1, dtype=np.int64) for _ in range(G)] for _ in range(B)]
+    for t in range(steps):
+        lengths = list(w.lengths[t]) if lens is None else lens[t]
+        _, logits, stats = _logits(p, w, lengths, t)
+        lt = dev_lengths(lengths)
+        api.spc_group_max_topk_logits(shape, logits, stats, lt, two["sel"], two["cnt"])
+        api.spc_elastic_update(shape, two["sel"], two["cnt"], two["sp"], two["bm"], two["lp"], two["ls"], two["lc"],
+                               flags=api.SPC_PLAN)
+        api.spc_group_max_topk_plan_logits(shape, logits, stats, lt, one["sel"], one["cnt"], one["sp"], one["bm"],
+                                           one["lp"], one["ls"], one["lc"])
+        torch.cuda.synchronize()
+        for k in two:
+            np.testing.assert_array_equal(one[k].cpu().numpy(), two[k].cpu().numpy(), err_msg=f"{k} at step {t}")
+        # and the selection against the fp64 oracle chain, the plan against the oracle's plan
+        gsel = sel_lists(one["sel"], one["cnt"])
+        ref_probs = O.retrieval_scores(f64(w.q[t], p.dtype), f64(w.dlm_k, p.dtype), lengths, p.scale)
+        ref_grp = O.group_scores(ref_probs, G)
+        check_topk_tolerance(gsel, O.select_all(ref_grp, lengths, K), ref_grp, K)
+        lc, sp = one["lc"].cpu().numpy(), one["sp"].cpu().numpy()
+        for b in range(B):
+            for g in range(G):
+                to_load, _, ref_slots[b][g] = O.elastic_plan(gsel[b][g], ref_slots[b][g])
+                assert lc[b, g] == len(to_load)
+                np.testing.assert_array_equal(sp[b, g], ref_slots[b][g])
