@@ -359,15 +359,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const uint32_t
   if (tid == 0) sel_count[inst] = K;
 }
 
-// Rows of at most 32768 keys (staged in LDS, 32 keys per thread): one sweep over
-// each thread's contiguous keys records, as bit masks, the keys whose first
-// digit is above the threshold digit (always selected) and those equal to it
-// (candidates), and histograms the candidates' second digit.  Every later step
-// touches only the candidates.
+// Rows of at most 32768 keys (staged in LDS, 32 keys per thread).  The kernel's cost is the vector
+// instructions its one workgroup issues, so every step past the first sweep touches only the
+// candidates (the keys in the threshold's first-digit bin):
+//   - the keys are loaded with buffer loads (past the row: zeros, no branch) in strided, coalesced
+//     order, keyed, and staged in LDS; thread t then reads its contiguous positions [32t, 32t+32);
+//   - one sweep marks, as bit masks, the keys above the threshold's first digit (selected) and
+//     those in its bin (candidates), and appends the candidates' positions to an LDS list (one
+//     counter add per wave), whose length the first-digit histogram gives in advance;
+//   - the second and third digit passes and the final compare run over that list, one entry per
+//     thread, and mark the candidates above the threshold and those equal to it (ties) in two LDS
+//     bitmaps of the row, word t of which belongs to thread t;
+//   - two block scans order the selected keys and the ties (the lowest positions win), and the
+//     selection is staged in LDS and written out in coalesced order.
+// When the bin holds more candidates than the list, the passes run over each thread's own keys.
 //
-// With CPT > 0 the kernel also makes the instance's elastic plan: thread t's 32 keys are positions
-// [32t, 32t + 32), so its selection mask is word t of the selection's bitmap, and the plan
-// (plan_words) runs on those words with the keys' LDS, no longer read, holding its lists.
+// With CPT > 0 the kernel also makes the instance's elastic plan: the selection mask of thread t is
+// word t of the selection's bitmap, and the plan (plan_words) runs on those words with the keys'
+// LDS, no longer read, holding its lists.
 struct PlanBufs {
   int32_t* slot_pos;
   uint32_t* resident_bm;
@@ -376,6 +385,64 @@ struct PlanBufs {
   int32_t* load_count;
   int bm_words;
 };
+
+constexpr int kCandList = 3072;      // candidate positions the LDS list holds
+
+// Exclusive scan over the kSelThreads-thread block; `smem` holds 16 words, 16-byte aligned.
+// Ends with a barrier.
+__device__ __forceinline__ uint32_t scan_block(uint32_t v, uint32_t* smem, uint32_t& total) {
+  constexpr int kWaves = kSelThreads / kWave;
+  static_assert(kWaves == 16, "four 16-byte reads of wave totals");
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == kWave - 1) smem[wid] = incl;
+  __syncthreads();
+  const uint4* s4 = reinterpret_cast<const uint4*>(smem);
+  uint32_t base = 0u, tot = 0u;
+#pragma unroll
+  for (int q = 0; q < kWaves / 4; ++q) {
+    const uint4 x = s4[q];
+    const uint32_t a[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      base += 4 * q + e < wid ? a[e] : 0u;
+      tot += a[e];
+    }
+  }
+  total = tot;
+  __syncthreads();
+  return base + incl - v;
+}
+
+// find_bin over NB bins with the bin counts held in registers between the scan and the search.
+template <int NB>
+__device__ __forceinline__ void find_bin_fixed(const uint32_t* hist, int need, uint32_t* scan_smem, uint32_t* bcast) {
+  constexpr int BPT = NB >= kSelThreads ? NB / kSelThreads : 1;
+  const int hi = NB - (int)threadIdx.x * BPT;          // this thread's bins: hi-1, hi-2, ... (top down)
+  uint32_t h[BPT];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    h[i] = hi - 1 - i >= 0 ? hist[hi - 1 - i] : 0u;
+    local += h[i];
+  }
+  uint32_t total;
+  const uint32_t above = scan_block(local, scan_smem, total);
+  if ((int)above < need && need <= (int)(above + local)) {   // exactly one thread
+    uint32_t cum = above;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (!found && (int)(cum + h[i]) >= need) {
+        bcast[0] = (uint32_t)(hi - 1 - i);
+        bcast[1] = cum;
+        found = true;
+      }
+      cum += h[i];
+    }
+  }
+  __syncthreads();
+}
 
 template <bool RAW, int CPT>
 __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint32_t* __restrict__ keys,
@@ -387,9 +454,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
                                                                       int nchunk, PlanBufs pb) {
   __shared__ uint4 skeys[kTopkLdsKeys / 4];
   __shared__ uint32_t hist[4096];
-  __shared__ uint32_t scan_smem[16];
+  __shared__ int32_t clist[kCandList];
+  __shared__ __align__(16) uint32_t scan_smem[16];
   __shared__ uint32_t bcast[2];
+  __shared__ uint32_t ccount;
   constexpr int kVecPerThread = kTopkLdsKeys / 4 / kSelThreads;   // 8 vectors = 32 keys
+  constexpr int kKeysPerThread = 4 * kVecPerThread;
+  constexpr int kListPerThread = kCandList / kSelThreads;
+  static_assert(kCandList % kSelThreads == 0 && 2 * kSelThreads <= 4096, "list passes; bitmaps in the histogram");
   // digits of the order key: raw float32 keys take 12 + 12 + 8 bits (the top 12 bits -- sign,
   // exponent and 3 mantissa bits -- spread logits over many bins, so the first histogram's LDS
   // atomics rarely collide); keys of the keys pass take 8 (its chunk histograms) + 12 + 12
@@ -419,7 +491,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   auto plan = [&](uint32_t selw) {
     int32_t* sL = reinterpret_cast<int32_t*>(skeys);
     plan_words<kP>(selw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
-                   pb.load_count + inst, K, pb.bm_words, sL, sL + K, reinterpret_cast<uint32_t*>(sL + 2 * K),
+                   pb.load_count + inst, K, pb.bm_words, sL + K, sL + 2 * K, reinterpret_cast<uint32_t*>(sL + 3 * K),
                    scan_smem);
   };
   if (n <= K) {
@@ -433,58 +505,67 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   }
   const uint32_t* kin = keys + (size_t)inst * max_len;
   const int nv = (n + 3) / 4;
-  const bool aligned = (max_len % 4) == 0;
 
-  // issue the key loads (strided, coalesced) and the chunk-histogram loads together
+  // key loads (strided, coalesced) and the chunk-histogram loads, issued together
   uint4 v[kVecPerThread];
+  if ((max_len & 3) == 0) {                        // rows start 16-byte aligned: 16-byte loads
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kin), (short)0,
+                                                                       nv * 16, kBufferRsrcWord3);
 #pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const int i4 = tid + u * kSelThreads;
-    if (i4 < nv) {
-      if (aligned && 4 * i4 + 3 < n) {
-        v[u] = reinterpret_cast<const uint4*>(kin)[i4];
-      } else {
-        const int j = 4 * i4;
-        v[u] = make_uint4(kin[j], j + 1 < n ? kin[j + 1] : 0u, j + 2 < n ? kin[j + 2] : 0u,
-                          j + 3 < n ? kin[j + 3] : 0u);
-      }
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const Vec16 x = ld16_buffer(r, (uint32_t)(tid + u * kSelThreads) * 16u);
+      v[u] = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kin), (short)0, n * 4,
+                                                                       kBufferRsrcWord3);
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const int o = (tid + u * kSelThreads) * 16;
+      v[u] = make_uint4((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0),
+                        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, o + 4, 0, 0),
+                        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, o + 8, 0, 0),
+                        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, o + 12, 0, 0));
     }
   }
   const int hbin = tid & (kBins1 - 1), c0 = tid >> 8;
   uint32_t hs = 0u;
   if (!RAW) {                                       // first digit: the chunk histograms of the keys kernel
-    const int nch = (n + kKeyChunk - 1) / kKeyChunk;
-    const uint32_t* ch = chist + (size_t)inst * nchunk * kBins1 + hbin;
-    for (int cb = c0; cb < nch; cb += 32) {
-      uint32_t hv[8];
+    const int nch = (n + kKeyChunk - 1) / kKeyChunk;   // <= 32 = 4 x 8 loads per bin
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(chist + (size_t)inst * nchunk * kBins1), (short)0, nch * kBins1 * 4, kBufferRsrcWord3);
+    uint32_t hv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = cb + 4 * u;
-        hv[u] = c < nch ? ch[(size_t)c * kBins1] : 0u;
-      }
+    for (int u = 0; u < 8; ++u)
+      hv[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, ((c0 + 4 * u) * kBins1 + hbin) * 4, 0, 0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) hs += hv[u];
-    }
+    for (int u = 0; u < 8; ++u) hs += hv[u];
   }
-  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+  if (tid == 0) ccount = 0u;
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
     const int i4 = tid + u * kSelThreads;
-    if (i4 < nv) {
-      v[u] = to_keys<RAW>(v[u]);
-      skeys[vslot(i4)] = v[u];
-    }
+    v[u] = to_keys<RAW>(v[u]);
+    if (i4 < nv) skeys[vslot(i4)] = v[u];
   }
   __syncthreads();
   if (RAW) {
-    // one head per group: no keys pass ran; the first digit is counted here from the staged keys
+    // one head per group: no keys pass ran; the first digit is counted here from the loaded keys
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
-      const int i4 = tid + u * kSelThreads;
-      const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i4 < nv && 4 * i4 + e < n) atomicAdd(&hist[k4[e] >> S1], 1u);
+      const int j = 4 * (tid + u * kSelThreads);
+      if (j + 3 < n) {
+        atomicAdd(&hist[v[u].x >> S1], 1u);
+        atomicAdd(&hist[v[u].y >> S1], 1u);
+        atomicAdd(&hist[v[u].z >> S1], 1u);
+        atomicAdd(&hist[v[u].w >> S1], 1u);
+      } else if (j < n) {
+        atomicAdd(&hist[v[u].x >> S1], 1u);
+        if (j + 1 < n) atomicAdd(&hist[v[u].y >> S1], 1u);
+        if (j + 2 < n) atomicAdd(&hist[v[u].z >> S1], 1u);
+      }
     }
   } else {
     atomicAdd(&hist[hbin], hs);
@@ -492,77 +573,150 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   __syncthreads();
 
   int need = K;
-  find_bin(hist, 1 << (32 - S1), need, scan_smem, bcast);
+  find_bin_fixed<(1 << (32 - S1))>(hist, need, scan_smem, bcast);
   const uint32_t d1 = bcast[0];
   need -= (int)bcast[1];
+  const int ncand = (int)hist[d1];                  // keys in the threshold's first-digit bin
   __syncthreads();
-  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
 
-  // one sweep over the thread's contiguous 32 keys, which then stay in registers: the later
-  // passes over the candidates are unrolled, predicated loops with no LDS traffic and no
-  // per-lane trip counts
-  constexpr int kKeysPerThread = 4 * kVecPerThread;
+  // the sweep over the thread's contiguous keys (kept in registers for the long-bin path)
   const int v0 = tid * kVecPerThread;
-  uint32_t kr[kKeysPerThread];
+  const uint32_t* skw = reinterpret_cast<const uint32_t*>(skeys);
+  auto key_at = [&](int j) { return skw[vslot(j >> 2) * 4 + (j & 3)]; };
+  uint4 kv[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) kv[u] = skeys[vslot(v0 + u)];
+  const int nvalid = min(max(n - 4 * v0, 0), kKeysPerThread);
+  const uint32_t vmask = nvalid >= 32 ? 0xFFFFFFFFu : (1u << nvalid) - 1u;
   uint32_t gtm = 0u, cm = 0u;
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
-    const int vv = v0 + u;
-    const uint4 kv = vv < nv ? skeys[vslot(vv)] : make_uint4(0u, 0u, 0u, 0u);
-    kr[4 * u] = kv.x; kr[4 * u + 1] = kv.y; kr[4 * u + 2] = kv.z; kr[4 * u + 3] = kv.w;
+    const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool valid = 4 * vv + e < n;
-      const uint32_t top = kr[4 * u + e] >> S1;
-      gtm |= (uint32_t)(valid && top > d1) << (4 * u + e);
-      if (valid && top == d1) {
-        cm |= 1u << (4 * u + e);
-        atomicAdd(&hist[(kr[4 * u + e] >> S2) & 4095u], 1u);
-      }
+      const uint32_t top = k4[e] >> S1;
+      gtm |= (uint32_t)(top > d1) << (4 * u + e);
+      cm |= (uint32_t)(top == d1) << (4 * u + e);
+    }
+  }
+  gtm &= vmask;
+  cm &= vmask;
+  const bool use_list = ncand <= kCandList;         // uniform over the workgroup
+  if (use_list) {
+    // append the candidates' positions, in any order: one LDS counter add per wave
+    const uint32_t c = __popc(cm);
+    const uint32_t incl = wave_incl_scan(c);
+    uint32_t wbase = 0u;
+    if ((tid & (kWave - 1)) == kWave - 1 && incl) wbase = atomicAdd(&ccount, incl);
+    uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)wbase, kWave - 1) + incl - c;
+    for (uint32_t m = cm; m; m &= m - 1)
+      if (at < (uint32_t)kCandList) clist[at++] = 32 * tid + __ffs(m) - 1;
+  }
+  __syncthreads();
+  if (use_list) {
+#pragma unroll
+    for (int q = 0; q < kListPerThread; ++q) {
+      const int i = tid + q * kSelThreads;
+      if (i < ncand) atomicAdd(&hist[(key_at(clist[i]) >> S2) & 4095u], 1u);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((cm >> (4 * u + e)) & 1u) atomicAdd(&hist[(k4[e] >> S2) & 4095u], 1u);
     }
   }
   __syncthreads();
-  find_bin(hist, 4096, need, scan_smem, bcast);
+  find_bin_fixed<4096>(hist, need, scan_smem, bcast);
   uint32_t prefix = (d1 << S1) | (bcast[0] << S2);
   uint32_t pmask = ~((1u << S2) - 1u);
   need -= (int)bcast[1];
-  const bool whole = (int)hist[bcast[0]] == need;
+  const bool whole = (int)hist[bcast[0]] == need;   // every key of the bin is taken: T is resolved
   __syncthreads();
   if (!whole) {
-    for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kKeysPerThread; ++e)
-      if (((cm >> e) & 1u) && (kr[e] & pmask) == prefix) atomicAdd(&hist[kr[e] & ((1u << S2) - 1u)], 1u);
+    for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
     __syncthreads();
-    find_bin(hist, 1 << S2, need, scan_smem, bcast);
+    if (use_list) {
+#pragma unroll
+      for (int q = 0; q < kListPerThread; ++q) {
+        const int i = tid + q * kSelThreads;
+        if (i < ncand) {
+          const uint32_t k = key_at(clist[i]);
+          if ((k & pmask) == prefix) atomicAdd(&hist[k & ((1u << S2) - 1u)], 1u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kVecPerThread; ++u) {
+        const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (((cm >> (4 * u + e)) & 1u) && (k4[e] & pmask) == prefix) atomicAdd(&hist[k4[e] & ((1u << S2) - 1u)], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin_fixed<(1 << S2)>(hist, need, scan_smem, bcast);
     prefix |= bcast[0];
     pmask = 0xFFFFFFFFu;
     need -= (int)bcast[1];
-    __syncthreads();
   }
   // resolve the candidates: masked key > prefix -> selected; == prefix -> tie at T
   uint32_t eqm = 0u;
+  if (use_list) {
+    uint32_t* selbm = hist;                         // the histogram is read no more (find_bin's barrier)
+    uint32_t* tiebm = hist + kSelThreads;
+    selbm[tid] = 0u;
+    tiebm[tid] = 0u;
+    __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kKeysPerThread; ++e) {
-    const uint32_t mk = kr[e] & pmask;
-    const bool c = (cm >> e) & 1u;
-    gtm |= (uint32_t)(c && mk > prefix) << e;
-    eqm |= (uint32_t)(c && mk == prefix) << e;
+    for (int q = 0; q < kListPerThread; ++q) {
+      const int i = tid + q * kSelThreads;
+      if (i < ncand) {
+        const int j = clist[i];
+        const uint32_t mk = key_at(j) & pmask;
+        if (mk > prefix) atomicOr(&selbm[j >> 5], 1u << (j & 31));
+        else if (mk == prefix) atomicOr(&tiebm[j >> 5], 1u << (j & 31));
+      }
+    }
+    __syncthreads();
+    gtm |= selbm[tid];
+    eqm = tiebm[tid];
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t mk = k4[e] & pmask;
+        const bool c = (cm >> (4 * u + e)) & 1u;
+        gtm |= (uint32_t)(c && mk > prefix) << (4 * u + e);
+        eqm |= (uint32_t)(c && mk == prefix) << (4 * u + e);
+      }
+    }
   }
+  // when all 32 bits are resolved the tied keys are equal and the lower positions win; otherwise
+  // every one of them is taken (need equals their count)
   const uint32_t gt = __popc(gtm), eq = __popc(eqm);
   uint32_t tot;
-  const uint32_t before = block_excl_scan((eq << 16) | gt, scan_smem, tot);   // n <= 32768 < 2^16
+  const uint32_t before = scan_block((eq << 16) | gt, scan_smem, tot);   // n <= 32768 < 2^16
   const int eq_before = (int)(before >> 16), gt_before = (int)(before & 0xFFFFu);
   const int take_eq = max(0, min((int)eq, need - eq_before));
   uint32_t keep_eq = eqm;
   for (int drop = (int)eq - take_eq; drop > 0; --drop) keep_eq &= ~(0x80000000u >> __clz(keep_eq));
-  int o = gt_before + min(eq_before, need);
   const uint32_t selw = gtm | keep_eq;
-  for (uint32_t m = selw; m; m &= m - 1) {
-    if (o < K) out[o++] = 4 * v0 + __ffs(m) - 1;
-  }
+  // stage the selection in LDS (the keys are read no more: the scan's barriers passed), then write
+  // it out coalesced
+  int32_t* sOut = reinterpret_cast<int32_t*>(skeys);
+  int o = gt_before + min(eq_before, need);
+  for (uint32_t m = selw; m; m &= m - 1)
+    if (o < K) sOut[o++] = 32 * tid + __ffs(m) - 1;
+  __syncthreads();
+  for (int i = tid; i < K; i += kSelThreads) out[i] = sOut[i];
   if (tid == 0) sel_count[inst] = K;
   if (kPlan) plan(selw);
 }
@@ -633,8 +787,8 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
 }
 
 bool select_plan_fused(const spc_shape& s) {
-  // the plan's lists (2 K words) and the bitmap (<= 1024 words) fit the keys' LDS
-  return s.max_len <= kTopkLdsKeys && s.budget <= kPlanMaxBudget && 2 * s.budget + 1024 <= kTopkLdsKeys;
+  // the staged selection and the plan's lists (3 K words) and bitmap (<= 1024 words) fit the keys' LDS
+  return s.max_len <= kTopkLdsKeys && s.budget <= kPlanMaxBudget && 3 * s.budget + 1024 <= kTopkLdsKeys;
 }
 
 hipError_t launch_select_plan(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,

@@ -195,6 +195,8 @@ LOGIT_TIE_CASES = [
                                                  * np.float32(2.0 ** -23)), False),
     # -0.0 and +0.0 are one value: ties broken by the lower index
     (1, 2, 2, 30000, 2048, [30000], [-0.0, 0.0, -1.0], False),
+    # rows that do not start 16-byte aligned (a length no multiple of 4), one head per group
+    (2, 3, 3, 4999, 100, [4999, 4998], None, False),
 ]
 
 
@@ -251,6 +253,9 @@ TIE_CASES = [
     (1, 2, 2, 70000, 4096, [65537], [0.0, 1e-30, 2.0 ** -126, 1.0]), # streaming + ties + subnormal-ish
     (2, 4, 4, 1500, 1, [1500, 7], None),                            # K = 1
     (1, 6, 2, 33000, 5000, [33000], [-1.0, -0.5, 0.0, 0.5]),        # negative scores, heads 3 per group
+    # rows that do not start 16-byte aligned, and a threshold bin of some 2300 tied keys (the
+    # select's candidate list) next to the 3-value case above, whose bin outgrows the list
+    (2, 4, 2, 3001, 200, [3001, 2500], [0.0, 0.25]),
 ]
 
 
