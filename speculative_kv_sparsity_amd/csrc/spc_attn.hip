@@ -275,11 +275,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 // Each wave walks T tiles of 16 rows (8 lanes per row, 2 rows per lane) with an
 // online softmax, so the 8-lane-group reduction and the cross-wave merge are paid
 // once per 64 T rows instead of once per 16.
+//
+// The heads of a sequence select largely the same rows, so the grid is one-dimensional and
+// ordered for the L2 of each XCD: the dispatcher deals block ids round-robin over the 8 XCDs, and
+// the ids of XCD x run, in order, every head of (sequence, layer, split) groups x, x + 8, ... .
+// The heads of a group, in flight together on one XCD, walk their ascending row lists at about
+// the same pace, so a row one of them reads is usually still in that L2 for the others.
 template <int D, int DV, int T>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
-    int n_lay, int nsplit, int /*nhc: one head per group*/, int max_rows, float scale, float* __restrict__ part_o,
+    int n_lay, int nsplit, int n_glob, int max_rows, float scale, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
   constexpr int EB = 2;
   constexpr int CPLK = D * EB / 16 / 8;              // 16-byte chunks per lane of a row (9)
@@ -287,10 +293,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   constexpr int RPT = 16;                            // rows per wave tile (8 lanes per row, 2 rows per lane)
   constexpr int RPS = 4 * RPT * T;
   static_assert(CPLV <= CPLK && D * EB % 128 == 0 && DV * EB % 128 == 0, "latent row layout");
-  const int split = blockIdx.x;
-  const int inst = blockIdx.y;
-  const int r = inst % n_groups;
-  const int bl = inst / n_groups;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int r = j % n_groups;                          // head (one per group)
+  const int gidx = (j / n_groups) * 8 + xcd;           // (sequence, layer, split) group
+  if (gidx >= n_glob) return;
+  const int split = gidx % nsplit;
+  const int bl = gidx / nsplit;
+  const int inst = bl * n_groups + r;
   const int lo = bl % n_lay;
   const int b = bl / n_lay;
   const int layer = layer_begin + lo;
@@ -632,14 +641,17 @@ hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_la
   } else if (s.head_dim == 192) {
     e = launch_split_gqc<SPC_BF16, 192, 128>(gqc, s, grid, st, a);
   } else if (s.head_dim == 576 && gqc == 1) {
+    // one-dimensional grid: 8 XCD lanes x groups of every head (see the kernel)
+    const int n_glob = s.batch * g.n_lay * g.nsplit;
+    const dim3 lgrid((unsigned)(8 * ((n_glob + 7) / 8) * s.n_groups));
     if (latent_tiles(s) == kLatentTilesLarge)
-      attn_split_latent_kernel<576, 512, kLatentTilesLarge><<<grid, kThreads, 0, st>>>(
+      attn_split_latent_kernel<576, 512, kLatentTilesLarge><<<lgrid, kThreads, 0, st>>>(
           a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
-          a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
+          a.layer_begin, a.n_lay, a.nsplit, n_glob, a.max_rows, s.scale, a.part_o, a.part_ml);
     else
-      attn_split_latent_kernel<576, 512, kLatentTilesSmall><<<grid, kThreads, 0, st>>>(
+      attn_split_latent_kernel<576, 512, kLatentTilesSmall><<<lgrid, kThreads, 0, st>>>(
           a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
-          a.layer_begin, a.n_lay, a.nsplit, a.nhc, a.max_rows, s.scale, a.part_o, a.part_ml);
+          a.layer_begin, a.n_lay, a.nsplit, n_glob, a.max_rows, s.scale, a.part_o, a.part_ml);
     e = hipGetLastError();
   }
   return e;

@@ -35,10 +35,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMlaD = kMlaLatent + kMlaRope;      // 576 scored dims
 constexpr int kKSteps = kMlaD / 32;                // MFMA k-steps of 32
-constexpr int kSub = 32;                           // latent rows per LDS buffer
+constexpr int kSub = 64;                           // latent rows per LDS buffer: four 16-row blocks
 constexpr int kLdsRow = kMlaD + 8;                 // padded row (elements): spreads rows over banks
-constexpr int kScoreThreads = 256;                 // 4 waves x 16 heads
-static_assert(kMlaD % 32 == 0, "k-steps of 32");
+constexpr int kScoreThreads = 512;                 // 8 waves x 16 heads
+constexpr int kScoreHeads = 8 * 16;                // heads per workgroup
+constexpr int kScoreRowChunks = kLdsRow / 8;       // 16-byte chunks per padded LDS row (one pad chunk)
+constexpr int kScoreChunks = kSub * kScoreRowChunks;
+constexpr int kScoreLoads = (kScoreChunks + kWave - 1) / kWave;   // wave loads of 64 chunks per sub-tile
+constexpr int kScoreBuf = kScoreLoads * kWave * 8;   // LDS elements of a sub-tile buffer
+static_assert(kMlaD % 32 == 0 && kSub == 64, "k-steps of 32; two pairs of 16-row blocks per sub-tile");
+static_assert(kMlaScoreTile % kSub == 0 && kMlaScoreTileLarge % kSub == 0, "tiles of whole sub-tiles");
 
 // Workgroup = (quarter of the 512 latent dims, head), so a head's 128 KB of W_UK
 // is read by four workgroups.  Lane (g, c) of 16 row groups x 16 chunks holds the
@@ -130,37 +136,34 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
   m = M;
 }
 
-// Workgroup = (sequence, tile of 256 or 512 positions, 64 heads): 4 waves x 16 heads, two
-// workgroups per CU.  The tile is staged 32 rows at a time through two LDS
-// buffers, so one barrier per sub-tile separates the MFMAs on one buffer from the
-// staging of the next sub-tile into the other.  The two workgroups
-// of the 128 heads of one tile get block ids 8 apart, which the dispatcher's
-// round-robin over the 8 XCDs places on the same XCD, so the second reads the
-// tile from that L2.
-__global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const float* __restrict__ q_abs,
+// Workgroup = (sequence, tile of 256 or 512 positions): 8 waves x 16 heads, one workgroup per CU,
+// so the tile is read from memory and staged once for all 128 heads.  A wave keeps the float32
+// query of its 16 heads as bf16 hi + lo MFMA A fragments in registers for the whole tile (144
+// VGPRs: MFMA A operands live in VGPRs, and 32 heads would not fit).  The tile goes 64 rows at a
+// time from memory straight into LDS (global_load_lds_dwordx4: lane l of a wave load lands 16 l
+// bytes past the wave's LDS base; rows padded by one 16-byte chunk), double-buffered: the next
+// sub-tile is in flight while the MFMAs read the current one, and one barrier per sub-tile
+// separates the two.  A sub-tile's logits are stored at the start of the next, so that barrier
+// waits only for the next sub-tile's loads.
+__global__ __launch_bounds__(kScoreThreads, 1) void mla_scores_kernel(const float* __restrict__ q_abs,
                                                                    const uint16_t* __restrict__ lat,
                                                                    const int32_t* __restrict__ lengths,
                                                                    float* __restrict__ probs,
                                                                    float2* __restrict__ part, int H, int max_len,
-                                                                   int ntiles, int nhg, int tile_len,
-                                                                   float scale) {
-  __shared__ uint16_t sl[2][kSub * kLdsRow];
-  // block id -> (tile, head group): groups of 8 * nhg ids hold 8 tiles x nhg head groups
-  const int id = blockIdx.x;
-  const int grp = id / (8 * nhg), in = id - grp * 8 * nhg;
-  const int hg = in / 8, tile = grp * 8 + (in & 7);
-  const int b = blockIdx.y;
+                                                                   int ntiles, int tile_len, float scale) {
+  __shared__ __align__(16) uint16_t sl[2][kScoreBuf];
+  const int tile = blockIdx.x, b = blockIdx.y;
   if (tile >= ntiles) return;
   const int n = clamp_len(lengths, b, max_len);
   const int row0 = tile * tile_len;
   if (row0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int hbase = hg * 64 + 16 * wid;              // first head of this wave
-  const bool active = hbase < H;
   const int kc = lane >> 4, col = lane & 15;
+  const int hbase = 16 * wid;                      // this wave's heads: hbase .. hbase + 15
+  const bool active = hbase < H;                   // H is a multiple of 16
 
-  // this lane's query fragments (head hbase + col, k-chunk kc of every k-step), hi and lo parts
-  bf16x8_t ahi[kKSteps], alo[kKSteps];   // 144 VGPRs: the budget that fixes 2 workgroups per CU
+  // query fragments (head hbase + col, k-chunk kc of every k-step), hi and lo parts
+  bf16x8_t ahi[kKSteps], alo[kKSteps];
   if (active) {
     const float* qa = q_abs + ((size_t)b * H + hbase + col) * kMlaD;
 #pragma unroll
@@ -180,65 +183,73 @@ __global__ __launch_bounds__(kScoreThreads, 2) void mla_scores_kernel(const floa
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; s_run[i] = 0.f; }
 
-  constexpr int kChunks = kMlaD * 2 / 16;          // 16-byte chunks per latent row
-  constexpr int kPer = kSub * kChunks / kScoreThreads;
-  static_assert(kSub * kChunks % kScoreThreads == 0, "sub-tile load split");
   const uint16_t* lb = lat + (size_t)b * max_len * kMlaD;
   const int nsub = min(tile_len, n - row0 + kSub - 1) / kSub;   // sub-tiles with valid rows
-  uint4 v[kPer];
-  auto load = [&](int sub) {
+  // sub-tile sub -> LDS buffer: chunk k of the buffer is chunk ch of row r (pad chunks and rows
+  // past the sequence load the sequence's row 0; their columns are never written)
+  auto dma = [&](int sub, uint16_t* dst) {
     const int p_sub = row0 + sub * kSub;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + u * kScoreThreads;
-      const int r = c / kChunks, ch = c - (c / kChunks) * kChunks;
-      v[u] = p_sub + r < n ? *reinterpret_cast<const uint4*>(lb + (size_t)(p_sub + r) * kMlaD + 8 * ch)
-                           : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = wid; i < kScoreLoads; i += kScoreThreads / kWave) {
+      const int k = kWave * i + lane;
+      const int r = k / kScoreRowChunks, ch = k - r * kScoreRowChunks;
+      const uint16_t* src = lb;
+      if (k < kScoreChunks && ch < kMlaD / 8 && p_sub + r < n) src = lb + (size_t)(p_sub + r) * kMlaD + 8 * ch;
+      __builtin_amdgcn_global_load_lds(src, dst + 8 * kWave * i, 16, 0, 0);
     }
   };
-  auto stage = [&](int buf) {
+  // logits of the last sub-tile: [16-row block][head row i], rows from lpos
+  float lv[kSub / 16][4];
+  int lpos = -1;
+  auto store_held = [&]() {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + u * kScoreThreads;
-      const int r = c / kChunks, ch = c - (c / kChunks) * kChunks;
-      *reinterpret_cast<uint4*>(&sl[buf][r * kLdsRow + 8 * ch]) = v[u];
+    for (int blk = 0; blk < kSub / 16; ++blk) {
+      const int pos = lpos + 16 * blk + col;
+      if (pos < n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) probs[((size_t)b * H + hbase + 4 * kc + i) * max_len + pos] = lv[blk][i];
+      }
     }
   };
-  load(0);
-  stage(0);
+  dma(0, sl[0]);
   __syncthreads();
 #pragma unroll 1
   for (int sub = 0; sub < nsub; ++sub) {
     const int buf = sub & 1;
-
+    if (sub + 1 < nsub) dma(sub + 1, sl[buf ^ 1]);   // in flight during this sub-tile's MFMAs
+    if (lpos >= 0) store_held();
+    const int p_sub = row0 + sub * kSub;
     if (active) {
-      const int p_sub = row0 + sub * kSub;
 #pragma unroll
-      for (int blk = 0; blk < kSub / 16; ++blk) {
-        const int p0 = p_sub + 16 * blk;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* srow = &sl[buf][(16 * blk + col) * kLdsRow + 8 * kc];
+      for (int pr = 0; pr < kSub / 32; ++pr) {
+        // two 16-row blocks x (hi, lo): four independent MFMA chains per k-step
+        f32x4_t acc[2][2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) acc[blk][0] = acc[blk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* srow = &sl[buf][(32 * pr + col) * kLdsRow + 8 * kc];
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
-          const bf16x8_t bfrag = *reinterpret_cast<const bf16x8_t*>(srow + 32 * s);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], bfrag, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], bfrag, acc, 0, 0, 0);
+          const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(srow + 32 * s);
+          const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(srow + 16 * kLdsRow + 32 * s);
+          acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], b0, acc[0][0], 0, 0, 0);
+          acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], b1, acc[1][0], 0, 0, 0);
+          acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], b0, acc[0][1], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], b1, acc[1][1], 0, 0, 0);
         }
-        const int pos = p0 + col;
-        if (pos < n) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const bool valid = p_sub + 32 * pr + 16 * blk + col < n;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int h = hbase + 4 * kc + i;
-            const float l = acc[i] * scale;
-            probs[((size_t)b * H + h) * max_len + pos] = l;
-            online_ms(m_run[i], s_run[i], l);
+            lv[2 * pr + blk][i] = (acc[blk][0][i] + acc[blk][1][i]) * scale;
+            if (valid) online_ms(m_run[i], s_run[i], lv[2 * pr + blk][i]);
           }
         }
       }
+      lpos = p_sub;
     }
-    if (sub + 1 < nsub) { load(sub + 1); stage(buf ^ 1); }
-    __syncthreads();
+    __syncthreads();                                 // the next sub-tile landed; this buffer is free
   }
+  if (lpos >= 0) store_held();
   if (active) {
     // merge (max, sum) over the 16 lanes of each row group (the tile's positions)
 #pragma unroll
@@ -496,21 +507,19 @@ __global__ __launch_bounds__(kExpThreads, 1) void mla_expand_kernel(
 }  // namespace
 
 // 512-position tiles halve the workgroups and the query-fragment setup per position; they are
-// taken when the grid still holds two workgroups for each of the 256 CUs
+// taken when the grid still holds a workgroup for each of the 256 CUs
 int mla_score_tile(const spc_shape& s) {
-  const long nhg = (s.n_q_heads + 63) / 64;
-  const long wgs = (long)s.batch * nhg * ((s.max_len + kMlaScoreTileLarge - 1) / kMlaScoreTileLarge);
-  return wgs >= 512 ? kMlaScoreTileLarge : kMlaScoreTile;
+  const long wgs = (long)s.batch * ((s.max_len + kMlaScoreTileLarge - 1) / kMlaScoreTileLarge);
+  return wgs >= 256 ? kMlaScoreTileLarge : kMlaScoreTile;
 }
 
 hipError_t launch_mla_logits(const spc_shape& s, const float* q_abs, const void* latent, const int32_t* lengths,
                              float* logits, float2* stats, hipStream_t st) {
+  if (s.n_q_heads > kScoreHeads || s.n_q_heads % 16 != 0) return hipErrorInvalidValue;
   const int tl = mla_score_tile(s);
   const int ntiles = (s.max_len + tl - 1) / tl;
-  const int nhg = (s.n_q_heads + 63) / 64;         // head groups of 64
-  const int ngrp = (ntiles + 7) / 8;
-  mla_scores_kernel<<<dim3(ngrp * 8 * nhg, s.batch), kScoreThreads, 0, st>>>(
-      q_abs, static_cast<const uint16_t*>(latent), lengths, logits, stats, s.n_q_heads, s.max_len, ntiles, nhg, tl,
+  mla_scores_kernel<<<dim3(ntiles, s.batch), kScoreThreads, 0, st>>>(
+      q_abs, static_cast<const uint16_t*>(latent), lengths, logits, stats, s.n_q_heads, s.max_len, ntiles, tl,
       s.scale);
   return hipGetLastError();
 }
