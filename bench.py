@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--retrieval", default="head", choices=("head", "batch"),
                     help="head: one selection per KV head (GQA group; the path as built); batch: one selection "
                          "per sequence shared by every head (the comparison the pages draw)")
+    ap.add_argument("--graph", action="store_true",
+                    help="MLA: time the steps as HIP-graph replays instead of eager launches")
     ap.add_argument("--layer-chunks", type=int, default=2)
     ap.add_argument("--tail-layers", type=int, default=None,
                     help="layers in the last chunk (default n_layers // 8)")
@@ -701,13 +703,33 @@ def bench_mla(args, p, torch, W):
         dec.step(qn[t], qr[t], lens[t])
     torch.cuda.synchronize()
 
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(dec.main)
-    for t in range(Wm, Wm + K_):
-        dec.step(qn[t], qr[t], lens[t])
-    e1.record(dec.main)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / K_
+    # the timed steps: eager launches, or with --graph HIP-graph replays of one captured step (its
+    # inputs copied into the graph's static buffers, inside the timed region); the other launch
+    # mode is timed too, over the same steps replayed from the same state, and reported beside it.
+    # Eager launches run ahead of the GPU here, so the graph gains nothing (it measures slower)
+    state = (dec.slot_pos, dec.resident_bm, dec.load_pos, dec.load_slot, dec.load_count, dec.sel_idx,
+             dec.sel_count)
+    saved = [t.clone() for t in state]
+    dec.capture()
+
+    def timed(graph):
+        for t, v in zip(state, saved):
+            t.copy_(v)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(dec.main)
+        for t in range(Wm, Wm + K_):
+            if graph:
+                dec.step_graph(qn[t], qr[t], lens[t])
+            else:
+                dec.step(qn[t], qr[t], lens[t])
+        e1.record(dec.main)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K_
+
+    ms_eager = timed(False)
+    ms_graph = timed(True)
+    ms_per_step = ms_graph if args.graph else ms_eager
 
     # instrumented pass: K more steps launched back to back (no synchronize between steps), events
     # around every stage call and at the attention's merge; counts summed on the device
@@ -779,6 +801,9 @@ def bench_mla(args, p, torch, W):
               "cached_tokens": L, "kv_budget": p.budget, "parallelism": "single GPU"}
     result = _header(args, p, ms_per_step, config)
     result.update({
+        "step_launch": "hip_graph" if args.graph else "eager",
+        "ms_per_step_eager": round(ms_eager, 4),
+        "ms_per_step_graph": round(ms_graph, 4),
         "roofline": dict(roof("hbm", lat_bytes, iso_ms["attn_partial"], HBM_PEAK_GBS, "GB/s",
                               "attn_split_latent_kernel (the dominant kernel, timed alone through spc_attn_partial: "
                               "each head gathers its selected latent rows; a row selected by several heads is "

@@ -436,6 +436,43 @@ class MlaDecoder:
         api.spc_mla_out_proj(s, self.p.nope_dim, self.w_uv, self.o_lat, 0, self.out, stream=st)
         mark("end", st)
 
+    def capture(self) -> None:
+        """Capture one step into a HIP graph over static input buffers (the query parts and the
+        lengths), so that a serving loop launches the whole step at once: step_graph() copies a
+        step's inputs into those buffers and replays it.  The warm-up step that capture needs runs
+        on zero-length inputs, and the resident-set state is restored after it."""
+        p, dev = self.p, self.latent.device
+        B, H = p.batch, p.n_q_heads
+        self.g_qn = torch.zeros((B, H, p.nope_dim), dtype=p.torch_dtype, device=dev)
+        self.g_qr = torch.zeros((B, H, p.rope_dim), dtype=p.torch_dtype, device=dev)
+        self.g_len = torch.zeros((B,), dtype=torch.int32, device=dev)
+        main = self.main
+        state = (self.slot_pos, self.resident_bm, self.load_pos, self.load_slot, self.load_count, self.sel_idx,
+                 self.sel_count)
+        saved = [t.clone() for t in state]
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(main)
+        self.main = cap
+        try:
+            with torch.cuda.stream(cap):
+                self.step(self.g_qn, self.g_qr, self.g_len)      # warm-up on the capture stream
+                for t, v in zip(state, saved):                   # which must leave the state as it was
+                    t.copy_(v)
+            cap.synchronize()
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph, stream=cap):
+                self.step(self.g_qn, self.g_qr, self.g_len)
+        finally:
+            self.main = main
+        torch.cuda.synchronize(dev)
+
+    def step_graph(self, q_nope: torch.Tensor, q_rope: torch.Tensor, lengths: torch.Tensor) -> None:
+        """One step through the captured graph (capture() first); inputs as for step()."""
+        self.g_qn.copy_(q_nope)
+        self.g_qr.copy_(q_rope)
+        self.g_len.copy_(lengths)
+        self.graph.replay()
+
     def attend(self, stream=None, mark=None) -> None:
         """Attention of every head over its selected latent rows (gathered by position); with `mark`,
         as its split and merge halves with an event "attn_merge" between them."""

@@ -108,9 +108,10 @@ def test_mla_32k_full_shape_all_heads_of_one_sequence():
 
 
 def test_mla_512_position_tiles_with_ragged_lengths():
-    """The shape that scores on 512-position tiles (4 sequences x 2 head halves x 64 tiles), with
-    lengths that end inside a tile, inside its first 16-row block, and at zero: logits, tile stats
-    and Top-K against the oracle."""
+    """The shape that scores on 512-position tiles (4 sequences x 64 tiles, each workgroup all 128
+    heads: 8 waves of 16), with lengths that end inside a tile's last 64-row sub-tile, inside its
+    first 16-row block, and at zero: logits, tile stats and Top-K against the oracle; the heads
+    sampled sit in the first, fourth, fifth and last wave."""
     p = W.PRESETS["mla_32k"]
     w = W.generate(p, device="cuda", seed=4, steps=1)
     dec_shape = api.make_shape(p.batch, p.n_q_heads, 1, p.n_q_heads, p.head_dim, p.v_dim, p.max_len, p.budget, 1,
@@ -159,3 +160,35 @@ def test_mla_helpers_match_literal_up_projections(B, H, dn, dv, n_layers, layer)
                                      wuk[h], wuv[h])
             bound = (C + 32) * 2.0 ** -24 * (np.abs(wuv[h]) @ np.abs(o_lat[b, layer, h].numpy().astype(np.float64)))
             assert np.all(np.abs(got[b, h] - V[0]) <= bound), (b, h)
+
+
+def test_mla_graph_replay_equals_eager_steps():
+    """The step captured once into a HIP graph and replayed over its static input buffers gives,
+    step after step, the same selection, load lists, latent attention output and output projection
+    as eager launches from the same state, bit for bit; eager work and a synchronize run between
+    the replays."""
+    p = W.PRESETS["mla_32k"].with_(batch=2, n_q_heads=32, max_len=4096, budget=256)
+    steps = 4
+    w = W.generate(p, device="cuda", seed=8, steps=steps)
+    lens = [[4096, 3001], [4096, 3002], [10, 3003], [4096, 0]]
+    dec = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+    names = ("sel_idx", "sel_count", "load_pos", "load_slot", "load_count", "slot_pos", "resident_bm", "o_lat", "out")
+    start = {k: getattr(dec, k).clone() for k in names}
+    eager = []
+    for t in range(steps):
+        dec.step(w.q_nope[t].contiguous(), w.q_rope[t].contiguous(), dev_lengths(lens[t]))
+        torch.cuda.synchronize()
+        eager.append({k: getattr(dec, k).clone() for k in names})
+    for k in names:
+        getattr(dec, k).copy_(start[k])
+    dec.capture()
+    for k in ("slot_pos", "resident_bm"):                 # capture leaves the state as it was
+        assert torch.equal(getattr(dec, k), start[k]), k
+    for t in range(steps):
+        dec.step_graph(w.q_nope[t].contiguous(), w.q_rope[t].contiguous(), dev_lengths(lens[t]))
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 16, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k in names:
+            assert torch.equal(getattr(dec, k), eager[t][k]), f"{k} at step {t}"
