@@ -425,7 +425,7 @@ def bench_gqa(args, p, torch, W):
     dk = inputs(dec.dlm_k)
     iso_ms = {
         "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dk()[0], tl, dec.logits,
-                                                                 dec.tile_stats, stream=st), R),
+                                                                 dec.stats_out, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
                                                                     dec.sel_idx, dec.sel_count, ws=dec.ws_topk,
                                                                     stream=st), R),
@@ -640,7 +640,7 @@ def bench_lag1(args, p, torch, W):
     dk, kv = rotation(dec.dlm_k), rotation(dec.dev_kv)
     iso_ms = {
         "scores": iso(torch, lambda st: api.spc_retrieval_logits(dec.shape, tq, dk()[0], tl, dec.logits,
-                                                                 dec.tile_stats, stream=st), R),
+                                                                 dec.stats_out, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(dec.shape, dec.logits, dec.tile_stats, tl,
                                                                     dec.sel[nx], dec.cnt[nx], ws=dec.ws_topk,
                                                                     stream=st), R),
@@ -771,7 +771,7 @@ def bench_mla(args, p, torch, W):
         "absorb": iso(torch, lambda st: api.spc_mla_absorb_q(s, p.nope_dim, uk()[0], tq, tr, dec.q_abs,
                                                              stream=st), R),
         "scores": iso(torch, lambda st: api.spc_retrieval_logits(s, dec.q_abs, lat()[0], tl, dec.logits,
-                                                                 dec.tile_stats, stream=st), R),
+                                                                 dec.stats_out, stream=st), R),
         "topk": iso(torch, lambda st: api.spc_group_max_topk_logits(s, dec.logits, None, tl, dec.sel_idx,
                                                                     dec.sel_count, ws=dec.ws_topk, stream=st), R),
         "topk_plan": iso(torch, topk_plan_call(api, s, dec.logits, None, tl, dec), R),

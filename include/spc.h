@@ -193,7 +193,11 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
  * formula; the same inputs and supported shapes as spc_retrieval_scores).
  *   logits      device [B][H_q][max_len] float32 out; entries j >= lengths[b] untouched
  *   tile_stats  device float32 pairs [B][H_q][ceil(max_len / T)] out, 8-byte aligned,
- *               tile_stats_bytes >= spc_tile_stats_size(s) (else SPC_ERR_INVALID_ARG)
+ *               tile_stats_bytes >= spc_tile_stats_size(s) (else SPC_ERR_INVALID_ARG); may be NULL
+ *               (tile_stats_bytes ignored) when every query head is its own group
+ *               (n_q_heads == n_groups): the Top-K then ranks the logits as they are and needs no
+ *               stats, and none are computed; NULL with several heads per group is
+ *               SPC_ERR_INVALID_ARG
  */
 int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths,
                          float* logits, float* tile_stats, size_t tile_stats_bytes, void* stream);

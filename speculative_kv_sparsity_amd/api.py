@@ -131,8 +131,11 @@ def tile_stats_shape(shape: SpcShape) -> tuple:
 
 
 def spc_retrieval_logits(shape: SpcShape, q, k, lengths, logits, tile_stats, stream=None) -> None:
-    for t, n in ((q, "q"), (k, "k"), (lengths, "lengths"), (logits, "logits"), (tile_stats, "tile_stats")):
+    """tile_stats may be None when every query head is its own group (no stats are then computed)."""
+    for t, n in ((q, "q"), (k, "k"), (lengths, "lengths"), (logits, "logits")):
         _dev(t, n)
+    if tile_stats is not None:
+        _dev(tile_stats, "tile_stats")
     _check(L.lib().spc_retrieval_logits(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(lengths), _ptr(logits),
                                         _ptr(tile_stats), _nbytes(tile_stats), _stream(stream)))
 

@@ -157,15 +157,18 @@ int spc_retrieval_scores(const spc_shape* s, const void* q, const void* k, const
 int spc_retrieval_logits(const spc_shape* s, const void* q, const void* k, const int32_t* lengths, float* logits,
                          float* tile_stats, size_t tile_stats_bytes, void* stream) {
   if (int e = check_shape(s)) return e;
-  if (!q || !k || !lengths || !logits || !tile_stats)
-    return fail(SPC_ERR_INVALID_ARG, "NULL q, k, lengths, logits or tile_stats");
+  if (!q || !k || !lengths || !logits)
+    return fail(SPC_ERR_INVALID_ARG, "NULL q, k, lengths or logits");
+  if (!tile_stats && s->n_q_heads != s->n_groups)
+    return fail(SPC_ERR_INVALID_ARG, "tile_stats are needed with %d query heads per group",
+                s->n_q_heads / s->n_groups);
   if (!spc::scores_supported(*s))
     return fail(SPC_ERR_UNSUPPORTED, "retrieval logits: head_dim %d with dtype %d", s->head_dim, s->dtype);
   if (!aligned16(q) || !aligned16(k)) return fail(SPC_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
   if (!aligned4(logits) || !aligned4(lengths)) return fail(SPC_ERR_INVALID_ARG, "logits/lengths misaligned");
   if ((reinterpret_cast<uintptr_t>(tile_stats) & 7u) != 0)
     return fail(SPC_ERR_INVALID_ARG, "tile_stats must be 8-byte aligned");
-  if (tile_stats_bytes < spc::scores_ws_bytes(*s))
+  if (tile_stats && tile_stats_bytes < spc::scores_ws_bytes(*s))
     return fail(SPC_ERR_INVALID_ARG, "tile_stats holds %zu bytes, the shape needs %zu", tile_stats_bytes,
                 spc::scores_ws_bytes(*s));
   const hipError_t e = spc::launch_logits(*s, q, k, lengths, logits, reinterpret_cast<float2*>(tile_stats),

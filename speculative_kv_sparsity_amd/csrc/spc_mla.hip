@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void mla_scores_kernel(const floa
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             lv[2 * pr + blk][i] = (acc[blk][0][i] + acc[blk][1][i]) * scale;
-            if (valid) online_ms(m_run[i], s_run[i], lv[2 * pr + blk][i]);
+            if (valid && part) online_ms(m_run[i], s_run[i], lv[2 * pr + blk][i]);
           }
         }
       }
@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kScoreThreads, 1) void mla_scores_kernel(const floa
     __syncthreads();                                 // the next sub-tile landed; this buffer is free
   }
   if (lpos >= 0) store_held();
-  if (active) {
-    // merge (max, sum) over the 16 lanes of each row group (the tile's positions)
+  if (active && part) {
+    // merge (max, sum) over the 16 lanes of each row group (the tile's positions); part is NULL
+    // when the caller wants no tile stats
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll

@@ -112,15 +112,17 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
     }
   }
 
-  // tile (max, sum exp) of head p over this workgroup's rows
+  // tile (max, sum exp) of head p over this workgroup's rows (not wanted: part is NULL, uniform)
   __shared__ float s_m[4][8];
   __shared__ float s_s[4][8];
   float m = -INFINITY;
+  if (part) {
 #pragma unroll
-  for (int i = 0; i < kIters; ++i) m = fmaxf(m, lg[i]);
-  m = max_across_rows8(m);
-  if (rr == 0) s_m[wid][p] = m;
-  __syncthreads();
+    for (int i = 0; i < kIters; ++i) m = fmaxf(m, lg[i]);
+    m = max_across_rows8(m);
+    if (rr == 0) s_m[wid][p] = m;
+  }
+  __syncthreads();                                 // also publishes the logits in slg
   // logits of the valid rows: 16-byte stores where four rows are valid and the row start is aligned
   {
     const int nrow = min(kScoreTile, n - row0);
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(kThreads) void scores_logits_kernel(
       }
     }
   }
+  if (!part) return;
   const float M = fmaxf(fmaxf(s_m[0][p], s_m[1][p]), fmaxf(s_m[2][p], s_m[3][p]));
   float sum = 0.f;
   if (M != -INFINITY) {

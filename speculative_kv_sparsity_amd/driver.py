@@ -72,9 +72,11 @@ class SparseDecoder:
         self.host_kv = host_kv
         self.host_l = api.kv_layout(host_kv)
         i32 = dict(dtype=torch.int32, device=dev)
-        # stage 1 in log-domain form: logits + per-tile (max, sum exp); stage 2 ranks them directly
+        # stage 1 in log-domain form: logits + per-tile (max, sum exp); stage 2 ranks them directly.
+        # With one query head per group the ranking needs no stats, and stage 1 computes none
         self.logits = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
         self.tile_stats = torch.empty(api.tile_stats_shape(self.shape), dtype=torch.float32, device=dev)
+        self.stats_out = self.tile_stats if Hq > G else None
         self.sel_idx = torch.empty((B, G, K), **i32)
         self.sel_count = torch.empty((B, G), **i32)
         self.slot_pos = torch.empty((B, G, K), **i32)
@@ -147,7 +149,7 @@ class SparseDecoder:
 
     # --- the four stages --------------------------------------------------------------
     def scores(self, q: torch.Tensor, lengths: torch.Tensor) -> None:
-        api.spc_retrieval_logits(self.shape, q, self.dlm_k, lengths, self.logits, self.tile_stats, stream=self.main)
+        api.spc_retrieval_logits(self.shape, q, self.dlm_k, lengths, self.logits, self.stats_out, stream=self.main)
 
     def topk(self, lengths: torch.Tensor) -> None:
         api.spc_group_max_topk_logits(self.shape, self.logits, self.tile_stats, lengths, self.sel_idx,
@@ -285,9 +287,11 @@ class LagOneDecoder:
         self.dlm_k, self.host_kv = dlm_k, host_kv
         self.host_l = api.kv_layout(host_kv)
         i32 = dict(dtype=torch.int32, device=dev)
-        # stage 1 in log-domain form: logits + per-tile (max, sum exp); stage 2 ranks them directly
+        # stage 1 in log-domain form: logits + per-tile (max, sum exp); stage 2 ranks them directly.
+        # With one query head per group the ranking needs no stats, and stage 1 computes none
         self.logits = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
         self.tile_stats = torch.empty(api.tile_stats_shape(self.shape), dtype=torch.float32, device=dev)
+        self.stats_out = self.tile_stats if Hq > G else None
         self.sel = [torch.empty((B, G, K), **i32) for _ in range(2)]
         self.cnt = [torch.empty((B, G), **i32) for _ in range(2)]
         self.slot_pos = torch.empty((B, G, P), **i32)
@@ -317,7 +321,7 @@ class LagOneDecoder:
         nx = self.t % 2
         cur = nx if self.t == 0 else 1 - nx
         mark("scores", self.main)
-        api.spc_retrieval_logits(self.shape, q, self.dlm_k, lengths, self.logits, self.tile_stats, stream=self.main)
+        api.spc_retrieval_logits(self.shape, q, self.dlm_k, lengths, self.logits, self.stats_out, stream=self.main)
         mark("topk", self.main)
         api.spc_group_max_topk_logits(self.shape, self.logits, self.tile_stats, lengths, self.sel[nx],
                                       self.cnt[nx], ws=self.ws_topk, stream=self.main)
@@ -399,6 +403,7 @@ class MlaDecoder:
         self.q_abs = torch.empty((B, H, p.head_dim), **f32)
         self.logits = torch.empty((B, H, L), **f32)
         self.tile_stats = torch.empty(api.tile_stats_shape(self.shape), **f32)
+        self.stats_out = None       # one head per group: the Top-K ranks the logits, no stats needed
         self.sel_idx = torch.empty((B, H, K), **i32)
         self.sel_count = torch.empty((B, H), **i32)
         self.slot_pos = torch.empty((B, H, K), **i32)
@@ -425,7 +430,7 @@ class MlaDecoder:
         mark("absorb", st)
         api.spc_mla_absorb_q(s, self.p.nope_dim, self.w_uk, q_nope, q_rope, self.q_abs, stream=st)
         mark("scores", st)
-        api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.tile_stats, stream=st)
+        api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.stats_out, stream=st)
         mark("topk", st)
         api.spc_group_max_topk_plan_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count,
                                            self.slot_pos, self.resident_bm, self.load_pos, self.load_slot,
@@ -520,7 +525,7 @@ class MlaLiteralDecoder(MlaDecoder):
         mark("absorb", st)
         api.spc_mla_absorb_q(s, self.p.nope_dim, self.w_uk, q_nope, q_rope, self.q_abs, stream=st)
         mark("scores", st)
-        api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.tile_stats, stream=st)
+        api.spc_retrieval_logits(s, self.q_abs, self.latent, lengths, self.logits, self.stats_out, stream=st)
         mark("topk", st)
         api.spc_group_max_topk_plan_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count,
                                            self.slot_pos, self.resident_bm, self.load_pos, self.load_slot,

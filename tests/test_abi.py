@@ -205,12 +205,12 @@ def test_log_domain_scoring_sizes_and_validation():
     assert lib.spc_tile_stats_size(ctypes.byref(s)) == 2 * 32 * 8 * 8          # ceil(1000 / 128) = 8 tiles
     mla = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
                  budget=2048, scale=192 ** -0.5)
-    # 4 sequences x 2 head groups x 64 tiles of 512 = 512 scoring workgroups: the large tile
+    # 4 sequences x 64 tiles of 512 = 256 scoring workgroups (all 128 heads each): the large tile
     assert lib.spc_score_tile(ctypes.byref(mla)) == 512
     assert lib.spc_tile_stats_size(ctypes.byref(mla)) == 4 * 128 * 64 * 8
     mla1 = _shape(batch=1, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
                   budget=2048, scale=192 ** -0.5)
-    assert lib.spc_score_tile(ctypes.byref(mla1)) == 256                      # 128 workgroups of 512: too few
+    assert lib.spc_score_tile(ctypes.byref(mla1)) == 256                      # 64 workgroups of 512: too few
     assert lib.spc_tile_stats_size(ctypes.byref(mla1)) == 128 * 128 * 8
     assert lib.spc_score_tile(ctypes.byref(_shape(budget=0))) == 0
     p = ctypes.c_void_p(256)
@@ -228,6 +228,11 @@ def test_log_domain_scoring_sizes_and_validation():
                                     None) == L.SPC_ERR_UNSUPPORTED
     assert lib.spc_retrieval_logits(ctypes.byref(_shape(max_len=1 << 22)), p, p, p, p, None, 1 << 40,
                                     None) == L.SPC_ERR_INVALID_ARG
+    # with one query head per group the stats may be NULL: validation goes on past them (here to the
+    # unsupported head_dim) instead of rejecting the NULL
+    one = _shape(n_q_heads=8, n_groups=8, head_dim=96)
+    assert lib.spc_retrieval_logits(ctypes.byref(one), p, p, p, p, None, 0, None) == L.SPC_ERR_UNSUPPORTED
+    assert b"tile_stats" not in lib.spc_last_error()
     need = lib.spc_workspace_size(L.SPC_CALL_TOPK, ctypes.byref(s))
     # four heads per group: the tile stats are required, and their size is checked
     assert lib.spc_group_max_topk_logits(ctypes.byref(s), p, None, 0, p, p, p, p, need, None) == L.SPC_ERR_INVALID_ARG

@@ -20,6 +20,7 @@ def _bf(t):
 
 def _check_steps(p, w, steps, lengths_override=None, heads=None, batches=None):
     dec = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+    dec.stats_out = dec.tile_stats          # the step needs no tile stats; they are checked here
     T = api.spc_score_tile(dec.shape)
     C = p.latent_dim
     w_uk, w_uv = _bf(w.w_uk), _bf(w.w_uv)
@@ -192,3 +193,38 @@ def test_mla_graph_replay_equals_eager_steps():
         assert torch.isfinite(junk)
         for k in names:
             assert torch.equal(getattr(dec, k), eager[t][k]), f"{k} at step {t}"
+
+
+@pytest.mark.parametrize("kind", ["mla", "mha"])
+def test_logits_without_tile_stats_are_the_same(kind):
+    """With one query head per group the tile stats may be left out (NULL): the logits, and the Top-K
+    taken from them, are bit-identical to a call that computes them."""
+    if kind == "mla":
+        p = W.PRESETS["mla_32k"].with_(batch=2, n_q_heads=32, max_len=3000, budget=128)
+        w = W.generate(p, device="cuda", seed=12, steps=1)
+        dec = MlaDecoder(p, w.latent, w.w_uk, w.w_uv)
+        shape = dec.shape
+        q = torch.empty((p.batch, p.n_q_heads, p.head_dim), dtype=torch.float32, device="cuda")
+        api.spc_mla_absorb_q(shape, p.nope_dim, w.w_uk, w.q_nope[0].contiguous(), w.q_rope[0].contiguous(), q)
+        k = w.latent
+    else:
+        p = W.PRESETS["mha_64k"].with_(batch=2, n_q_heads=4, n_kv_heads=4, max_len=5000, budget=256)
+        w = W.generate(p, device="cuda", seed=12, steps=1)
+        shape = api.make_shape(p.batch, p.n_q_heads, p.n_kv_heads, p.n_groups, p.head_dim, p.v_dim, p.max_len,
+                               p.budget, 1, p.dtype, p.scale)
+        q, k = w.q[0].contiguous(), w.dlm_k
+    lengths = dev_lengths([p.max_len, p.max_len - 777])
+    a = torch.full((p.batch, p.n_q_heads, p.max_len), float("nan"), device="cuda")
+    b = a.clone()
+    stats = torch.empty(api.tile_stats_shape(shape), device="cuda")
+    api.spc_retrieval_logits(shape, q, k, lengths, a, stats)
+    api.spc_retrieval_logits(shape, q, k, lengths, b, None)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(a, nan=7.0), torch.nan_to_num(b, nan=7.0))
+    i32 = dict(dtype=torch.int32, device="cuda")
+    s1, c1 = torch.empty((p.batch, p.n_groups, p.budget), **i32), torch.empty((p.batch, p.n_groups), **i32)
+    s2, c2 = s1.clone(), c1.clone()
+    api.spc_group_max_topk_logits(shape, a, None, lengths, s1, c1)
+    api.spc_group_max_topk_logits(shape, b, None, lengths, s2, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(c1, c2)
