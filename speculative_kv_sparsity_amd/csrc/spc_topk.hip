@@ -721,6 +721,267 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   if (kPlan) plan(selw);
 }
 
+// Rows of 32 769 .. 65 536 keys with a budget of at most kRegList: the keys stay in registers, 64 per
+// thread in strided (coalesced) vectors v = tid + 1024 u, and never in LDS.  With one head per group
+// the first digit (12 bits) is counted here from the loaded keys and no keys pass runs; otherwise it
+// comes from the chunk histograms (8 bits).  The sweep marks keys above the threshold's first-digit
+// bin in an LDS bitmap of the row (one atomicOr per 4-key vector: a vector is 4 bits of one word) and
+// lists the candidates' positions; their keys are fetched once more from the row (L2) into the list,
+// so the later digit passes and the final compare run over the list alone.  Thread t then owns bitmap
+// words 2t and 2t + 1 (positions [64t, 64t + 64)) for the ordered output.
+constexpr int kRegKeys = 65536;
+constexpr int kRegList = 8192;
+
+template <bool RAW>
+__global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint32_t* __restrict__ keys,
+                                                                      const uint32_t* __restrict__ chist,
+                                                                      const int32_t* __restrict__ lengths,
+                                                                      int32_t* __restrict__ sel_idx,
+                                                                      int32_t* __restrict__ sel_count,
+                                                                      int n_groups, int max_len, int budget,
+                                                                      int nchunk) {
+  constexpr int kWords = kRegKeys / 32;            // bitmap words of a row: 2 per thread
+  constexpr int kVec = kRegKeys / 4 / kSelThreads;  // 16 vectors = 64 keys per thread
+  constexpr int S1 = RAW ? 20 : 24;
+  constexpr int S2 = S1 - 12;
+  static_assert(kWords == 2 * kSelThreads && kRegList % kSelThreads == 0, "row and list layout");
+  __shared__ uint32_t hist[4096];
+  __shared__ int32_t cpos[kRegList];               // candidate positions; later the staged selection
+  __shared__ uint32_t ckey[kRegList];
+  __shared__ uint32_t gtbm[kWords], selbm[kWords], tiebm[kWords];
+  __shared__ __align__(16) uint32_t scan_smem[16];
+  __shared__ uint32_t bcast[2];
+  __shared__ uint32_t ccount;
+
+  const int inst = blockIdx.x;
+  const int b = inst / n_groups;
+  const int n = clamp_len(lengths, b, max_len);
+  const int K = budget;
+  const int tid = threadIdx.x;
+  int32_t* out = sel_idx + (size_t)inst * K;
+  if (n <= K) {
+    for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
+    if (tid == 0) sel_count[inst] = n;
+    return;
+  }
+  const uint32_t* kin = keys + (size_t)inst * max_len;
+  const int nv = (n + 3) / 4;
+  const bool aligned = (max_len & 3) == 0;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kin), (short)0,
+                                                                      aligned ? nv * 16 : n * 4, kBufferRsrcWord3);
+  auto load_vec = [&](int u) -> uint4 {             // keys 4v .. 4v + 3, v = tid + 1024 u (zeros past the row)
+    const int o = (tid + u * kSelThreads) * 16;
+    if (aligned) {
+      const Vec16 x = ld16_buffer(kr, (uint32_t)o);
+      return make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
+    }
+    return make_uint4((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, o, 0, 0),
+                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, o + 4, 0, 0),
+                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, o + 8, 0, 0),
+                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, o + 12, 0, 0));
+  };
+  uint4 v[kVec];
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) v[u] = load_vec(u);
+  const int hbin = tid & (kBins1 - 1), c0 = tid >> 8;
+  uint32_t hs = 0u;
+  if (!RAW) {                                       // first digit: the chunk histograms (<= 64 chunks)
+    const int nch = (n + kKeyChunk - 1) / kKeyChunk;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(chist + (size_t)inst * nchunk * kBins1), (short)0, nch * kBins1 * 4, kBufferRsrcWord3);
+    uint32_t hv[kRegKeys / kKeyChunk / 4];
+#pragma unroll
+    for (int u = 0; u < kRegKeys / kKeyChunk / 4; ++u)
+      hv[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, ((c0 + 4 * u) * kBins1 + hbin) * 4, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kRegKeys / kKeyChunk / 4; ++u) hs += hv[u];
+  }
+#pragma unroll
+  for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    gtbm[tid + i * kSelThreads] = 0u;
+    selbm[tid + i * kSelThreads] = 0u;
+    tiebm[tid + i * kSelThreads] = 0u;
+  }
+  if (tid == 0) ccount = 0u;
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) v[u] = to_keys<RAW>(v[u]);
+  __syncthreads();
+  if (RAW) {
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const int j = 4 * (tid + u * kSelThreads);
+      if (j + 3 < n) {
+        atomicAdd(&hist[v[u].x >> S1], 1u);
+        atomicAdd(&hist[v[u].y >> S1], 1u);
+        atomicAdd(&hist[v[u].z >> S1], 1u);
+        atomicAdd(&hist[v[u].w >> S1], 1u);
+      } else if (j < n) {
+        atomicAdd(&hist[v[u].x >> S1], 1u);
+        if (j + 1 < n) atomicAdd(&hist[v[u].y >> S1], 1u);
+        if (j + 2 < n) atomicAdd(&hist[v[u].z >> S1], 1u);
+      }
+    }
+  } else {
+    atomicAdd(&hist[hbin], hs);
+  }
+  __syncthreads();
+
+  int need = K;
+  find_bin_fixed<(1 << (32 - S1))>(hist, need, scan_smem, bcast);
+  const uint32_t d1 = bcast[0];
+  need -= (int)bcast[1];
+  const int ncand = (int)hist[d1];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+
+  // the sweep: above the bin -> the gt bitmap; in the bin -> a candidate (bit 4u + e of cm)
+  uint64_t cm = 0u;
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const int i4 = tid + u * kSelThreads;
+    const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t g4 = 0u, c4 = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = 4 * i4 + e < n;
+      const uint32_t top = k4[e] >> S1;
+      g4 |= (uint32_t)(valid && top > d1) << e;
+      c4 |= (uint32_t)(valid && top == d1) << e;
+    }
+    if (g4) atomicOr(&gtbm[i4 >> 3], g4 << (4 * (i4 & 7)));
+    cm |= (uint64_t)c4 << (4 * u);
+  }
+  const bool use_list = ncand <= kRegList;         // uniform over the workgroup
+  if (use_list) {
+    const uint32_t c = (uint32_t)__popcll(cm);
+    const uint32_t incl = wave_incl_scan(c);
+    uint32_t wbase = 0u;
+    if ((tid & (kWave - 1)) == kWave - 1 && incl) wbase = atomicAdd(&ccount, incl);
+    uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)wbase, kWave - 1) + incl - c;
+    for (uint64_t m = cm; m; m &= m - 1) {
+      const int bit = __builtin_ctzll(m);
+      if (at < (uint32_t)kRegList) cpos[at++] = 4 * (tid + (bit >> 2) * kSelThreads) + (bit & 3);
+    }
+  }
+  __syncthreads();
+  constexpr int kListPerThread = kRegList / kSelThreads;
+  if (use_list) {
+    // the candidates' keys, fetched once more from the row (L2), all loads in flight together
+    uint32_t kk[kListPerThread];
+#pragma unroll
+    for (int q = 0; q < kListPerThread; ++q) {
+      const int i = tid + q * kSelThreads;
+      kk[q] = i < ncand ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, cpos[i] * 4, 0, 0) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kListPerThread; ++q) {
+      const int i = tid + q * kSelThreads;
+      if (i < ncand) {
+        const uint32_t k = RAW ? order_key(__uint_as_float(kk[q])) : kk[q];
+        ckey[i] = k;                                // read back only by this thread
+        atomicAdd(&hist[(k >> S2) & 4095u], 1u);
+      }
+    }
+  } else {                                          // a bin past the list: the keys read again (L2)
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const uint4 w = to_keys<RAW>(load_vec(u));
+      const uint32_t k4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((cm >> (4 * u + e)) & 1u) atomicAdd(&hist[(k4[e] >> S2) & 4095u], 1u);
+    }
+  }
+  __syncthreads();
+  find_bin_fixed<4096>(hist, need, scan_smem, bcast);
+  uint32_t prefix = (d1 << S1) | (bcast[0] << S2);
+  uint32_t pmask = ~((1u << S2) - 1u);
+  need -= (int)bcast[1];
+  const bool whole = (int)hist[bcast[0]] == need;
+  __syncthreads();
+  if (!whole) {
+#pragma unroll
+    for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+    __syncthreads();
+    if (use_list) {
+#pragma unroll
+      for (int q = 0; q < kListPerThread; ++q) {
+        const int i = tid + q * kSelThreads;
+        if (i < ncand) {
+          const uint32_t k = ckey[i];
+          if ((k & pmask) == prefix) atomicAdd(&hist[k & ((1u << S2) - 1u)], 1u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) {
+        const uint4 w = to_keys<RAW>(load_vec(u));
+        const uint32_t k4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (((cm >> (4 * u + e)) & 1u) && (k4[e] & pmask) == prefix) atomicAdd(&hist[k4[e] & ((1u << S2) - 1u)], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin_fixed<(1 << S2)>(hist, need, scan_smem, bcast);
+    prefix |= bcast[0];
+    pmask = 0xFFFFFFFFu;
+    need -= (int)bcast[1];
+  }
+  // resolve the candidates into the selected and tied bitmaps
+  if (use_list) {
+#pragma unroll
+    for (int q = 0; q < kListPerThread; ++q) {
+      const int i = tid + q * kSelThreads;
+      if (i < ncand) {
+        const int j = cpos[i];
+        const uint32_t mk = ckey[i] & pmask;
+        if (mk > prefix) atomicOr(&selbm[j >> 5], 1u << (j & 31));
+        else if (mk == prefix) atomicOr(&tiebm[j >> 5], 1u << (j & 31));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const int i4 = tid + u * kSelThreads;
+      const uint4 w = to_keys<RAW>(load_vec(u));
+      const uint32_t k4[4] = {w.x, w.y, w.z, w.w};
+      uint32_t s4 = 0u, t4 = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool c = (cm >> (4 * u + e)) & 1u;
+        const uint32_t mk = k4[e] & pmask;
+        s4 |= (uint32_t)(c && mk > prefix) << e;
+        t4 |= (uint32_t)(c && mk == prefix) << e;
+      }
+      if (s4) atomicOr(&selbm[i4 >> 3], s4 << (4 * (i4 & 7)));
+      if (t4) atomicOr(&tiebm[i4 >> 3], t4 << (4 * (i4 & 7)));
+    }
+  }
+  __syncthreads();
+  // thread t: positions [64t, 64t + 64) = words 2t, 2t + 1
+  const uint64_t selm = ((uint64_t)(gtbm[2 * tid + 1] | selbm[2 * tid + 1]) << 32) | (gtbm[2 * tid] | selbm[2 * tid]);
+  const uint64_t eqm = ((uint64_t)tiebm[2 * tid + 1] << 32) | tiebm[2 * tid];
+  const uint32_t gt = (uint32_t)__popcll(selm), eq = (uint32_t)__popcll(eqm);
+  uint32_t tot;
+  // gt totals at most K <= kRegList < 2^14; eq totals at most 65536 < 2^18
+  const uint32_t before = scan_block((eq << 14) | gt, scan_smem, tot);
+  const int eq_before = (int)(before >> 14), gt_before = (int)(before & 0x3FFFu);
+  const int take_eq = max(0, min((int)eq, need - eq_before));
+  uint64_t keep_eq = eqm;
+  for (int drop = (int)eq - take_eq; drop > 0; --drop) keep_eq &= ~(1ull << (63 - __clzll(keep_eq)));
+  // stage the selection in LDS (the candidate list is read no more: the scan's barriers passed)
+  int o = gt_before + min(eq_before, need);
+  for (uint64_t m = selm | keep_eq; m; m &= m - 1)
+    if (o < K) cpos[o++] = 64 * tid + __builtin_ctzll(m);
+  __syncthreads();
+  for (int i = tid; i < K; i += kSelThreads) out[i] = cpos[i];
+  if (tid == 0) sel_count[inst] = K;
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(const spc_shape& s) {
@@ -730,6 +991,11 @@ size_t topk_ws_bytes(const spc_shape& s) {
 }
 
 namespace {
+
+// Rows past the LDS stage that the register-resident select takes.
+bool reg_select(const spc_shape& s) {
+  return s.max_len > kTopkLdsKeys && s.max_len <= kRegKeys && s.budget <= kRegList;
+}
 
 // The keys pass (group max, first-digit histograms), unless one head per group with rows that fit
 // LDS lets the select key the scores and count the first digit itself.  *kin: the keys the select
@@ -743,7 +1009,7 @@ hipError_t launch_keys(const spc_shape& s, const float* scores, const float2* st
   *chist = keys + (size_t)inst * s.max_len;
   const bool raw = s.n_q_heads == s.n_groups;
   *kin = raw ? reinterpret_cast<const uint32_t*>(scores) : keys;
-  if (raw && s.max_len <= kTopkLdsKeys) return hipSuccess;
+  if (raw && (s.max_len <= kTopkLdsKeys || reg_select(s))) return hipSuccess;
   const dim3 kg(nchunk, inst);
   if (stats)
     topk_keys_kernel<true><<<kg, kKeyThreads, 0, st>>>(scores, stats, lengths, keys, *chist, s.n_q_heads,
@@ -775,6 +1041,13 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
       topk_select_lds_kernel<false, 0><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
                                                                            sel_count, s.n_groups, s.max_len,
                                                                            s.budget, nchunk, none);
+  } else if (reg_select(s)) {
+    if (raw)
+      topk_select_reg_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                       s.n_groups, s.max_len, s.budget, nchunk);
+    else
+      topk_select_reg_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                        s.n_groups, s.max_len, s.budget, nchunk);
   } else {
     if (raw)
       topk_select_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,

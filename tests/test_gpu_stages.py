@@ -197,6 +197,10 @@ LOGIT_TIE_CASES = [
     (1, 2, 2, 30000, 2048, [30000], [-0.0, 0.0, -1.0], False),
     # rows that do not start 16-byte aligned (a length no multiple of 4), one head per group
     (2, 3, 3, 4999, 100, [4999, 4998], None, False),
+    # rows past the LDS stage (keys held in registers): unaligned rows, and every key equal, so the
+    # threshold bin outgrows the candidate list
+    (2, 3, 3, 40001, 1000, [40001, 39000], None, False),
+    (1, 2, 2, 50000, 3000, [50000], [0.125], True),
 ]
 
 
