@@ -84,22 +84,26 @@ __device__ __forceinline__ void plan_bitmap(const int32_t* S, int c, int32_t* __
   if (tid == 0) *lcount = nl;
 }
 
-// The same plan with the selection given as bitmap words: thread t holds selw, bit i of which is
-// set iff position 32t + i is selected (so S is the set bits in ascending (t, i) order), oldw, word
-// t of the resident bitmap before the step, and pos[u], the slot map entries of its slots
-// [t*Cx, t*Cx + Cx) (Cx = ceil(K / 1024) <= CPT; -1 beyond K).  Requires bm_words <= kPlanThreads.
-// The results are those of plan_bitmap on the same selection, entry for entry.
-template <int CPT>
-__device__ __forceinline__ void plan_words(uint32_t selw, uint32_t oldw, const int32_t (&pos)[CPT],
-                                           int32_t* __restrict__ sp, uint32_t* __restrict__ bm,
-                                           int32_t* __restrict__ lp, int32_t* __restrict__ ls,
-                                           int32_t* __restrict__ lcount, int K, int bm_words, int32_t* sL,
-                                           int32_t* sF, uint32_t* sB, uint32_t* scan_smem) {
+// The same plan with the selection given as bitmap words: thread t holds WPT consecutive words,
+// selw[w] = word t WPT + w of the selection's bitmap (bit i set iff position 32 (t WPT + w) + i is
+// selected, so S is the set bits in ascending order), oldw[w], the same words of the resident bitmap
+// before the step, and pos[u], the slot map entries of its slots [t*Cx, t*Cx + Cx) (Cx = ceil(K /
+// 1024) <= CPT; -1 beyond K).  Requires bm_words <= WPT * kPlanThreads.  sL, sF: K words of LDS each,
+// sB: bm_words words.  The results are those of plan_bitmap on the same selection, entry for entry.
+template <int CPT, int WPT = 1>
+__device__ __forceinline__ void plan_words(const uint32_t (&selw)[WPT], const uint32_t (&oldw)[WPT],
+                                           const int32_t (&pos)[CPT], int32_t* __restrict__ sp,
+                                           uint32_t* __restrict__ bm, int32_t* __restrict__ lp,
+                                           int32_t* __restrict__ ls, int32_t* __restrict__ lcount, int K,
+                                           int bm_words, int32_t* sL, int32_t* sF, uint32_t* sB,
+                                           uint32_t* scan_smem) {
   const int tid = threadIdx.x;
   const int32_t pos_end = bm_words * 32;
   const int Cx = (K + kPlanThreads - 1) / kPlanThreads;
   const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
-  if (tid < bm_words) sB[tid] = selw;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w)
+    if (tid * WPT + w < bm_words) sB[tid * WPT + w] = selw[w];
   __syncthreads();
   uint32_t fmask = 0u, nf_loc = 0u;
 #pragma unroll
@@ -108,8 +112,12 @@ __device__ __forceinline__ void plan_words(uint32_t selw, uint32_t oldw, const i
     const bool keep = q >= 0 && q < pos_end && ((sB[q >> 5] >> (q & 31)) & 1u);
     if (x0 + u < x1 && !keep) { fmask |= 1u << u; ++nf_loc; }
   }
-  const uint32_t lmask = tid < bm_words ? selw & ~oldw : 0u;   // selected and not resident: loaded
-  const uint32_t nl_loc = __popc(lmask);
+  uint32_t lmask[WPT], nl_loc = 0u;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) {                          // selected and not resident: loaded
+    lmask[w] = tid * WPT + w < bm_words ? selw[w] & ~oldw[w] : 0u;
+    nl_loc += __popc(lmask[w]);
+  }
   uint32_t tot;
   const uint32_t before = block_excl_scan(nf_loc | (nl_loc << 16), scan_smem, tot);   // counts <= K < 2^16
   uint32_t fo = before & 0xFFFFu, lo = before >> 16;
@@ -117,10 +125,14 @@ __device__ __forceinline__ void plan_words(uint32_t selw, uint32_t oldw, const i
 #pragma unroll
   for (int u = 0; u < CPT; ++u)
     if ((fmask >> u) & 1u) sF[fo++] = x0 + u;
-  for (uint32_t m = lmask; m; m &= m - 1) sL[lo++] = 32 * tid + __ffs(m) - 1;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w)
+    for (uint32_t m = lmask[w]; m; m &= m - 1) sL[lo++] = 32 * (tid * WPT + w) + __ffs(m) - 1;
   __syncthreads();
   for (int i = tid; i < nf; i += kPlanThreads) sp[sF[i]] = i < nl ? sL[i] : -1;
-  if (tid < bm_words) bm[tid] = selw;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w)
+    if (tid * WPT + w < bm_words) bm[tid * WPT + w] = selw[w];
   for (int i = tid; i < K; i += kPlanThreads) {
     const bool v = i < nl;
     lp[i] = v ? sL[i] : -1;

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   constexpr bool kPlan = CPT > 0;
   constexpr int kP = kPlan ? CPT : 1;
   // the plan's inputs, loaded first so that their latency hides behind the select
-  uint32_t oldw = 0u;
+  uint32_t oldw[1] = {0u};
   int32_t pos[kP];
   int32_t* sp = pb.slot_pos + (size_t)inst * K;
   uint32_t* bm = pb.resident_bm + (size_t)inst * pb.bm_words;
@@ -486,13 +486,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
     const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
 #pragma unroll
     for (int u = 0; u < kP; ++u) pos[u] = x0 + u < x1 ? sp[x0 + u] : -1;
-    if (tid < pb.bm_words) oldw = bm[tid];
+    if (tid < pb.bm_words) oldw[0] = bm[tid];
   }
   auto plan = [&](uint32_t selw) {
     int32_t* sL = reinterpret_cast<int32_t*>(skeys);
-    plan_words<kP>(selw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
-                   pb.load_count + inst, K, pb.bm_words, sL + K, sL + 2 * K, reinterpret_cast<uint32_t*>(sL + 3 * K),
-                   scan_smem);
+    const uint32_t sw[1] = {selw};
+    plan_words<kP, 1>(sw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
+                      pb.load_count + inst, K, pb.bm_words, sL + K, sL + 2 * K,
+                      reinterpret_cast<uint32_t*>(sL + 3 * K), scan_smem);
   };
   if (n <= K) {
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
@@ -732,14 +733,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
 constexpr int kRegKeys = 65536;
 constexpr int kRegList = 8192;
 
-template <bool RAW>
+template <bool RAW, int CPT>
 __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint32_t* __restrict__ keys,
                                                                       const uint32_t* __restrict__ chist,
                                                                       const int32_t* __restrict__ lengths,
                                                                       int32_t* __restrict__ sel_idx,
                                                                       int32_t* __restrict__ sel_count,
                                                                       int n_groups, int max_len, int budget,
-                                                                      int nchunk) {
+                                                                      int nchunk, PlanBufs pb) {
   constexpr int kWords = kRegKeys / 32;            // bitmap words of a row: 2 per thread
   constexpr int kVec = kRegKeys / 4 / kSelThreads;  // 16 vectors = 64 keys per thread
   constexpr int S1 = RAW ? 20 : 24;
@@ -759,9 +760,35 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   const int K = budget;
   const int tid = threadIdx.x;
   int32_t* out = sel_idx + (size_t)inst * K;
+  // with CPT > 0 the instance's plan follows (2 K <= kRegList: its lists take the key list's LDS)
+  constexpr bool kPlan = CPT > 0;
+  constexpr int kP = kPlan ? CPT : 1;
+  uint32_t oldw[2] = {0u, 0u};
+  int32_t pos[kP];
+  int32_t* sp = pb.slot_pos + (size_t)inst * K;
+  uint32_t* bm = pb.resident_bm + (size_t)inst * pb.bm_words;
+  if (kPlan) {
+    const int Cx = (K + kSelThreads - 1) / kSelThreads;
+    const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
+#pragma unroll
+    for (int u = 0; u < kP; ++u) pos[u] = x0 + u < x1 ? sp[x0 + u] : -1;
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+      if (2 * tid + w < pb.bm_words) oldw[w] = bm[2 * tid + w];
+  }
+  auto plan = [&](uint64_t sel64) {
+    const uint32_t sw[2] = {(uint32_t)sel64, (uint32_t)(sel64 >> 32)};
+    plan_words<kP, 2>(sw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
+                      pb.load_count + inst, K, pb.bm_words, reinterpret_cast<int32_t*>(ckey),
+                      reinterpret_cast<int32_t*>(ckey) + K, gtbm, scan_smem);
+  };
   if (n <= K) {
     for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
     if (tid == 0) sel_count[inst] = n;
+    if (kPlan) {
+      const int r = n - 64 * tid;                  // this thread's positions [64 tid, 64 tid + 64)
+      plan(r >= 64 ? ~0ull : r > 0 ? (1ull << r) - 1ull : 0ull);
+    }
     return;
   }
   const uint32_t* kin = keys + (size_t)inst * max_len;
@@ -980,6 +1007,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   __syncthreads();
   for (int i = tid; i < K; i += kSelThreads) out[i] = cpos[i];
   if (tid == 0) sel_count[inst] = K;
+  if (kPlan) plan(selm | keep_eq);                  // its LDS (key list, gt bitmap) is read no more
 }
 
 }  // namespace
@@ -1043,11 +1071,13 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
                                                                            s.budget, nchunk, none);
   } else if (reg_select(s)) {
     if (raw)
-      topk_select_reg_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
-                                                                       s.n_groups, s.max_len, s.budget, nchunk);
+      topk_select_reg_kernel<true, 0><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
+                                                                          s.n_groups, s.max_len, s.budget, nchunk,
+                                                                          none);
     else
-      topk_select_reg_kernel<false><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
-                                                                        s.n_groups, s.max_len, s.budget, nchunk);
+      topk_select_reg_kernel<false, 0><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,
+                                                                           sel_count, s.n_groups, s.max_len,
+                                                                           s.budget, nchunk, none);
   } else {
     if (raw)
       topk_select_kernel<true><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
@@ -1060,8 +1090,11 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
 }
 
 bool select_plan_fused(const spc_shape& s) {
-  // the staged selection and the plan's lists (3 K words) and bitmap (<= 1024 words) fit the keys' LDS
-  return s.max_len <= kTopkLdsKeys && s.budget <= kPlanMaxBudget && 3 * s.budget + 1024 <= kTopkLdsKeys;
+  // LDS select: the staged selection and the plan's lists (3 K words) and bitmap (<= 1024 words) fit
+  // the keys' LDS; register select: the plan's two lists fit the key list
+  if (s.max_len <= kTopkLdsKeys)
+    return s.budget <= kPlanMaxBudget && 3 * s.budget + 1024 <= kTopkLdsKeys;
+  return reg_select(s) && 2 * s.budget <= kRegList;
 }
 
 hipError_t launch_select_plan(const spc_shape& s, const float* scores, const float2* stats, int stat_tile,
@@ -1078,6 +1111,26 @@ hipError_t launch_select_plan(const spc_shape& s, const float* scores, const flo
   const bool raw = s.n_q_heads == s.n_groups;
   const PlanBufs pb{slot_pos, resident_bm, load_pos, load_slot, load_count, (s.max_len + 31) / 32};
   const int cpt = (s.budget + kSelThreads - 1) / kSelThreads;
+  if (s.max_len > kTopkLdsKeys) {                  // register select (budget <= kRegList / 2: cpt <= 4)
+    switch ((cpt <= 1 ? 1 : cpt <= 2 ? 2 : 4) * (raw ? -1 : 1)) {
+#define SPC_CASE(N)                                                                                           \
+  case N:                                                                                                     \
+    topk_select_reg_kernel<false, N><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,        \
+                                                                         sel_count, s.n_groups, s.max_len,    \
+                                                                         s.budget, nchunk, pb);               \
+    break;                                                                                                    \
+  case -N:                                                                                                    \
+    topk_select_reg_kernel<true, N><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx,         \
+                                                                        sel_count, s.n_groups, s.max_len,     \
+                                                                        s.budget, nchunk, pb);                \
+    break;
+      SPC_CASE(1)
+      SPC_CASE(2)
+      SPC_CASE(4)
+#undef SPC_CASE
+    }
+    return hipGetLastError();
+  }
   switch ((cpt <= 1 ? 1 : cpt <= 2 ? 2 : cpt <= 4 ? 4 : 8) * (raw ? -1 : 1)) {
 #define SPC_CASE(N)                                                                                           \
   case N:                                                                                                     \

@@ -533,14 +533,17 @@ FUSED_CASES = [
     # 32768 positions) with several heads per group and with one (raw logits, 2 KB per thread of plan
     # lists at budget 4096), a batch with a short and an empty sequence and a row length that is no
     # multiple of 32, budget 8192 (8 slots per thread) with sequences at, below and just above the
-    # budget; and two where the plan runs as its own launch after the select: MHA at 64K and budget
-    # 8192 at 40000 positions
+    # budget; the register-resident select for rows past 32768 with the plan in its tail (two bitmap
+    # words per thread): MHA at 64K and two heads per group at 40000 positions with short rows; and
+    # budget 8192 at 40000 positions, where the plan runs as its own launch after the select
     ("gqa_32k", W.PRESETS["b1_32k"].with_(n_layers=1), None),
     ("mha_32k_raw", W.PRESETS["mha_64k"].with_(max_len=32768, batch=1), None),
     ("ragged", GQA_SMALL.with_(batch=3, max_len=3000, budget=256), [[3000, 100, 0], [3000, 257, 0], [2999, 300, 5]]),
     ("budget_8192_lds", GQA_SMALL.with_(batch=3, n_q_heads=4, n_kv_heads=2, max_len=20000, budget=8192),
      [[20000, 5000, 8192], [19999, 8192, 8193], [20000, 8193, 12000]]),
     ("mha_64k", W.PRESETS["mha_64k"], None),
+    ("reg_gqa_40k", GQA_SMALL.with_(batch=2, n_q_heads=4, n_kv_heads=2, max_len=40000, budget=1024),
+     [[40000, 1000], [39999, 1024], [40000, 1025]]),
     ("budget_8192", GQA_SMALL.with_(batch=1, n_q_heads=4, n_kv_heads=2, max_len=40000, budget=8192), None),
 ]
 
