@@ -106,6 +106,17 @@ __global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __r
     const int j = j0 + threadIdx.x + u * kKeyThreads;
     v[u] = j < j1 ? pb[j] : 0.f;
   }
+  // the other heads' rows of up to kMaxPre heads, loaded now so that their latency overlaps the
+  // tile-pair loads of the log-sum-exp below
+  constexpr int kMaxPre = 8;
+  float w[kMaxPre - 1][kPer];
+#pragma unroll
+  for (int hh = 1; hh < kMaxPre; ++hh)
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = j0 + threadIdx.x + u * kKeyThreads;
+      w[hh - 1][u] = hh < Gq && j < j1 ? pb[(size_t)hh * max_len + j] : 0.f;
+    }
   const bool lse = LOGITS && Gq > 1;
   if (lse) {
     // log-sum-exp of every head of the group from its tile pairs (one wave per head)
@@ -138,7 +149,17 @@ __global__ __launch_bounds__(kKeyThreads) void topk_keys_kernel(const float* __r
 #pragma unroll
     for (int u = 0; u < kPer; ++u) v[u] -= s_lse[0];
   }
-  for (int hh = 1; hh < Gq; ++hh) {
+#pragma unroll
+  for (int hh = 1; hh < kMaxPre; ++hh) {
+    if (hh >= Gq) break;
+    const float off = lse ? s_lse[hh] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = j0 + threadIdx.x + u * kKeyThreads;
+      if (j < j1) v[u] = fmaxf(v[u], w[hh - 1][u] - off);
+    }
+  }
+  for (int hh = kMaxPre; hh < Gq; ++hh) {             // groups of more than kMaxPre heads
     const float* ph = pb + (size_t)hh * max_len;
     const float off = lse ? s_lse[hh] : 0.f;
 #pragma unroll
