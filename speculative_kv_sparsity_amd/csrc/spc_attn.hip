@@ -36,6 +36,7 @@ namespace {
 constexpr int kThreads = 256;                 // 4 waves
 constexpr int kLatentTilesSmall = 4;          // MLA: 16-row tiles per wave and split (few instances)
 constexpr int kLatentTilesLarge = 16;         // (enough instances x splits to fill the chip)
+constexpr int kSplitRowsWide = 160;           // the wider splits of split_rows (5 iterations of 8 rows per wave)
 
 struct QL { int64_t b, layer, head; };        // byte strides
 struct KL { int64_t b, layer, head, row, kv; };
@@ -276,11 +277,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 // online softmax, so the 8-lane-group reduction and the cross-wave merge are paid
 // once per 64 T rows instead of once per 16.
 //
-// The heads of a sequence select largely the same rows, so the grid is one-dimensional and
-// ordered for the L2 of each XCD: the dispatcher deals block ids round-robin over the 8 XCDs, and
-// the ids of XCD x run, in order, every head of (sequence, layer, split) groups x, x + 8, ... .
-// The heads of a group, in flight together on one XCD, walk their ascending row lists at about
-// the same pace, so a row one of them reads is usually still in that L2 for the others.
+// A selected row is read by several heads of its sequence (about 8 of 128 at 32K positions and a
+// budget of 2048), so the grid is one-dimensional and ordered for the L2 of each XCD: the
+// dispatcher deals block ids round-robin over the 8 XCDs, and the ids of XCD x run, in order,
+// every head of (sequence, layer, split) groups x, x + 8, ... .  The heads of a group in flight
+// together on one XCD walk their ascending row lists at about the same pace, so a row one of
+// them reads is often still in that L2 for the others.
 template <int D, int DV, int T>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
@@ -542,6 +544,25 @@ int rows_per_split(const spc_shape& s) {
   return head_chunk(s) >= 8 ? 64 : 128;
 }
 
+// Rows per split of one call over n_lay layers.  The bf16 128-dim kernels with up to 4 heads
+// per workgroup also come with 5 iterations per wave (160 rows, still 4 workgroups per CU,
+// 1024 resident on the chip).  A launch runs in rounds of 1024 workgroups, each round about
+// as long as its split's rows; where 128-row splits leave a short last round (28 layers of
+// 8 groups x 4 head chunks x 16 splits = 3.5 rounds), the 160-row split needs fewer rounds
+// for fewer total row-times, and it is taken.  Never fewer splits than that: the workspace is
+// sized for rows_per_split.
+int split_rows(const spc_shape& s, int n_lay) {
+  const int base = rows_per_split(s);
+  if (s.dtype != SPC_BF16 || s.head_dim != 128 || s.v_dim != 128 || base != 128) return base;
+  constexpr long kResident = 1024;
+  const long per_split = (long)s.batch * n_lay * s.n_q_heads / head_chunk(s);   // workgroups per split index
+  auto cost = [&](int rows) {
+    const long wgs = per_split * ((s.budget + rows - 1) / rows);
+    return ((wgs + kResident - 1) / kResident) * rows;
+  };
+  return cost(kSplitRowsWide) < cost(base) ? kSplitRowsWide : base;
+}
+
 struct SplitArgs {
   const char* q; QL ql; const char* kv; KL kl; const int32_t* rows; const int32_t* row_count; int mode;
   int layer_begin, n_lay, nsplit, nhc, max_rows; float* part_o; float2* part_ml;
@@ -566,6 +587,17 @@ hipError_t launch_split_gqc(int gqc, const spc_shape& s, dim3 grid, hipStream_t 
   }
 }
 
+// the 160-row splits of split_rows (bf16, 128-dim keys and values, up to 4 heads per workgroup)
+hipError_t launch_split_wide(int gqc, const spc_shape& s, dim3 grid, hipStream_t st, const SplitArgs& a) {
+  static_assert(kSplitRowsWide == 4 * 8 * 5, "160 rows = 4 waves x 8 rows x 5 iterations");
+  switch (gqc) {
+    case 1: return launch_split<SPC_BF16, 128, 128, 1, 5>(s, grid, st, a);
+    case 2: return launch_split<SPC_BF16, 128, 128, 2, 5>(s, grid, st, a);
+    case 4: return launch_split<SPC_BF16, 128, 128, 4, 5>(s, grid, st, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 bool attn_supported(const spc_shape& s) {
@@ -577,6 +609,7 @@ bool attn_supported(const spc_shape& s) {
 
 int attn_splits(const spc_shape& s) { return (s.budget + rows_per_split(s) - 1) / rows_per_split(s); }
 
+// sized for rows_per_split: a call's split_rows is never smaller, so its partials fit
 size_t attn_ws_bytes_layers(const spc_shape& s, int n_lay) {
   const size_t nsplit = (size_t)(s.budget + rows_per_split(s) - 1) / rows_per_split(s);
   const size_t heads = (size_t)s.batch * n_lay * s.n_q_heads;        // one partial per head per split
@@ -588,7 +621,7 @@ size_t attn_ws_bytes(const spc_shape& s) { return attn_ws_bytes_layers(s, s.n_la
 namespace {
 
 struct AttnGeom {
-  int n_lay, nsplit, gqc, nhc;
+  int n_lay, rows, nsplit, gqc, nhc;
   size_t n_inst;
   float* part_o;
   float2* part_ml;
@@ -597,7 +630,8 @@ struct AttnGeom {
 AttnGeom attn_geom(const spc_shape& s, int layer_begin, int layer_end, void* ws) {
   AttnGeom g;
   g.n_lay = layer_end - layer_begin;
-  g.nsplit = attn_splits(s);
+  g.rows = split_rows(s, g.n_lay);
+  g.nsplit = (s.budget + g.rows - 1) / g.rows;
   g.gqc = head_chunk(s);
   g.nhc = s.n_q_heads / s.n_groups / g.gqc;
   g.n_inst = (size_t)s.batch * g.n_lay * s.n_groups;
@@ -634,6 +668,8 @@ hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_la
   hipError_t e = hipErrorInvalidValue;
   if (s.dtype == SPC_F32) {
     e = launch_split_gqc<SPC_F32, 128>(gqc, s, grid, st, a);
+  } else if (s.head_dim == 128 && g.rows == kSplitRowsWide) {
+    e = launch_split_wide(gqc, s, grid, st, a);
   } else if (s.head_dim == 128) {
     e = launch_split_gqc<SPC_BF16, 128>(gqc, s, grid, st, a);
   } else if (s.head_dim == 64) {

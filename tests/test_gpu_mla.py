@@ -228,3 +228,48 @@ def test_logits_without_tile_stats_are_the_same(kind):
     api.spc_group_max_topk_logits(shape, b, None, lengths, s2, c2)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2) and torch.equal(c1, c2)
+
+
+# Latent attention called directly: the absorbed float32 query against latent rows (keys: all 576
+# dims, values: the first 512), with ragged per-head counts and garbage past each count.
+#   large: 8 x 64 heads x 2 blocks of 1024 rows = 1024 workgroups -> splits of 1024 rows
+#   odd:   9 x 115 heads (an odd number of groups, a budget of one split) -> splits of 1024 rows
+#   small: under 1024 workgroups -> splits of 256 rows, a ragged last one
+LATENT_CASES = [("large", 8, 64, 4096, 2048), ("odd", 9, 115, 3000, 1024), ("small", 2, 6, 1500, 700)]
+
+
+@pytest.mark.parametrize("name,B,H,L,K", LATENT_CASES, ids=[c[0] for c in LATENT_CASES])
+def test_latent_attention_matches_oracle(name, B, H, L, K):
+    p = W.PRESETS["mla_32k"]
+    D, DV = p.head_dim, p.v_dim
+    rng = np.random.default_rng(11)
+    g = torch.Generator().manual_seed(12)
+    latent = torch.randn((B, L, D), generator=g).to(torch.bfloat16)
+    q = (0.6 * torch.randn((B, H, D), generator=g)).float()
+    counts = rng.integers(0, K + 1, size=(B, H)).astype(np.int32)
+    edges = [0, 1, K, K - 1, 17, 511, 512, 513, 1023, 1025]
+    for i, c in enumerate(edges):
+        if c <= K:
+            counts.flat[(i * 7) % counts.size] = c
+    rows = np.full((B, H, K), L + 7, dtype=np.int32)          # past each count: ignored
+    for b in range(B):
+        for h in range(H):
+            n = int(counts[b, h])
+            rows[b, h, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    shape = api.make_shape(B, H, 1, H, D, DV, L, K, 1, "bf16", p.scale)
+    out = torch.full((B, 1, H, DV), float("nan"), device="cuda")
+    api.spc_sparse_decode_attn(shape, q.cuda(), api.q_layout(H * D, 0, D), latent.cuda(),
+                               api.SpcKvLayout(L * D, 0, 0, D, 0), torch.from_numpy(rows).cuda(),
+                               torch.from_numpy(counts).cuda(), api.SPC_ROWS_GATHER, 0, 1, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)[:, 0]
+    lat64, q64 = _bf(latent), q.numpy().astype(np.float64)
+    err = 0.0
+    for b in range(B):
+        for h in range(H):
+            n = int(counts[b, h])
+            ref = O.sparse_attention(q64[b, h], lat64[b], lat64[b][:, :DV], rows[b, h, :n], p.scale)
+            if n == 0:
+                assert np.all(got[b, h] == 0), (b, h)
+            err = max(err, float(np.max(np.abs(got[b, h] - ref))))
+    assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, err

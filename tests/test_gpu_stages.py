@@ -475,6 +475,15 @@ ATTN_CASES = [
     ("batch_level_gather", GQA_SMALL.with_(kind="mqa"), [1000, 0], api.SPC_ROWS_GATHER),
     ("batch_level_32_heads_slots", GQA_SMALL.with_(kind="mqa", n_q_heads=32, n_kv_heads=8, max_len=1500),
      [1500, 1001], api.SPC_ROWS_SLOTS),
+    # 400 workgroups per split index (4 sequences x 25 layers x 4 groups x 4 head chunks or the
+    # like) and 300 rows: 3 splits of 128 rows need 2 rounds of 1024 workgroups, 2 of 160 rows
+    # one, so the launch takes the 160-row kernels, the second split ragged (140 rows)
+    ("wide_splits_slots", GQA_SMALL.with_(batch=4, n_layers=25, n_q_heads=16, n_kv_heads=4, max_len=600,
+                                          budget=300), [600, 599, 301, 17], api.SPC_ROWS_SLOTS),
+    ("wide_splits_2_heads_gather", GQA_SMALL.with_(batch=4, n_layers=25, n_q_heads=8, n_kv_heads=4, max_len=600,
+                                                   budget=300), [600, 0, 450, 299], api.SPC_ROWS_GATHER),
+    ("wide_splits_mha_slots", GQA_SMALL.with_(kind="mha", batch=4, n_layers=25, n_q_heads=4, n_kv_heads=4,
+                                              max_len=600, budget=300), [600, 1, 160, 161], api.SPC_ROWS_SLOTS),
 ]
 
 
@@ -489,8 +498,8 @@ def test_attention_matches_oracle(name, p, lengths, mode):
             assert np.all(got[b] == 0)
 
 
-@pytest.mark.parametrize("name,p,lengths,mode", [ATTN_CASES[i] for i in (0, 1, 2, 3)],
-                         ids=[ATTN_CASES[i][0] for i in (0, 1, 2, 3)])
+@pytest.mark.parametrize("name,p,lengths,mode", [ATTN_CASES[i] for i in (0, 1, 2, 3, 12, 13)],
+                         ids=[ATTN_CASES[i][0] for i in (0, 1, 2, 3, 12, 13)])
 def test_partial_then_merge_equals_the_whole_call(name, p, lengths, mode):
     _, _, whole = _attn_case(p, lengths, mode)
     _, _, halves = _attn_case(p, lengths, mode, halves=True)
