@@ -36,6 +36,7 @@ namespace {
 constexpr int kThreads = 256;                 // 4 waves
 constexpr int kLatentTilesSmall = 4;          // MLA: 16-row tiles per wave and split (few instances)
 constexpr int kLatentTilesLarge = 16;         // (enough instances x splits to fill the chip)
+constexpr int kLatentTilesWhole = 32;         // (a budget of <= 2048 rows in one split per head)
 constexpr int kSplitRowsWide = 160;           // the wider splits of split_rows (5 iterations of 8 rows per wave)
 
 struct QL { int64_t b, layer, head; };        // byte strides
@@ -283,12 +284,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 // every head of (sequence, layer, split) groups x, x + 8, ... .  The heads of a group in flight
 // together on one XCD walk their ascending row lists at about the same pace, so a row one of
 // them reads is often still in that L2 for the others.
-template <int D, int DV, int T>
+//
+// With fewer than 8 such groups (n_glob = 1, 2 or 4: `parts` = 8 / n_glob), each group is shared by
+// `parts` XCDs, each taking a contiguous range of its heads, so that no XCD idles.  FIN: the head
+// has one split, and the workgroup writes the normalised output itself (no merge launch).
+template <int D, int DV, int T, bool FIN>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
-    int n_lay, int nsplit, int n_glob, int max_rows, float scale, float* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
+    int n_lay, int nsplit, int n_glob, int parts, int max_rows, float scale, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, float* __restrict__ out, int n_layers) {
   constexpr int EB = 2;
   constexpr int CPLK = D * EB / 16 / 8;              // 16-byte chunks per lane of a row (9)
   constexpr int CPLV = DV * EB / 16 / 8;             // of them in the value part (8)
@@ -296,8 +301,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   constexpr int RPS = 4 * RPT * T;
   static_assert(CPLV <= CPLK && D * EB % 128 == 0 && DV * EB % 128 == 0, "latent row layout");
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int r = j % n_groups;                          // head (one per group)
-  const int gidx = (j / n_groups) * 8 + xcd;           // (sequence, layer, split) group
+  int r, gidx;                                         // head (one per group); (sequence, layer, split) group
+  if (parts > 1) {
+    const int hpp = (n_groups + parts - 1) / parts;
+    gidx = xcd % n_glob;
+    r = (xcd / n_glob) * hpp + j;
+    if (j >= hpp || r >= n_groups) return;
+  } else {
+    r = j % n_groups;
+    gidx = (j / n_groups) * 8 + xcd;
+  }
   if (gidx >= n_glob) return;
   const int split = gidx % nsplit;
   const int bl = gidx / nsplit;
@@ -414,16 +427,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
       for (int e = 0; e < 8; ++e) red[wid][(p + 8 * c) * 8 + e] = acc[c * 8 + e] * fw;
   }
   __syncthreads();
+  float L = 0.f;
+  if (MM != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += s_m[w] == -INFINITY ? 0.f : s_l[w] * __expf(s_m[w] - MM);
+  }
+  if (FIN) {
+    // the head's only split: out = sum / L (no rows: zeros), as the merge would write it
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float* o = out + (((size_t)b * n_layers + layer) * Hq + head) * DV;
+    for (int d = tid; d < DV; d += kThreads) o[d] = (red[0][d] + red[1][d] + red[2][d] + red[3][d]) * inv;
+    return;
+  }
   const size_t pbase = (size_t)inst * nsplit + split;
   for (int d = tid; d < DV; d += kThreads) part_o[pbase * DV + d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
-  if (tid == 0) {
-    float L = 0.f;
-    if (MM != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) L += s_m[w] == -INFINITY ? 0.f : s_l[w] * __expf(s_m[w] - MM);
-    }
-    part_ml[pbase] = make_float2(MM, L);
-  }
+  if (tid == 0) part_ml[pbase] = make_float2(MM, L);
 }
 
 // One workgroup per head: every thread first issues the loads of its
@@ -533,10 +551,15 @@ int head_chunk(const spc_shape& s) {
 
 // rows per split = 4 waves x 8 rows x NI of the instantiation launched below
 // (NI = 4, or 2 where registers are tight: 8 heads per workgroup); MLA latent rows:
-// 4 waves x 4 or 16 tiles of 16 rows (16 once the launch has >= 1024 workgroups)
+// 4 waves x 4, 16 or 32 tiles of 16 rows (32 for budgets of up to 2048 rows once there are >= 512
+// heads: one split per head, 512 workgroups at two per CU; else 16 once the launch has >= 1024
+// workgroups)
 int latent_tiles(const spc_shape& s) {
+  constexpr int kWhole = 4 * 16 * kLatentTilesWhole;
   constexpr int kLarge = 4 * 16 * kLatentTilesLarge;
-  const long wgs = (long)s.batch * s.n_layers * s.n_q_heads * ((s.budget + kLarge - 1) / kLarge);
+  const long heads = (long)s.batch * s.n_layers * s.n_q_heads;
+  if (s.budget <= kWhole && heads >= 512) return kLatentTilesWhole;   // one split per head, a full round
+  const long wgs = heads * ((s.budget + kLarge - 1) / kLarge);
   return wgs >= 1024 ? kLatentTilesLarge : kLatentTilesSmall;
 }
 int rows_per_split(const spc_shape& s) {
@@ -642,9 +665,13 @@ AttnGeom attn_geom(const spc_shape& s, int layer_begin, int layer_end, void* ws)
 
 }  // namespace
 
-hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
-                               const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
-                               int layer_begin, int layer_end, void* ws, hipStream_t st) {
+namespace {
+
+// fin_out: the attention output, written by the split kernel itself where the shape has one split per
+// head (MLA latent rows; the caller then launches no merge), else NULL
+hipError_t launch_partial(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
+                          const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
+                          int layer_begin, int layer_end, void* ws, float* fin_out, hipStream_t st) {
   const int eb = s.dtype == SPC_BF16 ? 2 : 4;
   const AttnGeom g = attn_geom(s, layer_begin, layer_end, ws);
   SplitArgs a;
@@ -679,18 +706,36 @@ hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_la
   } else if (s.head_dim == 576 && gqc == 1) {
     // one-dimensional grid: 8 XCD lanes x groups of every head (see the kernel)
     const int n_glob = s.batch * g.n_lay * g.nsplit;
-    const dim3 lgrid((unsigned)(8 * ((n_glob + 7) / 8) * s.n_groups));
-    if (latent_tiles(s) == kLatentTilesLarge)
-      attn_split_latent_kernel<576, 512, kLatentTilesLarge><<<lgrid, kThreads, 0, st>>>(
-          a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
-          a.layer_begin, a.n_lay, a.nsplit, n_glob, a.max_rows, s.scale, a.part_o, a.part_ml);
+    const int parts = n_glob < 8 && 8 % n_glob == 0 ? 8 / n_glob : 1;
+    const dim3 lgrid((unsigned)(parts > 1 ? 8 * ((s.n_groups + parts - 1) / parts)
+                                          : 8 * ((n_glob + 7) / 8) * s.n_groups));
+    const int tiles = latent_tiles(s);
+#define SPC_LATENT(TT, FF)                                                                                    \
+  attn_split_latent_kernel<576, 512, TT, FF><<<lgrid, kThreads, 0, st>>>(                                    \
+      a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,     \
+      a.layer_begin, a.n_lay, a.nsplit, n_glob, parts, a.max_rows, s.scale, a.part_o, a.part_ml, fin_out,      \
+      s.n_layers)
+    if (fin_out && (tiles != kLatentTilesWhole || g.nsplit != 1)) return hipErrorInvalidValue;
+    if (tiles == kLatentTilesWhole && fin_out)
+      SPC_LATENT(kLatentTilesWhole, true);
+    else if (tiles == kLatentTilesWhole)
+      SPC_LATENT(kLatentTilesWhole, false);
+    else if (tiles == kLatentTilesLarge)
+      SPC_LATENT(kLatentTilesLarge, false);
     else
-      attn_split_latent_kernel<576, 512, kLatentTilesSmall><<<lgrid, kThreads, 0, st>>>(
-          a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,
-          a.layer_begin, a.n_lay, a.nsplit, n_glob, a.max_rows, s.scale, a.part_o, a.part_ml);
+      SPC_LATENT(kLatentTilesSmall, false);
+#undef SPC_LATENT
     e = hipGetLastError();
   }
   return e;
+}
+
+}  // namespace
+
+hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
+                               const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
+                               int layer_begin, int layer_end, void* ws, hipStream_t st) {
+  return launch_partial(s, q, qlay, kv, klay, rows, row_count, mode, layer_begin, layer_end, ws, nullptr, st);
 }
 
 hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end, const void* ws, float* out,
@@ -718,9 +763,11 @@ hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end,
 hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
                        const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
                        int layer_begin, int layer_end, float* out, void* ws, hipStream_t st) {
-  const hipError_t e = launch_attn_partial(s, q, qlay, kv, klay, rows, row_count, mode, layer_begin, layer_end, ws,
-                                           st);
-  if (e != hipSuccess) return e;
+  // MLA latent rows with one split per head: the split kernel writes the output, no merge
+  const bool fin = s.head_dim == 576 && head_chunk(s) == 1 && latent_tiles(s) == kLatentTilesWhole;
+  const hipError_t e = launch_partial(s, q, qlay, kv, klay, rows, row_count, mode, layer_begin, layer_end, ws,
+                                      fin ? out : nullptr, st);
+  if (e != hipSuccess || fin) return e;
   return launch_attn_merge(s, layer_begin, layer_end, ws, out, st);
 }
 

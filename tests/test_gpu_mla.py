@@ -232,10 +232,13 @@ def test_logits_without_tile_stats_are_the_same(kind):
 
 # Latent attention called directly: the absorbed float32 query against latent rows (keys: all 576
 # dims, values: the first 512), with ragged per-head counts and garbage past each count.
-#   large: 8 x 64 heads x 2 blocks of 1024 rows = 1024 workgroups -> splits of 1024 rows
-#   odd:   9 x 115 heads (an odd number of groups, a budget of one split) -> splits of 1024 rows
-#   small: under 1024 workgroups -> splits of 256 rows, a ragged last one
-LATENT_CASES = [("large", 8, 64, 4096, 2048), ("odd", 9, 115, 3000, 1024), ("small", 2, 6, 1500, 700)]
+#   whole*: budgets of <= 2048 rows with >= 512 heads -> one split per head, the output written by
+#     the split kernel (no merge); 8, 4 and 2 (sequence, layer) groups, the last two shared by 2 and
+#     4 XCDs (an odd number of heads in the 2-XCD case)
+#   large:  a budget over 2048 rows -> splits of 1024 rows and the merge
+#   small:  few heads -> splits of 256 rows, a ragged last one
+LATENT_CASES = [("whole", 8, 64, 4096, 2048), ("whole_xcd2_odd", 4, 129, 3000, 1500),
+                ("whole_xcd4", 2, 256, 2500, 2048), ("large", 4, 128, 4096, 3000), ("small", 2, 6, 1500, 700)]
 
 
 @pytest.mark.parametrize("name,B,H,L,K", LATENT_CASES, ids=[c[0] for c in LATENT_CASES])
@@ -247,7 +250,7 @@ def test_latent_attention_matches_oracle(name, B, H, L, K):
     latent = torch.randn((B, L, D), generator=g).to(torch.bfloat16)
     q = (0.6 * torch.randn((B, H, D), generator=g)).float()
     counts = rng.integers(0, K + 1, size=(B, H)).astype(np.int32)
-    edges = [0, 1, K, K - 1, 17, 511, 512, 513, 1023, 1025]
+    edges = [0, 1, K, K - 1, 17, 511, 512, 513, 1023, 1025, 2047, 2049]
     for i, c in enumerate(edges):
         if c <= K:
             counts.flat[(i * 7) % counts.size] = c
@@ -257,11 +260,17 @@ def test_latent_attention_matches_oracle(name, B, H, L, K):
             n = int(counts[b, h])
             rows[b, h, :n] = np.sort(rng.choice(L, size=n, replace=False))
     shape = api.make_shape(B, H, 1, H, D, DV, L, K, 1, "bf16", p.scale)
+    args = (shape, q.cuda(), api.q_layout(H * D, 0, D), latent.cuda(), api.SpcKvLayout(L * D, 0, 0, D, 0),
+            torch.from_numpy(rows).cuda(), torch.from_numpy(counts).cuda(), api.SPC_ROWS_GATHER)
     out = torch.full((B, 1, H, DV), float("nan"), device="cuda")
-    api.spc_sparse_decode_attn(shape, q.cuda(), api.q_layout(H * D, 0, D), latent.cuda(),
-                               api.SpcKvLayout(L * D, 0, 0, D, 0), torch.from_numpy(rows).cuda(),
-                               torch.from_numpy(counts).cuda(), api.SPC_ROWS_GATHER, 0, 1, out)
+    api.spc_sparse_decode_attn(*args, 0, 1, out)
+    # the split kernel and the merge as two calls: the same bits as the whole call
+    ws = torch.empty(api.spc_workspace_size(api.SPC_CALL_ATTN, shape), dtype=torch.uint8, device="cuda")
+    halves = torch.full((B, 1, H, DV), float("nan"), device="cuda")
+    api.spc_attn_partial(*args, 0, 1, ws)
+    api.spc_attn_merge(shape, 0, 1, ws, halves)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(halves.cpu().numpy(), out.cpu().numpy())
     got = out.cpu().numpy().astype(np.float64)[:, 0]
     lat64, q64 = _bf(latent), q.numpy().astype(np.float64)
     err = 0.0
