@@ -752,7 +752,6 @@ def bench_mla(args, p, torch, W):
     torch.cuda.synchronize()
     churn, sel_rows, union_rows = (moved[:, j].tolist() for j in range(3))
     spans = dict(zip(names[:-1], zip(names[:-1], names[1:])))
-    spans["attn_split"] = ("attn", "attn_merge")
     avg = {k: float(np.mean([tm.ms(a, z) for tm in timers])) for k, (a, z) in spans.items()}
 
     tq, tr, tl = qn[total - 1], qr[total - 1], lens[total - 1]
@@ -812,7 +811,9 @@ def bench_mla(args, p, torch, W):
                          gathered_bytes_per_launch=int(gathered),
                          gathered_GBs=round(gathered / (iso_ms["attn_partial"] * 1e-3) / 1e9, 1)),
         "roofline_attn_call": roof("hbm", attn_bytes, iso_ms["attn"], HBM_PEAK_GBS, "GB/s",
-                                   "attn_split_latent_kernel + attn_combine_kernel (the whole stage-4 call)", 1,
+                                   "spc_sparse_decode_attn, the whole stage-4 call: one attn_split_latent_kernel "
+                                   "launch that writes the output where each head's budget fits one split (up to "
+                                   "2048 rows, 512 or more heads), else the split kernel + attn_combine_kernel", 1,
                                    traffic.get("attn")),
         "roofline_scores": roof("mfma", score_flop, iso_ms["scores"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
                                 "mla_scores_kernel (logits and per-tile max / sum exp; bf16 MFMA, fp32 query as "

@@ -436,7 +436,7 @@ class MlaDecoder:
                                            self.slot_pos, self.resident_bm, self.load_pos, self.load_slot,
                                            self.load_count, ws=self.ws_topk, stream=st)
         mark("attn", st)
-        self.attend(mark=timer.mark if timer is not None else None)
+        self.attend()
         mark("out_proj", st)
         api.spc_mla_out_proj(s, self.p.nope_dim, self.w_uv, self.o_lat, 0, self.out, stream=st)
         mark("end", st)
@@ -478,18 +478,14 @@ class MlaDecoder:
         self.g_len.copy_(lengths)
         self.graph.replay()
 
-    def attend(self, stream=None, mark=None) -> None:
-        """Attention of every head over its selected latent rows (gathered by position); with `mark`,
-        as its split and merge halves with an event "attn_merge" between them."""
+    def attend(self, stream=None) -> None:
+        """Attention of every head over its selected latent rows (gathered by position).  One call:
+        where the budget fits one split per head the library runs it as a single launch, so the
+        step is timed as it runs, without a split at the merge."""
         st = self.main if stream is None else stream
-        args = (self.shape, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx, self.sel_count,
-                api.SPC_ROWS_GATHER, 0, 1)
-        if mark is None:
-            api.spc_sparse_decode_attn(*args, self.o_lat, ws=self.ws_attn, stream=st)
-        else:
-            api.spc_attn_partial(*args, self.ws_attn, stream=st)
-            mark("attn_merge", st)
-            api.spc_attn_merge(self.shape, 0, 1, self.ws_attn, self.o_lat, stream=st)
+        api.spc_sparse_decode_attn(self.shape, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx,
+                                   self.sel_count, api.SPC_ROWS_GATHER, 0, 1, self.o_lat, ws=self.ws_attn,
+                                   stream=st)
 
 
 class MlaLiteralDecoder(MlaDecoder):

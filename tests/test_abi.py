@@ -96,8 +96,13 @@ def test_workspace_sizes():
     m = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
                budget=2048, scale=192 ** -0.5)
     assert lib.spc_workspace_size(L.SPC_CALL_SCORES, ctypes.byref(m)) == 4 * 128 * 64 * 8   # tiles of 512
-    # 1024-row splits once the launch has >= 1024 workgroups (4 x 128 x 2 here)
-    assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(m)) == 4 * 128 * 2 * (512 * 4 + 8)
+    # one 2048-row split per head for budgets of up to 2048 rows with >= 512 heads (4 x 128 here; the
+    # whole call then writes the output from the split kernel, but spc_attn_partial still fills these)
+    assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(m)) == 4 * 128 * 1 * (512 * 4 + 8)
+    # a larger budget: 1024-row splits once the launch has >= 1024 workgroups (4 x 128 x 3 here)
+    m3 = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                budget=3000, scale=192 ** -0.5)
+    assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(m3)) == 4 * 128 * 3 * (512 * 4 + 8)
     small = _shape(batch=1, n_q_heads=16, n_kv_heads=1, n_groups=16, head_dim=576, v_dim=512, max_len=4096,
                    budget=512, scale=192 ** -0.5)
     assert lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(small)) == 16 * 2 * (512 * 4 + 8)   # 256-row splits
