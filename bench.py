@@ -733,7 +733,7 @@ def bench_mla(args, p, torch, W):
 
     # instrumented pass: K more steps launched back to back (no synchronize between steps), events
     # around every stage call and at the attention's merge; counts summed on the device
-    names = ("absorb", "scores", "topk", "attn", "out_proj", "end")
+    names = ("absorb", "scores", "topk", "attn", "end")       # "attn": attention + output projection
     timers = []
     moved = torch.zeros((K_, 3), dtype=torch.int64, device="cuda")
     mark = torch.zeros((p.batch, p.max_len + 1), dtype=torch.int32, device="cuda")
@@ -783,6 +783,9 @@ def bench_mla(args, p, torch, W):
             dec.ws_attn, stream=st), R),
         "out_proj": iso(torch, lambda st: api.spc_mla_out_proj(s, p.nope_dim, uv()[0], dec.o_lat, 0, dec.out,
                                                                stream=st), R),
+        "attn_out_proj": iso(torch, lambda st: api.spc_mla_attn_out_proj(
+            s, dec.q_abs, dec.q_l, lat()[0], dec.lat_l, dec.sel_idx, dec.sel_count, api.SPC_ROWS_GATHER, 0,
+            p.nope_dim, uv()[0], dec.o_lat, dec.out, ws=dec.ws_attn, stream=st), R),
     }
     B, H, L, D = p.batch, p.n_q_heads, p.max_len, p.head_dim
     n_valid = float(np.mean(w.lengths[Wm + K_:total].sum(axis=1)))

@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-#define SPC_ABI_VERSION 2
+/* 3: adds spc_mla_attn_out_proj */
+#define SPC_ABI_VERSION 3
 
 typedef enum spc_status {
   SPC_OK = 0,
@@ -440,6 +441,26 @@ int spc_mla_absorb_q(const spc_shape* s, int32_t nope_dim, const void* w_uk, con
  *   out    device float32 [B][H][dv] out */
 int spc_mla_out_proj(const spc_shape* s, int32_t dv, const void* w_uv, const float* o_lat, int32_t layer,
                      float* out, void* stream);
+
+/* spc_mla_attn_out_proj: stage 4 of one MLA layer and the output projection in one call,
+ *   out[b][h][0:dv) = W_UV[h] o[b][h],  o = the latent attention of spc_sparse_decode_attn
+ * over the layer range [layer, layer + 1) with the same q, kv, rows and workspace arguments
+ * (the absorbed form of the per-head output up-projection, SpeContext blog section 5 and paper
+ * summary section 4.3, MLA bullet, as for spc_mla_out_proj).  Where each head's budget fits one
+ * attention split (budget <= 2048 rows, batch x n_layers x n_q_heads >= 512) it is one launch, each
+ * workgroup attending one head and projecting its output, and o_lat is not written; otherwise
+ * spc_sparse_decode_attn writes o into o_lat and spc_mla_out_proj projects it, on the same stream.
+ *   s, q, q_l, kv, kv_l, rows, row_count, rows_mode, ws, ws_bytes  as spc_sparse_decode_attn
+ *          (an MLA shape: head_dim 576, v_dim 512, n_kv_heads 1, n_groups = n_q_heads, bf16)
+ *   layer  the layer, in [0, n_layers)
+ *   dv     output rows per head, in [1, 4096];  w_uv  device bf16 [H][dv][512]
+ *   o_lat  device float32 [B][n_layers][H][512] (the second path's attention output)
+ *   out    device float32 [B][H][dv] out
+ * Errors: those of spc_sparse_decode_attn and spc_mla_out_proj, checked before any launch. */
+int spc_mla_attn_out_proj(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                          const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
+                          int32_t layer, int32_t dv, const void* w_uv, float* o_lat, float* out, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * MLA in the literal form (SpeContext blog section 5, last paragraph; paper summary

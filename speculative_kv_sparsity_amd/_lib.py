@@ -93,6 +93,8 @@ SIGNATURES = {
     "spc_mla_expand": (_I, [ctypes.POINTER(SpcShape), _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "spc_mla_absorb_q": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P, _P, _P]),
     "spc_mla_out_proj": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _I32, _P, _P]),
+    "spc_mla_attn_out_proj": (_I, [ctypes.POINTER(SpcShape), _P, ctypes.POINTER(SpcQLayout), _P,
+                                   ctypes.POINTER(SpcKvLayout), _P, _P, _I, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "spc_elastic_plan_lag1": (_I, [ctypes.POINTER(SpcShape), _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "spc_offload_thresholds": (_I, [ctypes.POINTER(SpcMemModel), ctypes.POINTER(ctypes.c_int32)]),
     "spc_retrieval_head_qk": (_I, [ctypes.POINTER(SpcShape), _I32, ctypes.c_int64, ctypes.POINTER(SpcRope),

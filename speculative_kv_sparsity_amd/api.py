@@ -256,6 +256,20 @@ def spc_mla_out_proj(shape: SpcShape, dv: int, w_uv, o_lat, layer: int, out, str
                                     _stream(stream)))
 
 
+def spc_mla_attn_out_proj(shape: SpcShape, q, q_l: SpcQLayout, kv, kv_l: SpcKvLayout, rows, row_count,
+                          rows_mode: int, layer: int, dv: int, w_uv, o_lat, out, ws=None, stream=None) -> None:
+    for t, n in ((q, "q"), (kv, "kv"), (rows, "rows")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a device tensor")
+    for t, n in ((w_uv, "w_uv"), (o_lat, "o_lat"), (out, "out")):
+        _dev(t, n)
+    ws = _workspace(SPC_CALL_ATTN, shape, out.device) if ws is None else ws
+    _check(L.lib().spc_mla_attn_out_proj(
+        ctypes.byref(shape), _ptr(q), ctypes.byref(q_l), _ptr(kv), ctypes.byref(kv_l), _ptr(rows), _ptr(row_count),
+        int(rows_mode), int(layer), int(dv), _ptr(w_uv), _ptr(o_lat), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def rope_params(base: float, factor: float = 1.0, orig_max_pos: int = 2048, beta_fast: float = 32.0,
                 beta_slow: float = 1.0) -> SpcRope:
     return SpcRope(float(base), float(factor), int(orig_max_pos), float(beta_fast), float(beta_slow))

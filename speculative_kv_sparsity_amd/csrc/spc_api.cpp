@@ -491,6 +491,24 @@ int spc_mla_out_proj(const spc_shape* s, int32_t dv, const void* w_uv, const flo
   return e == hipSuccess ? ok() : hip_fail(e, "MLA output projection launch");
 }
 
+int spc_mla_attn_out_proj(const spc_shape* s, const void* q, const spc_q_layout* q_l, const void* kv,
+                          const spc_kv_layout* kv_l, const int32_t* rows, const int32_t* row_count, int rows_mode,
+                          int32_t layer, int32_t dv, const void* w_uv, float* o_lat, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (int e = check_mla(s)) return e;
+  if (layer < 0 || layer >= s->n_layers) return fail(SPC_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, s->n_layers);
+  if (int e = check_attn(s, q, q_l, kv, kv_l, rows, row_count, rows_mode, layer, layer + 1, ws, ws_bytes,
+                         spc::attn_ws_bytes(*s)))
+    return e;
+  if (!w_uv || !o_lat || !out) return fail(SPC_ERR_INVALID_ARG, "NULL argument");
+  if (dv < 1 || dv > 4096) return fail(SPC_ERR_INVALID_ARG, "dv %d outside [1, 4096]", dv);
+  if (!aligned16(w_uv) || !aligned16(o_lat) || !aligned16(out))
+    return fail(SPC_ERR_INVALID_ARG, "w_uv, o_lat and out must be 16-byte aligned");
+  const hipError_t e = spc::launch_mla_attn_out_proj(*s, q, *q_l, kv, *kv_l, rows, row_count, rows_mode, layer, dv,
+                                                     w_uv, o_lat, out, ws, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "MLA attention and output projection launch");
+}
+
 int spc_retrieval_head_qk(const spc_shape* s, int32_t hidden, int64_t vocab, const spc_rope* rope, float eps,
                           const int32_t* tokens, const int32_t* positions, const void* emb, const void* gamma,
                           const void* wq, const void* wk, void* q_out, void* dlm_k, void* ws, size_t ws_bytes,

@@ -287,13 +287,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 //
 // With fewer than 8 such groups (n_glob = 1, 2 or 4: `parts` = 8 / n_glob), each group is shared by
 // `parts` XCDs, each taking a contiguous range of its heads, so that no XCD idles.  FIN: the head
-// has one split, and the workgroup writes the normalised output itself (no merge launch).
-template <int D, int DV, int T, bool FIN>
+// has one split, and the workgroup writes the normalised output itself (no merge launch); PROJ (with
+// FIN): it writes the head's output projection instead, W_UV[head] (bf16 [dv][DV]) times the
+// normalised output held in LDS, two threads per output row.
+template <int D, int DV, int T, bool FIN, bool PROJ>
 __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
     const char* __restrict__ q, QL ql, const char* __restrict__ kv, KL kl, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ row_count, int mode, int Hq, int Hkv, int n_groups, int K, int layer_begin,
     int n_lay, int nsplit, int n_glob, int parts, int max_rows, float scale, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, float* __restrict__ out, int n_layers) {
+    float2* __restrict__ part_ml, float* __restrict__ out, int n_layers, const uint16_t* __restrict__ w_uv, int dv) {
+  static_assert(FIN || !PROJ, "the projection needs the whole output of the head");
   constexpr int EB = 2;
   constexpr int CPLK = D * EB / 16 / 8;              // 16-byte chunks per lane of a row (9)
   constexpr int CPLV = DV * EB / 16 / 8;             // of them in the value part (8)
@@ -412,6 +415,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
         a1 = dot2_bf16(ph, wlo, dot2_bf16(ph, whi, a1));
       }
   }
+  // PROJ: this thread's first output row of W_UV[head] (half of it), requested now so that the
+  // loads overlap the merge below; they do not depend on the attention
+  constexpr int kHalfChunks = DV / 2 / 8;            // 16-byte chunks of bf16 weights per half row
+  constexpr int kPre = kHalfChunks / 2;              // of them requested before the merge (registers)
+  const int half = tid & 1;
+  const char* wrow = reinterpret_cast<const char*>(w_uv + ((size_t)head * dv + (tid >> 1)) * DV + half * (DV / 2));
+  Vec16 wpre[PROJ ? kHalfChunks : 1];
+  if (PROJ && (tid >> 1) < dv) {
+#pragma unroll
+    for (int c = 0; c < (PROJ ? kPre : 0); ++c) wpre[c] = ld16(wrow + 16 * c);
+  }
   // wave totals (the 8 lanes that share p hold different rows), then the cross-wave merge
   const float lw = sum_across_rows8(lsum);
 #pragma unroll
@@ -435,8 +449,52 @@ __global__ __launch_bounds__(kThreads) void attn_split_latent_kernel(
   if (FIN) {
     // the head's only split: out = sum / L (no rows: zeros), as the merge would write it
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    float* o = out + (((size_t)b * n_layers + layer) * Hq + head) * DV;
-    for (int d = tid; d < DV; d += kThreads) o[d] = (red[0][d] + red[1][d] + red[2][d] + red[3][d]) * inv;
+    if (!PROJ) {
+      float* o = out + (((size_t)b * n_layers + layer) * Hq + head) * DV;
+      for (int d = tid; d < DV; d += kThreads) o[d] = (red[0][d] + red[1][d] + red[2][d] + red[3][d]) * inv;
+      return;
+    }
+    // out[b][head][0:dv) = W_UV[head] o: o in red[0] (each dim owned by one thread), then thread
+    // (r, half) takes the dims [half DV/2, (half + 1) DV/2) of output row r (its first row's weights
+    // requested before the barrier, half of them before the merge)
+    if ((tid >> 1) < dv) {
+#pragma unroll
+      for (int c = kPre; c < kHalfChunks; ++c) wpre[c] = ld16(wrow + 16 * c);
+    }
+    for (int d = tid; d < DV; d += kThreads) red[0][d] = (red[0][d] + red[1][d] + red[2][d] + red[3][d]) * inv;
+    __syncthreads();
+    const float* oh = &red[0][half * (DV / 2)];
+    auto dot_half = [&](const Vec16* w, int nchunk, int c0, float acc) {
+#pragma unroll
+      for (int c = 0; c < nchunk; ++c) {
+        const float4 o0 = *reinterpret_cast<const float4*>(oh + 8 * (c0 + c));
+        const float4 o1 = *reinterpret_cast<const float4*>(oh + 8 * (c0 + c) + 4);
+        acc = fmaf(bf_lo(w[c].w[0]), o0.x, acc); acc = fmaf(bf_hi(w[c].w[0]), o0.y, acc);
+        acc = fmaf(bf_lo(w[c].w[1]), o0.z, acc); acc = fmaf(bf_hi(w[c].w[1]), o0.w, acc);
+        acc = fmaf(bf_lo(w[c].w[2]), o1.x, acc); acc = fmaf(bf_hi(w[c].w[2]), o1.y, acc);
+        acc = fmaf(bf_lo(w[c].w[3]), o1.z, acc); acc = fmaf(bf_hi(w[c].w[3]), o1.w, acc);
+      }
+      return acc;
+    };
+    if ((tid >> 1) < dv) {                             // the first row: weights already requested
+      float a = dot_half(wpre, kHalfChunks, 0, 0.f);
+      a += __shfl_xor(a, 1, kWave);
+      if (half == 0) out[((size_t)b * Hq + head) * dv + (tid >> 1)] = a;
+    }
+    for (int r = (tid >> 1) + kThreads / 2; r < dv; r += kThreads / 2) {   // rows past the first 128
+      const char* wr = reinterpret_cast<const char*>(w_uv + ((size_t)head * dv + r) * DV + half * (DV / 2));
+      constexpr int kGroup = 8;
+      float a = 0.f;
+#pragma unroll 1
+      for (int c0 = 0; c0 < kHalfChunks; c0 += kGroup) {
+        Vec16 w[kGroup];
+#pragma unroll
+        for (int c = 0; c < kGroup; ++c) w[c] = ld16(wr + 16 * (c0 + c));
+        a = dot_half(w, kGroup, c0, a);
+      }
+      a += __shfl_xor(a, 1, kWave);
+      if (half == 0) out[((size_t)b * Hq + head) * dv + r] = a;
+    }
     return;
   }
   const size_t pbase = (size_t)inst * nsplit + split;
@@ -669,9 +727,11 @@ namespace {
 
 // fin_out: the attention output, written by the split kernel itself where the shape has one split per
 // head (MLA latent rows; the caller then launches no merge), else NULL
+// proj_w (with fin_out): W_UV, and fin_out receives the output projection [B][H][proj_dv] instead
 hipError_t launch_partial(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
                           const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
-                          int layer_begin, int layer_end, void* ws, float* fin_out, hipStream_t st) {
+                          int layer_begin, int layer_end, void* ws, float* fin_out, hipStream_t st,
+                          const uint16_t* proj_w = nullptr, int proj_dv = 0) {
   const int eb = s.dtype == SPC_BF16 ? 2 : 4;
   const AttnGeom g = attn_geom(s, layer_begin, layer_end, ws);
   SplitArgs a;
@@ -710,20 +770,23 @@ hipError_t launch_partial(const spc_shape& s, const void* q, const spc_q_layout&
     const dim3 lgrid((unsigned)(parts > 1 ? 8 * ((s.n_groups + parts - 1) / parts)
                                           : 8 * ((n_glob + 7) / 8) * s.n_groups));
     const int tiles = latent_tiles(s);
-#define SPC_LATENT(TT, FF)                                                                                    \
-  attn_split_latent_kernel<576, 512, TT, FF><<<lgrid, kThreads, 0, st>>>(                                    \
+#define SPC_LATENT(TT, FF, PP)                                                                                \
+  attn_split_latent_kernel<576, 512, TT, FF, PP><<<lgrid, kThreads, 0, st>>>(                                \
       a.q, a.ql, a.kv, a.kl, a.rows, a.row_count, a.mode, s.n_q_heads, s.n_kv_heads, s.n_groups, s.budget,     \
       a.layer_begin, a.n_lay, a.nsplit, n_glob, parts, a.max_rows, s.scale, a.part_o, a.part_ml, fin_out,      \
-      s.n_layers)
+      s.n_layers, proj_w, proj_dv)
     if (fin_out && (tiles != kLatentTilesWhole || g.nsplit != 1)) return hipErrorInvalidValue;
-    if (tiles == kLatentTilesWhole && fin_out)
-      SPC_LATENT(kLatentTilesWhole, true);
+    if (proj_w && (!fin_out || g.n_lay != 1)) return hipErrorInvalidValue;
+    if (tiles == kLatentTilesWhole && proj_w)
+      SPC_LATENT(kLatentTilesWhole, true, true);
+    else if (tiles == kLatentTilesWhole && fin_out)
+      SPC_LATENT(kLatentTilesWhole, true, false);
     else if (tiles == kLatentTilesWhole)
-      SPC_LATENT(kLatentTilesWhole, false);
+      SPC_LATENT(kLatentTilesWhole, false, false);
     else if (tiles == kLatentTilesLarge)
-      SPC_LATENT(kLatentTilesLarge, false);
+      SPC_LATENT(kLatentTilesLarge, false, false);
     else
-      SPC_LATENT(kLatentTilesSmall, false);
+      SPC_LATENT(kLatentTilesSmall, false, false);
 #undef SPC_LATENT
     e = hipGetLastError();
   }
@@ -760,11 +823,28 @@ hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end,
   return hipGetLastError();
 }
 
+bool latent_one_split(const spc_shape& s) {
+  return s.head_dim == 576 && head_chunk(s) == 1 && latent_tiles(s) == kLatentTilesWhole;
+}
+
+hipError_t launch_mla_attn_out_proj(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
+                                    const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count,
+                                    int mode, int layer, int dv, const void* w_uv, float* o_lat, float* out, void* ws,
+                                    hipStream_t st) {
+  if (latent_one_split(s))                      // one launch: attention and projection per head
+    return launch_partial(s, q, qlay, kv, klay, rows, row_count, mode, layer, layer + 1, ws, out, st,
+                          static_cast<const uint16_t*>(w_uv), dv);
+  const hipError_t e = launch_attn(s, q, qlay, kv, klay, rows, row_count, mode, layer, layer + 1, o_lat, ws, st);
+  if (e != hipSuccess) return e;
+  return launch_mla_out_proj(s.batch, s.n_q_heads, dv, w_uv, o_lat + (size_t)layer * s.n_q_heads * kMlaLatent,
+                             (int64_t)s.n_layers * s.n_q_heads * kMlaLatent, out, st);
+}
+
 hipError_t launch_attn(const spc_shape& s, const void* q, const spc_q_layout& qlay, const void* kv,
                        const spc_kv_layout& klay, const int32_t* rows, const int32_t* row_count, int mode,
                        int layer_begin, int layer_end, float* out, void* ws, hipStream_t st) {
   // MLA latent rows with one split per head: the split kernel writes the output, no merge
-  const bool fin = s.head_dim == 576 && head_chunk(s) == 1 && latent_tiles(s) == kLatentTilesWhole;
+  const bool fin = latent_one_split(s);
   const hipError_t e = launch_partial(s, q, qlay, kv, klay, rows, row_count, mode, layer_begin, layer_end, ws,
                                       fin ? out : nullptr, st);
   if (e != hipSuccess || fin) return e;

@@ -107,5 +107,13 @@ hipError_t launch_attn_partial(const spc_shape& s, const void* q, const spc_q_la
 size_t attn_ws_bytes_layers(const spc_shape& s, int n_lay);   // the partials of n_lay layers of one call
 hipError_t launch_attn_merge(const spc_shape& s, int layer_begin, int layer_end, const void* ws, float* out,
                              hipStream_t st);
+// MLA: the latent attention of one layer and its output projection W_UV[h] o[h] -> out [B][H][dv]; one
+// launch where each head's budget fits one split (o_lat not written), else the attention into o_lat
+// and launch_mla_out_proj
+bool latent_one_split(const spc_shape& s);
+hipError_t launch_mla_attn_out_proj(const spc_shape& s, const void* q, const spc_q_layout& ql, const void* kv,
+                                    const spc_kv_layout& kl, const int32_t* rows, const int32_t* row_count,
+                                    int mode, int layer, int dv, const void* w_uv, float* o_lat, float* out, void* ws,
+                                    hipStream_t st);
 
 }  // namespace spc

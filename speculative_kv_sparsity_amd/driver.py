@@ -435,10 +435,10 @@ class MlaDecoder:
         api.spc_group_max_topk_plan_logits(s, self.logits, None, lengths, self.sel_idx, self.sel_count,
                                            self.slot_pos, self.resident_bm, self.load_pos, self.load_slot,
                                            self.load_count, ws=self.ws_topk, stream=st)
-        mark("attn", st)
-        self.attend()
-        mark("out_proj", st)
-        api.spc_mla_out_proj(s, self.p.nope_dim, self.w_uv, self.o_lat, 0, self.out, stream=st)
+        mark("attn", st)                 # attention and output projection (one launch where it fits)
+        api.spc_mla_attn_out_proj(s, self.q_abs, self.q_l, self.latent, self.lat_l, self.sel_idx, self.sel_count,
+                                  api.SPC_ROWS_GATHER, 0, self.p.nope_dim, self.w_uv, self.o_lat, self.out,
+                                  ws=self.ws_attn, stream=st)
         mark("end", st)
 
     def capture(self) -> None:

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     lib = L.lib()
-    assert lib.spc_abi_version() == 2
+    assert lib.spc_abi_version() == 3
     assert lib.spc_status_string(0) == b"ok"
     assert b"workspace" in lib.spc_status_string(L.SPC_ERR_WORKSPACE)
 
@@ -374,3 +374,31 @@ def test_group_and_kv_head_counts():
     st = lib.spc_elastic_update(ctypes.byref(_shape(n_groups=1)), None, None, None, None, p, p, p, p,
                                 ctypes.byref(lay), p, ctypes.byref(lay), 0, 1, L.SPC_COPY, None, None)
     assert st == L.SPC_ERR_NOT_MAPPED
+
+
+def test_mla_attention_with_projection_validation():
+    """spc_mla_attn_out_proj rejects what it does not support before launching (fake pointers unused)."""
+    lib = L.lib()
+    mla = _shape(batch=4, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                 budget=2048, scale=192 ** -0.5)
+    p = ctypes.c_void_p(256)
+    ql = L.SpcQLayout(128 * 576, 0, 576)
+    kl = L.SpcKvLayout(32768 * 576, 0, 0, 576, 0)
+    ws_ok = lib.spc_workspace_size(L.SPC_CALL_ATTN, ctypes.byref(mla))
+
+    def call(shape=mla, q=p, rows=p, layer=0, dv=128, w_uv=p, o_lat=p, out=p, ws_bytes=ws_ok, kvl=kl):
+        return lib.spc_mla_attn_out_proj(ctypes.byref(shape), q, ctypes.byref(ql), p, ctypes.byref(kvl), rows, p,
+                                         L.SPC_ROWS_GATHER, layer, dv, w_uv, o_lat, out, p, ws_bytes, None)
+
+    assert call(q=None) == L.SPC_ERR_INVALID_ARG
+    assert call(w_uv=None) == L.SPC_ERR_INVALID_ARG and call(o_lat=None) == L.SPC_ERR_INVALID_ARG
+    assert call(out=None) == L.SPC_ERR_INVALID_ARG
+    assert call(layer=1) == L.SPC_ERR_INVALID_ARG and call(layer=-1) == L.SPC_ERR_INVALID_ARG
+    assert call(dv=0) == L.SPC_ERR_INVALID_ARG and call(dv=4097) == L.SPC_ERR_INVALID_ARG
+    assert call(w_uv=ctypes.c_void_p(264)) == L.SPC_ERR_INVALID_ARG                   # alignment
+    assert call(ws_bytes=ws_ok - 1) == L.SPC_ERR_WORKSPACE
+    assert call(kvl=L.SpcKvLayout(32768 * 576, 0, 0, 576, 512)) == L.SPC_ERR_UNSUPPORTED   # V inside the row
+    assert call(shape=_shape()) == L.SPC_ERR_UNSUPPORTED                              # a GQA shape
+    big = _shape(batch=17, n_q_heads=128, n_kv_heads=1, n_groups=128, head_dim=576, v_dim=512, max_len=32768,
+                 budget=2048)
+    assert call(shape=big) == L.SPC_ERR_UNSUPPORTED

@@ -1,5 +1,7 @@
 """MLA variant: head-level retrieval over the latent cache, per-head Top-K, attention over the
 selected latent rows, against the oracle's literal expansion of only the selected rows."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -281,4 +283,58 @@ def test_latent_attention_matches_oracle(name, B, H, L, K):
             if n == 0:
                 assert np.all(got[b, h] == 0), (b, h)
             err = max(err, float(np.max(np.abs(got[b, h] - ref))))
+    assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, err
+
+
+# The attention of one MLA layer with its output projection in one call, against the two calls it
+# replaces (spc_sparse_decode_attn, then spc_mla_out_proj) and against the oracle on sampled heads.
+#   one_launch*: one split per head (budget <= 2048, >= 512 heads): attention and projection in
+#     one launch, o_lat not written; 128 and 100 output rows per head
+#   two_calls:  few heads: the attention into o_lat and the projection kernel, the same bits
+PROJ_CASES = [("one_launch", 4, 128, 4096, 2048, 128), ("one_launch_dv100", 4, 128, 3000, 1024, 100),
+              ("two_calls", 2, 16, 1500, 700, 128)]
+
+
+@pytest.mark.parametrize("name,B,H,L,K,dv", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_attention_with_projection_equals_the_two_calls(name, B, H, L, K, dv):
+    p = W.PRESETS["mla_32k"]
+    D, DV = p.head_dim, p.v_dim
+    rng = np.random.default_rng(21)
+    g = torch.Generator().manual_seed(22)
+    latent = torch.randn((B, L, D), generator=g).to(torch.bfloat16)
+    q = (0.6 * torch.randn((B, H, D), generator=g)).float()
+    w_uv = (torch.randn((H, dv, DV), generator=g) / math.sqrt(DV)).to(torch.bfloat16)
+    counts = rng.integers(0, K + 1, size=(B, H)).astype(np.int32)
+    counts[0, 0], counts[-1, -1], counts[0, -1] = 0, K, 1
+    rows = np.full((B, H, K), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            n = int(counts[b, h])
+            rows[b, h, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    shape = api.make_shape(B, H, 1, H, D, DV, L, K, 1, "bf16", p.scale)
+    args = (shape, q.cuda(), api.q_layout(H * D, 0, D), latent.cuda(), api.SpcKvLayout(L * D, 0, 0, D, 0),
+            torch.from_numpy(rows).cuda(), torch.from_numpy(counts).cuda(), api.SPC_ROWS_GATHER)
+    wd = w_uv.cuda()
+    nan = dict(dtype=torch.float32, device="cuda")
+    o_two, out_two = torch.full((B, 1, H, DV), float("nan"), **nan), torch.full((B, H, dv), float("nan"), **nan)
+    api.spc_sparse_decode_attn(*args, 0, 1, o_two)
+    api.spc_mla_out_proj(shape, dv, wd, o_two, 0, out_two)
+    o_one, out_one = torch.full((B, 1, H, DV), float("nan"), **nan), torch.full((B, H, dv), float("nan"), **nan)
+    api.spc_mla_attn_out_proj(*args, 0, dv, wd, o_one, out_one)
+    torch.cuda.synchronize()
+    a, z = out_one.cpu().numpy(), out_two.cpu().numpy()
+    if name.startswith("two"):
+        np.testing.assert_array_equal(a, z)
+        np.testing.assert_array_equal(o_one.cpu().numpy(), o_two.cpu().numpy())
+    else:
+        # the same float32 output of each head, projected in another summation order
+        np.testing.assert_allclose(a, z, rtol=1e-5, atol=1e-6)
+        assert torch.isnan(o_one).all()                     # one launch: o_lat is not written
+    assert np.all(a[0, 0] == 0)                             # a head without rows
+    lat64, q64, w64 = _bf(latent), q.numpy().astype(np.float64), _bf(w_uv)
+    err = 0.0
+    for b, h in [(0, 1), (0, H - 1), (B - 1, H // 2), (B - 1, H - 1)]:
+        n = int(counts[b, h])
+        ref = w64[h] @ O.sparse_attention(q64[b, h], lat64[b], lat64[b][:, :DV], rows[b, h, :n], p.scale)
+        err = max(err, float(np.max(np.abs(a[b, h].astype(np.float64) - ref))))
     assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, err
