@@ -291,18 +291,21 @@ def test_latent_attention_matches_oracle(name, B, H, L, K):
 #   one_launch*: one split per head (budget <= 2048, >= 512 heads): attention and projection in
 #     one launch, o_lat not written; 128 and 100 output rows per head
 #   two_calls:  few heads: the attention into o_lat and the projection kernel, the same bits
-PROJ_CASES = [("one_launch", 4, 128, 4096, 2048, 128), ("one_launch_dv100", 4, 128, 3000, 1024, 100),
-              ("two_calls", 2, 16, 1500, 700, 128)]
+#   one_launch_layer1: two layers (the second attended), 2 sequences x 2 layers x 128 heads = 512
+PROJ_CASES = [("one_launch", 4, 128, 4096, 2048, 128, 1), ("one_launch_dv100", 4, 128, 3000, 1024, 100, 1),
+              ("one_launch_layer1", 2, 128, 2500, 2048, 128, 2), ("two_calls", 2, 16, 1500, 700, 128, 1)]
 
 
-@pytest.mark.parametrize("name,B,H,L,K,dv", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
-def test_attention_with_projection_equals_the_two_calls(name, B, H, L, K, dv):
+@pytest.mark.parametrize("name,B,H,L,K,dv,NL", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_attention_with_projection_equals_the_two_calls(name, B, H, L, K, dv, NL):
     p = W.PRESETS["mla_32k"]
     D, DV = p.head_dim, p.v_dim
     rng = np.random.default_rng(21)
     g = torch.Generator().manual_seed(22)
-    latent = torch.randn((B, L, D), generator=g).to(torch.bfloat16)
-    q = (0.6 * torch.randn((B, H, D), generator=g)).float()
+    # [B][NL][L][D] latent rows and [B][NL][H][D] queries; the attended layer is the last one
+    latent = torch.randn((B, NL, L, D), generator=g).to(torch.bfloat16)
+    q = (0.6 * torch.randn((B, NL, H, D), generator=g)).float()
+    layer = NL - 1
     w_uv = (torch.randn((H, dv, DV), generator=g) / math.sqrt(DV)).to(torch.bfloat16)
     counts = rng.integers(0, K + 1, size=(B, H)).astype(np.int32)
     counts[0, 0], counts[-1, -1], counts[0, -1] = 0, K, 1
@@ -311,16 +314,17 @@ def test_attention_with_projection_equals_the_two_calls(name, B, H, L, K, dv):
         for h in range(H):
             n = int(counts[b, h])
             rows[b, h, :n] = np.sort(rng.choice(L, size=n, replace=False))
-    shape = api.make_shape(B, H, 1, H, D, DV, L, K, 1, "bf16", p.scale)
-    args = (shape, q.cuda(), api.q_layout(H * D, 0, D), latent.cuda(), api.SpcKvLayout(L * D, 0, 0, D, 0),
-            torch.from_numpy(rows).cuda(), torch.from_numpy(counts).cuda(), api.SPC_ROWS_GATHER)
+    shape = api.make_shape(B, H, 1, H, D, DV, L, K, NL, "bf16", p.scale)
+    args = (shape, q.cuda(), api.q_layout(NL * H * D, H * D, D), latent.cuda(),
+            api.SpcKvLayout(NL * L * D, L * D, 0, D, 0), torch.from_numpy(rows).cuda(),
+            torch.from_numpy(counts).cuda(), api.SPC_ROWS_GATHER)
     wd = w_uv.cuda()
     nan = dict(dtype=torch.float32, device="cuda")
-    o_two, out_two = torch.full((B, 1, H, DV), float("nan"), **nan), torch.full((B, H, dv), float("nan"), **nan)
-    api.spc_sparse_decode_attn(*args, 0, 1, o_two)
-    api.spc_mla_out_proj(shape, dv, wd, o_two, 0, out_two)
-    o_one, out_one = torch.full((B, 1, H, DV), float("nan"), **nan), torch.full((B, H, dv), float("nan"), **nan)
-    api.spc_mla_attn_out_proj(*args, 0, dv, wd, o_one, out_one)
+    o_two, out_two = torch.full((B, NL, H, DV), float("nan"), **nan), torch.full((B, H, dv), float("nan"), **nan)
+    api.spc_sparse_decode_attn(*args, layer, layer + 1, o_two)
+    api.spc_mla_out_proj(shape, dv, wd, o_two, layer, out_two)
+    o_one, out_one = torch.full((B, NL, H, DV), float("nan"), **nan), torch.full((B, H, dv), float("nan"), **nan)
+    api.spc_mla_attn_out_proj(*args, layer, dv, wd, o_one, out_one)
     torch.cuda.synchronize()
     a, z = out_one.cpu().numpy(), out_two.cpu().numpy()
     if name.startswith("two"):
@@ -335,6 +339,7 @@ def test_attention_with_projection_equals_the_two_calls(name, B, H, L, K, dv):
     err = 0.0
     for b, h in [(0, 1), (0, H - 1), (B - 1, H // 2), (B - 1, H - 1)]:
         n = int(counts[b, h])
-        ref = w64[h] @ O.sparse_attention(q64[b, h], lat64[b], lat64[b][:, :DV], rows[b, h, :n], p.scale)
+        lb = lat64[b, layer]
+        ref = w64[h] @ O.sparse_attention(q64[b, layer, h], lb, lb[:, :DV], rows[b, h, :n], p.scale)
         err = max(err, float(np.max(np.abs(a[b, h].astype(np.float64) - ref))))
     assert err <= ATTN_MAX_ABS and err <= ATTN_DERIVED, err
