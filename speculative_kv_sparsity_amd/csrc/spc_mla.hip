@@ -36,10 +36,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMlaD = kMlaLatent + kMlaRope;      // 576 scored dims
 constexpr int kKSteps = kMlaD / 32;                // MFMA k-steps of 32
 constexpr int kSub = 64;                           // latent rows per LDS buffer: four 16-row blocks
-constexpr int kLdsRow = kMlaD + 8;                 // padded row (elements): spreads rows over banks
+// padded row (elements): two 16-byte pad chunks, so that the 16 rows of a B-fragment read fall on
+// distinct banks (with one pad chunk the reads conflicted: 38% of the LDS's busy cycles)
+constexpr int kLdsRow = kMlaD + 16;
 constexpr int kScoreThreads = 512;                 // 8 waves x 16 heads
 constexpr int kScoreHeads = 8 * 16;                // heads per workgroup
-constexpr int kScoreRowChunks = kLdsRow / 8;       // 16-byte chunks per padded LDS row (one pad chunk)
+constexpr int kScoreRowChunks = kLdsRow / 8;       // 16-byte chunks per padded LDS row (two pad chunks)
 constexpr int kScoreChunks = kSub * kScoreRowChunks;
 constexpr int kScoreLoads = (kScoreChunks + kWave - 1) / kWave;   // wave loads of 64 chunks per sub-tile
 constexpr int kScoreBuf = kScoreLoads * kWave * 8;   // LDS elements of a sub-tile buffer
@@ -141,7 +143,7 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
 // query of its 16 heads as bf16 hi + lo MFMA A fragments in registers for the whole tile (144
 // VGPRs: MFMA A operands live in VGPRs, and 32 heads would not fit).  The tile goes 64 rows at a
 // time from memory straight into LDS (global_load_lds_dwordx4: lane l of a wave load lands 16 l
-// bytes past the wave's LDS base; rows padded by one 16-byte chunk), double-buffered: the next
+// bytes past the wave's LDS base; rows padded by two 16-byte chunks), double-buffered: the next
 // sub-tile is in flight while the MFMAs read the current one, and one barrier per sub-tile
 // separates the two.  A sub-tile's logits are stored at the start of the next, so that barrier
 // waits only for the next sub-tile's loads.
