@@ -88,9 +88,10 @@ __device__ __forceinline__ void plan_bitmap(const int32_t* S, int c, int32_t* __
 // selw[w] = word t WPT + w of the selection's bitmap (bit i set iff position 32 (t WPT + w) + i is
 // selected, so S is the set bits in ascending order), oldw[w], the same words of the resident bitmap
 // before the step, and pos[u], the slot map entries of its slots [t*Cx, t*Cx + Cx) (Cx = ceil(K /
-// 1024) <= CPT; -1 beyond K).  Requires bm_words <= WPT * kPlanThreads.  sL, sF: K words of LDS each,
-// sB: bm_words words.  The results are those of plan_bitmap on the same selection, entry for entry.
-template <int CPT, int WPT = 1>
+// NT) <= CPT; -1 beyond K), for a workgroup of NT threads.  Requires bm_words <= WPT * NT.  sL, sF: K
+// words of LDS each, sB: bm_words words.  The results are those of plan_bitmap on the same selection,
+// entry for entry.
+template <int CPT, int WPT = 1, int NT = kPlanThreads>
 __device__ __forceinline__ void plan_words(const uint32_t (&selw)[WPT], const uint32_t (&oldw)[WPT],
                                            const int32_t (&pos)[CPT], int32_t* __restrict__ sp,
                                            uint32_t* __restrict__ bm, int32_t* __restrict__ lp,
@@ -99,7 +100,7 @@ __device__ __forceinline__ void plan_words(const uint32_t (&selw)[WPT], const ui
                                            uint32_t* scan_smem) {
   const int tid = threadIdx.x;
   const int32_t pos_end = bm_words * 32;
-  const int Cx = (K + kPlanThreads - 1) / kPlanThreads;
+  const int Cx = (K + NT - 1) / NT;
   const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
 #pragma unroll
   for (int w = 0; w < WPT; ++w)
@@ -129,11 +130,11 @@ __device__ __forceinline__ void plan_words(const uint32_t (&selw)[WPT], const ui
   for (int w = 0; w < WPT; ++w)
     for (uint32_t m = lmask[w]; m; m &= m - 1) sL[lo++] = 32 * (tid * WPT + w) + __ffs(m) - 1;
   __syncthreads();
-  for (int i = tid; i < nf; i += kPlanThreads) sp[sF[i]] = i < nl ? sL[i] : -1;
+  for (int i = tid; i < nf; i += NT) sp[sF[i]] = i < nl ? sL[i] : -1;
 #pragma unroll
   for (int w = 0; w < WPT; ++w)
     if (tid * WPT + w < bm_words) bm[tid * WPT + w] = selw[w];
-  for (int i = tid; i < K; i += kPlanThreads) {
+  for (int i = tid; i < K; i += NT) {
     const bool v = i < nl;
     lp[i] = v ? sL[i] : -1;
     ls[i] = v ? sF[i] : -1;

@@ -409,11 +409,12 @@ struct PlanBufs {
 
 constexpr int kCandList = 3072;      // candidate positions the LDS list holds
 
-// Exclusive scan over the kSelThreads-thread block; `smem` holds 16 words, 16-byte aligned.
+// Exclusive scan over the NT-thread block; `smem` holds NT / 64 words, 16-byte aligned.
 // Ends with a barrier.
+template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t scan_block(uint32_t v, uint32_t* smem, uint32_t& total) {
-  constexpr int kWaves = kSelThreads / kWave;
-  static_assert(kWaves == 16, "four 16-byte reads of wave totals");
+  constexpr int kWaves = NT / kWave;
+  static_assert(kWaves % 4 == 0 && kWaves <= 16, "16-byte reads of wave totals");
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == kWave - 1) smem[wid] = incl;
@@ -435,10 +436,11 @@ __device__ __forceinline__ uint32_t scan_block(uint32_t v, uint32_t* smem, uint3
   return base + incl - v;
 }
 
-// find_bin over NB bins with the bin counts held in registers between the scan and the search.
-template <int NB>
+// find_bin over NB bins with the bin counts held in registers between the scan and the search
+// (NT threads).
+template <int NB, int NT = kSelThreads>
 __device__ __forceinline__ void find_bin_fixed(const uint32_t* hist, int need, uint32_t* scan_smem, uint32_t* bcast) {
-  constexpr int BPT = NB >= kSelThreads ? NB / kSelThreads : 1;
+  constexpr int BPT = NB >= NT ? NB / NT : 1;
   const int hi = NB - (int)threadIdx.x * BPT;          // this thread's bins: hi-1, hi-2, ... (top down)
   uint32_t h[BPT];
   uint32_t local = 0u;
@@ -448,7 +450,7 @@ __device__ __forceinline__ void find_bin_fixed(const uint32_t* hist, int need, u
     local += h[i];
   }
   uint32_t total;
-  const uint32_t above = scan_block(local, scan_smem, total);
+  const uint32_t above = scan_block<NT>(local, scan_smem, total);
   if ((int)above < need && need <= (int)(above + local)) {   // exactly one thread
     uint32_t cum = above;
     bool found = false;
@@ -744,32 +746,37 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
 }
 
 // Rows of 32 769 .. 65 536 keys with a budget of at most kRegList: the keys stay in registers, 64 per
-// thread in strided (coalesced) vectors v = tid + 1024 u, and never in LDS.  With one head per group
+// thread in strided (coalesced) vectors v = tid + NT u, and never in LDS.  With one head per group
 // the first digit (12 bits) is counted here from the loaded keys and no keys pass runs; otherwise it
 // comes from the chunk histograms (8 bits).  The sweep marks keys above the threshold's first-digit
 // bin in an LDS bitmap of the row (one atomicOr per 4-key vector: a vector is 4 bits of one word) and
 // lists the candidates' positions; their keys are fetched once more from the row (L2) into the list,
 // so the later digit passes and the final compare run over the list alone.  Thread t then owns bitmap
 // words 2t and 2t + 1 (positions [64t, 64t + 64)) for the ordered output.
+// NT = 512 (rows of up to 32 768 keys, a list of 4096, ~60 KB of LDS): two workgroups share a CU, for
+// many instances of one head each (MLA: 4 x 128), which the LDS-staged select runs one per CU.
 constexpr int kRegKeys = 65536;
 constexpr int kRegList = 8192;
+constexpr int kRegThreadsHalf = 512;
 
-template <bool RAW, int CPT>
-__global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint32_t* __restrict__ keys,
+template <bool RAW, int CPT, int NT = kSelThreads>
+__global__ __launch_bounds__(NT, 4) void topk_select_reg_kernel(const uint32_t* __restrict__ keys,
                                                                       const uint32_t* __restrict__ chist,
                                                                       const int32_t* __restrict__ lengths,
                                                                       int32_t* __restrict__ sel_idx,
                                                                       int32_t* __restrict__ sel_count,
                                                                       int n_groups, int max_len, int budget,
                                                                       int nchunk, PlanBufs pb) {
-  constexpr int kWords = kRegKeys / 32;            // bitmap words of a row: 2 per thread
-  constexpr int kVec = kRegKeys / 4 / kSelThreads;  // 16 vectors = 64 keys per thread
+  constexpr int kKeys = 64 * NT;                   // keys of a row at most
+  constexpr int kList = 8 * NT;                    // candidate list entries
+  constexpr int kWords = kKeys / 32;               // bitmap words of a row: 2 per thread
+  constexpr int kVec = kKeys / 4 / NT;             // 16 vectors = 64 keys per thread
   constexpr int S1 = RAW ? 20 : 24;
   constexpr int S2 = S1 - 12;
-  static_assert(kWords == 2 * kSelThreads && kRegList % kSelThreads == 0, "row and list layout");
+  static_assert(kWords == 2 * NT && kList % NT == 0 && 4096 % NT == 0, "row and list layout");
   __shared__ uint32_t hist[4096];
-  __shared__ int32_t cpos[kRegList];               // candidate positions; later the staged selection
-  __shared__ uint32_t ckey[kRegList];
+  __shared__ int32_t cpos[kList];                  // candidate positions; later the staged selection
+  __shared__ uint32_t ckey[kList];
   __shared__ uint32_t gtbm[kWords], selbm[kWords], tiebm[kWords];
   __shared__ __align__(16) uint32_t scan_smem[16];
   __shared__ uint32_t bcast[2];
@@ -781,7 +788,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   const int K = budget;
   const int tid = threadIdx.x;
   int32_t* out = sel_idx + (size_t)inst * K;
-  // with CPT > 0 the instance's plan follows (2 K <= kRegList: its lists take the key list's LDS)
+  // with CPT > 0 the instance's plan follows (2 K <= kList: its lists take the key list's LDS)
   constexpr bool kPlan = CPT > 0;
   constexpr int kP = kPlan ? CPT : 1;
   uint32_t oldw[2] = {0u, 0u};
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   int32_t* sp = pb.slot_pos + (size_t)inst * K;
   uint32_t* bm = pb.resident_bm + (size_t)inst * pb.bm_words;
   if (kPlan) {
-    const int Cx = (K + kSelThreads - 1) / kSelThreads;
+    const int Cx = (K + NT - 1) / NT;
     const int x0 = min(tid * Cx, K), x1 = min(x0 + Cx, K);
 #pragma unroll
     for (int u = 0; u < kP; ++u) pos[u] = x0 + u < x1 ? sp[x0 + u] : -1;
@@ -799,12 +806,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   }
   auto plan = [&](uint64_t sel64) {
     const uint32_t sw[2] = {(uint32_t)sel64, (uint32_t)(sel64 >> 32)};
-    plan_words<kP, 2>(sw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
+    plan_words<kP, 2, NT>(sw, oldw, pos, sp, bm, pb.load_pos + (size_t)inst * K, pb.load_slot + (size_t)inst * K,
                       pb.load_count + inst, K, pb.bm_words, reinterpret_cast<int32_t*>(ckey),
                       reinterpret_cast<int32_t*>(ckey) + K, gtbm, scan_smem);
   };
   if (n <= K) {
-    for (int i = tid; i < K; i += kSelThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
     if (tid == 0) sel_count[inst] = n;
     if (kPlan) {
       const int r = n - 64 * tid;                  // this thread's positions [64 tid, 64 tid + 64)
@@ -817,8 +824,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   const bool aligned = (max_len & 3) == 0;
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kin), (short)0,
                                                                       aligned ? nv * 16 : n * 4, kBufferRsrcWord3);
-  auto load_vec = [&](int u) -> uint4 {             // keys 4v .. 4v + 3, v = tid + 1024 u (zeros past the row)
-    const int o = (tid + u * kSelThreads) * 16;
+  auto load_vec = [&](int u) -> uint4 {             // keys 4v .. 4v + 3, v = tid + NT u (zeros past the row)
+    const int o = (tid + u * NT) * 16;
     if (aligned) {
       const Vec16 x = ld16_buffer(kr, (uint32_t)o);
       return make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
@@ -831,26 +838,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   uint4 v[kVec];
 #pragma unroll
   for (int u = 0; u < kVec; ++u) v[u] = load_vec(u);
-  const int hbin = tid & (kBins1 - 1), c0 = tid >> 8;
+  // first digit from the chunk histograms (<= kKeys / kKeyChunk chunks): bin tid % 256 of chunks
+  // c0, c0 + NT / 256, ...
+  constexpr int kChunkGroups = NT / kBins1;
+  constexpr int kChunkLoads = kKeys / kKeyChunk / kChunkGroups;
+  const int hbin = tid & (kBins1 - 1), c0 = tid / kBins1;
   uint32_t hs = 0u;
-  if (!RAW) {                                       // first digit: the chunk histograms (<= 64 chunks)
+  if (!RAW) {
     const int nch = (n + kKeyChunk - 1) / kKeyChunk;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(chist + (size_t)inst * nchunk * kBins1), (short)0, nch * kBins1 * 4, kBufferRsrcWord3);
-    uint32_t hv[kRegKeys / kKeyChunk / 4];
+    uint32_t hv[kChunkLoads];
 #pragma unroll
-    for (int u = 0; u < kRegKeys / kKeyChunk / 4; ++u)
-      hv[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, ((c0 + 4 * u) * kBins1 + hbin) * 4, 0, 0);
+    for (int u = 0; u < kChunkLoads; ++u)
+      hv[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, ((c0 + kChunkGroups * u) * kBins1 + hbin) * 4, 0, 0);
 #pragma unroll
-    for (int u = 0; u < kRegKeys / kKeyChunk / 4; ++u) hs += hv[u];
+    for (int u = 0; u < kChunkLoads; ++u) hs += hv[u];
   }
 #pragma unroll
-  for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+  for (int i = 0; i < 4096 / NT; ++i) hist[tid + i * NT] = 0u;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    gtbm[tid + i * kSelThreads] = 0u;
-    selbm[tid + i * kSelThreads] = 0u;
-    tiebm[tid + i * kSelThreads] = 0u;
+    gtbm[tid + i * NT] = 0u;
+    selbm[tid + i * NT] = 0u;
+    tiebm[tid + i * NT] = 0u;
   }
   if (tid == 0) ccount = 0u;
 #pragma unroll
@@ -859,7 +870,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   if (RAW) {
 #pragma unroll
     for (int u = 0; u < kVec; ++u) {
-      const int j = 4 * (tid + u * kSelThreads);
+      const int j = 4 * (tid + u * NT);
       if (j + 3 < n) {
         atomicAdd(&hist[v[u].x >> S1], 1u);
         atomicAdd(&hist[v[u].y >> S1], 1u);
@@ -877,19 +888,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   __syncthreads();
 
   int need = K;
-  find_bin_fixed<(1 << (32 - S1))>(hist, need, scan_smem, bcast);
+  find_bin_fixed<(1 << (32 - S1)), NT>(hist, need, scan_smem, bcast);
   const uint32_t d1 = bcast[0];
   need -= (int)bcast[1];
   const int ncand = (int)hist[d1];
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+  for (int i = 0; i < 4096 / NT; ++i) hist[tid + i * NT] = 0u;
 
   // the sweep: above the bin -> the gt bitmap; in the bin -> a candidate (bit 4u + e of cm)
   uint64_t cm = 0u;
 #pragma unroll
   for (int u = 0; u < kVec; ++u) {
-    const int i4 = tid + u * kSelThreads;
+    const int i4 = tid + u * NT;
     const uint32_t k4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
     uint32_t g4 = 0u, c4 = 0u;
 #pragma unroll
@@ -902,7 +913,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
     if (g4) atomicOr(&gtbm[i4 >> 3], g4 << (4 * (i4 & 7)));
     cm |= (uint64_t)c4 << (4 * u);
   }
-  const bool use_list = ncand <= kRegList;         // uniform over the workgroup
+  const bool use_list = ncand <= kList;            // uniform over the workgroup
   if (use_list) {
     const uint32_t c = (uint32_t)__popcll(cm);
     const uint32_t incl = wave_incl_scan(c);
@@ -911,22 +922,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
     uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)wbase, kWave - 1) + incl - c;
     for (uint64_t m = cm; m; m &= m - 1) {
       const int bit = __builtin_ctzll(m);
-      if (at < (uint32_t)kRegList) cpos[at++] = 4 * (tid + (bit >> 2) * kSelThreads) + (bit & 3);
+      if (at < (uint32_t)kList) cpos[at++] = 4 * (tid + (bit >> 2) * NT) + (bit & 3);
     }
   }
   __syncthreads();
-  constexpr int kListPerThread = kRegList / kSelThreads;
+  constexpr int kListPerThread = kList / NT;
   if (use_list) {
     // the candidates' keys, fetched once more from the row (L2), all loads in flight together
     uint32_t kk[kListPerThread];
 #pragma unroll
     for (int q = 0; q < kListPerThread; ++q) {
-      const int i = tid + q * kSelThreads;
+      const int i = tid + q * NT;
       kk[q] = i < ncand ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, cpos[i] * 4, 0, 0) : 0u;
     }
 #pragma unroll
     for (int q = 0; q < kListPerThread; ++q) {
-      const int i = tid + q * kSelThreads;
+      const int i = tid + q * NT;
       if (i < ncand) {
         const uint32_t k = RAW ? order_key(__uint_as_float(kk[q])) : kk[q];
         ckey[i] = k;                                // read back only by this thread
@@ -944,7 +955,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
     }
   }
   __syncthreads();
-  find_bin_fixed<4096>(hist, need, scan_smem, bcast);
+  find_bin_fixed<4096, NT>(hist, need, scan_smem, bcast);
   uint32_t prefix = (d1 << S1) | (bcast[0] << S2);
   uint32_t pmask = ~((1u << S2) - 1u);
   need -= (int)bcast[1];
@@ -952,12 +963,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   __syncthreads();
   if (!whole) {
 #pragma unroll
-    for (int i = 0; i < 4096 / kSelThreads; ++i) hist[tid + i * kSelThreads] = 0u;
+    for (int i = 0; i < 4096 / NT; ++i) hist[tid + i * NT] = 0u;
     __syncthreads();
     if (use_list) {
 #pragma unroll
       for (int q = 0; q < kListPerThread; ++q) {
-        const int i = tid + q * kSelThreads;
+        const int i = tid + q * NT;
         if (i < ncand) {
           const uint32_t k = ckey[i];
           if ((k & pmask) == prefix) atomicAdd(&hist[k & ((1u << S2) - 1u)], 1u);
@@ -974,7 +985,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
       }
     }
     __syncthreads();
-    find_bin_fixed<(1 << S2)>(hist, need, scan_smem, bcast);
+    find_bin_fixed<(1 << S2), NT>(hist, need, scan_smem, bcast);
     prefix |= bcast[0];
     pmask = 0xFFFFFFFFu;
     need -= (int)bcast[1];
@@ -983,7 +994,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   if (use_list) {
 #pragma unroll
     for (int q = 0; q < kListPerThread; ++q) {
-      const int i = tid + q * kSelThreads;
+      const int i = tid + q * NT;
       if (i < ncand) {
         const int j = cpos[i];
         const uint32_t mk = ckey[i] & pmask;
@@ -994,7 +1005,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   } else {
 #pragma unroll
     for (int u = 0; u < kVec; ++u) {
-      const int i4 = tid + u * kSelThreads;
+      const int i4 = tid + u * NT;
       const uint4 w = to_keys<RAW>(load_vec(u));
       const uint32_t k4[4] = {w.x, w.y, w.z, w.w};
       uint32_t s4 = 0u, t4 = 0u;
@@ -1015,8 +1026,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   const uint64_t eqm = ((uint64_t)tiebm[2 * tid + 1] << 32) | tiebm[2 * tid];
   const uint32_t gt = (uint32_t)__popcll(selm), eq = (uint32_t)__popcll(eqm);
   uint32_t tot;
-  // gt totals at most K <= kRegList < 2^14; eq totals at most 65536 < 2^18
-  const uint32_t before = scan_block((eq << 14) | gt, scan_smem, tot);
+  // gt totals at most K <= kList < 2^14; eq totals at most 65536 < 2^18
+  const uint32_t before = scan_block<NT>((eq << 14) | gt, scan_smem, tot);
   const int eq_before = (int)(before >> 14), gt_before = (int)(before & 0x3FFFu);
   const int take_eq = max(0, min((int)eq, need - eq_before));
   uint64_t keep_eq = eqm;
@@ -1026,7 +1037,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_reg_kernel(const uint
   for (uint64_t m = selm | keep_eq; m; m &= m - 1)
     if (o < K) cpos[o++] = 64 * tid + __builtin_ctzll(m);
   __syncthreads();
-  for (int i = tid; i < K; i += kSelThreads) out[i] = cpos[i];
+  for (int i = tid; i < K; i += NT) out[i] = cpos[i];
   if (tid == 0) sel_count[inst] = K;
   if (kPlan) plan(selm | keep_eq);                  // its LDS (key list, gt bitmap) is read no more
 }
@@ -1044,6 +1055,14 @@ namespace {
 // Rows past the LDS stage that the register-resident select takes.
 bool reg_select(const spc_shape& s) {
   return s.max_len > kTopkLdsKeys && s.max_len <= kRegKeys && s.budget <= kRegList;
+}
+
+// Many instances of one head each with rows that fit the LDS stage: the LDS-staged select runs one
+// workgroup per CU (more than 256 instances: several rounds), the 512-thread register select two per
+// CU.  Budgets of up to 2048 (its plan's two lists take the 4096-entry key list).
+bool half_select(const spc_shape& s) {
+  return s.n_q_heads == s.n_groups && s.max_len <= kTopkLdsKeys && s.batch * s.n_groups > 256 &&
+         s.budget <= 8 * kRegThreadsHalf / 2;
 }
 
 // The keys pass (group max, first-digit histograms), unless one head per group with rows that fit
@@ -1081,7 +1100,10 @@ hipError_t launch_topk(const spc_shape& s, const float* scores, const float2* st
   if (e != hipSuccess) return e;
   const bool raw = s.n_q_heads == s.n_groups;
   const PlanBufs none{};
-  if (s.max_len <= kTopkLdsKeys) {
+  if (half_select(s)) {
+    topk_select_reg_kernel<true, 0, kRegThreadsHalf><<<dim3(inst), kRegThreadsHalf, 0, st>>>(
+        kin, chist, lengths, sel_idx, sel_count, s.n_groups, s.max_len, s.budget, nchunk, none);
+  } else if (s.max_len <= kTopkLdsKeys) {
     if (raw)
       topk_select_lds_kernel<true, 0><<<dim3(inst), kSelThreads, 0, st>>>(kin, chist, lengths, sel_idx, sel_count,
                                                                           s.n_groups, s.max_len, s.budget, nchunk,
@@ -1131,6 +1153,21 @@ hipError_t launch_select_plan(const spc_shape& s, const float* scores, const flo
   if (e != hipSuccess) return e;
   const bool raw = s.n_q_heads == s.n_groups;
   const PlanBufs pb{slot_pos, resident_bm, load_pos, load_slot, load_count, (s.max_len + 31) / 32};
+  if (half_select(s)) {                            // 512 threads, budget <= 2048: cpt <= 4
+    const int hc = (s.budget + kRegThreadsHalf - 1) / kRegThreadsHalf;
+    switch (hc <= 1 ? 1 : hc <= 2 ? 2 : 4) {
+#define SPC_CASE(N)                                                                                           \
+  case N:                                                                                                     \
+    topk_select_reg_kernel<true, N, kRegThreadsHalf><<<dim3(inst), kRegThreadsHalf, 0, st>>>(                 \
+        kin, chist, lengths, sel_idx, sel_count, s.n_groups, s.max_len, s.budget, nchunk, pb);                 \
+    break;
+      SPC_CASE(1)
+      SPC_CASE(2)
+      SPC_CASE(4)
+#undef SPC_CASE
+    }
+    return hipGetLastError();
+  }
   const int cpt = (s.budget + kSelThreads - 1) / kSelThreads;
   if (s.max_len > kTopkLdsKeys) {                  // register select (budget <= kRegList / 2: cpt <= 4)
     switch ((cpt <= 1 ? 1 : cpt <= 2 ? 2 : 4) * (raw ? -1 : 1)) {

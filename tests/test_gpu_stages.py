@@ -201,6 +201,13 @@ LOGIT_TIE_CASES = [
     # threshold bin outgrows the candidate list
     (2, 3, 3, 40001, 1000, [40001, 39000], None, False),
     (1, 2, 2, 50000, 3000, [50000], [0.125], True),
+    # more than 256 instances of one head each (the 512-thread register select, two workgroups per
+    # CU): heavy ties; unaligned rows with n < K; every key equal in rows of 32768, so the threshold
+    # bin outgrows its 4096-entry list; an empty sequence beside a full one
+    (2, 136, 136, 3000, 300, [3000, 2999], [-3.0, 0.0, 2.5], False),
+    (2, 130, 130, 4001, 400, [4001, 1], None, False),
+    (1, 300, 300, 32768, 2048, [32768], [0.125], False),
+    (2, 140, 140, 20000, 2048, [20000, 0], None, False),
 ]
 
 
@@ -551,6 +558,13 @@ FUSED_CASES = [
     ("budget_8192_lds", GQA_SMALL.with_(batch=3, n_q_heads=4, n_kv_heads=2, max_len=20000, budget=8192),
      [[20000, 5000, 8192], [19999, 8192, 8193], [20000, 8193, 12000]]),
     ("mha_64k", W.PRESETS["mha_64k"], None),
+    # more than 256 instances of one head each: the 512-thread register select with the plan in its
+    # tail (budgets 1024 and 2048: two and four slots per thread), lengths at, just above and below
+    # the budget and zero
+    ("raw_many_1024", GQA_SMALL.with_(kind="mha", batch=2, n_q_heads=136, n_kv_heads=136, n_layers=1,
+                                      max_len=3000, budget=1024), [[3000, 1000], [2999, 1024], [3000, 1025]]),
+    ("raw_many_2048", GQA_SMALL.with_(kind="mha", batch=2, n_q_heads=132, n_kv_heads=132, n_layers=1,
+                                      max_len=4000, budget=2048), [[4000, 2048], [3999, 2049], [4000, 0]]),
     ("reg_gqa_40k", GQA_SMALL.with_(batch=2, n_q_heads=4, n_kv_heads=2, max_len=40000, budget=1024),
      [[40000, 1000], [39999, 1024], [40000, 1025]]),
     ("budget_8192", GQA_SMALL.with_(batch=1, n_q_heads=4, n_kv_heads=2, max_len=40000, budget=8192), None),
