@@ -747,9 +747,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
 
 // Rows of 32 769 .. 65 536 keys with a budget of at most kRegList: the keys stay in registers, 64 per
 // thread in strided (coalesced) vectors v = tid + NT u, and never in LDS.  With one head per group
-// the first digit (12 bits) is counted here from the loaded keys and no keys pass runs; otherwise it
-// comes from the chunk histograms (8 bits).  The sweep marks keys above the threshold's first-digit
-// bin in an LDS bitmap of the row (one atomicOr per 4-key vector: a vector is 4 bits of one word) and
+// the first digit (12 bits) is counted here from the loaded keys, each vector as it lands, and no
+// keys pass runs; otherwise it comes from the chunk histograms (8 bits).  The sweep marks keys above
+// the threshold's first-digit bin in an LDS bitmap of the row (a 4-key vector is 4 bits of one word;
+// the 8 lanes of a word OR their pieces by DPP and one of them stores it) and
 // lists the candidates' positions; their keys are fetched once more from the row (L2) into the list,
 // so the later digit passes and the final compare run over the list alone.  Thread t then owns bitmap
 // words 2t and 2t + 1 (positions [64t, 64t + 64)) for the ordered output.
@@ -835,9 +836,19 @@ __global__ __launch_bounds__(NT, 4) void topk_select_reg_kernel(const uint32_t* 
                       (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, o + 8, 0, 0),
                       (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(kr, o + 12, 0, 0));
   };
+  // one branch around all the loads (not one per vector), so that the waits before each vector's
+  // first use count only the loads issued after it
   uint4 v[kVec];
+  if (aligned) {
 #pragma unroll
-  for (int u = 0; u < kVec; ++u) v[u] = load_vec(u);
+    for (int u = 0; u < kVec; ++u) {
+      const Vec16 x = ld16_buffer(kr, (uint32_t)(tid + u * NT) * 16u);
+      v[u] = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) v[u] = load_vec(u);
+  }
   // first digit from the chunk histograms (<= kKeys / kKeyChunk chunks): bin tid % 256 of chunks
   // c0, c0 + NT / 256, ...
   constexpr int kChunkGroups = NT / kBins1;
@@ -859,17 +870,17 @@ __global__ __launch_bounds__(NT, 4) void topk_select_reg_kernel(const uint32_t* 
   for (int i = 0; i < 4096 / NT; ++i) hist[tid + i * NT] = 0u;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    gtbm[tid + i * NT] = 0u;
     selbm[tid + i * NT] = 0u;
     tiebm[tid + i * NT] = 0u;
   }
   if (tid == 0) ccount = 0u;
-#pragma unroll
-  for (int u = 0; u < kVec; ++u) v[u] = to_keys<RAW>(v[u]);
+  // the cleared histogram is visible to every thread; the key loads are still in flight, and each
+  // vector is keyed and counted as it lands
   __syncthreads();
   if (RAW) {
 #pragma unroll
     for (int u = 0; u < kVec; ++u) {
+      v[u] = to_keys<RAW>(v[u]);
       const int j = 4 * (tid + u * NT);
       if (j + 3 < n) {
         atomicAdd(&hist[v[u].x >> S1], 1u);
@@ -910,7 +921,13 @@ __global__ __launch_bounds__(NT, 4) void topk_select_reg_kernel(const uint32_t* 
       g4 |= (uint32_t)(valid && top > d1) << e;
       c4 |= (uint32_t)(valid && top == d1) << e;
     }
-    if (g4) atomicOr(&gtbm[i4 >> 3], g4 << (4 * (i4 & 7)));
+    // the 8 lanes tid & ~7 .. tid | 7 hold the 32 positions of bitmap word i4 >> 3: their 4-bit
+    // pieces are OR-ed by DPP and one lane stores the word (every word is written once, no clear)
+    uint32_t gw = g4 << (4 * (i4 & 7));
+    gw |= dpp_u<kDppQuadXor1>(gw);
+    gw |= dpp_u<kDppQuadXor2>(gw);
+    gw |= dpp_u<kDppHalfMirror>(gw);
+    if ((tid & 7) == 0) gtbm[i4 >> 3] = gw;
     cm |= (uint64_t)c4 << (4 * u);
   }
   const bool use_list = ncand <= kList;            // uniform over the workgroup
