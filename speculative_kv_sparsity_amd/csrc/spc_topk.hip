@@ -745,8 +745,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
   if (kPlan) plan(selw);
 }
 
-// Rows of 32 769 .. 65 536 keys with a budget of at most kRegList: the keys stay in registers, 64 per
-// thread in strided (coalesced) vectors v = tid + NT u, and never in LDS.  With one head per group
+// The register-resident select: the keys of a row stay in registers, 64 per thread in strided
+// (coalesced) vectors v = tid + NT u, and never in LDS.  NT = 1024 takes rows of 32 769 .. 65 536
+// keys with a budget of at most kRegList; NT = 512 takes rows of up to 32 768 keys for many instances
+// of one head each (see below).  With one head per group
 // the first digit (12 bits) is counted here from the loaded keys, each vector as it lands, and no
 // keys pass runs; otherwise it comes from the chunk histograms (8 bits).  The sweep marks keys above
 // the threshold's first-digit bin in an LDS bitmap of the row (a 4-key vector is 4 bits of one word;
@@ -754,8 +756,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_lds_kernel(const uint
 // lists the candidates' positions; their keys are fetched once more from the row (L2) into the list,
 // so the later digit passes and the final compare run over the list alone.  Thread t then owns bitmap
 // words 2t and 2t + 1 (positions [64t, 64t + 64)) for the ordered output.
-// NT = 512 (rows of up to 32 768 keys, a list of 4096, ~60 KB of LDS): two workgroups share a CU, for
-// many instances of one head each (MLA: 4 x 128), which the LDS-staged select runs one per CU.
+// NT = 512 (a list of 4096, ~60 KB of LDS, at most 128 registers): two workgroups share a CU, so that
+// many instances of one head each (MLA: 4 x 128) run as one round, where the LDS-staged select runs
+// one workgroup per CU.
 constexpr int kRegKeys = 65536;
 constexpr int kRegList = 8192;
 constexpr int kRegThreadsHalf = 512;
